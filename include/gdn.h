@@ -1,0 +1,138 @@
+/*
+ * gdn.h -- C ABI of the MI355X (gfx950) library for the packed-batch (varlen)
+ * forward of a gated-delta-net linear-attention layer under continuous batching.
+ *
+ * The operation (page "Continuous batching for linear attention layers", PR
+ * description and the commit that adds the linear attention cache allocator):
+ * many requests of different lengths are packed into one row of T tokens,
+ * delimited by cu_seqlens.  Each request keeps a fixed-size state in one block
+ * of a paged cache: the last W-1 inputs of its causal convolution ("conv"
+ * state) and its recurrent state.  A request with no past reads the zeroed
+ * trash block (block 0); every forward pass overwrites the request's own block
+ * in place.  For every sequence the layer
+ *   1. runs a depthwise causal conv1d of width W over the C = 2*H_k*d_k + H_v*d_v
+ *      channels, continued from the conv state, followed by SiLU;
+ *   2. splits the result into q (H_k heads of d_k), k (H_k heads of d_k) and
+ *      v (H_v heads of d_v), in that channel order, L2-normalises q and k per
+ *      head ( x / sqrt(sum x^2 + eps) ) and multiplies q by q_scale;
+ *   3. runs the gated delta rule (Gated Delta Networks, Yang et al., ICLR 2025)
+ *      for every value head m, reading key head m / (H_v / H_k):
+ *         S_t = a_t (I - b_t k_t k_t^T) S_{t-1} + b_t k_t v_t^T,  o_t = S_t^T q_t,
+ *      with a_t = exp(g_t), b_t = beta_t, S stored [d_k][d_v];
+ *   4. writes o to out and the new conv state and recurrent state to the
+ *      sequence's write block.
+ *
+ * All device work is enqueued on the caller's stream; no call synchronises
+ * with the host, none allocates device memory, and host arrays passed in are
+ * no longer needed when the call returns (the warmup race the page's commit
+ * "...inputs" describes cannot arise from this library).
+ *
+ * Errors: every function returns a gdn_status; gdn_last_error() gives a
+ * readable message for the last non-OK status of the calling thread (the page's
+ * allocator commit refuses bad state declarations "with a readable error").
+ * Nothing aborts and no exception crosses this ABI.
+ */
+#ifndef GDN_H_
+#define GDN_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  GDN_OK = 0,
+  GDN_EINVAL = -1,        /* an argument is invalid (null, inconsistent, out of range) */
+  GDN_EUNSUPPORTED = -2,  /* valid, but a shape or dtype this build does not run */
+  GDN_EWORKSPACE = -3,    /* workspace missing or smaller than gdn_workspace_size() */
+  GDN_EHIP = -4           /* the HIP runtime reported an error (message has its text) */
+} gdn_status;
+
+typedef enum { GDN_F32 = 0, GDN_BF16 = 1 } gdn_dtype;
+
+/* Shapes and numeric options of one layer; every shape is passed explicitly
+ * (the page's allocator commit: shapes are declared by the layer, not read
+ * from one model family's config). */
+typedef struct {
+  int32_t num_k_heads;  /* H_k >= 1 */
+  int32_t num_v_heads;  /* H_v, a multiple of H_k */
+  int32_t head_k_dim;   /* d_k in {16, 32, 64, 128} */
+  int32_t head_v_dim;   /* d_v in {16, 32, 64, 128} */
+  int32_t conv_width;   /* W in [1, 4] */
+  int32_t act_dtype;    /* gdn_dtype of x, conv weight, conv pool and out; the
+                           recurrent state, g and beta are always fp32 */
+  float l2norm_eps;     /* eps of the q/k L2 normalisation, >= 0 (1e-6 usual) */
+  float q_scale;        /* multiplies normalised q; <= 0 means 1/sqrt(d_k) */
+} gdn_layer_desc;
+
+/* One per-request state a layer declares (page "Continuous batching for linear
+ * attention layers", commit declaring linear_attention_states: each state has a
+ * shape and a dtype, and a block holds each on a 128-byte boundary). */
+typedef struct {
+  char name[16];      /* "conv" or "recurrent" */
+  int32_t ndim;
+  int64_t shape[4];
+  int32_t dtype;      /* gdn_dtype */
+  int64_t bytes;      /* product of shape times element size */
+  int32_t align;      /* required alignment of the state inside a block: 128 */
+} gdn_state_decl;
+
+/* Fills out[0] = conv state [W-1][C] in act dtype (W-1 may be 0) and
+ * out[1] = recurrent state [H_v][d_k][d_v] fp32.  Host only. */
+int gdn_state_spec(const gdn_layer_desc* desc, gdn_state_decl out[2]);
+
+/* Bytes of device workspace gdn_varlen_forward needs for a batch of
+ * total_tokens packed tokens and num_seqs sequences.  Host only. */
+int gdn_workspace_size(const gdn_layer_desc* desc, int32_t total_tokens,
+                       int32_t num_seqs, size_t* bytes);
+
+/* The packed-batch forward (steps 1-4 above).
+ *
+ * Device pointers (all on the current HIP device, 16-byte aligned):
+ *   x            [T][C] act dtype, row-major (the packed row of conv inputs)
+ *   conv_weight  [C][W] act dtype
+ *   g            [T][H_v] fp32, log of the decay (a = exp(g), g <= 0 expected)
+ *   beta         [T][H_v] fp32, the delta-rule write strength
+ *   cu_seqlens   [N+1] int32, cu_seqlens[0] = 0, non-decreasing, cu_seqlens[N] = T
+ *   read_idx     [N] int32, block each sequence reads its states from (0 = trash
+ *                block, for a request with no past)
+ *   write_idx    [N] int32, block each sequence owns and overwrites; < 0 marks a
+ *                padding sequence: nothing is read or written for it and its out
+ *                rows are left as they are
+ *   conv_pool    P blocks of the conv state, block i at conv_pool + i*conv_block_stride
+ *                bytes; may be NULL when W == 1
+ *   ssm_pool     P blocks of the recurrent state [H_v][d_k][d_v] fp32, block i at
+ *                ssm_pool + i*ssm_block_stride bytes (the two pools may be views of
+ *                one block buffer at different 128-byte aligned offsets)
+ *   out          [T][H_v][d_v] act dtype
+ *   workspace    device scratch of at least gdn_workspace_size() bytes, 256-byte
+ *                aligned; its contents on entry do not matter
+ * Host pointer:
+ *   cu_seqlens_host  the same N+1 offsets in host memory; the library plans its
+ *                launches from it so that it never reads device memory back.
+ * Preconditions the library cannot check without a sync (violations give
+ * undefined results, never out-of-bounds accesses for indices outside [0, P),
+ * which are skipped): device cu_seqlens equals cu_seqlens_host; write blocks are
+ * distinct, never block 0 and never another sequence's read block; block 0 is
+ * all zero.  read_idx[i] == write_idx[i] is the ordinary in-place continue.
+ * stream is a hipStream_t (NULL = the default stream).
+ */
+int gdn_varlen_forward(const gdn_layer_desc* desc, const void* x,
+                       const void* conv_weight, const float* g, const float* beta,
+                       const int32_t* cu_seqlens, const int32_t* cu_seqlens_host,
+                       int32_t num_seqs, int32_t total_tokens,
+                       const int32_t* read_idx, const int32_t* write_idx,
+                       void* conv_pool, int64_t conv_block_stride, float* ssm_pool,
+                       int64_t ssm_block_stride, int32_t num_blocks, void* out,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
+/* Message of the last non-OK status returned on this thread ("" if none). */
+const char* gdn_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN_H_ */

@@ -1,0 +1,159 @@
+"""Python binding of the gfx950 gated-delta-net varlen forward library.
+
+Thin ctypes marshalling over ``include/gdn.h``: every function has the C name
+and only turns torch tensors into pointers, sizes and strides; all computation
+happens in the HIP kernels of ``_lib/libgdn.so``.  PyTorch is used for device
+memory and the current HIP stream only.  There is no fallback: if the library
+is not built, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "_lib", "libgdn.so")
+
+GDN_OK, GDN_EINVAL, GDN_EUNSUPPORTED, GDN_EWORKSPACE, GDN_EHIP = 0, -1, -2, -3, -4
+GDN_F32, GDN_BF16 = 0, 1
+EXPORTS = ("gdn_state_spec", "gdn_workspace_size", "gdn_varlen_forward", "gdn_last_error")
+
+_lib = None
+
+
+class GdnError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__("gdn status %d: %s" % (status, message))
+        self.status = status
+        self.message = message
+
+
+class gdn_layer_desc(ctypes.Structure):
+    _fields_ = [
+        ("num_k_heads", ctypes.c_int32),
+        ("num_v_heads", ctypes.c_int32),
+        ("head_k_dim", ctypes.c_int32),
+        ("head_v_dim", ctypes.c_int32),
+        ("conv_width", ctypes.c_int32),
+        ("act_dtype", ctypes.c_int32),
+        ("l2norm_eps", ctypes.c_float),
+        ("q_scale", ctypes.c_float),
+    ]
+
+
+class gdn_state_decl(ctypes.Structure):
+    _fields_ = [
+        ("name", ctypes.c_char * 16),
+        ("ndim", ctypes.c_int32),
+        ("shape", ctypes.c_int64 * 4),
+        ("dtype", ctypes.c_int32),
+        ("bytes", ctypes.c_int64),
+        ("align", ctypes.c_int32),
+    ]
+
+
+def load_library():
+    """Loads ``_lib/libgdn.so``; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                "libgdn.so is not built (expected %s); run `python -m linear_attention_state_amd.build`"
+                % LIB_PATH)
+        lib = ctypes.CDLL(LIB_PATH)
+        P = ctypes.c_void_p
+        lib.gdn_state_spec.restype = ctypes.c_int
+        lib.gdn_state_spec.argtypes = [ctypes.POINTER(gdn_layer_desc), ctypes.POINTER(gdn_state_decl)]
+        lib.gdn_workspace_size.restype = ctypes.c_int
+        lib.gdn_workspace_size.argtypes = [ctypes.POINTER(gdn_layer_desc), ctypes.c_int32, ctypes.c_int32,
+                                           ctypes.POINTER(ctypes.c_size_t)]
+        lib.gdn_last_error.restype = ctypes.c_char_p
+        lib.gdn_last_error.argtypes = []
+        lib.gdn_varlen_forward.restype = ctypes.c_int
+        lib.gdn_varlen_forward.argtypes = [
+            ctypes.POINTER(gdn_layer_desc), P, P, P, P, P, P, ctypes.c_int32, ctypes.c_int32, P, P,
+            P, ctypes.c_int64, P, ctypes.c_int64, ctypes.c_int32, P, P, ctypes.c_size_t, P]
+        _lib = lib
+    return _lib
+
+
+def make_desc(layer) -> gdn_layer_desc:
+    """Descriptor from any object with the layer's attributes (``workloads.Layer``)."""
+    return gdn_layer_desc(int(layer.num_k_heads), int(layer.num_v_heads), int(layer.head_k_dim),
+                          int(layer.head_v_dim), int(layer.conv_width),
+                          GDN_BF16 if layer.act_dtype == "bf16" else GDN_F32,
+                          float(layer.l2norm_eps), float(layer.q_scale))
+
+
+def gdn_last_error() -> str:
+    return load_library().gdn_last_error().decode()
+
+
+def _check(rc: int):
+    if rc != GDN_OK:
+        raise GdnError(rc, gdn_last_error())
+
+
+def gdn_state_spec(layer) -> list:
+    arr = (gdn_state_decl * 2)()
+    _check(load_library().gdn_state_spec(ctypes.byref(make_desc(layer)), arr))
+    return [dict(name=d.name.decode(), shape=tuple(d.shape[i] for i in range(d.ndim)), dtype=d.dtype,
+                 bytes=d.bytes, align=d.align) for d in arr]
+
+
+def gdn_workspace_size(layer, total_tokens: int, num_seqs: int) -> int:
+    out = ctypes.c_size_t(0)
+    _check(load_library().gdn_workspace_size(ctypes.byref(make_desc(layer)), int(total_tokens), int(num_seqs),
+                                             ctypes.byref(out)))
+    return out.value
+
+
+def _dev_ptr(t, name):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("%s must be a device tensor" % name)
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def gdn_varlen_forward(layer, x, conv_weight, g, beta, cu_seqlens, cu_seqlens_host, read_idx, write_idx,
+                       conv_pool, ssm_pool, out, workspace=None, stream=None):
+    """Enqueues the packed-batch forward on ``stream`` (default: torch's current
+    stream).  Device tensors as in ``gdn.h``; ``cu_seqlens_host`` is a CPU int32
+    tensor (or list) with the same offsets.  Pools are updated in place; block
+    strides are taken from the pool tensors' first dimension."""
+    import torch
+
+    lib = load_library()
+    if not isinstance(cu_seqlens_host, torch.Tensor):
+        cu_seqlens_host = torch.tensor(list(cu_seqlens_host), dtype=torch.int32)
+    cu_h = cu_seqlens_host.to(torch.int32).contiguous()
+    if cu_h.is_cuda:
+        raise ValueError("cu_seqlens_host must be host memory")
+    num_seqs = cu_h.numel() - 1
+    total = int(x.shape[0])
+    for name, t, dt in (("cu_seqlens", cu_seqlens, torch.int32), ("read_idx", read_idx, torch.int32),
+                        ("write_idx", write_idx, torch.int32), ("g", g, torch.float32),
+                        ("beta", beta, torch.float32), ("ssm_pool", ssm_pool, torch.float32)):
+        if t.dtype != dt:
+            raise ValueError("%s must be %s" % (name, dt))
+    if workspace is None:
+        nbytes = gdn_workspace_size(layer, total, num_seqs)
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=x.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(x.device).cuda_stream
+    conv_stride = conv_pool.stride(0) * conv_pool.element_size() if conv_pool is not None and conv_pool.dim() else 0
+    ssm_stride = ssm_pool.stride(0) * ssm_pool.element_size()
+    rc = lib.gdn_varlen_forward(
+        ctypes.byref(make_desc(layer)), _dev_ptr(x, "x"), _dev_ptr(conv_weight, "conv_weight"),
+        _dev_ptr(g, "g"), _dev_ptr(beta, "beta"), _dev_ptr(cu_seqlens, "cu_seqlens"),
+        ctypes.c_void_p(cu_h.data_ptr()), num_seqs, total, _dev_ptr(read_idx, "read_idx"),
+        _dev_ptr(write_idx, "write_idx"),
+        _dev_ptr(conv_pool, "conv_pool") if conv_pool is not None and conv_pool.numel() else None,
+        conv_stride, _dev_ptr(ssm_pool, "ssm_pool"), ssm_stride, int(ssm_pool.shape[0]),
+        _dev_ptr(out, "out"), _dev_ptr(workspace, "workspace"), workspace.numel(),
+        ctypes.c_void_p(stream))
+    _check(rc)
+    return out

@@ -1,0 +1,216 @@
+// gdn_api.cpp -- the C ABI (include/gdn.h): argument checks, launch planning
+// from the host copy of cu_seqlens, and the kernel launches on the caller's
+// stream.  No device memory is allocated and nothing synchronises with the host.
+//
+// Planning follows the page "Continuous batching for linear attention layers":
+// the linear layers' state indices hold one entry per sequence (allocator
+// commit), the prefill path must not sync with the host (the PR notes the fla
+// chunked kernel does, which keeps accelerator graphs off), and the engine's
+// batch preparation (page input_ouputs.py, prepare_batch_tensors) builds
+// cu_seqlens on the host and rejects an empty batch.
+#include <hip/hip_runtime.h>
+
+#include <climits>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "../../include/gdn.h"
+#include "gdn_device.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+bool pow2_dim(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
+
+int check_desc(const gdn_layer_desc* d) {
+  if (!d) return fail(GDN_EINVAL, "layer descriptor is NULL");
+  if (d->num_k_heads < 1 || d->num_v_heads < 1)
+    return fail(GDN_EINVAL, "head counts must be >= 1 (H_k=%d, H_v=%d)", d->num_k_heads, d->num_v_heads);
+  if (d->num_v_heads % d->num_k_heads != 0)
+    return fail(GDN_EINVAL, "H_v=%d is not a multiple of H_k=%d", d->num_v_heads, d->num_k_heads);
+  if (d->act_dtype != GDN_F32 && d->act_dtype != GDN_BF16)
+    return fail(GDN_EINVAL, "act_dtype %d is neither GDN_F32 nor GDN_BF16", d->act_dtype);
+  if (!(d->l2norm_eps >= 0.0f)) return fail(GDN_EINVAL, "l2norm_eps must be >= 0");
+  if (d->head_k_dim < 1 || d->head_v_dim < 1)
+    return fail(GDN_EINVAL, "head dims must be >= 1 (d_k=%d, d_v=%d)", d->head_k_dim, d->head_v_dim);
+  if (d->conv_width < 1) return fail(GDN_EINVAL, "conv_width must be >= 1 (got %d)", d->conv_width);
+  if (!pow2_dim(d->head_k_dim) || !pow2_dim(d->head_v_dim))
+    return fail(GDN_EUNSUPPORTED, "head dims must be 16, 32, 64 or 128 (d_k=%d, d_v=%d)", d->head_k_dim,
+                d->head_v_dim);
+  if (d->conv_width > 4) return fail(GDN_EUNSUPPORTED, "conv_width %d > 4 is not built", d->conv_width);
+  const int64_t C = 2LL * d->num_k_heads * d->head_k_dim + (int64_t)d->num_v_heads * d->head_v_dim;
+  if (C > INT_MAX / 8) return fail(GDN_EUNSUPPORTED, "too many conv channels (%lld)", (long long)C);
+  return GDN_OK;
+}
+
+int64_t channels(const gdn_layer_desc* d) {
+  return 2LL * d->num_k_heads * d->head_k_dim + (int64_t)d->num_v_heads * d->head_v_dim;
+}
+
+int64_t act_size(const gdn_layer_desc* d) { return d->act_dtype == GDN_BF16 ? 2 : 4; }
+
+int64_t conv_state_bytes(const gdn_layer_desc* d) { return (int64_t)(d->conv_width - 1) * channels(d) * act_size(d); }
+
+int64_t ssm_state_bytes(const gdn_layer_desc* d) {
+  return (int64_t)d->num_v_heads * d->head_k_dim * d->head_v_dim * 4;
+}
+
+size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+size_t workspace_bytes_for(const gdn_layer_desc* d, int64_t total_tokens) {
+  return round_up((size_t)total_tokens * (size_t)channels(d) * (size_t)act_size(d), 256);
+}
+
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
+
+}  // namespace
+
+extern "C" int gdn_state_spec(const gdn_layer_desc* desc, gdn_state_decl out[2]) {
+  int rc = check_desc(desc);
+  if (rc) return rc;
+  if (!out) return fail(GDN_EINVAL, "output array is NULL");
+  memset(out, 0, 2 * sizeof(gdn_state_decl));
+  snprintf(out[0].name, sizeof(out[0].name), "conv");
+  out[0].ndim = 2;
+  out[0].shape[0] = desc->conv_width - 1;
+  out[0].shape[1] = channels(desc);
+  out[0].dtype = desc->act_dtype;
+  out[0].bytes = conv_state_bytes(desc);
+  out[0].align = 128;
+  snprintf(out[1].name, sizeof(out[1].name), "recurrent");
+  out[1].ndim = 3;
+  out[1].shape[0] = desc->num_v_heads;
+  out[1].shape[1] = desc->head_k_dim;
+  out[1].shape[2] = desc->head_v_dim;
+  out[1].dtype = GDN_F32;
+  out[1].bytes = ssm_state_bytes(desc);
+  out[1].align = 128;
+  return GDN_OK;
+}
+
+extern "C" int gdn_workspace_size(const gdn_layer_desc* desc, int32_t total_tokens, int32_t num_seqs,
+                                  size_t* bytes) {
+  int rc = check_desc(desc);
+  if (rc) return rc;
+  if (!bytes) return fail(GDN_EINVAL, "bytes is NULL");
+  if (total_tokens < 0 || num_seqs < 0) return fail(GDN_EINVAL, "negative token or sequence count");
+  *bytes = workspace_bytes_for(desc, total_tokens);
+  return GDN_OK;
+}
+
+extern "C" const char* gdn_last_error(void) { return g_last_error.c_str(); }
+
+extern "C" int gdn_varlen_forward(const gdn_layer_desc* desc, const void* x, const void* conv_weight,
+                                  const float* g, const float* beta, const int32_t* cu_seqlens,
+                                  const int32_t* cu_seqlens_host, int32_t num_seqs, int32_t total_tokens,
+                                  const int32_t* read_idx, const int32_t* write_idx, void* conv_pool,
+                                  int64_t conv_block_stride, float* ssm_pool, int64_t ssm_block_stride,
+                                  int32_t num_blocks, void* out, void* workspace, size_t workspace_bytes,
+                                  void* stream) {
+  int rc = check_desc(desc);
+  if (rc) return rc;
+  const int W = desc->conv_width;
+  const bool bf16 = desc->act_dtype == GDN_BF16;
+
+  // ---- host-side checks; nothing below reads device memory
+  if (num_seqs < 1) return fail(GDN_EINVAL, "no sequences in batch (num_seqs=%d)", num_seqs);
+  if (total_tokens < 0) return fail(GDN_EINVAL, "total_tokens=%d is negative", total_tokens);
+  if (!cu_seqlens_host) return fail(GDN_EINVAL, "cu_seqlens_host is NULL");
+  if (cu_seqlens_host[0] != 0) return fail(GDN_EINVAL, "cu_seqlens[0]=%d, expected 0", cu_seqlens_host[0]);
+  for (int i = 0; i < num_seqs; ++i)
+    if (cu_seqlens_host[i + 1] < cu_seqlens_host[i])
+      return fail(GDN_EINVAL, "cu_seqlens decreases at %d (%d -> %d)", i, cu_seqlens_host[i],
+                  cu_seqlens_host[i + 1]);
+  if (cu_seqlens_host[num_seqs] != total_tokens)
+    return fail(GDN_EINVAL, "cu_seqlens[%d]=%d differs from total_tokens=%d", num_seqs,
+                cu_seqlens_host[num_seqs], total_tokens);
+  if (!cu_seqlens || !read_idx || !write_idx) return fail(GDN_EINVAL, "device cu_seqlens/read_idx/write_idx is NULL");
+  if (!ssm_pool) return fail(GDN_EINVAL, "ssm_pool is NULL");
+  if (W > 1 && !conv_pool) return fail(GDN_EINVAL, "conv_pool is NULL but conv_width=%d > 1", W);
+  if (total_tokens > 0 && (!x || !g || !beta || !out))
+    return fail(GDN_EINVAL, "x, g, beta and out must be non-NULL when total_tokens > 0");
+  if (!conv_weight && total_tokens > 0) return fail(GDN_EINVAL, "conv_weight is NULL");
+  if (num_blocks < 2) return fail(GDN_EINVAL, "num_blocks=%d; the pool needs the trash block and one more", num_blocks);
+  if (ssm_block_stride < ssm_state_bytes(desc) || ssm_block_stride % 128)
+    return fail(GDN_EINVAL, "ssm_block_stride=%lld must be a multiple of 128 and >= %lld", (long long)ssm_block_stride,
+                (long long)ssm_state_bytes(desc));
+  if (W > 1 && (conv_block_stride < conv_state_bytes(desc) || conv_block_stride % 128))
+    return fail(GDN_EINVAL, "conv_block_stride=%lld must be a multiple of 128 and >= %lld",
+                (long long)conv_block_stride, (long long)conv_state_bytes(desc));
+  if (!aligned(x, 16) || !aligned(out, 16) || !aligned(ssm_pool, 16) || !aligned(conv_pool, 16) ||
+      !aligned(g, 4) || !aligned(beta, 4))
+    return fail(GDN_EINVAL, "x, out and the pools must be 16-byte aligned");
+  const size_t need = workspace_bytes_for(desc, total_tokens);
+  if (need > 0 && (!workspace || workspace_bytes < need))
+    return fail(GDN_EWORKSPACE, "workspace of %zu bytes is smaller than the %zu needed", workspace_bytes, need);
+  if (workspace && !aligned(workspace, 256)) return fail(GDN_EINVAL, "workspace must be 256-byte aligned");
+
+  // ---- plan from the host offsets
+  int n_long = 0, n_short = 0;
+  for (int i = 0; i < num_seqs; ++i) {
+    const int L = cu_seqlens_host[i + 1] - cu_seqlens_host[i];
+    if (L >= 2) ++n_long; else ++n_short;
+  }
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const int C = (int)channels(desc);
+  hipError_t e = hipSuccess;
+
+  if (total_tokens > 0) {
+    gdn::ConvArgs ca{};
+    ca.x = x; ca.w = conv_weight; ca.cu = cu_seqlens; ca.read_idx = read_idx; ca.write_idx = write_idx;
+    ca.conv_pool = reinterpret_cast<const char*>(conv_pool); ca.conv_stride = conv_block_stride;
+    ca.y = workspace;
+    ca.num_seqs = num_seqs; ca.total_tokens = total_tokens; ca.num_blocks = num_blocks; ca.channels = C;
+    ca.qk_channels = desc->num_k_heads * desc->head_k_dim; ca.head_k_dim = desc->head_k_dim;
+    ca.rows_per_block = total_tokens >= 16384 ? 16 : (total_tokens >= 2048 ? 4 : 1);
+    ca.eps = desc->l2norm_eps;
+    ca.q_scale = desc->q_scale > 0.f ? desc->q_scale : 1.0f / sqrtf((float)desc->head_k_dim);
+    e = gdn::launch_conv(ca, W, bf16, st);
+    if (e != hipSuccess) return fail(GDN_EHIP, "conv launch: %s", hipGetErrorString(e));
+  }
+  if (W > 1) {
+    gdn::TailArgs ta{};
+    ta.x = x; ta.cu = cu_seqlens; ta.read_idx = read_idx; ta.write_idx = write_idx;
+    ta.conv_pool = reinterpret_cast<char*>(conv_pool); ta.conv_stride = conv_block_stride;
+    ta.num_seqs = num_seqs; ta.num_blocks = num_blocks; ta.channels = C;
+    e = gdn::launch_tail_commit(ta, W, bf16, st);
+    if (e != hipSuccess) return fail(GDN_EHIP, "conv state commit launch: %s", hipGetErrorString(e));
+  }
+
+  gdn::ScanArgs sa{};
+  sa.y = workspace; sa.g = g; sa.beta = beta; sa.cu = cu_seqlens; sa.read_idx = read_idx;
+  sa.write_idx = write_idx; sa.ssm_pool = ssm_pool; sa.ssm_stride = ssm_block_stride; sa.out = out;
+  sa.num_seqs = num_seqs; sa.num_blocks = num_blocks; sa.num_k_heads = desc->num_k_heads;
+  sa.num_v_heads = desc->num_v_heads; sa.channels = C;
+  const bool chunked = bf16 && gdn::chunk_supported(desc->head_k_dim, desc->head_v_dim);
+  if (chunked) {
+    if (n_long > 0) {
+      sa.min_len = 2; sa.max_len = INT_MAX;
+      e = gdn::launch_chunk(sa, desc->head_k_dim, desc->head_v_dim, st);
+      if (e != hipSuccess) return fail(GDN_EHIP, "chunk scan launch: %s", hipGetErrorString(e));
+    }
+    if (n_short > 0) {
+      sa.min_len = 0; sa.max_len = 1;
+      e = gdn::launch_recurrent(sa, desc->head_k_dim, desc->head_v_dim, true, st);
+      if (e != hipSuccess) return fail(GDN_EHIP, "decode launch: %s", hipGetErrorString(e));
+    }
+  } else {
+    sa.min_len = 0; sa.max_len = INT_MAX;
+    e = gdn::launch_recurrent(sa, desc->head_k_dim, desc->head_v_dim, bf16, st);
+    if (e != hipSuccess) return fail(GDN_EHIP, "recurrent launch: %s", hipGetErrorString(e));
+  }
+  return GDN_OK;
+}

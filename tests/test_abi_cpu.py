@@ -1,0 +1,105 @@
+"""The C ABI on the CPU: the library loads, exports every function gdn.h
+declares, describes the states, and rejects bad arguments with a readable
+message before touching the GPU (no call here reaches a kernel launch)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import linear_attention_state_amd as gdn
+import workloads
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    with open(os.path.join(ROOT, "include", "gdn.h")) as f:
+        text = f.read()
+    return sorted(set(re.findall(r"\b(gdn_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    lib = gdn.load_library()
+    names = _declared()
+    assert set(names) == set(gdn.EXPORTS)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_state_spec_bf16_layer():
+    conv, rec = gdn.gdn_state_spec(workloads.BIG)
+    assert conv["name"] == "conv" and conv["shape"] == (3, 8192) and conv["bytes"] == 3 * 8192 * 2
+    assert rec["name"] == "recurrent" and rec["shape"] == (32, 128, 128) and rec["bytes"] == 2 * 1024 * 1024
+    assert conv["align"] == rec["align"] == 128
+
+
+def test_state_spec_width1_has_empty_conv_state():
+    conv, _ = gdn.gdn_state_spec(workloads.Layer(1, 1, 16, 16, 1, "f32"))
+    assert conv["shape"] == (0, 48) and conv["bytes"] == 0
+
+
+def test_workspace_size():
+    n = gdn.gdn_workspace_size(workloads.BIG, 1000, 3)
+    assert n >= 1000 * 8192 * 2 and n % 256 == 0
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("num_k_heads", 0, gdn.GDN_EINVAL),
+    ("num_v_heads", 3, gdn.GDN_EINVAL),
+    ("head_k_dim", 48, gdn.GDN_EUNSUPPORTED),
+    ("head_v_dim", 256, gdn.GDN_EUNSUPPORTED),
+    ("conv_width", 5, gdn.GDN_EUNSUPPORTED),
+    ("conv_width", 0, gdn.GDN_EINVAL),
+    ("act_dtype", "fp8", gdn.GDN_EINVAL),
+])
+def test_bad_layer_rejected(field, value, status):
+    import dataclasses
+    layer = dataclasses.replace(workloads.BIG, **{field: value})
+    with pytest.raises(gdn.GdnError) as ei:
+        if field == "act_dtype":
+            d = gdn.make_desc(workloads.BIG)
+            d.act_dtype = 7
+            arr = (gdn.gdn_state_decl * 2)()
+            rc = gdn.load_library().gdn_state_spec(ctypes.byref(d), arr)
+            gdn._check(rc)
+        else:
+            gdn.gdn_state_spec(layer)
+    assert ei.value.status == status and ei.value.message
+
+
+def _call(layer, cu_host, T, n=None, **over):
+    """gdn_varlen_forward with fake (never dereferenced) device pointers."""
+    lib = gdn.load_library()
+    fake = ctypes.c_void_p(1 << 20)
+    n = len(cu_host) - 1 if n is None else n
+    cu = (ctypes.c_int32 * len(cu_host))(*cu_host)
+    args = dict(x=fake, w=fake, g=fake, b=fake, cu=fake, cuh=cu, n=n, T=T, ri=fake, wi=fake,
+                conv=fake, cstride=3 * 8192 * 2, ssm=fake, sstride=2 << 20, P=8, out=fake,
+                ws=fake, wsb=1 << 40, st=None)
+    args.update(over)
+    rc = lib.gdn_varlen_forward(ctypes.byref(gdn.make_desc(layer)), args["x"], args["w"], args["g"], args["b"],
+                                args["cu"], args["cuh"], args["n"], args["T"], args["ri"], args["wi"],
+                                args["conv"], args["cstride"], args["ssm"], args["sstride"], args["P"],
+                                args["out"], args["ws"], args["wsb"], args["st"])
+    return rc, gdn.gdn_last_error()
+
+
+@pytest.mark.parametrize("cu,T,over,status,needle", [
+    ([0], 0, {}, gdn.GDN_EINVAL, "no sequences"),
+    ([1, 4], 4, {}, gdn.GDN_EINVAL, "cu_seqlens[0]"),
+    ([0, 5, 3], 3, {}, gdn.GDN_EINVAL, "decreases"),
+    ([0, 5, 9], 8, {}, gdn.GDN_EINVAL, "total_tokens"),
+    ([0, 4], 4, {"cuh": None}, gdn.GDN_EINVAL, "cu_seqlens_host"),
+    ([0, 4], 4, {"ssm": None}, gdn.GDN_EINVAL, "ssm_pool"),
+    ([0, 4], 4, {"conv": None}, gdn.GDN_EINVAL, "conv_pool"),
+    ([0, 4], 4, {"P": 1}, gdn.GDN_EINVAL, "num_blocks"),
+    ([0, 4], 4, {"sstride": (2 << 20) - 128}, gdn.GDN_EINVAL, "ssm_block_stride"),
+    ([0, 4], 4, {"cstride": 3 * 8192 * 2 + 64}, gdn.GDN_EINVAL, "conv_block_stride"),
+    ([0, 4], 4, {"wsb": 100}, gdn.GDN_EWORKSPACE, "workspace"),
+    ([0, 4], 4, {"ws": None}, gdn.GDN_EWORKSPACE, "workspace"),
+    ([0, 4], 4, {"x": ctypes.c_void_p((1 << 20) + 8)}, gdn.GDN_EINVAL, "aligned"),
+])
+def test_forward_rejects_bad_arguments(cu, T, over, status, needle):
+    rc, msg = _call(workloads.BIG, cu, T, **over)
+    assert rc == status and needle in msg, (rc, msg)
