@@ -70,6 +70,7 @@ int64_t ssm_state_bytes(const gdn_layer_desc* d) {
 
 size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
+// The workspace holds the conv output of the packed row for the chunked prefill.
 size_t workspace_bytes_for(const gdn_layer_desc* d, int64_t total_tokens) {
   return round_up((size_t)total_tokens * (size_t)channels(d) * (size_t)act_size(d), 256);
 }
@@ -168,7 +169,23 @@ extern "C" int gdn_varlen_forward(const gdn_layer_desc* desc, const void* x, con
   const int C = (int)channels(desc);
   hipError_t e = hipSuccess;
 
-  if (total_tokens > 0) {
+  gdn::ScanArgs sa{};
+  sa.y = workspace; sa.x = x; sa.w = conv_weight;
+  sa.conv_pool = W > 1 ? reinterpret_cast<const char*>(conv_pool) : nullptr;
+  sa.conv_stride = conv_block_stride; sa.width = W; sa.eps = desc->l2norm_eps;
+  sa.q_scale = desc->q_scale > 0.f ? desc->q_scale : 1.0f / sqrtf((float)desc->head_k_dim);
+  sa.g = g; sa.beta = beta; sa.cu = cu_seqlens; sa.read_idx = read_idx;
+  sa.write_idx = write_idx; sa.ssm_pool = ssm_pool; sa.ssm_stride = ssm_block_stride; sa.out = out;
+  sa.num_seqs = num_seqs; sa.num_blocks = num_blocks; sa.num_k_heads = desc->num_k_heads;
+  sa.num_v_heads = desc->num_v_heads; sa.channels = C;
+
+  // Order on the stream: (1) conv + SiLU + norm of the packed row into the
+  // workspace for the chunked prefill, (2) chunked prefill, (3) the token path
+  // (decode, or everything in fp32 / other head sizes), which runs its own conv
+  // from the conv states, (4) conv-state commit, last, once every reader of the
+  // old conv states has been enqueued.
+  const bool chunked = bf16 && gdn::chunk_supported(desc->head_k_dim, desc->head_v_dim);
+  if (chunked && n_long > 0) {
     gdn::ConvArgs ca{};
     ca.x = x; ca.w = conv_weight; ca.cu = cu_seqlens; ca.read_idx = read_idx; ca.write_idx = write_idx;
     ca.conv_pool = reinterpret_cast<const char*>(conv_pool); ca.conv_stride = conv_block_stride;
@@ -176,10 +193,18 @@ extern "C" int gdn_varlen_forward(const gdn_layer_desc* desc, const void* x, con
     ca.num_seqs = num_seqs; ca.total_tokens = total_tokens; ca.num_blocks = num_blocks; ca.channels = C;
     ca.qk_channels = desc->num_k_heads * desc->head_k_dim; ca.head_k_dim = desc->head_k_dim;
     ca.rows_per_block = total_tokens >= 16384 ? 16 : (total_tokens >= 2048 ? 4 : 1);
-    ca.eps = desc->l2norm_eps;
-    ca.q_scale = desc->q_scale > 0.f ? desc->q_scale : 1.0f / sqrtf((float)desc->head_k_dim);
+    ca.eps = sa.eps;
+    ca.q_scale = sa.q_scale;
     e = gdn::launch_conv(ca, W, bf16, st);
     if (e != hipSuccess) return fail(GDN_EHIP, "conv launch: %s", hipGetErrorString(e));
+    sa.min_len = 2; sa.max_len = INT_MAX;
+    e = gdn::launch_chunk(sa, desc->head_k_dim, desc->head_v_dim, st);
+    if (e != hipSuccess) return fail(GDN_EHIP, "chunk scan launch: %s", hipGetErrorString(e));
+  }
+  if (!chunked || n_short > 0) {
+    sa.min_len = 0; sa.max_len = chunked ? 1 : INT_MAX;
+    e = gdn::launch_recurrent(sa, desc->head_k_dim, desc->head_v_dim, bf16, st);
+    if (e != hipSuccess) return fail(GDN_EHIP, "token path launch: %s", hipGetErrorString(e));
   }
   if (W > 1) {
     gdn::TailArgs ta{};
@@ -188,29 +213,6 @@ extern "C" int gdn_varlen_forward(const gdn_layer_desc* desc, const void* x, con
     ta.num_seqs = num_seqs; ta.num_blocks = num_blocks; ta.channels = C;
     e = gdn::launch_tail_commit(ta, W, bf16, st);
     if (e != hipSuccess) return fail(GDN_EHIP, "conv state commit launch: %s", hipGetErrorString(e));
-  }
-
-  gdn::ScanArgs sa{};
-  sa.y = workspace; sa.g = g; sa.beta = beta; sa.cu = cu_seqlens; sa.read_idx = read_idx;
-  sa.write_idx = write_idx; sa.ssm_pool = ssm_pool; sa.ssm_stride = ssm_block_stride; sa.out = out;
-  sa.num_seqs = num_seqs; sa.num_blocks = num_blocks; sa.num_k_heads = desc->num_k_heads;
-  sa.num_v_heads = desc->num_v_heads; sa.channels = C;
-  const bool chunked = bf16 && gdn::chunk_supported(desc->head_k_dim, desc->head_v_dim);
-  if (chunked) {
-    if (n_long > 0) {
-      sa.min_len = 2; sa.max_len = INT_MAX;
-      e = gdn::launch_chunk(sa, desc->head_k_dim, desc->head_v_dim, st);
-      if (e != hipSuccess) return fail(GDN_EHIP, "chunk scan launch: %s", hipGetErrorString(e));
-    }
-    if (n_short > 0) {
-      sa.min_len = 0; sa.max_len = 1;
-      e = gdn::launch_recurrent(sa, desc->head_k_dim, desc->head_v_dim, true, st);
-      if (e != hipSuccess) return fail(GDN_EHIP, "decode launch: %s", hipGetErrorString(e));
-    }
-  } else {
-    sa.min_len = 0; sa.max_len = INT_MAX;
-    e = gdn::launch_recurrent(sa, desc->head_k_dim, desc->head_v_dim, bf16, st);
-    if (e != hipSuccess) return fail(GDN_EHIP, "recurrent launch: %s", hipGetErrorString(e));
   }
   return GDN_OK;
 }

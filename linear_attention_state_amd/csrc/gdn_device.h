@@ -67,7 +67,13 @@ struct TailArgs {
 };
 
 struct ScanArgs {
-  const void* y;  // conv output after SiLU/normalisation, [T][C]
+  const void* y;  // conv output after SiLU/normalisation, [T][C] (chunked path)
+  const void* x;  // conv input [T][C] and weights [C][W] (token path, which runs the conv itself)
+  const void* w;
+  const char* conv_pool;
+  int64_t conv_stride;
+  int width;
+  float eps, q_scale;
   const float* g;
   const float* beta;
   const int32_t* cu;

@@ -7,7 +7,11 @@
 //     S_t = a_t (I - b_t k_t k_t^T) S_{t-1} + b_t k_t v_t^T,   o_t = S_t^T q_t.
 // Evaluated in delta form: kS = S^T k, u = b (v - a kS), S <- a S + k u^T, and
 // o = a S_{t-1}^T q + (k.q) u, so one reduction pass over d_k serves both kS and
-// the output.
+// the output.  The kernel also runs the token's causal conv + SiLU for the
+// 2 d_k + d_v channels its head reads (window of W-1 inputs in registers,
+// started from the conv state) and folds the q/k L2 normalisation into that same
+// reduction pass (|k|^2 and |q|^2 are reduced with the dot products and applied
+// afterwards), so q, k and v stay in fp32 from x to the output.
 //
 // One workgroup of 256 threads owns one (sequence, value head).  A thread holds
 // 4 adjacent d_v columns of d_k/(256/(d_v/4)) rows in registers; a wave's load
@@ -60,7 +64,9 @@ __global__ __launch_bounds__(256) void recurrent_kernel(ScanArgs a) {
   constexpr int RG = NT / C4;         // row groups
   constexpr int RPT = (DK + RG - 1) / RG;
   constexpr int NW = NT / 64;
+  constexpr int NCH = 2 * DK + DV;    // conv channels this head reads: q, k of its key head, its v
   static_assert(C4 <= 64 && (64 % C4) == 0, "row group must fit a wave");
+  static_assert(NCH <= 2 * NT, "two channels per thread at most");
 
   const int s = blockIdx.x, m = blockIdx.y;
   if (s >= a.num_seqs) return;
@@ -85,31 +91,68 @@ __global__ __launch_bounds__(256) void recurrent_kernel(ScanArgs a) {
     S[i] = row < DK ? *reinterpret_cast<const float4*>(S0 + row * DV + c4 * 4) : make_float4(0.f, 0.f, 0.f, 0.f);
   }
 
-  __shared__ float sq[DK], sk[DK];
-  __shared__ float red[NW][2 * DV + 4];
+  // conv channels owned by this thread (index i into [q | k | v] of this head)
   const int64_t C = a.channels;
-  const int64_t qoff = (int64_t)h * DK, koff = (int64_t)a.num_k_heads * DK + h * DK;
-  const int64_t voff = 2 * (int64_t)a.num_k_heads * DK + (int64_t)m * DV + c4 * 4;
+  const int W = a.width;
+  int64_t gch[2];
+  bool has[2];
+  float wt[2][4], win[2][3], wlast[2];
+  const char* tail = a.conv_pool ? a.conv_pool + (int64_t)a.read_idx[s] * a.conv_stride : nullptr;
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    const int i = tid + NT * e;
+    has[e] = i < NCH && L > 0;  // an empty sequence reads no input at all
+    gch[e] = i < DK ? (int64_t)h * DK + i
+           : i < 2 * DK ? (int64_t)a.num_k_heads * DK + h * DK + (i - DK)
+                        : 2 * (int64_t)a.num_k_heads * DK + (int64_t)m * DV + (i - 2 * DK);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) wt[e][j] = (has[e] && j < W) ? ld1<BF16>(a.w, gch[e] * W + j) : 0.f;
+#pragma unroll
+    for (int j = 0; j < 3; ++j) win[e][j] = (has[e] && j < W - 1) ? ld1<BF16>(tail, (int64_t)j * C + gch[e]) : 0.f;
+    wlast[e] = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (j == W - 1) wlast[e] = wt[e][j];
+  }
+
+  __shared__ __align__(16) float sy[NCH];
+  __shared__ __align__(16) float red[NW][2 * DV + 4];
 
   for (int t = 0; t < L; ++t) {
     const int64_t r = r0 + t;
-    if (tid < DK) sq[tid] = ld1<BF16>(a.y, r * C + qoff + tid);
-    else if (tid < 2 * DK) sk[tid - DK] = ld1<BF16>(a.y, r * C + koff + tid - DK);
-    const float4 v = ld4<BF16>(a.y, r * C + voff);
+    // ---- causal conv + SiLU of this token for the head's channels
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      if (!has[e]) continue;
+      const float xin = ld1<BF16>(a.x, r * C + gch[e]);
+      float acc = wlast[e] * xin;
+#pragma unroll
+      for (int j = 0; j < 3; ++j)
+        if (j < W - 1) acc = fmaf(wt[e][j], win[e][j], acc);
+#pragma unroll
+      for (int j = 0; j < 3; ++j) {
+        if (j + 1 < W - 1) win[e][j] = win[e][j + 1];
+        else if (j == W - 2) win[e][j] = xin;
+      }
+      sy[tid + NT * e] = silu(acc);
+    }
     const float gv = a.g[r * a.num_v_heads + m];
     const float bv = a.beta[r * a.num_v_heads + m];
     __syncthreads();
 
+    // ---- one pass over the state rows: S^T k, S^T q, k.q, |k|^2, |q|^2 (unnormalised q, k)
     float4 kS = make_float4(0.f, 0.f, 0.f, 0.f), Sq = kS;
-    float kq = 0.f;
+    float kq = 0.f, kk = 0.f, qq = 0.f;
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
       const int row = rg + RG * i;
       if (row < DK) {
-        const float kr = sk[row], qr = sq[row];
+        const float kr = sy[DK + row], qr = sy[row];
         kS = f4_fma(kr, S[i], kS);
         Sq = f4_fma(qr, S[i], Sq);
         kq = fmaf(kr, qr, kq);
+        kk = fmaf(kr, kr, kk);
+        qq = fmaf(qr, qr, qq);
       }
     }
 #pragma unroll
@@ -119,16 +162,22 @@ __global__ __launch_bounds__(256) void recurrent_kernel(ScanArgs a) {
       Sq.x += __shfl_xor(Sq.x, off); Sq.y += __shfl_xor(Sq.y, off);
       Sq.z += __shfl_xor(Sq.z, off); Sq.w += __shfl_xor(Sq.w, off);
       kq += __shfl_xor(kq, off);
+      kk += __shfl_xor(kk, off);
+      qq += __shfl_xor(qq, off);
     }
     if (lane < C4) {
       *reinterpret_cast<float4*>(&red[wave][c4 * 4]) = kS;
       *reinterpret_cast<float4*>(&red[wave][DV + c4 * 4]) = Sq;
-      if (c4 == 0) red[wave][2 * DV] = kq;
+      if (c4 == 0) {
+        red[wave][2 * DV] = kq;
+        red[wave][2 * DV + 1] = kk;
+        red[wave][2 * DV + 2] = qq;
+      }
     }
     __syncthreads();
     kS = make_float4(0.f, 0.f, 0.f, 0.f);
     Sq = kS;
-    kq = 0.f;
+    kq = kk = qq = 0.f;
 #pragma unroll
     for (int w = 0; w < NW; ++w) {
       const float4 x = *reinterpret_cast<const float4*>(&red[w][c4 * 4]);
@@ -136,24 +185,31 @@ __global__ __launch_bounds__(256) void recurrent_kernel(ScanArgs a) {
       kS.x += x.x; kS.y += x.y; kS.z += x.z; kS.w += x.w;
       Sq.x += y.x; Sq.y += y.y; Sq.z += y.z; Sq.w += y.w;
       kq += red[w][2 * DV];
+      kk += red[w][2 * DV + 1];
+      qq += red[w][2 * DV + 2];
     }
+    // normalisation folded in: k_hat = k / sqrt(|k|^2 + eps), q_hat = q_scale q / sqrt(|q|^2 + eps)
+    const float ik = 1.0f / sqrtf(kk + a.eps);
+    const float iq = a.q_scale / sqrtf(qq + a.eps);
     const float av = __expf(gv);
+    const float4 v = *reinterpret_cast<const float4*>(&sy[2 * DK + c4 * 4]);
     float4 u;
-    u.x = bv * (v.x - av * kS.x); u.y = bv * (v.y - av * kS.y);
-    u.z = bv * (v.z - av * kS.z); u.w = bv * (v.w - av * kS.w);
+    u.x = bv * (v.x - av * kS.x * ik); u.y = bv * (v.y - av * kS.y * ik);
+    u.z = bv * (v.z - av * kS.z * ik); u.w = bv * (v.w - av * kS.w * ik);
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
       const int row = rg + RG * i;
       if (row < DK) {
-        const float kr = sk[row];
+        const float kr = sy[DK + row] * ik;
         S[i].x = fmaf(av, S[i].x, kr * u.x); S[i].y = fmaf(av, S[i].y, kr * u.y);
         S[i].z = fmaf(av, S[i].z, kr * u.z); S[i].w = fmaf(av, S[i].w, kr * u.w);
       }
     }
     if (rg == 0) {
+      const float kqn = kq * ik * iq, aq = av * iq;
       float4 o;
-      o.x = fmaf(av, Sq.x, kq * u.x); o.y = fmaf(av, Sq.y, kq * u.y);
-      o.z = fmaf(av, Sq.z, kq * u.z); o.w = fmaf(av, Sq.w, kq * u.w);
+      o.x = fmaf(aq, Sq.x, kqn * u.x); o.y = fmaf(aq, Sq.y, kqn * u.y);
+      o.z = fmaf(aq, Sq.z, kqn * u.z); o.w = fmaf(aq, Sq.w, kqn * u.w);
       st4<BF16>(a.out, (r * a.num_v_heads + m) * DV + c4 * 4, o);
     }
     __syncthreads();
