@@ -1,0 +1,198 @@
+"""Benchmark of the packed-batch gated-delta-net layer forward on one MI355X.
+
+One step = one gdn_varlen_forward call over one batch of the workload: conv +
+SiLU + q/k normalisation, the gated delta rule with state read from and written
+to the pools, outputs written.  Inputs (x, weights, g, beta, offsets, indices,
+state pools) are generated once, copied to HBM before timing, and stay there.
+
+Primary line: the prefill workload (8 sequences, lengths uniform in [256, 4096],
+H_k=16, H_v=32, d_k=d_v=128, W=4, bf16 activations, fp32 state), tokens/s.
+The same JSON line carries the decode workload (256 sequences of one token,
+1024-block pool) as a nested object, each with the roofline of its dominant
+kernel, the per-kernel event timings, and the fp64 CPU oracle timed on the
+host cores beside it.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_MFMA = 2.5e15  # dense bf16 MFMA, MI355X
+PEAK_HBM = 8.0e12        # HBM3E, MI355X
+METRIC = "GDN layer tokens/s (prefill, decode) at 1 GPU; % MFMA / HBM peak"
+
+
+def chunk_flops(layer, lengths, c: int = 64) -> float:
+    """Algorithmic flops of the chunked (WY / UT) form: per chunk of c rows,
+    H_k Gram pairs (Q K^T, K K^T: 4 c^2 d_k) and per value head the dense
+    products W, U~ (2 c^2 (d_k + d_v)), P U (2 c^2 d_v), W S, Q S, K^T U
+    (6 c d_k d_v) and the triangular inverse (2/3 c^3)."""
+    Hk, Hv, dk, dv = layer.num_k_heads, layer.num_v_heads, layer.head_k_dim, layer.head_v_dim
+    total = 0.0
+    for L in lengths:
+        if L < 2:
+            continue
+        full, rem = divmod(L, c)
+        for cc in [c] * full + ([rem] if rem else []):
+            total += Hk * 4 * cc * cc * dk + Hv * (2 * cc * cc * (dk + dv) + 2 * cc * cc * dv
+                                                   + 6 * cc * dk * dv + (2.0 / 3.0) * cc ** 3)
+    return total
+
+
+def token_path_bytes(layer, n_tokens: int) -> float:
+    """Algorithmic HBM bytes of the one-token path per launch: per token the
+    fp32 state of every value head read and written, the token's x row, the
+    conv state read, the output row, g and beta."""
+    C = layer.conv_channels
+    s = 2 if layer.act_dtype == "bf16" else 4
+    state = layer.num_v_heads * layer.head_k_dim * layer.head_v_dim * 4
+    per_tok = 2 * state + C * s + (layer.conv_width - 1) * C * s + layer.num_v_heads * layer.head_v_dim * s \
+        + 2 * layer.num_v_heads * 4
+    return n_tokens * per_tok + C * layer.conv_width * s
+
+
+def load_traffic(kernel: str):
+    """HBM bytes per launch measured with rocprofv3 counters, if a summary for
+    this kernel's current source is committed under profiles/."""
+    import hashlib
+
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    src = {"chunk_scan": "gdn_chunk.hip", "token_recurrent": "gdn_recurrent.hip",
+           "conv_silu_norm": "gdn_conv.hip"}.get(kernel)
+    if src is None:
+        return None
+    with open(os.path.join(ROOT, "linear_attention_state_amd", "csrc", src), "rb") as f:
+        sha = hashlib.sha256(f.read()).hexdigest()[:16]
+    with open(path) as f:
+        for line in f:
+            parts = line.split()
+            if len(parts) >= 4 and not line.startswith("#") and parts[0] == kernel and parts[1] == sha:
+                return float(parts[2]) + float(parts[3])
+    return None
+
+
+def run(cfg_id: int, steps: int, warmup: int):
+    import torch
+
+    import linear_attention_state_amd as gdn
+    import workloads
+
+    b = workloads.config(cfg_id)
+    L = b.layer
+    dev = torch.device("cuda", 0)
+    d = {k: getattr(b, k).to(dev).contiguous() for k in
+         ("x", "conv_weight", "g", "beta", "cu_seqlens", "read_idx", "write_idx", "conv_pool", "ssm_pool")}
+    T = b.total_tokens
+    out = torch.empty(T, L.num_v_heads, L.head_v_dim, dtype=L.torch_act, device=dev)
+    ws = torch.empty(max(gdn.gdn_workspace_size(L, T, len(b.lengths)), 1), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    cu_host = b.cu_seqlens.clone()
+
+    def step():
+        gdn.gdn_varlen_forward(L, d["x"], d["conv_weight"], d["g"], d["beta"], d["cu_seqlens"], cu_host,
+                               d["read_idx"], d["write_idx"], d["conv_pool"], d["ssm_pool"], out,
+                               workspace=ws, stream=stream.cuda_stream)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    gdn.gdn_kernel_timing(True)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kt = gdn.gdn_kernel_times()
+    gdn.gdn_kernel_timing(False)
+    ms = ev0.elapsed_time(ev1) / steps
+    kernels = {k: {"avg_ms": v[0] / max(v[1], 1), "launches": v[1]} for k, v in kt.items()}
+    dom = max(kernels, key=lambda k: kernels[k]["avg_ms"] * kernels[k]["launches"])
+    dom_s = kernels[dom]["avg_ms"] * 1e-3
+    if dom == "chunk_scan":
+        work = chunk_flops(L, b.lengths)
+        roof = {"bound": "mfma", "achieved": work / dom_s / 1e12, "peak": PEAK_BF16_MFMA / 1e12,
+                "unit": "TFLOP/s"}
+    else:
+        n_short = sum(1 for v in b.lengths if v <= 1)
+        work = token_path_bytes(L, n_short)
+        roof = {"bound": "hbm", "achieved": work / dom_s / 1e9, "peak": PEAK_HBM / 1e9, "unit": "GB/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    traffic = load_traffic(dom)
+    roof["traffic"] = traffic
+    roof["kernel"] = dom
+    return {
+        "batch": b, "ms_per_step": ms, "wall_s": wall, "tokens": T,
+        "value": T * steps / (ms * steps * 1e-3), "kernels": kernels, "roofline": roof,
+    }
+
+
+def cpu_baseline(batch):
+    """The fp64 oracle on the host cores, on the same workload (all of it when
+    it takes under half a minute), tokens/s."""
+    import oracle
+
+    threads = len(os.sched_getaffinity(0))
+    omp = os.environ.get("OMP_NUM_THREADS")
+    if omp and omp.isdigit():
+        threads = min(threads, int(omp))
+    t0 = time.perf_counter()
+    oracle.forward(batch.layer, batch.x, batch.conv_weight, batch.g, batch.beta, batch.cu_seqlens,
+                   batch.read_idx, batch.write_idx, batch.conv_pool, batch.ssm_pool, threads=threads)
+    dt = time.perf_counter() - t0
+    return {"value": batch.total_tokens / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": "the whole workload (%d tokens, %d sequences), %.1f s" % (batch.total_tokens,
+                                                                              len(batch.lengths), dt)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this layer's path runs on a single MI355X "
+              "(--gpus %d was asked for)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    pre = run(1, args.steps, args.warmup)
+    b = pre["batch"]
+    line = {
+        "metric": METRIC, "value": pre["value"], "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": pre["ms_per_step"], "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "prefill: %d sequences, lengths %s, T=%d; H_k=16, H_v=32, d_k=d_v=128, W=4, "
+                               "C=8192; bf16 activations, fp32 state; all from the trash block"
+                               % (len(b.lengths), b.lengths, b.total_tokens),
+                   "global_batch": len(b.lengths), "seq_len": max(b.lengths), "tokens": b.total_tokens},
+        "roofline": pre["roofline"], "kernels": pre["kernels"],
+    }
+    if not args.no_decode:
+        dec = run(2, args.steps, args.warmup)
+        line["decode"] = {"workload": "decode: 256 sequences of 1 token, 1024-block pool of 2 MiB fp32 states",
+                          "value": dec["value"], "unit": "tokens/s", "ms_per_step": dec["ms_per_step"],
+                          "roofline": dec["roofline"], "kernels": dec["kernels"]}
+        del dec
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(b)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

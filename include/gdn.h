@@ -131,6 +131,23 @@ int gdn_varlen_forward(const gdn_layer_desc* desc, const void* x,
 /* Message of the last non-OK status returned on this thread ("" if none). */
 const char* gdn_last_error(void);
 
+/* Measurement support (not needed to run the layer).
+ * gdn_kernel_timing(1) makes every later gdn_varlen_forward in this process
+ * record a HIP event pair on the call's stream around each kernel it launches,
+ * and clears the totals; gdn_kernel_timing(0) stops recording.
+ * gdn_kernel_times() waits for the recorded events (a host sync), adds their
+ * elapsed times to per-kernel totals and copies up to `max` entries to `out`;
+ * `count` receives the number of kernels with at least one timed launch.
+ * The library creates the events it records and keeps them for reuse. */
+typedef struct {
+  char name[32];      /* kernel: "conv_silu_norm", "chunk_scan", "token_recurrent", "conv_state_commit" */
+  double total_ms;    /* summed event-to-event time of its timed launches */
+  int64_t launches;
+} gdn_kernel_time;
+
+int gdn_kernel_timing(int enable);
+int gdn_kernel_times(gdn_kernel_time* out, int32_t max, int32_t* count);
+
 #ifdef __cplusplus
 }
 #endif

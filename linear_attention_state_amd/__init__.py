@@ -16,7 +16,8 @@ LIB_PATH = os.path.join(HERE, "_lib", "libgdn.so")
 
 GDN_OK, GDN_EINVAL, GDN_EUNSUPPORTED, GDN_EWORKSPACE, GDN_EHIP = 0, -1, -2, -3, -4
 GDN_F32, GDN_BF16 = 0, 1
-EXPORTS = ("gdn_state_spec", "gdn_workspace_size", "gdn_varlen_forward", "gdn_last_error")
+EXPORTS = ("gdn_state_spec", "gdn_workspace_size", "gdn_varlen_forward", "gdn_last_error",
+           "gdn_kernel_timing", "gdn_kernel_times")
 
 _lib = None
 
@@ -52,6 +53,10 @@ class gdn_state_decl(ctypes.Structure):
     ]
 
 
+class gdn_kernel_time(ctypes.Structure):
+    _fields_ = [("name", ctypes.c_char * 32), ("total_ms", ctypes.c_double), ("launches", ctypes.c_int64)]
+
+
 def load_library():
     """Loads ``_lib/libgdn.so``; raises if it has not been built."""
     global _lib
@@ -73,6 +78,11 @@ def load_library():
         lib.gdn_varlen_forward.argtypes = [
             ctypes.POINTER(gdn_layer_desc), P, P, P, P, P, P, ctypes.c_int32, ctypes.c_int32, P, P,
             P, ctypes.c_int64, P, ctypes.c_int64, ctypes.c_int32, P, P, ctypes.c_size_t, P]
+        lib.gdn_kernel_timing.restype = ctypes.c_int
+        lib.gdn_kernel_timing.argtypes = [ctypes.c_int]
+        lib.gdn_kernel_times.restype = ctypes.c_int
+        lib.gdn_kernel_times.argtypes = [ctypes.POINTER(gdn_kernel_time), ctypes.c_int32,
+                                         ctypes.POINTER(ctypes.c_int32)]
         _lib = lib
     return _lib
 
@@ -157,3 +167,16 @@ def gdn_varlen_forward(layer, x, conv_weight, g, beta, cu_seqlens, cu_seqlens_ho
         ctypes.c_void_p(stream))
     _check(rc)
     return out
+
+
+def gdn_kernel_timing(enable: bool) -> None:
+    """Turns per-kernel HIP event timing of later forward calls on or off."""
+    _check(load_library().gdn_kernel_timing(1 if enable else 0))
+
+
+def gdn_kernel_times() -> dict:
+    """{kernel: (total_ms, launches)} of the timed launches so far (waits for them)."""
+    arr = (gdn_kernel_time * 8)()
+    n = ctypes.c_int32(0)
+    _check(load_library().gdn_kernel_times(arr, 8, ctypes.byref(n)))
+    return {arr[i].name.decode(): (arr[i].total_ms, arr[i].launches) for i in range(min(n.value, 8))}

@@ -14,7 +14,9 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
+#include <vector>
 
 #include "../../include/gdn.h"
 #include "gdn_device.h"
@@ -77,7 +79,90 @@ size_t workspace_bytes_for(const gdn_layer_desc* d, int64_t total_tokens) {
 
 bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
 
+// ---- optional per-kernel event timing (measurement only)
+enum { K_CONV = 0, K_CHUNK, K_TOKEN, K_TAIL, K_COUNT };
+const char* const kKernelNames[K_COUNT] = {"conv_silu_norm", "chunk_scan", "token_recurrent", "conv_state_commit"};
+
+struct Timing {
+  std::mutex mu;
+  bool on = false;
+  struct Rec { int k; hipEvent_t a, b; };
+  std::vector<Rec> pending;
+  std::vector<hipEvent_t> spare;
+  double total_ms[K_COUNT] = {};
+  int64_t launches[K_COUNT] = {};
+};
+Timing g_timing;
+
+hipEvent_t take_event() {
+  if (!g_timing.spare.empty()) {
+    hipEvent_t e = g_timing.spare.back();
+    g_timing.spare.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+// Runs `launch` (which enqueues one kernel on st), bracketed by events when timing is on.
+template <class F>
+hipError_t timed(int k, hipStream_t st, F launch) {
+  if (!g_timing.on) return launch();
+  std::lock_guard<std::mutex> lock(g_timing.mu);
+  hipEvent_t a = take_event(), b = take_event();
+  if (!a || !b) return launch();
+  hipEventRecord(a, st);
+  hipError_t e = launch();
+  hipEventRecord(b, st);
+  g_timing.pending.push_back({k, a, b});
+  return e;
+}
+
 }  // namespace
+
+extern "C" int gdn_kernel_timing(int enable) {
+  std::lock_guard<std::mutex> lock(g_timing.mu);
+  if (enable) {
+    for (auto& r : g_timing.pending) {
+      hipEventSynchronize(r.b);
+      g_timing.spare.push_back(r.a);
+      g_timing.spare.push_back(r.b);
+    }
+    g_timing.pending.clear();
+    for (int k = 0; k < K_COUNT; ++k) { g_timing.total_ms[k] = 0; g_timing.launches[k] = 0; }
+  }
+  g_timing.on = enable != 0;
+  return GDN_OK;
+}
+
+extern "C" int gdn_kernel_times(gdn_kernel_time* out, int32_t max, int32_t* count) {
+  std::lock_guard<std::mutex> lock(g_timing.mu);
+  for (auto& r : g_timing.pending) {
+    hipError_t e = hipEventSynchronize(r.b);
+    float ms = 0.f;
+    if (e == hipSuccess) e = hipEventElapsedTime(&ms, r.a, r.b);
+    if (e != hipSuccess) return fail(GDN_EHIP, "kernel timing: %s", hipGetErrorString(e));
+    g_timing.total_ms[r.k] += ms;
+    g_timing.launches[r.k] += 1;
+    g_timing.spare.push_back(r.a);
+    g_timing.spare.push_back(r.b);
+  }
+  g_timing.pending.clear();
+  int n = 0;
+  for (int k = 0; k < K_COUNT; ++k) {
+    if (!g_timing.launches[k]) continue;
+    if (out && n < max) {
+      memset(&out[n], 0, sizeof(out[n]));
+      snprintf(out[n].name, sizeof(out[n].name), "%s", kKernelNames[k]);
+      out[n].total_ms = g_timing.total_ms[k];
+      out[n].launches = g_timing.launches[k];
+    }
+    ++n;
+  }
+  if (count) *count = n;
+  return GDN_OK;
+}
 
 extern "C" int gdn_state_spec(const gdn_layer_desc* desc, gdn_state_decl out[2]) {
   int rc = check_desc(desc);
@@ -195,15 +280,15 @@ extern "C" int gdn_varlen_forward(const gdn_layer_desc* desc, const void* x, con
     ca.rows_per_block = total_tokens >= 16384 ? 16 : (total_tokens >= 2048 ? 4 : 1);
     ca.eps = sa.eps;
     ca.q_scale = sa.q_scale;
-    e = gdn::launch_conv(ca, W, bf16, st);
+    e = timed(K_CONV, st, [&] { return gdn::launch_conv(ca, W, bf16, st); });
     if (e != hipSuccess) return fail(GDN_EHIP, "conv launch: %s", hipGetErrorString(e));
     sa.min_len = 2; sa.max_len = INT_MAX;
-    e = gdn::launch_chunk(sa, desc->head_k_dim, desc->head_v_dim, st);
+    e = timed(K_CHUNK, st, [&] { return gdn::launch_chunk(sa, desc->head_k_dim, desc->head_v_dim, st); });
     if (e != hipSuccess) return fail(GDN_EHIP, "chunk scan launch: %s", hipGetErrorString(e));
   }
   if (!chunked || n_short > 0) {
     sa.min_len = 0; sa.max_len = chunked ? 1 : INT_MAX;
-    e = gdn::launch_recurrent(sa, desc->head_k_dim, desc->head_v_dim, bf16, st);
+    e = timed(K_TOKEN, st, [&] { return gdn::launch_recurrent(sa, desc->head_k_dim, desc->head_v_dim, bf16, st); });
     if (e != hipSuccess) return fail(GDN_EHIP, "token path launch: %s", hipGetErrorString(e));
   }
   if (W > 1) {
@@ -211,7 +296,7 @@ extern "C" int gdn_varlen_forward(const gdn_layer_desc* desc, const void* x, con
     ta.x = x; ta.cu = cu_seqlens; ta.read_idx = read_idx; ta.write_idx = write_idx;
     ta.conv_pool = reinterpret_cast<char*>(conv_pool); ta.conv_stride = conv_block_stride;
     ta.num_seqs = num_seqs; ta.num_blocks = num_blocks; ta.channels = C;
-    e = gdn::launch_tail_commit(ta, W, bf16, st);
+    e = timed(K_TAIL, st, [&] { return gdn::launch_tail_commit(ta, W, bf16, st); });
     if (e != hipSuccess) return fail(GDN_EHIP, "conv state commit launch: %s", hipGetErrorString(e));
   }
   return GDN_OK;
