@@ -165,12 +165,30 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--only", choices=["prefill", "decode"], default=None,
+                    help="run one workload alone and print its numbers (profiling runs)")
+    ap.add_argument("--copy-bytes", type=int, default=0,
+                    help="run only a device-to-device copy of this many bytes (calibrates HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this layer's path runs on a single MI355X "
               "(--gpus %d was asked for)" % args.gpus, file=sys.stderr)
         sys.exit(2)
 
+    if args.copy_bytes:
+        import torch
+        src = torch.ones(args.copy_bytes // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(args.warmup + args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": args.copy_bytes, "launches": args.warmup + args.steps}), flush=True)
+        return
+    if args.only:
+        r = run(1 if args.only == "prefill" else 2, args.steps, args.warmup)
+        print(json.dumps({"workload": args.only, "value": r["value"], "ms_per_step": r["ms_per_step"],
+                          "roofline": r["roofline"], "kernels": r["kernels"]}), flush=True)
+        return
     pre = run(1, args.steps, args.warmup)
     b = pre["batch"]
     line = {

@@ -105,7 +105,9 @@ int gdn_workspace_size(const gdn_layer_desc* desc, int32_t total_tokens,
  *                bytes; may be NULL when W == 1
  *   ssm_pool     P blocks of the recurrent state [H_v][d_k][d_v] fp32, block i at
  *                ssm_pool + i*ssm_block_stride bytes (the two pools may be views of
- *                one block buffer at different 128-byte aligned offsets)
+ *                one block buffer at different 128-byte aligned offsets, the
+ *                placement gdn_state_spec asks for; the library itself needs both
+ *                strides to be multiples of 16 bytes and at least the state size)
  *   out          [T][H_v][d_v] act dtype
  *   workspace    device scratch of at least gdn_workspace_size() bytes, 256-byte
  *                aligned; its contents on entry do not matter

@@ -10,6 +10,7 @@
 // cu_seqlens on the host and rejects an empty batch.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <climits>
 #include <cstdarg>
 #include <cstdio>
@@ -230,11 +231,11 @@ extern "C" int gdn_varlen_forward(const gdn_layer_desc* desc, const void* x, con
     return fail(GDN_EINVAL, "x, g, beta and out must be non-NULL when total_tokens > 0");
   if (!conv_weight && total_tokens > 0) return fail(GDN_EINVAL, "conv_weight is NULL");
   if (num_blocks < 2) return fail(GDN_EINVAL, "num_blocks=%d; the pool needs the trash block and one more", num_blocks);
-  if (ssm_block_stride < ssm_state_bytes(desc) || ssm_block_stride % 128)
-    return fail(GDN_EINVAL, "ssm_block_stride=%lld must be a multiple of 128 and >= %lld", (long long)ssm_block_stride,
+  if (ssm_block_stride < ssm_state_bytes(desc) || ssm_block_stride % 16)
+    return fail(GDN_EINVAL, "ssm_block_stride=%lld must be a multiple of 16 and >= %lld", (long long)ssm_block_stride,
                 (long long)ssm_state_bytes(desc));
-  if (W > 1 && (conv_block_stride < conv_state_bytes(desc) || conv_block_stride % 128))
-    return fail(GDN_EINVAL, "conv_block_stride=%lld must be a multiple of 128 and >= %lld",
+  if (W > 1 && (conv_block_stride < conv_state_bytes(desc) || conv_block_stride % 16))
+    return fail(GDN_EINVAL, "conv_block_stride=%lld must be a multiple of 16 and >= %lld",
                 (long long)conv_block_stride, (long long)conv_state_bytes(desc));
   if (!aligned(x, 16) || !aligned(out, 16) || !aligned(ssm_pool, 16) || !aligned(conv_pool, 16) ||
       !aligned(g, 4) || !aligned(beta, 4))
@@ -283,7 +284,22 @@ extern "C" int gdn_varlen_forward(const gdn_layer_desc* desc, const void* x, con
     e = timed(K_CONV, st, [&] { return gdn::launch_conv(ca, W, bf16, st); });
     if (e != hipSuccess) return fail(GDN_EHIP, "conv launch: %s", hipGetErrorString(e));
     sa.min_len = 2; sa.max_len = INT_MAX;
-    e = timed(K_CHUNK, st, [&] { return gdn::launch_chunk(sa, desc->head_k_dim, desc->head_v_dim, st); });
+    // longest sequences first, so the longest chains start before the short ones
+    static thread_local gdn::SeqOrder order;
+    order.n = 0;
+    if (n_long <= gdn::kMaxOrder) {
+      std::vector<std::pair<int, int>> lens;
+      lens.reserve(n_long);
+      for (int i = 0; i < num_seqs; ++i) {
+        const int L = cu_seqlens_host[i + 1] - cu_seqlens_host[i];
+        if (L >= 2) lens.push_back({-L, i});
+      }
+      std::stable_sort(lens.begin(), lens.end());
+      for (size_t i = 0; i < lens.size(); ++i) order.seq[i] = (uint16_t)lens[i].second;
+      order.n = (int32_t)lens.size();
+      if (num_seqs > 65535) order.n = 0;
+    }
+    e = timed(K_CHUNK, st, [&] { return gdn::launch_chunk(sa, order, desc->head_k_dim, desc->head_v_dim, st); });
     if (e != hipSuccess) return fail(GDN_EHIP, "chunk scan launch: %s", hipGetErrorString(e));
   }
   if (!chunked || n_short > 0) {

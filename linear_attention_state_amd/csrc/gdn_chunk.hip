@@ -13,52 +13,61 @@
 //     S <- Gamma_c S + K^T diag(e^{gamma_c-gamma}) U
 // Only differences of running sums are exponentiated, so every factor is <= 1.
 //
-// Work split: one 256-thread workgroup (4 waves) per (sequence, value head,
-// 64-wide slice of d_v); it walks the sequence's chunks in order with its
-// 128 x 64 fp32 state slice in registers (the columns of S evolve
-// independently, so slicing d_v is exact).  All products are
-// v_mfma_f32_16x16x32_bf16 with fp32 accumulation; operands are bf16 tiles in
-// LDS.  T is built from fp32 forward substitution on its four 16x16 diagonal
-// blocks and two levels of block products for the rest.  W is kept in
-// registers between the product that makes it and the one that uses it: its
-// accumulator rows are exactly the A operand rows the next product needs,
-// taken in a permuted k order (the MFMA sums over k, so any order shared by both
-// operands gives the same result).
+// Work split: one 512-thread workgroup (8 waves, two per SIMD) per (sequence,
+// value head); it walks the sequence's chunks in order.  Wave w owns the d_v
+// columns [16w, 16w+16) of the 128 x 128 fp32 state, held in its registers.
+// The columns of S evolve independently, so the state pass of a chunk
+// (U = U~ - W S, O, S update) is local to each wave: S, U and O stay in
+// registers and only the shared operands W, Q, P, K^T come from LDS.  The
+// chunk preparation (Gram products, T, W, P) is shared by all waves through
+// LDS.  All products are v_mfma_f32_16x16x32_bf16 (bf16 operands, fp32
+// accumulate).  T comes from fp32 forward substitution on its four 16x16
+// diagonal blocks (column-oriented, so each step's updates are independent)
+// and two levels of block products.  The next chunk's K, V, Q, g, beta are
+// loaded into registers while the current chunk computes and staged in LDS at
+// the top of the next iteration; global pointers are address space 1 and the
+// workgroup barriers wait for LDS traffic only, so those loads and the output
+// stores stay in flight across them.  Sequences are launched longest first.
 //
 // MFMA 16x16x32 bf16 operand layout (lane l, r = l & 15, grp = l >> 4):
 //   A: row r, 8 values of k;  B: column r, the same 8 values of k;
 //   D: column r, rows 4*grp + {0,1,2,3}.
+// The MFMA sums over k, so any k order shared by both operands gives the same
+// product; "permuted" operands below take k = {4grp..4grp+3, 16+4grp..16+4grp+3}
+// of each 32-wide step, which is what a D tile pair holds.
 #include "gdn_device.h"
 
 namespace gdn {
 namespace {
 
-constexpr int BT = 64;    // chunk length
-constexpr int D = 128;    // d_k = d_v
-constexpr int NS = 64;    // d_v columns per workgroup
-constexpr int PQ = D + 8; // LDS pitch (elements) of [*][128] bf16 tiles
-constexpr int PT = BT + 8;// LDS pitch of [*][64] bf16 tiles
-constexpr int PY = 40;    // LDS pitch of the [*][32] temporaries
-constexpr int PA = 17;    // fp32 pitch of the diagonal blocks of A
+constexpr int BT = 64;     // chunk length
+constexpr int D = 128;     // d_k = d_v
+constexpr int PQ = D + 8;  // LDS pitch (elements) of [*][128] bf16 tiles
+constexpr int PT = BT + 8; // LDS pitch of [*][64] bf16 tiles
+constexpr int PY = 40;     // LDS pitch of the [*][32] temporaries
+constexpr int PA = 20;     // fp32 pitch of the transposed diagonal blocks of A
+constexpr int PS = D + 4;  // fp32 pitch of the staged state
 
 struct alignas(16) Smem {
   uint16_t q[BT * PQ];        // Q rows [t][d]
-  uint16_t k[BT * PQ];        // K rows [t][d]
-  uint16_t kt[D * PT];        // K^T [d][t]
-  uint16_t vt[NS * PT];       // V^T slice [n][t]
-  uint16_t st[NS * PQ];       // S^T slice [n][d] (bf16 operand copy of the state)
-  uint16_t p[BT * PT];        // M o Q K^T [t][j]
-  uint16_t t1[BT * PT];       // T diag(b Gamma) [t][j]
-  uint16_t t2[BT * PT];       // T diag(b) [t][j]
   union {
-    uint16_t ab[BT * PT];     // A, off-diagonal blocks, bf16 [t][j] (T solve)
-    uint16_t ut[NS * PT];     // U^T [n][t] (state pass)
-  } u;
-  uint16_t tr[BT * PT];       // T bf16 [t][j]; its upper blocks stay zero
-  uint16_t upt[NS * PT];      // (diag(e^{gamma_c-gamma}) U)^T [n][t]
-  uint16_t tt[BT * PT];       // T^T bf16 [j][t]
+    uint16_t k[BT * PQ];      // K rows [t][d] (Gram products)
+    uint16_t w[BT * PQ];      // -W rows [t][d] (state pass)
+  } kw;
+  union {
+    struct {
+      uint16_t kt[D * PT];    // K^T [d][t]
+      uint16_t vt[D * PT];    // (diag(b) V)^T [n][t]
+      uint16_t p[BT * PT];    // P = M o Q K^T [t][j]; blocks above the diagonal stay zero
+      uint16_t t1[BT * PT];   // T diag(b Gamma) [t][j]; blocks above the diagonal stay zero
+      uint16_t tr[BT * PT];   // T [t][j]
+      uint16_t tt[BT * PT];   // T^T [j][t]
+    };
+    float sst[D * PS];        // the fp32 state [d][n], staged at the start and the end
+  };
+  uint16_t ab[BT * PT];       // A, off-diagonal blocks [t][j]
   uint16_t yt[BT * PY];       // transposed temporaries of the block products
-  float af[4 * 16 * PA];      // diagonal blocks of A, fp32
+  float at[4 * 16 * PA];      // diagonal blocks of A, fp32, transposed: [block][j][t]
   float gam[BT];              // running sum of g inside the chunk
   float beta[BT];
 };
@@ -67,381 +76,434 @@ __device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-__device__ __forceinline__ bf16x8 lds8(const uint16_t* p) {
-  return *reinterpret_cast<const bf16x8*>(p);
-}
+__device__ __forceinline__ bf16x8 lds8(const uint16_t* p) { return *reinterpret_cast<const bf16x8*>(p); }
 
-// 4 + 4 values from two 8-byte halves (the permuted k order).
-__device__ __forceinline__ bf16x8 lds4x2(const uint16_t* p0, const uint16_t* p1) {
-  bf16x4 lo = *reinterpret_cast<const bf16x4*>(p0);
-  bf16x4 hi = *reinterpret_cast<const bf16x4*>(p1);
+// permuted k: 4 values at p, 4 values at p + 16
+__device__ __forceinline__ bf16x8 ldsp(const uint16_t* p) {
+  bf16x4 lo = *reinterpret_cast<const bf16x4*>(p);
+  bf16x4 hi = *reinterpret_cast<const bf16x4*>(p + 16);
   return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
-// k values 8*grp..8*grp+7 of a 16-deep product padded to 32 (groups 2, 3 give zero).
+// k values 8*grp..8*grp+7 of a 16-deep product padded to 32 (groups 2, 3 give zero)
 __device__ __forceinline__ bf16x8 lds8_k16(const uint16_t* p, int grp) {
-  if (grp < 2) return lds8(p);
   bf16x8 z = {};
-  return z;
+  return grp < 2 ? lds8(p) : z;
 }
 
-__device__ __forceinline__ uint16_t bfbits(float f) { return f32_to_bf16_bits(f); }
+__device__ __forceinline__ uint16_t bfb(float f) { return f32_to_bf16_bits(f); }
 
 __device__ __forceinline__ void st4bf(uint16_t* p, float a, float b, float c, float d) {
-  uint2 u;
-  u.x = (uint32_t)bfbits(a) | ((uint32_t)bfbits(b) << 16);
-  u.y = (uint32_t)bfbits(c) | ((uint32_t)bfbits(d) << 16);
-  *reinterpret_cast<uint2*>(p) = u;
+  *reinterpret_cast<uint2*>(p) = make_uint2(pack_bf16x2(a, b), pack_bf16x2(c, d));
 }
 
-__device__ __forceinline__ __bf16 tobf(float f) {
-  uint16_t b = bfbits(f);
-  return __builtin_bit_cast(__bf16, b);
+// two accumulator tiles (rows 4grp+i of 16-row blocks 2kk and 2kk+1) as one
+// permuted operand over those 32 rows
+__device__ __forceinline__ bf16x8 pair_operand(f32x4 lo, f32x4 hi) {
+  bf16x8 v;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[i] = (__bf16)lo[i];
+    v[4 + i] = (__bf16)hi[i];
+  }
+  return v;
 }
 
-__global__ __launch_bounds__(256) void chunk_scan_kernel(ScanArgs a) {
+struct Prefetch {
+  u32x4 k[2], v[2], q[2];  // row t = tid & 63, columns [8c8, 8c8+8), c8 = (tid >> 6) + 8 it
+  float g, b;              // g and beta of row t
+};
+
+// Loads the nv rows of a chunk starting at packed row rbase; buffer ranges end
+// at row nv, so rows past the end read as zero.
+__device__ __forceinline__ void prefetch(Prefetch& p, const ScanArgs& a, int64_t rbase, int nv, int m,
+                                         int qoff, int koff, int voff, int tid) {
+  const int C = a.channels, Hv = a.num_v_heads;
+  const __amdgpu_buffer_rsrc_t ry =
+      make_rsrc(reinterpret_cast<const uint16_t*>(a.y) + rbase * C, (uint32_t)nv * C * 2);
+  const __amdgpu_buffer_rsrc_t rg = make_rsrc(a.g + rbase * Hv, (uint32_t)nv * Hv * 4);
+  const __amdgpu_buffer_rsrc_t rb = make_rsrc(a.beta + rbase * Hv, (uint32_t)nv * Hv * 4);
+  const int t = tid & 63, wv = tid >> 6;
+  const int row = t * C;
+#pragma unroll
+  for (int it = 0; it < 2; ++it) {
+    const int c8 = wv + 8 * it;
+    p.k[it] = __builtin_amdgcn_raw_buffer_load_b128(ry, 2 * (row + koff + 8 * c8), 0, 0);
+    p.v[it] = __builtin_amdgcn_raw_buffer_load_b128(ry, 2 * (row + voff + 8 * c8), 0, 0);
+    p.q[it] = __builtin_amdgcn_raw_buffer_load_b128(ry, 2 * (row + qoff + 8 * c8), 0, 0);
+  }
+  p.g = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rg, 4 * (t * Hv + m), 0, 0));
+  p.b = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rb, 4 * (t * Hv + m), 0, 0));
+}
+
+// Output rows [row0, row0 + nv) of the wave's 16 columns: lane holds rows
+// 16tb + 4lg + i as packed bf16 pairs.  The buffer range ends at row nv, so the
+// stores of rows past the end are dropped.
+__device__ __forceinline__ void store_out(const ScanArgs& a, const uint32_t (&opk)[8], int64_t row0, int nv, int m,
+                                          int n0, int li, int lg) {
+  const int Hv = a.num_v_heads;
+  const __amdgpu_buffer_rsrc_t ro =
+      make_rsrc(reinterpret_cast<uint16_t*>(a.out) + row0 * Hv * D, (uint32_t)nv * Hv * D * 2);
+  const int obase = m * D + n0 + li + 4 * lg * Hv * D;
+#pragma unroll
+  for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t w = opk[2 * tb + (i >> 1)];
+      __builtin_amdgcn_raw_buffer_store_b16((uint16_t)((i & 1) ? (w >> 16) : (w & 0xffff)), ro,
+                                            2 * (obase + (16 * tb + i) * Hv * D), 0, 0);
+    }
+}
+
+// lower 16x16 block pair number e (0..9) in row order: (0,0) (1,0) (1,1) (2,0) ...
+__device__ __forceinline__ void lower_pair(int e, int& bi, int& bj) {
+  bi = e >= 6 ? 3 : e >= 3 ? 2 : e >= 1 ? 1 : 0;
+  bj = e - (bi * (bi + 1)) / 2;
+}
+
+__global__ __launch_bounds__(512) void chunk_scan_kernel(ScanArgs a, SeqOrder ord) {
   __shared__ Smem sm;
-  constexpr int NSL = D / NS;
-  const int bid = blockIdx.x;
-  const int slice = bid % NSL;
-  const int m = (bid / NSL) % a.num_v_heads;
-  const int s = bid / (NSL * a.num_v_heads);
+  const int Hv = a.num_v_heads;
+  const int rank = blockIdx.x / Hv;
+  const int m = blockIdx.x % Hv;
+  const int s = ord.n > 0 ? (rank < ord.n ? (int)ord.seq[rank] : a.num_seqs) : rank;
   if (s >= a.num_seqs) return;
   const int r0 = a.cu[s];
   const int L = a.cu[s + 1] - r0;
   if (L < a.min_len || L > a.max_len) return;
   if (!seq_active(a.read_idx, a.write_idx, s, a.num_blocks)) return;
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int li = lane & 15, lg = lane >> 4;
-  const int h = m / (a.num_v_heads / a.num_k_heads);
-  const int n0 = slice * NS;
-  const int64_t C = a.channels;
-  const int64_t qoff = (int64_t)h * D, koff = (int64_t)a.num_k_heads * D + h * D;
-  const int64_t voff = 2 * (int64_t)a.num_k_heads * D + (int64_t)m * D + n0;
+  const int h = m / (Hv / a.num_k_heads);
+  const int qoff = h * D, koff = a.num_k_heads * D + h * D;
+  const int voff = 2 * a.num_k_heads * D + m * D;
   const int64_t head_off = (int64_t)m * D * D;
-  const uint16_t* Y = reinterpret_cast<const uint16_t*>(a.y);
-  uint16_t* OUT = reinterpret_cast<uint16_t*>(a.out);
+  const int n0 = 16 * wv;  // this wave's state / output columns
 
-  // blocks above the diagonal of T, T diag(.) and P stay zero for the whole run
-  for (int i = tid; i < BT * PT; i += 256) {
-    sm.t1[i] = 0; sm.t2[i] = 0; sm.p[i] = 0; sm.tt[i] = 0;
-    sm.tr[i] = 0;
-  }
-
-  // state slice: wave w holds rows d in [32w, 32w+32) as two 16-row blocks
-  f32x4 sacc[2][4];
+  // S[:, n0 .. n0+16): sacc[db] holds rows d = 16 db + 4 lg + i of column n0 + li.
+  // Read with coalesced 16-byte loads, staged through LDS.
+  f32x4 sacc[8];
   {
-    const float* S0 = reinterpret_cast<const float*>(
-        reinterpret_cast<const char*>(a.ssm_pool) + (int64_t)a.read_idx[s] * a.ssm_stride) + head_off;
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(
+        reinterpret_cast<const float*>(reinterpret_cast<const char*>(a.ssm_pool) +
+                                       (int64_t)a.read_idx[s] * a.ssm_stride) + head_off, D * D * 4);
 #pragma unroll
-    for (int db = 0; db < 2; ++db)
+    for (int it = 0; it < 8; ++it) {
+      const int f = tid + 512 * it, row = f >> 5, c4 = f & 31;
+      const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rs, 16 * f, 0, 0);
+      *reinterpret_cast<u32x4*>(&sm.sst[row * PS + 4 * c4]) = v;
+    }
+    lds_barrier();
 #pragma unroll
-      for (int cb = 0; cb < 4; ++cb)
+    for (int db = 0; db < 8; ++db)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int d = 32 * w + 16 * db + 4 * lg + i;
-          sacc[db][cb][i] = S0[(int64_t)d * D + n0 + 16 * cb + li];
-        }
+      for (int i = 0; i < 4; ++i) sacc[db][i] = sm.sst[(16 * db + 4 * lg + i) * PS + n0 + li];
+    lds_barrier();
   }
-#pragma unroll
-  for (int db = 0; db < 2; ++db)
-#pragma unroll
-    for (int cb = 0; cb < 4; ++cb)
-      st4bf(&sm.st[(16 * cb + li) * PQ + 32 * w + 16 * db + 4 * lg], sacc[db][cb][0], sacc[db][cb][1],
-            sacc[db][cb][2], sacc[db][cb][3]);
-  __syncthreads();
+  for (int i = tid; i < BT * PT; i += 512) {
+    sm.t1[i] = 0;
+    sm.p[i] = 0;
+  }
+
+  Prefetch pf;
+  prefetch(pf, a, r0, min(BT, L), m, qoff, koff, voff, tid);
+  // the previous chunk's output (rows 16tb + 4lg + i of the wave's columns,
+  // packed bf16 pairs); stored during the next chunk so that the stores are long
+  // complete when the loop top waits for the prefetched loads
+  uint32_t opk[8];
+  int64_t obase_row = 0;
+  int onv = 0;
 
   for (int c0 = 0; c0 < L; c0 += BT) {
     const int nv = min(BT, L - c0);
     const int64_t rbase = r0 + c0;
 
-    // ---- load Q, K (rows and K^T), V^T slice, g, beta; rows past the end are zero
+    // ---- stage this chunk from the prefetch registers, then prefetch the next one
+    {
+      const int t = lane;
 #pragma unroll
-    for (int it = 0; it < 4; ++it) {
-      const int t = (tid >> 4) + 16 * it, c8 = tid & 15;
-      uint4 qv = make_uint4(0, 0, 0, 0), kv = qv;
-      if (t < nv) {
-        qv = *reinterpret_cast<const uint4*>(Y + (rbase + t) * C + qoff + 8 * c8);
-        kv = *reinterpret_cast<const uint4*>(Y + (rbase + t) * C + koff + 8 * c8);
-      }
-      *reinterpret_cast<uint4*>(&sm.q[t * PQ + 8 * c8]) = qv;
-      *reinterpret_cast<uint4*>(&sm.k[t * PQ + 8 * c8]) = kv;
-      const uint32_t kw[4] = {kv.x, kv.y, kv.z, kv.w};
+      for (int it = 0; it < 2; ++it) {
+        const int c8 = wv + 8 * it;
+        *reinterpret_cast<u32x4*>(&sm.kw.k[t * PQ + 8 * c8]) = pf.k[it];
+        *reinterpret_cast<u32x4*>(&sm.q[t * PQ + 8 * c8]) = pf.q[it];
+        const uint32_t kw[4] = {pf.k[it][0], pf.k[it][1], pf.k[it][2], pf.k[it][3]};
+        const uint32_t vw[4] = {pf.v[it][0], pf.v[it][1], pf.v[it][2], pf.v[it][3]};
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        sm.kt[(8 * c8 + 2 * e) * PT + t] = (uint16_t)(kw[e] & 0xffff);
-        sm.kt[(8 * c8 + 2 * e + 1) * PT + t] = (uint16_t)(kw[e] >> 16);
-      }
-    }
-#pragma unroll
-    for (int it = 0; it < 2; ++it) {
-      const int t = (tid >> 3) + 32 * it, c8 = tid & 7;
-      uint4 vv = make_uint4(0, 0, 0, 0);
-      if (t < nv) vv = *reinterpret_cast<const uint4*>(Y + (rbase + t) * C + voff + 8 * c8);
-      const uint32_t vw[4] = {vv.x, vv.y, vv.z, vv.w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        sm.vt[(8 * c8 + 2 * e) * PT + t] = (uint16_t)(vw[e] & 0xffff);
-        sm.vt[(8 * c8 + 2 * e + 1) * PT + t] = (uint16_t)(vw[e] >> 16);
-      }
-    }
-    if (w == 0) {
-      float gv = 0.f, bv = 0.f;
-      if (lane < nv) {
-        gv = a.g[(rbase + lane) * a.num_v_heads + m];
-        bv = a.beta[(rbase + lane) * a.num_v_heads + m];
-      }
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const float o = __shfl_up(gv, off);
-        if (lane >= off) gv += o;
-      }
-      sm.gam[lane] = gv;
-      sm.beta[lane] = bv;
-    }
-    __syncthreads();
-
-    // ---- Gram products: K K^T -> A (lower blocks), Q K^T -> P (lower blocks)
-#pragma unroll
-    for (int e = w; e < 20; e += 4) {
-      const int pair = e % 10;
-      const int bi = pair == 0 ? 0 : pair < 3 ? 1 : pair < 6 ? 2 : 3;
-      const int bj = pair - (bi * (bi + 1)) / 2;
-      const bool isq = e >= 10;
-      const uint16_t* arow = (isq ? sm.q : sm.k) + (16 * bi + li) * PQ;
-      const uint16_t* brow = sm.k + (16 * bj + li) * PQ;
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk)
-        acc = mfma(lds8(arow + 32 * kk + 8 * lg), lds8(brow + 32 * kk + 8 * lg), acc);
-      const int j = 16 * bj + li;
-      const float gj = sm.gam[j];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int t = 16 * bi + 4 * lg + i;
-        const float gt = sm.gam[t];
-        if (isq) {
-          const float v = (j <= t) ? __expf(gt - gj) * acc[i] : 0.f;
-          sm.p[t * PT + j] = bfbits(v);
-        } else {
-          const float v = (j < t) ? sm.beta[t] * __expf(gt - gj) * acc[i] : 0.f;
-          if (bi == bj) sm.af[(bi * 16 + 4 * lg + i) * PA + li] = v;
-          else sm.u.ab[t * PT + j] = bfbits(v);
+        for (int e = 0; e < 4; ++e) {
+          sm.kt[(8 * c8 + 2 * e) * PT + t] = (uint16_t)(kw[e] & 0xffff);
+          sm.kt[(8 * c8 + 2 * e + 1) * PT + t] = (uint16_t)(kw[e] >> 16);
+          const uint32_t vv = pack_bf16x2(pf.b * __uint_as_float(vw[e] << 16),
+                                          pf.b * __uint_as_float(vw[e] & 0xffff0000u));
+          sm.vt[(8 * c8 + 2 * e) * PT + t] = (uint16_t)(vv & 0xffff);
+          sm.vt[(8 * c8 + 2 * e + 1) * PT + t] = (uint16_t)(vv >> 16);
         }
       }
-    }
-    __syncthreads();
-
-    // ---- T = (I + A)^-1, diagonal blocks: fp32 forward substitution, wave w -> block w
-    {
-      const int c = li;
-      const float* ab = &sm.af[(w * 16) * PA];
-      float tc[16];
+      if (wv == 0) {
+        float gv = pf.g;
 #pragma unroll
-      for (int t = 0; t < 16; ++t) {
-        float v = (t == c) ? 1.f : 0.f;
-#pragma unroll
-        for (int j = 0; j < t; ++j) v -= ab[t * PA + j] * tc[j];
-        tc[t] = v;
+        for (int off = 1; off < 64; off <<= 1) {
+          const float o = __shfl_up(gv, off);
+          if (lane >= off) gv += o;
+        }
+        sm.gam[lane] = gv;
+        sm.beta[lane] = pf.b;
       }
-      const int cg = 16 * w + c;
-      const float bc = sm.beta[cg];
-      const float bgc = bc * __expf(sm.gam[cg]);
+    }
+    if (c0 + BT < L) prefetch(pf, a, rbase + BT, min(BT, L - c0 - BT), m, qoff, koff, voff, tid);
+    lds_barrier();
+    if (c0 > 0) store_out(a, opk, obase_row, onv, m, n0, li, lg);
+
+    // ---- Gram products: 10 lower 16x16 blocks of K K^T (-> A) and 10 of Q K^T
+    //      (-> P), spread over the 8 waves
+    for (int e = wv; e < 20; e += 8) {
+      int bi, bj;
+      lower_pair(e % 10, bi, bj);
+      if (e < 10) {
+        // K K^T block (bi, bj): lane holds A[t = 16bi + 4lg + i][j = 16bj + li]
+        bf16x8 xa[4], yb[4];
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+          xa[kk] = ldsp(&sm.kw.k[(16 * bi + li) * PQ + 32 * kk + 4 * lg]);
+          yb[kk] = ldsp(&sm.kw.k[(16 * bj + li) * PQ + 32 * kk + 4 * lg]);
+        }
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) acc = mfma(xa[kk], yb[kk], acc);
+        const int j = 16 * bj + li;
+        const float gj = sm.gam[j];
+        float v[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int t = 16 * bi + 4 * lg + i;
+          v[i] = (j < t) ? sm.beta[t] * __expf(sm.gam[t] - gj) * acc[i] : 0.f;
+        }
+        if (bi == bj) {
+          *reinterpret_cast<float4*>(&sm.at[(16 * bi + li) * PA + 4 * lg]) = make_float4(v[0], v[1], v[2], v[3]);
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) sm.ab[(16 * bi + 4 * lg + i) * PT + j] = bfb(v[i]);
+        }
+      } else {
+        // (Q K^T)^T block: rows j of block bj, columns t of block bi; lane holds
+        // P[t = 16bi + li][j = 16bj + 4lg + i]
+        bf16x8 xa[4], yb[4];
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+          xa[kk] = ldsp(&sm.kw.k[(16 * bj + li) * PQ + 32 * kk + 4 * lg]);
+          yb[kk] = ldsp(&sm.q[(16 * bi + li) * PQ + 32 * kk + 4 * lg]);
+        }
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) acc = mfma(xa[kk], yb[kk], acc);
+        const int t = 16 * bi + li;
+        const float gt = sm.gam[t];
+        float v[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int j = 16 * bj + 4 * lg + i;
+          v[i] = (j <= t) ? __expf(gt - sm.gam[j]) * acc[i] : 0.f;
+        }
+        st4bf(&sm.p[t * PT + 16 * bj + 4 * lg], v[0], v[1], v[2], v[3]);
+      }
+    }
+    lds_barrier();
+
+    // ---- T = (I + A)^-1, diagonal blocks by column-oriented fp32 forward
+    //      substitution (waves 0..3, lane li = column); waves 4..7 clear the
+    //      blocks above the diagonal that later products read: T(0,1), T(2,3), T^T(1,0)
+    if (wv < 4) {
+      // lane (li = column c, lg) holds rows t = 4lg..4lg+3 of column c; step j
+      // broadcasts the finished x_j from its owner (lane li + 16 (j >> 2)) and
+      // every lane applies x_t -= A[t][j] x_j (A is zero on and above the diagonal)
+      const int rg = wv, c = li;
+      const float* ab = &sm.at[(16 * rg) * PA + 4 * lg];
+      f32x4 x;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) x[i] = (4 * lg + i == c) ? 1.f : 0.f;
+#pragma unroll
+      for (int j = 0; j < 15; ++j) {
+        const float xj = __shfl(x[j & 3], li + 16 * (j >> 2));
+        const f32x4 col = *reinterpret_cast<const f32x4*>(&ab[j * PA]);
+        x -= col * xj;
+      }
+      const int cg = 16 * rg + c;
+      const float bgc = sm.beta[cg] * __expf(sm.gam[cg]);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int tl = 4 * lg + i, tg = 16 * w + tl;
-        const float v = tc[tl];
-        sm.tr[tg * PT + cg] = bfbits(v);
-        sm.t1[tg * PT + cg] = bfbits(v * bgc);
-        sm.t2[tg * PT + cg] = bfbits(v * bc);
+        const int tg = 16 * rg + 4 * lg + i;
+        sm.tr[tg * PT + cg] = bfb(x[i]);
+        sm.t1[tg * PT + cg] = bfb(x[i] * bgc);
       }
-      st4bf(&sm.tt[cg * PT + 16 * w + 4 * lg], tc[4 * lg], tc[4 * lg + 1], tc[4 * lg + 2], tc[4 * lg + 3]);
+      st4bf(&sm.tt[cg * PT + 16 * rg + 4 * lg], x[0], x[1], x[2], x[3]);
+    } else {
+      const int rg = wv - 4, c = li;
+      if (rg == 0 || rg == 2)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sm.tr[(16 * rg + 4 * lg + i) * PT + 16 * rg + 16 + c] = 0;
+      if (rg == 1) st4bf(&sm.tt[(16 + c) * PT + 4 * lg], 0.f, 0.f, 0.f, 0.f);
     }
-    __syncthreads();
+    lds_barrier();
 
-    // ---- first-level blocks: T10 = -T11 A10 T00 (wave 0), T32 = -T33 A32 T22 (wave 1)
-    if (w < 2) {
-      const int rb = 16 * (2 * w + 1), cbk = 16 * (2 * w);  // row block, column block
-      f32x4 y = {0.f, 0.f, 0.f, 0.f};
-      y = mfma(lds8_k16(&sm.u.ab[(rb + li) * PT + cbk + 8 * lg], lg),
-               lds8_k16(&sm.tt[(cbk + li) * PT + cbk + 8 * lg], lg), y);
-      st4bf(&sm.yt[(16 * w + li) * PY + 4 * lg], y[0], y[1], y[2], y[3]);
-    }
-    __syncthreads();
-    if (w < 2) {
-      const int rb = 16 * (2 * w + 1), cbk = 16 * (2 * w);
-      f32x4 t = {0.f, 0.f, 0.f, 0.f};
-      t = mfma(lds8_k16(&sm.tr[(rb + li) * PT + rb + 8 * lg], lg),
-               lds8_k16(&sm.yt[(16 * w + li) * PY + 8 * lg], lg), t);
-      const int cg = cbk + li;
-      const float bc = sm.beta[cg];
-      const float bgc = bc * __expf(sm.gam[cg]);
+    // ---- first-level blocks in the wave that solved the row block:
+    //      wave 1: T10 = -T11 (A10 T00);  wave 3: T32 = -T33 (A32 T22)
+    if (wv == 1 || wv == 3) {
+      const int rb = 16 * wv, cb0 = 16 * (wv - 1);
+      uint16_t* y = &sm.yt[(16 * (wv >> 1)) * PY];
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      acc = mfma(lds8_k16(&sm.ab[(rb + li) * PT + cb0 + 8 * lg], lg),
+                 lds8_k16(&sm.tt[(cb0 + li) * PT + cb0 + 8 * lg], lg), acc);
+      st4bf(&y[li * PY + 4 * lg], acc[0], acc[1], acc[2], acc[3]);
+      f32x4 tacc = {0.f, 0.f, 0.f, 0.f};
+      tacc = mfma(lds8_k16(&sm.tr[(rb + li) * PT + rb + 8 * lg], lg), lds8_k16(&y[li * PY + 8 * lg], lg), tacc);
+      const int cg = cb0 + li;
+      const float bgc = sm.beta[cg] * __expf(sm.gam[cg]);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int tg = rb + 4 * lg + i;
-        const float v = -t[i];
-        sm.tr[tg * PT + cg] = bfbits(v);
-        sm.t1[tg * PT + cg] = bfbits(v * bgc);
-        sm.t2[tg * PT + cg] = bfbits(v * bc);
+        sm.tr[tg * PT + cg] = bfb(-tacc[i]);
+        sm.t1[tg * PT + cg] = bfb(-tacc[i] * bgc);
       }
-      st4bf(&sm.tt[cg * PT + rb + 4 * lg], -t[0], -t[1], -t[2], -t[3]);
+      st4bf(&sm.tt[cg * PT + rb + 4 * lg], -tacc[0], -tacc[1], -tacc[2], -tacc[3]);
     }
-    __syncthreads();
+    lds_barrier();
 
-    // ---- second level: T[32:64, 0:32] = -T_BB (A_BA T_AA), one 16x16 tile per wave
-    {
-      const int tr_ = 2 + (w >> 1), tc_ = w & 1;
-      f32x4 y = {0.f, 0.f, 0.f, 0.f};
-      y = mfma(lds8(&sm.u.ab[(16 * tr_ + li) * PT + 8 * lg]),
-               lds8(&sm.tt[(16 * tc_ + li) * PT + 8 * lg]), y);
-      st4bf(&sm.yt[(32 + 16 * tc_ + li) * PY + 16 * (tr_ - 2) + 4 * lg], y[0], y[1], y[2], y[3]);
-    }
-    __syncthreads();
-    {
-      const int tr_ = 2 + (w >> 1), tc_ = w & 1;
-      f32x4 t = {0.f, 0.f, 0.f, 0.f};
-      t = mfma(lds8(&sm.tr[(16 * tr_ + li) * PT + 32 + 8 * lg]),
-               lds8(&sm.yt[(32 + 16 * tc_ + li) * PY + 8 * lg]), t);
-      const int cg = 16 * tc_ + li;
-      const float bc = sm.beta[cg];
-      const float bgc = bc * __expf(sm.gam[cg]);
+    // ---- second level: T[32:64, 16c:16c+16] = -T_BB (A_BA T_AA)[:, 16c:16c+16],
+    //      one 16-column block c per wave 0..1, both row blocks
+    if (wv < 2) {
+      const int cb0 = 16 * wv;
+      uint16_t* y = &sm.yt[(32 + 16 * wv) * PY];
+      const bf16x8 tb = lds8(&sm.tt[(cb0 + li) * PT + 8 * lg]);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int tg = 16 * tr_ + 4 * lg + i;
-        sm.t1[tg * PT + cg] = bfbits(-t[i] * bgc);
-        sm.t2[tg * PT + cg] = bfbits(-t[i] * bc);
+      for (int hb = 0; hb < 2; ++hb) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        acc = mfma(lds8(&sm.ab[(32 + 16 * hb + li) * PT + 8 * lg]), tb, acc);
+        st4bf(&y[li * PY + 16 * hb + 4 * lg], acc[0], acc[1], acc[2], acc[3]);
+      }
+      const int cg = cb0 + li;
+      const float bgc = sm.beta[cg] * __expf(sm.gam[cg]);
+      const bf16x8 yb = lds8(&y[li * PY + 8 * lg]);
+#pragma unroll
+      for (int hb = 0; hb < 2; ++hb) {
+        f32x4 tacc = {0.f, 0.f, 0.f, 0.f};
+        tacc = mfma(lds8(&sm.tr[(32 + 16 * hb + li) * PT + 32 + 8 * lg]), yb, tacc);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int tg = 32 + 16 * hb + 4 * lg + i;
+          sm.tr[tg * PT + cg] = bfb(-tacc[i]);
+          sm.t1[tg * PT + cg] = bfb(-tacc[i] * bgc);
+        }
       }
     }
-    __syncthreads();
+    lds_barrier();
 
-    // ---- W^T = K^T (T diag(b Gamma))^T for rows t of block w, kept as A operands;
-    //      U~ = T diag(b) V for rows t of block w, in the U accumulators
-    bf16x8 wa[4];
+    // ---- -W = -(T diag(b Gamma)) K into LDS (wave w: d block w, all chunk rows),
+    //      and U~ = T (diag(b) V) for the wave's columns in the U accumulators
     f32x4 uacc[4];
     {
-      f32x4 wacc[8];
 #pragma unroll
-      for (int db = 0; db < 8; ++db) wacc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
-      const int nk = (w < 2) ? 1 : 2;
-      for (int kk = 0; kk < nk; ++kk) {
-        const bf16x8 bt = lds8(&sm.t1[(16 * w + li) * PT + 32 * kk + 8 * lg]);
+      for (int tb = 0; tb < 4; ++tb) {
+        const int nk = tb < 2 ? 1 : 2;
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        uacc[tb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int db = 0; db < 8; ++db)
-          wacc[db] = mfma(lds8(&sm.kt[(16 * db + li) * PT + 32 * kk + 8 * lg]), bt, wacc[db]);
+        for (int kk = 0; kk < nk; ++kk) {
+          const bf16x8 ka = lds8(&sm.kt[(16 * wv + li) * PT + 32 * kk + 8 * lg]);
+          const bf16x8 bt = lds8(&sm.t1[(16 * tb + li) * PT + 32 * kk + 8 * lg]);
+          const bf16x8 at = lds8(&sm.tr[(16 * tb + li) * PT + 32 * kk + 8 * lg]);
+          const bf16x8 vb = lds8(&sm.vt[(n0 + li) * PT + 32 * kk + 8 * lg]);
+          acc = mfma(ka, bt, acc);
+          uacc[tb] = mfma(at, vb, uacc[tb]);
+        }
+        // lane holds W[t = 16tb + li][d = 16w + 4lg + i]
+        st4bf(&sm.kw.w[(16 * tb + li) * PQ + 16 * wv + 4 * lg], -acc[0], -acc[1], -acc[2], -acc[3]);
       }
+    }
+    lds_barrier();
+
+    // ---- state pass for the wave's 16 columns, in registers
+    {
+      bf16x8 sb[4];
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        bf16x8 v;
+      for (int kk = 0; kk < 4; ++kk) sb[kk] = pair_operand(sacc[2 * kk], sacc[2 * kk + 1]);
+      f32x4 oacc[4];
+#pragma unroll
+      for (int tb = 0; tb < 4; ++tb) {
+        oacc[tb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        bf16x8 wa[4], qa[4];
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+          wa[kk] = ldsp(&sm.kw.w[(16 * tb + li) * PQ + 32 * kk + 4 * lg]);
+          qa[kk] = ldsp(&sm.q[(16 * tb + li) * PQ + 32 * kk + 4 * lg]);
+        }
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+          uacc[tb] = mfma(wa[kk], sb[kk], uacc[tb]);   // U = U~ - W S
+          oacc[tb] = mfma(qa[kk], sb[kk], oacc[tb]);   // Q S
+        }
+      }
+      const float glast = sm.gam[BT - 1];
+      bf16x8 ub[2], upb[2];
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        ub[kk] = pair_operand(uacc[2 * kk], uacc[2 * kk + 1]);
+        f32x4 lo, hi;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          v[i] = tobf(-wacc[2 * kk][i]);
-          v[4 + i] = tobf(-wacc[2 * kk + 1][i]);
+          const float g0 = sm.gam[32 * kk + 4 * lg + i], g1 = sm.gam[32 * kk + 16 + 4 * lg + i];
+          lo[i] = uacc[2 * kk][i] * __expf(glast - g0);
+          hi[i] = uacc[2 * kk + 1][i] * __expf(glast - g1);
+          oacc[2 * kk][i] *= __expf(g0);
+          oacc[2 * kk + 1][i] *= __expf(g1);
         }
-        wa[kk] = v;
+        upb[kk] = pair_operand(lo, hi);
       }
+      // O += P U
 #pragma unroll
-      for (int cb = 0; cb < 4; ++cb) uacc[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
-      for (int kk = 0; kk < nk; ++kk) {
-        const bf16x8 at = lds8(&sm.t2[(16 * w + li) * PT + 32 * kk + 8 * lg]);
+      for (int tb = 0; tb < 4; ++tb) {
+        const int nk = tb < 2 ? 1 : 2;
 #pragma unroll
-        for (int cb = 0; cb < 4; ++cb)
-          uacc[cb] = mfma(at, lds8(&sm.vt[(16 * cb + li) * PT + 32 * kk + 8 * lg]), uacc[cb]);
+        for (int kk = 0; kk < nk; ++kk)
+          oacc[tb] = mfma(ldsp(&sm.p[(16 * tb + li) * PT + 32 * kk + 4 * lg]), ub[kk], oacc[tb]);
       }
-    }
-
-    // ---- U = U~ - W S  and  Q S  (rows t of block w, all 64 columns of the slice)
-    f32x4 oacc[4];
-#pragma unroll
-    for (int cb = 0; cb < 4; ++cb) oacc[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      const uint16_t* qrow = &sm.q[(16 * w + li) * PQ + 32 * kk + 4 * lg];
-      const bf16x8 qa = lds4x2(qrow, qrow + 16);
-#pragma unroll
-      for (int cb = 0; cb < 4; ++cb) {
-        const uint16_t* srow = &sm.st[(16 * cb + li) * PQ + 32 * kk + 4 * lg];
-        const bf16x8 bs = lds4x2(srow, srow + 16);
-        uacc[cb] = mfma(wa[kk], bs, uacc[cb]);
-        oacc[cb] = mfma(qa, bs, oacc[cb]);
-      }
-    }
-    const float glast = sm.gam[BT - 1];
-#pragma unroll
-    for (int cb = 0; cb < 4; ++cb) {
-      float dec[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int t = 16 * w + 4 * lg + i;
-        const float gt = sm.gam[t];
-        dec[i] = __expf(glast - gt);
-        oacc[cb][i] *= __expf(gt);
-      }
-      uint16_t* ut = &sm.u.ut[(16 * cb + li) * PT + 16 * w + 4 * lg];
-      st4bf(ut, uacc[cb][0], uacc[cb][1], uacc[cb][2], uacc[cb][3]);
-      uint16_t* upt = &sm.upt[(16 * cb + li) * PT + 16 * w + 4 * lg];
-      st4bf(upt, uacc[cb][0] * dec[0], uacc[cb][1] * dec[1], uacc[cb][2] * dec[2], uacc[cb][3] * dec[3]);
-    }
-    __syncthreads();
-
-    // ---- O += P U ; write the chunk's output rows
-    {
-      const int nk = (w < 2) ? 1 : 2;
-      for (int kk = 0; kk < nk; ++kk) {
-        const bf16x8 pa = lds8(&sm.p[(16 * w + li) * PT + 32 * kk + 8 * lg]);
-#pragma unroll
-        for (int cb = 0; cb < 4; ++cb)
-          oacc[cb] = mfma(pa, lds8(&sm.u.ut[(16 * cb + li) * PT + 32 * kk + 8 * lg]), oacc[cb]);
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int t = 16 * w + 4 * lg + i;
-        if (t < nv) {
-          uint16_t* orow = OUT + ((rbase + t) * a.num_v_heads + m) * D + n0 + li;
-#pragma unroll
-          for (int cb = 0; cb < 4; ++cb) orow[16 * cb] = bfbits(oacc[cb][i]);
-        }
-      }
-    }
-
-    // ---- S <- Gamma_c S + K^T U'
-    {
+      // S <- Gamma_c S + K^T U'
       const float gc = __expf(glast);
 #pragma unroll
-      for (int db = 0; db < 2; ++db)
+      for (int db = 0; db < 8; ++db) {
+        sacc[db] *= gc;
+        bf16x8 ka[2];
 #pragma unroll
-        for (int cb = 0; cb < 4; ++cb) sacc[db][cb] *= gc;
+        for (int kk = 0; kk < 2; ++kk) ka[kk] = ldsp(&sm.kt[(16 * db + li) * PT + 32 * kk + 4 * lg]);
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk)
+        for (int kk = 0; kk < 2; ++kk) sacc[db] = mfma(ka[kk], upb[kk], sacc[db]);
+      }
 #pragma unroll
-        for (int db = 0; db < 2; ++db) {
-          const bf16x8 ka = lds8(&sm.kt[(32 * w + 16 * db + li) * PT + 32 * kk + 8 * lg]);
-#pragma unroll
-          for (int cb = 0; cb < 4; ++cb)
-            sacc[db][cb] = mfma(ka, lds8(&sm.upt[(16 * cb + li) * PT + 32 * kk + 8 * lg]), sacc[db][cb]);
-        }
-#pragma unroll
-      for (int db = 0; db < 2; ++db)
-#pragma unroll
-        for (int cb = 0; cb < 4; ++cb)
-          st4bf(&sm.st[(16 * cb + li) * PQ + 32 * w + 16 * db + 4 * lg], sacc[db][cb][0], sacc[db][cb][1],
-                sacc[db][cb][2], sacc[db][cb][3]);
+      for (int tb = 0; tb < 4; ++tb) {
+        opk[2 * tb] = pack_bf16x2(oacc[tb][0], oacc[tb][1]);
+        opk[2 * tb + 1] = pack_bf16x2(oacc[tb][2], oacc[tb][3]);
+      }
+      obase_row = rbase;
+      onv = nv;
     }
-    __syncthreads();
+    lds_barrier();
   }
 
+  store_out(a, opk, obase_row, onv, m, n0, li, lg);
   {
-    float* S1 = reinterpret_cast<float*>(
-        reinterpret_cast<char*>(a.ssm_pool) + (int64_t)a.write_idx[s] * a.ssm_stride) + head_off;
 #pragma unroll
-    for (int db = 0; db < 2; ++db)
+    for (int db = 0; db < 8; ++db)
 #pragma unroll
-      for (int cb = 0; cb < 4; ++cb)
+      for (int i = 0; i < 4; ++i) sm.sst[(16 * db + 4 * lg + i) * PS + n0 + li] = sacc[db][i];
+    lds_barrier();
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(
+        reinterpret_cast<float*>(reinterpret_cast<char*>(a.ssm_pool) + (int64_t)a.write_idx[s] * a.ssm_stride) +
+            head_off, D * D * 4);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int d = 32 * w + 16 * db + 4 * lg + i;
-          S1[(int64_t)d * D + n0 + 16 * cb + li] = sacc[db][cb][i];
-        }
+    for (int it = 0; it < 8; ++it) {
+      const int f = tid + 512 * it, row = f >> 5, c4 = f & 31;
+      __builtin_amdgcn_raw_buffer_store_b128(*reinterpret_cast<const u32x4*>(&sm.sst[row * PS + 4 * c4]), rs,
+                                             16 * f, 0, 0);
+    }
   }
 }
 
@@ -449,10 +511,11 @@ __global__ __launch_bounds__(256) void chunk_scan_kernel(ScanArgs a) {
 
 bool chunk_supported(int dk, int dv) { return dk == D && dv == D; }
 
-hipError_t launch_chunk(const ScanArgs& a, int dk, int dv, hipStream_t st) {
+hipError_t launch_chunk(const ScanArgs& a, const SeqOrder& order, int dk, int dv, hipStream_t st) {
   if (!chunk_supported(dk, dv)) return hipErrorInvalidValue;
-  dim3 grid(a.num_seqs * a.num_v_heads * (D / NS));
-  hipLaunchKernelGGL(chunk_scan_kernel, grid, dim3(256), 0, st, a);
+  const int rows = order.n > 0 ? order.n : a.num_seqs;
+  dim3 grid(rows * a.num_v_heads);
+  hipLaunchKernelGGL(chunk_scan_kernel, grid, dim3(512), 0, st, a, order);
   return hipGetLastError();
 }
 

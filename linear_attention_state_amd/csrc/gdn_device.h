@@ -11,16 +11,45 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
+// Global-memory pointers in address space 1: loads and stores through them
+// are global (not flat) instructions, so they are counted by vmcnt only and an
+// LDS wait never waits for them.
+template <class T>
+using gptr = __attribute__((address_space(1))) T*;
+template <class T>
+__device__ __forceinline__ gptr<T> as_global(T* p) {
+  return (gptr<T>)(p);
+}
+
+// Buffer resource (V#) over `bytes` bytes from `base`: raw buffer loads past
+// the end return zero and raw buffer stores past the end are dropped, which
+// bounds every access by hardware.  Offsets are 32-bit byte offsets.
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
 __device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {
   return __uint_as_float((uint32_t)b << 16);
 }
 
-// Round-to-nearest-even fp32 -> bf16 bits (NaN kept quiet).
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// fp32 -> bf16 bits, round to nearest even (v_cvt_pk_bf16_f32 on gfx950).
 __device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
+  return __builtin_bit_cast(uint16_t, (__bf16)f);
+}
+
+// Two fp32 -> two bf16 packed in one dword (first in the low half).
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  bf16x2 v = {(__bf16)a, (__bf16)b};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// Workgroup barrier that only waits for this wave's LDS traffic: outstanding
+// global loads (prefetches) and stores stay in flight across it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
 __device__ __forceinline__ float silu(float v) { return v / (1.0f + __expf(-v)); }
@@ -86,10 +115,17 @@ struct ScanArgs {
   int min_len, max_len;  // only sequences with min_len <= L <= max_len
 };
 
+// Sequences of the chunked launch, longest first (one workgroup row per entry).
+constexpr int kMaxOrder = 1024;
+struct SeqOrder {
+  int32_t n;                    // entries used; 0 means "every sequence, in index order"
+  uint16_t seq[kMaxOrder];
+};
+
 hipError_t launch_conv(const ConvArgs& a, int width, bool bf16, hipStream_t st);
 hipError_t launch_tail_commit(const TailArgs& a, int width, bool bf16, hipStream_t st);
 hipError_t launch_recurrent(const ScanArgs& a, int dk, int dv, bool bf16, hipStream_t st);
-hipError_t launch_chunk(const ScanArgs& a, int dk, int dv, hipStream_t st);
+hipError_t launch_chunk(const ScanArgs& a, const SeqOrder& order, int dk, int dv, hipStream_t st);
 bool chunk_supported(int dk, int dv);
 
 }  // namespace gdn

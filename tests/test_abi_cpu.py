@@ -95,7 +95,9 @@ def _call(layer, cu_host, T, n=None, **over):
     ([0, 4], 4, {"conv": None}, gdn.GDN_EINVAL, "conv_pool"),
     ([0, 4], 4, {"P": 1}, gdn.GDN_EINVAL, "num_blocks"),
     ([0, 4], 4, {"sstride": (2 << 20) - 128}, gdn.GDN_EINVAL, "ssm_block_stride"),
-    ([0, 4], 4, {"cstride": 3 * 8192 * 2 + 64}, gdn.GDN_EINVAL, "conv_block_stride"),
+    ([0, 4], 4, {"sstride": (2 << 20) + 8}, gdn.GDN_EINVAL, "ssm_block_stride"),
+    ([0, 4], 4, {"cstride": 3 * 8192 * 2 - 16}, gdn.GDN_EINVAL, "conv_block_stride"),
+    ([0, 4], 4, {"cstride": 3 * 8192 * 2 + 4}, gdn.GDN_EINVAL, "conv_block_stride"),
     ([0, 4], 4, {"wsb": 100}, gdn.GDN_EWORKSPACE, "workspace"),
     ([0, 4], 4, {"ws": None}, gdn.GDN_EWORKSPACE, "workspace"),
     ([0, 4], 4, {"x": ctypes.c_void_p((1 << 20) + 8)}, gdn.GDN_EINVAL, "aligned"),
