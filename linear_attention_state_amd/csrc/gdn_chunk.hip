@@ -40,72 +40,84 @@
 namespace gdn {
 namespace {
 
-constexpr int BT = 64;     // chunk length
-constexpr int D = 128;     // d_k = d_v
-constexpr int PQ = D + 8;  // LDS pitch (elements) of [*][128] bf16 tiles
-constexpr int PT = BT + 8; // LDS pitch of [*][64] bf16 tiles
-constexpr int PY = 40;     // LDS pitch of the [*][32] temporaries
-constexpr int PA = 20;     // fp32 pitch of the transposed diagonal blocks of A
-constexpr int PS = D + 4;  // fp32 pitch of the staged state
+constexpr int BT = 64;            // chunk length
+constexpr int D = 128;            // d_k = d_v
+constexpr int NW = 4;             // waves per workgroup
+constexpr int NT = 64 * NW;       // threads per workgroup
+constexpr int NB = D / 16 / NW;   // 16-column state tiles per wave
+constexpr int PV = D + 16;        // pitch (elements) of the V rows
+constexpr int PW = D + 8;         // pitch of the -W rows
+constexpr int PP = BT + 8;        // pitch of the P rows
+constexpr int PX = BT + 16;       // pitch of the transposed 64 x 64 tiles
+constexpr int PA = 20;            // fp32 pitch of the transposed diagonal blocks of A
+constexpr int PS = D + 4;         // fp32 pitch of the staged state
+constexpr int PO = BT + 8;        // pitch of a wave's staged output tile [n][t]
 
+// LDS.  "k-permuted" rows store element d of each 32-wide group at
+// 8*((d>>2)&3) + 4*((d>>4)&1) + (d&3): the 8 values an operand lane needs
+// (k = 4g..4g+3 and 16+4g..16+4g+3 of the group) are then one 16-byte read.
 struct alignas(16) Smem {
-  uint16_t q[BT * PQ];        // Q rows [t][d]
-  union {
-    uint16_t k[BT * PQ];      // K rows [t][d] (Gram products)
-    uint16_t w[BT * PQ];      // -W rows [t][d] (state pass)
-  } kw;
   union {
     struct {
-      uint16_t kt[D * PT];    // K^T [d][t ^ swz(d)]
-      uint16_t vt[D * PT];    // (diag(b) V)^T [n][t ^ swz(n)]
-      uint16_t p[BT * PT];    // P = M o Q K^T [t][j]; blocks above the diagonal stay zero
-      uint16_t t1[BT * PT];   // T diag(b Gamma) [t][j]; blocks above the diagonal stay zero
-      uint16_t tr[BT * PT];   // T [t][j]
-      uint16_t tt[BT * PT];   // T^T [j][t]
+      uint16_t q[BT * D];     // Q rows [t][perm d], 16-byte chunks XOR-swizzled by row
+      uint16_t k[BT * D];     // K rows, same layout
+      uint16_t v[BT * PV];    // V rows [j][n]; after the W phase, each wave's output tile
+      uint16_t w[BT * PW];    // -W rows [t][perm d]
     };
     float sst[D * PS];        // the fp32 state [d][n], staged at the start and the end
   };
-  uint16_t ab[BT * PT];       // A, off-diagonal blocks [t][j]
-  uint16_t yt[BT * PY];       // transposed temporaries of the block products
-  float at[4 * 16 * PA];      // diagonal blocks of A, fp32, transposed: [block][j][t]
+  uint16_t p[BT * PP];        // P = M o Q K^T, [t][perm j]; blocks above the diagonal stay zero
+  uint16_t tt[BT * PX];       // T^T [j][t]; blocks above the diagonal of T stay zero
+  uint16_t t1t[BT * PX];      // (T diag(b Gamma))^T
+  uint16_t t2t[BT * PX];      // (T diag(b))^T
+  uint16_t abt[BT * PX];      // A^T, blocks below the diagonal
+  float at[4 * 16 * PA];      // diagonal blocks of A, fp32, [block][j][t]
   float gam[BT];              // running sum of g inside the chunk
+  float eg[BT];               // e^gamma
+  float ed[BT];               // e^(gamma_last - gamma)
   float beta[BT];
+  float bg[BT];               // beta e^gamma
 };
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 __device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
+__device__ __forceinline__ f32x4 mfma16(bf16x4 a, bf16x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
 
 __device__ __forceinline__ bf16x8 lds8(const uint16_t* p) { return *reinterpret_cast<const bf16x8*>(p); }
-
-// permuted k: 4 values at p, 4 values at p + 16
-__device__ __forceinline__ bf16x8 ldsp(const uint16_t* p) {
-  bf16x4 lo = *reinterpret_cast<const bf16x4*>(p);
-  bf16x4 hi = *reinterpret_cast<const bf16x4*>(p + 16);
+__device__ __forceinline__ bf16x4 lds4(const uint16_t* p) { return *reinterpret_cast<const bf16x4*>(p); }
+__device__ __forceinline__ bf16x8 cat(bf16x4 lo, bf16x4 hi) {
   return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
-// permuted k from two separate 4-value halves
-__device__ __forceinline__ bf16x8 ldsp2(const uint16_t* lo_p, const uint16_t* hi_p) {
-  bf16x4 lo = *reinterpret_cast<const bf16x4*>(lo_p);
-  bf16x4 hi = *reinterpret_cast<const bf16x4*>(hi_p);
-  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-}
-
-// k values 8*grp..8*grp+7 of a 16-deep product padded to 32 (groups 2, 3 give zero)
-__device__ __forceinline__ bf16x8 lds8_k16(const uint16_t* p, int grp) {
-  bf16x8 z = {};
-  return grp < 2 ? lds8(p) : z;
+// ds_read_b64_tr_b16.  Within each 16-lane group g, every lane reads 4
+// consecutive 16-bit values at its own address; lane 16g + 4a + b then
+// receives value b of lanes 16g + a, 16g + a + 4, 16g + a + 8, 16g + a + 12.
+// When lane 16g + a + 4i points at row (base + i), columns c0 + 4a .. c0 + 4a + 3
+// of a row-major tile, lane 16g + n receives column c0 + n of rows base..base+3:
+// a transposed operand read straight from row-major storage.
+__device__ __forceinline__ bf16x4 ldtr(const uint16_t* p) {
+  return __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(const_cast<uint16_t*>(p))));
 }
 
 __device__ __forceinline__ uint16_t bfb(float f) { return f32_to_bf16_bits(f); }
-
 __device__ __forceinline__ void st4bf(uint16_t* p, float a, float b, float c, float d) {
   *reinterpret_cast<uint2*>(p) = make_uint2(pack_bf16x2(a, b), pack_bf16x2(c, d));
 }
+__device__ __forceinline__ bf16x4 to_bf16x4(f32x4 v) {
+  bf16x4 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) r[i] = (__bf16)v[i];
+  return r;
+}
 
-// two accumulator tiles (rows 4grp+i of 16-row blocks 2kk and 2kk+1) as one
-// permuted operand over those 32 rows
+// two accumulator tiles (rows 4g+i of 16-row blocks 2kk and 2kk+1) as one
+// k-permuted operand over those 32 rows
 __device__ __forceinline__ bf16x8 pair_operand(f32x4 lo, f32x4 hi) {
   bf16x8 v;
 #pragma unroll
@@ -116,19 +128,49 @@ __device__ __forceinline__ bf16x8 pair_operand(f32x4 lo, f32x4 hi) {
   return v;
 }
 
-// K^T and V^T rows are stored with their token index XOR-swizzled by a
-// multiple of 8 that depends on the row (d >> 3): the transposed stores of
-// 16 lanes holding different 8-row groups then hit different banks, and
-// every aligned group of 4 or 8 tokens stays contiguous for the operand reads.
-__device__ __forceinline__ int swz(int d) { return 8 * ((d >> 3) & 7); }
+// stored position of natural index d in a k-permuted row
+__device__ __forceinline__ constexpr int perm(int d) {
+  return (d & ~31) | ((d & 12) << 1) | ((d & 16) >> 2) | (d & 3);
+}
 
-constexpr int NW = 4;            // waves per workgroup
-constexpr int NT = 64 * NW;      // threads per workgroup
-constexpr int NB = D / 16 / NW;  // 16-column state tiles per wave
+// element offset of (row t, stored position pos) in a swizzled [64][128] tile:
+// 16-byte chunk c of row t sits at chunk c ^ (2 (t & 7) + ((t >> 3) & 1)).  The
+// 16 rows of a row-operand read and the 8 rows x 32 bytes of each half of a
+// transposed read then fall on distinct banks.
+__device__ __forceinline__ int swz_off(int t, int pos) {
+  const int f = 2 * (t & 7) + ((t >> 3) & 1);
+  return t * D + (((pos >> 3) ^ f) << 3) + (pos & 7);
+}
+
+// Operand lanes: r = l & 15, g = l >> 4; as a transposed-read source, lane l
+// supplies row i = (l >> 2) & 3 and column group a = l & 3.
+struct Lane {
+  int r, g, a, i;
+};
+
+// rows t0 + r of a swizzled Q / K tile, k = d of 32-group kk (permuted)
+__device__ __forceinline__ bf16x8 ld_row_qk(const uint16_t* base, int t0, int kk, const Lane& L) {
+  return lds8(base + swz_off(t0 + L.r, 32 * kk + 8 * L.g));
+}
+
+// K^T operand from the swizzled K tile: lane gets K[t][16 db + r] for the
+// permuted token set t = 32 kk + {4g..4g+3, 16+4g..16+4g+3}
+__device__ __forceinline__ bf16x8 ld_tr_qk(const uint16_t* base, int db, int kk, const Lane& L) {
+  const int pos = perm(16 * db + 4 * L.a);
+  const int t = 32 * kk + 4 * L.g + L.i;
+  return cat(ldtr(base + swz_off(t, pos)), ldtr(base + swz_off(t + 16, pos)));
+}
+
+// transposed operand from a row-major [j][c] tile of pitch P: lane gets
+// X[j][c0 + r] for the permuted set j = 32 kk + {4g..4g+3, 16+4g..16+4g+3}
+template <int P>
+__device__ __forceinline__ bf16x8 ld_tr(const uint16_t* base, int c0, int kk, const Lane& L) {
+  const uint16_t* p = base + (32 * kk + 4 * L.g + L.i) * P + c0 + 4 * L.a;
+  return cat(ldtr(p), ldtr(p + 16 * P));
+}
 
 struct Prefetch {
   u32x4 k[4], v[4], q[4];  // row (tid + NT it) >> 4, columns [8c8, 8c8+8), c8 = tid & 15
-  float b[4];              // beta of those rows
   float g0, b0;            // g and beta of row (tid & 63), read by wave 0
 };
 
@@ -138,52 +180,158 @@ struct Prefetch {
 __device__ __forceinline__ void prefetch(Prefetch& p, const ScanArgs& a, int64_t rbase, int nv, int m,
                                          int qoff, int koff, int voff, int tid, int wv) {
   const int C = a.channels, Hv = a.num_v_heads;
-  const __amdgpu_buffer_rsrc_t ry =
-      make_rsrc(reinterpret_cast<const uint16_t*>(a.y) + rbase * C, (uint32_t)nv * C * 2);
-  const __amdgpu_buffer_rsrc_t rg = make_rsrc(a.g + rbase * Hv, (uint32_t)nv * Hv * 4);
-  const __amdgpu_buffer_rsrc_t rb = make_rsrc(a.beta + rbase * Hv, (uint32_t)nv * Hv * 4);
   if (wv == 0) {
+    const __amdgpu_buffer_rsrc_t rg = make_rsrc(a.g + rbase * Hv, (uint32_t)nv * Hv * 4);
+    const __amdgpu_buffer_rsrc_t rb = make_rsrc(a.beta + rbase * Hv, (uint32_t)nv * Hv * 4);
     const int t = tid & 63;
     p.g0 = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rg, 4 * (t * Hv + m), 0, 0));
     p.b0 = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rb, 4 * (t * Hv + m), 0, 0));
   }
+  const __amdgpu_buffer_rsrc_t ry =
+      make_rsrc(reinterpret_cast<const uint16_t*>(a.y) + rbase * C, (uint32_t)nv * C * 2);
   const int c8 = tid & 15;
 #pragma unroll
   for (int it = 0; it < 4; ++it) {
-    const int r = (tid + NT * it) >> 4;
-    const int row = r * C + 8 * c8;
+    const int row = ((tid + NT * it) >> 4) * C + 8 * c8;
     p.k[it] = __builtin_amdgcn_raw_buffer_load_b128(ry, 2 * (row + koff), 0, 0);
     p.v[it] = __builtin_amdgcn_raw_buffer_load_b128(ry, 2 * (row + voff), 0, 0);
     p.q[it] = __builtin_amdgcn_raw_buffer_load_b128(ry, 2 * (row + qoff), 0, 0);
-    p.b[it] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rb, 4 * (r * Hv + m), 0, 0));
   }
 }
 
-// Output rows [row0, row0 + nv) of the wave's state columns: lane holds rows
-// 16tb + 4lg + i of columns n0 + 16nb + li as packed bf16 pairs.  The buffer
-// range ends at row nv, so the stores of rows past the end are dropped.
-__device__ __forceinline__ void store_out(const ScanArgs& a, const uint32_t (&opk)[4][NB][2], int64_t row0, int nv,
-                                          int m, int n0, int li, int lg) {
-  const int Hv = a.num_v_heads;
-  const __amdgpu_buffer_rsrc_t ro =
-      make_rsrc(reinterpret_cast<uint16_t*>(a.out) + row0 * Hv * D, (uint32_t)nv * Hv * D * 2);
-  const int obase = m * D + n0 + li + 4 * lg * Hv * D;
+// One 16x16 block (bi, bj), bj <= bi, of A = strictly-lower(b_t e^{gamma_t - gamma_j} K K^T).
+// Lane holds A[t = 16bi + 4g + i][j = 16bj + r].  Diagonal blocks go to `at`
+// in fp32, the others to `abt` in bf16, both transposed.
+__device__ __forceinline__ void gram_a(Smem& sm, int bi, int bj, const Lane& L) {
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int tb = 0; tb < 4; ++tb)
+  for (int kk = 0; kk < 4; ++kk) acc = mfma(ld_row_qk(sm.k, 16 * bi, kk, L), ld_row_qk(sm.k, 16 * bj, kk, L), acc);
+  const int j = 16 * bj + L.r;
+  const float gj = sm.gam[j];
+  const f32x4 gt = *reinterpret_cast<const f32x4*>(&sm.gam[16 * bi + 4 * L.g]);
+  const f32x4 bt = *reinterpret_cast<const f32x4*>(&sm.beta[16 * bi + 4 * L.g]);
+  float v[4];
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const uint32_t w = opk[tb][nb][i >> 1];
-        __builtin_amdgcn_raw_buffer_store_b16((uint16_t)((i & 1) ? (w >> 16) : (w & 0xffff)), ro,
-                                              2 * (obase + 16 * nb + (16 * tb + i) * Hv * D), 0, 0);
-      }
+  for (int i = 0; i < 4; ++i) {
+    const float f = bt[i] * __expf(gt[i] - gj) * acc[i];
+    v[i] = (j < 16 * bi + 4 * L.g + i) ? f : 0.f;
+  }
+  if (bi == bj)
+    *reinterpret_cast<float4*>(&sm.at[(16 * bi + L.r) * PA + 4 * L.g]) = make_float4(v[0], v[1], v[2], v[3]);
+  else
+    st4bf(&sm.abt[j * PX + 16 * bi + 4 * L.g], v[0], v[1], v[2], v[3]);
 }
 
-// lower 16x16 block pair number e (0..9) in row order: (0,0) (1,0) (1,1) (2,0) ...
-__device__ __forceinline__ void lower_pair(int e, int& bi, int& bj) {
-  bi = e >= 6 ? 3 : e >= 3 ? 2 : e >= 1 ? 1 : 0;
-  bj = e - (bi * (bi + 1)) / 2;
+// One 16x16 block (bi, bj), bj <= bi, of P = M o Q K^T, computed transposed:
+// lane holds P[t = 16bi + r][j = 16bj + 4g + i].
+__device__ __forceinline__ void gram_p(Smem& sm, int bi, int bj, const Lane& L) {
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) acc = mfma(ld_row_qk(sm.k, 16 * bj, kk, L), ld_row_qk(sm.q, 16 * bi, kk, L), acc);
+  const int t = 16 * bi + L.r;
+  const float gt = sm.gam[t];
+  const f32x4 gj = *reinterpret_cast<const f32x4*>(&sm.gam[16 * bj + 4 * L.g]);
+  float v[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float f = __expf(gt - gj[i]) * acc[i];
+    v[i] = (16 * bj + 4 * L.g + i <= t) ? f : 0.f;
+  }
+  st4bf(&sm.p[t * PP + perm(16 * bj + 4 * L.g)], v[0], v[1], v[2], v[3]);
+}
+
+// Column c of T's block (R, C) in a lane's D tile (rows 4g + i) -> T^T and its
+// two column-scaled copies.
+__device__ __forceinline__ void put_t(Smem& sm, int R, int C, f32x4 tv, const Lane& L) {
+  const int jc = 16 * C + L.r;
+  const int o = jc * PX + 16 * R + 4 * L.g;
+  const float s1 = sm.bg[jc], s2 = sm.beta[jc];
+  st4bf(&sm.tt[o], tv[0], tv[1], tv[2], tv[3]);
+  st4bf(&sm.t1t[o], s1 * tv[0], s1 * tv[1], s1 * tv[2], s1 * tv[3]);
+  st4bf(&sm.t2t[o], s2 * tv[0], s2 * tv[1], s2 * tv[2], s2 * tv[3]);
+}
+
+// 16x16x16 operands of the block products, from the transposed tiles:
+// A rows 16R + r, k = 16C + 4g + i (lane gets X[16R + r][16C + 4g..+3])
+__device__ __forceinline__ bf16x4 blk_a(const uint16_t* xt, int R, int C, const Lane& L) {
+  return ldtr(xt + (16 * C + 4 * L.g + L.i) * PX + 16 * R + 4 * L.a);
+}
+// B k = 16R + 4g + i, column 16C + r (lane gets X[16R + 4g..+3][16C + r])
+__device__ __forceinline__ bf16x4 blk_b(const uint16_t* xt, int R, int C, const Lane& L) {
+  return lds4(xt + (16 * C + L.r) * PX + 16 * R + 4 * L.g);
+}
+
+// T = (I + A)^-1 in one wave.  The four diagonal blocks by fp32 forward
+// substitution, one column per lane (lane 16 rg + c solves block rg, column
+// c, all 16 rows in registers, so no lane exchange is needed), then the blocks
+// below the diagonal by MFMA block products:
+//   T10 = -T11 A10 T00,  T32 = -T33 A32 T22,
+//   [T20 T21; T30 T31] = -[T22 0; T32 T33] [A20 A21; A30 A31] [T00 0; T10 T11].
+__device__ __forceinline__ void solve_t(Smem& sm, const Lane& L, int lane) {
+  {
+    const int c = lane & 15, rg = lane >> 4;
+    float x[16];
+#pragma unroll
+    for (int t = 0; t < 16; ++t) x[t] = (t == c) ? 1.f : 0.f;
+    const float* col = &sm.at[16 * rg * PA];
+#pragma unroll
+    for (int j = 0; j < 15; ++j) {
+      const float xj = x[j];
+      float aj[16];
+#pragma unroll
+      for (int q4 = (j + 1) >> 2; q4 < 4; ++q4) {
+        const f32x4 v = *reinterpret_cast<const f32x4*>(&col[j * PA + 4 * q4]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) aj[4 * q4 + e] = v[e];
+      }
+#pragma unroll
+      for (int t = j + 1; t < 16; ++t) x[t] -= aj[t] * xj;
+    }
+    const int jc = 16 * rg + c;
+    const float s1 = sm.bg[jc], s2 = sm.beta[jc];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int o = jc * PX + 16 * rg + 8 * h;
+      u32x4 w0, w1, w2;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float x0 = x[8 * h + 2 * e], x1 = x[8 * h + 2 * e + 1];
+        w0[e] = pack_bf16x2(x0, x1);
+        w1[e] = pack_bf16x2(s1 * x0, s1 * x1);
+        w2[e] = pack_bf16x2(s2 * x0, s2 * x1);
+      }
+      *reinterpret_cast<u32x4*>(&sm.tt[o]) = w0;
+      *reinterpret_cast<u32x4*>(&sm.t1t[o]) = w1;
+      *reinterpret_cast<u32x4*>(&sm.t2t[o]) = w2;
+    }
+  }
+  const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+  // first level: T10, T32 (the wave's own LDS writes are visible to its later reads)
+  f32x4 t10, t32;
+  {
+    const f32x4 y10 = mfma16(blk_a(sm.abt, 1, 0, L), blk_b(sm.tt, 0, 0, L), z);
+    const f32x4 y32 = mfma16(blk_a(sm.abt, 3, 2, L), blk_b(sm.tt, 2, 2, L), z);
+    t10 = -mfma16(blk_a(sm.tt, 1, 1, L), to_bf16x4(y10), z);
+    t32 = -mfma16(blk_a(sm.tt, 3, 3, L), to_bf16x4(y32), z);
+    put_t(sm, 1, 0, t10, L);
+    put_t(sm, 3, 2, t32, L);
+  }
+  // second level
+  {
+    const bf16x4 b00 = blk_b(sm.tt, 0, 0, L), b11 = blk_b(sm.tt, 1, 1, L), b10 = to_bf16x4(t10);
+    const bf16x4 a20 = blk_a(sm.abt, 2, 0, L), a21 = blk_a(sm.abt, 2, 1, L);
+    const bf16x4 a30 = blk_a(sm.abt, 3, 0, L), a31 = blk_a(sm.abt, 3, 1, L);
+    const f32x4 y20 = mfma16(a21, b10, mfma16(a20, b00, z));
+    const f32x4 y21 = mfma16(a21, b11, z);
+    const f32x4 y30 = mfma16(a31, b10, mfma16(a30, b00, z));
+    const f32x4 y31 = mfma16(a31, b11, z);
+    const bf16x4 t22 = blk_a(sm.tt, 2, 2, L), t33 = blk_a(sm.tt, 3, 3, L), t32a = blk_a(sm.tt, 3, 2, L);
+    const bf16x4 c20 = to_bf16x4(y20), c21 = to_bf16x4(y21);
+    put_t(sm, 2, 0, -mfma16(t22, c20, z), L);
+    put_t(sm, 2, 1, -mfma16(t22, c21, z), L);
+    put_t(sm, 3, 0, -mfma16(t33, to_bf16x4(y30), mfma16(t32a, c20, z)), L);
+    put_t(sm, 3, 1, -mfma16(t33, to_bf16x4(y31), mfma16(t32a, c21, z)), L);
+  }
 }
 
 __global__ __launch_bounds__(NT) void chunk_scan_kernel(ScanArgs a, SeqOrder ord) {
@@ -200,7 +348,8 @@ __global__ __launch_bounds__(NT) void chunk_scan_kernel(ScanArgs a, SeqOrder ord
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, kept in a scalar register
-  const int li = lane & 15, lg = lane >> 4;
+  const Lane ln{lane & 15, lane >> 4, lane & 3, (lane >> 2) & 3};
+  const int li = ln.r, lg = ln.g;
   const int h = m / (Hv / a.num_k_heads);
   const int qoff = h * D, koff = a.num_k_heads * D + h * D;
   const int voff = 2 * a.num_k_heads * D + m * D;
@@ -229,43 +378,36 @@ __global__ __launch_bounds__(NT) void chunk_scan_kernel(ScanArgs a, SeqOrder ord
         for (int i = 0; i < 4; ++i) sacc[db][nb][i] = sm.sst[(16 * db + 4 * lg + i) * PS + n0 + 16 * nb + li];
     lds_barrier();
   }
-  for (int i = tid; i < BT * PT; i += NT) {
-    sm.t1[i] = 0;
-    sm.p[i] = 0;
+  // blocks above the diagonal are read by the full-width products and never written
+  {
+    const u32x4 zero = {0u, 0u, 0u, 0u};
+    for (int i = tid; i < BT * PP / 8; i += NT) reinterpret_cast<u32x4*>(sm.p)[i] = zero;
+    for (int i = tid; i < BT * PX / 8; i += NT) {
+      reinterpret_cast<u32x4*>(sm.tt)[i] = zero;
+      reinterpret_cast<u32x4*>(sm.t1t)[i] = zero;
+      reinterpret_cast<u32x4*>(sm.t2t)[i] = zero;
+    }
   }
 
   Prefetch pf;
   prefetch(pf, a, r0, min(BT, L), m, qoff, koff, voff, tid, wv);
-  // the previous chunk's output, packed bf16 pairs; stored during the next chunk
-  // so the stores are long complete when the loop top waits for the prefetch
-  uint32_t opk[4][NB][2];
-  int64_t obase_row = 0;
-  int onv = 0;
 
   for (int c0 = 0; c0 < L; c0 += BT) {
     const int nv = min(BT, L - c0);
     const int64_t rbase = r0 + c0;
 
-    // ---- stage this chunk from the prefetch registers, then prefetch the next one
+    // ---- stage this chunk from the prefetch registers
     {
-      const int c8 = tid & 15, tsw = 8 * (c8 & 7);  // swz(8 c8 + e) for every e
+      const int c8 = tid & 15;
+      const int p1 = perm(8 * c8), p2 = perm(8 * c8 + 4);
 #pragma unroll
       for (int it = 0; it < 4; ++it) {
         const int t = (tid + NT * it) >> 4;
-        *reinterpret_cast<u32x4*>(&sm.kw.k[t * PQ + 8 * c8]) = pf.k[it];
-        *reinterpret_cast<u32x4*>(&sm.q[t * PQ + 8 * c8]) = pf.q[it];
-        const uint32_t kw[4] = {pf.k[it][0], pf.k[it][1], pf.k[it][2], pf.k[it][3]};
-        const uint32_t vw[4] = {pf.v[it][0], pf.v[it][1], pf.v[it][2], pf.v[it][3]};
-        const int ts = t ^ tsw;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          sm.kt[(8 * c8 + 2 * e) * PT + ts] = (uint16_t)(kw[e] & 0xffff);
-          sm.kt[(8 * c8 + 2 * e + 1) * PT + ts] = (uint16_t)(kw[e] >> 16);
-          const uint32_t vv = pack_bf16x2(pf.b[it] * __uint_as_float(vw[e] << 16),
-                                          pf.b[it] * __uint_as_float(vw[e] & 0xffff0000u));
-          sm.vt[(8 * c8 + 2 * e) * PT + ts] = (uint16_t)(vv & 0xffff);
-          sm.vt[(8 * c8 + 2 * e + 1) * PT + ts] = (uint16_t)(vv >> 16);
-        }
+        *reinterpret_cast<uint2*>(&sm.q[swz_off(t, p1)]) = make_uint2(pf.q[it][0], pf.q[it][1]);
+        *reinterpret_cast<uint2*>(&sm.q[swz_off(t, p2)]) = make_uint2(pf.q[it][2], pf.q[it][3]);
+        *reinterpret_cast<uint2*>(&sm.k[swz_off(t, p1)]) = make_uint2(pf.k[it][0], pf.k[it][1]);
+        *reinterpret_cast<uint2*>(&sm.k[swz_off(t, p2)]) = make_uint2(pf.k[it][2], pf.k[it][3]);
+        *reinterpret_cast<u32x4*>(&sm.v[t * PV + 8 * c8]) = pf.v[it];
       }
       if (wv == 0) {
         float gv = pf.g0;
@@ -274,191 +416,81 @@ __global__ __launch_bounds__(NT) void chunk_scan_kernel(ScanArgs a, SeqOrder ord
           const float o = __shfl_up(gv, off);
           if (lane >= off) gv += o;
         }
+        const float glast = __shfl(gv, 63);
+        const float e = __expf(gv);
         sm.gam[lane] = gv;
+        sm.eg[lane] = e;
+        sm.ed[lane] = __expf(glast - gv);
         sm.beta[lane] = pf.b0;
+        sm.bg[lane] = pf.b0 * e;
       }
     }
     lds_barrier();
 
-    // ---- Gram products: 10 lower 16x16 blocks of K K^T (-> A) and 10 of Q K^T
-    //      (-> P), five per wave
-#pragma unroll
-    for (int r = 0; r < 5; ++r) {
-      const int e = wv + NW * r;
-      int bi, bj;
-      lower_pair(e % 10, bi, bj);
-      const bool isq = e >= 10;
-      // K K^T block (bi, bj): lane holds A[t = 16bi + 4lg + i][j = 16bj + li];
-      // (Q K^T)^T block: lane holds P[t = 16bi + li][j = 16bj + 4lg + i]
-      const uint16_t* xrow = isq ? &sm.kw.k[(16 * bj + li) * PQ] : &sm.kw.k[(16 * bi + li) * PQ];
-      const uint16_t* yrow = isq ? &sm.q[(16 * bi + li) * PQ] : &sm.kw.k[(16 * bj + li) * PQ];
-      bf16x8 xa[4], yb[4];
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        xa[kk] = ldsp(xrow + 32 * kk + 4 * lg);
-        yb[kk] = ldsp(yrow + 32 * kk + 4 * lg);
-      }
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) acc = mfma(xa[kk], yb[kk], acc);
-      float v[4];
-      if (!isq) {
-        const int j = 16 * bj + li;
-        const float gj = sm.gam[j];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int t = 16 * bi + 4 * lg + i;
-          const float f = sm.beta[t] * __expf(sm.gam[t] - gj) * acc[i];
-          v[i] = (j < t) ? f : 0.f;
-        }
-        if (bi == bj) {
-          *reinterpret_cast<float4*>(&sm.at[(16 * bi + li) * PA + 4 * lg]) = make_float4(v[0], v[1], v[2], v[3]);
-        } else {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) sm.ab[(16 * bi + 4 * lg + i) * PT + j] = bfb(v[i]);
-        }
-      } else {
-        const int t = 16 * bi + li;
-        const float gt = sm.gam[t];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int j = 16 * bj + 4 * lg + i;
-          const float f = __expf(gt - sm.gam[j]) * acc[i];
-          v[i] = (j <= t) ? f : 0.f;
-        }
-        st4bf(&sm.p[t * PT + 16 * bj + 4 * lg], v[0], v[1], v[2], v[3]);
-      }
+    // ---- A = strictly-lower(b e^{gamma_t - gamma_j} K K^T): ten 16x16 blocks
+    if (wv == 0) {
+      gram_a(sm, 0, 0, ln); gram_a(sm, 3, 0, ln); gram_a(sm, 3, 3, ln);
+    } else if (wv == 1) {
+      gram_a(sm, 1, 0, ln); gram_a(sm, 1, 1, ln); gram_a(sm, 3, 1, ln);
+    } else if (wv == 2) {
+      gram_a(sm, 2, 0, ln); gram_a(sm, 2, 2, ln);
+    } else {
+      gram_a(sm, 2, 1, ln); gram_a(sm, 3, 2, ln);
     }
     lds_barrier();
 
-    // ---- T = (I + A)^-1, diagonal block w by column-oriented fp32 forward
-    //      substitution: lane (li = column c, lg) holds rows t = 4lg..4lg+3 of
-    //      column c; step j broadcasts the finished x_j from its owner (lane
-    //      li + 16 (j >> 2)) and every lane applies x_t -= A[t][j] x_j (A is zero
-    //      on and above the diagonal).  Then the blocks above the diagonal that
-    //      later products read are cleared: T(0,1), T(2,3), T^T(1,0).
-    {
-      const int rg = wv, c = li;
-      const float* ab = &sm.at[(16 * rg) * PA + 4 * lg];
-      f32x4 x;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) x[i] = (4 * lg + i == c) ? 1.f : 0.f;
-#pragma unroll
-      for (int j = 0; j < 15; ++j) {
-        const float xj = __shfl(x[j & 3], li + 16 * (j >> 2));
-        const f32x4 col = *reinterpret_cast<const f32x4*>(&ab[j * PA]);
-        x -= col * xj;
-      }
-      const int cg = 16 * rg + c;
-      const float bgc = sm.beta[cg] * __expf(sm.gam[cg]);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int tg = 16 * rg + 4 * lg + i;
-        sm.tr[tg * PT + cg] = bfb(x[i]);
-        sm.t1[tg * PT + cg] = bfb(x[i] * bgc);
-      }
-      st4bf(&sm.tt[cg * PT + 16 * rg + 4 * lg], x[0], x[1], x[2], x[3]);
-      if (rg == 0 || rg == 2)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) sm.tr[(16 * rg + 4 * lg + i) * PT + 16 * rg + 16 + c] = 0;
-      if (rg == 1) st4bf(&sm.tt[(16 + c) * PT + 4 * lg], 0.f, 0.f, 0.f, 0.f);
+    // ---- T = (I + A)^-1 in wave 0; P = M o Q K^T in the others
+    if (wv == 0) {
+      solve_t(sm, ln, lane);
+    } else if (wv == 1) {
+      gram_p(sm, 3, 0, ln); gram_p(sm, 3, 1, ln); gram_p(sm, 3, 2, ln); gram_p(sm, 3, 3, ln);
+    } else if (wv == 2) {
+      gram_p(sm, 2, 0, ln); gram_p(sm, 2, 1, ln); gram_p(sm, 2, 2, ln);
+    } else {
+      gram_p(sm, 1, 0, ln); gram_p(sm, 1, 1, ln); gram_p(sm, 0, 0, ln);
     }
     lds_barrier();
 
-    // ---- first-level blocks in the wave that solved the row block:
-    //      wave 1: T10 = -T11 (A10 T00);  wave 3: T32 = -T33 (A32 T22)
-    if (wv == 1 || wv == 3) {
-      const int rb = 16 * wv, cb0 = 16 * (wv - 1);
-      uint16_t* y = &sm.yt[(16 * (wv >> 1)) * PY];
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      acc = mfma(lds8_k16(&sm.ab[(rb + li) * PT + cb0 + 8 * lg], lg),
-                 lds8_k16(&sm.tt[(cb0 + li) * PT + cb0 + 8 * lg], lg), acc);
-      st4bf(&y[li * PY + 4 * lg], acc[0], acc[1], acc[2], acc[3]);
-      f32x4 tacc = {0.f, 0.f, 0.f, 0.f};
-      tacc = mfma(lds8_k16(&sm.tr[(rb + li) * PT + rb + 8 * lg], lg), lds8_k16(&y[li * PY + 8 * lg], lg), tacc);
-      const int cg = cb0 + li;
-      const float bgc = sm.beta[cg] * __expf(sm.gam[cg]);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int tg = rb + 4 * lg + i;
-        sm.tr[tg * PT + cg] = bfb(-tacc[i]);
-        sm.t1[tg * PT + cg] = bfb(-tacc[i] * bgc);
-      }
-      st4bf(&sm.tt[cg * PT + rb + 4 * lg], -tacc[0], -tacc[1], -tacc[2], -tacc[3]);
-    }
-    lds_barrier();
-
-    // ---- second level: T[32:64, 16c:16c+16] = -T_BB (A_BA T_AA)[:, 16c:16c+16],
-    //      one 16-column block c per wave 0..1, both row blocks
-    if (wv < 2) {
-      const int cb0 = 16 * wv;
-      uint16_t* y = &sm.yt[(32 + 16 * wv) * PY];
-      const bf16x8 tb = lds8(&sm.tt[(cb0 + li) * PT + 8 * lg]);
-#pragma unroll
-      for (int hb = 0; hb < 2; ++hb) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        acc = mfma(lds8(&sm.ab[(32 + 16 * hb + li) * PT + 8 * lg]), tb, acc);
-        st4bf(&y[li * PY + 16 * hb + 4 * lg], acc[0], acc[1], acc[2], acc[3]);
-      }
-      const int cg = cb0 + li;
-      const float bgc = sm.beta[cg] * __expf(sm.gam[cg]);
-      const bf16x8 yb = lds8(&y[li * PY + 8 * lg]);
-#pragma unroll
-      for (int hb = 0; hb < 2; ++hb) {
-        f32x4 tacc = {0.f, 0.f, 0.f, 0.f};
-        tacc = mfma(lds8(&sm.tr[(32 + 16 * hb + li) * PT + 32 + 8 * lg]), yb, tacc);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int tg = 32 + 16 * hb + 4 * lg + i;
-          sm.tr[tg * PT + cg] = bfb(-tacc[i]);
-          sm.t1[tg * PT + cg] = bfb(-tacc[i] * bgc);
-        }
-      }
-    }
-    lds_barrier();
-
-    // the global traffic of this chunk is issued here, after the small solve
-    // phases, so that their waits never wait for it
+    // the next chunk's loads are issued here, after the short phases, and
+    // have the W phase and the state pass to arrive
     if (c0 + BT < L) prefetch(pf, a, rbase + BT, min(BT, L - c0 - BT), m, qoff, koff, voff, tid, wv);
-    if (c0 > 0) store_out(a, opk, obase_row, onv, m, n0, li, lg);
 
-    // ---- -W = -(T diag(b Gamma)) K into LDS (wave w: d blocks 2w, 2w+1, all
-    //      chunk rows), and U~ = T (diag(b) V) for the wave's columns in the U
-    //      accumulators
+    // ---- -W = -(T diag(b Gamma) K) rows into LDS (wave w: d blocks 2w, 2w+1),
+    //      U~ = T diag(b) V for the wave's columns in registers
     f32x4 uacc[4][NB];
+    {
+      f32x4 wacc[4][2];
 #pragma unroll
-    for (int tb = 0; tb < 4; ++tb) {
-      const int nk = tb < 2 ? 1 : 2;
-      f32x4 acc[2];
+      for (int tb = 0; tb < 4; ++tb) {
 #pragma unroll
-      for (int e = 0; e < 2; ++e) acc[e] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int e = 0; e < 2; ++e) wacc[tb][e] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) uacc[tb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int nb = 0; nb < NB; ++nb) uacc[tb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
 #pragma unroll
-      for (int kk = 0; kk < nk; ++kk) {
-        const bf16x8 bt = lds8(&sm.t1[(16 * tb + li) * PT + 32 * kk + 8 * lg]);
-        const bf16x8 at = lds8(&sm.tr[(16 * tb + li) * PT + 32 * kk + 8 * lg]);
+      for (int kk = 0; kk < 2; ++kk) {
         bf16x8 ka[2], vb[NB];
 #pragma unroll
-        for (int e = 0; e < 2; ++e) {
-          const int d = 16 * (2 * wv + e) + li;
-          ka[e] = lds8(&sm.kt[d * PT + ((32 * kk + 8 * lg) ^ swz(d))]);
+        for (int e = 0; e < 2; ++e) ka[e] = ld_tr_qk(sm.k, 2 * wv + e, kk, ln);
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) vb[nb] = ld_tr<PV>(sm.v, n0 + 16 * nb, kk, ln);
+#pragma unroll
+        for (int tb = 2 * kk; tb < 4; ++tb) {
+          const bf16x8 b1 = ld_tr<PX>(sm.t1t, 16 * tb, kk, ln);  // T1[t][j] as the B operand
+          const bf16x8 a2 = ld_tr<PX>(sm.t2t, 16 * tb, kk, ln);  // T2[t][j] as the A operand
+#pragma unroll
+          for (int e = 0; e < 2; ++e) wacc[tb][e] = mfma(ka[e], b1, wacc[tb][e]);
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb) uacc[tb][nb] = mfma(a2, vb[nb], uacc[tb][nb]);
         }
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-          const int n = n0 + 16 * nb + li;
-          vb[nb] = lds8(&sm.vt[n * PT + ((32 * kk + 8 * lg) ^ swz(n))]);
-        }
-#pragma unroll
-        for (int e = 0; e < 2; ++e) acc[e] = mfma(ka[e], bt, acc[e]);
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) uacc[tb][nb] = mfma(at, vb[nb], uacc[tb][nb]);
       }
       // lane holds W[t = 16tb + li][d = 16(2w+e) + 4lg + i]
 #pragma unroll
-      for (int e = 0; e < 2; ++e)
-        st4bf(&sm.kw.w[(16 * tb + li) * PQ + 16 * (2 * wv + e) + 4 * lg], -acc[e][0], -acc[e][1], -acc[e][2],
-              -acc[e][3]);
+      for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+        for (int e = 0; e < 2; ++e)
+          st4bf(&sm.w[(16 * tb + li) * PW + perm(16 * (2 * wv + e) + 4 * lg)], -wacc[tb][e][0], -wacc[tb][e][1],
+                -wacc[tb][e][2], -wacc[tb][e][3]);
     }
     lds_barrier();
 
@@ -476,8 +508,8 @@ __global__ __launch_bounds__(NT) void chunk_scan_kernel(ScanArgs a, SeqOrder ord
         for (int nb = 0; nb < NB; ++nb) sb[nb] = pair_operand(sacc[2 * kk][nb], sacc[2 * kk + 1][nb]);
 #pragma unroll
         for (int tb = 0; tb < 4; ++tb) {
-          const bf16x8 wa = ldsp(&sm.kw.w[(16 * tb + li) * PQ + 32 * kk + 4 * lg]);
-          const bf16x8 qa = ldsp(&sm.q[(16 * tb + li) * PQ + 32 * kk + 4 * lg]);
+          const bf16x8 wa = lds8(&sm.w[(16 * tb + li) * PW + 32 * kk + 8 * lg]);
+          const bf16x8 qa = ld_row_qk(sm.q, 16 * tb, kk, ln);
 #pragma unroll
           for (int nb = 0; nb < NB; ++nb) {
             uacc[tb][nb] = mfma(wa, sb[nb], uacc[tb][nb]);  // U = U~ - W S
@@ -485,71 +517,66 @@ __global__ __launch_bounds__(NT) void chunk_scan_kernel(ScanArgs a, SeqOrder ord
           }
         }
       }
-      const float glast = sm.gam[BT - 1];
       bf16x8 ub[2][NB], upb[2][NB];
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
-        float g0[4], g1[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          g0[i] = sm.gam[32 * kk + 4 * lg + i];
-          g1[i] = sm.gam[32 * kk + 16 + 4 * lg + i];
-        }
+        const f32x4 e0 = *reinterpret_cast<const f32x4*>(&sm.eg[32 * kk + 4 * lg]);
+        const f32x4 e1 = *reinterpret_cast<const f32x4*>(&sm.eg[32 * kk + 16 + 4 * lg]);
+        const f32x4 d0 = *reinterpret_cast<const f32x4*>(&sm.ed[32 * kk + 4 * lg]);
+        const f32x4 d1 = *reinterpret_cast<const f32x4*>(&sm.ed[32 * kk + 16 + 4 * lg]);
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
           ub[kk][nb] = pair_operand(uacc[2 * kk][nb], uacc[2 * kk + 1][nb]);
-          f32x4 lo, hi;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            lo[i] = uacc[2 * kk][nb][i] * __expf(glast - g0[i]);
-            hi[i] = uacc[2 * kk + 1][nb][i] * __expf(glast - g1[i]);
-            oacc[2 * kk][nb][i] *= __expf(g0[i]);
-            oacc[2 * kk + 1][nb][i] *= __expf(g1[i]);
-          }
-          upb[kk][nb] = pair_operand(lo, hi);
+          upb[kk][nb] = pair_operand(uacc[2 * kk][nb] * d0, uacc[2 * kk + 1][nb] * d1);
+          oacc[2 * kk][nb] *= e0;
+          oacc[2 * kk + 1][nb] *= e1;
         }
       }
       // O += P U
 #pragma unroll
-      for (int tb = 0; tb < 4; ++tb) {
-        const int nk = tb < 2 ? 1 : 2;
+      for (int tb = 0; tb < 4; ++tb)
 #pragma unroll
-        for (int kk = 0; kk < nk; ++kk) {
-          const bf16x8 pa = ldsp(&sm.p[(16 * tb + li) * PT + 32 * kk + 4 * lg]);
+        for (int kk = 0; kk <= (tb >> 1); ++kk) {
+          const bf16x8 pa = lds8(&sm.p[(16 * tb + li) * PP + 32 * kk + 8 * lg]);
 #pragma unroll
           for (int nb = 0; nb < NB; ++nb) oacc[tb][nb] = mfma(pa, ub[kk][nb], oacc[tb][nb]);
         }
-      }
       // S <- Gamma_c S + K^T U'
-      const float gc = __expf(glast);
+      const float gc = sm.eg[BT - 1];
 #pragma unroll
-      for (int db = 0; db < 8; ++db) {
-        const uint16_t* row = &sm.kt[(16 * db + li) * PT];
-        const int sw = swz(16 * db + li);
+      for (int db = 0; db < 8; ++db)
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
-          const bf16x8 ka = ldsp2(row + ((32 * kk + 4 * lg) ^ sw), row + ((32 * kk + 16 + 4 * lg) ^ sw));
+          const bf16x8 ka = ld_tr_qk(sm.k, db, kk, ln);
 #pragma unroll
           for (int nb = 0; nb < NB; ++nb) {
             if (kk == 0) sacc[db][nb] *= gc;
             sacc[db][nb] = mfma(ka, upb[kk][nb], sacc[db][nb]);
           }
         }
-      }
+      // O: through the wave's LDS tile [n][t] to 16-byte row stores
+      uint16_t* ot = &sm.v[wv * 32 * PO];
 #pragma unroll
       for (int tb = 0; tb < 4; ++tb)
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-          opk[tb][nb][0] = pack_bf16x2(oacc[tb][nb][0], oacc[tb][nb][1]);
-          opk[tb][nb][1] = pack_bf16x2(oacc[tb][nb][2], oacc[tb][nb][3]);
-        }
-      obase_row = rbase;
-      onv = nv;
+        for (int nb = 0; nb < NB; ++nb)
+          st4bf(&ot[(16 * nb + li) * PO + 16 * tb + 4 * lg], oacc[tb][nb][0], oacc[tb][nb][1], oacc[tb][nb][2],
+                oacc[tb][nb][3]);
+      const __amdgpu_buffer_rsrc_t ro =
+          make_rsrc(reinterpret_cast<uint16_t*>(a.out) + rbase * Hv * D, (uint32_t)nv * Hv * D * 2);
+      const int ao = (lane & 15) >> 2, bo = lane & 3;  // this lane's output: columns 8 ao.., row 16 rho + 4 lg + bo
+#pragma unroll
+      for (int rho = 0; rho < 4; ++rho) {
+        const uint16_t* src = &ot[(8 * ln.a + ln.i) * PO + 16 * rho + 4 * lg];
+        const bf16x8 o8 = cat(ldtr(src), ldtr(src + 4 * PO));
+        const int t = 16 * rho + 4 * lg + bo;
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, o8), ro,
+                                               2 * (t * Hv * D + m * D + n0 + 8 * ao), 0, 0);
+      }
     }
     lds_barrier();
   }
 
-  store_out(a, opk, obase_row, onv, m, n0, li, lg);
   {
 #pragma unroll
     for (int db = 0; db < 8; ++db)
