@@ -1,7 +1,9 @@
 """Builds the gfx950 HIP library ``_lib/libgdn.so`` in-tree with hipcc.
 
 Every HIP source is compiled for gfx950 only, with packed-fp32 instruction
-forms disabled (plain fp32 code is emitted instead).
+forms disabled (plain fp32 code is emitted instead) and MFMA results kept in
+architectural VGPRs where possible (fewer accumulator-register copies around
+the VALU work on them).
 """
 from __future__ import annotations
 
@@ -17,6 +19,7 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wall", "-Wno-unused-function",
 ]
 

@@ -85,8 +85,13 @@ typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 __device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
+// A 16-deep product (lane holds k = 4g..4g+3 of each operand) on the same
+// 16x16x32 instruction, zero-padded: every accumulation chain in the kernel
+// then uses one MFMA shape (the two shapes take the same issue time).
 __device__ __forceinline__ f32x4 mfma16(bf16x4 a, bf16x4 b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+  const bf16x4 z = {};
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_shufflevector(a, z, 0, 1, 2, 3, 4, 5, 6, 7),
+                                                 __builtin_shufflevector(b, z, 0, 1, 2, 3, 4, 5, 6, 7), c, 0, 0, 0);
 }
 
 __device__ __forceinline__ bf16x8 lds8(const uint16_t* p) { return *reinterpret_cast<const bf16x8*>(p); }
@@ -104,6 +109,30 @@ __device__ __forceinline__ bf16x8 cat(bf16x4 lo, bf16x4 hi) {
 __device__ __forceinline__ bf16x4 ldtr(const uint16_t* p) {
   return __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(const_cast<uint16_t*>(p))));
 }
+
+// DPP lane move within each row of 16 lanes (or across rows for the row
+// broadcasts); lanes without a source lane get zero.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_move(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, ROW_MASK, 0xf, false));
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave: shifts by 1, 2, 4, 8 inside
+// each row of 16 lanes, then lane 15 of row 0 and lane 31 carried into the
+// later rows.
+__device__ __forceinline__ float wave_prefix_sum(float v) {
+  v += dpp_move<0x111, 0xf>(v);  // row_shr:1
+  v += dpp_move<0x112, 0xf>(v);  // row_shr:2
+  v += dpp_move<0x114, 0xf>(v);  // row_shr:4
+  v += dpp_move<0x118, 0xf>(v);  // row_shr:8
+  v += dpp_move<0x142, 0xa>(v);  // row_bcast:15 into rows 1 and 3
+  v += dpp_move<0x143, 0xc>(v);  // row_bcast:31 into rows 2 and 3
+  return v;
+}
+
+// Scheduling fence: the compiler keeps every instruction on its side, so
+// operand reads placed before it are issued ahead of the products after it.
+__device__ __forceinline__ void fence() { __builtin_amdgcn_sched_barrier(0); }
 
 __device__ __forceinline__ uint16_t bfb(float f) { return f32_to_bf16_bits(f); }
 __device__ __forceinline__ void st4bf(uint16_t* p, float a, float b, float c, float d) {
@@ -199,13 +228,28 @@ __device__ __forceinline__ void prefetch(Prefetch& p, const ScanArgs& a, int64_t
   }
 }
 
-// One 16x16 block (bi, bj), bj <= bi, of A = strictly-lower(b_t e^{gamma_t - gamma_j} K K^T).
-// Lane holds A[t = 16bi + 4g + i][j = 16bj + r].  Diagonal blocks go to `at`
-// in fp32, the others to `abt` in bf16, both transposed.
-__device__ __forceinline__ void gram_a(Smem& sm, int bi, int bj, const Lane& L) {
+// The 16 rows 16b..16b+15 of a swizzled Q / K tile as four row operands (all 128 d).
+struct Blk {
+  bf16x8 v[4];
+};
+__device__ __forceinline__ Blk ld_blk(const uint16_t* base, int b, const Lane& L) {
+  Blk x;
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) x.v[kk] = ld_row_qk(base, 16 * b, kk, L);
+  return x;
+}
+// D[row][col] = sum_d X[row][d] Y[col][d] over two 16-row blocks
+__device__ __forceinline__ f32x4 dot_blk(const Blk& x, const Blk& y) {
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int kk = 0; kk < 4; ++kk) acc = mfma(ld_row_qk(sm.k, 16 * bi, kk, L), ld_row_qk(sm.k, 16 * bj, kk, L), acc);
+  for (int kk = 0; kk < 4; ++kk) acc = mfma(x.v[kk], y.v[kk], acc);
+  return acc;
+}
+
+// Block (bi, bj), bj <= bi, of A = strictly-lower(b_t e^{gamma_t - gamma_j} K K^T)
+// from acc = K_bi K_bj^T: lane holds A[t = 16bi + 4g + i][j = 16bj + r].
+// Diagonal blocks go to `at` in fp32, the others to `abt` in bf16, both transposed.
+__device__ __forceinline__ void put_a(Smem& sm, int bi, int bj, f32x4 acc, const Lane& L) {
   const int j = 16 * bj + L.r;
   const float gj = sm.gam[j];
   const f32x4 gt = *reinterpret_cast<const f32x4*>(&sm.gam[16 * bi + 4 * L.g]);
@@ -222,12 +266,9 @@ __device__ __forceinline__ void gram_a(Smem& sm, int bi, int bj, const Lane& L) 
     st4bf(&sm.abt[j * PX + 16 * bi + 4 * L.g], v[0], v[1], v[2], v[3]);
 }
 
-// One 16x16 block (bi, bj), bj <= bi, of P = M o Q K^T, computed transposed:
+// Block (bi, bj), bj <= bi, of P = M o Q K^T from acc = K_bj Q_bi^T (transposed):
 // lane holds P[t = 16bi + r][j = 16bj + 4g + i].
-__device__ __forceinline__ void gram_p(Smem& sm, int bi, int bj, const Lane& L) {
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int kk = 0; kk < 4; ++kk) acc = mfma(ld_row_qk(sm.k, 16 * bj, kk, L), ld_row_qk(sm.q, 16 * bi, kk, L), acc);
+__device__ __forceinline__ void put_p(Smem& sm, int bi, int bj, f32x4 acc, const Lane& L) {
   const int t = 16 * bi + L.r;
   const float gt = sm.gam[t];
   const f32x4 gj = *reinterpret_cast<const f32x4*>(&sm.gam[16 * bj + 4 * L.g]);
@@ -410,13 +451,8 @@ __global__ __launch_bounds__(NT) void chunk_scan_kernel(ScanArgs a, SeqOrder ord
         *reinterpret_cast<u32x4*>(&sm.v[t * PV + 8 * c8]) = pf.v[it];
       }
       if (wv == 0) {
-        float gv = pf.g0;
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-          const float o = __shfl_up(gv, off);
-          if (lane >= off) gv += o;
-        }
-        const float glast = __shfl(gv, 63);
+        const float gv = wave_prefix_sum(pf.g0);
+        const float glast = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, gv), 63));
         const float e = __expf(gv);
         sm.gam[lane] = gv;
         sm.eg[lane] = e;
@@ -427,15 +463,28 @@ __global__ __launch_bounds__(NT) void chunk_scan_kernel(ScanArgs a, SeqOrder ord
     }
     lds_barrier();
 
-    // ---- A = strictly-lower(b e^{gamma_t - gamma_j} K K^T): ten 16x16 blocks
+    // ---- A = strictly-lower(b e^{gamma_t - gamma_j} K K^T): ten 16x16 blocks,
+    //      operand blocks read before the products
     if (wv == 0) {
-      gram_a(sm, 0, 0, ln); gram_a(sm, 3, 0, ln); gram_a(sm, 3, 3, ln);
+      const Blk k0 = ld_blk(sm.k, 0, ln), k3 = ld_blk(sm.k, 3, ln);
+      fence();
+      const f32x4 a00 = dot_blk(k0, k0), a30 = dot_blk(k3, k0), a33 = dot_blk(k3, k3);
+      put_a(sm, 0, 0, a00, ln); put_a(sm, 3, 0, a30, ln); put_a(sm, 3, 3, a33, ln);
     } else if (wv == 1) {
-      gram_a(sm, 1, 0, ln); gram_a(sm, 1, 1, ln); gram_a(sm, 3, 1, ln);
+      const Blk k0 = ld_blk(sm.k, 0, ln), k1 = ld_blk(sm.k, 1, ln), k3 = ld_blk(sm.k, 3, ln);
+      fence();
+      const f32x4 a10 = dot_blk(k1, k0), a11 = dot_blk(k1, k1), a31 = dot_blk(k3, k1);
+      put_a(sm, 1, 0, a10, ln); put_a(sm, 1, 1, a11, ln); put_a(sm, 3, 1, a31, ln);
     } else if (wv == 2) {
-      gram_a(sm, 2, 0, ln); gram_a(sm, 2, 2, ln);
+      const Blk k0 = ld_blk(sm.k, 0, ln), k2 = ld_blk(sm.k, 2, ln);
+      fence();
+      const f32x4 a20 = dot_blk(k2, k0), a22 = dot_blk(k2, k2);
+      put_a(sm, 2, 0, a20, ln); put_a(sm, 2, 2, a22, ln);
     } else {
-      gram_a(sm, 2, 1, ln); gram_a(sm, 3, 2, ln);
+      const Blk k1 = ld_blk(sm.k, 1, ln), k2 = ld_blk(sm.k, 2, ln), k3 = ld_blk(sm.k, 3, ln);
+      fence();
+      const f32x4 a21 = dot_blk(k2, k1), a32 = dot_blk(k3, k2);
+      put_a(sm, 2, 1, a21, ln); put_a(sm, 3, 2, a32, ln);
     }
     lds_barrier();
 
@@ -443,11 +492,23 @@ __global__ __launch_bounds__(NT) void chunk_scan_kernel(ScanArgs a, SeqOrder ord
     if (wv == 0) {
       solve_t(sm, ln, lane);
     } else if (wv == 1) {
-      gram_p(sm, 3, 0, ln); gram_p(sm, 3, 1, ln); gram_p(sm, 3, 2, ln); gram_p(sm, 3, 3, ln);
+      const Blk q3 = ld_blk(sm.q, 3, ln), k0 = ld_blk(sm.k, 0, ln), k1 = ld_blk(sm.k, 1, ln);
+      const Blk k2 = ld_blk(sm.k, 2, ln), k3 = ld_blk(sm.k, 3, ln);
+      fence();
+      const f32x4 p30 = dot_blk(k0, q3), p31 = dot_blk(k1, q3), p32 = dot_blk(k2, q3), p33 = dot_blk(k3, q3);
+      put_p(sm, 3, 0, p30, ln); put_p(sm, 3, 1, p31, ln); put_p(sm, 3, 2, p32, ln); put_p(sm, 3, 3, p33, ln);
     } else if (wv == 2) {
-      gram_p(sm, 2, 0, ln); gram_p(sm, 2, 1, ln); gram_p(sm, 2, 2, ln);
+      const Blk q2 = ld_blk(sm.q, 2, ln), k0 = ld_blk(sm.k, 0, ln), k1 = ld_blk(sm.k, 1, ln);
+      const Blk k2 = ld_blk(sm.k, 2, ln);
+      fence();
+      const f32x4 p20 = dot_blk(k0, q2), p21 = dot_blk(k1, q2), p22 = dot_blk(k2, q2);
+      put_p(sm, 2, 0, p20, ln); put_p(sm, 2, 1, p21, ln); put_p(sm, 2, 2, p22, ln);
     } else {
-      gram_p(sm, 1, 0, ln); gram_p(sm, 1, 1, ln); gram_p(sm, 0, 0, ln);
+      const Blk q0 = ld_blk(sm.q, 0, ln), q1 = ld_blk(sm.q, 1, ln), k0 = ld_blk(sm.k, 0, ln);
+      const Blk k1 = ld_blk(sm.k, 1, ln);
+      fence();
+      const f32x4 p10 = dot_blk(k0, q1), p11 = dot_blk(k1, q1), p00 = dot_blk(k0, q0);
+      put_p(sm, 1, 0, p10, ln); put_p(sm, 1, 1, p11, ln); put_p(sm, 0, 0, p00, ln);
     }
     lds_barrier();
 
@@ -467,23 +528,29 @@ __global__ __launch_bounds__(NT) void chunk_scan_kernel(ScanArgs a, SeqOrder ord
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) uacc[tb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
       }
+      bf16x8 ka[2][2], vb[2][NB], b1[2][4], a2[2][4];
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
-        bf16x8 ka[2], vb[NB];
 #pragma unroll
-        for (int e = 0; e < 2; ++e) ka[e] = ld_tr_qk(sm.k, 2 * wv + e, kk, ln);
+        for (int e = 0; e < 2; ++e) ka[kk][e] = ld_tr_qk(sm.k, 2 * wv + e, kk, ln);
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) vb[nb] = ld_tr<PV>(sm.v, n0 + 16 * nb, kk, ln);
+        for (int nb = 0; nb < NB; ++nb) vb[kk][nb] = ld_tr<PV>(sm.v, n0 + 16 * nb, kk, ln);
 #pragma unroll
         for (int tb = 2 * kk; tb < 4; ++tb) {
-          const bf16x8 b1 = ld_tr<PX>(sm.t1t, 16 * tb, kk, ln);  // T1[t][j] as the B operand
-          const bf16x8 a2 = ld_tr<PX>(sm.t2t, 16 * tb, kk, ln);  // T2[t][j] as the A operand
-#pragma unroll
-          for (int e = 0; e < 2; ++e) wacc[tb][e] = mfma(ka[e], b1, wacc[tb][e]);
-#pragma unroll
-          for (int nb = 0; nb < NB; ++nb) uacc[tb][nb] = mfma(a2, vb[nb], uacc[tb][nb]);
+          b1[kk][tb] = ld_tr<PX>(sm.t1t, 16 * tb, kk, ln);  // T1[t][j] as the B operand
+          a2[kk][tb] = ld_tr<PX>(sm.t2t, 16 * tb, kk, ln);  // T2[t][j] as the A operand
         }
+        fence();
       }
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+        for (int tb = 2 * kk; tb < 4; ++tb) {
+#pragma unroll
+          for (int e = 0; e < 2; ++e) wacc[tb][e] = mfma(ka[kk][e], b1[kk][tb], wacc[tb][e]);
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb) uacc[tb][nb] = mfma(a2[kk][tb], vb[kk][nb], uacc[tb][nb]);
+        }
       // lane holds W[t = 16tb + li][d = 16(2w+e) + 4lg + i]
 #pragma unroll
       for (int tb = 0; tb < 4; ++tb)
@@ -494,29 +561,52 @@ __global__ __launch_bounds__(NT) void chunk_scan_kernel(ScanArgs a, SeqOrder ord
     }
     lds_barrier();
 
-    // ---- state pass for the wave's columns, in registers
+    // ---- state pass for the wave's columns, in registers.  Operand reads run
+    //      one step ahead of the products that use them (the scheduling
+    //      barriers keep them there).
     {
       f32x4 oacc[4][NB];
 #pragma unroll
       for (int tb = 0; tb < 4; ++tb)
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) oacc[tb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      bf16x8 wa[2][4], qa[2][4];
+#pragma unroll
+      for (int tb = 0; tb < 4; ++tb) {
+        wa[0][tb] = lds8(&sm.w[(16 * tb + li) * PW + 8 * lg]);
+        qa[0][tb] = ld_row_qk(sm.q, 16 * tb, 0, ln);
+      }
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
+        const int cur = kk & 1;
+        fence();
+        if (kk < 3) {
+#pragma unroll
+          for (int tb = 0; tb < 4; ++tb) {
+            wa[cur ^ 1][tb] = lds8(&sm.w[(16 * tb + li) * PW + 32 * (kk + 1) + 8 * lg]);
+            qa[cur ^ 1][tb] = ld_row_qk(sm.q, 16 * tb, kk + 1, ln);
+          }
+        }
+        fence();
         bf16x8 sb[NB];
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) sb[nb] = pair_operand(sacc[2 * kk][nb], sacc[2 * kk + 1][nb]);
 #pragma unroll
-        for (int tb = 0; tb < 4; ++tb) {
-          const bf16x8 wa = lds8(&sm.w[(16 * tb + li) * PW + 32 * kk + 8 * lg]);
-          const bf16x8 qa = ld_row_qk(sm.q, 16 * tb, kk, ln);
+        for (int tb = 0; tb < 4; ++tb)
 #pragma unroll
           for (int nb = 0; nb < NB; ++nb) {
-            uacc[tb][nb] = mfma(wa, sb[nb], uacc[tb][nb]);  // U = U~ - W S
-            oacc[tb][nb] = mfma(qa, sb[nb], oacc[tb][nb]);  // Q S
+            uacc[tb][nb] = mfma(wa[cur][tb], sb[nb], uacc[tb][nb]);  // U = U~ - W S
+            oacc[tb][nb] = mfma(qa[cur][tb], sb[nb], oacc[tb][nb]);  // Q S
           }
-        }
       }
+      fence();
+      // P rows, read while U is scaled
+      bf16x8 pa[6];
+#pragma unroll
+      for (int tb = 0, e = 0; tb < 4; ++tb)
+#pragma unroll
+        for (int kk = 0; kk <= (tb >> 1); ++kk, ++e) pa[e] = lds8(&sm.p[(16 * tb + li) * PP + 32 * kk + 8 * lg]);
+      fence();
       bf16x8 ub[2][NB], upb[2][NB];
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
@@ -532,28 +622,44 @@ __global__ __launch_bounds__(NT) void chunk_scan_kernel(ScanArgs a, SeqOrder ord
           oacc[2 * kk + 1][nb] *= e1;
         }
       }
-      // O += P U
+      fence();
+      // O += P U, while the K^T operands of the first half of the state update arrive
+      bf16x8 kt[8];
 #pragma unroll
-      for (int tb = 0; tb < 4; ++tb)
+      for (int db = 0; db < 8; ++db) kt[db] = ld_tr_qk(sm.k, db, 0, ln);
+      fence();
 #pragma unroll
-        for (int kk = 0; kk <= (tb >> 1); ++kk) {
-          const bf16x8 pa = lds8(&sm.p[(16 * tb + li) * PP + 32 * kk + 8 * lg]);
+      for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-          for (int nb = 0; nb < NB; ++nb) oacc[tb][nb] = mfma(pa, ub[kk][nb], oacc[tb][nb]);
-        }
-      // S <- Gamma_c S + K^T U'
+        for (int tb = 2 * kk; tb < 4; ++tb)
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb)
+            oacc[tb][nb] = mfma(pa[kk == 0 ? (tb < 2 ? tb : 2 * tb - 2) : 2 * tb - 1], ub[kk][nb], oacc[tb][nb]);
+      // S <- Gamma_c S + K^T U', tokens 0..31 then 32..63; the second half's
+      // operands are read during the first half's products
       const float gc = sm.eg[BT - 1];
 #pragma unroll
-      for (int db = 0; db < 8; ++db)
+      for (int kk = 0; kk < 2; ++kk) {
+        bf16x8 kn[8];
+        fence();
+        if (kk == 0) {
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-          const bf16x8 ka = ld_tr_qk(sm.k, db, kk, ln);
+          for (int db = 0; db < 8; ++db) kn[db] = ld_tr_qk(sm.k, db, 1, ln);
+        }
+        fence();
+#pragma unroll
+        for (int db = 0; db < 8; ++db)
 #pragma unroll
           for (int nb = 0; nb < NB; ++nb) {
             if (kk == 0) sacc[db][nb] *= gc;
-            sacc[db][nb] = mfma(ka, upb[kk][nb], sacc[db][nb]);
+            sacc[db][nb] = mfma(kt[db], upb[kk][nb], sacc[db][nb]);
           }
+        if (kk == 0) {
+#pragma unroll
+          for (int db = 0; db < 8; ++db) kt[db] = kn[db];
         }
+      }
+      fence();
       // O: through the wave's LDS tile [n][t] to 16-byte row stores
       uint16_t* ot = &sm.v[wv * 32 * PO];
 #pragma unroll
