@@ -22,10 +22,13 @@ namespace {
 
 template <bool BF16>
 struct Act8 {
+  // NT: non-temporal access (the activations stream through once)
+  template <bool NT = false>
   static __device__ __forceinline__ void load(const void* base, int64_t idx, float v[8]) {
     if constexpr (BF16) {
-      uint4 u = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(base) + idx);
-      uint32_t w[4] = {u.x, u.y, u.z, u.w};
+      const u32x4* p = reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(base) + idx);
+      const u32x4 u = NT ? __builtin_nontemporal_load(p) : *p;
+      uint32_t w[4] = {u[0], u[1], u[2], u[3]};
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         v[2 * i] = __uint_as_float(w[i] << 16);
@@ -38,13 +41,15 @@ struct Act8 {
       v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
     }
   }
+  template <bool NT = false>
   static __device__ __forceinline__ void store(void* base, int64_t idx, const float v[8]) {
     if constexpr (BF16) {
-      uint32_t w[4];
+      u32x4 w;
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        w[i] = (uint32_t)f32_to_bf16_bits(v[2 * i]) | ((uint32_t)f32_to_bf16_bits(v[2 * i + 1]) << 16);
-      *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(base) + idx) = make_uint4(w[0], w[1], w[2], w[3]);
+      for (int i = 0; i < 4; ++i) w[i] = pack_bf16x2(v[2 * i], v[2 * i + 1]);
+      u32x4* p = reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(base) + idx);
+      if (NT) __builtin_nontemporal_store(w, p);
+      else *p = w;
     } else {
       float4* p = reinterpret_cast<float4*>(reinterpret_cast<float*>(base) + idx);
       p[0] = make_float4(v[0], v[1], v[2], v[3]);
@@ -53,7 +58,8 @@ struct Act8 {
   }
 };
 
-// 8 raw elements (bit-exact copies of the conv state).
+// 8 raw elements (bit-exact copies of the conv state, and the rows in flight
+// of the conv kernel).
 template <bool BF16>
 struct Raw8 {
   uint4 u[BF16 ? 1 : 2];
@@ -66,6 +72,31 @@ struct Raw8 {
     uint4* q = reinterpret_cast<uint4*>(p);
 #pragma unroll
     for (int i = 0; i < (BF16 ? 1 : 2); ++i) q[i] = u[i];
+  }
+  // non-temporal load of activation row elements [idx, idx + 8)
+  __device__ __forceinline__ void load_stream(const void* base, int64_t idx) {
+    const u32x4* q = reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(base) + idx * (BF16 ? 2 : 4));
+#pragma unroll
+    for (int i = 0; i < (BF16 ? 1 : 2); ++i) {
+      const u32x4 v = __builtin_nontemporal_load(q + i);
+      u[i] = make_uint4(v[0], v[1], v[2], v[3]);
+    }
+  }
+  __device__ __forceinline__ void to_f32(float v[8]) const {
+    if constexpr (BF16) {
+      const uint32_t w[4] = {u[0].x, u[0].y, u[0].z, u[0].w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        v[2 * i] = __uint_as_float(w[i] << 16);
+        v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        v[4 * i] = __uint_as_float(u[i].x); v[4 * i + 1] = __uint_as_float(u[i].y);
+        v[4 * i + 2] = __uint_as_float(u[i].z); v[4 * i + 3] = __uint_as_float(u[i].w);
+      }
+    }
   }
 };
 
@@ -104,61 +135,71 @@ __global__ __launch_bounds__(256) void conv_silu_norm_kernel(ConvArgs a) {
 
   int s = find_seq(a.cu, a.num_seqs, r_begin);
   int seq_begin = a.cu[s], seq_end = a.cu[s + 1];
-  float win[W > 1 ? W - 1 : 1][8];
   bool fresh = true;
-  for (int r = r_begin; r < r_end; ++r) {
-    while (r >= seq_end && s < a.num_seqs - 1) {
-      ++s;
-      seq_begin = seq_end;
-      seq_end = a.cu[s + 1];
-      fresh = true;
-    }
-    if constexpr (W > 1) {
-      if (fresh) {
-        const bool act = seq_active(a.read_idx, a.write_idx, s, a.num_blocks);
-        const char* tail = a.conv_pool + (act ? (int64_t)a.read_idx[s] * a.conv_stride : 0);
-        const int pos = r - seq_begin;
+  // LA rows of x in flight per thread (row r is loaded LA rows ahead of its
+  // use), and the inputs of rows r-LA+1..r in a circular buffer indexed by
+  // r mod LA; r_begin is a multiple of LA, so every index is static.
+  constexpr int LA = 4;
+  static_assert(W <= LA, "window must fit the buffer");
+  Raw8<BF16> ring[LA];
+  float xr[LA][8];
 #pragma unroll
-        for (int j = 0; j < W - 1; ++j) {
-          const int p = pos - (W - 1) + j;
+  for (int k = 0; k < LA; ++k) {
 #pragma unroll
-          for (int e = 0; e < 8; ++e) win[j][e] = 0.f;
-          if (!cok) continue;
-          if (p >= 0)
-            Act8<BF16>::load(a.x, (int64_t)(seq_begin + p) * a.channels + c0, win[j]);
-          else if (act)
-            Act8<BF16>::load(tail, ((int64_t)(W - 1 + p) * a.channels + c0), win[j]);
+    for (int e = 0; e < 8; ++e) xr[k][e] = 0.f;
+    if (cok && r_begin + k < r_end) ring[k].load_stream(a.x, (int64_t)(r_begin + k) * a.channels + c0);
+  }
+  for (int rb = r_begin; rb < r_end; rb += LA) {
+#pragma unroll
+    for (int k = 0; k < LA; ++k) {
+      const int r = rb + k;
+      if (r >= r_end) break;
+      while (r >= seq_end && s < a.num_seqs - 1) {
+        ++s;
+        seq_begin = seq_end;
+        seq_end = a.cu[s + 1];
+        fresh = true;
+      }
+      if constexpr (W > 1) {
+        if (fresh) {  // the W-1 inputs before row r: earlier rows of the sequence, else its conv state
+          const bool act = seq_active(a.read_idx, a.write_idx, s, a.num_blocks);
+          const char* tail = a.conv_pool + (act ? (int64_t)a.read_idx[s] * a.conv_stride : 0);
+          const int pos = r - seq_begin;
+#pragma unroll
+          for (int j = 1; j < W; ++j) {
+            float* dst = xr[(k - j + LA) % LA];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) dst[e] = 0.f;
+            if (!cok) continue;
+            const int p = pos - j;
+            if (p >= 0)
+              Act8<BF16>::load(a.x, (int64_t)(seq_begin + p) * a.channels + c0, dst);
+            else if (act)
+              Act8<BF16>::load(tail, ((int64_t)(W - 1 + p) * a.channels + c0), dst);
+          }
         }
       }
+      fresh = false;
+      if (cok) ring[k].to_f32(xr[k]);
+      if (cok && r + LA < r_end) ring[k].load_stream(a.x, (int64_t)(r + LA) * a.channels + c0);
+      float yv[8];
+      float ss = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        float acc = wt[e][W - 1] * xr[k][e];
+#pragma unroll
+        for (int j = 1; j < W; ++j) acc += wt[e][W - 1 - j] * xr[(k - j + LA) % LA][e];
+        yv[e] = silu(acc);
+        ss += yv[e] * yv[e];
+      }
+      for (int off = 1; off < group; off <<= 1) ss += __shfl_xor(ss, off);
+      if (do_norm) {
+        const float inv = scale * rsqrt_fast(ss + a.eps);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) yv[e] *= inv;
+      }
+      if (cok) Act8<BF16>::template store<true>(a.y, (int64_t)r * a.channels + c0, yv);
     }
-    fresh = false;
-    float xin[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    if (cok) Act8<BF16>::load(a.x, (int64_t)r * a.channels + c0, xin);
-    float yv[8];
-    float ss = 0.f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      float acc = wt[e][W - 1] * xin[e];
-#pragma unroll
-      for (int j = 0; j < W - 1; ++j) acc += wt[e][j] * win[j][e];
-      yv[e] = silu(acc);
-      ss += yv[e] * yv[e];
-    }
-    if constexpr (W > 1) {
-#pragma unroll
-      for (int j = 0; j < W - 2; ++j)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) win[j][e] = win[j + 1][e];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) win[W - 2][e] = xin[e];
-    }
-    for (int off = 1; off < group; off <<= 1) ss += __shfl_xor(ss, off);
-    if (do_norm) {
-      const float inv = scale / sqrtf(ss + a.eps);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) yv[e] *= inv;
-    }
-    if (cok) Act8<BF16>::store(a.y, (int64_t)r * a.channels + c0, yv);
   }
   (void)ESZ;
 }

@@ -52,7 +52,11 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-__device__ __forceinline__ float silu(float v) { return v / (1.0f + __expf(-v)); }
+// SiLU with the hardware reciprocal (about 1 ulp) instead of an IEEE division.
+__device__ __forceinline__ float silu(float v) { return v * __builtin_amdgcn_rcpf(1.0f + __expf(-v)); }
+
+// 1 / sqrt(x) with the hardware reciprocal square root (about 1 ulp), x > 0.
+__device__ __forceinline__ float rsqrt_fast(float x) { return __builtin_amdgcn_rsqf(x); }
 
 // A sequence takes part in a call when it has a write block inside the pool and
 // a read block inside the pool; anything else is skipped without memory access.

@@ -53,22 +53,34 @@ __device__ __forceinline__ void st4(void* base, int64_t i, float4 v) {
   }
 }
 
+// The state is read once and written once per call: non-temporal accesses
+// keep it from displacing cached data.
+__device__ __forceinline__ float4 ld_stream(const float* p) {
+  const f32x4 v = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
+  return make_float4(v[0], v[1], v[2], v[3]);
+}
+__device__ __forceinline__ void st_stream(float* p, float4 v) {
+  const f32x4 w = {v.x, v.y, v.z, v.w};
+  __builtin_nontemporal_store(w, reinterpret_cast<f32x4*>(p));
+}
+
 __device__ __forceinline__ float4 f4_fma(float a, float4 x, float4 y) {
   return make_float4(fmaf(a, x.x, y.x), fmaf(a, x.y, y.y), fmaf(a, x.z, y.z), fmaf(a, x.w, y.w));
 }
 
-template <bool BF16, int DK, int DV>
+template <bool BF16, int DK, int DV, int DVS>
 __global__ __launch_bounds__(256) void recurrent_kernel(ScanArgs a) {
   constexpr int NT = 256;
-  constexpr int C4 = DV / 4;          // threads across one state row
+  constexpr int C4 = DVS / 4;         // threads across the workgroup's part of a state row
   constexpr int RG = NT / C4;         // row groups
   constexpr int RPT = (DK + RG - 1) / RG;
   constexpr int NW = NT / 64;
-  constexpr int NCH = 2 * DK + DV;    // conv channels this head reads: q, k of its key head, its v
+  constexpr int NCH = 2 * DK + DVS;   // conv channels read: q, k of the key head, this part of v
   static_assert(C4 <= 64 && (64 % C4) == 0, "row group must fit a wave");
   static_assert(NCH <= 2 * NT, "two channels per thread at most");
 
   const int s = blockIdx.x, m = blockIdx.y;
+  const int n0 = DVS * blockIdx.z;  // this workgroup's d_v columns [n0, n0 + DVS)
   if (s >= a.num_seqs) return;
   const int r0 = a.cu[s];
   const int L = a.cu[s + 1] - r0;
@@ -78,7 +90,7 @@ __global__ __launch_bounds__(256) void recurrent_kernel(ScanArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int c4 = tid % C4, rg = tid / C4;
   const int h = m / (a.num_v_heads / a.num_k_heads);
-  const int64_t head_off = (int64_t)m * DK * DV;
+  const int64_t head_off = (int64_t)m * DK * DV + n0;
   const float* S0 = reinterpret_cast<const float*>(
       reinterpret_cast<const char*>(a.ssm_pool) + (int64_t)a.read_idx[s] * a.ssm_stride) + head_off;
   float* S1 = reinterpret_cast<float*>(
@@ -88,7 +100,7 @@ __global__ __launch_bounds__(256) void recurrent_kernel(ScanArgs a) {
 #pragma unroll
   for (int i = 0; i < RPT; ++i) {
     const int row = rg + RG * i;
-    S[i] = row < DK ? *reinterpret_cast<const float4*>(S0 + row * DV + c4 * 4) : make_float4(0.f, 0.f, 0.f, 0.f);
+    S[i] = row < DK ? ld_stream(S0 + row * DV + c4 * 4) : make_float4(0.f, 0.f, 0.f, 0.f);
   }
 
   // conv channels owned by this thread (index i into [q | k | v] of this head)
@@ -104,7 +116,7 @@ __global__ __launch_bounds__(256) void recurrent_kernel(ScanArgs a) {
     has[e] = i < NCH && L > 0;  // an empty sequence reads no input at all
     gch[e] = i < DK ? (int64_t)h * DK + i
            : i < 2 * DK ? (int64_t)a.num_k_heads * DK + h * DK + (i - DK)
-                        : 2 * (int64_t)a.num_k_heads * DK + (int64_t)m * DV + (i - 2 * DK);
+                        : 2 * (int64_t)a.num_k_heads * DK + (int64_t)m * DV + n0 + (i - 2 * DK);
 #pragma unroll
     for (int j = 0; j < 4; ++j) wt[e][j] = (has[e] && j < W) ? ld1<BF16>(a.w, gch[e] * W + j) : 0.f;
 #pragma unroll
@@ -116,7 +128,7 @@ __global__ __launch_bounds__(256) void recurrent_kernel(ScanArgs a) {
   }
 
   __shared__ __align__(16) float sy[NCH];
-  __shared__ __align__(16) float red[NW][2 * DV + 4];
+  __shared__ __align__(16) float red[NW][2 * DVS + 4];
 
   for (int t = 0; t < L; ++t) {
     const int64_t r = r0 + t;
@@ -167,11 +179,11 @@ __global__ __launch_bounds__(256) void recurrent_kernel(ScanArgs a) {
     }
     if (lane < C4) {
       *reinterpret_cast<float4*>(&red[wave][c4 * 4]) = kS;
-      *reinterpret_cast<float4*>(&red[wave][DV + c4 * 4]) = Sq;
+      *reinterpret_cast<float4*>(&red[wave][DVS + c4 * 4]) = Sq;
       if (c4 == 0) {
-        red[wave][2 * DV] = kq;
-        red[wave][2 * DV + 1] = kk;
-        red[wave][2 * DV + 2] = qq;
+        red[wave][2 * DVS] = kq;
+        red[wave][2 * DVS + 1] = kk;
+        red[wave][2 * DVS + 2] = qq;
       }
     }
     __syncthreads();
@@ -181,16 +193,16 @@ __global__ __launch_bounds__(256) void recurrent_kernel(ScanArgs a) {
 #pragma unroll
     for (int w = 0; w < NW; ++w) {
       const float4 x = *reinterpret_cast<const float4*>(&red[w][c4 * 4]);
-      const float4 y = *reinterpret_cast<const float4*>(&red[w][DV + c4 * 4]);
+      const float4 y = *reinterpret_cast<const float4*>(&red[w][DVS + c4 * 4]);
       kS.x += x.x; kS.y += x.y; kS.z += x.z; kS.w += x.w;
       Sq.x += y.x; Sq.y += y.y; Sq.z += y.z; Sq.w += y.w;
-      kq += red[w][2 * DV];
-      kk += red[w][2 * DV + 1];
-      qq += red[w][2 * DV + 2];
+      kq += red[w][2 * DVS];
+      kk += red[w][2 * DVS + 1];
+      qq += red[w][2 * DVS + 2];
     }
     // normalisation folded in: k_hat = k / sqrt(|k|^2 + eps), q_hat = q_scale q / sqrt(|q|^2 + eps)
-    const float ik = 1.0f / sqrtf(kk + a.eps);
-    const float iq = a.q_scale / sqrtf(qq + a.eps);
+    const float ik = rsqrt_fast(kk + a.eps);
+    const float iq = a.q_scale * rsqrt_fast(qq + a.eps);
     const float av = __expf(gv);
     const float4 v = *reinterpret_cast<const float4*>(&sy[2 * DK + c4 * 4]);
     float4 u;
@@ -210,7 +222,7 @@ __global__ __launch_bounds__(256) void recurrent_kernel(ScanArgs a) {
       float4 o;
       o.x = fmaf(aq, Sq.x, kqn * u.x); o.y = fmaf(aq, Sq.y, kqn * u.y);
       o.z = fmaf(aq, Sq.z, kqn * u.z); o.w = fmaf(aq, Sq.w, kqn * u.w);
-      st4<BF16>(a.out, (r * a.num_v_heads + m) * DV + c4 * 4, o);
+      st4<BF16>(a.out, (r * a.num_v_heads + m) * DV + n0 + c4 * 4, o);
     }
     __syncthreads();
   }
@@ -218,14 +230,18 @@ __global__ __launch_bounds__(256) void recurrent_kernel(ScanArgs a) {
 #pragma unroll
   for (int i = 0; i < RPT; ++i) {
     const int row = rg + RG * i;
-    if (row < DK) *reinterpret_cast<float4*>(S1 + row * DV + c4 * 4) = S[i];
+    if (row < DK) st_stream(S1 + row * DV + c4 * 4, S[i]);
   }
 }
 
+// d_v is split over DV / DVS workgroups per (sequence, head): the columns of S
+// evolve independently, so each part needs only q, k and its own columns of v;
+// smaller parts leave more workgroups resident to cover the state's memory latency.
 template <bool BF16, int DK, int DV>
 hipError_t rec_dispatch(const ScanArgs& a, hipStream_t st) {
-  dim3 grid(a.num_seqs, a.num_v_heads);
-  hipLaunchKernelGGL((recurrent_kernel<BF16, DK, DV>), grid, dim3(256), 0, st, a);
+  constexpr int DVS = DV;
+  dim3 grid(a.num_seqs, a.num_v_heads, DV / DVS);
+  hipLaunchKernelGGL((recurrent_kernel<BF16, DK, DV, DVS>), grid, dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
