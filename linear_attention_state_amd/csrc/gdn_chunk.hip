@@ -18,31 +18,38 @@
 // Work split: one 512-thread workgroup (8 waves, two per SIMD) per (sequence,
 // value head), walking the sequence's chunks as a software pipeline with one
 // workgroup barrier per step.  In step i:
-//   waves 0-3 (state)   chunk i: wave w owns d_v columns [32w, 32w+32) of the
-//                       128 x 128 fp32 state, in registers; it computes K S,
-//                       (Q S)^T, U, O^T and the state update for its columns;
-//   wave 4 (gram)       chunk i+2: the Gram products and A from K rows loaded
-//                       straight into registers, then fp32 forward
-//                       substitution on the four 16x16 diagonal blocks of T;
-//   wave 5 (blocks)     chunk i+1: the blocks of T below the diagonal by block
-//                       products (two levels), written as T2^T;
-//   waves 6-7 (stage)   chunk i+1: Q and K rows into LDS for the state waves,
-//                       P = M o Q K^T, e^gamma and e^(gamma_c - gamma).
-// Every producer writes a buffer its consumer reads one or two steps later
-// (double-buffered Q/K/P, triple-buffered T2), so the only synchronisation is
-// the barrier that ends each step.  Each wave loads its next chunk's inputs
-// into registers one step ahead; global pointers are address space 1 and the
-// barriers wait for LDS traffic only, so those loads and the output stores stay
-// in flight across them.  All products are v_mfma_f32_16x16x32_bf16 (bf16
-// operands, fp32 accumulate).  Sequences are launched longest first.
+//   waves 0-3 (state)  chunk i: wave w owns d_v columns [32w, 32w+32) of the
+//                      128 x 128 fp32 state, in registers; it computes K S,
+//                      (Q S)^T, U, O^T and the state update for its columns;
+//   wave 4 (gram)      chunk i+2: the Gram products and A from K rows loaded
+//                      straight into registers, then fp32 forward
+//                      substitution on the four 16x16 diagonal blocks of T;
+//   wave 5 (blocks)    chunk i+1: the blocks of T below the diagonal by block
+//                      products (two levels), written as T2^T;
+//   wave 6 (loads)     chunk i+1: Q, K and V rows copied from global memory
+//                      straight into LDS (no registers), whole rows per load;
+//   wave 7 (decay)     chunk i: P = M o Q K^T for the state waves, which wait
+//                      for it on an LDS flag before they use it; chunk i+1:
+//                      gamma, e^gamma and e^(gamma_c - gamma).
+// Every other producer writes buffers its consumers read one or two steps
+// later (double-buffered Q/K/V, triple-buffered T2), so the barrier that ends
+// each step is the only other synchronisation.  Global pointers are address
+// space 1 and the barriers wait for LDS traffic only, so loads and the output
+// stores stay in flight across them.  All products are
+// v_mfma_f32_16x16x32_bf16 (bf16 operands, fp32 accumulate).  Sequences are
+// launched longest first.
 //
 // MFMA 16x16x32 bf16 operand layout (lane l, r = l & 15, grp = l >> 4):
 //   A: row r, 8 values of k;  B: column r, the same 8 values of k;
 //   D: column r, rows 4*grp + {0,1,2,3}.
 // The MFMA sums over k, so any k order shared by both operands gives the same
-// product; "permuted" operands below take k = {4grp..4grp+3, 16+4grp..16+4grp+3}
-// of each 32-wide step, which is what a D tile pair holds.  A D tile X can be
-// used as the B operand X or as the A operand X^T of a later product.
+// product.  A D tile X can be used as the B operand X or as the A operand X^T
+// of a later product; a pair of D tiles (row blocks 2kk and 2kk+1) is then an
+// operand over the 32 k values {4grp..4grp+3, 16+4grp..16+4grp+3} of step kk
+// ("pair order").  The state rows are kept in registers relabelled so that
+// pair order over d is natural order over the columns of K and Q: register
+// row d = 32kk + 16h + 4g + i holds state row sigma(d) = 32kk + 8g + 4h + i.
+// K and Q rows can then stay in natural column order in LDS.
 #include "gdn_device.h"
 
 namespace gdn {
@@ -55,28 +62,32 @@ constexpr int NT = 512;           // threads per workgroup (8 waves)
 constexpr int NB = D / 16 / NS;   // 16-column state tiles per state wave
 constexpr int PP = BT + 8;        // pitch of the P rows
 constexpr int PX = BT + 16;       // pitch of the transposed 64 x 64 tiles
+constexpr int PB = 16;            // pitch of a 16 x 16 block
 constexpr int PA = 20;            // fp32 pitch of the transposed diagonal blocks of A
 constexpr int PS = D + 4;         // fp32 pitch of the state staged in LDS (start and end)
 
-// LDS.  "k-permuted" rows store element d of each 32-wide group at
-// 8*((d>>2)&3) + 4*((d>>4)&1) + (d&3): the 8 values an operand lane needs
-// (k = 4g..4g+3 and 16+4g..16+4g+3 of the group) are then one 16-byte read.
+// LDS.  The [64][128] bf16 tiles keep natural row-major order with the 16-byte
+// chunk c of row t stored at chunk c ^ f(t), f(t) = 2 (t & 7) + ((t >> 3) & 1):
+// the 16 rows of a row-operand read, and the 16 rows of a transposed read, then
+// fall on distinct banks.
 struct ChunkBuf {
-  uint16_t q[BT * D];         // Q rows [t][perm d], 16-byte chunks XOR-swizzled by row
-  uint16_t k[BT * D];         // K rows, same layout
-  uint16_t p[BT * PP];        // P = M o Q K^T, [t][perm j]; blocks above the diagonal stay zero
+  uint16_t q[BT * D];
+  uint16_t k[BT * D];
+  uint16_t v[BT * D];
+  float gam[BT];              // running sum of g
   float eg[BT];               // e^gamma
   float ed[BT];               // e^(gamma_last - gamma)
 };
 struct alignas(16) Smem {
-  ChunkBuf cb[2];             // chunk i & 1: written by the stage waves, read by the state waves
+  ChunkBuf cb[2];             // chunk i & 1: written by waves 6-7, read by the state waves and wave 7
+  uint16_t p[BT * PP];        // P of chunk i, [t][j in pair order]; blocks above the diagonal stay zero
   uint16_t t2t[3][BT * PX];   // (T diag(b))^T [j][t], chunk i % 3; blocks above the diagonal stay zero
-  uint16_t abt[2][BT * PX];   // A^T, blocks below the diagonal (gram wave -> blocks wave)
-  uint16_t tt[2][BT * PX];    // T^T: diagonal blocks (gram wave) and T10, T32 (blocks wave)
+  uint16_t ab[2][6][16 * PB]; // A^T blocks below the diagonal (gram wave -> blocks wave)
+  uint16_t tb[2][5][16 * PB]; // T^T blocks 00, 11, 22, 33 (gram wave) and 32 (blocks wave)
   float at[4 * 16 * PA];      // diagonal blocks of A, fp32, [block][j][t] (gram wave only)
   float bsc[2][BT];           // beta of the chunk (gram wave -> blocks wave)
   float gw[BT];               // gamma, gram wave
-  float gs[2][BT];            // gamma, stage waves
+  int pflag;                  // steps whose P is complete
 };
 static_assert(sizeof(Smem) <= 160 * 1024, "LDS");
 static_assert(D * PS * 4 <= sizeof(ChunkBuf) * 2, "state staging");
@@ -148,7 +159,7 @@ __device__ __forceinline__ bf16x4 to_bf16x4(f32x4 v) {
 }
 
 // two accumulator tiles (rows 4g+i of 16-row blocks 2kk and 2kk+1) as one
-// k-permuted operand over those 32 rows
+// operand over those 32 rows in pair order
 __device__ __forceinline__ bf16x8 pair_operand(f32x4 lo, f32x4 hi) {
   bf16x8 v;
 #pragma unroll
@@ -159,46 +170,23 @@ __device__ __forceinline__ bf16x8 pair_operand(f32x4 lo, f32x4 hi) {
   return v;
 }
 
-// stored position of natural index d in a k-permuted row
+// position of index j of P's rows in pair order: j = 32kk + 4g + i -> 32kk + 8g + i and
+// j = 32kk + 16 + 4g + i -> 32kk + 8g + 4 + i, so the 8 values a lane needs are one
+// 16-byte read
 __device__ __forceinline__ constexpr int perm(int d) {
   return (d & ~31) | ((d & 12) << 1) | ((d & 16) >> 2) | (d & 3);
 }
 
-// element offset of (row t, stored position pos) in a swizzled [64][128] tile:
-// 16-byte chunk c of row t sits at chunk c ^ (2 (t & 7) + ((t >> 3) & 1)).  The
-// 16 rows of a row-operand read and the 8 rows x 32 bytes of each half of a
-// transposed read then fall on distinct banks.
-__device__ __forceinline__ int swz_off(int t, int pos) {
-  const int f = 2 * (t & 7) + ((t >> 3) & 1);
-  return t * D + (((pos >> 3) ^ f) << 3) + (pos & 7);
-}
+// element offset of (row t, column c) in a swizzled [64][128] tile: 16-byte
+// chunk c >> 3 of row t sits at chunk (c >> 3) ^ (2 (t & 7) + ((t >> 3) & 1)).
+__device__ __forceinline__ constexpr int swz_f(int t) { return 2 * (t & 7) + ((t >> 3) & 1); }
+__device__ __forceinline__ int swz_off(int t, int c) { return t * D + (((c >> 3) ^ swz_f(t)) << 3) + (c & 7); }
 
 // Operand lanes: r = l & 15, g = l >> 4; as a transposed-read source, lane l
 // supplies row i = (l >> 2) & 3 and column group a = l & 3.
 struct Lane {
   int r, g, a, i;
 };
-
-// rows t0 + r of a swizzled Q / K tile, k = d of 32-group kk (permuted)
-__device__ __forceinline__ bf16x8 ld_row_qk(const uint16_t* base, int t0, int kk, const Lane& L) {
-  return lds8(base + swz_off(t0 + L.r, 32 * kk + 8 * L.g));
-}
-
-// K^T operand from the swizzled K tile: lane gets K[t][16 db + r] for the
-// permuted token set t = 32 kk + {4g..4g+3, 16+4g..16+4g+3}
-__device__ __forceinline__ bf16x8 ld_tr_qk(const uint16_t* base, int db, int kk, const Lane& L) {
-  const int pos = perm(16 * db + 4 * L.a);
-  const int t = 32 * kk + 4 * L.g + L.i;
-  return cat(ldtr(base + swz_off(t, pos)), ldtr(base + swz_off(t + 16, pos)));
-}
-
-// transposed operand from a row-major [j][c] tile of pitch P: lane gets
-// X[j][c0 + r] for the permuted set j = 32 kk + {4g..4g+3, 16+4g..16+4g+3}
-template <int P>
-__device__ __forceinline__ bf16x8 ld_tr(const uint16_t* base, int c0, int kk, const Lane& L) {
-  const uint16_t* p = base + (32 * kk + 4 * L.g + L.i) * P + c0 + 4 * L.a;
-  return cat(ldtr(p), ldtr(p + 16 * P));
-}
 
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
@@ -216,31 +204,15 @@ __device__ __forceinline__ Blk ld_blk_g(__amdgpu_buffer_rsrc_t rs, int C, int co
         bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rs, 2 * ((16 * b + L.r) * C + col + 32 * kk + 8 * L.g), 0, 0));
   return x;
 }
-// D[row][col] = sum_d X[row][d] Y[col][d] over two 16-row blocks
-__device__ __forceinline__ f32x4 dot_blk(const Blk& x, const Blk& y) {
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int kk = 0; kk < 4; ++kk) acc = mfma(x.v[kk], y.v[kk], acc);
-  return acc;
-}
-// A register block (natural order) into rows 16b.. of a swizzled k-permuted tile:
-// the 8 values d = 32kk + 8g .. +7 land at perm(32kk + 8g) and perm(32kk + 8g + 4).
-__device__ __forceinline__ void stage_blk(uint16_t* tile, const Blk& x, int b, const Lane& L) {
-  const int t = 16 * b + L.r;
-#pragma unroll
-  for (int kk = 0; kk < 4; ++kk) {
-    const u32x4 w = __builtin_bit_cast(u32x4, x.v[kk]);
-    const int p0 = 32 * kk + 16 * (L.g & 1) + 4 * (L.g >> 1);
-    *reinterpret_cast<uint2*>(&tile[swz_off(t, p0)]) = make_uint2(w[0], w[1]);
-    *reinterpret_cast<uint2*>(&tile[swz_off(t, p0 + 8)]) = make_uint2(w[2], w[3]);
-  }
-}
+
+// Blocks below the diagonal, stored as 16 x 16 tiles: slot of block (R, C), R > C
+__device__ __forceinline__ constexpr int low_slot(int R, int C) { return R * (R - 1) / 2 + C; }
 
 // Block (bi, bj), bj <= bi, of A = strictly-lower(b_t e^{gamma_t - gamma_j} K K^T)
 // from acc = K_bi K_bj^T: lane holds A[t = 16bi + 4g + i][j = 16bj + r].
-// Diagonal blocks go to `at` in fp32, the others to `abt` in bf16, both transposed.
-__device__ __forceinline__ void put_a(float* at, uint16_t* abt, const float* gam, const float* beta, int bi, int bj,
-                                      f32x4 acc, const Lane& L) {
+// Diagonal blocks go to `at` in fp32, the others to `ab` in bf16, both transposed.
+__device__ __forceinline__ void put_a(float* at, uint16_t (*ab)[16 * PB], const float* gam, const float* beta, int bi,
+                                      int bj, f32x4 acc, const Lane& L) {
   const int j = 16 * bj + L.r;
   const float gj = gam[j];
   const f32x4 gt = *reinterpret_cast<const f32x4*>(&gam[16 * bi + 4 * L.g]);
@@ -254,7 +226,7 @@ __device__ __forceinline__ void put_a(float* at, uint16_t* abt, const float* gam
   if (bi == bj)
     *reinterpret_cast<float4*>(&at[(16 * bi + L.r) * PA + 4 * L.g]) = make_float4(v[0], v[1], v[2], v[3]);
   else
-    st4bf(&abt[j * PX + 16 * bi + 4 * L.g], v[0], v[1], v[2], v[3]);
+    st4bf(&ab[low_slot(bi, bj)][L.r * PB + 4 * L.g], v[0], v[1], v[2], v[3]);
 }
 
 // Block (bi, bj), bj <= bi, of P = M o Q K^T from acc = K_bj Q_bi^T (transposed):
@@ -272,31 +244,28 @@ __device__ __forceinline__ void put_p(uint16_t* p, const float* gam, int bi, int
   st4bf(&p[t * PP + perm(16 * bj + 4 * L.g)], v[0], v[1], v[2], v[3]);
 }
 
-// Column c of T's block (R, C) in a lane's D tile (rows 4g + i) -> T2^T (column
-// scaled by beta) and, for blocks a later product reads, T^T.
-__device__ __forceinline__ void put_t(uint16_t* tt, uint16_t* t2, const float* beta, int R, int C, f32x4 tv,
-                                      bool keep, const Lane& L) {
-  const int jc = 16 * C + L.r;
-  const int o = jc * PX + 16 * R + 4 * L.g;
-  const float s = beta[jc];
-  if (keep) st4bf(&tt[o], tv[0], tv[1], tv[2], tv[3]);
-  st4bf(&t2[o], s * tv[0], s * tv[1], s * tv[2], s * tv[3]);
+// 16x16x16 operands of the block products from transposed 16 x 16 tiles xt = X^T:
+// A: lane gets X[r][4g..4g+3];  B: lane gets X[4g..4g+3][r]
+__device__ __forceinline__ bf16x4 blk_a(const uint16_t* xt, const Lane& L) {
+  return ldtr(xt + (4 * L.g + L.i) * PB + 4 * L.a);
 }
+__device__ __forceinline__ bf16x4 blk_b(const uint16_t* xt, const Lane& L) { return lds4(xt + L.r * PB + 4 * L.g); }
 
-// 16x16x16 operands of the block products, from the transposed tiles:
-// A rows 16R + r, k = 16C + 4g + i (lane gets X[16R + r][16C + 4g..+3])
-__device__ __forceinline__ bf16x4 blk_a(const uint16_t* xt, int R, int C, const Lane& L) {
-  return ldtr(xt + (16 * C + 4 * L.g + L.i) * PX + 16 * R + 4 * L.a);
-}
-// B k = 16R + 4g + i, column 16C + r (lane gets X[16R + 4g..+3][16C + r])
-__device__ __forceinline__ bf16x4 blk_b(const uint16_t* xt, int R, int C, const Lane& L) {
-  return lds4(xt + (16 * C + L.r) * PX + 16 * R + 4 * L.g);
+// Column c of T's block (R, C) in a lane's D tile (rows 4g + i) -> T2^T (column
+// scaled by beta) and, when a later product reads it, the T^T tile `keep`.
+__device__ __forceinline__ void put_t(uint16_t* keep, uint16_t* t2, const float* beta, int R, int C, f32x4 tv,
+                                      const Lane& L) {
+  const int jc = 16 * C + L.r;
+  const float s = beta[jc];
+  if (keep) st4bf(&keep[L.r * PB + 4 * L.g], tv[0], tv[1], tv[2], tv[3]);
+  st4bf(&t2[jc * PX + 16 * R + 4 * L.g], s * tv[0], s * tv[1], s * tv[2], s * tv[3]);
 }
 
 // The four 16x16 diagonal blocks of T = (I + A)^-1 by fp32 forward
 // substitution, one column per lane: lane 16 rg + c solves block rg, column c,
 // with all 16 rows in registers, so no lane exchange is needed.
-__device__ __forceinline__ void solve_diag(const float* at, uint16_t* tt, uint16_t* t2, const float* beta, int lane) {
+__device__ __forceinline__ void solve_diag(const float* at, uint16_t (*tb)[16 * PB], uint16_t* t2, const float* beta,
+                                           int lane) {
   const int c = lane & 15, rg = lane >> 4;
   float x[16];
 #pragma unroll
@@ -319,7 +288,6 @@ __device__ __forceinline__ void solve_diag(const float* at, uint16_t* tt, uint16
   const float s = beta[jc];
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
-    const int o = jc * PX + 16 * rg + 8 * h;
     u32x4 w0, w2;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -327,8 +295,8 @@ __device__ __forceinline__ void solve_diag(const float* at, uint16_t* tt, uint16
       w0[e] = pack_bf16x2(x0, x1);
       w2[e] = pack_bf16x2(s * x0, s * x1);
     }
-    *reinterpret_cast<u32x4*>(&tt[o]) = w0;
-    *reinterpret_cast<u32x4*>(&t2[o]) = w2;
+    *reinterpret_cast<u32x4*>(&tb[rg][c * PB + 8 * h]) = w0;
+    *reinterpret_cast<u32x4*>(&t2[jc * PX + 16 * rg + 8 * h]) = w2;
   }
 }
 
@@ -336,32 +304,32 @@ __device__ __forceinline__ void solve_diag(const float* at, uint16_t* tt, uint16
 //   T10 = -T11 A10 T00,  T32 = -T33 A32 T22,
 //   [T20 T21; T30 T31] = -[T22 0; T32 T33] [A20 A21; A30 A31] [T00 0; T10 T11].
 // (The wave's own LDS writes are visible to its later reads.)
-__device__ __forceinline__ void solve_blocks(const uint16_t* abt, uint16_t* tt, uint16_t* t2, const float* beta,
-                                             const Lane& L) {
+__device__ __forceinline__ void solve_blocks(uint16_t (*ab)[16 * PB], uint16_t (*tb)[16 * PB], uint16_t* t2,
+                                             const float* beta, const Lane& L) {
   const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-  f32x4 t10, t32;
+  f32x4 t10;
   {
-    const f32x4 y10 = mfma16(blk_a(abt, 1, 0, L), blk_b(tt, 0, 0, L), z);
-    const f32x4 y32 = mfma16(blk_a(abt, 3, 2, L), blk_b(tt, 2, 2, L), z);
-    t10 = -mfma16(blk_a(tt, 1, 1, L), to_bf16x4(y10), z);
-    t32 = -mfma16(blk_a(tt, 3, 3, L), to_bf16x4(y32), z);
-    put_t(tt, t2, beta, 1, 0, t10, false, L);
-    put_t(tt, t2, beta, 3, 2, t32, true, L);
+    const f32x4 y10 = mfma16(blk_a(ab[low_slot(1, 0)], L), blk_b(tb[0], L), z);
+    const f32x4 y32 = mfma16(blk_a(ab[low_slot(3, 2)], L), blk_b(tb[2], L), z);
+    t10 = -mfma16(blk_a(tb[1], L), to_bf16x4(y10), z);
+    const f32x4 t32 = -mfma16(blk_a(tb[3], L), to_bf16x4(y32), z);
+    put_t(nullptr, t2, beta, 1, 0, t10, L);
+    put_t(tb[4], t2, beta, 3, 2, t32, L);
   }
   {
-    const bf16x4 b00 = blk_b(tt, 0, 0, L), b11 = blk_b(tt, 1, 1, L), b10 = to_bf16x4(t10);
-    const bf16x4 a20 = blk_a(abt, 2, 0, L), a21 = blk_a(abt, 2, 1, L);
-    const bf16x4 a30 = blk_a(abt, 3, 0, L), a31 = blk_a(abt, 3, 1, L);
+    const bf16x4 b00 = blk_b(tb[0], L), b11 = blk_b(tb[1], L), b10 = to_bf16x4(t10);
+    const bf16x4 a20 = blk_a(ab[low_slot(2, 0)], L), a21 = blk_a(ab[low_slot(2, 1)], L);
+    const bf16x4 a30 = blk_a(ab[low_slot(3, 0)], L), a31 = blk_a(ab[low_slot(3, 1)], L);
     const f32x4 y20 = mfma16(a21, b10, mfma16(a20, b00, z));
     const f32x4 y21 = mfma16(a21, b11, z);
     const f32x4 y30 = mfma16(a31, b10, mfma16(a30, b00, z));
     const f32x4 y31 = mfma16(a31, b11, z);
-    const bf16x4 t22 = blk_a(tt, 2, 2, L), t33 = blk_a(tt, 3, 3, L), t32a = blk_a(tt, 3, 2, L);
+    const bf16x4 t22 = blk_a(tb[2], L), t33 = blk_a(tb[3], L), t32a = blk_a(tb[4], L);
     const bf16x4 c20 = to_bf16x4(y20), c21 = to_bf16x4(y21);
-    put_t(tt, t2, beta, 2, 0, -mfma16(t22, c20, z), false, L);
-    put_t(tt, t2, beta, 2, 1, -mfma16(t22, c21, z), false, L);
-    put_t(tt, t2, beta, 3, 0, -mfma16(t33, to_bf16x4(y30), mfma16(t32a, c20, z)), false, L);
-    put_t(tt, t2, beta, 3, 1, -mfma16(t33, to_bf16x4(y31), mfma16(t32a, c21, z)), false, L);
+    put_t(nullptr, t2, beta, 2, 0, -mfma16(t22, c20, z), L);
+    put_t(nullptr, t2, beta, 2, 1, -mfma16(t22, c21, z), L);
+    put_t(nullptr, t2, beta, 3, 0, -mfma16(t33, to_bf16x4(y30), mfma16(t32a, c20, z)), L);
+    put_t(nullptr, t2, beta, 3, 1, -mfma16(t33, to_bf16x4(y31), mfma16(t32a, c21, z)), L);
   }
 }
 
@@ -389,55 +357,58 @@ __device__ __forceinline__ void load_gb(const ScanArgs& a, const Seq& q, int c, 
   }
 }
 
-// ---- waves 0-3: the state pass of chunk i for d_v columns [n0, n0 + 32)
-//
-// LDS addressing: within a swizzled [64][128] tile the XOR pattern of row t
-// depends on t & 15 only, so every operand read below is one of a few per-lane
-// base offsets plus a compile-time constant.
+// LDS flag accesses (ds_read / ds_write, never flat, so a poll waits for LDS only)
+typedef __attribute__((address_space(3))) int lds_int;
+__device__ __forceinline__ void set_flag(int* flag, int v) {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the data it publishes is written first
+  *(volatile lds_int*)(flag) = v;
+}
+// Waits until the flag reaches `target`.  The wait is bounded (about 2^20
+// polls), so a kernel can never hang on it.
+__device__ __forceinline__ void wait_flag(const int* flag, int target) {
+  for (int n = 0; n < (1 << 20); ++n) {
+    const int v = __builtin_amdgcn_readfirstlane(*(const volatile lds_int*)(flag));
+    if (v >= target) break;
+    __builtin_amdgcn_s_sleep(1);
+  }
+  asm volatile("" ::: "memory");
+}
+
+// state row held in register row d (see the header): the pair-order map
+__device__ __forceinline__ constexpr int sigma(int d) { return perm(d); }
+
+// ---- waves 0-3: the state pass of chunk i for d_v columns [n0, n0 + 32).
+// Every LDS operand read is a per-lane base offset plus a compile-time constant:
+// the swizzle of row t depends on t & 15 only.
 __device__ __forceinline__ void state_role(Smem& sm, float* sst, const ScanArgs& a, const Seq& q, int wv,
                                            const Lane& ln) {
   const int n0 = 16 * NB * wv, li = ln.r, lg = ln.g;
-  const int Hv = a.num_v_heads, C = a.channels;
-  // S[:, n0 + 16nb + li]: sacc[db][nb] holds rows d = 16 db + 4 lg + i (staged in LDS by the kernel)
+  const int Hv = a.num_v_heads;
+  // register row d = 16 db + 4 lg + i of column n0 + 16 nb + li holds state row sigma(d)
   f32x4 sacc[8][NB];
 #pragma unroll
   for (int db = 0; db < 8; ++db)
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) sacc[db][nb][i] = sst[(16 * db + 4 * lg + i) * PS + n0 + 16 * nb + li];
+      for (int i = 0; i < 4; ++i) sacc[db][nb][i] = sst[sigma(16 * db + 4 * lg + i) * PS + n0 + 16 * nb + li];
   lds_barrier();  // the staged state is dead; P / T2 are cleared next
   lds_barrier();
-  // row operand of rows 16 tb + li, k group kk: roff[kk] + 16 tb * D
+  // row operands (K, Q): row 16 tb + li, columns 32 kk + 8 lg .. +7
   int roff[4];
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk) roff[kk] = swz_off(li, 32 * kk + 8 * lg);
-  // K^T operand (ld_tr_qk): toff[db >> 1] + 4 (db & 1) + 32 kk D (+ 16 D for the second half)
+  // K^T operand for register rows 16 db..: the transposed-read source lane reads
+  // row 4 lg + i (+32 kk, +16), columns sigma(16 db + 4 a) = 32 (db >> 1) + 8 a + 4 (db & 1)
   int toff[4];
 #pragma unroll
-  for (int h = 0; h < 4; ++h) toff[h] = swz_off(4 * lg + ln.i, perm(32 * h + 4 * ln.a));
+  for (int h = 0; h < 4; ++h) toff[h] = swz_off(4 * lg + ln.i, 32 * h + 8 * ln.a);
+  // V in D layout: source lane reads row 4 lg + i (+16 tb), columns n0 + 16 nb + 4 a .. +3
+  int voffs[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) voffs[nb] = swz_off(4 * lg + ln.i, n0 + 16 * nb + 4 * ln.a);
   const int t2off = (4 * lg + ln.i) * PX + 4 * ln.a;  // T2^T rows as A operands
   const int poff = li * PP + 8 * lg;                   // P rows as B operands
-  // identity B operand (k = 4g + i, column r): V row chunks -> V in D layout
-  bf16x4 ident;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) ident[i] = (4 * lg + i == li) ? (__bf16)1.f : (__bf16)0.f;
-  // V[16 tb + li][n0 + 16 nb + 4 lg .. +3] of the chunk to come
-  u32x2 vr[4][NB];
-  // one buffer range per 16-row block, so a single lane offset serves every tile
-  const int vlane = 2 * (li * C + 4 * lg + q.voff + n0);
-  auto load_v = [&](int c) {
-    const int nv = min(BT, q.L - c * BT);
-#pragma unroll
-    for (int tb = 0; tb < 4; ++tb) {
-      const __amdgpu_buffer_rsrc_t rv =
-          make_rsrc(reinterpret_cast<const uint16_t*>(a.y) + (int64_t)(q.r0 + c * BT + 16 * tb) * C,
-                    (uint32_t)max(nv - 16 * tb, 0) * C * 2);
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) vr[tb][nb] = __builtin_amdgcn_raw_buffer_load_b64(rv, vlane + 32 * nb, 0, 0);
-    }
-  };
-  load_v(0);
   const int olane = 2 * (li * Hv * D + 4 * lg + q.m * D + n0);
   lds_barrier();  // step -2
   lds_barrier();  // step -1
@@ -481,33 +452,33 @@ __device__ __forceinline__ void state_role(Smem& sm, float* sst, const ScanArgs&
         }
     }
     fence();
-    // ---- X = V - diag(Gamma) K S (V through the identity product), U = T2 X
-    bf16x8 a2[2][4];  // T2 rows 16 tb + li, k = j of group kk (permuted), tb >= 2 kk
+    // ---- X = V - diag(Gamma) K S,  U = T2 X
+    bf16x8 a2[2][4];  // T2 rows 16 tb + li, j of step kk in pair order, tb >= 2 kk
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
       for (int tb = 2 * kk; tb < 4; ++tb)
         a2[kk][tb] = cat(ldtr(t2 + t2off + 32 * kk * PX + 16 * tb), ldtr(t2 + t2off + (32 * kk + 16) * PX + 16 * tb));
+    bf16x4 vv[4][NB];  // V[16 tb + 4 lg + i][n0 + 16 nb + li]
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) vv[tb][nb] = ldtr(cb.v + voffs[nb] + 16 * tb * D);
+    f32x4 gv[4];
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb) gv[tb] = *reinterpret_cast<const f32x4*>(&cb.eg[16 * tb + 4 * lg]);
+    fence();
     f32x4 u[4][NB];
     {
-      f32x4 gv[4];
-#pragma unroll
-      for (int tb = 0; tb < 4; ++tb) gv[tb] = *reinterpret_cast<const f32x4*>(&cb.eg[16 * tb + 4 * lg]);
-      const f32x4 z = {0.f, 0.f, 0.f, 0.f};
       f32x4 x[4][NB];
 #pragma unroll
       for (int tb = 0; tb < 4; ++tb)
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
-          const f32x4 vt = mfma16(__builtin_bit_cast(bf16x4, vr[tb][nb]), ident, z);
 #pragma unroll
-          for (int i = 0; i < 4; ++i) x[tb][nb][i] = __builtin_fmaf(-gv[tb][i], ks[tb][nb][i], vt[i]);
+          for (int i = 0; i < 4; ++i) x[tb][nb][i] = __builtin_fmaf(-gv[tb][i], ks[tb][nb][i], (float)vv[tb][nb][i]);
+          u[tb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
-      if (it + 1 < q.N) load_v(it + 1);
-#pragma unroll
-      for (int tb = 0; tb < 4; ++tb)
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) u[tb][nb] = z;
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
         bf16x8 xb[NB];
@@ -521,11 +492,6 @@ __device__ __forceinline__ void state_role(Smem& sm, float* sst, const ScanArgs&
     }
     fence();
     // ---- O^T = Gamma-scaled (Q S)^T + U^T P^T;  S <- Gamma_c S + K^T diag(e^{gamma_c - gamma}) U
-    bf16x8 pa[6];
-#pragma unroll
-    for (int tb = 0, e = 0; tb < 4; ++tb)
-#pragma unroll
-      for (int kk = 0; kk <= (tb >> 1); ++kk, ++e) pa[e] = lds8(cb.p + poff + 16 * tb * PP + 32 * kk);
     float egt[4];
 #pragma unroll
     for (int tb = 0; tb < 4; ++tb) egt[tb] = cb.eg[16 * tb + li];
@@ -547,6 +513,12 @@ __device__ __forceinline__ void state_role(Smem& sm, float* sst, const ScanArgs&
       const uint16_t* src = cb.k + toff[db >> 1] + 4 * (db & 1);
       kt[db] = cat(ldtr(src), ldtr(src + 16 * D));
     }
+    wait_flag(&sm.pflag, it + 1);  // P of this chunk is in LDS
+    bf16x8 pa[6];
+#pragma unroll
+    for (int tb = 0, e = 0; tb < 4; ++tb)
+#pragma unroll
+      for (int kk = 0; kk <= (tb >> 1); ++kk, ++e) pa[e] = lds8(sm.p + poff + 16 * tb * PP + 32 * kk);
     fence();
 #pragma unroll
     for (int tb = 0; tb < 4; ++tb)
@@ -584,7 +556,8 @@ __device__ __forceinline__ void state_role(Smem& sm, float* sst, const ScanArgs&
       }
     }
     fence();
-    // ---- O rows: lane holds O[16 tb + li][n0 + 16 nb + 4 lg .. +3]; rows past the end are dropped
+    // ---- O rows: lane holds O[16 tb + li][n0 + 16 nb + 4 lg .. +3]; one buffer
+    //      range per 16-row block drops the rows past the end
     {
       const int nv = min(BT, q.L - it * BT);
 #pragma unroll
@@ -607,7 +580,7 @@ __device__ __forceinline__ void state_role(Smem& sm, float* sst, const ScanArgs&
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) sst[(16 * db + 4 * lg + i) * PS + n0 + 16 * nb + li] = sacc[db][nb][i];
+      for (int i = 0; i < 4; ++i) sst[sigma(16 * db + 4 * lg + i) * PS + n0 + 16 * nb + li] = sacc[db][nb][i];
 }
 
 // ---- wave 4: A and the diagonal blocks of T for chunk i + 2
@@ -628,17 +601,22 @@ __device__ __forceinline__ void gram_role(Smem& sm, const ScanArgs& a, const Seq
       float* beta = sm.bsc[c & 1];
       sm.gw[lane] = wave_prefix_sum(g4);
       beta[lane] = b4;
+      // K K^T blocks (bi, bj), bj <= bi; the ten accumulation chains interleaved
       f32x4 acc[10];
 #pragma unroll
-      for (int bi = 0, e = 0; bi < 4; ++bi)
+      for (int e = 0; e < 10; ++e) acc[e] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int bj = 0; bj <= bi; ++bj, ++e) acc[e] = dot_blk(gk[bi], gk[bj]);
+      for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+        for (int bi = 0, e = 0; bi < 4; ++bi)
+#pragma unroll
+          for (int bj = 0; bj <= bi; ++bj, ++e) acc[e] = mfma(gk[bi].v[kk], gk[bj].v[kk], acc[e]);
       if (c + 1 < q.N) load(c + 1);
 #pragma unroll
       for (int bi = 0, e = 0; bi < 4; ++bi)
 #pragma unroll
-        for (int bj = 0; bj <= bi; ++bj, ++e) put_a(sm.at, sm.abt[c & 1], sm.gw, beta, bi, bj, acc[e], ln);
-      solve_diag(sm.at, sm.tt[c & 1], sm.t2t[b3], beta, lane);
+        for (int bj = 0; bj <= bi; ++bj, ++e) put_a(sm.at, sm.ab[c & 1], sm.gw, beta, bi, bj, acc[e], ln);
+      solve_diag(sm.at, sm.tb[c & 1], sm.t2t[b3], beta, lane);
     }
     b3 = b3 == 2 ? 0 : b3 + 1;
     lds_barrier();
@@ -650,69 +628,93 @@ __device__ __forceinline__ void blocks_role(Smem& sm, const Seq& q, const Lane& 
   int b3 = 2;  // (i + 1) % 3
   for (int it = -2; it < q.N; ++it) {
     const int c = it + 1;
-    if (c >= 0 && c < q.N) solve_blocks(sm.abt[c & 1], sm.tt[c & 1], sm.t2t[b3], sm.bsc[c & 1], ln);
+    if (c >= 0 && c < q.N) solve_blocks(sm.ab[c & 1], sm.tb[c & 1], sm.t2t[b3], sm.bsc[c & 1], ln);
     b3 = b3 == 2 ? 0 : b3 + 1;
     lds_barrier();
   }
 }
 
-// ---- waves 6-7: Q / K rows, P and the decay vectors of chunk i + 1.
-// W = 0: Q and K blocks 0-2, P blocks (bi, bj) with bi <= 2;
-// W = 1: Q and K block 3, P blocks (3, bj), e^gamma and e^(gamma_c - gamma).
-template <int W>
-__device__ __forceinline__ void stage_role(Smem& sm, const ScanArgs& a, const Seq& q, int lane, const Lane& ln) {
-  constexpr int NQ = W ? 1 : 3, NK = W ? 4 : 3, QB = W ? 3 : 0;
-  Blk sq[NQ], sk[NK];
-  float gv;
-  auto load = [&](int c) {
-    const __amdgpu_buffer_rsrc_t ry = chunk_rows(a, q, c);
-#pragma unroll
-    for (int b = 0; b < NQ; ++b) sq[b] = ld_blk_g(ry, a.channels, q.qoff, QB + b, ln);
-#pragma unroll
-    for (int b = 0; b < NK; ++b) sk[b] = ld_blk_g(ry, a.channels, q.koff, b, ln);
-    load_gb(a, q, c, lane, gv, nullptr);
-  };
-  load(0);
+// ---- wave 6: Q, K and V rows of chunk i + 1 copied from global memory straight
+// into LDS.  Load j writes LDS bytes [1024 j, 1024 j + 1024) of a tile, i.e.
+// rows 4j..4j+3; lane l fills chunk slot l & 15 of row 4j + (l >> 4), so it reads
+// the natural chunk (l & 15) ^ f(row): every load covers four whole 256-byte rows.
+__device__ __forceinline__ void load_role(Smem& sm, const ScanArgs& a, const Seq& q, int lane) {
+  const int C = a.channels, t0 = lane >> 4, sl = lane & 15;
   for (int it = -2; it < q.N; ++it) {
     const int c = it + 1;
     if (c >= 0 && c < q.N) {
-      ChunkBuf& cb = sm.cb[c & 1];
-      float* gs = sm.gs[W];
+      ChunkBuf& cn = sm.cb[c & 1];
+      const __amdgpu_buffer_rsrc_t ry = chunk_rows(a, q, c);
+#pragma unroll
+      for (int j = 0; j < BT / 4; ++j) {
+        const int t = 4 * j + t0;
+        const int go = 2 * (t * C + 8 * (sl ^ swz_f(t)));
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ry, (__attribute__((address_space(3))) void*)(cn.q + 512 * j), 16,
+                                                 go + 2 * q.qoff, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ry, (__attribute__((address_space(3))) void*)(cn.k + 512 * j), 16,
+                                                 go + 2 * q.koff, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ry, (__attribute__((address_space(3))) void*)(cn.v + 512 * j), 16,
+                                                 go + 2 * q.voff, 0, 0, 0);
+      }
+      const int nv = min(BT, q.L - c * BT);
+      if (nv < BT) {  // rows past the end of the sequence become zero
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        const u32x4 zero = {0u, 0u, 0u, 0u};
+        for (int e = nv * 16 + lane; e < BT * 16; e += 64) {
+          reinterpret_cast<u32x4*>(cn.q)[e] = zero;
+          reinterpret_cast<u32x4*>(cn.k)[e] = zero;
+          reinterpret_cast<u32x4*>(cn.v)[e] = zero;
+        }
+      }
+    }
+    // the copies must have landed before the consumers read them next step
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  }
+}
+
+// ---- wave 7: P of chunk i (the state waves wait for its flag), then gamma,
+// e^gamma and e^(gamma_c - gamma) of chunk i + 1
+__device__ __forceinline__ void decay_role(Smem& sm, const ScanArgs& a, const Seq& q, int lane, const Lane& ln) {
+  int roff[4];
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) roff[kk] = swz_off(ln.r, 32 * kk + 8 * ln.g);
+  float gv;
+  load_gb(a, q, 0, lane, gv, nullptr);
+  for (int it = -2; it < q.N; ++it) {
+    if (it >= 0) {
+      const ChunkBuf& cb = sm.cb[it & 1];
+      // K_bj Q_bi^T for bj <= bi, the ten chains interleaved
+      f32x4 acc[10];
+#pragma unroll
+      for (int e = 0; e < 10; ++e) acc[e] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        bf16x8 kr[4], qr[4];
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          kr[b] = lds8(cb.k + roff[kk] + 16 * b * D);
+          qr[b] = lds8(cb.q + roff[kk] + 16 * b * D);
+        }
+#pragma unroll
+        for (int bi = 0, e = 0; bi < 4; ++bi)
+#pragma unroll
+          for (int bj = 0; bj <= bi; ++bj, ++e) acc[e] = mfma(kr[bj], qr[bi], acc[e]);
+      }
+#pragma unroll
+      for (int bi = 0, e = 0; bi < 4; ++bi)
+#pragma unroll
+        for (int bj = 0; bj <= bi; ++bj, ++e) put_p(sm.p, cb.gam, bi, bj, acc[e], ln);
+      set_flag(&sm.pflag, it + 1);
+    }
+    const int c = it + 1;
+    if (c >= 0 && c < q.N) {
+      ChunkBuf& cn = sm.cb[c & 1];
       const float gam = wave_prefix_sum(gv);
-      gs[lane] = gam;
-      if (W == 1) {
-        const float glast = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, gam), 63));
-        cb.eg[lane] = __expf(gam);
-        cb.ed[lane] = __expf(glast - gam);
-      }
-#pragma unroll
-      for (int b = 0; b < NQ; ++b) stage_blk(cb.q, sq[b], QB + b, ln);
-      if (W == 0) {
-#pragma unroll
-        for (int b = 0; b < 3; ++b) stage_blk(cb.k, sk[b], b, ln);
-      } else {
-        stage_blk(cb.k, sk[NK - 1], 3, ln);
-      }
-      f32x4 acc[W ? 4 : 6];
-      if (W == 0) {
-#pragma unroll
-        for (int bi = 0, e = 0; bi < 3; ++bi)
-#pragma unroll
-          for (int bj = 0; bj <= bi; ++bj, ++e) acc[e] = dot_blk(sk[bj], sq[bi]);
-      } else {
-#pragma unroll
-        for (int bj = 0; bj < 4; ++bj) acc[bj] = dot_blk(sk[bj], sq[0]);
-      }
-      if (c + 1 < q.N) load(c + 1);
-      if (W == 0) {
-#pragma unroll
-        for (int bi = 0, e = 0; bi < 3; ++bi)
-#pragma unroll
-          for (int bj = 0; bj <= bi; ++bj, ++e) put_p(cb.p, gs, bi, bj, acc[e], ln);
-      } else {
-#pragma unroll
-        for (int bj = 0; bj < 4; ++bj) put_p(cb.p, gs, 3, bj, acc[bj], ln);
-      }
+      const float glast = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, gam), 63));
+      cn.gam[lane] = gam;
+      cn.eg[lane] = __expf(gam);
+      cn.ed[lane] = __expf(glast - gam);
+      if (c + 1 < q.N) load_gb(a, q, c + 1, lane, gv, nullptr);
     }
     lds_barrier();
   }
@@ -761,16 +763,14 @@ __global__ __launch_bounds__(NT) void chunk_scan_kernel(ScanArgs a, SeqOrder ord
     lds_barrier();  // the state waves have read the staged state
     // blocks above the diagonal of P and T2 are read by the full-width products and never written
     const u32x4 zero = {0u, 0u, 0u, 0u};
-    for (int i = tid - 64 * NS; i < BT * PP / 8; i += NT - 64 * NS) {
-      reinterpret_cast<u32x4*>(sm.cb[0].p)[i] = zero;
-      reinterpret_cast<u32x4*>(sm.cb[1].p)[i] = zero;
-    }
+    for (int i = tid - 64 * NS; i < BT * PP / 8; i += NT - 64 * NS) reinterpret_cast<u32x4*>(sm.p)[i] = zero;
     for (int i = tid - 64 * NS; i < 3 * BT * PX / 8; i += NT - 64 * NS) reinterpret_cast<u32x4*>(&sm.t2t[0][0])[i] = zero;
+    if (tid == 64 * NS) sm.pflag = 0;
     lds_barrier();
     if (wv == NS) gram_role(sm, a, q, lane, ln);
     else if (wv == NS + 1) blocks_role(sm, q, ln);
-    else if (wv == NS + 2) stage_role<0>(sm, a, q, lane, ln);
-    else stage_role<1>(sm, a, q, lane, ln);
+    else if (wv == NS + 2) load_role(sm, a, q, lane);
+    else decay_role(sm, a, q, lane, ln);
   }
   lds_barrier();
   {
