@@ -22,18 +22,22 @@
 //                      128 x 128 fp32 state, in registers; it computes K S,
 //                      (Q S)^T, U, O^T and the state update for its columns;
 //   wave 4 (gram)      chunk i+2: the Gram products and A from K rows loaded
-//                      straight into registers, then fp32 forward
-//                      substitution on the four 16x16 diagonal blocks of T;
-//   wave 5 (blocks)    chunk i+1: the blocks of T below the diagonal by block
-//                      products (two levels), written as T2^T;
+//                      straight into registers, diagonal blocks first;
 //   wave 6 (loads)     chunk i+1: Q, K and V rows copied from global memory
 //                      straight into LDS (no registers), whole rows per load;
-//   wave 7 (decay)     chunk i: P = M o Q K^T for the state waves, which wait
-//                      for it on an LDS flag before they use it; chunk i+1:
-//                      gamma, e^gamma and e^(gamma_c - gamma).
-// Every other producer writes buffers its consumers read one or two steps
-// later (double-buffered Q/K/V, triple-buffered T2), so the barrier that ends
-// each step is the only other synchronisation.  Global pointers are address
+//                      chunk i+2: fp32 forward substitution on the four 16x16
+//                      diagonal blocks of T, as soon as wave 4 has published
+//                      the diagonal blocks of A;
+//   wave 5 (blocks)    chunk i: rows 48-63 of P = M o Q K^T; chunk i+1: the
+//                      blocks of T below the diagonal by block products (two
+//                      levels), written as T2^T;
+//   wave 7 (decay)     chunk i: rows 0-47 of P; chunk i+1: gamma, e^gamma and
+//                      e^(gamma_c - gamma).  The state waves wait for both
+//                      parts of P before they use it.
+// Within a step, a consumer waits for its producer on an LDS flag (P, the
+// diagonal blocks of A); everything else is read one or two steps after it is
+// written (double-buffered Q/K/V, triple-buffered T2), across the barrier that
+// ends each step.  Global pointers are address
 // space 1 and the barriers wait for LDS traffic only, so loads and the output
 // stores stay in flight across them.  All products are
 // v_mfma_f32_16x16x32_bf16 (bf16 operands, fp32 accumulate).  Sequences are
@@ -84,10 +88,11 @@ struct alignas(16) Smem {
   uint16_t t2t[3][BT * PX];   // (T diag(b))^T [j][t], chunk i % 3; blocks above the diagonal stay zero
   uint16_t ab[2][6][16 * PB]; // A^T blocks below the diagonal (gram wave -> blocks wave)
   uint16_t tb[2][5][16 * PB]; // T^T blocks 00, 11, 22, 33 (gram wave) and 32 (blocks wave)
-  float at[4 * 16 * PA];      // diagonal blocks of A, fp32, [block][j][t] (gram wave only)
+  float at[4 * 16 * PA];      // diagonal blocks of A, fp32, [block][j][t] (gram wave -> wave 6)
   float bsc[2][BT];           // beta of the chunk (gram wave -> blocks wave)
   float gw[BT];               // gamma, gram wave
-  int pflag;                  // steps whose P is complete
+  int pflag, pflag2;          // steps whose P rows 0-47 / 48-63 are complete
+  int aflag;                  // chunks whose diagonal blocks of A are in `at`
 };
 static_assert(sizeof(Smem) <= 160 * 1024, "LDS");
 static_assert(D * PS * 4 <= sizeof(ChunkBuf) * 2, "state staging");
@@ -377,6 +382,64 @@ __device__ __forceinline__ void wait_flag(const int* flag, int target) {
 // state row held in register row d (see the header): the pair-order map
 __device__ __forceinline__ constexpr int sigma(int d) { return perm(d); }
 
+// Rows 16 B0 .. 16 B1 + 15 of P = M o Q K^T for one chunk, into the P buffer:
+// blocks (bi, bj), bj <= bi, as D tiles of K_bj Q_bi^T, chains interleaved, each
+// step's operand rows read one step ahead.
+template <int B0, int B1>
+__device__ __forceinline__ void p_rows(Smem& sm, const ChunkBuf& cb, const Lane& ln) {
+  constexpr int NBLK = (B1 + 1) * (B1 + 2) / 2 - B0 * (B0 + 1) / 2;
+  int roff[4];
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) roff[kk] = swz_off(ln.r, 32 * kk + 8 * ln.g);
+  f32x4 acc[NBLK];
+#pragma unroll
+  for (int e = 0; e < NBLK; ++e) acc[e] = f32x4{0.f, 0.f, 0.f, 0.f};
+  bf16x8 kr[2][B1 + 1], qr[2][B1 + 1];
+#pragma unroll
+  for (int b = 0; b <= B1; ++b) {
+    kr[0][b] = lds8(cb.k + roff[0] + 16 * b * D);
+    if (b >= B0) qr[0][b] = lds8(cb.q + roff[0] + 16 * b * D);
+  }
+  float gt[B1 + 1];
+  f32x4 gj[B1 + 1];
+#pragma unroll
+  for (int b = 0; b <= B1; ++b) {
+    gt[b] = cb.gam[16 * b + ln.r];
+    gj[b] = *reinterpret_cast<const f32x4*>(&cb.gam[16 * b + 4 * ln.g]);
+  }
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) {
+    const int cur = kk & 1;
+    fence();
+    if (kk < 3) {
+#pragma unroll
+      for (int b = 0; b <= B1; ++b) {
+        kr[cur ^ 1][b] = lds8(cb.k + roff[kk + 1] + 16 * b * D);
+        if (b >= B0) qr[cur ^ 1][b] = lds8(cb.q + roff[kk + 1] + 16 * b * D);
+      }
+    }
+    fence();
+#pragma unroll
+    for (int bi = B0, e = 0; bi <= B1; ++bi)
+#pragma unroll
+      for (int bj = 0; bj <= bi; ++bj, ++e) acc[e] = mfma(kr[cur][bj], qr[cur][bi], acc[e]);
+  }
+  // lane holds P[t = 16bi + r][j = 16bj + 4g + i]
+#pragma unroll
+  for (int bi = B0, e = 0; bi <= B1; ++bi)
+#pragma unroll
+    for (int bj = 0; bj <= bi; ++bj, ++e) {
+      const int t = 16 * bi + ln.r;
+      float v[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float f = __expf(gt[bi] - gj[bj][i]) * acc[e][i];
+        v[i] = (16 * bj + 4 * ln.g + i <= t) ? f : 0.f;
+      }
+      st4bf(&sm.p[t * PP + perm(16 * bj + 4 * ln.g)], v[0], v[1], v[2], v[3]);
+    }
+}
+
 // ---- waves 0-3: the state pass of chunk i for d_v columns [n0, n0 + 32).
 // Every LDS operand read is a per-lane base offset plus a compile-time constant:
 // the swizzle of row t depends on t & 15 only.
@@ -514,6 +577,7 @@ __device__ __forceinline__ void state_role(Smem& sm, float* sst, const ScanArgs&
       kt[db] = cat(ldtr(src), ldtr(src + 16 * D));
     }
     wait_flag(&sm.pflag, it + 1);  // P of this chunk is in LDS
+    wait_flag(&sm.pflag2, it + 1);
     bf16x8 pa[6];
 #pragma unroll
     for (int tb = 0, e = 0; tb < 4; ++tb)
@@ -583,7 +647,7 @@ __device__ __forceinline__ void state_role(Smem& sm, float* sst, const ScanArgs&
       for (int i = 0; i < 4; ++i) sst[sigma(16 * db + 4 * lg + i) * PS + n0 + 16 * nb + li] = sacc[db][nb][i];
 }
 
-// ---- wave 4: A and the diagonal blocks of T for chunk i + 2
+// ---- wave 4: A for chunk i + 2, its diagonal blocks published first
 __device__ __forceinline__ void gram_role(Smem& sm, const ScanArgs& a, const Seq& q, int lane, const Lane& ln) {
   Blk gk[4];
   float g4, b4;
@@ -594,39 +658,50 @@ __device__ __forceinline__ void gram_role(Smem& sm, const ScanArgs& a, const Seq
     load_gb(a, q, c, lane, g4, &b4);
   };
   load(0);
-  int b3 = 0;  // (i + 2) % 3
   for (int it = -2; it < q.N; ++it) {
     const int c = it + 2;
     if (c < q.N) {
       float* beta = sm.bsc[c & 1];
       sm.gw[lane] = wave_prefix_sum(g4);
       beta[lane] = b4;
-      // K K^T blocks (bi, bj), bj <= bi; the ten accumulation chains interleaved
-      f32x4 acc[10];
+      // K K^T blocks (b, b), then (bi, bj) with bj < bi; the chains interleaved
+      f32x4 ad[4], ao[6];
 #pragma unroll
-      for (int e = 0; e < 10; ++e) acc[e] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int b = 0; b < 4; ++b) ad[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int e = 0; e < 6; ++e) ao[e] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
-        for (int bi = 0, e = 0; bi < 4; ++bi)
+        for (int b = 0; b < 4; ++b) ad[b] = mfma(gk[b].v[kk], gk[b].v[kk], ad[b]);
 #pragma unroll
-          for (int bj = 0; bj <= bi; ++bj, ++e) acc[e] = mfma(gk[bi].v[kk], gk[bj].v[kk], acc[e]);
+      for (int b = 0; b < 4; ++b) put_a(sm.at, sm.ab[c & 1], sm.gw, beta, b, b, ad[b], ln);
+      set_flag(&sm.aflag, c + 1);
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+        for (int bi = 1, e = 0; bi < 4; ++bi)
+#pragma unroll
+          for (int bj = 0; bj < bi; ++bj, ++e) ao[e] = mfma(gk[bi].v[kk], gk[bj].v[kk], ao[e]);
       if (c + 1 < q.N) load(c + 1);
 #pragma unroll
-      for (int bi = 0, e = 0; bi < 4; ++bi)
+      for (int bi = 1, e = 0; bi < 4; ++bi)
 #pragma unroll
-        for (int bj = 0; bj <= bi; ++bj, ++e) put_a(sm.at, sm.ab[c & 1], sm.gw, beta, bi, bj, acc[e], ln);
-      solve_diag(sm.at, sm.tb[c & 1], sm.t2t[b3], beta, lane);
+        for (int bj = 0; bj < bi; ++bj, ++e) put_a(sm.at, sm.ab[c & 1], sm.gw, beta, bi, bj, ao[e], ln);
     }
-    b3 = b3 == 2 ? 0 : b3 + 1;
     lds_barrier();
   }
 }
 
-// ---- wave 5: the blocks of T below the diagonal for chunk i + 1
+// ---- wave 5: rows 48-63 of P of chunk i, then the blocks of T below the
+// diagonal for chunk i + 1
 __device__ __forceinline__ void blocks_role(Smem& sm, const Seq& q, const Lane& ln) {
   int b3 = 2;  // (i + 1) % 3
   for (int it = -2; it < q.N; ++it) {
+    if (it >= 0) {
+      p_rows<3, 3>(sm, sm.cb[it & 1], ln);
+      set_flag(&sm.pflag2, it + 1);
+    }
     const int c = it + 1;
     if (c >= 0 && c < q.N) solve_blocks(sm.ab[c & 1], sm.tb[c & 1], sm.t2t[b3], sm.bsc[c & 1], ln);
     b3 = b3 == 2 ? 0 : b3 + 1;
@@ -635,11 +710,12 @@ __device__ __forceinline__ void blocks_role(Smem& sm, const Seq& q, const Lane& 
 }
 
 // ---- wave 6: Q, K and V rows of chunk i + 1 copied from global memory straight
-// into LDS.  Load j writes LDS bytes [1024 j, 1024 j + 1024) of a tile, i.e.
+// into LDS, then the diagonal blocks of T for chunk i + 2.  Load j writes LDS bytes [1024 j, 1024 j + 1024) of a tile, i.e.
 // rows 4j..4j+3; lane l fills chunk slot l & 15 of row 4j + (l >> 4), so it reads
 // the natural chunk (l & 15) ^ f(row): every load covers four whole 256-byte rows.
 __device__ __forceinline__ void load_role(Smem& sm, const ScanArgs& a, const Seq& q, int lane) {
   const int C = a.channels, t0 = lane >> 4, sl = lane & 15;
+  int b3 = 0;  // (i + 2) % 3
   for (int it = -2; it < q.N; ++it) {
     const int c = it + 1;
     if (c >= 0 && c < q.N) {
@@ -667,43 +743,25 @@ __device__ __forceinline__ void load_role(Smem& sm, const ScanArgs& a, const Seq
         }
       }
     }
+    const int cd = it + 2;
+    if (cd < q.N) {
+      wait_flag(&sm.aflag, cd + 1);  // the gram wave has written the diagonal blocks of A
+      solve_diag(sm.at, sm.tb[cd & 1], sm.t2t[b3], sm.bsc[cd & 1], lane);
+    }
+    b3 = b3 == 2 ? 0 : b3 + 1;
     // the copies must have landed before the consumers read them next step
     asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
   }
 }
 
-// ---- wave 7: P of chunk i (the state waves wait for its flag), then gamma,
+// ---- wave 7: rows 0-47 of P of chunk i (the state waves wait for its flag), then gamma,
 // e^gamma and e^(gamma_c - gamma) of chunk i + 1
 __device__ __forceinline__ void decay_role(Smem& sm, const ScanArgs& a, const Seq& q, int lane, const Lane& ln) {
-  int roff[4];
-#pragma unroll
-  for (int kk = 0; kk < 4; ++kk) roff[kk] = swz_off(ln.r, 32 * kk + 8 * ln.g);
   float gv;
   load_gb(a, q, 0, lane, gv, nullptr);
   for (int it = -2; it < q.N; ++it) {
     if (it >= 0) {
-      const ChunkBuf& cb = sm.cb[it & 1];
-      // K_bj Q_bi^T for bj <= bi, the ten chains interleaved
-      f32x4 acc[10];
-#pragma unroll
-      for (int e = 0; e < 10; ++e) acc[e] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        bf16x8 kr[4], qr[4];
-#pragma unroll
-        for (int b = 0; b < 4; ++b) {
-          kr[b] = lds8(cb.k + roff[kk] + 16 * b * D);
-          qr[b] = lds8(cb.q + roff[kk] + 16 * b * D);
-        }
-#pragma unroll
-        for (int bi = 0, e = 0; bi < 4; ++bi)
-#pragma unroll
-          for (int bj = 0; bj <= bi; ++bj, ++e) acc[e] = mfma(kr[bj], qr[bi], acc[e]);
-      }
-#pragma unroll
-      for (int bi = 0, e = 0; bi < 4; ++bi)
-#pragma unroll
-        for (int bj = 0; bj <= bi; ++bj, ++e) put_p(sm.p, cb.gam, bi, bj, acc[e], ln);
+      p_rows<0, 2>(sm, sm.cb[it & 1], ln);
       set_flag(&sm.pflag, it + 1);
     }
     const int c = it + 1;
@@ -765,7 +823,11 @@ __global__ __launch_bounds__(NT) void chunk_scan_kernel(ScanArgs a, SeqOrder ord
     const u32x4 zero = {0u, 0u, 0u, 0u};
     for (int i = tid - 64 * NS; i < BT * PP / 8; i += NT - 64 * NS) reinterpret_cast<u32x4*>(sm.p)[i] = zero;
     for (int i = tid - 64 * NS; i < 3 * BT * PX / 8; i += NT - 64 * NS) reinterpret_cast<u32x4*>(&sm.t2t[0][0])[i] = zero;
-    if (tid == 64 * NS) sm.pflag = 0;
+    if (tid == 64 * NS) {
+      sm.pflag = 0;
+      sm.pflag2 = 0;
+      sm.aflag = 0;
+    }
     lds_barrier();
     if (wv == NS) gram_role(sm, a, q, lane, ln);
     else if (wv == NS + 1) blocks_role(sm, q, ln);
