@@ -21,6 +21,8 @@
 //   waves 0-3 (state)  chunk i: wave w owns d_v columns [32w, 32w+32) of the
 //                      128 x 128 fp32 state, in registers; it computes K S,
 //                      (Q S)^T, U, O^T and the state update for its columns;
+//                      its two 16-column tiles interleave in groups of 4
+//                      columns, so each lane ends with 8 adjacent outputs;
 //   wave 4 (gram)      chunk i+2: the Gram products and A from K rows loaded
 //                      straight into registers, diagonal blocks first;
 //   wave 6 (loads)     chunk i+1: Q, K and V rows copied from global memory
@@ -28,16 +30,14 @@
 //                      chunk i+2: fp32 forward substitution on the four 16x16
 //                      diagonal blocks of T, as soon as wave 4 has published
 //                      the diagonal blocks of A;
-//   wave 5 (blocks)    chunk i: rows 48-63 of P = M o Q K^T; chunk i+1: the
-//                      blocks of T below the diagonal by block products (two
-//                      levels), written as T2^T;
-//   wave 7 (decay)     chunk i: rows 0-47 of P; chunk i+1: gamma, e^gamma and
-//                      e^(gamma_c - gamma).  The state waves wait for both
-//                      parts of P before they use it.
-// Within a step, a consumer waits for its producer on an LDS flag (P, the
-// diagonal blocks of A); everything else is read one or two steps after it is
-// written (double-buffered Q/K/V, triple-buffered T2), across the barrier that
-// ends each step.  Global pointers are address
+//   wave 5 (blocks)    chunk i+1: the blocks of T below the diagonal by block
+//                      products (two levels), written as T2^T;
+//   wave 7 (decay)     chunk i+1: gamma, e^gamma, e^(gamma_c - gamma) and, once
+//                      wave 6 has published the rows, P = M o Q K^T.
+// Within a step, a consumer waits for its producer on an LDS flag (the rows of
+// the next chunk, the diagonal blocks of A); everything else is read one or two
+// steps after it is written (double-buffered Q/K/V and P, triple-buffered T2),
+// across the barrier that ends each step.  Global pointers are address
 // space 1 and the barriers wait for LDS traffic only, so loads and the output
 // stores stay in flight across them.  All products are
 // v_mfma_f32_16x16x32_bf16 (bf16 operands, fp32 accumulate).  Sequences are
@@ -52,8 +52,12 @@
 // operand over the 32 k values {4grp..4grp+3, 16+4grp..16+4grp+3} of step kk
 // ("pair order").  The state rows are kept in registers relabelled so that
 // pair order over d is natural order over the columns of K and Q: register
-// row d = 32kk + 16h + 4g + i holds state row sigma(d) = 32kk + 8g + 4h + i.
-// K and Q rows can then stay in natural column order in LDS.
+// row d = 32kk + 16h + 4g + i holds state row sigma(d) = 32kk + 8g + 4(h ^ (g >> 1)) + i,
+// so a pair operand over d is one natural 16-byte chunk of a K or Q row (its
+// halves swapped in lanes with g >= 2).  K and Q rows can then stay in natural
+// column order in LDS, and the transposed reads of K for the state update
+// alternate 8-byte halves between lane groups, which keeps them free of bank
+// conflicts.
 #include "gdn_device.h"
 
 namespace gdn {
@@ -65,7 +69,6 @@ constexpr int NS = 4;             // state waves
 constexpr int NT = 512;           // threads per workgroup (8 waves)
 constexpr int NB = D / 16 / NS;   // 16-column state tiles per state wave
 constexpr int PP = BT + 8;        // pitch of the P rows
-constexpr int PX = BT + 16;       // pitch of the transposed 64 x 64 tiles
 constexpr int PB = 16;            // pitch of a 16 x 16 block
 constexpr int PA = 20;            // fp32 pitch of the transposed diagonal blocks of A
 constexpr int PS = D + 4;         // fp32 pitch of the state staged in LDS (start and end)
@@ -84,14 +87,14 @@ struct ChunkBuf {
 };
 struct alignas(16) Smem {
   ChunkBuf cb[2];             // chunk i & 1: written by waves 6-7, read by the state waves and wave 7
-  uint16_t p[BT * PP];        // P of chunk i, [t][j in pair order]; blocks above the diagonal stay zero
-  uint16_t t2t[3][BT * PX];   // (T diag(b))^T [j][t], chunk i % 3; blocks above the diagonal stay zero
+  uint16_t p[2][BT * PP];     // P of chunk i & 1, [t][j in pair order]; blocks above the diagonal stay zero
+  uint16_t t2[3][11][16 * PB]; // (T diag(b))^T of chunk i % 3 as 16 x 16 blocks [j][t] (t2_slot), and a zero block
   uint16_t ab[2][6][16 * PB]; // A^T blocks below the diagonal (gram wave -> blocks wave)
   uint16_t tb[2][5][16 * PB]; // T^T blocks 00, 11, 22, 33 (gram wave) and 32 (blocks wave)
   float at[4 * 16 * PA];      // diagonal blocks of A, fp32, [block][j][t] (gram wave -> wave 6)
   float bsc[2][BT];           // beta of the chunk (gram wave -> blocks wave)
   float gw[BT];               // gamma, gram wave
-  int pflag, pflag2;          // steps whose P rows 0-47 / 48-63 are complete
+  int dflag;                  // chunks whose Q / K / V rows are in LDS
   int aflag;                  // chunks whose diagonal blocks of A are in `at`
 };
 static_assert(sizeof(Smem) <= 160 * 1024, "LDS");
@@ -212,6 +215,8 @@ __device__ __forceinline__ Blk ld_blk_g(__amdgpu_buffer_rsrc_t rs, int C, int co
 
 // Blocks below the diagonal, stored as 16 x 16 tiles: slot of block (R, C), R > C
 __device__ __forceinline__ constexpr int low_slot(int R, int C) { return R * (R - 1) / 2 + C; }
+// Blocks of T2 (R >= C), and the zero block (slot 10) that stands for R < C
+__device__ __forceinline__ constexpr int t2_slot(int R, int C) { return C <= R ? R * (R + 1) / 2 + C : 10; }
 
 // Block (bi, bj), bj <= bi, of A = strictly-lower(b_t e^{gamma_t - gamma_j} K K^T)
 // from acc = K_bi K_bj^T: lane holds A[t = 16bi + 4g + i][j = 16bj + r].
@@ -263,7 +268,7 @@ __device__ __forceinline__ void put_t(uint16_t* keep, uint16_t* t2, const float*
   const int jc = 16 * C + L.r;
   const float s = beta[jc];
   if (keep) st4bf(&keep[L.r * PB + 4 * L.g], tv[0], tv[1], tv[2], tv[3]);
-  st4bf(&t2[jc * PX + 16 * R + 4 * L.g], s * tv[0], s * tv[1], s * tv[2], s * tv[3]);
+  st4bf(&t2[t2_slot(R, C) * 16 * PB + L.r * PB + 4 * L.g], s * tv[0], s * tv[1], s * tv[2], s * tv[3]);
 }
 
 // The four 16x16 diagonal blocks of T = (I + A)^-1 by fp32 forward
@@ -289,8 +294,7 @@ __device__ __forceinline__ void solve_diag(const float* at, uint16_t (*tb)[16 * 
 #pragma unroll
     for (int t = j + 1; t < 16; ++t) x[t] -= aj[t] * xj;
   }
-  const int jc = 16 * rg + c;
-  const float s = beta[jc];
+  const float s = beta[16 * rg + c];
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     u32x4 w0, w2;
@@ -301,7 +305,7 @@ __device__ __forceinline__ void solve_diag(const float* at, uint16_t (*tb)[16 * 
       w2[e] = pack_bf16x2(s * x0, s * x1);
     }
     *reinterpret_cast<u32x4*>(&tb[rg][c * PB + 8 * h]) = w0;
-    *reinterpret_cast<u32x4*>(&t2[jc * PX + 16 * rg + 8 * h]) = w2;
+    *reinterpret_cast<u32x4*>(&t2[t2_slot(rg, rg) * 16 * PB + c * PB + 8 * h]) = w2;
   }
 }
 
@@ -379,14 +383,22 @@ __device__ __forceinline__ void wait_flag(const int* flag, int target) {
   asm volatile("" ::: "memory");
 }
 
-// state row held in register row d (see the header): the pair-order map
-__device__ __forceinline__ constexpr int sigma(int d) { return perm(d); }
+// state row held in register row d (see the header)
+__device__ __forceinline__ constexpr int sigma(int d) {
+  return (d & ~31) | (((d >> 2) & 3) << 3) | ((((d >> 4) ^ (d >> 3)) & 1) << 2) | (d & 3);
+}
+// pair operand over d of two state tiles: halves swapped when `sw` (lanes with g >= 2)
+__device__ __forceinline__ bf16x8 pair_state(f32x4 lo, f32x4 hi, bool sw) {
+  const u32x4 a = __builtin_bit_cast(u32x4, pair_operand(lo, hi));
+  const u32x4 r = {sw ? a[2] : a[0], sw ? a[3] : a[1], sw ? a[0] : a[2], sw ? a[1] : a[3]};
+  return __builtin_bit_cast(bf16x8, r);
+}
 
-// Rows 16 B0 .. 16 B1 + 15 of P = M o Q K^T for one chunk, into the P buffer:
+// Rows 16 B0 .. 16 B1 + 15 of P = M o Q K^T for one chunk, into a P buffer:
 // blocks (bi, bj), bj <= bi, as D tiles of K_bj Q_bi^T, chains interleaved, each
 // step's operand rows read one step ahead.
 template <int B0, int B1>
-__device__ __forceinline__ void p_rows(Smem& sm, const ChunkBuf& cb, const Lane& ln) {
+__device__ __forceinline__ void p_rows(uint16_t* p, const ChunkBuf& cb, const Lane& ln) {
   constexpr int NBLK = (B1 + 1) * (B1 + 2) / 2 - B0 * (B0 + 1) / 2;
   int roff[4];
 #pragma unroll
@@ -436,7 +448,7 @@ __device__ __forceinline__ void p_rows(Smem& sm, const ChunkBuf& cb, const Lane&
         const float f = __expf(gt[bi] - gj[bj][i]) * acc[e][i];
         v[i] = (16 * bj + 4 * ln.g + i <= t) ? f : 0.f;
       }
-      st4bf(&sm.p[t * PP + perm(16 * bj + 4 * ln.g)], v[0], v[1], v[2], v[3]);
+      st4bf(&p[t * PP + perm(16 * bj + 4 * ln.g)], v[0], v[1], v[2], v[3]);
     }
 }
 
@@ -447,14 +459,18 @@ __device__ __forceinline__ void state_role(Smem& sm, float* sst, const ScanArgs&
                                            const Lane& ln) {
   const int n0 = 16 * NB * wv, li = ln.r, lg = ln.g;
   const int Hv = a.num_v_heads;
-  // register row d = 16 db + 4 lg + i of column n0 + 16 nb + li holds state row sigma(d)
+  // tile nb, lane column r stands for state column n0 + 8 (r >> 2) + 4 nb + (r & 3);
+  // register row d = 16 db + 4 lg + i holds state row sigma(d)
+  int col[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) col[nb] = n0 + 8 * (li >> 2) + 4 * nb + (li & 3);
   f32x4 sacc[8][NB];
 #pragma unroll
   for (int db = 0; db < 8; ++db)
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) sacc[db][nb][i] = sst[sigma(16 * db + 4 * lg + i) * PS + n0 + 16 * nb + li];
+      for (int i = 0; i < 4; ++i) sacc[db][nb][i] = sst[sigma(16 * db + 4 * lg + i) * PS + col[nb]];
   lds_barrier();  // the staged state is dead; P / T2 are cleared next
   lds_barrier();
   // row operands (K, Q): row 16 tb + li, columns 32 kk + 8 lg .. +7
@@ -462,23 +478,27 @@ __device__ __forceinline__ void state_role(Smem& sm, float* sst, const ScanArgs&
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk) roff[kk] = swz_off(li, 32 * kk + 8 * lg);
   // K^T operand for register rows 16 db..: the transposed-read source lane reads
-  // row 4 lg + i (+32 kk, +16), columns sigma(16 db + 4 a) = 32 (db >> 1) + 8 a + 4 (db & 1)
-  int toff[4];
+  // row 4 lg + i (+32 kk, +16), columns sigma(16 db + 4 a) = 32 (db >> 1) + 8 a + 4 ((db & 1) ^ (a >> 1))
+  int toff[4][2];
 #pragma unroll
-  for (int h = 0; h < 4; ++h) toff[h] = swz_off(4 * lg + ln.i, 32 * h + 8 * ln.a);
-  // V in D layout: source lane reads row 4 lg + i (+16 tb), columns n0 + 16 nb + 4 a .. +3
+  for (int h = 0; h < 4; ++h)
+#pragma unroll
+    for (int e = 0; e < 2; ++e) toff[h][e] = swz_off(4 * lg + ln.i, 32 * h + 8 * ln.a) + 4 * (e ^ (ln.a >> 1));
+  const bool sw = lg >= 2;
+  // V in D layout: source lane reads row 4 lg + i (+16 tb), columns n0 + 8 a + 4 nb .. +3
   int voffs[NB];
 #pragma unroll
-  for (int nb = 0; nb < NB; ++nb) voffs[nb] = swz_off(4 * lg + ln.i, n0 + 16 * nb + 4 * ln.a);
-  const int t2off = (4 * lg + ln.i) * PX + 4 * ln.a;  // T2^T rows as A operands
+  for (int nb = 0; nb < NB; ++nb) voffs[nb] = swz_off(4 * lg + ln.i, n0 + 8 * ln.a + 4 * nb);
+  const int t2off = (4 * lg + ln.i) * PB + 4 * ln.a;  // T2 rows as A operands, within a block
   const int poff = li * PP + 8 * lg;                   // P rows as B operands
-  const int olane = 2 * (li * Hv * D + 4 * lg + q.m * D + n0);
+  const int olane = 2 * (li * Hv * D + 8 * lg + q.m * D + n0);
   lds_barrier();  // step -2
   lds_barrier();  // step -1
   int b3 = 0;     // i % 3
   for (int it = 0; it < q.N; ++it) {
     const ChunkBuf& cb = sm.cb[it & 1];
-    const uint16_t* t2 = sm.t2t[b3];
+    const uint16_t* t2 = &sm.t2[b3][0][0];
+    const uint16_t* pb = sm.p[it & 1];
     // ---- K S (rows t, columns n) and (Q S)^T (rows n, columns t)
     f32x4 ks[4][NB], ot[NB][4];
 #pragma unroll
@@ -505,7 +525,7 @@ __device__ __forceinline__ void state_role(Smem& sm, float* sst, const ScanArgs&
       fence();
       bf16x8 sb[NB];
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) sb[nb] = pair_operand(sacc[2 * kk][nb], sacc[2 * kk + 1][nb]);
+      for (int nb = 0; nb < NB; ++nb) sb[nb] = pair_state(sacc[2 * kk][nb], sacc[2 * kk + 1][nb], sw);
 #pragma unroll
       for (int tb = 0; tb < 4; ++tb)
 #pragma unroll
@@ -521,7 +541,8 @@ __device__ __forceinline__ void state_role(Smem& sm, float* sst, const ScanArgs&
     for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
       for (int tb = 2 * kk; tb < 4; ++tb)
-        a2[kk][tb] = cat(ldtr(t2 + t2off + 32 * kk * PX + 16 * tb), ldtr(t2 + t2off + (32 * kk + 16) * PX + 16 * tb));
+        a2[kk][tb] = cat(ldtr(t2 + t2_slot(tb, 2 * kk) * 16 * PB + t2off),
+                         ldtr(t2 + t2_slot(tb, 2 * kk + 1) * 16 * PB + t2off));
     bf16x4 vv[4][NB];  // V[16 tb + 4 lg + i][n0 + 16 nb + li]
 #pragma unroll
     for (int tb = 0; tb < 4; ++tb)
@@ -573,16 +594,14 @@ __device__ __forceinline__ void state_role(Smem& sm, float* sst, const ScanArgs&
     bf16x8 kt[8];
 #pragma unroll
     for (int db = 0; db < 8; ++db) {
-      const uint16_t* src = cb.k + toff[db >> 1] + 4 * (db & 1);
+      const uint16_t* src = cb.k + toff[db >> 1][db & 1];
       kt[db] = cat(ldtr(src), ldtr(src + 16 * D));
     }
-    wait_flag(&sm.pflag, it + 1);  // P of this chunk is in LDS
-    wait_flag(&sm.pflag2, it + 1);
     bf16x8 pa[6];
 #pragma unroll
     for (int tb = 0, e = 0; tb < 4; ++tb)
 #pragma unroll
-      for (int kk = 0; kk <= (tb >> 1); ++kk, ++e) pa[e] = lds8(sm.p + poff + 16 * tb * PP + 32 * kk);
+      for (int kk = 0; kk <= (tb >> 1); ++kk, ++e) pa[e] = lds8(pb + poff + 16 * tb * PP + 32 * kk);
     fence();
 #pragma unroll
     for (int tb = 0; tb < 4; ++tb)
@@ -602,7 +621,7 @@ __device__ __forceinline__ void state_role(Smem& sm, float* sst, const ScanArgs&
       if (kk == 0) {
 #pragma unroll
         for (int db = 0; db < 8; ++db) {
-          const uint16_t* src = cb.k + toff[db >> 1] + 4 * (db & 1) + 32 * D;
+          const uint16_t* src = cb.k + toff[db >> 1][db & 1] + 32 * D;
           kn[db] = cat(ldtr(src), ldtr(src + 16 * D));
         }
       }
@@ -620,8 +639,8 @@ __device__ __forceinline__ void state_role(Smem& sm, float* sst, const ScanArgs&
       }
     }
     fence();
-    // ---- O rows: lane holds O[16 tb + li][n0 + 16 nb + 4 lg .. +3]; one buffer
-    //      range per 16-row block drops the rows past the end
+    // ---- O rows: lane holds O[16 tb + li][n0 + 8 lg .. +7]; one buffer range per
+    //      16-row block drops the rows past the end
     {
       const int nv = min(BT, q.L - it * BT);
 #pragma unroll
@@ -629,11 +648,9 @@ __device__ __forceinline__ void state_role(Smem& sm, float* sst, const ScanArgs&
         const __amdgpu_buffer_rsrc_t ro =
             make_rsrc(reinterpret_cast<uint16_t*>(a.out) + (int64_t)(q.r0 + it * BT + 16 * tb) * Hv * D,
                       (uint32_t)max(nv - 16 * tb, 0) * Hv * D * 2);
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-          const u32x2 o = {pack_bf16x2(ot[nb][tb][0], ot[nb][tb][1]), pack_bf16x2(ot[nb][tb][2], ot[nb][tb][3])};
-          __builtin_amdgcn_raw_buffer_store_b64(o, ro, olane + 32 * nb, 0, 0);
-        }
+        const u32x4 o = {pack_bf16x2(ot[0][tb][0], ot[0][tb][1]), pack_bf16x2(ot[0][tb][2], ot[0][tb][3]),
+                         pack_bf16x2(ot[1][tb][0], ot[1][tb][1]), pack_bf16x2(ot[1][tb][2], ot[1][tb][3])};
+        __builtin_amdgcn_raw_buffer_store_b128(o, ro, olane, 0, 0);
       }
     }
     b3 = b3 == 2 ? 0 : b3 + 1;
@@ -644,7 +661,7 @@ __device__ __forceinline__ void state_role(Smem& sm, float* sst, const ScanArgs&
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) sst[sigma(16 * db + 4 * lg + i) * PS + n0 + 16 * nb + li] = sacc[db][nb][i];
+      for (int i = 0; i < 4; ++i) sst[sigma(16 * db + 4 * lg + i) * PS + col[nb]] = sacc[db][nb][i];
 }
 
 // ---- wave 4: A for chunk i + 2, its diagonal blocks published first
@@ -693,17 +710,12 @@ __device__ __forceinline__ void gram_role(Smem& sm, const ScanArgs& a, const Seq
   }
 }
 
-// ---- wave 5: rows 48-63 of P of chunk i, then the blocks of T below the
-// diagonal for chunk i + 1
+// ---- wave 5: the blocks of T below the diagonal for chunk i + 1
 __device__ __forceinline__ void blocks_role(Smem& sm, const Seq& q, const Lane& ln) {
   int b3 = 2;  // (i + 1) % 3
   for (int it = -2; it < q.N; ++it) {
-    if (it >= 0) {
-      p_rows<3, 3>(sm, sm.cb[it & 1], ln);
-      set_flag(&sm.pflag2, it + 1);
-    }
     const int c = it + 1;
-    if (c >= 0 && c < q.N) solve_blocks(sm.ab[c & 1], sm.tb[c & 1], sm.t2t[b3], sm.bsc[c & 1], ln);
+    if (c >= 0 && c < q.N) solve_blocks(sm.ab[c & 1], sm.tb[c & 1], &sm.t2[b3][0][0], sm.bsc[c & 1], ln);
     b3 = b3 == 2 ? 0 : b3 + 1;
     lds_barrier();
   }
@@ -733,8 +745,8 @@ __device__ __forceinline__ void load_role(Smem& sm, const ScanArgs& a, const Seq
                                                  go + 2 * q.voff, 0, 0, 0);
       }
       const int nv = min(BT, q.L - c * BT);
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       if (nv < BT) {  // rows past the end of the sequence become zero
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         const u32x4 zero = {0u, 0u, 0u, 0u};
         for (int e = nv * 16 + lane; e < BT * 16; e += 64) {
           reinterpret_cast<u32x4*>(cn.q)[e] = zero;
@@ -742,11 +754,12 @@ __device__ __forceinline__ void load_role(Smem& sm, const ScanArgs& a, const Seq
           reinterpret_cast<u32x4*>(cn.v)[e] = zero;
         }
       }
+      set_flag(&sm.dflag, c + 1);
     }
     const int cd = it + 2;
     if (cd < q.N) {
       wait_flag(&sm.aflag, cd + 1);  // the gram wave has written the diagonal blocks of A
-      solve_diag(sm.at, sm.tb[cd & 1], sm.t2t[b3], sm.bsc[cd & 1], lane);
+      solve_diag(sm.at, sm.tb[cd & 1], &sm.t2[b3][0][0], sm.bsc[cd & 1], lane);
     }
     b3 = b3 == 2 ? 0 : b3 + 1;
     // the copies must have landed before the consumers read them next step
@@ -754,16 +767,11 @@ __device__ __forceinline__ void load_role(Smem& sm, const ScanArgs& a, const Seq
   }
 }
 
-// ---- wave 7: rows 0-47 of P of chunk i (the state waves wait for its flag), then gamma,
-// e^gamma and e^(gamma_c - gamma) of chunk i + 1
+// ---- wave 7: gamma, e^gamma, e^(gamma_c - gamma) and P of chunk i + 1
 __device__ __forceinline__ void decay_role(Smem& sm, const ScanArgs& a, const Seq& q, int lane, const Lane& ln) {
   float gv;
   load_gb(a, q, 0, lane, gv, nullptr);
   for (int it = -2; it < q.N; ++it) {
-    if (it >= 0) {
-      p_rows<0, 2>(sm, sm.cb[it & 1], ln);
-      set_flag(&sm.pflag, it + 1);
-    }
     const int c = it + 1;
     if (c >= 0 && c < q.N) {
       ChunkBuf& cn = sm.cb[c & 1];
@@ -773,6 +781,8 @@ __device__ __forceinline__ void decay_role(Smem& sm, const ScanArgs& a, const Se
       cn.eg[lane] = __expf(gam);
       cn.ed[lane] = __expf(glast - gam);
       if (c + 1 < q.N) load_gb(a, q, c + 1, lane, gv, nullptr);
+      wait_flag(&sm.dflag, c + 1);  // the chunk's rows are in LDS
+      p_rows<0, 3>(sm.p[c & 1], cn, ln);
     }
     lds_barrier();
   }
@@ -819,13 +829,16 @@ __global__ __launch_bounds__(NT) void chunk_scan_kernel(ScanArgs a, SeqOrder ord
     state_role(sm, sst, a, q, wv, ln);
   } else {
     lds_barrier();  // the state waves have read the staged state
-    // blocks above the diagonal of P and T2 are read by the full-width products and never written
+    // blocks above the diagonal of P, and the zero block of T2, are read by the
+    // full-width products and never written
     const u32x4 zero = {0u, 0u, 0u, 0u};
-    for (int i = tid - 64 * NS; i < BT * PP / 8; i += NT - 64 * NS) reinterpret_cast<u32x4*>(sm.p)[i] = zero;
-    for (int i = tid - 64 * NS; i < 3 * BT * PX / 8; i += NT - 64 * NS) reinterpret_cast<u32x4*>(&sm.t2t[0][0])[i] = zero;
+    for (int i = tid - 64 * NS; i < 2 * BT * PP / 8; i += NT - 64 * NS) reinterpret_cast<u32x4*>(&sm.p[0][0])[i] = zero;
+    for (int i = tid - 64 * NS; i < 3 * 16 * PB / 8; i += NT - 64 * NS) {
+      const int b = i / (16 * PB / 8), e = i % (16 * PB / 8);
+      reinterpret_cast<u32x4*>(&sm.t2[b][10][0])[e] = zero;
+    }
     if (tid == 64 * NS) {
-      sm.pflag = 0;
-      sm.pflag2 = 0;
+      sm.dflag = 0;
       sm.aflag = 0;
     }
     lds_barrier();
