@@ -26,14 +26,16 @@
 //   wave 4 (gram)      chunk i+2: the Gram products and A from K rows loaded
 //                      straight into registers, diagonal blocks first;
 //   wave 6 (loads)     chunk i+1: Q, K and V rows copied from global memory
-//                      straight into LDS (no registers), whole rows per load;
+//                      straight into LDS (no registers), whole rows per load,
+//                      and gamma, e^gamma, e^(gamma_c - gamma);
 //                      chunk i+2: fp32 forward substitution on the four 16x16
 //                      diagonal blocks of T, as soon as wave 4 has published
 //                      the diagonal blocks of A;
 //   wave 5 (blocks)    chunk i+1: the blocks of T below the diagonal by block
-//                      products (two levels), written as T2^T;
-//   wave 7 (decay)     chunk i+1: gamma, e^gamma, e^(gamma_c - gamma) and, once
-//                      wave 6 has published the rows, P = M o Q K^T.
+//                      products (two levels), written as T2^T, then rows
+//                      48-63 of P = M o Q K^T;
+//   wave 7 (P)         chunk i+1: once wave 6 has published the Q and K rows
+//                      and gamma, rows 0-47 of P.
 // Within a step, a consumer waits for its producer on an LDS flag (the rows of
 // the next chunk, the diagonal blocks of A); everything else is read one or two
 // steps after it is written (double-buffered Q/K/V and P, triple-buffered T2),
@@ -86,7 +88,7 @@ struct ChunkBuf {
   float ed[BT];               // e^(gamma_last - gamma)
 };
 struct alignas(16) Smem {
-  ChunkBuf cb[2];             // chunk i & 1: written by waves 6-7, read by the state waves and wave 7
+  ChunkBuf cb[2];             // chunk i & 1: written by wave 6, read by the state waves and waves 5, 7
   uint16_t p[2][BT * PP];     // P of chunk i & 1, [t][j in pair order]; blocks above the diagonal stay zero
   uint16_t t2[3][11][16 * PB]; // (T diag(b))^T of chunk i % 3 as 16 x 16 blocks [j][t] (t2_slot), and a zero block
   uint16_t ab[2][6][16 * PB]; // A^T blocks below the diagonal (gram wave -> blocks wave)
@@ -710,29 +712,37 @@ __device__ __forceinline__ void gram_role(Smem& sm, const ScanArgs& a, const Seq
   }
 }
 
-// ---- wave 5: the blocks of T below the diagonal for chunk i + 1
+// ---- wave 5: the blocks of T below the diagonal and rows 48-63 of P for chunk i + 1
 __device__ __forceinline__ void blocks_role(Smem& sm, const Seq& q, const Lane& ln) {
   int b3 = 2;  // (i + 1) % 3
   for (int it = -2; it < q.N; ++it) {
     const int c = it + 1;
-    if (c >= 0 && c < q.N) solve_blocks(sm.ab[c & 1], sm.tb[c & 1], &sm.t2[b3][0][0], sm.bsc[c & 1], ln);
+    if (c >= 0 && c < q.N) {
+      solve_blocks(sm.ab[c & 1], sm.tb[c & 1], &sm.t2[b3][0][0], sm.bsc[c & 1], ln);
+      wait_flag(&sm.dflag, c + 1);  // the chunk's Q and K rows are in LDS
+      p_rows<3, 3>(sm.p[c & 1], sm.cb[c & 1], ln);
+    }
     b3 = b3 == 2 ? 0 : b3 + 1;
     lds_barrier();
   }
 }
 
 // ---- wave 6: Q, K and V rows of chunk i + 1 copied from global memory straight
-// into LDS, then the diagonal blocks of T for chunk i + 2.  Load j writes LDS bytes [1024 j, 1024 j + 1024) of a tile, i.e.
+// into LDS, with the decay vectors; then the diagonal blocks of T for chunk
+// i + 2.  Load j writes LDS bytes [1024 j, 1024 j + 1024) of a tile, i.e.
 // rows 4j..4j+3; lane l fills chunk slot l & 15 of row 4j + (l >> 4), so it reads
 // the natural chunk (l & 15) ^ f(row): every load covers four whole 256-byte rows.
 __device__ __forceinline__ void load_role(Smem& sm, const ScanArgs& a, const Seq& q, int lane) {
   const int C = a.channels, t0 = lane >> 4, sl = lane & 15;
+  float gv;
+  load_gb(a, q, 0, lane, gv, nullptr);
   int b3 = 0;  // (i + 2) % 3
   for (int it = -2; it < q.N; ++it) {
     const int c = it + 1;
     if (c >= 0 && c < q.N) {
       ChunkBuf& cn = sm.cb[c & 1];
       const __amdgpu_buffer_rsrc_t ry = chunk_rows(a, q, c);
+      // Q and K first (P waits for them), then V (read next step)
 #pragma unroll
       for (int j = 0; j < BT / 4; ++j) {
         const int t = 4 * j + t0;
@@ -741,20 +751,36 @@ __device__ __forceinline__ void load_role(Smem& sm, const ScanArgs& a, const Seq
                                                  go + 2 * q.qoff, 0, 0, 0);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(ry, (__attribute__((address_space(3))) void*)(cn.k + 512 * j), 16,
                                                  go + 2 * q.koff, 0, 0, 0);
+      }
+#pragma unroll
+      for (int j = 0; j < BT / 4; ++j) {
+        const int t = 4 * j + t0;
+        const int go = 2 * (t * C + 8 * (sl ^ swz_f(t)));
         __builtin_amdgcn_raw_ptr_buffer_load_lds(ry, (__attribute__((address_space(3))) void*)(cn.v + 512 * j), 16,
                                                  go + 2 * q.voff, 0, 0, 0);
       }
+      {
+        const float gam = wave_prefix_sum(gv);
+        const float glast = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, gam), 63));
+        cn.gam[lane] = gam;
+        cn.eg[lane] = __expf(gam);
+        cn.ed[lane] = __expf(glast - gam);
+      }
       const int nv = min(BT, q.L - c * BT);
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      const u32x4 zero = {0u, 0u, 0u, 0u};
+      asm volatile("s_waitcnt vmcnt(16)" ::: "memory");  // loads complete in order: Q and K have landed
       if (nv < BT) {  // rows past the end of the sequence become zero
-        const u32x4 zero = {0u, 0u, 0u, 0u};
         for (int e = nv * 16 + lane; e < BT * 16; e += 64) {
           reinterpret_cast<u32x4*>(cn.q)[e] = zero;
           reinterpret_cast<u32x4*>(cn.k)[e] = zero;
-          reinterpret_cast<u32x4*>(cn.v)[e] = zero;
         }
       }
       set_flag(&sm.dflag, c + 1);
+      if (nv < BT) {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        for (int e = nv * 16 + lane; e < BT * 16; e += 64) reinterpret_cast<u32x4*>(cn.v)[e] = zero;
+      }
+      if (c + 1 < q.N) load_gb(a, q, c + 1, lane, gv, nullptr);
     }
     const int cd = it + 2;
     if (cd < q.N) {
@@ -767,22 +793,13 @@ __device__ __forceinline__ void load_role(Smem& sm, const ScanArgs& a, const Seq
   }
 }
 
-// ---- wave 7: gamma, e^gamma, e^(gamma_c - gamma) and P of chunk i + 1
-__device__ __forceinline__ void decay_role(Smem& sm, const ScanArgs& a, const Seq& q, int lane, const Lane& ln) {
-  float gv;
-  load_gb(a, q, 0, lane, gv, nullptr);
+// ---- wave 7: rows 0-47 of P of chunk i + 1
+__device__ __forceinline__ void p_role(Smem& sm, const Seq& q, const Lane& ln) {
   for (int it = -2; it < q.N; ++it) {
     const int c = it + 1;
     if (c >= 0 && c < q.N) {
-      ChunkBuf& cn = sm.cb[c & 1];
-      const float gam = wave_prefix_sum(gv);
-      const float glast = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, gam), 63));
-      cn.gam[lane] = gam;
-      cn.eg[lane] = __expf(gam);
-      cn.ed[lane] = __expf(glast - gam);
-      if (c + 1 < q.N) load_gb(a, q, c + 1, lane, gv, nullptr);
-      wait_flag(&sm.dflag, c + 1);  // the chunk's rows are in LDS
-      p_rows<0, 3>(sm.p[c & 1], cn, ln);
+      wait_flag(&sm.dflag, c + 1);  // the chunk's Q and K rows and gamma are in LDS
+      p_rows<0, 2>(sm.p[c & 1], sm.cb[c & 1], ln);
     }
     lds_barrier();
   }
@@ -845,7 +862,7 @@ __global__ __launch_bounds__(NT) void chunk_scan_kernel(ScanArgs a, SeqOrder ord
     if (wv == NS) gram_role(sm, a, q, lane, ln);
     else if (wv == NS + 1) blocks_role(sm, q, ln);
     else if (wv == NS + 2) load_role(sm, a, q, lane);
-    else decay_role(sm, a, q, lane, ln);
+    else p_role(sm, q, ln);
   }
   lds_barrier();
   {
