@@ -12,7 +12,11 @@ The same JSON line carries the decode workload (256 sequences of one token,
 kernel, the per-kernel event timings, and the fp64 CPU oracle timed on the
 host cores beside it.
 
-    python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps 50] [--warmup 50] [--no-cpu-baseline]
+
+The default warm-up is long enough (about 20 ms of GPU work) for the clocks to
+settle: the first few dozen steps after the inputs are uploaded run up to 10%
+slower, and the line reports the steady rate.
 """
 from __future__ import annotations
 
@@ -161,8 +165,8 @@ def cpu_baseline(batch):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--only", choices=["prefill", "decode"], default=None,
