@@ -278,7 +278,12 @@ extern "C" int gdn_varlen_forward(const gdn_layer_desc* desc, const void* x, con
     ca.y = workspace;
     ca.num_seqs = num_seqs; ca.total_tokens = total_tokens; ca.num_blocks = num_blocks; ca.channels = C;
     ca.qk_channels = desc->num_k_heads * desc->head_k_dim; ca.head_k_dim = desc->head_k_dim;
-    ca.rows_per_block = total_tokens >= 16384 ? 16 : (total_tokens >= 2048 ? 4 : 1);
+    {  // about 4096 one-wave blocks (16 per CU): rows per block a multiple of the 4 rows in flight
+      const int groups = (C + 511) / 512;
+      const int slices = std::max(1, 4096 / groups);
+      const int rows = (total_tokens + slices - 1) / slices;
+      ca.rows_per_block = std::min(256, std::max(4, (rows + 3) / 4 * 4));
+    }
     ca.eps = sa.eps;
     ca.q_scale = sa.q_scale;
     e = timed(K_CONV, st, [&] { return gdn::launch_conv(ca, W, bf16, st); });

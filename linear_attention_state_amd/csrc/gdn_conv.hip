@@ -9,9 +9,11 @@
 // head as x / sqrt(sum x^2 + eps), q also multiplied by q_scale.
 //
 // Layout: x and the output y are [T][C] rows; one thread owns 8 consecutive
-// channels (one 16-byte bf16 load per row, two for fp32), a 256-thread block
-// covers 2048 channels of `rows_per_block` consecutive rows, so every row read
-// is a coalesced 4 KB (bf16) segment.  The W-1 previous inputs of each channel
+// channels (one 16-byte bf16 load per row, two for fp32), a one-wave block
+// covers 512 channels of `rows_per_block` consecutive rows, so every row read
+// is a coalesced 1 KB (bf16) segment.  The host sizes the blocks so that there
+// are about 16 per CU: long row ranges keep the W-1 re-read rows at a block's
+// start a small fraction of the traffic.  The W-1 previous inputs of each channel
 // slide along in registers; the first rows of a sequence take them from the
 // sequence's conv state.  The Σx² of a head is reduced across the d_k/8 lanes
 // that hold it with lane shuffles, so the normalisation costs no extra pass.
@@ -234,7 +236,7 @@ __global__ __launch_bounds__(256) void conv_tail_commit_kernel(TailArgs a) {
 
 template <bool BF16, int W>
 hipError_t conv_dispatch(const ConvArgs& a, hipStream_t st) {
-  const int threads = 256;
+  const int threads = 64;  // one wave: 512 channels
   const int per_block = threads * 8;
   dim3 grid((a.total_tokens + a.rows_per_block - 1) / a.rows_per_block,
             (a.channels + per_block - 1) / per_block);
