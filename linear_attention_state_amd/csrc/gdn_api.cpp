@@ -102,7 +102,9 @@ hipEvent_t take_event() {
     return e;
   }
   hipEvent_t e = nullptr;
-  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  // timing only: no system-scope fence, which would write back and invalidate
+  // the caches between the kernels it brackets and slow the step down
+  if (hipEventCreateWithFlags(&e, hipEventDisableSystemFence) != hipSuccess) return nullptr;
   return e;
 }
 
