@@ -501,28 +501,36 @@ __device__ __forceinline__ void state_role(Smem& sm, float* sst, const ScanArgs&
     const ChunkBuf& cb = sm.cb[it & 1];
     const uint16_t* t2 = &sm.t2[b3][0][0];
     const uint16_t* pb = sm.p[it & 1];
-    // ---- K S (rows t, columns n) and (Q S)^T (rows n, columns t)
-    f32x4 ks[4][NB], ot[NB][4];
+    // The chain K S -> X -> U -> state update is serial; (Q S)^T is only needed
+    // for O, so its products run while U and its operand packing complete.
+    // ---- K S (rows t, columns n)
+    f32x4 ks[4][NB];
 #pragma unroll
     for (int tb = 0; tb < 4; ++tb)
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) ks[tb][nb] = ot[nb][tb] = f32x4{0.f, 0.f, 0.f, 0.f};
-    bf16x8 ka[2][4], qa[2][4];
+      for (int nb = 0; nb < NB; ++nb) ks[tb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    bf16x8 ka[2][4], a2[2][4];
+    bf16x4 vv[4][NB];  // V[16 tb + 4 lg + i][state columns of tile nb]
 #pragma unroll
-    for (int tb = 0; tb < 4; ++tb) {
-      ka[0][tb] = lds8(cb.k + roff[0] + 16 * tb * D);
-      qa[0][tb] = lds8(cb.q + roff[0] + 16 * tb * D);
-    }
+    for (int tb = 0; tb < 4; ++tb) ka[0][tb] = lds8(cb.k + roff[0] + 16 * tb * D);
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
       const int cur = kk & 1;
       fence();
       if (kk < 3) {
 #pragma unroll
-        for (int tb = 0; tb < 4; ++tb) {
-          ka[cur ^ 1][tb] = lds8(cb.k + roff[kk + 1] + 16 * tb * D);
-          qa[cur ^ 1][tb] = lds8(cb.q + roff[kk + 1] + 16 * tb * D);
-        }
+        for (int tb = 0; tb < 4; ++tb) ka[cur ^ 1][tb] = lds8(cb.k + roff[kk + 1] + 16 * tb * D);
+      } else {  // the operands of X and U
+#pragma unroll
+        for (int k2 = 0; k2 < 2; ++k2)
+#pragma unroll
+          for (int tb = 2 * k2; tb < 4; ++tb)  // T2 rows 16 tb + li, j of step k2 in pair order
+            a2[k2][tb] = cat(ldtr(t2 + t2_slot(tb, 2 * k2) * 16 * PB + t2off),
+                             ldtr(t2 + t2_slot(tb, 2 * k2 + 1) * 16 * PB + t2off));
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb) vv[tb][nb] = ldtr(cb.v + voffs[nb] + 16 * tb * D);
       }
       fence();
       bf16x8 sb[NB];
@@ -531,40 +539,23 @@ __device__ __forceinline__ void state_role(Smem& sm, float* sst, const ScanArgs&
 #pragma unroll
       for (int tb = 0; tb < 4; ++tb)
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-          ks[tb][nb] = mfma(ka[cur][tb], sb[nb], ks[tb][nb]);
-          ot[nb][tb] = mfma(sb[nb], qa[cur][tb], ot[nb][tb]);
-        }
+        for (int nb = 0; nb < NB; ++nb) ks[tb][nb] = mfma(ka[cur][tb], sb[nb], ks[tb][nb]);
     }
     fence();
     // ---- X = V - diag(Gamma) K S,  U = T2 X
-    bf16x8 a2[2][4];  // T2 rows 16 tb + li, j of step kk in pair order, tb >= 2 kk
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-      for (int tb = 2 * kk; tb < 4; ++tb)
-        a2[kk][tb] = cat(ldtr(t2 + t2_slot(tb, 2 * kk) * 16 * PB + t2off),
-                         ldtr(t2 + t2_slot(tb, 2 * kk + 1) * 16 * PB + t2off));
-    bf16x4 vv[4][NB];  // V[16 tb + 4 lg + i][n0 + 16 nb + li]
-#pragma unroll
-    for (int tb = 0; tb < 4; ++tb)
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) vv[tb][nb] = ldtr(cb.v + voffs[nb] + 16 * tb * D);
-    f32x4 gv[4];
-#pragma unroll
-    for (int tb = 0; tb < 4; ++tb) gv[tb] = *reinterpret_cast<const f32x4*>(&cb.eg[16 * tb + 4 * lg]);
-    fence();
     f32x4 u[4][NB];
     {
       f32x4 x[4][NB];
 #pragma unroll
-      for (int tb = 0; tb < 4; ++tb)
+      for (int tb = 0; tb < 4; ++tb) {
+        const f32x4 gv = *reinterpret_cast<const f32x4*>(&cb.eg[16 * tb + 4 * lg]);
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
 #pragma unroll
-          for (int i = 0; i < 4; ++i) x[tb][nb][i] = __builtin_fmaf(-gv[tb][i], ks[tb][nb][i], (float)vv[tb][nb][i]);
+          for (int i = 0; i < 4; ++i) x[tb][nb][i] = __builtin_fmaf(-gv[i], ks[tb][nb][i], (float)vv[tb][nb][i]);
           u[tb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
+      }
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
         bf16x8 xb[NB];
@@ -577,33 +568,66 @@ __device__ __forceinline__ void state_role(Smem& sm, float* sst, const ScanArgs&
       }
     }
     fence();
-    // ---- O^T = Gamma-scaled (Q S)^T + U^T P^T;  S <- Gamma_c S + K^T diag(e^{gamma_c - gamma}) U
+    // ---- (Q S)^T (rows n, columns t); U's operands are packed between its steps
+    f32x4 ot[NB][4];
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) ot[nb][tb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    bf16x8 qa[2][4], ub[2][NB], upb[2][NB], kt[8], pa[6];
     float egt[4];
+    float gc = 0.f;
 #pragma unroll
-    for (int tb = 0; tb < 4; ++tb) egt[tb] = cb.eg[16 * tb + li];
-    const float gc = cb.eg[BT - 1];
-    bf16x8 ub[2][NB], upb[2][NB];
+    for (int tb = 0; tb < 4; ++tb) qa[0][tb] = lds8(cb.q + roff[0] + 16 * tb * D);
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      const f32x4 d0 = *reinterpret_cast<const f32x4*>(&cb.ed[32 * kk + 4 * lg]);
-      const f32x4 d1 = *reinterpret_cast<const f32x4*>(&cb.ed[32 * kk + 16 + 4 * lg]);
+    for (int kk = 0; kk < 4; ++kk) {
+      const int cur = kk & 1;
+      fence();
+      if (kk < 3) {
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb) qa[cur ^ 1][tb] = lds8(cb.q + roff[kk + 1] + 16 * tb * D);
+      }
+      if (kk == 3) {  // the operands of O
+#pragma unroll
+        for (int tb = 0, e = 0; tb < 4; ++tb)
+#pragma unroll
+          for (int k2 = 0; k2 <= (tb >> 1); ++k2, ++e) pa[e] = lds8(pb + poff + 16 * tb * PP + 32 * k2);
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb) egt[tb] = cb.eg[16 * tb + li];
+        gc = cb.eg[BT - 1];
+      }
+      fence();
+      bf16x8 sb[NB];  // packed again (opaquely: keeping the K S loop's costs 32 registers)
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
-        ub[kk][nb] = pair_operand(u[2 * kk][nb], u[2 * kk + 1][nb]);
-        upb[kk][nb] = pair_operand(u[2 * kk][nb] * d0, u[2 * kk + 1][nb] * d1);
+        f32x4 lo = sacc[2 * kk][nb], hi = sacc[2 * kk + 1][nb];
+        asm volatile("" : "+v"(lo), "+v"(hi));
+        sb[nb] = pair_state(lo, hi, sw);
+      }
+#pragma unroll
+      for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) ot[nb][tb] = mfma(sb[nb], qa[cur][tb], ot[nb][tb]);
+      if (kk == 1) {
+#pragma unroll
+        for (int k2 = 0; k2 < 2; ++k2) {
+          const f32x4 d0 = *reinterpret_cast<const f32x4*>(&cb.ed[32 * k2 + 4 * lg]);
+          const f32x4 d1 = *reinterpret_cast<const f32x4*>(&cb.ed[32 * k2 + 16 + 4 * lg]);
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb) {
+            ub[k2][nb] = pair_operand(u[2 * k2][nb], u[2 * k2 + 1][nb]);
+            upb[k2][nb] = pair_operand(u[2 * k2][nb] * d0, u[2 * k2 + 1][nb] * d1);
+          }
+        }
       }
     }
-    bf16x8 kt[8];
+    fence();
+    // ---- O^T = Gamma-scaled (Q S)^T + U^T P^T;  S <- Gamma_c S + K^T diag(e^{gamma_c - gamma}) U
 #pragma unroll
     for (int db = 0; db < 8; ++db) {
       const uint16_t* src = cb.k + toff[db >> 1][db & 1];
       kt[db] = cat(ldtr(src), ldtr(src + 16 * D));
     }
-    bf16x8 pa[6];
-#pragma unroll
-    for (int tb = 0, e = 0; tb < 4; ++tb)
-#pragma unroll
-      for (int kk = 0; kk <= (tb >> 1); ++kk, ++e) pa[e] = lds8(pb + poff + 16 * tb * PP + 32 * kk);
     fence();
 #pragma unroll
     for (int tb = 0; tb < 4; ++tb)
