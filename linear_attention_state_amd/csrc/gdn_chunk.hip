@@ -597,12 +597,12 @@ __device__ __forceinline__ void state_role(Smem& sm, float* sst, const ScanArgs&
         gc = cb.eg[BT - 1];
       }
       fence();
-      bf16x8 sb[NB];  // packed again (opaquely: keeping the K S loop's costs 32 registers)
+      bf16x8 sb[NB];  // packed again: an empty asm hides that the K S loop packed the same
+                      // values, which would otherwise be kept alive (32 registers)
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
-        f32x4 lo = sacc[2 * kk][nb], hi = sacc[2 * kk + 1][nb];
-        asm volatile("" : "+v"(lo), "+v"(hi));
-        sb[nb] = pair_state(lo, hi, sw);
+        asm volatile("" : "+v"(sacc[2 * kk][nb]), "+v"(sacc[2 * kk + 1][nb]));
+        sb[nb] = pair_state(sacc[2 * kk][nb], sacc[2 * kk + 1][nb], sw);
       }
 #pragma unroll
       for (int tb = 0; tb < 4; ++tb)
@@ -640,30 +640,28 @@ __device__ __forceinline__ void state_role(Smem& sm, float* sst, const ScanArgs&
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb)
           ot[nb][tb] = mfma(ub[kk][nb], pa[kk == 0 ? (tb < 2 ? tb : 2 * tb - 2) : 2 * tb - 1], ot[nb][tb]);
+    // tokens 0..31, then 32..63; the second half's operands are read during the
+    // first half's products
+    bf16x8 kn[8];
+    fence();
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      bf16x8 kn[8];
-      fence();
-      if (kk == 0) {
-#pragma unroll
-        for (int db = 0; db < 8; ++db) {
-          const uint16_t* src = cb.k + toff[db >> 1][db & 1] + 32 * D;
-          kn[db] = cat(ldtr(src), ldtr(src + 16 * D));
-        }
-      }
-      fence();
-#pragma unroll
-      for (int db = 0; db < 8; ++db)
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-          if (kk == 0) sacc[db][nb] *= gc;
-          sacc[db][nb] = mfma(kt[db], upb[kk][nb], sacc[db][nb]);
-        }
-      if (kk == 0) {
-#pragma unroll
-        for (int db = 0; db < 8; ++db) kt[db] = kn[db];
-      }
+    for (int db = 0; db < 8; ++db) {
+      const uint16_t* src = cb.k + toff[db >> 1][db & 1] + 32 * D;
+      kn[db] = cat(ldtr(src), ldtr(src + 16 * D));
     }
+    fence();
+#pragma unroll
+    for (int db = 0; db < 8; ++db)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        sacc[db][nb] *= gc;
+        sacc[db][nb] = mfma(kt[db], upb[0][nb], sacc[db][nb]);
+      }
+    fence();
+#pragma unroll
+    for (int db = 0; db < 8; ++db)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) sacc[db][nb] = mfma(kn[db], upb[1][nb], sacc[db][nb]);
     fence();
     // ---- O rows: lane holds O[16 tb + li][n0 + 8 lg .. +7]; one buffer range per
     //      16-row block drops the rows past the end
