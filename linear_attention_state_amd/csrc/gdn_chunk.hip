@@ -54,12 +54,9 @@
 // operand over the 32 k values {4grp..4grp+3, 16+4grp..16+4grp+3} of step kk
 // ("pair order").  The state rows are kept in registers relabelled so that
 // pair order over d is natural order over the columns of K and Q: register
-// row d = 32kk + 16h + 4g + i holds state row sigma(d) = 32kk + 8g + 4(h ^ (g >> 1)) + i,
-// so a pair operand over d is one natural 16-byte chunk of a K or Q row (its
-// halves swapped in lanes with g >= 2).  K and Q rows can then stay in natural
-// column order in LDS, and the transposed reads of K for the state update
-// alternate 8-byte halves between lane groups, which keeps them free of bank
-// conflicts.
+// row d = 32kk + 16h + 4g + i holds state row sigma(d) = 32kk + 8g + 4h + i, so
+// a pair operand over d is one natural 16-byte chunk of a K or Q row, and K
+// and Q rows can stay in natural column order in LDS.
 #include "gdn_device.h"
 
 namespace gdn {
@@ -387,13 +384,7 @@ __device__ __forceinline__ void wait_flag(const int* flag, int target) {
 
 // state row held in register row d (see the header)
 __device__ __forceinline__ constexpr int sigma(int d) {
-  return (d & ~31) | (((d >> 2) & 3) << 3) | ((((d >> 4) ^ (d >> 3)) & 1) << 2) | (d & 3);
-}
-// pair operand over d of two state tiles: halves swapped when `sw` (lanes with g >= 2)
-__device__ __forceinline__ bf16x8 pair_state(f32x4 lo, f32x4 hi, bool sw) {
-  const u32x4 a = __builtin_bit_cast(u32x4, pair_operand(lo, hi));
-  const u32x4 r = {sw ? a[2] : a[0], sw ? a[3] : a[1], sw ? a[0] : a[2], sw ? a[1] : a[3]};
-  return __builtin_bit_cast(bf16x8, r);
+  return (d & ~31) | (((d >> 2) & 3) << 3) | (((d >> 4) & 1) << 2) | (d & 3);
 }
 
 // Rows 16 B0 .. 16 B1 + 15 of P = M o Q K^T for one chunk, into a P buffer:
@@ -480,13 +471,12 @@ __device__ __forceinline__ void state_role(Smem& sm, float* sst, const ScanArgs&
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk) roff[kk] = swz_off(li, 32 * kk + 8 * lg);
   // K^T operand for register rows 16 db..: the transposed-read source lane reads
-  // row 4 lg + i (+32 kk, +16), columns sigma(16 db + 4 a) = 32 (db >> 1) + 8 a + 4 ((db & 1) ^ (a >> 1))
+  // row 4 lg + i (+32 kk, +16), columns sigma(16 db + 4 a) = 32 (db >> 1) + 8 a + 4 (db & 1)
   int toff[4][2];
 #pragma unroll
   for (int h = 0; h < 4; ++h)
 #pragma unroll
-    for (int e = 0; e < 2; ++e) toff[h][e] = swz_off(4 * lg + ln.i, 32 * h + 8 * ln.a) + 4 * (e ^ (ln.a >> 1));
-  const bool sw = lg >= 2;
+    for (int e = 0; e < 2; ++e) toff[h][e] = swz_off(4 * lg + ln.i, 32 * h + 8 * ln.a) + 4 * e;
   // V in D layout: source lane reads row 4 lg + i (+16 tb), columns n0 + 8 a + 4 nb .. +3
   int voffs[NB];
 #pragma unroll
@@ -535,7 +525,7 @@ __device__ __forceinline__ void state_role(Smem& sm, float* sst, const ScanArgs&
       fence();
       bf16x8 sb[NB];
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) sb[nb] = pair_state(sacc[2 * kk][nb], sacc[2 * kk + 1][nb], sw);
+      for (int nb = 0; nb < NB; ++nb) sb[nb] = pair_operand(sacc[2 * kk][nb], sacc[2 * kk + 1][nb]);
 #pragma unroll
       for (int tb = 0; tb < 4; ++tb)
 #pragma unroll
@@ -602,7 +592,7 @@ __device__ __forceinline__ void state_role(Smem& sm, float* sst, const ScanArgs&
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
         asm volatile("" : "+v"(sacc[2 * kk][nb]), "+v"(sacc[2 * kk + 1][nb]));
-        sb[nb] = pair_state(sacc[2 * kk][nb], sacc[2 * kk + 1][nb], sw);
+        sb[nb] = pair_operand(sacc[2 * kk][nb], sacc[2 * kk + 1][nb]);
       }
 #pragma unroll
       for (int tb = 0; tb < 4; ++tb)
