@@ -73,9 +73,26 @@ int64_t ssm_state_bytes(const gdn_layer_desc* d) {
 
 size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
-// The workspace holds the conv output of the packed row for the chunked prefill.
+// The workspace holds the conv output of the packed row for the chunked
+// prefill, then the task counters of the conv run inside the scan kernel.
 size_t workspace_bytes_for(const gdn_layer_desc* d, int64_t total_tokens) {
-  return round_up((size_t)total_tokens * (size_t)channels(d) * (size_t)act_size(d), 256);
+  if (total_tokens <= 0) return 0;
+  return round_up((size_t)total_tokens * (size_t)channels(d) * (size_t)act_size(d), 256) + gdn::kFusedSyncBytes;
+}
+
+// Compute units of the device that owns `st` (0 if unknown), looked up once per device.
+int device_cus(hipStream_t st) {
+  static std::mutex mu;
+  static std::vector<int> cus;
+  int dev = 0;
+  if (hipStreamGetDevice(st, &dev) != hipSuccess || dev < 0) return 0;
+  std::lock_guard<std::mutex> lock(mu);
+  if ((int)cus.size() <= dev) cus.resize(dev + 1, -1);
+  if (cus[dev] < 0) {
+    int n = 0;
+    cus[dev] = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess ? n : 0;
+  }
+  return cus[dev];
 }
 
 bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
@@ -268,33 +285,18 @@ extern "C" int gdn_varlen_forward(const gdn_layer_desc* desc, const void* x, con
   sa.num_v_heads = desc->num_v_heads; sa.channels = C;
 
   // Order on the stream: (1) conv + SiLU + norm of the packed row into the
-  // workspace for the chunked prefill, (2) chunked prefill, (3) the token path
+  // workspace for the chunked prefill (its own kernel, or inside the chunk
+  // kernel ahead of the scans), (2) chunked prefill, (3) the token path
   // (decode, or everything in fp32 / other head sizes), which runs its own conv
   // from the conv states, (4) conv-state commit, last, once every reader of the
   // old conv states has been enqueued.
   const bool chunked = bf16 && gdn::chunk_supported(desc->head_k_dim, desc->head_v_dim);
   if (chunked && n_long > 0) {
-    gdn::ConvArgs ca{};
-    ca.x = x; ca.w = conv_weight; ca.cu = cu_seqlens; ca.read_idx = read_idx; ca.write_idx = write_idx;
-    ca.conv_pool = reinterpret_cast<const char*>(conv_pool); ca.conv_stride = conv_block_stride;
-    ca.y = workspace;
-    ca.num_seqs = num_seqs; ca.total_tokens = total_tokens; ca.num_blocks = num_blocks; ca.channels = C;
-    ca.qk_channels = desc->num_k_heads * desc->head_k_dim; ca.head_k_dim = desc->head_k_dim;
-    {  // about 4096 one-wave blocks (16 per CU): rows per block a multiple of the 4 rows in flight
-      const int groups = (C + 511) / 512;
-      const int slices = std::max(1, 4096 / groups);
-      const int rows = (total_tokens + slices - 1) / slices;
-      ca.rows_per_block = std::min(256, std::max(4, (rows + 3) / 4 * 4));
-    }
-    ca.eps = sa.eps;
-    ca.q_scale = sa.q_scale;
-    e = timed(K_CONV, st, [&] { return gdn::launch_conv(ca, W, bf16, st); });
-    if (e != hipSuccess) return fail(GDN_EHIP, "conv launch: %s", hipGetErrorString(e));
     sa.min_len = 2; sa.max_len = INT_MAX;
     // longest sequences first, so the longest chains start before the short ones
     static thread_local gdn::SeqOrder order;
     order.n = 0;
-    if (n_long <= gdn::kMaxOrder) {
+    if (n_long <= gdn::kMaxOrder && num_seqs <= 65535) {
       std::vector<std::pair<int, int>> lens;
       lens.reserve(n_long);
       for (int i = 0; i < num_seqs; ++i) {
@@ -304,9 +306,63 @@ extern "C" int gdn_varlen_forward(const gdn_layer_desc* desc, const void* x, con
       std::stable_sort(lens.begin(), lens.end());
       for (size_t i = 0; i < lens.size(); ++i) order.seq[i] = (uint16_t)lens[i].second;
       order.n = (int32_t)lens.size();
-      if (num_seqs > 65535) order.n = 0;
     }
-    e = timed(K_CHUNK, st, [&] { return gdn::launch_chunk(sa, order, desc->head_k_dim, desc->head_v_dim, st); });
+    // The conv of the chunked rows runs inside the scan kernel when every
+    // workgroup of the scan is resident at once (one per CU): the workgroups
+    // convert rows, longest sequence first, until their own sequence's rows are
+    // all taken, and start their scans while the others go on converting.
+    // Otherwise the conv kernel writes all of y first.
+    static thread_local gdn::FusedConv fc;
+    fc.n = 0;
+    if (order.n > 0 && order.n <= gdn::kMaxFusedRanks && aligned(conv_weight, 16) &&
+        (int64_t)order.n * desc->num_v_heads <= device_cus(st)) {
+      fc.slices = (C + gdn::kConvTaskChannels - 1) / gdn::kConvTaskChannels;
+      fc.first[0] = 0;
+      // Time model (microseconds, measured on the 128 x 128 head): a scan
+      // takes 11 + 2.8 per chunk; a conv task moves its rows in and out at
+      // about 17 GB/s per workgroup; the conv kernel runs at about 4.2 TB/s.
+      const double scan0 = 11.0, scan1 = 2.8;
+      const double task_us = 2.0 * gdn::kConvTaskRows * std::min(C, gdn::kConvTaskChannels) * act_size(desc) / 17e3;
+      double scans = 0.0;
+      for (int r = 0; r < order.n; ++r) {
+        const int L = cu_seqlens_host[order.seq[r] + 1] - cu_seqlens_host[order.seq[r]];
+        fc.first[r + 1] = fc.first[r] + (L + gdn::kConvTaskRows - 1) / gdn::kConvTaskRows * fc.slices;
+        scans += scan0 + scan1 * ((L + 63) / 64);
+      }
+      const int L0 = cu_seqlens_host[order.seq[0] + 1] - cu_seqlens_host[order.seq[0]];
+      const double longest = scan0 + scan1 * ((L0 + 63) / 64);
+      // work spread evenly over the workgroups, but no earlier than the longest scan allows
+      const double fused = std::max((fc.first[order.n] * task_us + desc->num_v_heads * scans) /
+                                    ((double)order.n * desc->num_v_heads), longest + 2.0 * task_us);
+      const double apart = 2.0 * (double)total_tokens * C * act_size(desc) / 4.2e6 + longest + 3.0;
+      if (1.05 * fused < apart) {
+        fc.n = order.n;
+        fc.sync = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(workspace) + (need - gdn::kFusedSyncBytes));
+        fc.target = (int32_t)(fused * 100.0);  // 100 ticks per microsecond
+        fc.task = (int32_t)(task_us * 100.0);
+        fc.scan0 = (int32_t)(scan0 * 100.0);
+        fc.scan1 = (int32_t)(scan1 * 100.0);
+      }
+    }
+    if (fc.n == 0) {
+      gdn::ConvArgs ca{};
+      ca.x = x; ca.w = conv_weight; ca.cu = cu_seqlens; ca.read_idx = read_idx; ca.write_idx = write_idx;
+      ca.conv_pool = reinterpret_cast<const char*>(conv_pool); ca.conv_stride = conv_block_stride;
+      ca.y = workspace;
+      ca.num_seqs = num_seqs; ca.total_tokens = total_tokens; ca.num_blocks = num_blocks; ca.channels = C;
+      ca.qk_channels = desc->num_k_heads * desc->head_k_dim; ca.head_k_dim = desc->head_k_dim;
+      {  // about 4096 one-wave blocks (16 per CU): rows per block a multiple of the 4 rows in flight
+        const int groups = (C + 511) / 512;
+        const int slices = std::max(1, 4096 / groups);
+        const int rows = (total_tokens + slices - 1) / slices;
+        ca.rows_per_block = std::min(256, std::max(4, (rows + 3) / 4 * 4));
+      }
+      ca.eps = sa.eps;
+      ca.q_scale = sa.q_scale;
+      e = timed(K_CONV, st, [&] { return gdn::launch_conv(ca, W, bf16, st); });
+      if (e != hipSuccess) return fail(GDN_EHIP, "conv launch: %s", hipGetErrorString(e));
+    }
+    e = timed(K_CHUNK, st, [&] { return gdn::launch_chunk(sa, order, fc, desc->head_k_dim, desc->head_v_dim, st); });
     if (e != hipSuccess) return fail(GDN_EHIP, "chunk scan launch: %s", hipGetErrorString(e));
   }
   if (!chunked || n_short > 0) {

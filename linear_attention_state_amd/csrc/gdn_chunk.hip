@@ -45,6 +45,14 @@
 // v_mfma_f32_16x16x32_bf16 (bf16 operands, fp32 accumulate).  Sequences are
 // launched longest first.
 //
+// Before the scans, the workgroups can also run the depthwise conv + SiLU +
+// q/k normalisation of the launch's rows themselves, as tasks claimed from a
+// global counter (conv_phase below): the workgroups of the longest sequences
+// start their scans as soon as their own rows are done, while the others go
+// on converting, so most of the conv is hidden behind the long scans.  The
+// host picks this when every workgroup is resident at once (one per CU) and
+// its time model says it pays; otherwise a separate conv kernel runs first.
+//
 // MFMA 16x16x32 bf16 operand layout (lane l, r = l & 15, grp = l >> 4):
 //   A: row r, 8 values of k;  B: column r, the same 8 values of k;
 //   D: column r, rows 4*grp + {0,1,2,3}.
@@ -95,6 +103,7 @@ struct alignas(16) Smem {
   float gw[BT];               // gamma, gram wave
   int dflag;                  // chunks whose Q / K / V rows are in LDS
   int aflag;                  // chunks whose diagonal blocks of A are in `at`
+  int task;                   // conv task claimed by thread 0, for the workgroup
 };
 static_assert(sizeof(Smem) <= 160 * 1024, "LDS");
 static_assert(D * PS * 4 <= sizeof(ChunkBuf) * 2, "state staging");
@@ -817,13 +826,181 @@ __device__ __forceinline__ void p_role(Smem& sm, const Seq& q, const Lane& ln) {
   }
 }
 
-__global__ __launch_bounds__(NT) void chunk_scan_kernel(ScanArgs a, SeqOrder ord) {
+// ---- the conv of the chunked rows, run by the scan workgroups as claimed tasks
+//
+// Every workgroup first claims conv tasks (16 rows x 4096 channels of one
+// sequence; the tasks of the longest sequence come first) from a counter in
+// global memory: at least until every task of its own sequence has been
+// claimed, and beyond that while its scan, priced by the host's time model,
+// can still end by the host's estimate of the balanced finish.  It then waits
+// until its own sequence's tasks are finished and starts its scan.  A
+// workgroup only ever waits for tasks that are already claimed, and a claimed
+// task never waits for anything, so the wait ends whatever the number of
+// resident workgroups.  The rows are computed exactly as by the conv kernel
+// (same tap order, SiLU, and head reduction across the 16 lanes of a key
+// head), so y is bitwise the same either way.
+//
+// Visibility across XCDs without writing back whole L2 caches: the rows are
+// stored with device-scope coherence (the SC1 bit, as the compiler emits for an
+// agent-scope atomic store), every wave waits for its stores to complete, the
+// workgroup meets at a barrier, and only then is the task counted.  A
+// workgroup that has seen its count reach the total invalidates its caches (an
+// agent-scope acquire fence) before the scan reads the rows.
+constexpr int kStoreDeviceScope = 16 | 2;  // buffer store cache policy: SC1 (device scope) | NT (streaming)
+
+// One task: rows [r0, r0 + n) of sequence s (rows from seq0), channels c0..c0+7 per thread.
+template <int W>
+__device__ __forceinline__ void conv_task(const ScanArgs& a, int s, int seq0, int r0, int n, int c0) {
+  const int C = a.channels;
+  const gptr<const u32x4> x = as_global(reinterpret_cast<const u32x4*>(a.x));
+  // taps: w[c][j], 8 channels x W taps contiguous
+  float wt[8][W];
+  {
+    const gptr<const u32x4> wp = as_global(reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(a.w) + (int64_t)c0 * W));
+    u32x4 wr[W];
+#pragma unroll
+    for (int i = 0; i < W; ++i) wr[i] = wp[i];
+#pragma unroll
+    for (int i = 0; i < 8 * W; ++i) {
+      const uint32_t word = wr[i / 8][(i % 8) / 2];
+      wt[i / W][i % W] = __uint_as_float((i & 1) ? (word & 0xffff0000u) : (word << 16));
+    }
+  }
+  // the W-1 inputs before r0 (earlier rows of the sequence, else its conv state, else zero) and the rows
+  u32x4 hx[W > 1 ? W - 1 : 1];
+  u32x4 rx[kConvTaskRows];
+  const bool act = seq_active(a.read_idx, a.write_idx, s, a.num_blocks);
+  const int64_t cq = c0 / 8;  // 16-byte column of this thread
+#pragma unroll
+  for (int j = 1; j < W; ++j) {
+    const int p = r0 - j;
+    hx[j - 1] = u32x4{0u, 0u, 0u, 0u};
+    if (p >= seq0) {
+      hx[j - 1] = x[(int64_t)p * (C / 8) + cq];
+    } else if (act) {
+      const gptr<const u32x4> tail = as_global(reinterpret_cast<const u32x4*>(a.conv_pool + (int64_t)a.read_idx[s] * a.conv_stride));
+      hx[j - 1] = tail[(int64_t)(W - 1 + p - seq0) * (C / 8) + cq];
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < kConvTaskRows; ++k)  // rows past the task's end load its last row again (no branch)
+    rx[k] = __builtin_nontemporal_load(&x[(int64_t)(r0 + min(k, n - 1)) * (C / 8) + cq]);
+  const bool do_norm = c0 < 2 * a.num_k_heads * D;
+  const float scale = c0 < a.num_k_heads * D ? a.q_scale : 1.0f;
+  // window of the last 4 inputs, slot (row mod 4)
+  float xw[4][8];
+#pragma unroll
+  for (int j = 1; j < W; ++j)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      xw[(4 - j) & 3][2 * i] = __uint_as_float(hx[j - 1][i] << 16);
+      xw[(4 - j) & 3][2 * i + 1] = __uint_as_float(hx[j - 1][i] & 0xffff0000u);
+    }
+  const __amdgpu_buffer_rsrc_t ys = make_rsrc(reinterpret_cast<const uint16_t*>(a.y) + (int64_t)r0 * C, (uint32_t)(n * C * 2));
+#pragma unroll
+  for (int k = 0; k < kConvTaskRows; ++k) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      xw[k & 3][2 * i] = __uint_as_float(rx[k][i] << 16);
+      xw[k & 3][2 * i + 1] = __uint_as_float(rx[k][i] & 0xffff0000u);
+    }
+    float yv[8];
+    float ss = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float acc = wt[e][W - 1] * xw[k & 3][e];
+#pragma unroll
+      for (int j = 1; j < W; ++j) acc += wt[e][W - 1 - j] * xw[(k - j) & 3][e];
+      yv[e] = silu(acc);
+      ss += yv[e] * yv[e];
+    }
+    for (int off = 1; off < D / 8; off <<= 1) ss += __shfl_xor(ss, off);
+    if (do_norm) {
+      const float inv = scale * rsqrt_fast(ss + a.eps);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) yv[e] *= inv;
+    }
+    u32x4 o;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o[i] = pack_bf16x2(yv[2 * i], yv[2 * i + 1]);
+    if (k < n) __builtin_amdgcn_raw_buffer_store_b128(o, ys, (k * C + c0) * 2, 0, kStoreDeviceScope);
+  }
+}
+
+// Claims and runs conv tasks (at least until every task of `rank` is claimed),
+// then waits for the tasks of `rank` to finish.  All threads of the workgroup call it.
+template <int W>
+__device__ void conv_phase(Smem& sm, const ScanArgs& a, const SeqOrder& ord, const FusedConv& fc, int rank) {
+  const int tid = threadIdx.x;
+  const int total = fc.first[fc.n];
+  const int last = fc.first[rank + 1];  // my rank's tasks end here
+  int* next = fc.sync;
+  // latest start of a task that is to be followed by one more and by my scan
+  const int my_s = ord.seq[rank];
+  const int32_t latest = fc.target - fc.scan0 - fc.scan1 * ((a.cu[my_s + 1] - a.cu[my_s] + BT - 1) / BT) - 2 * fc.task;
+  const uint64_t t_begin = __builtin_amdgcn_s_memrealtime();
+  if (tid == 0) sm.task = __hip_atomic_fetch_add(next, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  lds_barrier();
+  int t = sm.task;
+  while (t < total) {
+    lds_barrier();  // every thread has read sm.task
+    // claim the following task while this one runs, while my rank has unclaimed
+    // tasks or there is time for one more before my scan
+    int pre = total;
+    if (tid == 0 && (t < last - 1 || (int64_t)(__builtin_amdgcn_s_memrealtime() - t_begin) <= latest))
+      pre = __hip_atomic_fetch_add(next, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    int lo = 0, hi = fc.n;  // rank r of task t: first[r] <= t < first[r + 1]
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (fc.first[mid] <= t) lo = mid; else hi = mid;
+    }
+    const int loc = t - fc.first[lo];
+    const int s = ord.seq[lo];
+    const int seq0 = a.cu[s], seq1 = a.cu[s + 1];
+    const int r0 = seq0 + (loc / fc.slices) * kConvTaskRows;
+    const int c0 = (loc % fc.slices) * kConvTaskChannels + tid * 8;
+    if (c0 < a.channels) conv_task<W>(a, s, seq0, r0, min(kConvTaskRows, seq1 - r0), c0);
+    // publish: every wave's device-scope stores complete, then one count
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    if (tid == 0) sm.task = pre;
+    __syncthreads();
+    if (tid == 0) __hip_atomic_fetch_add(&fc.sync[1 + lo], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    t = sm.task;
+  }
+  if (tid == 0) {
+    const int need = last - fc.first[rank];
+    // bounded: every task counted here is claimed and finishes without waiting
+    for (int it = 0; it < (1 << 24); ++it) {
+      if (__hip_atomic_load(&fc.sync[1 + rank], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= need) break;
+      __builtin_amdgcn_s_sleep(2);
+    }
+  }
+  __syncthreads();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+}
+
+__device__ __forceinline__ void conv_phase_w(Smem& sm, const ScanArgs& a, const SeqOrder& ord, const FusedConv& fc,
+                                             int rank) {
+  switch (a.width) {
+    case 1: conv_phase<1>(sm, a, ord, fc, rank); break;
+    case 2: conv_phase<2>(sm, a, ord, fc, rank); break;
+    case 3: conv_phase<3>(sm, a, ord, fc, rank); break;
+    default: conv_phase<4>(sm, a, ord, fc, rank); break;
+  }
+}
+
+__global__ void zero_sync_kernel(int32_t* p, int n) {
+  for (int i = threadIdx.x; i < n; i += blockDim.x) p[i] = 0;
+}
+
+__global__ __launch_bounds__(NT) void chunk_scan_kernel(ScanArgs a, SeqOrder ord, FusedConv fc) {
   __shared__ Smem sm;
   const int Hv = a.num_v_heads;
   const int rank = blockIdx.x / Hv;
   Seq q;
   q.m = blockIdx.x % Hv;
   q.s = ord.n > 0 ? (rank < ord.n ? (int)ord.seq[rank] : a.num_seqs) : rank;
+  if (fc.n > 0) conv_phase_w(sm, a, ord, fc, rank);  // every rank < fc.n == ord.n
   if (q.s >= a.num_seqs) return;
   q.r0 = a.cu[q.s];
   q.L = a.cu[q.s + 1] - q.r0;
@@ -893,11 +1070,19 @@ __global__ __launch_bounds__(NT) void chunk_scan_kernel(ScanArgs a, SeqOrder ord
 
 bool chunk_supported(int dk, int dv) { return dk == D && dv == D; }
 
-hipError_t launch_chunk(const ScanArgs& a, const SeqOrder& order, int dk, int dv, hipStream_t st) {
+hipError_t launch_chunk(const ScanArgs& a, const SeqOrder& order, const FusedConv& fc, int dk, int dv,
+                        hipStream_t st) {
   if (!chunk_supported(dk, dv)) return hipErrorInvalidValue;
+  if (fc.n > 0 && (fc.n != order.n || fc.n > kMaxFusedRanks || !fc.sync || a.width < 1 || a.width > 4))
+    return hipErrorInvalidValue;
   const int rows = order.n > 0 ? order.n : a.num_seqs;
+  if (fc.n > 0) {  // the task counters start at zero (a kernel, not a memset, so the call stays capturable)
+    hipLaunchKernelGGL(zero_sync_kernel, dim3(1), dim3(256), 0, st, fc.sync, 1 + fc.n);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   dim3 grid(rows * a.num_v_heads);
-  hipLaunchKernelGGL(chunk_scan_kernel, grid, dim3(NT), 0, st, a, order);
+  hipLaunchKernelGGL(chunk_scan_kernel, grid, dim3(NT), 0, st, a, order, fc);
   return hipGetLastError();
 }
 

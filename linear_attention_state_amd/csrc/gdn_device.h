@@ -129,7 +129,31 @@ struct SeqOrder {
 hipError_t launch_conv(const ConvArgs& a, int width, bool bf16, hipStream_t st);
 hipError_t launch_tail_commit(const TailArgs& a, int width, bool bf16, hipStream_t st);
 hipError_t launch_recurrent(const ScanArgs& a, int dk, int dv, bool bf16, hipStream_t st);
-hipError_t launch_chunk(const ScanArgs& a, const SeqOrder& order, int dk, int dv, hipStream_t st);
+// The conv of the chunked sequences run by the chunk-scan workgroups
+// themselves, as tasks they claim before their scans.  Task t belongs to
+// rank r of the launch order when first[r] <= t < first[r + 1]; it covers rows
+// [cu[s] + b * kConvTaskRows, ...) of sequence s = order.seq[r] and channels
+// [c * kConvTaskChannels, ...), with b = (t - first[r]) / slices and
+// c = (t - first[r]) % slices.  n == 0: y was written by the conv kernel.
+constexpr int kConvTaskRows = 16;
+constexpr int kConvTaskChannels = 4096;
+constexpr int kMaxFusedRanks = 256;
+// Times are in ticks of the 100 MHz real-time counter, counted from the start
+// of a workgroup's conv phase.  A workgroup of a sequence with N chunks keeps
+// claiming tasks beyond its own sequence's while it can still finish one more
+// task and its scan by `target`: its scan is priced scan0 + N * scan1, a task
+// `task`.  The figures only steer who converts which rows, never the result.
+struct FusedConv {
+  int32_t n;         // ranks (entries of the launch order), 0 = no fused conv
+  int32_t slices;    // channel slices per row block
+  int32_t* sync;     // [0] next task to claim, [1 + r] tasks of rank r finished; zero before the launch
+  int32_t target, task, scan0, scan1;
+  int32_t first[kMaxFusedRanks + 1];
+};
+constexpr size_t kFusedSyncBytes = 4096;  // room for sync[0 .. kMaxFusedRanks]
+
+hipError_t launch_chunk(const ScanArgs& a, const SeqOrder& order, const FusedConv& fc, int dk, int dv,
+                        hipStream_t st);
 bool chunk_supported(int dk, int dv);
 
 }  // namespace gdn
