@@ -338,7 +338,8 @@ extern "C" int gdn_varlen_forward(const gdn_layer_desc* desc, const void* x, con
       if (1.05 * fused < apart) {
         fc.n = order.n;
         fc.sync = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(workspace) + (need - gdn::kFusedSyncBytes));
-        fc.target = (int32_t)(fused * 100.0);  // 100 ticks per microsecond
+        // 100 ticks per microsecond; aiming 3% past the even spread measured best
+        fc.target = (int32_t)(fused * 103.0);
         fc.task = (int32_t)(task_us * 100.0);
         fc.scan0 = (int32_t)(scan0 * 100.0);
         fc.scan1 = (int32_t)(scan1 * 100.0);

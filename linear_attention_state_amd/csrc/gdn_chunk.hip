@@ -848,73 +848,125 @@ __device__ __forceinline__ void p_role(Smem& sm, const Seq& q, const Lane& ln) {
 // agent-scope acquire fence) before the scan reads the rows.
 constexpr int kStoreDeviceScope = 16 | 2;  // buffer store cache policy: SC1 (device scope) | NT (streaming)
 
-// One task: rows [r0, r0 + n) of sequence s (rows from seq0), channels c0..c0+7 per thread.
+// One task: rows [r0, r0 + n) of sequence s (rows from seq0) at channels
+// c0..c0+7 of each thread; `on` is false for the threads past the channel count.
+struct ConvTask {
+  int rank, s, seq0, r0, n, c0;
+  bool on;
+};
+
+__device__ __forceinline__ ConvTask conv_decode(const ScanArgs& a, const SeqOrder& ord, const FusedConv& fc, int t) {
+  int lo = 0, hi = fc.n;  // rank of task t: first[r] <= t < first[r + 1]
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (fc.first[mid] <= t) lo = mid; else hi = mid;
+  }
+  ConvTask k;
+  const int loc = t - fc.first[lo];
+  k.rank = lo;
+  k.s = ord.seq[lo];
+  k.seq0 = a.cu[k.s];
+  k.r0 = k.seq0 + (loc / fc.slices) * kConvTaskRows;
+  k.n = min(kConvTaskRows, a.cu[k.s + 1] - k.r0);
+  k.c0 = (loc % fc.slices) * kConvTaskChannels + (int)threadIdx.x * 8;
+  k.on = k.c0 < a.channels;
+  return k;
+}
+
+// A task's inputs in registers: the W-1 inputs before r0 (earlier rows of the
+// sequence, else its conv state, else zero), the taps w[c][j] (8 channels x W
+// contiguous), and the rows.
 template <int W>
-__device__ __forceinline__ void conv_task(const ScanArgs& a, int s, int seq0, int r0, int n, int c0) {
-  const int C = a.channels;
-  const gptr<const u32x4> x = as_global(reinterpret_cast<const u32x4*>(a.x));
-  // taps: w[c][j], 8 channels x W taps contiguous
-  float wt[8][W];
-  {
-    const gptr<const u32x4> wp = as_global(reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(a.w) + (int64_t)c0 * W));
-    u32x4 wr[W];
-#pragma unroll
-    for (int i = 0; i < W; ++i) wr[i] = wp[i];
-#pragma unroll
-    for (int i = 0; i < 8 * W; ++i) {
-      const uint32_t word = wr[i / 8][(i % 8) / 2];
-      wt[i / W][i % W] = __uint_as_float((i & 1) ? (word & 0xffff0000u) : (word << 16));
-    }
-  }
-  // the W-1 inputs before r0 (earlier rows of the sequence, else its conv state, else zero) and the rows
+struct ConvIn {
   u32x4 hx[W > 1 ? W - 1 : 1];
+  u32x4 wr[W];
   u32x4 rx[kConvTaskRows];
-  const bool act = seq_active(a.read_idx, a.write_idx, s, a.num_blocks);
-  const int64_t cq = c0 / 8;  // 16-byte column of this thread
+};
+
+// Issues every load of a task; the row loads are the last kConvTaskRows
+// vector-memory instructions (rows past the task's end load its last row again).
+template <int W>
+__device__ __forceinline__ void conv_load(const ScanArgs& a, const ConvTask& k, ConvIn<W>& in) {
+  const int C = a.channels;
+  const int64_t cq = k.c0 / 8;  // 16-byte column of this thread
+  const gptr<const u32x4> x = as_global(reinterpret_cast<const u32x4*>(a.x));
+  if (k.on) {
+    const bool act = seq_active(a.read_idx, a.write_idx, k.s, a.num_blocks);
 #pragma unroll
-  for (int j = 1; j < W; ++j) {
-    const int p = r0 - j;
-    hx[j - 1] = u32x4{0u, 0u, 0u, 0u};
-    if (p >= seq0) {
-      hx[j - 1] = x[(int64_t)p * (C / 8) + cq];
-    } else if (act) {
-      const gptr<const u32x4> tail = as_global(reinterpret_cast<const u32x4*>(a.conv_pool + (int64_t)a.read_idx[s] * a.conv_stride));
-      hx[j - 1] = tail[(int64_t)(W - 1 + p - seq0) * (C / 8) + cq];
+    for (int j = 1; j < W; ++j) {
+      const int p = k.r0 - j;
+      in.hx[j - 1] = u32x4{0u, 0u, 0u, 0u};
+      if (p >= k.seq0) {
+        in.hx[j - 1] = x[(int64_t)p * (C / 8) + cq];
+      } else if (act) {
+        const gptr<const u32x4> tail =
+            as_global(reinterpret_cast<const u32x4*>(a.conv_pool + (int64_t)a.read_idx[k.s] * a.conv_stride));
+        in.hx[j - 1] = tail[(int64_t)(W - 1 + p - k.seq0) * (C / 8) + cq];
+      }
     }
-  }
+    const gptr<const u32x4> wp =
+        as_global(reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(a.w) + (int64_t)k.c0 * W));
 #pragma unroll
-  for (int k = 0; k < kConvTaskRows; ++k)  // rows past the task's end load its last row again (no branch)
-    rx[k] = __builtin_nontemporal_load(&x[(int64_t)(r0 + min(k, n - 1)) * (C / 8) + cq]);
-  const bool do_norm = c0 < 2 * a.num_k_heads * D;
-  const float scale = c0 < a.num_k_heads * D ? a.q_scale : 1.0f;
-  // window of the last 4 inputs, slot (row mod 4)
-  float xw[4][8];
+    for (int i = 0; i < W; ++i) in.wr[i] = wp[i];
+  }
+  const int64_t cr = k.on ? cq : 0;  // threads past the channel count load column 0 (never used)
+#pragma unroll
+  for (int r = 0; r < kConvTaskRows; ++r)
+    in.rx[r] = __builtin_nontemporal_load(&x[(int64_t)(k.r0 + min(r, k.n - 1)) * (C / 8) + cr]);
+}
+
+// Sum over the 16 lanes of a key head (a DPP row): the same pairings as a
+// butterfly over lane xor 1, 2, 4, 8, so every lane ends with the same bits as
+// the conv kernel's shuffle reduction (each step adds two equal partial sums
+// of the two halves, and the order of the two does not change a float sum).
+__device__ __forceinline__ float head_sum(float v) {
+  v += dpp_move<0xB1, 0xf>(v);   // quad_perm [1,0,3,2]: lane ^ 1
+  v += dpp_move<0x4E, 0xf>(v);   // quad_perm [2,3,0,1]: lane ^ 2
+  v += dpp_move<0x141, 0xf>(v);  // row_half_mirror: lane 7 - i within 8, the other quad
+  v += dpp_move<0x140, 0xf>(v);  // row_mirror: lane 15 - i, the other half row
+  return v;
+}
+
+template <int W>
+__device__ __forceinline__ void conv_compute(const ScanArgs& a, const ConvTask& k, const ConvIn<W>& in) {
+  if (!k.on) return;  // whole 16-lane head groups (the channel count is a multiple of 128)
+  const int C = a.channels;
+  float wt[8][W];
+#pragma unroll
+  for (int i = 0; i < 8 * W; ++i) {
+    const uint32_t word = in.wr[i / 8][(i % 8) / 2];
+    wt[i / W][i % W] = __uint_as_float((i & 1) ? (word & 0xffff0000u) : (word << 16));
+  }
+  const bool do_norm = k.c0 < 2 * a.num_k_heads * D;
+  const float scale = k.c0 < a.num_k_heads * D ? a.q_scale : 1.0f;
+  float xw[4][8];  // the last 4 inputs, slot (row mod 4)
 #pragma unroll
   for (int j = 1; j < W; ++j)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      xw[(4 - j) & 3][2 * i] = __uint_as_float(hx[j - 1][i] << 16);
-      xw[(4 - j) & 3][2 * i + 1] = __uint_as_float(hx[j - 1][i] & 0xffff0000u);
+      xw[(4 - j) & 3][2 * i] = __uint_as_float(in.hx[j - 1][i] << 16);
+      xw[(4 - j) & 3][2 * i + 1] = __uint_as_float(in.hx[j - 1][i] & 0xffff0000u);
     }
-  const __amdgpu_buffer_rsrc_t ys = make_rsrc(reinterpret_cast<const uint16_t*>(a.y) + (int64_t)r0 * C, (uint32_t)(n * C * 2));
+  const __amdgpu_buffer_rsrc_t ys =
+      make_rsrc(reinterpret_cast<const uint16_t*>(a.y) + (int64_t)k.r0 * C, (uint32_t)(k.n * C * 2));
 #pragma unroll
-  for (int k = 0; k < kConvTaskRows; ++k) {
+  for (int r = 0; r < kConvTaskRows; ++r) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      xw[k & 3][2 * i] = __uint_as_float(rx[k][i] << 16);
-      xw[k & 3][2 * i + 1] = __uint_as_float(rx[k][i] & 0xffff0000u);
+      xw[r & 3][2 * i] = __uint_as_float(in.rx[r][i] << 16);
+      xw[r & 3][2 * i + 1] = __uint_as_float(in.rx[r][i] & 0xffff0000u);
     }
     float yv[8];
     float ss = 0.f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      float acc = wt[e][W - 1] * xw[k & 3][e];
+      float acc = wt[e][W - 1] * xw[r & 3][e];
 #pragma unroll
-      for (int j = 1; j < W; ++j) acc += wt[e][W - 1 - j] * xw[(k - j) & 3][e];
+      for (int j = 1; j < W; ++j) acc += wt[e][W - 1 - j] * xw[(r - j) & 3][e];
       yv[e] = silu(acc);
       ss += yv[e] * yv[e];
     }
-    for (int off = 1; off < D / 8; off <<= 1) ss += __shfl_xor(ss, off);
+    ss = head_sum(ss);
     if (do_norm) {
       const float inv = scale * rsqrt_fast(ss + a.eps);
 #pragma unroll
@@ -923,12 +975,14 @@ __device__ __forceinline__ void conv_task(const ScanArgs& a, int s, int seq0, in
     u32x4 o;
 #pragma unroll
     for (int i = 0; i < 4; ++i) o[i] = pack_bf16x2(yv[2 * i], yv[2 * i + 1]);
-    if (k < n) __builtin_amdgcn_raw_buffer_store_b128(o, ys, (k * C + c0) * 2, 0, kStoreDeviceScope);
+    if (r < k.n) __builtin_amdgcn_raw_buffer_store_b128(o, ys, (r * C + k.c0) * 2, 0, kStoreDeviceScope);
   }
 }
 
 // Claims and runs conv tasks (at least until every task of `rank` is claimed),
-// then waits for the tasks of `rank` to finish.  All threads of the workgroup call it.
+// then waits for the tasks of `rank` to finish.  All threads of the workgroup
+// call it.  The loads of the next task are issued before the stores of the
+// current one are waited for, so the two latencies overlap.
 template <int W>
 __device__ void conv_phase(Smem& sm, const ScanArgs& a, const SeqOrder& ord, const FusedConv& fc, int rank) {
   const int tid = threadIdx.x;
@@ -942,30 +996,35 @@ __device__ void conv_phase(Smem& sm, const ScanArgs& a, const SeqOrder& ord, con
   if (tid == 0) sm.task = __hip_atomic_fetch_add(next, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   lds_barrier();
   int t = sm.task;
+  lds_barrier();  // every thread has read sm.task before thread 0 writes it again
+  ConvTask k{};
+  ConvIn<W> in;
+  if (t < total) {
+    k = conv_decode(a, ord, fc, t);
+    conv_load<W>(a, k, in);
+  }
   while (t < total) {
-    lds_barrier();  // every thread has read sm.task
     // claim the following task while this one runs, while my rank has unclaimed
     // tasks or there is time for one more before my scan
     int pre = total;
     if (tid == 0 && (t < last - 1 || (int64_t)(__builtin_amdgcn_s_memrealtime() - t_begin) <= latest))
       pre = __hip_atomic_fetch_add(next, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    int lo = 0, hi = fc.n;  // rank r of task t: first[r] <= t < first[r + 1]
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (fc.first[mid] <= t) lo = mid; else hi = mid;
-    }
-    const int loc = t - fc.first[lo];
-    const int s = ord.seq[lo];
-    const int seq0 = a.cu[s], seq1 = a.cu[s + 1];
-    const int r0 = seq0 + (loc / fc.slices) * kConvTaskRows;
-    const int c0 = (loc % fc.slices) * kConvTaskChannels + tid * 8;
-    if (c0 < a.channels) conv_task<W>(a, s, seq0, r0, min(kConvTaskRows, seq1 - r0), c0);
-    // publish: every wave's device-scope stores complete, then one count
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    conv_compute<W>(a, k, in);
     if (tid == 0) sm.task = pre;
-    __syncthreads();
-    if (tid == 0) __hip_atomic_fetch_add(&fc.sync[1 + lo], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    t = sm.task;
+    lds_barrier();  // the next task's number is in sm.task
+    const int u = sm.task;
+    const int done_rank = k.rank;
+    if (u < total) {
+      k = conv_decode(a, ord, fc, u);
+      conv_load<W>(a, k, in);
+    }
+    // this task's device-scope stores are older than the next task's row loads:
+    // wait for all but those, then count the task once every wave is through
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kConvTaskRows) : "memory");
+    if (u >= total) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    lds_barrier();  // also: every thread has read sm.task
+    if (tid == 0) __hip_atomic_fetch_add(&fc.sync[1 + done_rank], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    t = u;
   }
   if (tid == 0) {
     const int need = last - fc.first[rank];
