@@ -20,6 +20,11 @@ slower, and the line reports the steady rate.  The K timed steps run twice:
 once end to end for `value` and `ms_per_step`, once more with the library's
 event pair around every kernel for `kernels` and `roofline` (those events
 add a few percent to a step, so they stay out of the first pass).
+
+On the prefill workload the chunk kernel also runs the conv of the rows (its
+workgroups convert rows before their scans), so its duration covers both; the
+roofline's `frac` prices only the chunk flops over it, and `step_frac` prices
+the same flops over the whole step.
 """
 from __future__ import annotations
 
@@ -146,6 +151,10 @@ def run(cfg_id: int, steps: int, warmup: int):
         work = token_path_bytes(L, n_short)
         roof = {"bound": "hbm", "achieved": work / dom_s / 1e9, "peak": PEAK_HBM / 1e9, "unit": "GB/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
+    # the same work over the whole step (every kernel of the path, and the gaps)
+    roof["step_frac"] = roof["achieved"] * dom_s / (ms * 1e-3) / roof["peak"]
+    if dom == "chunk_scan" and "conv_silu_norm" not in kernels:
+        roof["note"] = "chunk_scan also ran the conv of the rows (no separate conv kernel)"
     traffic = load_traffic(dom)
     roof["traffic"] = traffic
     roof["kernel"] = dom

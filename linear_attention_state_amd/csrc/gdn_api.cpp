@@ -289,8 +289,10 @@ extern "C" int gdn_varlen_forward(const gdn_layer_desc* desc, const void* x, con
   // kernel ahead of the scans), (2) chunked prefill, (3) the token path
   // (decode, or everything in fp32 / other head sizes), which runs its own conv
   // from the conv states, (4) conv-state commit, last, once every reader of the
-  // old conv states has been enqueued.
+  // old conv states has been enqueued (when the chunk kernel ran the conv, it
+  // also wrote the chunked sequences' states, and this covers the rest).
   const bool chunked = bf16 && gdn::chunk_supported(desc->head_k_dim, desc->head_v_dim);
+  bool tails_done = false;  // the chunk kernel has written the chunked sequences' conv states
   if (chunked && n_long > 0) {
     sa.min_len = 2; sa.max_len = INT_MAX;
     // longest sequences first, so the longest chains start before the short ones
@@ -365,17 +367,19 @@ extern "C" int gdn_varlen_forward(const gdn_layer_desc* desc, const void* x, con
     }
     e = timed(K_CHUNK, st, [&] { return gdn::launch_chunk(sa, order, fc, desc->head_k_dim, desc->head_v_dim, st); });
     if (e != hipSuccess) return fail(GDN_EHIP, "chunk scan launch: %s", hipGetErrorString(e));
+    tails_done = fc.n > 0;
   }
   if (!chunked || n_short > 0) {
     sa.min_len = 0; sa.max_len = chunked ? 1 : INT_MAX;
     e = timed(K_TOKEN, st, [&] { return gdn::launch_recurrent(sa, desc->head_k_dim, desc->head_v_dim, bf16, st); });
     if (e != hipSuccess) return fail(GDN_EHIP, "token path launch: %s", hipGetErrorString(e));
   }
-  if (W > 1) {
+  if (W > 1 && (!tails_done || n_short > 0)) {
     gdn::TailArgs ta{};
     ta.x = x; ta.cu = cu_seqlens; ta.read_idx = read_idx; ta.write_idx = write_idx;
     ta.conv_pool = reinterpret_cast<char*>(conv_pool); ta.conv_stride = conv_block_stride;
     ta.num_seqs = num_seqs; ta.num_blocks = num_blocks; ta.channels = C;
+    ta.max_len = tails_done ? 1 : INT_MAX;
     e = timed(K_TAIL, st, [&] { return gdn::launch_tail_commit(ta, W, bf16, st); });
     if (e != hipSuccess) return fail(GDN_EHIP, "conv state commit launch: %s", hipGetErrorString(e));
   }

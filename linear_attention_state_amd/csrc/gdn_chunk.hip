@@ -1048,6 +1048,41 @@ __device__ __forceinline__ void conv_phase_w(Smem& sm, const ScanArgs& a, const 
   }
 }
 
+// New conv state of the sequence of `rank`: the last W-1 rows of [old state; x],
+// once every conv task of the sequence (the readers of the old state) is done.
+// Each thread reads all W-1 rows of its 8 channels before it writes, so the
+// ordinary in-place case (read block == write block) is safe.
+__device__ void commit_tail(Smem& sm, const ScanArgs& a, const SeqOrder& ord, const FusedConv& fc, int rank) {
+  const int W = a.width;
+  if (W < 2) return;
+  if (threadIdx.x == 0) {
+    const int need = fc.first[rank + 1] - fc.first[rank];
+    for (int it = 0; it < (1 << 24); ++it) {  // bounded, as in conv_phase: the tasks are all claimed
+      if (__hip_atomic_load(&fc.sync[1 + rank], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= need) break;
+      __builtin_amdgcn_s_sleep(2);
+    }
+  }
+  __syncthreads();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  const int s = ord.seq[rank];
+  if (!seq_active(a.read_idx, a.write_idx, s, a.num_blocks)) return;  // uniform
+  const int r0 = a.cu[s], L = a.cu[s + 1] - r0, C = a.channels;
+  const gptr<const u32x4> x = as_global(reinterpret_cast<const u32x4*>(a.x));
+  const gptr<const u32x4> src = as_global(reinterpret_cast<const u32x4*>(a.conv_pool + (int64_t)a.read_idx[s] * a.conv_stride));
+  const gptr<u32x4> dst = as_global(reinterpret_cast<u32x4*>(const_cast<char*>(a.conv_pool) + (int64_t)a.write_idx[s] * a.conv_stride));
+  for (int cq = threadIdx.x; cq < C / 8; cq += NT) {  // 16-byte column
+    u32x4 v[3];
+#pragma unroll
+    for (int j = 0; j < 3; ++j) {
+      const int i = L + j;  // row of [old state; x]
+      if (j < W - 1) v[j] = i < W - 1 ? src[(int64_t)i * (C / 8) + cq] : x[(int64_t)(r0 + i - (W - 1)) * (C / 8) + cq];
+    }
+#pragma unroll
+    for (int j = 0; j < 3; ++j)
+      if (j < W - 1) dst[(int64_t)j * (C / 8) + cq] = v[j];
+  }
+}
+
 __global__ void zero_sync_kernel(int32_t* p, int n) {
   for (int i = threadIdx.x; i < n; i += blockDim.x) p[i] = 0;
 }
@@ -1059,7 +1094,20 @@ __global__ __launch_bounds__(NT) void chunk_scan_kernel(ScanArgs a, SeqOrder ord
   Seq q;
   q.m = blockIdx.x % Hv;
   q.s = ord.n > 0 ? (rank < ord.n ? (int)ord.seq[rank] : a.num_seqs) : rank;
-  if (fc.n > 0) conv_phase_w(sm, a, ord, fc, rank);  // every rank < fc.n == ord.n
+  if (fc.n > 0) {
+    conv_phase_w(sm, a, ord, fc, rank);  // every rank < fc.n == ord.n
+    // the workgroups of the shortest sequence, which finish long before the
+    // others, write the new conv states: workgroup j those of ranks j, j + H_v, ...
+    if (rank == fc.n - 1)
+      for (int r = q.m; r < fc.n; r += Hv) commit_tail(sm, a, ord, fc, r);
+    // value heads of one key head on one XCD (workgroups go round-robin over
+    // the 8 XCDs), so the second reader of the shared Q and K rows can hit L2
+    const int g = Hv / a.num_k_heads, per = Hv / 8;
+    if (Hv % 8 == 0 && per % g == 0) {
+      const int x = q.m % 8, sl = q.m / 8;
+      q.m = g * (x * (per / g) + sl / g) + sl % g;
+    }
+  }
   if (q.s >= a.num_seqs) return;
   q.r0 = a.cu[q.s];
   q.L = a.cu[q.s + 1] - q.r0;

@@ -219,6 +219,7 @@ __global__ __launch_bounds__(256) void conv_tail_commit_kernel(TailArgs a) {
   if (!seq_active(a.read_idx, a.write_idx, s, a.num_blocks)) return;
   const int r0 = a.cu[s];
   const int L = a.cu[s + 1] - r0;
+  if (L > a.max_len) return;
   const char* src_tail = a.conv_pool + (int64_t)a.read_idx[s] * a.conv_stride;
   char* dst_tail = a.conv_pool + (int64_t)a.write_idx[s] * a.conv_stride;
   const char* xb = reinterpret_cast<const char*>(a.x);

@@ -97,6 +97,7 @@ struct TailArgs {
   char* conv_pool;
   int64_t conv_stride;
   int num_seqs, num_blocks, channels;
+  int max_len;  // sequences longer than this are committed elsewhere (the chunk kernel)
 };
 
 struct ScanArgs {
