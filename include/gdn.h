@@ -120,6 +120,11 @@ int gdn_workspace_size(const gdn_layer_desc* desc, int32_t total_tokens,
  * distinct, never block 0 and never another sequence's read block; block 0 is
  * all zero.  read_idx[i] == write_idx[i] is the ordinary in-place continue.
  * stream is a hipStream_t (NULL = the default stream).
+ *
+ * Launch plan: the conv of the chunked rows runs either in its own kernel or
+ * inside the chunk kernel, chosen by a time model; the environment variable
+ * GDN_CONV_IN_SCAN=always|never (read at every call) overrides the choice.
+ * Every output and state is the same bit for bit either way.
  */
 int gdn_varlen_forward(const gdn_layer_desc* desc, const void* x,
                        const void* conv_weight, const float* g, const float* beta,

@@ -14,6 +14,7 @@
 #include <climits>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <mutex>
 #include <string>
@@ -78,6 +79,18 @@ size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 size_t workspace_bytes_for(const gdn_layer_desc* d, int64_t total_tokens) {
   if (total_tokens <= 0) return 0;
   return round_up((size_t)total_tokens * (size_t)channels(d) * (size_t)act_size(d), 256) + gdn::kFusedSyncBytes;
+}
+
+// GDN_CONV_IN_SCAN: "always" runs the conv inside the chunk kernel whenever
+// its workgroups all fit on the device, "never" always runs the conv kernel,
+// anything else (or unset) lets the time model choose.  The result is the same
+// bit for bit either way; the override exists for tests and tuning.
+int conv_in_scan_mode() {
+  const char* v = getenv("GDN_CONV_IN_SCAN");
+  if (!v) return 0;
+  if (!strcmp(v, "always")) return 1;
+  if (!strcmp(v, "never")) return -1;
+  return 0;
 }
 
 // Compute units of the device that owns `st` (0 if unknown), looked up once per device.
@@ -316,7 +329,8 @@ extern "C" int gdn_varlen_forward(const gdn_layer_desc* desc, const void* x, con
     // Otherwise the conv kernel writes all of y first.
     static thread_local gdn::FusedConv fc;
     fc.n = 0;
-    if (order.n > 0 && order.n <= gdn::kMaxFusedRanks && aligned(conv_weight, 16) &&
+    const int mode = conv_in_scan_mode();
+    if (mode >= 0 && order.n > 0 && order.n <= gdn::kMaxFusedRanks && aligned(conv_weight, 16) &&
         (int64_t)order.n * desc->num_v_heads <= device_cus(st)) {
       fc.slices = (C + gdn::kConvTaskChannels - 1) / gdn::kConvTaskChannels;
       fc.first[0] = 0;
@@ -337,7 +351,7 @@ extern "C" int gdn_varlen_forward(const gdn_layer_desc* desc, const void* x, con
       const double fused = std::max((fc.first[order.n] * task_us + desc->num_v_heads * scans) /
                                     ((double)order.n * desc->num_v_heads), longest + 2.0 * task_us);
       const double apart = 2.0 * (double)total_tokens * C * act_size(desc) / 4.2e6 + longest + 3.0;
-      if (1.05 * fused < apart) {
+      if (mode > 0 || 1.05 * fused < apart) {
         fc.n = order.n;
         fc.sync = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(workspace) + (need - gdn::kFusedSyncBytes));
         // 100 ticks per microsecond; aiming 3% past the even spread measured best

@@ -1,0 +1,97 @@
+"""GPU: the conv of the chunked rows run inside the chunk kernel ("fused")
+against the conv kernel, forced both ways with GDN_CONV_IN_SCAN.
+
+Both placements must give the same outputs, conv states and recurrent states
+bit for bit (same arithmetic in the same order), and the fused one must also
+meet the oracle bar.  The kernel timing of each call shows which placement ran.
+"""
+import os
+
+import pytest
+import torch
+
+import linear_attention_state_amd as gdn
+import workloads
+from gpu_util import compare, run_gpu, run_oracle
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(batch, mode):
+    old = os.environ.get("GDN_CONV_IN_SCAN")
+    os.environ["GDN_CONV_IN_SCAN"] = mode
+    try:
+        gdn.gdn_kernel_timing(True)
+        res = run_gpu(batch)
+        kernels = gdn.gdn_kernel_times()
+    finally:
+        gdn.gdn_kernel_timing(False)
+        if old is None:
+            del os.environ["GDN_CONV_IN_SCAN"]
+        else:
+            os.environ["GDN_CONV_IN_SCAN"] = old
+    return res, kernels
+
+
+def _bits(t):
+    return t.view(torch.int16) if t.dtype == torch.bfloat16 else t.view(torch.int32)
+
+
+def _both_ways(batch, name):
+    print("case %s: lengths %s" % (name, batch.lengths), flush=True)
+    (out_f, cp_f, sp_f), k_f = _run(batch, "always")
+    (out_s, cp_s, sp_s), k_s = _run(batch, "never")
+    assert "conv_silu_norm" not in k_f and "chunk_scan" in k_f, k_f
+    assert "conv_silu_norm" in k_s, k_s
+    assert torch.equal(_bits(out_f), _bits(out_s))
+    assert torch.equal(_bits(cp_f), _bits(cp_s))
+    assert torch.equal(sp_f, sp_s)
+    errs = compare(batch, (out_f, cp_f, sp_f), run_oracle(batch))
+    print("%s: out %.3e state %.3e" % (name, errs["out_rel_l2"], errs["state_rel_l2"]), flush=True)
+    return k_f
+
+
+def test_ragged_lengths_with_priors():
+    """Lengths around the 16-row task and 64-row chunk edges, and 2 and 3
+    (shorter than the conv window), each continuing in place from its own block."""
+    b = workloads.random_batch(workloads.BIG, [2, 3, 17, 63, 65, 130, 200, 16], seed=41)
+    _both_ways(b, "ragged")
+
+
+def test_fresh_and_continuing_sequences():
+    b = workloads.random_batch(workloads.BIG, [90, 5, 300, 48], seed=42, fresh=[1, 0, 1, 0])
+    _both_ways(b, "fresh")
+
+
+def test_mixed_with_decode_tokens():
+    """One-token sequences beside chunked ones: the conv-state commit kernel then
+    runs for the one-token sequences only."""
+    b = workloads.random_batch(workloads.BIG, [1, 70, 1, 33, 1], seed=43)
+    k = _both_ways(b, "mixed")
+    assert "token_recurrent" in k and "conv_state_commit" in k, k
+
+
+def test_pure_prefill_skips_the_commit_kernel():
+    b = workloads.random_batch(workloads.BIG, [40, 129], seed=44)
+    k = _both_ways(b, "prefill")
+    assert "conv_state_commit" not in k, k
+
+
+def test_padding_sequence():
+    b = workloads.random_batch(workloads.BIG, [64, 70, 9], seed=45)
+    b.write_idx[1] = -2
+    _both_ways(b, "padding")
+
+
+@pytest.mark.parametrize("W", [2, 3])
+def test_conv_widths(W):
+    layer = workloads.Layer(16, 32, 128, 128, W, "bf16")
+    b = workloads.random_batch(layer, [2, 31, 100], seed=46 + W)
+    _both_ways(b, "W%d" % W)
+
+
+def test_narrow_layer_partial_channel_slice():
+    """C = 1024 < 4096 channels per task: most threads of a task have no channel."""
+    layer = workloads.Layer(2, 4, 128, 128, 4, "bf16")
+    b = workloads.random_batch(layer, [77, 3, 140], seed=49)
+    _both_ways(b, "narrow")
