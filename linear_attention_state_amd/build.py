@@ -1,9 +1,10 @@
 """Builds the gfx950 HIP library ``_lib/libgdn.so`` in-tree with hipcc.
 
 Every HIP source is compiled for gfx950 only, with packed-fp32 instruction
-forms disabled (plain fp32 code is emitted instead) and MFMA results kept in
+forms disabled (plain fp32 code is emitted instead), MFMA results kept in
 architectural VGPRs where possible (fewer accumulator-register copies around
-the VALU work on them).
+the VALU work on them), and the atomic optimizer off (all atomics are
+single-lane; see FLAGS).
 """
 from __future__ import annotations
 
@@ -20,6 +21,10 @@ FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-mllvm", "-amdgpu-mfma-vgpr-form",
+    # every atomic here is issued by one lane; the optimizer's wave-wide
+    # expansion would read its result at once, which waits for all older
+    # vector-memory operations (the conv task prefetch) right after issue
+    "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
     "-Wall", "-Wno-unused-function",
 ]
 

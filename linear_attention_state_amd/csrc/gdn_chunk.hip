@@ -106,6 +106,7 @@ struct alignas(16) Smem {
   int task;                   // conv task claimed by thread 0, for the workgroup
 };
 static_assert(sizeof(Smem) <= 160 * 1024, "LDS");
+static_assert(offsetof(Smem, task) >= 16 * 8 * 1024, "the conv row staging (16 rows x 8 KiB) stays clear of the task slot");
 static_assert(D * PS * 4 <= sizeof(ChunkBuf) * 2, "state staging");
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
@@ -873,46 +874,54 @@ __device__ __forceinline__ ConvTask conv_decode(const ScanArgs& a, const SeqOrde
   return k;
 }
 
-// A task's inputs in registers: the W-1 inputs before r0 (earlier rows of the
-// sequence, else its conv state, else zero), the taps w[c][j] (8 channels x W
-// contiguous), and the rows.
+// Halo and taps of a task in registers: the W-1 inputs before r0 (earlier rows
+// of the sequence, else its conv state, else zero) and w[c][j] (8 channels x W
+// contiguous).  The task's rows go through LDS (conv_prefetch).
 template <int W>
-struct ConvIn {
+struct ConvSide {
   u32x4 hx[W > 1 ? W - 1 : 1];
   u32x4 wr[W];
-  u32x4 rx[kConvTaskRows];
 };
 
-// Issues every load of a task; the row loads are the last kConvTaskRows
-// vector-memory instructions (rows past the task's end load its last row again).
+// During the conv phase the LDS of the scan is free: it stages the rows of the
+// next task.  Wave w's 512-channel segment of row r sits at (8 r + w) KiB,
+// lane l's 16 bytes at + 16 l, so every wave reads back only what it loaded.
+constexpr int kConvWaves = NT / 64;
+__device__ __forceinline__ u32x4* conv_stage(Smem& sm) { return reinterpret_cast<u32x4*>(&sm); }
+
+// Issues the loads of task k: halo and taps into `sd`, the rows straight into
+// LDS (no registers), all in flight while the current task is computed.
 template <int W>
-__device__ __forceinline__ void conv_load(const ScanArgs& a, const ConvTask& k, ConvIn<W>& in) {
+__device__ __forceinline__ void conv_prefetch(Smem& sm, const ScanArgs& a, const ConvTask& k, ConvSide<W>& sd) {
+  if (!k.on) return;
   const int C = a.channels;
   const int64_t cq = k.c0 / 8;  // 16-byte column of this thread
   const gptr<const u32x4> x = as_global(reinterpret_cast<const u32x4*>(a.x));
-  if (k.on) {
-    const bool act = seq_active(a.read_idx, a.write_idx, k.s, a.num_blocks);
+  const bool act = seq_active(a.read_idx, a.write_idx, k.s, a.num_blocks);
 #pragma unroll
-    for (int j = 1; j < W; ++j) {
-      const int p = k.r0 - j;
-      in.hx[j - 1] = u32x4{0u, 0u, 0u, 0u};
-      if (p >= k.seq0) {
-        in.hx[j - 1] = x[(int64_t)p * (C / 8) + cq];
-      } else if (act) {
-        const gptr<const u32x4> tail =
-            as_global(reinterpret_cast<const u32x4*>(a.conv_pool + (int64_t)a.read_idx[k.s] * a.conv_stride));
-        in.hx[j - 1] = tail[(int64_t)(W - 1 + p - k.seq0) * (C / 8) + cq];
-      }
+  for (int j = 1; j < W; ++j) {
+    const int p = k.r0 - j;
+    sd.hx[j - 1] = u32x4{0u, 0u, 0u, 0u};
+    if (p >= k.seq0) {
+      sd.hx[j - 1] = x[(int64_t)p * (C / 8) + cq];
+    } else if (act) {
+      const gptr<const u32x4> tail =
+          as_global(reinterpret_cast<const u32x4*>(a.conv_pool + (int64_t)a.read_idx[k.s] * a.conv_stride));
+      sd.hx[j - 1] = tail[(int64_t)(W - 1 + p - k.seq0) * (C / 8) + cq];
     }
-    const gptr<const u32x4> wp =
-        as_global(reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(a.w) + (int64_t)k.c0 * W));
-#pragma unroll
-    for (int i = 0; i < W; ++i) in.wr[i] = wp[i];
   }
-  const int64_t cr = k.on ? cq : 0;  // threads past the channel count load column 0 (never used)
+  const gptr<const u32x4> wp =
+      as_global(reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(a.w) + (int64_t)k.c0 * W));
 #pragma unroll
-  for (int r = 0; r < kConvTaskRows; ++r)
-    in.rx[r] = __builtin_nontemporal_load(&x[(int64_t)(k.r0 + min(r, k.n - 1)) * (C / 8) + cr]);
+  for (int i = 0; i < W; ++i) sd.wr[i] = wp[i];
+  const int wv = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+  const __amdgpu_buffer_rsrc_t xs =
+      make_rsrc(reinterpret_cast<const uint16_t*>(a.x) + (int64_t)k.r0 * C, (uint32_t)(k.n * C * 2));
+  u32x4* st = conv_stage(sm);
+#pragma unroll
+  for (int r = 0; r < kConvTaskRows; ++r)  // rows past the task's end load its last row again
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(xs, (__attribute__((address_space(3))) void*)(st + (r * kConvWaves + wv) * 64),
+                                             16, (min(r, k.n - 1) * C + k.c0) * 2, 0, 0, 0);
 }
 
 // Sum over the 16 lanes of a key head (a DPP row): the same pairings as a
@@ -927,14 +936,16 @@ __device__ __forceinline__ float head_sum(float v) {
   return v;
 }
 
+// Computes and stores task k from its rows (registers) and its halo and taps.
 template <int W>
-__device__ __forceinline__ void conv_compute(const ScanArgs& a, const ConvTask& k, const ConvIn<W>& in) {
+__device__ __forceinline__ void conv_compute(const ScanArgs& a, const ConvTask& k, const ConvSide<W>& sd,
+                                             const u32x4 (&rx)[kConvTaskRows]) {
   if (!k.on) return;  // whole 16-lane head groups (the channel count is a multiple of 128)
   const int C = a.channels;
   float wt[8][W];
 #pragma unroll
   for (int i = 0; i < 8 * W; ++i) {
-    const uint32_t word = in.wr[i / 8][(i % 8) / 2];
+    const uint32_t word = sd.wr[i / 8][(i % 8) / 2];
     wt[i / W][i % W] = __uint_as_float((i & 1) ? (word & 0xffff0000u) : (word << 16));
   }
   const bool do_norm = k.c0 < 2 * a.num_k_heads * D;
@@ -944,8 +955,8 @@ __device__ __forceinline__ void conv_compute(const ScanArgs& a, const ConvTask& 
   for (int j = 1; j < W; ++j)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      xw[(4 - j) & 3][2 * i] = __uint_as_float(in.hx[j - 1][i] << 16);
-      xw[(4 - j) & 3][2 * i + 1] = __uint_as_float(in.hx[j - 1][i] & 0xffff0000u);
+      xw[(4 - j) & 3][2 * i] = __uint_as_float(sd.hx[j - 1][i] << 16);
+      xw[(4 - j) & 3][2 * i + 1] = __uint_as_float(sd.hx[j - 1][i] & 0xffff0000u);
     }
   const __amdgpu_buffer_rsrc_t ys =
       make_rsrc(reinterpret_cast<const uint16_t*>(a.y) + (int64_t)k.r0 * C, (uint32_t)(k.n * C * 2));
@@ -953,8 +964,8 @@ __device__ __forceinline__ void conv_compute(const ScanArgs& a, const ConvTask& 
   for (int r = 0; r < kConvTaskRows; ++r) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      xw[r & 3][2 * i] = __uint_as_float(in.rx[r][i] << 16);
-      xw[r & 3][2 * i + 1] = __uint_as_float(in.rx[r][i] & 0xffff0000u);
+      xw[r & 3][2 * i] = __uint_as_float(rx[r][i] << 16);
+      xw[r & 3][2 * i + 1] = __uint_as_float(rx[r][i] & 0xffff0000u);
     }
     float yv[8];
     float ss = 0.f;
@@ -979,52 +990,71 @@ __device__ __forceinline__ void conv_compute(const ScanArgs& a, const ConvTask& 
   }
 }
 
+// Thread 0: claim one more task after the newest claimed one, while my rank
+// has unclaimed tasks or there is time for it before my scan.
+__device__ __forceinline__ int claim_after(const FusedConv& fc, int newest, int total, int last, int32_t latest,
+                                           uint64_t t_begin) {
+  if (newest >= total) return total;
+  if (newest < last - 1 || (int64_t)(__builtin_amdgcn_s_memrealtime() - t_begin) <= latest)
+    return __hip_atomic_fetch_add(fc.sync, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return total;
+}
+
 // Claims and runs conv tasks (at least until every task of `rank` is claimed),
 // then waits for the tasks of `rank` to finish.  All threads of the workgroup
-// call it.  The loads of the next task are issued before the stores of the
-// current one are waited for, so the two latencies overlap.
+// call it.  While a task is computed from registers, the rows of the next
+// claimed task are loading into LDS, and a third task is being claimed.
 template <int W>
 __device__ void conv_phase(Smem& sm, const ScanArgs& a, const SeqOrder& ord, const FusedConv& fc, int rank) {
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int total = fc.first[fc.n];
   const int last = fc.first[rank + 1];  // my rank's tasks end here
-  int* next = fc.sync;
-  // latest start of a task that is to be followed by one more and by my scan
+  // latest claim of a task that two more precede before my scan
   const int my_s = ord.seq[rank];
-  const int32_t latest = fc.target - fc.scan0 - fc.scan1 * ((a.cu[my_s + 1] - a.cu[my_s] + BT - 1) / BT) - 2 * fc.task;
+  const int32_t latest = fc.target - fc.scan0 - fc.scan1 * ((a.cu[my_s + 1] - a.cu[my_s] + BT - 1) / BT) - 3 * fc.task;
   const uint64_t t_begin = __builtin_amdgcn_s_memrealtime();
-  if (tid == 0) sm.task = __hip_atomic_fetch_add(next, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (tid == 0) sm.task = __hip_atomic_fetch_add(fc.sync, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   lds_barrier();
   int t = sm.task;
   lds_barrier();  // every thread has read sm.task before thread 0 writes it again
   ConvTask k{};
-  ConvIn<W> in;
+  ConvSide<W> cur, nxt;
   if (t < total) {
     k = conv_decode(a, ord, fc, t);
-    conv_load<W>(a, k, in);
+    conv_prefetch<W>(sm, a, k, nxt);
   }
+  if (tid == 0) sm.task = claim_after(fc, t, total, last, latest, t_begin);
+  lds_barrier();
+  int u = sm.task;
+  u32x4 rx[kConvTaskRows];
+  const u32x4* st = conv_stage(sm);
   while (t < total) {
-    // claim the following task while this one runs, while my rank has unclaimed
-    // tasks or there is time for one more before my scan
-    int pre = total;
-    if (tid == 0 && (t < last - 1 || (int64_t)(__builtin_amdgcn_s_memrealtime() - t_begin) <= latest))
-      pre = __hip_atomic_fetch_add(next, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    conv_compute<W>(a, k, in);
-    if (tid == 0) sm.task = pre;
-    lds_barrier();  // the next task's number is in sm.task
-    const int u = sm.task;
-    const int done_rank = k.rank;
-    if (u < total) {
-      k = conv_decode(a, ord, fc, u);
-      conv_load<W>(a, k, in);
+    // this task's rows and halo have arrived; read the rows back from LDS
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    cur = nxt;
+    if (k.on) {
+#pragma unroll
+      for (int r = 0; r < kConvTaskRows; ++r) rx[r] = st[(r * kConvWaves + wv) * 64 + lane];
     }
-    // this task's device-scope stores are older than the next task's row loads:
-    // wait for all but those, then count the task once every wave is through
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kConvTaskRows) : "memory");
-    if (u >= total) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    lds_barrier();  // also: every thread has read sm.task
-    if (tid == 0) __hip_atomic_fetch_add(&fc.sync[1 + done_rank], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // read before the next rows overwrite them
+    lds_barrier();  // every thread has read sm.task (u)
+    ConvTask kn{};
+    if (u < total) {
+      kn = conv_decode(a, ord, fc, u);
+      conv_prefetch<W>(sm, a, kn, nxt);
+    }
+    int v = total;
+    if (tid == 0) v = claim_after(fc, u, total, last, latest, t_begin);
+    conv_compute<W>(a, k, cur, rx);
+    if (tid == 0) sm.task = v;
+    // this task's device-scope stores complete (and the next task's loads), then one count
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    lds_barrier();
+    if (tid == 0) __hip_atomic_fetch_add(&fc.sync[1 + k.rank], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    k = kn;
     t = u;
+    u = sm.task;
   }
   if (tid == 0) {
     const int need = last - fc.first[rank];
