@@ -1000,10 +1000,11 @@ __device__ __forceinline__ int claim_after(const FusedConv& fc, int newest, int 
   return total;
 }
 
-// Claims and runs conv tasks (at least until every task of `rank` is claimed),
-// then waits for the tasks of `rank` to finish.  All threads of the workgroup
+// Claims and runs conv tasks, at least until every task of `rank` is claimed
+// (conv_wait then waits for those to finish).  All threads of the workgroup
 // call it.  While a task is computed from registers, the rows of the next
-// claimed task are loading into LDS, and a third task is being claimed.
+// claimed task are loading into LDS, and a third task is being claimed.  On
+// return no LDS access or load of the phase is outstanding.
 template <int W>
 __device__ void conv_phase(Smem& sm, const ScanArgs& a, const SeqOrder& ord, const FusedConv& fc, int rank) {
   const int tid = threadIdx.x, lane = tid & 63;
@@ -1056,9 +1057,14 @@ __device__ void conv_phase(Smem& sm, const ScanArgs& a, const SeqOrder& ord, con
     t = u;
     u = sm.task;
   }
-  if (tid == 0) {
-    const int need = last - fc.first[rank];
-    // bounded: every task counted here is claimed and finishes without waiting
+}
+
+// Waits until every conv task of `rank` is counted, then makes their rows
+// visible to this workgroup.  Bounded: every task counted here is claimed (the
+// workgroup claimed past them before it stopped) and finishes without waiting.
+__device__ __forceinline__ void conv_wait(const FusedConv& fc, int rank) {
+  if (threadIdx.x == 0) {
+    const int need = fc.first[rank + 1] - fc.first[rank];
     for (int it = 0; it < (1 << 24); ++it) {
       if (__hip_atomic_load(&fc.sync[1 + rank], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= need) break;
       __builtin_amdgcn_s_sleep(2);
@@ -1085,15 +1091,7 @@ __device__ __forceinline__ void conv_phase_w(Smem& sm, const ScanArgs& a, const 
 __device__ void commit_tail(Smem& sm, const ScanArgs& a, const SeqOrder& ord, const FusedConv& fc, int rank) {
   const int W = a.width;
   if (W < 2) return;
-  if (threadIdx.x == 0) {
-    const int need = fc.first[rank + 1] - fc.first[rank];
-    for (int it = 0; it < (1 << 24); ++it) {  // bounded, as in conv_phase: the tasks are all claimed
-      if (__hip_atomic_load(&fc.sync[1 + rank], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= need) break;
-      __builtin_amdgcn_s_sleep(2);
-    }
-  }
-  __syncthreads();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  conv_wait(fc, rank);  // the tasks of every rank are claimed before the last rank's are
   const int s = ord.seq[rank];
   if (!seq_active(a.read_idx, a.write_idx, s, a.num_blocks)) return;  // uniform
   const int r0 = a.cu[s], L = a.cu[s + 1] - r0, C = a.channels;
@@ -1125,7 +1123,7 @@ __global__ __launch_bounds__(NT) void chunk_scan_kernel(ScanArgs a, SeqOrder ord
   q.m = blockIdx.x % Hv;
   q.s = ord.n > 0 ? (rank < ord.n ? (int)ord.seq[rank] : a.num_seqs) : rank;
   if (fc.n > 0) {
-    conv_phase_w(sm, a, ord, fc, rank);  // every rank < fc.n == ord.n
+    conv_phase_w(sm, a, ord, fc, rank);  // every rank < fc.n == ord.n; waits come later
     // the workgroups of the shortest sequence, which finish long before the
     // others, write the new conv states: workgroup j those of ranks j, j + H_v, ...
     if (rank == fc.n - 1)
@@ -1167,6 +1165,9 @@ __global__ __launch_bounds__(NT) void chunk_scan_kernel(ScanArgs a, SeqOrder ord
       *reinterpret_cast<u32x4*>(&sst[row * PS + 4 * c4]) = __builtin_amdgcn_raw_buffer_load_b128(rs, 16 * f, 0, 0);
     }
   }
+  // the state does not depend on the conv: it was staged while the sequence's
+  // last rows may still have been converting; now wait for those rows
+  if (fc.n > 0) conv_wait(fc, rank);
   lds_barrier();
   if (wv < NS) {
     state_role(sm, sst, a, q, wv, ln);
