@@ -8,9 +8,10 @@ state pools) are generated once, copied to HBM before timing, and stay there.
 Primary line: the prefill workload (8 sequences, lengths uniform in [256, 4096],
 H_k=16, H_v=32, d_k=d_v=128, W=4, bf16 activations, fp32 state), tokens/s.
 The same JSON line carries the decode workload (256 sequences of one token,
-1024-block pool) as a nested object, each with the roofline of its dominant
-kernel, the per-kernel event timings, and the fp64 CPU oracle timed on the
-host cores beside it.
+1024-block pool) and the standalone varlen conv layer (gdn_varlen_conv on the
+prefill rows) as nested objects, each with the roofline of its dominant
+kernel and the per-kernel event timings, and the fp64 CPU oracle timed on the
+host cores beside them.
 
     python bench.py [--gpus 1] [--steps 50] [--warmup 50] [--no-cpu-baseline]
 
@@ -164,6 +165,58 @@ def run(cfg_id: int, steps: int, warmup: int):
     }
 
 
+def run_conv(steps: int, warmup: int):
+    """The standalone varlen conv layer (gdn_varlen_conv, SiLU) on the prefill
+    workload's rows: x [T][8192] bf16, W = 4, every sequence from the trash block."""
+    import torch
+
+    import linear_attention_state_amd as gdn
+    import workloads
+
+    b = workloads.config(1)
+    dev = torch.device("cuda", 0)
+    x = b.x.to(dev).contiguous()
+    w = b.conv_weight.to(dev).contiguous()
+    cu = b.cu_seqlens.to(dev)
+    ri, wi = b.read_idx.to(dev), b.write_idx.to(dev)
+    pool = b.conv_pool.to(dev).contiguous()
+    y = torch.empty_like(x)
+    stream = torch.cuda.current_stream(dev)
+    cu_host = b.cu_seqlens.clone()
+
+    def step():
+        gdn.gdn_varlen_conv(x, w, cu, cu_host, ri, wi, pool, y, silu=True, stream=stream.cuda_stream)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for _ in range(steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / steps
+    gdn.gdn_kernel_timing(True)
+    for _ in range(steps):
+        step()
+    kt = gdn.gdn_kernel_times()
+    gdn.gdn_kernel_timing(False)
+    T, C, W = b.total_tokens, b.layer.conv_channels, b.layer.conv_width
+    n = len(b.lengths)
+    # algorithmic bytes: x read, y written, each sequence's state read and written, the taps
+    work = 2 * T * C * 2 + 2 * n * (W - 1) * C * 2 + C * W * 2
+    conv_ms = kt["conv_silu_norm"][0] / kt["conv_silu_norm"][1]
+    roof = {"bound": "hbm", "achieved": work / (conv_ms * 1e-3) / 1e9, "peak": PEAK_HBM / 1e9, "unit": "GB/s",
+            "kernel": "conv_silu_norm"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = load_traffic("conv_silu_norm")
+    return {"workload": "standalone varlen conv + SiLU: the prefill rows (T=%d, C=%d, W=%d, bf16), "
+                        "%d sequences from the trash block" % (T, C, W, n),
+            "value": T / (ms * 1e-3), "unit": "tokens/s", "ms_per_step": ms, "roofline": roof,
+            "kernels": {k: {"avg_ms": v[0] / max(v[1], 1), "launches": v[1]} for k, v in kt.items()}}
+
+
 def cpu_baseline(batch):
     """The fp64 oracle on the host cores, on the same workload (all of it when
     it takes under half a minute), tokens/s."""
@@ -189,7 +242,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
-    ap.add_argument("--only", choices=["prefill", "decode"], default=None,
+    ap.add_argument("--no-conv", action="store_true", help="skip the standalone conv layer entry")
+    ap.add_argument("--only", choices=["prefill", "decode", "conv"], default=None,
                     help="run one workload alone and print its numbers (profiling runs)")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="run only a device-to-device copy of this many bytes (calibrates HBM byte counters)")
@@ -207,6 +261,9 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes": args.copy_bytes, "launches": args.warmup + args.steps}), flush=True)
+        return
+    if args.only == "conv":
+        print(json.dumps(run_conv(args.steps, args.warmup)), flush=True)
         return
     if args.only:
         r = run(1 if args.only == "prefill" else 2, args.steps, args.warmup)
@@ -231,6 +288,8 @@ def main():
                           "value": dec["value"], "unit": "tokens/s", "ms_per_step": dec["ms_per_step"],
                           "roofline": dec["roofline"], "kernels": dec["kernels"]}
         del dec
+    if not args.no_conv:
+        line["conv"] = run_conv(args.steps, args.warmup)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(b)
     print(json.dumps(line), flush=True)

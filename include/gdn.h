@@ -24,12 +24,13 @@
  *
  * All device work is enqueued on the caller's stream; no call synchronises
  * with the host, none allocates device memory, and host arrays passed in are
- * no longer needed when the call returns (the warmup race the page's commit
- * "...inputs" describes cannot arise from this library).
+ * no longer needed when the call returns (so the warmup race that a commit on
+ * the page fixes, inputs rewritten while a stream still read them, cannot arise
+ * from this library).
  *
  * Errors: every function returns a gdn_status; gdn_last_error() gives a
  * readable message for the last non-OK status of the calling thread (the page's
- * allocator commit refuses bad state declarations "with a readable error").
+ * allocator commit likewise refuses bad state declarations with a message).
  * Nothing aborts and no exception crosses this ABI.
  */
 #ifndef GDN_H_
@@ -134,6 +135,31 @@ int gdn_varlen_forward(const gdn_layer_desc* desc, const void* x,
                        void* conv_pool, int64_t conv_block_stride, float* ssm_pool,
                        int64_t ssm_block_stride, int32_t num_blocks, void* out,
                        void* workspace, size_t workspace_bytes, void* stream);
+
+/* A standalone varlen conv layer (the tracker page lists models with conv-only
+ * layers): step 1 above, with or without the SiLU, and the conv-state part of
+ * step 4, without the split, normalisation and recurrence.  For every sequence
+ * i of the packed row,
+ *   y[t][c] = act( sum_j w[c][j] * xext[t + j][c] ),  xext = [conv state of
+ *   read_idx[i] (W-1 rows); the sequence's x rows],
+ * with act = SiLU when silu != 0, else the identity, w[c][W-1] multiplying the
+ * current token; then the last W-1 rows of xext become the conv state of
+ * write_idx[i].  A padding sequence (write_idx < 0) reads and writes nothing
+ * and its y rows are left as they are.
+ *   channels   C, a multiple of 8;  conv_width W in 1..4;  act_dtype GDN_F32 or GDN_BF16
+ *   x          [T][C] act dtype, device, 16-byte aligned
+ *   conv_weight [C][W] act dtype, device
+ *   cu_seqlens, cu_seqlens_host, read_idx, write_idx, num_blocks: as for gdn_varlen_forward
+ *   conv_pool  P blocks of [W-1][C] act dtype at conv_pool + i*conv_block_stride
+ *              (stride a multiple of 16 and >= (W-1)*C*size); may be NULL when W == 1
+ *   y          [T][C] act dtype, device, 16-byte aligned (may not alias x)
+ * Enqueued on `stream`; no allocation, no host sync.  Preconditions as for
+ * gdn_varlen_forward (block 0 all zero, distinct write blocks). */
+int gdn_varlen_conv(int32_t channels, int32_t conv_width, int32_t act_dtype, int32_t silu,
+                    const void* x, const void* conv_weight, const int32_t* cu_seqlens,
+                    const int32_t* cu_seqlens_host, int32_t num_seqs, int32_t total_tokens,
+                    const int32_t* read_idx, const int32_t* write_idx, void* conv_pool,
+                    int64_t conv_block_stride, int32_t num_blocks, void* y, void* stream);
 
 /* Message of the last non-OK status returned on this thread ("" if none). */
 const char* gdn_last_error(void);

@@ -16,7 +16,7 @@ LIB_PATH = os.path.join(HERE, "_lib", "libgdn.so")
 
 GDN_OK, GDN_EINVAL, GDN_EUNSUPPORTED, GDN_EWORKSPACE, GDN_EHIP = 0, -1, -2, -3, -4
 GDN_F32, GDN_BF16 = 0, 1
-EXPORTS = ("gdn_state_spec", "gdn_workspace_size", "gdn_varlen_forward", "gdn_last_error",
+EXPORTS = ("gdn_state_spec", "gdn_workspace_size", "gdn_varlen_forward", "gdn_varlen_conv", "gdn_last_error",
            "gdn_kernel_timing", "gdn_kernel_times")
 
 _lib = None
@@ -78,6 +78,10 @@ def load_library():
         lib.gdn_varlen_forward.argtypes = [
             ctypes.POINTER(gdn_layer_desc), P, P, P, P, P, P, ctypes.c_int32, ctypes.c_int32, P, P,
             P, ctypes.c_int64, P, ctypes.c_int64, ctypes.c_int32, P, P, ctypes.c_size_t, P]
+        lib.gdn_varlen_conv.restype = ctypes.c_int
+        lib.gdn_varlen_conv.argtypes = [
+            ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, P, P, P, P, ctypes.c_int32,
+            ctypes.c_int32, P, P, P, ctypes.c_int64, ctypes.c_int32, P, P]
         lib.gdn_kernel_timing.restype = ctypes.c_int
         lib.gdn_kernel_timing.argtypes = [ctypes.c_int]
         lib.gdn_kernel_times.restype = ctypes.c_int
@@ -167,6 +171,40 @@ def gdn_varlen_forward(layer, x, conv_weight, g, beta, cu_seqlens, cu_seqlens_ho
         ctypes.c_void_p(stream))
     _check(rc)
     return out
+
+
+def gdn_varlen_conv(x, conv_weight, cu_seqlens, cu_seqlens_host, read_idx, write_idx, conv_pool, y,
+                    silu: bool = True, stream=None):
+    """Enqueues the standalone varlen conv layer (``gdn.h``): x [T][C] and
+    conv_weight [C][W] in bf16 or float32, conv_pool [P][W-1][C] updated in place,
+    y [T][C] written."""
+    import torch
+
+    lib = load_library()
+    if not isinstance(cu_seqlens_host, torch.Tensor):
+        cu_seqlens_host = torch.tensor(list(cu_seqlens_host), dtype=torch.int32)
+    cu_h = cu_seqlens_host.to(torch.int32).contiguous()
+    if cu_h.is_cuda:
+        raise ValueError("cu_seqlens_host must be host memory")
+    if x.dtype not in (torch.bfloat16, torch.float32) or conv_weight.dtype != x.dtype or y.dtype != x.dtype:
+        raise ValueError("x, conv_weight and y must share one dtype, bf16 or float32")
+    for name, t in (("cu_seqlens", cu_seqlens), ("read_idx", read_idx), ("write_idx", write_idx)):
+        if t.dtype != torch.int32:
+            raise ValueError("%s must be int32" % name)
+    C, W = int(conv_weight.shape[0]), int(conv_weight.shape[1])
+    if stream is None:
+        stream = torch.cuda.current_stream(x.device).cuda_stream
+    has_pool = conv_pool is not None and conv_pool.numel() > 0
+    conv_stride = conv_pool.stride(0) * conv_pool.element_size() if has_pool else 0
+    num_blocks = int(conv_pool.shape[0]) if conv_pool is not None else 0
+    rc = lib.gdn_varlen_conv(
+        C, W, GDN_BF16 if x.dtype == torch.bfloat16 else GDN_F32, 1 if silu else 0,
+        _dev_ptr(x, "x"), _dev_ptr(conv_weight, "conv_weight"), _dev_ptr(cu_seqlens, "cu_seqlens"),
+        ctypes.c_void_p(cu_h.data_ptr()), cu_h.numel() - 1, int(x.shape[0]), _dev_ptr(read_idx, "read_idx"),
+        _dev_ptr(write_idx, "write_idx"), _dev_ptr(conv_pool, "conv_pool") if has_pool else None, conv_stride,
+        num_blocks, _dev_ptr(y, "y"), ctypes.c_void_p(stream))
+    _check(rc)
+    return y
 
 
 def gdn_kernel_timing(enable: bool) -> None:

@@ -376,7 +376,7 @@ extern "C" int gdn_varlen_forward(const gdn_layer_desc* desc, const void* x, con
       }
       ca.eps = sa.eps;
       ca.q_scale = sa.q_scale;
-      e = timed(K_CONV, st, [&] { return gdn::launch_conv(ca, W, bf16, st); });
+      e = timed(K_CONV, st, [&] { return gdn::launch_conv(ca, W, bf16, true, st); });
       if (e != hipSuccess) return fail(GDN_EHIP, "conv launch: %s", hipGetErrorString(e));
     }
     e = timed(K_CHUNK, st, [&] { return gdn::launch_chunk(sa, order, fc, desc->head_k_dim, desc->head_v_dim, st); });
@@ -394,6 +394,70 @@ extern "C" int gdn_varlen_forward(const gdn_layer_desc* desc, const void* x, con
     ta.conv_pool = reinterpret_cast<char*>(conv_pool); ta.conv_stride = conv_block_stride;
     ta.num_seqs = num_seqs; ta.num_blocks = num_blocks; ta.channels = C;
     ta.max_len = tails_done ? 1 : INT_MAX;
+    e = timed(K_TAIL, st, [&] { return gdn::launch_tail_commit(ta, W, bf16, st); });
+    if (e != hipSuccess) return fail(GDN_EHIP, "conv state commit launch: %s", hipGetErrorString(e));
+  }
+  return GDN_OK;
+}
+
+extern "C" int gdn_varlen_conv(int32_t channels, int32_t conv_width, int32_t act_dtype, int32_t silu,
+                               const void* x, const void* conv_weight, const int32_t* cu_seqlens,
+                               const int32_t* cu_seqlens_host, int32_t num_seqs, int32_t total_tokens,
+                               const int32_t* read_idx, const int32_t* write_idx, void* conv_pool,
+                               int64_t conv_block_stride, int32_t num_blocks, void* y, void* stream) {
+  if (act_dtype != GDN_F32 && act_dtype != GDN_BF16)
+    return fail(GDN_EINVAL, "act_dtype %d is neither GDN_F32 nor GDN_BF16", act_dtype);
+  if (channels < 1 || conv_width < 1) return fail(GDN_EINVAL, "channels and conv_width must be >= 1");
+  if (channels % 8) return fail(GDN_EUNSUPPORTED, "channels=%d is not a multiple of 8", channels);
+  if (channels > INT_MAX / 8) return fail(GDN_EUNSUPPORTED, "too many channels (%d)", channels);
+  if (conv_width > 4) return fail(GDN_EUNSUPPORTED, "conv_width %d > 4 is not built", conv_width);
+  const int W = conv_width;
+  const bool bf16 = act_dtype == GDN_BF16;
+  const int64_t esz = bf16 ? 2 : 4;
+  if (num_seqs < 1) return fail(GDN_EINVAL, "no sequences in batch (num_seqs=%d)", num_seqs);
+  if (total_tokens < 0) return fail(GDN_EINVAL, "total_tokens=%d is negative", total_tokens);
+  if (!cu_seqlens_host) return fail(GDN_EINVAL, "cu_seqlens_host is NULL");
+  if (cu_seqlens_host[0] != 0) return fail(GDN_EINVAL, "cu_seqlens[0]=%d, expected 0", cu_seqlens_host[0]);
+  for (int i = 0; i < num_seqs; ++i)
+    if (cu_seqlens_host[i + 1] < cu_seqlens_host[i])
+      return fail(GDN_EINVAL, "cu_seqlens decreases at %d (%d -> %d)", i, cu_seqlens_host[i], cu_seqlens_host[i + 1]);
+  if (cu_seqlens_host[num_seqs] != total_tokens)
+    return fail(GDN_EINVAL, "cu_seqlens[%d]=%d differs from total_tokens=%d", num_seqs, cu_seqlens_host[num_seqs],
+                total_tokens);
+  if (!cu_seqlens || !read_idx || !write_idx) return fail(GDN_EINVAL, "device cu_seqlens/read_idx/write_idx is NULL");
+  if (W > 1 && !conv_pool) return fail(GDN_EINVAL, "conv_pool is NULL but conv_width=%d > 1", W);
+  if (total_tokens > 0 && (!x || !conv_weight || !y)) return fail(GDN_EINVAL, "x, conv_weight and y must be non-NULL");
+  if (num_blocks < 2) return fail(GDN_EINVAL, "num_blocks=%d; the pool needs the trash block and one more", num_blocks);
+  if (W > 1 && (conv_block_stride < (W - 1) * (int64_t)channels * esz || conv_block_stride % 16))
+    return fail(GDN_EINVAL, "conv_block_stride=%lld must be a multiple of 16 and >= %lld", (long long)conv_block_stride,
+                (long long)((W - 1) * (int64_t)channels * esz));
+  if (!aligned(x, 16) || !aligned(y, 16) || !aligned(conv_pool, 16))
+    return fail(GDN_EINVAL, "x, y and conv_pool must be 16-byte aligned");
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e = hipSuccess;
+  if (total_tokens > 0) {
+    gdn::ConvArgs ca{};
+    ca.x = x; ca.w = conv_weight; ca.cu = cu_seqlens; ca.read_idx = read_idx; ca.write_idx = write_idx;
+    ca.conv_pool = reinterpret_cast<const char*>(conv_pool); ca.conv_stride = conv_block_stride;
+    ca.y = y;
+    ca.num_seqs = num_seqs; ca.total_tokens = total_tokens; ca.num_blocks = num_blocks; ca.channels = channels;
+    ca.qk_channels = 0;   // no normalisation
+    ca.head_k_dim = 128;  // lanes of the (unused) head sums
+    ca.eps = 0.f;
+    ca.q_scale = 1.f;
+    const int groups = (channels + 511) / 512;
+    const int slices = std::max(1, 4096 / groups);
+    const int rows = (total_tokens + slices - 1) / slices;
+    ca.rows_per_block = std::min(256, std::max(4, (rows + 3) / 4 * 4));
+    e = timed(K_CONV, st, [&] { return gdn::launch_conv(ca, W, bf16, silu != 0, st); });
+    if (e != hipSuccess) return fail(GDN_EHIP, "conv launch: %s", hipGetErrorString(e));
+  }
+  if (W > 1) {
+    gdn::TailArgs ta{};
+    ta.x = x; ta.cu = cu_seqlens; ta.read_idx = read_idx; ta.write_idx = write_idx;
+    ta.conv_pool = reinterpret_cast<char*>(conv_pool); ta.conv_stride = conv_block_stride;
+    ta.num_seqs = num_seqs; ta.num_blocks = num_blocks; ta.channels = channels;
+    ta.max_len = INT_MAX;
     e = timed(K_TAIL, st, [&] { return gdn::launch_tail_commit(ta, W, bf16, st); });
     if (e != hipSuccess) return fail(GDN_EHIP, "conv state commit launch: %s", hipGetErrorString(e));
   }

@@ -102,7 +102,7 @@ struct Raw8 {
   }
 };
 
-template <bool BF16, int W>
+template <bool BF16, int W, bool SILU>
 __global__ __launch_bounds__(256) void conv_silu_norm_kernel(ConvArgs a) {
   constexpr int ESZ = BF16 ? 2 : 4;
   const int c0 = (blockIdx.y * blockDim.x + threadIdx.x) * 8;
@@ -138,6 +138,7 @@ __global__ __launch_bounds__(256) void conv_silu_norm_kernel(ConvArgs a) {
   int s = find_seq(a.cu, a.num_seqs, r_begin);
   int seq_begin = a.cu[s], seq_end = a.cu[s + 1];
   bool fresh = true;
+  bool on = seq_active(a.read_idx, a.write_idx, s, a.num_blocks);  // rows of a padding sequence are not written
   // LA rows of x in flight per thread (row r is loaded LA rows ahead of its
   // use), and the inputs of rows r-LA+1..r in a circular buffer indexed by
   // r mod LA; r_begin is a multiple of LA, so every index is static.
@@ -161,6 +162,7 @@ __global__ __launch_bounds__(256) void conv_silu_norm_kernel(ConvArgs a) {
         seq_begin = seq_end;
         seq_end = a.cu[s + 1];
         fresh = true;
+        on = seq_active(a.read_idx, a.write_idx, s, a.num_blocks);
       }
       if constexpr (W > 1) {
         if (fresh) {  // the W-1 inputs before row r: earlier rows of the sequence, else its conv state
@@ -191,7 +193,7 @@ __global__ __launch_bounds__(256) void conv_silu_norm_kernel(ConvArgs a) {
         float acc = wt[e][W - 1] * xr[k][e];
 #pragma unroll
         for (int j = 1; j < W; ++j) acc += wt[e][W - 1 - j] * xr[(k - j + LA) % LA][e];
-        yv[e] = silu(acc);
+        yv[e] = SILU ? silu(acc) : acc;
         ss += yv[e] * yv[e];
       }
       for (int off = 1; off < group; off <<= 1) ss += __shfl_xor(ss, off);
@@ -200,7 +202,7 @@ __global__ __launch_bounds__(256) void conv_silu_norm_kernel(ConvArgs a) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) yv[e] *= inv;
       }
-      if (cok) Act8<BF16>::template store<true>(a.y, (int64_t)r * a.channels + c0, yv);
+      if (cok && on) Act8<BF16>::template store<true>(a.y, (int64_t)r * a.channels + c0, yv);
     }
   }
   (void)ESZ;
@@ -243,13 +245,13 @@ __global__ __launch_bounds__(256) void conv_tail_commit_kernel(TailArgs a) {
   }
 }
 
-template <bool BF16, int W>
+template <bool BF16, int W, bool SILU>
 hipError_t conv_dispatch(const ConvArgs& a, hipStream_t st) {
   const int threads = 64;  // one wave: 512 channels
   const int per_block = threads * 8;
   dim3 grid((a.total_tokens + a.rows_per_block - 1) / a.rows_per_block,
             (a.channels + per_block - 1) / per_block);
-  hipLaunchKernelGGL((conv_silu_norm_kernel<BF16, W>), grid, dim3(threads), 0, st, a);
+  hipLaunchKernelGGL((conv_silu_norm_kernel<BF16, W, SILU>), grid, dim3(threads), 0, st, a);
   return hipGetLastError();
 }
 
@@ -264,16 +266,24 @@ hipError_t tail_dispatch(const TailArgs& a, hipStream_t st) {
 
 }  // namespace
 
-hipError_t launch_conv(const ConvArgs& a, int width, bool bf16, hipStream_t st) {
-  switch (width * 2 + (bf16 ? 1 : 0)) {
-    case 2: return conv_dispatch<false, 1>(a, st);
-    case 3: return conv_dispatch<true, 1>(a, st);
-    case 4: return conv_dispatch<false, 2>(a, st);
-    case 5: return conv_dispatch<true, 2>(a, st);
-    case 6: return conv_dispatch<false, 3>(a, st);
-    case 7: return conv_dispatch<true, 3>(a, st);
-    case 8: return conv_dispatch<false, 4>(a, st);
-    case 9: return conv_dispatch<true, 4>(a, st);
+hipError_t launch_conv(const ConvArgs& a, int width, bool bf16, bool silu, hipStream_t st) {
+  switch (width * 4 + (bf16 ? 2 : 0) + (silu ? 1 : 0)) {
+    case 4: return conv_dispatch<false, 1, false>(a, st);
+    case 5: return conv_dispatch<false, 1, true>(a, st);
+    case 6: return conv_dispatch<true, 1, false>(a, st);
+    case 7: return conv_dispatch<true, 1, true>(a, st);
+    case 8: return conv_dispatch<false, 2, false>(a, st);
+    case 9: return conv_dispatch<false, 2, true>(a, st);
+    case 10: return conv_dispatch<true, 2, false>(a, st);
+    case 11: return conv_dispatch<true, 2, true>(a, st);
+    case 12: return conv_dispatch<false, 3, false>(a, st);
+    case 13: return conv_dispatch<false, 3, true>(a, st);
+    case 14: return conv_dispatch<true, 3, false>(a, st);
+    case 15: return conv_dispatch<true, 3, true>(a, st);
+    case 16: return conv_dispatch<false, 4, false>(a, st);
+    case 17: return conv_dispatch<false, 4, true>(a, st);
+    case 18: return conv_dispatch<true, 4, false>(a, st);
+    case 19: return conv_dispatch<true, 4, true>(a, st);
   }
   return hipErrorInvalidValue;
 }

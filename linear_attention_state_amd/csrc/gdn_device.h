@@ -127,7 +127,8 @@ struct SeqOrder {
   uint16_t seq[kMaxOrder];
 };
 
-hipError_t launch_conv(const ConvArgs& a, int width, bool bf16, hipStream_t st);
+// silu: SiLU after the conv; q/k normalisation of the channels below 2 * qk_channels
+hipError_t launch_conv(const ConvArgs& a, int width, bool bf16, bool silu, hipStream_t st);
 hipError_t launch_tail_commit(const TailArgs& a, int width, bool bf16, hipStream_t st);
 hipError_t launch_recurrent(const ScanArgs& a, int dk, int dv, bool bf16, hipStream_t st);
 // The conv of the chunked sequences run by the chunk-scan workgroups

@@ -63,6 +63,9 @@ def _load():
         ]
         lib.gdn_oracle_conv_silu.restype = None
         lib.gdn_oracle_conv_silu.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_int64, P, P, P, P]
+        lib.gdn_oracle_varlen_conv.restype = ctypes.c_int
+        lib.gdn_oracle_varlen_conv.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                               P, P, P, ctypes.c_int32, P, P, P, ctypes.c_int32, P]
         lib.gdn_oracle_l2norm.restype = None
         lib.gdn_oracle_l2norm.argtypes = [ctypes.c_int64, P, ctypes.c_double, ctypes.c_double]
         lib.gdn_oracle_delta_rule.restype = None
@@ -96,6 +99,30 @@ def conv_silu(tail, x, w) -> np.ndarray:
     y = np.zeros((max(L, 1), C))
     _load().gdn_oracle_conv_silu(C, W, L, _ptr(tail), _ptr(xb), _ptr(w), _ptr(y))
     return y[:L]
+
+
+def varlen_conv(x, conv_weight, cu_seqlens, read_idx, write_idx, conv_pool, silu: bool = True):
+    """Standalone varlen conv layer over a packed row (see gdn_oracle.c).
+
+    CPU torch tensors: x [T][C] and conv_weight [C][W] and conv_pool [P][W-1][C]
+    in one act dtype (bf16 or float32), indices int32.  Returns ``(y, conv_pool_new)``:
+    y [T][C] float64, NaN on the rows of padding sequences."""
+    bf16 = x.dtype == torch.bfloat16
+    assert conv_weight.dtype == x.dtype and conv_pool.dtype == x.dtype
+    x = x.contiguous()
+    w = conv_weight.contiguous()
+    C, W = w.shape
+    T = x.shape[0]
+    cu = cu_seqlens.to(torch.int32).contiguous()
+    ri = read_idx.to(torch.int32).contiguous()
+    wi = write_idx.to(torch.int32).contiguous()
+    pool = conv_pool.clone().contiguous()
+    y = np.full((max(T, 1), C), np.nan)
+    rc = _load().gdn_oracle_varlen_conv(C, W, int(bf16), int(bool(silu)), _ptr(x), _ptr(w), _ptr(cu),
+                                        cu.numel() - 1, _ptr(ri), _ptr(wi), _ptr(pool), pool.shape[0], _ptr(y))
+    if rc != 0:
+        raise ValueError("oracle rejected its arguments (rc=%d)" % rc)
+    return y[:T], pool
 
 
 def l2norm(v, eps: float = 1e-6, scale: float = 1.0) -> np.ndarray:

@@ -89,6 +89,49 @@ void gdn_oracle_conv_silu(int64_t C, int32_t W, int64_t L, const double* tail,
   }
 }
 
+/* Standalone varlen conv layer over a packed row (the tracker page lists
+ * models with conv-only layers; the mechanism is the varlen conv of the PR
+ * description, without the split, normalisation and recurrence).  For every
+ * sequence, with xext = [conv state of its read block; its x rows]:
+ *   y[t][c] = act( sum_j w[c][j] * xext[t+j][c] ),  act = SiLU if silu else identity,
+ * and the last W-1 rows of xext become the conv state of its write block
+ * (raw storage copies).  write_idx < 0: the sequence is skipped (its y rows are
+ * left as they are, NaN from the caller).
+ *   x [T][C] act, w [C][W] act, conv_pool [P][W-1][C] act (updated), y [T][C] fp64.
+ * Returns 0, or -1 on an index it cannot use. */
+int gdn_oracle_varlen_conv(int64_t C, int32_t W, int32_t act_bf16, int32_t silu, const void* x,
+                           const void* conv_weight, const int32_t* cu_seqlens, int32_t num_seqs,
+                           const int32_t* read_idx, const int32_t* write_idx, void* conv_pool,
+                           int32_t num_blocks, double* y) {
+  const size_t esz = act_bf16 ? 2 : 4;
+  const int64_t tail_elems = (int64_t)(W - 1) * C;
+  for (int32_t s = 0; s < num_seqs; ++s) {
+    const int64_t r0 = cu_seqlens[s];
+    const int64_t L = (int64_t)cu_seqlens[s + 1] - r0;
+    const int32_t rb = read_idx[s], wb = write_idx[s];
+    if (wb < 0) continue;
+    if (L < 0 || rb < 0 || rb >= num_blocks || wb >= num_blocks) return -1;
+    /* xext as raw storage: W-1 state rows then the L input rows */
+    const int64_t rows = (W - 1) + L;
+    char* ext = (char*)malloc(esz * (size_t)(rows * C > 0 ? rows * C : 1));
+    if (tail_elems > 0)
+      memcpy(ext, (char*)conv_pool + (size_t)rb * esz * (size_t)tail_elems, esz * (size_t)tail_elems);
+    if (L > 0) memcpy(ext + esz * (size_t)tail_elems, (const char*)x + esz * (size_t)(r0 * C), esz * (size_t)(L * C));
+    for (int64_t t = 0; t < L; ++t)
+      for (int64_t c = 0; c < C; ++c) {
+        double acc = 0.0;
+        for (int32_t j = 0; j < W; ++j)
+          acc += act_load(conv_weight, c * W + j, act_bf16) * act_load(ext, (t + j) * C + c, act_bf16);
+        y[(r0 + t) * C + c] = silu ? acc / (1.0 + exp(-acc)) : acc;
+      }
+    if (tail_elems > 0)
+      memcpy((char*)conv_pool + (size_t)wb * esz * (size_t)tail_elems, ext + esz * (size_t)(L * C),
+             esz * (size_t)tail_elems);
+    free(ext);
+  }
+  return 0;
+}
+
 /* In-place L2 normalisation of n values, then multiplication by scale. */
 void gdn_oracle_l2norm(int64_t n, double* v, double eps, double scale) {
   double ss = 0.0;

@@ -105,3 +105,36 @@ def _call(layer, cu_host, T, n=None, **over):
 def test_forward_rejects_bad_arguments(cu, T, over, status, needle):
     rc, msg = _call(workloads.BIG, cu, T, **over)
     assert rc == status and needle in msg, (rc, msg)
+
+
+def _conv_call(cu_host, T, C=1024, W=4, act=gdn.GDN_BF16, **over):
+    """gdn_varlen_conv with fake (never dereferenced) device pointers."""
+    lib = gdn.load_library()
+    fake = ctypes.c_void_p(1 << 20)
+    cu = (ctypes.c_int32 * len(cu_host))(*cu_host)
+    args = dict(C=C, W=W, act=act, x=fake, w=fake, cu=fake, cuh=cu, n=len(cu_host) - 1, T=T, ri=fake, wi=fake,
+                conv=fake, cstride=(W - 1) * C * 2, P=8, y=fake)
+    args.update(over)
+    rc = lib.gdn_varlen_conv(args["C"], args["W"], args["act"], 1, args["x"], args["w"], args["cu"], args["cuh"],
+                             args["n"], args["T"], args["ri"], args["wi"], args["conv"], args["cstride"], args["P"],
+                             args["y"], None)
+    return rc, gdn.gdn_last_error()
+
+
+@pytest.mark.parametrize("cu,T,over,status,needle", [
+    ([0], 0, {}, gdn.GDN_EINVAL, "no sequences"),
+    ([0, 5, 3], 3, {}, gdn.GDN_EINVAL, "decreases"),
+    ([0, 5, 9], 8, {}, gdn.GDN_EINVAL, "total_tokens"),
+    ([0, 4], 4, {"C": 1020, "cstride": 3 * 1020 * 2}, gdn.GDN_EUNSUPPORTED, "multiple of 8"),
+    ([0, 4], 4, {"W": 5}, gdn.GDN_EUNSUPPORTED, "conv_width"),
+    ([0, 4], 4, {"W": 0}, gdn.GDN_EINVAL, "conv_width"),
+    ([0, 4], 4, {"act": 7}, gdn.GDN_EINVAL, "act_dtype"),
+    ([0, 4], 4, {"conv": None}, gdn.GDN_EINVAL, "conv_pool"),
+    ([0, 4], 4, {"P": 1}, gdn.GDN_EINVAL, "num_blocks"),
+    ([0, 4], 4, {"cstride": 3 * 1024 * 2 - 16}, gdn.GDN_EINVAL, "conv_block_stride"),
+    ([0, 4], 4, {"y": ctypes.c_void_p((1 << 20) + 8)}, gdn.GDN_EINVAL, "aligned"),
+    ([0, 4], 4, {"cuh": None}, gdn.GDN_EINVAL, "cu_seqlens_host"),
+])
+def test_varlen_conv_rejects_bad_arguments(cu, T, over, status, needle):
+    rc, msg = _conv_call(cu, T, **over)
+    assert rc == status and needle in msg, (rc, msg)

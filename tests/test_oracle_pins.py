@@ -320,3 +320,84 @@ def test_empty_sequence_is_identity():
     out, fin, cp, sp = _run(b)
     rb, wb = int(b.read_idx[0]), int(b.write_idx[0])
     assert torch.equal(sp[wb], b.ssm_pool[rb]) and torch.equal(cp[wb], b.conv_pool[rb])
+
+
+# ------------------------------------------------------- standalone varlen conv
+
+def _vc_batch(C, W, lengths, seed, dtype=torch.float32, P=6):
+    rng = np.random.default_rng(seed)
+    T = sum(lengths)
+    x = torch.tensor(rng.standard_normal((T, C)), dtype=torch.float32).to(dtype)
+    w = torch.tensor(rng.standard_normal((C, W)) / math.sqrt(W), dtype=torch.float32).to(dtype)
+    pool = torch.tensor(rng.standard_normal((P, W - 1, C)), dtype=torch.float32).to(dtype)
+    pool[0] = 0
+    cu = torch.tensor(np.concatenate([[0], np.cumsum(lengths)]), dtype=torch.int32)
+    return x, w, pool, cu
+
+
+def test_varlen_conv_hand_example():
+    """W = 2, one channel: x = 1, 2, 3 after a state of 4, taps (0.5, 2)."""
+    x = torch.tensor([[1.0], [2.0], [3.0]])
+    w = torch.tensor([[0.5, 2.0]])
+    pool = torch.tensor([[[0.0]], [[4.0]], [[9.0]]])
+    y, new = oracle.varlen_conv(x, w, torch.tensor([0, 3], dtype=torch.int32), torch.tensor([1], dtype=torch.int32),
+                                torch.tensor([2], dtype=torch.int32), pool, silu=False)
+    assert y[:, 0].tolist() == [4.0, 4.5, 7.0]
+    assert new[2, 0, 0].item() == 3.0 and new[1, 0, 0].item() == 4.0
+
+
+def test_varlen_conv_silu_closed_form():
+    """A single tap of 1 on x = ln 3 gives SiLU(ln 3) = 0.75 ln 3."""
+    x = torch.tensor([[math.log(3.0)]], dtype=torch.float32)
+    y, _ = oracle.varlen_conv(x, torch.tensor([[1.0]]), torch.tensor([0, 1], dtype=torch.int32),
+                              torch.tensor([0], dtype=torch.int32), torch.tensor([1], dtype=torch.int32),
+                              torch.zeros(2, 0, 1), silu=True)
+    xv = float(x[0, 0])
+    assert abs(y[0, 0] - 0.75 * math.log(3.0)) < 1e-6
+    assert abs(y[0, 0] - xv / (1.0 + math.exp(-xv))) < 1e-12
+
+
+@pytest.mark.parametrize("W", [1, 2, 4])
+def test_varlen_conv_matches_numpy_correlate(W):
+    """Each sequence and channel is numpy's valid cross-correlation of
+    [state; x] with the taps; sequences continue from their own blocks."""
+    C, lengths = 5, [7, 1, 12]
+    x, w, pool, cu = _vc_batch(C, W, lengths, seed=61)
+    ri = torch.tensor([3, 0, 5], dtype=torch.int32)
+    wi = torch.tensor([3, 1, 2], dtype=torch.int32)
+    y, new = oracle.varlen_conv(x, w, cu, ri, wi, pool, silu=False)
+    for s in range(3):
+        xs = x[cu[s]:cu[s + 1]].double().numpy()
+        ext = np.concatenate([pool[ri[s]].double().numpy().reshape(W - 1, C), xs], axis=0)
+        for c in range(C):
+            ref = np.correlate(ext[:, c], w[c].double().numpy(), mode="valid")
+            assert np.allclose(y[cu[s]:cu[s + 1], c], ref, rtol=1e-12, atol=1e-12)
+        # new state: the last W-1 rows of [state; x], copied bit for bit
+        exp_tail = torch.cat([pool[ri[s]], x[cu[s]:cu[s + 1]]], dim=0)[-(W - 1):] if W > 1 else pool[wi[s]]
+        assert torch.equal(new[wi[s]], exp_tail.reshape(new[wi[s]].shape))
+
+
+def test_varlen_conv_silu_equals_layer_conv():
+    """With SiLU, every sequence equals the layer oracle's conv_silu on its rows."""
+    C, W, lengths = 6, 4, [9, 3]
+    x, w, pool, cu = _vc_batch(C, W, lengths, seed=62, dtype=torch.bfloat16)
+    ri = torch.tensor([2, 4], dtype=torch.int32)
+    y, _ = oracle.varlen_conv(x, w, cu, ri, torch.tensor([2, 4], dtype=torch.int32), pool, silu=True)
+    for s in range(2):
+        ref = oracle.conv_silu(pool[ri[s]].float().numpy(), x[cu[s]:cu[s + 1]].float().numpy(), w.float().numpy())
+        assert np.array_equal(y[cu[s]:cu[s + 1]], ref)
+
+
+def test_varlen_conv_short_sequence_shifts_state_and_padding_is_skipped():
+    C, W = 3, 4
+    x, w, pool, cu = _vc_batch(C, W, [1, 2], seed=63)
+    ri = torch.tensor([1, 2], dtype=torch.int32)
+    wi = torch.tensor([4, -1], dtype=torch.int32)
+    y, new = oracle.varlen_conv(x, w, cu, ri, wi, pool, silu=False)
+    # one token: the new state drops the oldest row and appends the token
+    assert torch.equal(new[4], torch.cat([pool[1][1:], x[0:1]], dim=0))
+    # padding: its rows untouched (NaN), and no block changes other than block 4
+    assert np.isnan(y[1:3]).all()
+    for b in range(6):
+        if b != 4:
+            assert torch.equal(new[b], pool[b])
