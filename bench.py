@@ -8,8 +8,8 @@ state pools) are generated once, copied to HBM before timing, and stay there.
 Primary line: the prefill workload (8 sequences, lengths uniform in [256, 4096],
 H_k=16, H_v=32, d_k=d_v=128, W=4, bf16 activations, fp32 state), tokens/s.
 The same JSON line carries the decode workload (256 sequences of one token,
-1024-block pool) and the standalone varlen conv layer (gdn_varlen_conv on the
-prefill rows) as nested objects, each with the roofline of its dominant
+1024-block pool), the standalone varlen conv layer (gdn_varlen_conv on the
+prefill rows) and the fork copy (gdn_state_copy of 256 blocks) as nested objects, each with the roofline of its dominant
 kernel and the per-kernel event timings, and the fp64 CPU oracle timed on the
 host cores beside them.
 
@@ -217,6 +217,54 @@ def run_conv(steps: int, warmup: int):
             "kernels": {k: {"avg_ms": v[0] / max(v[1], 1), "launches": v[1]} for k, v in kt.items()}}
 
 
+def run_state_copy(steps: int, warmup: int):
+    """The fork copy (gdn_state_copy) of 256 blocks of the decode workload's
+    1024-block pool into 256 other blocks."""
+    import torch
+
+    import linear_attention_state_amd as gdn
+    import workloads
+
+    b = workloads.config(2)
+    dev = torch.device("cuda", 0)
+    cp = b.conv_pool.to(dev).contiguous()
+    sp = b.ssm_pool.to(dev).contiguous()
+    P = sp.shape[0]
+    perm = torch.randperm(P - 1, generator=torch.Generator().manual_seed(5)) + 1
+    src = perm[:256].to(torch.int32).to(dev)
+    dst = perm[256:512].to(torch.int32).to(dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        gdn.gdn_state_copy(b.layer, cp, sp, src, dst, stream=stream.cuda_stream)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for _ in range(steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / steps
+    gdn.gdn_kernel_timing(True)
+    for _ in range(steps):
+        step()
+    kt = gdn.gdn_kernel_times()
+    gdn.gdn_kernel_timing(False)
+    per_block = sp[0].numel() * 4 + cp[0].numel() * cp.element_size()
+    work = 2 * 256 * per_block  # each block read once and written once
+    k_ms = kt["state_copy"][0] / kt["state_copy"][1]
+    roof = {"bound": "hbm", "achieved": work / (k_ms * 1e-3) / 1e9, "peak": PEAK_HBM / 1e9, "unit": "GB/s",
+            "kernel": "state_copy"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = None
+    return {"workload": "fork copy of 256 blocks (2 MiB recurrent + 48 KiB conv state each) within a 1024-block pool",
+            "value": 256 / (ms * 1e-3), "unit": "blocks/s", "ms_per_step": ms, "roofline": roof,
+            "kernels": {k: {"avg_ms": v[0] / max(v[1], 1), "launches": v[1]} for k, v in kt.items()}}
+
+
 def cpu_baseline(batch):
     """The fp64 oracle on the host cores, on the same workload (all of it when
     it takes under half a minute), tokens/s."""
@@ -242,8 +290,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
-    ap.add_argument("--no-conv", action="store_true", help="skip the standalone conv layer entry")
-    ap.add_argument("--only", choices=["prefill", "decode", "conv"], default=None,
+    ap.add_argument("--no-conv", action="store_true", help="skip the standalone conv layer and fork copy entries")
+    ap.add_argument("--only", choices=["prefill", "decode", "conv", "copy"], default=None,
                     help="run one workload alone and print its numbers (profiling runs)")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="run only a device-to-device copy of this many bytes (calibrates HBM byte counters)")
@@ -264,6 +312,9 @@ def main():
         return
     if args.only == "conv":
         print(json.dumps(run_conv(args.steps, args.warmup)), flush=True)
+        return
+    if args.only == "copy":
+        print(json.dumps(run_state_copy(args.steps, args.warmup)), flush=True)
         return
     if args.only:
         r = run(1 if args.only == "prefill" else 2, args.steps, args.warmup)
@@ -290,6 +341,7 @@ def main():
         del dec
     if not args.no_conv:
         line["conv"] = run_conv(args.steps, args.warmup)
+        line["state_copy"] = run_state_copy(args.steps, args.warmup)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(b)
     print(json.dumps(line), flush=True)

@@ -161,19 +161,35 @@ int gdn_varlen_conv(int32_t channels, int32_t conv_width, int32_t act_dtype, int
                     const int32_t* read_idx, const int32_t* write_idx, void* conv_pool,
                     int64_t conv_block_stride, int32_t num_blocks, void* y, void* stream);
 
+/* Fork copy (the PR description: a request's states are copied when it forks):
+ * for i < n, both states of block src[i] (its conv state and its recurrent
+ * state) are copied bit for bit to block dst[i], so the child continues
+ * exactly where the parent stands.
+ *   conv_pool, conv_block_stride, ssm_pool, ssm_block_stride, num_blocks: as
+ *       for gdn_varlen_forward (conv_pool may be NULL when W == 1)
+ *   src, dst  [n] int32 block indices, device memory; a pair with an index
+ *       outside [0, num_blocks), or with src[i] == dst[i], is skipped
+ * Preconditions: the dst blocks are distinct and none is a src block of the
+ * same call (pairs run in parallel).  Enqueued on `stream`; no allocation, no
+ * host sync. */
+int gdn_state_copy(const gdn_layer_desc* desc, void* conv_pool, int64_t conv_block_stride,
+                   float* ssm_pool, int64_t ssm_block_stride, int32_t num_blocks,
+                   const int32_t* src, const int32_t* dst, int32_t n, void* stream);
+
 /* Message of the last non-OK status returned on this thread ("" if none). */
 const char* gdn_last_error(void);
 
 /* Measurement support (not needed to run the layer).
- * gdn_kernel_timing(1) makes every later gdn_varlen_forward in this process
- * record a HIP event pair on the call's stream around each kernel it launches,
+ * gdn_kernel_timing(1) makes every later gdn_varlen_forward, gdn_varlen_conv
+ * and gdn_state_copy in this process record a HIP event pair on the call's
+ * stream around each kernel it launches,
  * and clears the totals; gdn_kernel_timing(0) stops recording.
  * gdn_kernel_times() waits for the recorded events (a host sync), adds their
  * elapsed times to per-kernel totals and copies up to `max` entries to `out`;
  * `count` receives the number of kernels with at least one timed launch.
  * The library creates the events it records and keeps them for reuse. */
 typedef struct {
-  char name[32];      /* kernel: "conv_silu_norm", "chunk_scan", "token_recurrent", "conv_state_commit" */
+  char name[32];      /* kernel: "conv_silu_norm", "chunk_scan", "token_recurrent", "conv_state_commit", "state_copy" */
   double total_ms;    /* summed event-to-event time of its timed launches */
   int64_t launches;
 } gdn_kernel_time;

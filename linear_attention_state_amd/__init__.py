@@ -16,7 +16,8 @@ LIB_PATH = os.path.join(HERE, "_lib", "libgdn.so")
 
 GDN_OK, GDN_EINVAL, GDN_EUNSUPPORTED, GDN_EWORKSPACE, GDN_EHIP = 0, -1, -2, -3, -4
 GDN_F32, GDN_BF16 = 0, 1
-EXPORTS = ("gdn_state_spec", "gdn_workspace_size", "gdn_varlen_forward", "gdn_varlen_conv", "gdn_last_error",
+EXPORTS = ("gdn_state_spec", "gdn_workspace_size", "gdn_varlen_forward", "gdn_varlen_conv", "gdn_state_copy",
+           "gdn_last_error",
            "gdn_kernel_timing", "gdn_kernel_times")
 
 _lib = None
@@ -82,6 +83,9 @@ def load_library():
         lib.gdn_varlen_conv.argtypes = [
             ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, P, P, P, P, ctypes.c_int32,
             ctypes.c_int32, P, P, P, ctypes.c_int64, ctypes.c_int32, P, P]
+        lib.gdn_state_copy.restype = ctypes.c_int
+        lib.gdn_state_copy.argtypes = [ctypes.POINTER(gdn_layer_desc), P, ctypes.c_int64, P, ctypes.c_int64,
+                                       ctypes.c_int32, P, P, ctypes.c_int32, P]
         lib.gdn_kernel_timing.restype = ctypes.c_int
         lib.gdn_kernel_timing.argtypes = [ctypes.c_int]
         lib.gdn_kernel_times.restype = ctypes.c_int
@@ -205,6 +209,25 @@ def gdn_varlen_conv(x, conv_weight, cu_seqlens, cu_seqlens_host, read_idx, write
         num_blocks, _dev_ptr(y, "y"), ctypes.c_void_p(stream))
     _check(rc)
     return y
+
+
+def gdn_state_copy(layer, conv_pool, ssm_pool, src, dst, stream=None):
+    """Enqueues the fork copy of both states of blocks ``src`` to blocks ``dst``
+    (device int32 tensors of equal length); the pools are updated in place."""
+    import torch
+
+    if src.dtype != torch.int32 or dst.dtype != torch.int32 or src.numel() != dst.numel():
+        raise ValueError("src and dst must be int32 tensors of one length")
+    if ssm_pool.dtype != torch.float32:
+        raise ValueError("ssm_pool must be float32")
+    if stream is None:
+        stream = torch.cuda.current_stream(ssm_pool.device).cuda_stream
+    has_conv = conv_pool is not None and conv_pool.numel() > 0
+    conv_stride = conv_pool.stride(0) * conv_pool.element_size() if has_conv else 0
+    _check(load_library().gdn_state_copy(
+        ctypes.byref(make_desc(layer)), _dev_ptr(conv_pool, "conv_pool") if has_conv else None, conv_stride,
+        _dev_ptr(ssm_pool, "ssm_pool"), ssm_pool.stride(0) * ssm_pool.element_size(), int(ssm_pool.shape[0]),
+        _dev_ptr(src, "src"), _dev_ptr(dst, "dst"), int(src.numel()), ctypes.c_void_p(stream)))
 
 
 def gdn_kernel_timing(enable: bool) -> None:

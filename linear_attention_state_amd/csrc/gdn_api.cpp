@@ -111,8 +111,9 @@ int device_cus(hipStream_t st) {
 bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
 
 // ---- optional per-kernel event timing (measurement only)
-enum { K_CONV = 0, K_CHUNK, K_TOKEN, K_TAIL, K_COUNT };
-const char* const kKernelNames[K_COUNT] = {"conv_silu_norm", "chunk_scan", "token_recurrent", "conv_state_commit"};
+enum { K_CONV = 0, K_CHUNK, K_TOKEN, K_TAIL, K_COPY, K_COUNT };
+const char* const kKernelNames[K_COUNT] = {"conv_silu_norm", "chunk_scan", "token_recurrent", "conv_state_commit",
+                                           "state_copy"};
 
 struct Timing {
   std::mutex mu;
@@ -461,5 +462,40 @@ extern "C" int gdn_varlen_conv(int32_t channels, int32_t conv_width, int32_t act
     e = timed(K_TAIL, st, [&] { return gdn::launch_tail_commit(ta, W, bf16, st); });
     if (e != hipSuccess) return fail(GDN_EHIP, "conv state commit launch: %s", hipGetErrorString(e));
   }
+  return GDN_OK;
+}
+
+extern "C" int gdn_state_copy(const gdn_layer_desc* desc, void* conv_pool, int64_t conv_block_stride,
+                              float* ssm_pool, int64_t ssm_block_stride, int32_t num_blocks, const int32_t* src,
+                              const int32_t* dst, int32_t n, void* stream) {
+  int rc = check_desc(desc);
+  if (rc) return rc;
+  const int W = desc->conv_width;
+  if (n < 0) return fail(GDN_EINVAL, "n=%d is negative", n);
+  if (n == 0) return GDN_OK;
+  if (!src || !dst) return fail(GDN_EINVAL, "src or dst is NULL");
+  if (!ssm_pool) return fail(GDN_EINVAL, "ssm_pool is NULL");
+  if (W > 1 && !conv_pool) return fail(GDN_EINVAL, "conv_pool is NULL but conv_width=%d > 1", W);
+  if (num_blocks < 1) return fail(GDN_EINVAL, "num_blocks=%d", num_blocks);
+  if (ssm_block_stride < ssm_state_bytes(desc) || ssm_block_stride % 16)
+    return fail(GDN_EINVAL, "ssm_block_stride=%lld must be a multiple of 16 and >= %lld", (long long)ssm_block_stride,
+                (long long)ssm_state_bytes(desc));
+  if (W > 1 && (conv_block_stride < conv_state_bytes(desc) || conv_block_stride % 16))
+    return fail(GDN_EINVAL, "conv_block_stride=%lld must be a multiple of 16 and >= %lld",
+                (long long)conv_block_stride, (long long)conv_state_bytes(desc));
+  if (!aligned(ssm_pool, 16) || !aligned(conv_pool, 16)) return fail(GDN_EINVAL, "the pools must be 16-byte aligned");
+  gdn::StateCopyArgs ca{};
+  ca.ssm_pool = reinterpret_cast<char*>(ssm_pool);
+  ca.conv_pool = reinterpret_cast<char*>(conv_pool);
+  ca.ssm_stride = ssm_block_stride;
+  ca.conv_stride = conv_block_stride;
+  ca.ssm_bytes = ssm_state_bytes(desc);
+  ca.conv_bytes = W > 1 ? conv_state_bytes(desc) : 0;
+  ca.src = src;
+  ca.dst = dst;
+  ca.num_blocks = num_blocks;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const hipError_t e = timed(K_COPY, st, [&] { return gdn::launch_state_copy(ca, n, st); });
+  if (e != hipSuccess) return fail(GDN_EHIP, "state copy launch: %s", hipGetErrorString(e));
   return GDN_OK;
 }

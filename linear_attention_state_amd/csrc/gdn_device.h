@@ -130,6 +130,19 @@ struct SeqOrder {
 // silu: SiLU after the conv; q/k normalisation of the channels below 2 * qk_channels
 hipError_t launch_conv(const ConvArgs& a, int width, bool bf16, bool silu, hipStream_t st);
 hipError_t launch_tail_commit(const TailArgs& a, int width, bool bf16, hipStream_t st);
+
+// Fork copy: both states of block src[i] to block dst[i].  Sizes and strides
+// are multiples of 16 bytes; pairs with an index outside [0, num_blocks) or
+// src == dst are skipped.
+struct StateCopyArgs {
+  char* ssm_pool;
+  char* conv_pool;
+  int64_t ssm_stride, conv_stride, ssm_bytes, conv_bytes;
+  const int32_t* src;
+  const int32_t* dst;
+  int num_blocks;
+};
+hipError_t launch_state_copy(const StateCopyArgs& a, int n, hipStream_t st);
 hipError_t launch_recurrent(const ScanArgs& a, int dk, int dv, bool bf16, hipStream_t st);
 // The conv of the chunked sequences run by the chunk-scan workgroups
 // themselves, as tasks they claim before their scans.  Task t belongs to

@@ -138,3 +138,32 @@ def _conv_call(cu_host, T, C=1024, W=4, act=gdn.GDN_BF16, **over):
 def test_varlen_conv_rejects_bad_arguments(cu, T, over, status, needle):
     rc, msg = _conv_call(cu, T, **over)
     assert rc == status and needle in msg, (rc, msg)
+
+
+def _copy_call(**over):
+    lib = gdn.load_library()
+    fake = ctypes.c_void_p(1 << 20)
+    args = dict(conv=fake, cstride=3 * 8192 * 2, ssm=fake, sstride=2 << 20, P=8, src=fake, dst=fake, n=3)
+    args.update(over)
+    rc = lib.gdn_state_copy(ctypes.byref(gdn.make_desc(workloads.BIG)), args["conv"], args["cstride"], args["ssm"],
+                            args["sstride"], args["P"], args["src"], args["dst"], args["n"], None)
+    return rc, gdn.gdn_last_error()
+
+
+@pytest.mark.parametrize("over,status,needle", [
+    ({"n": -1}, gdn.GDN_EINVAL, "negative"),
+    ({"src": None}, gdn.GDN_EINVAL, "src or dst"),
+    ({"ssm": None}, gdn.GDN_EINVAL, "ssm_pool"),
+    ({"conv": None}, gdn.GDN_EINVAL, "conv_pool"),
+    ({"sstride": (2 << 20) - 16}, gdn.GDN_EINVAL, "ssm_block_stride"),
+    ({"cstride": 3 * 8192 * 2 + 8}, gdn.GDN_EINVAL, "conv_block_stride"),
+    ({"ssm": ctypes.c_void_p((1 << 20) + 4)}, gdn.GDN_EINVAL, "aligned"),
+])
+def test_state_copy_rejects_bad_arguments(over, status, needle):
+    rc, msg = _copy_call(**over)
+    assert rc == status and needle in msg, (rc, msg)
+
+
+def test_state_copy_of_nothing_is_ok():
+    rc, _ = _copy_call(n=0, src=None, dst=None)
+    assert rc == gdn.GDN_OK
