@@ -8,8 +8,9 @@ state pools) are generated once, copied to HBM before timing, and stay there.
 Primary line: the prefill workload (8 sequences, lengths uniform in [256, 4096],
 H_k=16, H_v=32, d_k=d_v=128, W=4, bf16 activations, fp32 state), tokens/s.
 The same JSON line carries the decode workload (256 sequences of one token,
-1024-block pool), the standalone varlen conv layer (gdn_varlen_conv on the
-prefill rows) and the fork copy (gdn_state_copy of 256 blocks) as nested objects, each with the roofline of its dominant
+1024-block pool), the prefill step planned on the device and replayed from a
+HIP graph, the standalone varlen conv layer (gdn_varlen_conv on the prefill
+rows) and the fork copy (gdn_state_copy of 256 blocks) as nested objects, each with the roofline of its dominant
 kernel and the per-kernel event timings, and the fp64 CPU oracle timed on the
 host cores beside them.
 
@@ -165,6 +166,51 @@ def run(cfg_id: int, steps: int, warmup: int):
     }
 
 
+def run_graph(steps: int, warmup: int):
+    """The prefill step planned on the device (cu_seqlens_host = NULL), captured
+    once in a HIP graph and replayed."""
+    import torch
+
+    import linear_attention_state_amd as gdn
+    import workloads
+
+    b = workloads.config(1)
+    L = b.layer
+    dev = torch.device("cuda", 0)
+    d = {k: getattr(b, k).to(dev).contiguous() for k in
+         ("x", "conv_weight", "g", "beta", "cu_seqlens", "read_idx", "write_idx", "conv_pool", "ssm_pool")}
+    T = b.total_tokens
+    out = torch.empty(T, L.num_v_heads, L.head_v_dim, dtype=L.torch_act, device=dev)
+    ws = torch.empty(gdn.gdn_workspace_size(L, T, len(b.lengths)), dtype=torch.uint8, device=dev)
+
+    def step():
+        gdn.gdn_varlen_forward(L, d["x"], d["conv_weight"], d["g"], d["beta"], d["cu_seqlens"], None,
+                               d["read_idx"], d["write_idx"], d["conv_pool"], d["ssm_pool"], out, workspace=ws)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for _ in range(3):
+            step()
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    stream = torch.cuda.current_stream(dev)
+    for _ in range(warmup):
+        graph.replay()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for _ in range(steps):
+        graph.replay()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / steps
+    return {"workload": "the prefill workload planned on the device, one HIP graph replay per step",
+            "value": T / (ms * 1e-3), "unit": "tokens/s", "ms_per_step": ms}
+
+
 def run_conv(steps: int, warmup: int):
     """The standalone varlen conv layer (gdn_varlen_conv, SiLU) on the prefill
     workload's rows: x [T][8192] bf16, W = 4, every sequence from the trash block."""
@@ -291,7 +337,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-conv", action="store_true", help="skip the standalone conv layer and fork copy entries")
-    ap.add_argument("--only", choices=["prefill", "decode", "conv", "copy"], default=None,
+    ap.add_argument("--only", choices=["prefill", "decode", "conv", "copy", "graph"], default=None,
                     help="run one workload alone and print its numbers (profiling runs)")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="run only a device-to-device copy of this many bytes (calibrates HBM byte counters)")
@@ -315,6 +361,9 @@ def main():
         return
     if args.only == "copy":
         print(json.dumps(run_state_copy(args.steps, args.warmup)), flush=True)
+        return
+    if args.only == "graph":
+        print(json.dumps(run_graph(args.steps, args.warmup)), flush=True)
         return
     if args.only:
         r = run(1 if args.only == "prefill" else 2, args.steps, args.warmup)
@@ -340,6 +389,7 @@ def main():
                           "roofline": dec["roofline"], "kernels": dec["kernels"]}
         del dec
     if not args.no_conv:
+        line["prefill_graph"] = run_graph(args.steps, args.warmup)
         line["conv"] = run_conv(args.steps, args.warmup)
         line["state_copy"] = run_state_copy(args.steps, args.warmup)
     if not args.no_cpu_baseline:

@@ -85,7 +85,8 @@ typedef struct {
 int gdn_state_spec(const gdn_layer_desc* desc, gdn_state_decl out[2]);
 
 /* Bytes of device workspace gdn_varlen_forward needs for a batch of
- * total_tokens packed tokens and num_seqs sequences.  Host only. */
+ * total_tokens packed tokens and num_seqs sequences (y, the conv task
+ * counters and the device plan).  Host only. */
 int gdn_workspace_size(const gdn_layer_desc* desc, int32_t total_tokens,
                        int32_t num_seqs, size_t* bytes);
 
@@ -115,6 +116,14 @@ int gdn_workspace_size(const gdn_layer_desc* desc, int32_t total_tokens,
  * Host pointer:
  *   cu_seqlens_host  the same N+1 offsets in host memory; the library plans its
  *                launches from it so that it never reads device memory back.
+ *                NULL: the launch is planned on the device from cu_seqlens by a
+ *                small planning kernel (at most 1024 sequences), and every launch
+ *                size and argument depends only on N, total_tokens and the
+ *                pointers, so a captured graph of the call replays correctly for
+ *                any offsets, indices and data of the same N and total_tokens
+ *                (the offsets are then not checked: they must be non-decreasing
+ *                from 0 to total_tokens).  Results are bitwise the same as with
+ *                the host plan.
  * Preconditions the library cannot check without a sync (violations give
  * undefined results, never out-of-bounds accesses for indices outside [0, P),
  * which are skipped): device cu_seqlens equals cu_seqlens_host; write blocks are

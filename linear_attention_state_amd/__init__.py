@@ -140,17 +140,22 @@ def gdn_varlen_forward(layer, x, conv_weight, g, beta, cu_seqlens, cu_seqlens_ho
                        conv_pool, ssm_pool, out, workspace=None, stream=None):
     """Enqueues the packed-batch forward on ``stream`` (default: torch's current
     stream).  Device tensors as in ``gdn.h``; ``cu_seqlens_host`` is a CPU int32
-    tensor (or list) with the same offsets.  Pools are updated in place; block
-    strides are taken from the pool tensors' first dimension."""
+    tensor (or list) with the same offsets, or None to plan the launch on the
+    device (graph capture).  Pools are updated in place; block strides are taken
+    from the pool tensors' first dimension."""
     import torch
 
     lib = load_library()
-    if not isinstance(cu_seqlens_host, torch.Tensor):
-        cu_seqlens_host = torch.tensor(list(cu_seqlens_host), dtype=torch.int32)
-    cu_h = cu_seqlens_host.to(torch.int32).contiguous()
-    if cu_h.is_cuda:
-        raise ValueError("cu_seqlens_host must be host memory")
-    num_seqs = cu_h.numel() - 1
+    if cu_seqlens_host is None:  # plan on the device (graph capture)
+        cu_h = None
+        num_seqs = cu_seqlens.numel() - 1
+    else:
+        if not isinstance(cu_seqlens_host, torch.Tensor):
+            cu_seqlens_host = torch.tensor(list(cu_seqlens_host), dtype=torch.int32)
+        cu_h = cu_seqlens_host.to(torch.int32).contiguous()
+        if cu_h.is_cuda:
+            raise ValueError("cu_seqlens_host must be host memory")
+        num_seqs = cu_h.numel() - 1
     total = int(x.shape[0])
     for name, t, dt in (("cu_seqlens", cu_seqlens, torch.int32), ("read_idx", read_idx, torch.int32),
                         ("write_idx", write_idx, torch.int32), ("g", g, torch.float32),
@@ -167,7 +172,8 @@ def gdn_varlen_forward(layer, x, conv_weight, g, beta, cu_seqlens, cu_seqlens_ho
     rc = lib.gdn_varlen_forward(
         ctypes.byref(make_desc(layer)), _dev_ptr(x, "x"), _dev_ptr(conv_weight, "conv_weight"),
         _dev_ptr(g, "g"), _dev_ptr(beta, "beta"), _dev_ptr(cu_seqlens, "cu_seqlens"),
-        ctypes.c_void_p(cu_h.data_ptr()), num_seqs, total, _dev_ptr(read_idx, "read_idx"),
+        ctypes.c_void_p(cu_h.data_ptr()) if cu_h is not None else None, num_seqs, total,
+        _dev_ptr(read_idx, "read_idx"),
         _dev_ptr(write_idx, "write_idx"),
         _dev_ptr(conv_pool, "conv_pool") if conv_pool is not None and conv_pool.numel() else None,
         conv_stride, _dev_ptr(ssm_pool, "ssm_pool"), ssm_stride, int(ssm_pool.shape[0]),

@@ -75,10 +75,34 @@ int64_t ssm_state_bytes(const gdn_layer_desc* d) {
 size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 // The workspace holds the conv output of the packed row for the chunked
-// prefill, then the task counters of the conv run inside the scan kernel.
-size_t workspace_bytes_for(const gdn_layer_desc* d, int64_t total_tokens) {
-  if (total_tokens <= 0) return 0;
-  return round_up((size_t)total_tokens * (size_t)channels(d) * (size_t)act_size(d), 256) + gdn::kFusedSyncBytes;
+// prefill, the task counters of the conv run inside the scan kernel, and the
+// device plan (used when the launch is planned on the device).
+struct WsLayout {
+  size_t sync, plan, total;
+};
+WsLayout ws_layout(const gdn_layer_desc* d, int64_t total_tokens, int64_t num_seqs) {
+  WsLayout l{0, 0, 0};
+  if (total_tokens <= 0) return l;
+  l.sync = round_up((size_t)total_tokens * (size_t)channels(d) * (size_t)act_size(d), 256);
+  const size_t sync_bytes = std::max(gdn::kFusedSyncBytes, 4 * (size_t)(1 + std::max<int64_t>(num_seqs, 0)));
+  l.plan = l.sync + round_up(sync_bytes, 256);
+  l.total = l.plan + round_up(4 * gdn::plan_ints((int)std::min<int64_t>(std::max<int64_t>(num_seqs, 0), INT_MAX / 4)), 256);
+  return l;
+}
+size_t workspace_bytes_for(const gdn_layer_desc* d, int64_t total_tokens, int64_t num_seqs) {
+  return ws_layout(d, total_tokens, num_seqs).total;
+}
+
+// Time model of the fused prefill (microseconds, measured on MI355X with the
+// 128 x 128 head): a scan takes kScan0Us + kScan1Us per chunk; a conv task
+// moves its rows in and out at about 17 GB/s per workgroup; the conv kernel
+// runs at about 4.2 TB/s; the makespan target sits 3% past the even spread of
+// all conv and scan work over the workgroups (3% measured best of 0-10%).
+constexpr double kScan0Us = 11.0, kScan1Us = 2.8, kTaskBytesPerUs = 17e3, kConvBytesPerUs = 4.2e6;
+constexpr double kTargetMargin = 1.03;
+
+double task_us(int C, const gdn_layer_desc* d) {
+  return 2.0 * gdn::kConvTaskRows * std::min(C, gdn::kConvTaskChannels) * act_size(d) / kTaskBytesPerUs;
 }
 
 // GDN_CONV_IN_SCAN: "always" runs the conv inside the chunk kernel whenever
@@ -227,7 +251,7 @@ extern "C" int gdn_workspace_size(const gdn_layer_desc* desc, int32_t total_toke
   if (rc) return rc;
   if (!bytes) return fail(GDN_EINVAL, "bytes is NULL");
   if (total_tokens < 0 || num_seqs < 0) return fail(GDN_EINVAL, "negative token or sequence count");
-  *bytes = workspace_bytes_for(desc, total_tokens);
+  *bytes = workspace_bytes_for(desc, total_tokens, num_seqs);
   return GDN_OK;
 }
 
@@ -248,15 +272,21 @@ extern "C" int gdn_varlen_forward(const gdn_layer_desc* desc, const void* x, con
   // ---- host-side checks; nothing below reads device memory
   if (num_seqs < 1) return fail(GDN_EINVAL, "no sequences in batch (num_seqs=%d)", num_seqs);
   if (total_tokens < 0) return fail(GDN_EINVAL, "total_tokens=%d is negative", total_tokens);
-  if (!cu_seqlens_host) return fail(GDN_EINVAL, "cu_seqlens_host is NULL");
-  if (cu_seqlens_host[0] != 0) return fail(GDN_EINVAL, "cu_seqlens[0]=%d, expected 0", cu_seqlens_host[0]);
-  for (int i = 0; i < num_seqs; ++i)
-    if (cu_seqlens_host[i + 1] < cu_seqlens_host[i])
-      return fail(GDN_EINVAL, "cu_seqlens decreases at %d (%d -> %d)", i, cu_seqlens_host[i],
-                  cu_seqlens_host[i + 1]);
-  if (cu_seqlens_host[num_seqs] != total_tokens)
-    return fail(GDN_EINVAL, "cu_seqlens[%d]=%d differs from total_tokens=%d", num_seqs,
-                cu_seqlens_host[num_seqs], total_tokens);
+  const bool dev_plan = cu_seqlens_host == nullptr;  // plan on the device (graph capture)
+  if (dev_plan) {
+    if (num_seqs > gdn::kMaxPlanSeqs)
+      return fail(GDN_EUNSUPPORTED, "planning on the device takes at most %d sequences (num_seqs=%d)",
+                  gdn::kMaxPlanSeqs, num_seqs);
+  } else {
+    if (cu_seqlens_host[0] != 0) return fail(GDN_EINVAL, "cu_seqlens[0]=%d, expected 0", cu_seqlens_host[0]);
+    for (int i = 0; i < num_seqs; ++i)
+      if (cu_seqlens_host[i + 1] < cu_seqlens_host[i])
+        return fail(GDN_EINVAL, "cu_seqlens decreases at %d (%d -> %d)", i, cu_seqlens_host[i],
+                    cu_seqlens_host[i + 1]);
+    if (cu_seqlens_host[num_seqs] != total_tokens)
+      return fail(GDN_EINVAL, "cu_seqlens[%d]=%d differs from total_tokens=%d", num_seqs,
+                  cu_seqlens_host[num_seqs], total_tokens);
+  }
   if (!cu_seqlens || !read_idx || !write_idx) return fail(GDN_EINVAL, "device cu_seqlens/read_idx/write_idx is NULL");
   if (!ssm_pool) return fail(GDN_EINVAL, "ssm_pool is NULL");
   if (W > 1 && !conv_pool) return fail(GDN_EINVAL, "conv_pool is NULL but conv_width=%d > 1", W);
@@ -273,17 +303,12 @@ extern "C" int gdn_varlen_forward(const gdn_layer_desc* desc, const void* x, con
   if (!aligned(x, 16) || !aligned(out, 16) || !aligned(ssm_pool, 16) || !aligned(conv_pool, 16) ||
       !aligned(g, 4) || !aligned(beta, 4))
     return fail(GDN_EINVAL, "x, out and the pools must be 16-byte aligned");
-  const size_t need = workspace_bytes_for(desc, total_tokens);
+  const WsLayout wl = ws_layout(desc, total_tokens, num_seqs);
+  const size_t need = wl.total;
   if (need > 0 && (!workspace || workspace_bytes < need))
     return fail(GDN_EWORKSPACE, "workspace of %zu bytes is smaller than the %zu needed", workspace_bytes, need);
   if (workspace && !aligned(workspace, 256)) return fail(GDN_EINVAL, "workspace must be 256-byte aligned");
 
-  // ---- plan from the host offsets
-  int n_long = 0, n_short = 0;
-  for (int i = 0; i < num_seqs; ++i) {
-    const int L = cu_seqlens_host[i + 1] - cu_seqlens_host[i];
-    if (L >= 2) ++n_long; else ++n_short;
-  }
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   const int C = (int)channels(desc);
   hipError_t e = hipSuccess;
@@ -297,6 +322,79 @@ extern "C" int gdn_varlen_forward(const gdn_layer_desc* desc, const void* x, con
   sa.write_idx = write_idx; sa.ssm_pool = ssm_pool; sa.ssm_stride = ssm_block_stride; sa.out = out;
   sa.num_seqs = num_seqs; sa.num_blocks = num_blocks; sa.num_k_heads = desc->num_k_heads;
   sa.num_v_heads = desc->num_v_heads; sa.channels = C;
+  const bool chunked = bf16 && gdn::chunk_supported(desc->head_k_dim, desc->head_v_dim);
+
+  gdn::TailArgs ta{};
+  ta.x = x; ta.cu = cu_seqlens; ta.read_idx = read_idx; ta.write_idx = write_idx;
+  ta.conv_pool = reinterpret_cast<char*>(conv_pool); ta.conv_stride = conv_block_stride;
+  ta.num_seqs = num_seqs; ta.num_blocks = num_blocks; ta.channels = C;
+  ta.max_len = INT_MAX;
+
+  gdn::ConvArgs ca{};
+  ca.x = x; ca.w = conv_weight; ca.cu = cu_seqlens; ca.read_idx = read_idx; ca.write_idx = write_idx;
+  ca.conv_pool = reinterpret_cast<const char*>(conv_pool); ca.conv_stride = conv_block_stride;
+  ca.y = workspace;
+  ca.num_seqs = num_seqs; ca.total_tokens = total_tokens; ca.num_blocks = num_blocks; ca.channels = C;
+  ca.qk_channels = desc->num_k_heads * desc->head_k_dim; ca.head_k_dim = desc->head_k_dim;
+  {  // about 4096 one-wave blocks (16 per CU): rows per block a multiple of the 4 rows in flight
+    const int groups = (C + 511) / 512;
+    const int slices = std::max(1, 4096 / groups);
+    const int rows = (total_tokens + slices - 1) / slices;
+    ca.rows_per_block = std::min(256, std::max(4, (rows + 3) / 4 * 4));
+  }
+  ca.eps = sa.eps;
+  ca.q_scale = sa.q_scale;
+
+  // ---- plan on the device: every launch size depends on num_seqs and
+  // total_tokens only, so a captured graph replays for any offsets and indices
+  if (dev_plan) {
+    if (chunked && total_tokens > 0) {
+      int32_t* plan = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(workspace) + wl.plan);
+      int32_t* sync = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(workspace) + wl.sync);
+      const int mode = conv_in_scan_mode();
+      gdn::PlanArgs pa{};
+      pa.cu = cu_seqlens; pa.num_seqs = num_seqs; pa.num_v_heads = desc->num_v_heads;
+      pa.slices = (C + gdn::kConvTaskChannels - 1) / gdn::kConvTaskChannels; pa.conv_rows = gdn::kConvTaskRows;
+      pa.fused_allowed = mode >= 0 && aligned(conv_weight, 16) &&
+                         (int64_t)num_seqs * desc->num_v_heads <= device_cus(st);
+      pa.fused_forced = mode > 0;
+      pa.conv_us_per_token = 2.0 * C * act_size(desc) / kConvBytesPerUs;
+      pa.task_us = task_us(C, desc);
+      pa.scan0_us = kScan0Us; pa.scan1_us = kScan1Us; pa.margin = kTargetMargin * 100.0;
+      pa.plan = plan; pa.sync = sync;
+      e = gdn::launch_plan(pa, st);
+      if (e != hipSuccess) return fail(GDN_EHIP, "plan launch: %s", hipGetErrorString(e));
+      ca.skip = plan + gdn::kPlanFused;
+      e = timed(K_CONV, st, [&] { return gdn::launch_conv(ca, W, bf16, true, st); });
+      if (e != hipSuccess) return fail(GDN_EHIP, "conv launch: %s", hipGetErrorString(e));
+      static thread_local gdn::SeqOrder none;
+      none.n = 0;
+      static thread_local gdn::FusedConv fc;
+      fc.n = 0; fc.slices = pa.slices; fc.sync = sync;
+      fc.target = 0; fc.task = (int32_t)(pa.task_us * 100.0);
+      fc.scan0 = (int32_t)(kScan0Us * 100.0); fc.scan1 = (int32_t)(kScan1Us * 100.0);
+      fc.plan = plan; fc.plan_seqs = num_seqs;
+      sa.min_len = 2; sa.max_len = INT_MAX;
+      e = timed(K_CHUNK, st, [&] { return gdn::launch_chunk(sa, none, fc, desc->head_k_dim, desc->head_v_dim, st); });
+      if (e != hipSuccess) return fail(GDN_EHIP, "chunk scan launch: %s", hipGetErrorString(e));
+      ta.fused = plan + gdn::kPlanFused;
+    }
+    sa.min_len = 0; sa.max_len = chunked ? 1 : INT_MAX;
+    e = timed(K_TOKEN, st, [&] { return gdn::launch_recurrent(sa, desc->head_k_dim, desc->head_v_dim, bf16, st); });
+    if (e != hipSuccess) return fail(GDN_EHIP, "token path launch: %s", hipGetErrorString(e));
+    if (W > 1) {
+      e = timed(K_TAIL, st, [&] { return gdn::launch_tail_commit(ta, W, bf16, st); });
+      if (e != hipSuccess) return fail(GDN_EHIP, "conv state commit launch: %s", hipGetErrorString(e));
+    }
+    return GDN_OK;
+  }
+
+  // ---- plan from the host offsets
+  int n_long = 0, n_short = 0;
+  for (int i = 0; i < num_seqs; ++i) {
+    const int L = cu_seqlens_host[i + 1] - cu_seqlens_host[i];
+    if (L >= 2) ++n_long; else ++n_short;
+  }
 
   // Order on the stream: (1) conv + SiLU + norm of the packed row into the
   // workspace for the chunked prefill (its own kernel, or inside the chunk
@@ -305,7 +403,6 @@ extern "C" int gdn_varlen_forward(const gdn_layer_desc* desc, const void* x, con
   // from the conv states, (4) conv-state commit, last, once every reader of the
   // old conv states has been enqueued (when the chunk kernel ran the conv, it
   // also wrote the chunked sequences' states, and this covers the rest).
-  const bool chunked = bf16 && gdn::chunk_supported(desc->head_k_dim, desc->head_v_dim);
   bool tails_done = false;  // the chunk kernel has written the chunked sequences' conv states
   if (chunked && n_long > 0) {
     sa.min_len = 2; sa.max_len = INT_MAX;
@@ -330,16 +427,15 @@ extern "C" int gdn_varlen_forward(const gdn_layer_desc* desc, const void* x, con
     // Otherwise the conv kernel writes all of y first.
     static thread_local gdn::FusedConv fc;
     fc.n = 0;
+    fc.plan = nullptr;
+    fc.plan_seqs = 0;
     const int mode = conv_in_scan_mode();
     if (mode >= 0 && order.n > 0 && order.n <= gdn::kMaxFusedRanks && aligned(conv_weight, 16) &&
         (int64_t)order.n * desc->num_v_heads <= device_cus(st)) {
       fc.slices = (C + gdn::kConvTaskChannels - 1) / gdn::kConvTaskChannels;
       fc.first[0] = 0;
-      // Time model (microseconds, measured on the 128 x 128 head): a scan
-      // takes 11 + 2.8 per chunk; a conv task moves its rows in and out at
-      // about 17 GB/s per workgroup; the conv kernel runs at about 4.2 TB/s.
-      const double scan0 = 11.0, scan1 = 2.8;
-      const double task_us = 2.0 * gdn::kConvTaskRows * std::min(C, gdn::kConvTaskChannels) * act_size(desc) / 17e3;
+      const double scan0 = kScan0Us, scan1 = kScan1Us;
+      const double task_us = ::task_us(C, desc);
       double scans = 0.0;
       for (int r = 0; r < order.n; ++r) {
         const int L = cu_seqlens_host[order.seq[r] + 1] - cu_seqlens_host[order.seq[r]];
@@ -351,32 +447,17 @@ extern "C" int gdn_varlen_forward(const gdn_layer_desc* desc, const void* x, con
       // work spread evenly over the workgroups, but no earlier than the longest scan allows
       const double fused = std::max((fc.first[order.n] * task_us + desc->num_v_heads * scans) /
                                     ((double)order.n * desc->num_v_heads), longest + 2.0 * task_us);
-      const double apart = 2.0 * (double)total_tokens * C * act_size(desc) / 4.2e6 + longest + 3.0;
+      const double apart = 2.0 * (double)total_tokens * C * act_size(desc) / kConvBytesPerUs + longest + 3.0;
       if (mode > 0 || 1.05 * fused < apart) {
         fc.n = order.n;
-        fc.sync = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(workspace) + (need - gdn::kFusedSyncBytes));
-        // 100 ticks per microsecond; aiming 3% past the even spread measured best
-        fc.target = (int32_t)(fused * 103.0);
+        fc.sync = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(workspace) + wl.sync);
+        fc.target = (int32_t)(fused * kTargetMargin * 100.0);  // 100 ticks per microsecond
         fc.task = (int32_t)(task_us * 100.0);
         fc.scan0 = (int32_t)(scan0 * 100.0);
         fc.scan1 = (int32_t)(scan1 * 100.0);
       }
     }
     if (fc.n == 0) {
-      gdn::ConvArgs ca{};
-      ca.x = x; ca.w = conv_weight; ca.cu = cu_seqlens; ca.read_idx = read_idx; ca.write_idx = write_idx;
-      ca.conv_pool = reinterpret_cast<const char*>(conv_pool); ca.conv_stride = conv_block_stride;
-      ca.y = workspace;
-      ca.num_seqs = num_seqs; ca.total_tokens = total_tokens; ca.num_blocks = num_blocks; ca.channels = C;
-      ca.qk_channels = desc->num_k_heads * desc->head_k_dim; ca.head_k_dim = desc->head_k_dim;
-      {  // about 4096 one-wave blocks (16 per CU): rows per block a multiple of the 4 rows in flight
-        const int groups = (C + 511) / 512;
-        const int slices = std::max(1, 4096 / groups);
-        const int rows = (total_tokens + slices - 1) / slices;
-        ca.rows_per_block = std::min(256, std::max(4, (rows + 3) / 4 * 4));
-      }
-      ca.eps = sa.eps;
-      ca.q_scale = sa.q_scale;
       e = timed(K_CONV, st, [&] { return gdn::launch_conv(ca, W, bf16, true, st); });
       if (e != hipSuccess) return fail(GDN_EHIP, "conv launch: %s", hipGetErrorString(e));
     }
@@ -390,10 +471,6 @@ extern "C" int gdn_varlen_forward(const gdn_layer_desc* desc, const void* x, con
     if (e != hipSuccess) return fail(GDN_EHIP, "token path launch: %s", hipGetErrorString(e));
   }
   if (W > 1 && (!tails_done || n_short > 0)) {
-    gdn::TailArgs ta{};
-    ta.x = x; ta.cu = cu_seqlens; ta.read_idx = read_idx; ta.write_idx = write_idx;
-    ta.conv_pool = reinterpret_cast<char*>(conv_pool); ta.conv_stride = conv_block_stride;
-    ta.num_seqs = num_seqs; ta.num_blocks = num_blocks; ta.channels = C;
     ta.max_len = tails_done ? 1 : INT_MAX;
     e = timed(K_TAIL, st, [&] { return gdn::launch_tail_commit(ta, W, bf16, st); });
     if (e != hipSuccess) return fail(GDN_EHIP, "conv state commit launch: %s", hipGetErrorString(e));

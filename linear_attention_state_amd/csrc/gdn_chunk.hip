@@ -849,6 +849,36 @@ __device__ __forceinline__ void p_role(Smem& sm, const Seq& q, const Lane& ln) {
 // agent-scope acquire fence) before the scan reads the rows.
 constexpr int kStoreDeviceScope = 16 | 2;  // buffer store cache policy: SC1 (device scope) | NT (streaming)
 
+// The launch order and the conv task plan: from the kernel arguments (planned
+// on the host, DP = false), or from the device plan array (planned by
+// plan_kernel, DP = true).  Two instantiations, so that the host-planned
+// kernel carries no trace of the device plan (registers are at the limit).
+template <bool DP>
+__device__ __forceinline__ int plan_n(const SeqOrder& ord, const FusedConv& fc) {
+  if constexpr (DP) return fc.plan[kPlanN];
+  else return ord.n;
+}
+template <bool DP>
+__device__ __forceinline__ int plan_fused_n(const FusedConv& fc) {
+  if constexpr (DP) return fc.plan[kPlanFused] ? fc.plan[kPlanN] : 0;
+  else return fc.n;
+}
+template <bool DP>
+__device__ __forceinline__ int plan_seq(const SeqOrder& ord, const FusedConv& fc, int r) {
+  if constexpr (DP) return fc.plan[kPlanOrder + r];
+  else return (int)ord.seq[r];
+}
+template <bool DP>
+__device__ __forceinline__ int plan_first(const FusedConv& fc, int r) {
+  if constexpr (DP) return fc.plan[kPlanOrder + fc.plan_seqs + r];
+  else return fc.first[r];
+}
+template <bool DP>
+__device__ __forceinline__ int32_t plan_target(const FusedConv& fc) {
+  if constexpr (DP) return fc.plan[kPlanTarget];
+  else return fc.target;
+}
+
 // One task: rows [r0, r0 + n) of sequence s (rows from seq0) at channels
 // c0..c0+7 of each thread; `on` is false for the threads past the channel count.
 struct ConvTask {
@@ -856,16 +886,17 @@ struct ConvTask {
   bool on;
 };
 
+template <bool DP>
 __device__ __forceinline__ ConvTask conv_decode(const ScanArgs& a, const SeqOrder& ord, const FusedConv& fc, int t) {
-  int lo = 0, hi = fc.n;  // rank of task t: first[r] <= t < first[r + 1]
+  int lo = 0, hi = plan_fused_n<DP>(fc);  // rank of task t: first[r] <= t < first[r + 1]
   while (hi - lo > 1) {
     const int mid = (lo + hi) >> 1;
-    if (fc.first[mid] <= t) lo = mid; else hi = mid;
+    if (plan_first<DP>(fc, mid) <= t) lo = mid; else hi = mid;
   }
   ConvTask k;
-  const int loc = t - fc.first[lo];
+  const int loc = t - plan_first<DP>(fc, lo);
   k.rank = lo;
-  k.s = ord.seq[lo];
+  k.s = plan_seq<DP>(ord, fc, lo);
   k.seq0 = a.cu[k.s];
   k.r0 = k.seq0 + (loc / fc.slices) * kConvTaskRows;
   k.n = min(kConvTaskRows, a.cu[k.s + 1] - k.r0);
@@ -1005,15 +1036,16 @@ __device__ __forceinline__ int claim_after(const FusedConv& fc, int newest, int 
 // call it.  While a task is computed from registers, the rows of the next
 // claimed task are loading into LDS, and a third task is being claimed.  On
 // return no LDS access or load of the phase is outstanding.
-template <int W>
+template <bool DP, int W>
 __device__ void conv_phase(Smem& sm, const ScanArgs& a, const SeqOrder& ord, const FusedConv& fc, int rank) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int total = fc.first[fc.n];
-  const int last = fc.first[rank + 1];  // my rank's tasks end here
+  const int total = plan_first<DP>(fc, plan_fused_n<DP>(fc));
+  const int last = plan_first<DP>(fc, rank + 1);  // my rank's tasks end here
   // latest claim of a task that two more precede before my scan
-  const int my_s = ord.seq[rank];
-  const int32_t latest = fc.target - fc.scan0 - fc.scan1 * ((a.cu[my_s + 1] - a.cu[my_s] + BT - 1) / BT) - 3 * fc.task;
+  const int my_s = plan_seq<DP>(ord, fc, rank);
+  const int32_t latest =
+      plan_target<DP>(fc) - fc.scan0 - fc.scan1 * ((a.cu[my_s + 1] - a.cu[my_s] + BT - 1) / BT) - 3 * fc.task;
   const uint64_t t_begin = __builtin_amdgcn_s_memrealtime();
   if (tid == 0) sm.task = __hip_atomic_fetch_add(fc.sync, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   lds_barrier();
@@ -1022,7 +1054,7 @@ __device__ void conv_phase(Smem& sm, const ScanArgs& a, const SeqOrder& ord, con
   ConvTask k{};
   ConvSide<W> cur, nxt;
   if (t < total) {
-    k = conv_decode(a, ord, fc, t);
+    k = conv_decode<DP>(a, ord, fc, t);
     conv_prefetch<W>(sm, a, k, nxt);
   }
   if (tid == 0) sm.task = claim_after(fc, t, total, last, latest, t_begin);
@@ -1042,7 +1074,7 @@ __device__ void conv_phase(Smem& sm, const ScanArgs& a, const SeqOrder& ord, con
     lds_barrier();  // every thread has read sm.task (u)
     ConvTask kn{};
     if (u < total) {
-      kn = conv_decode(a, ord, fc, u);
+      kn = conv_decode<DP>(a, ord, fc, u);
       conv_prefetch<W>(sm, a, kn, nxt);
     }
     int v = total;
@@ -1062,9 +1094,10 @@ __device__ void conv_phase(Smem& sm, const ScanArgs& a, const SeqOrder& ord, con
 // Waits until every conv task of `rank` is counted, then makes their rows
 // visible to this workgroup.  Bounded: every task counted here is claimed (the
 // workgroup claimed past them before it stopped) and finishes without waiting.
+template <bool DP>
 __device__ __forceinline__ void conv_wait(const FusedConv& fc, int rank) {
   if (threadIdx.x == 0) {
-    const int need = fc.first[rank + 1] - fc.first[rank];
+    const int need = plan_first<DP>(fc, rank + 1) - plan_first<DP>(fc, rank);
     for (int it = 0; it < (1 << 24); ++it) {
       if (__hip_atomic_load(&fc.sync[1 + rank], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= need) break;
       __builtin_amdgcn_s_sleep(2);
@@ -1074,13 +1107,14 @@ __device__ __forceinline__ void conv_wait(const FusedConv& fc, int rank) {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
 }
 
+template <bool DP>
 __device__ __forceinline__ void conv_phase_w(Smem& sm, const ScanArgs& a, const SeqOrder& ord, const FusedConv& fc,
                                              int rank) {
   switch (a.width) {
-    case 1: conv_phase<1>(sm, a, ord, fc, rank); break;
-    case 2: conv_phase<2>(sm, a, ord, fc, rank); break;
-    case 3: conv_phase<3>(sm, a, ord, fc, rank); break;
-    default: conv_phase<4>(sm, a, ord, fc, rank); break;
+    case 1: conv_phase<DP, 1>(sm, a, ord, fc, rank); break;
+    case 2: conv_phase<DP, 2>(sm, a, ord, fc, rank); break;
+    case 3: conv_phase<DP, 3>(sm, a, ord, fc, rank); break;
+    default: conv_phase<DP, 4>(sm, a, ord, fc, rank); break;
   }
 }
 
@@ -1088,11 +1122,12 @@ __device__ __forceinline__ void conv_phase_w(Smem& sm, const ScanArgs& a, const 
 // once every conv task of the sequence (the readers of the old state) is done.
 // Each thread reads all W-1 rows of its 8 channels before it writes, so the
 // ordinary in-place case (read block == write block) is safe.
+template <bool DP>
 __device__ void commit_tail(Smem& sm, const ScanArgs& a, const SeqOrder& ord, const FusedConv& fc, int rank) {
   const int W = a.width;
   if (W < 2) return;
-  conv_wait(fc, rank);  // the tasks of every rank are claimed before the last rank's are
-  const int s = ord.seq[rank];
+  conv_wait<DP>(fc, rank);  // the tasks of every rank are claimed before the last rank's are
+  const int s = plan_seq<DP>(ord, fc, rank);
   if (!seq_active(a.read_idx, a.write_idx, s, a.num_blocks)) return;  // uniform
   const int r0 = a.cu[s], L = a.cu[s + 1] - r0, C = a.channels;
   const gptr<const u32x4> x = as_global(reinterpret_cast<const u32x4*>(a.x));
@@ -1111,23 +1146,87 @@ __device__ void commit_tail(Smem& sm, const ScanArgs& a, const SeqOrder& ord, co
   }
 }
 
+// Plans a launch on the device from cu_seqlens, for calls that leave the
+// planning to the device (graph capture): the launch order of the chunked
+// sequences (length >= 2; longest first, then lower index), the conv task
+// ranges, the choice between the conv inside the chunk kernel and the conv
+// kernel, and the makespan target, all by the same rules as the host plan; and
+// it zeroes the task counters.  One workgroup of 1024 threads, one thread per
+// sequence.
+__global__ __launch_bounds__(1024) void plan_kernel(PlanArgs a) {
+  __shared__ int len[kMaxPlanSeqs];
+  __shared__ int tasks[kMaxPlanSeqs];
+  __shared__ int n_long, longest, chunks_sum;
+  const int tid = threadIdx.x, N = a.num_seqs;
+  for (int i = tid; i < 1 + N; i += blockDim.x) a.sync[i] = 0;
+  if (tid == 0) {
+    n_long = 0;
+    longest = 0;
+    chunks_sum = 0;
+  }
+  for (int i = tid; i < N; i += blockDim.x) len[i] = a.cu[i + 1] - a.cu[i];
+  __syncthreads();
+  int rank = -1;
+  if (tid < N && len[tid] >= 2) {
+    const int L = len[tid];
+    rank = 0;
+    for (int j = 0; j < N; ++j) rank += (len[j] >= 2 && (len[j] > L || (len[j] == L && j < tid))) ? 1 : 0;
+    a.plan[kPlanOrder + rank] = tid;
+    atomicAdd(&n_long, 1);
+    atomicMax(&longest, L);
+    atomicAdd(&chunks_sum, (L + BT - 1) / BT);
+  }
+  __syncthreads();
+  const int n = n_long;
+  if (rank >= 0) tasks[rank] = (len[tid] + a.conv_rows - 1) / a.conv_rows * a.slices;
+  __syncthreads();
+  // inclusive scan of tasks[0 .. n) (Hillis-Steele; one entry per thread)
+  for (int off = 1; off < n; off <<= 1) {
+    const int v = (tid < n && tid >= off) ? tasks[tid - off] : 0;
+    __syncthreads();
+    if (tid < n) tasks[tid] += v;
+    __syncthreads();
+  }
+  int32_t* first = a.plan + kPlanOrder + N;
+  if (tid == 0) first[0] = 0;
+  if (tid < n) first[tid + 1] = tasks[tid];
+  if (tid == 0) {
+    const int T = a.cu[N];
+    const int total = n > 0 ? tasks[n - 1] : 0;
+    const double scans = n * a.scan0_us + a.scan1_us * chunks_sum;
+    const double lng = a.scan0_us + a.scan1_us * ((longest + BT - 1) / BT);
+    double fused = n > 0 ? (total * a.task_us + a.num_v_heads * scans) / ((double)n * a.num_v_heads) : 0.0;
+    fused = fmax(fused, lng + 2.0 * a.task_us);
+    const double apart = a.conv_us_per_token * T + lng + 3.0;
+    const int use = a.fused_allowed && n > 0 && (a.fused_forced || 1.05 * fused < apart);
+    a.plan[kPlanN] = n;
+    a.plan[kPlanFused] = use;
+    a.plan[kPlanTarget] = (int32_t)(fused * a.margin);
+    a.plan[3] = 0;
+  }
+}
+
 __global__ void zero_sync_kernel(int32_t* p, int n) {
   for (int i = threadIdx.x; i < n; i += blockDim.x) p[i] = 0;
 }
 
+template <bool DP>
 __global__ __launch_bounds__(NT) void chunk_scan_kernel(ScanArgs a, SeqOrder ord, FusedConv fc) {
   __shared__ Smem sm;
   const int Hv = a.num_v_heads;
   const int rank = blockIdx.x / Hv;
   Seq q;
   q.m = blockIdx.x % Hv;
-  q.s = ord.n > 0 ? (rank < ord.n ? (int)ord.seq[rank] : a.num_seqs) : rank;
-  if (fc.n > 0) {
-    conv_phase_w(sm, a, ord, fc, rank);  // every rank < fc.n == ord.n; waits come later
+  const int n_ord = plan_n<DP>(ord, fc);
+  const int fused_n = plan_fused_n<DP>(fc);  // 0, or every rank of the launch order
+  if (DP && rank >= n_ord) return;  // device plan: the grid covers every sequence
+  q.s = n_ord > 0 ? (rank < n_ord ? plan_seq<DP>(ord, fc, rank) : a.num_seqs) : rank;
+  if (fused_n > 0) {
+    conv_phase_w<DP>(sm, a, ord, fc, rank);  // every rank < fused_n; waits come later
     // the workgroups of the shortest sequence, which finish long before the
     // others, write the new conv states: workgroup j those of ranks j, j + H_v, ...
-    if (rank == fc.n - 1)
-      for (int r = q.m; r < fc.n; r += Hv) commit_tail(sm, a, ord, fc, r);
+    if (rank == fused_n - 1)
+      for (int r = q.m; r < fused_n; r += Hv) commit_tail<DP>(sm, a, ord, fc, r);
     // value heads of one key head on one XCD (workgroups go round-robin over
     // the 8 XCDs), so the second reader of the shared Q and K rows can hit L2
     const int g = Hv / a.num_k_heads, per = Hv / 8;
@@ -1167,7 +1266,7 @@ __global__ __launch_bounds__(NT) void chunk_scan_kernel(ScanArgs a, SeqOrder ord
   }
   // the state does not depend on the conv: it was staged while the sequence's
   // last rows may still have been converting; now wait for those rows
-  if (fc.n > 0) conv_wait(fc, rank);
+  if (fused_n > 0) conv_wait<DP>(fc, rank);
   lds_barrier();
   if (wv < NS) {
     state_role(sm, sst, a, q, wv, ln);
@@ -1208,19 +1307,27 @@ __global__ __launch_bounds__(NT) void chunk_scan_kernel(ScanArgs a, SeqOrder ord
 
 bool chunk_supported(int dk, int dv) { return dk == D && dv == D; }
 
+hipError_t launch_plan(const PlanArgs& a, hipStream_t st) {
+  if (a.num_seqs < 1 || a.num_seqs > kMaxPlanSeqs || !a.plan || !a.sync) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(1024), 0, st, a);
+  return hipGetLastError();
+}
+
 hipError_t launch_chunk(const ScanArgs& a, const SeqOrder& order, const FusedConv& fc, int dk, int dv,
                         hipStream_t st) {
   if (!chunk_supported(dk, dv)) return hipErrorInvalidValue;
   if (fc.n > 0 && (fc.n != order.n || fc.n > kMaxFusedRanks || !fc.sync || a.width < 1 || a.width > 4))
     return hipErrorInvalidValue;
-  const int rows = order.n > 0 ? order.n : a.num_seqs;
-  if (fc.n > 0) {  // the task counters start at zero (a kernel, not a memset, so the call stays capturable)
+  if (fc.plan && (fc.plan_seqs != a.num_seqs || !fc.sync || a.width < 1 || a.width > 4)) return hipErrorInvalidValue;
+  const int rows = fc.plan ? a.num_seqs : order.n > 0 ? order.n : a.num_seqs;
+  if (fc.n > 0 && !fc.plan) {  // the task counters start at zero (a kernel, not a memset, so the call stays capturable)
     hipLaunchKernelGGL(zero_sync_kernel, dim3(1), dim3(256), 0, st, fc.sync, 1 + fc.n);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   dim3 grid(rows * a.num_v_heads);
-  hipLaunchKernelGGL(chunk_scan_kernel, grid, dim3(NT), 0, st, a, order, fc);
+  if (fc.plan) hipLaunchKernelGGL(chunk_scan_kernel<true>, grid, dim3(NT), 0, st, a, order, fc);
+  else hipLaunchKernelGGL(chunk_scan_kernel<false>, grid, dim3(NT), 0, st, a, order, fc);
   return hipGetLastError();
 }
 

@@ -105,6 +105,7 @@ struct Raw8 {
 template <bool BF16, int W, bool SILU>
 __global__ __launch_bounds__(256) void conv_silu_norm_kernel(ConvArgs a) {
   constexpr int ESZ = BF16 ? 2 : 4;
+  if (a.skip && *a.skip) return;  // device plan: the chunk kernel runs the conv (uniform)
   const int c0 = (blockIdx.y * blockDim.x + threadIdx.x) * 8;
   const bool cok = c0 < a.channels;
   const int r_begin = blockIdx.x * a.rows_per_block;
@@ -221,7 +222,7 @@ __global__ __launch_bounds__(256) void conv_tail_commit_kernel(TailArgs a) {
   if (!seq_active(a.read_idx, a.write_idx, s, a.num_blocks)) return;
   const int r0 = a.cu[s];
   const int L = a.cu[s + 1] - r0;
-  if (L > a.max_len) return;
+  if (L > ((a.fused && *a.fused) ? 1 : a.max_len)) return;
   const char* src_tail = a.conv_pool + (int64_t)a.read_idx[s] * a.conv_stride;
   char* dst_tail = a.conv_pool + (int64_t)a.write_idx[s] * a.conv_stride;
   const char* xb = reinterpret_cast<const char*>(a.x);

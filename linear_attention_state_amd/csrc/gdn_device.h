@@ -87,6 +87,7 @@ struct ConvArgs {
   void* y;
   int num_seqs, total_tokens, num_blocks, channels, qk_channels, head_k_dim, rows_per_block;
   float eps, q_scale;
+  const int32_t* skip;  // device plan: the whole launch does nothing when *skip != 0 (NULL: never)
 };
 
 struct TailArgs {
@@ -98,6 +99,7 @@ struct TailArgs {
   int64_t conv_stride;
   int num_seqs, num_blocks, channels;
   int max_len;  // sequences longer than this are committed elsewhere (the chunk kernel)
+  const int32_t* fused;  // device plan: when *fused != 0, max_len is 1 (NULL: use max_len)
 };
 
 struct ScanArgs {
@@ -164,8 +166,31 @@ struct FusedConv {
   int32_t* sync;     // [0] next task to claim, [1 + r] tasks of rank r finished; zero before the launch
   int32_t target, task, scan0, scan1;
   int32_t first[kMaxFusedRanks + 1];
+  // Device plan (launches planned on the device from cu_seqlens, see
+  // plan_kernel): when non-NULL, n, target, first[] and the launch order come
+  // from this array instead, laid out as below, for up to plan_seqs sequences.
+  const int32_t* plan;
+  int32_t plan_seqs;
 };
 constexpr size_t kFusedSyncBytes = 4096;  // room for sync[0 .. kMaxFusedRanks]
+
+// Device plan layout (int32): [0] chunked sequences n, [1] conv inside the chunk
+// kernel (0/1), [2] makespan target (ticks), [3] unused, [4, 4 + N) launch order
+// (sequence of each rank), [4 + N, 5 + 2N) first task of each rank and the total.
+constexpr int kPlanN = 0, kPlanFused = 1, kPlanTarget = 2, kPlanOrder = 4;
+constexpr int kMaxPlanSeqs = 1024;  // one 1024-thread workgroup plans
+inline size_t plan_ints(int num_seqs) { return 5 + 2 * (size_t)num_seqs; }
+
+struct PlanArgs {
+  const int32_t* cu;
+  int num_seqs, num_v_heads, slices, conv_rows;
+  int fused_allowed;  // every scan workgroup fits at once, the weights are aligned, no override against
+  int fused_forced;   // the override asks for it whenever allowed
+  double conv_us_per_token, task_us, scan0_us, scan1_us, margin;
+  int32_t* plan;
+  int32_t* sync;      // zeroed: 1 + num_seqs counters
+};
+hipError_t launch_plan(const PlanArgs& a, hipStream_t st);
 
 hipError_t launch_chunk(const ScanArgs& a, const SeqOrder& order, const FusedConv& fc, int dk, int dv,
                         hipStream_t st);

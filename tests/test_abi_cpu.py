@@ -90,7 +90,7 @@ def _call(layer, cu_host, T, n=None, **over):
     ([1, 4], 4, {}, gdn.GDN_EINVAL, "cu_seqlens[0]"),
     ([0, 5, 3], 3, {}, gdn.GDN_EINVAL, "decreases"),
     ([0, 5, 9], 8, {}, gdn.GDN_EINVAL, "total_tokens"),
-    ([0, 4], 4, {"cuh": None}, gdn.GDN_EINVAL, "cu_seqlens_host"),
+    ([0] * 1026, 0, {"cuh": None}, gdn.GDN_EUNSUPPORTED, "planning on the device"),
     ([0, 4], 4, {"ssm": None}, gdn.GDN_EINVAL, "ssm_pool"),
     ([0, 4], 4, {"conv": None}, gdn.GDN_EINVAL, "conv_pool"),
     ([0, 4], 4, {"P": 1}, gdn.GDN_EINVAL, "num_blocks"),

@@ -1,0 +1,36 @@
+"""Compile-time resource check of the chunk kernel (CPU, no GPU needed).
+
+The chunk kernel uses all the registers two waves per SIMD allow.  A spill to
+scratch inside its step loop waits on the vector-memory counter, which also
+counts the step's output stores, and has cost a fifth of the kernel's time, so
+every instantiation must compile without scratch.
+"""
+import os
+import re
+import subprocess
+
+import pytest
+
+import linear_attention_state_amd.build as build
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.mark.skipif(not os.path.exists(build.HIPCC), reason="hipcc not installed")
+def test_chunk_kernel_has_no_scratch(tmp_path):
+    src = os.path.join(ROOT, "linear_attention_state_amd", "csrc", "gdn_chunk.hip")
+    flags = [f for f in build.FLAGS if f not in ("-shared", "-fPIC")]
+    cmd = [build.HIPCC, *flags, "--offload-device-only", "-c", "-I", os.path.join(ROOT, "include"), src,
+           "-o", str(tmp_path / "chunk.o"), "-Rpass-analysis=kernel-resource-usage"]
+    res = subprocess.run(cmd, capture_output=True, text=True, timeout=600)
+    assert res.returncode == 0, res.stderr[-2000:]
+    kernel, seen = None, {}
+    for line in res.stderr.splitlines():
+        m = re.search(r"Function Name: (\S+)", line)
+        if m:
+            kernel = m.group(1)
+        m = re.search(r"ScratchSize \[bytes/lane\]: (\d+)", line)
+        if m and kernel and "chunk_scan_kernel" in kernel:
+            seen[kernel] = int(m.group(1))
+    assert len(seen) == 2, seen  # host-planned and device-planned instantiations
+    assert all(v == 0 for v in seen.values()), seen
