@@ -198,7 +198,8 @@ const char* gdn_last_error(void);
  * `count` receives the number of kernels with at least one timed launch.
  * The library creates the events it records and keeps them for reuse. */
 typedef struct {
-  char name[32];      /* kernel: "conv_silu_norm", "chunk_scan", "token_recurrent", "conv_state_commit", "state_copy" */
+  char name[32];      /* kernel: "conv_silu_norm", "chunk_scan", "token_recurrent", "conv_state_commit",
+                         "state_copy", "task_counter_reset", "device_plan" */
   double total_ms;    /* summed event-to-event time of its timed launches */
   int64_t launches;
 } gdn_kernel_time;

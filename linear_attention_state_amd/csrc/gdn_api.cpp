@@ -135,9 +135,9 @@ int device_cus(hipStream_t st) {
 bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
 
 // ---- optional per-kernel event timing (measurement only)
-enum { K_CONV = 0, K_CHUNK, K_TOKEN, K_TAIL, K_COPY, K_COUNT };
+enum { K_CONV = 0, K_CHUNK, K_TOKEN, K_TAIL, K_COPY, K_ZERO, K_PLAN, K_COUNT };
 const char* const kKernelNames[K_COUNT] = {"conv_silu_norm", "chunk_scan", "token_recurrent", "conv_state_commit",
-                                           "state_copy"};
+                                           "state_copy", "task_counter_reset", "device_plan"};
 
 struct Timing {
   std::mutex mu;
@@ -362,7 +362,7 @@ extern "C" int gdn_varlen_forward(const gdn_layer_desc* desc, const void* x, con
       pa.task_us = task_us(C, desc);
       pa.scan0_us = kScan0Us; pa.scan1_us = kScan1Us; pa.margin = kTargetMargin * 100.0;
       pa.plan = plan; pa.sync = sync;
-      e = gdn::launch_plan(pa, st);
+      e = timed(K_PLAN, st, [&] { return gdn::launch_plan(pa, st); });
       if (e != hipSuccess) return fail(GDN_EHIP, "plan launch: %s", hipGetErrorString(e));
       ca.skip = plan + gdn::kPlanFused;
       e = timed(K_CONV, st, [&] { return gdn::launch_conv(ca, W, bf16, true, st); });
@@ -460,6 +460,9 @@ extern "C" int gdn_varlen_forward(const gdn_layer_desc* desc, const void* x, con
     if (fc.n == 0) {
       e = timed(K_CONV, st, [&] { return gdn::launch_conv(ca, W, bf16, true, st); });
       if (e != hipSuccess) return fail(GDN_EHIP, "conv launch: %s", hipGetErrorString(e));
+    } else {
+      e = timed(K_ZERO, st, [&] { return gdn::launch_zero_sync(fc.sync, 1 + fc.n, st); });
+      if (e != hipSuccess) return fail(GDN_EHIP, "counter reset launch: %s", hipGetErrorString(e));
     }
     e = timed(K_CHUNK, st, [&] { return gdn::launch_chunk(sa, order, fc, desc->head_k_dim, desc->head_v_dim, st); });
     if (e != hipSuccess) return fail(GDN_EHIP, "chunk scan launch: %s", hipGetErrorString(e));

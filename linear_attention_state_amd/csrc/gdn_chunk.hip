@@ -1307,6 +1307,14 @@ __global__ __launch_bounds__(NT) void chunk_scan_kernel(ScanArgs a, SeqOrder ord
 
 bool chunk_supported(int dk, int dv) { return dk == D && dv == D; }
 
+// The task counters of a host-planned launch start at zero: a kernel, not a
+// memset, so the call stays capturable.
+hipError_t launch_zero_sync(int32_t* sync, int n, hipStream_t st) {
+  if (!sync || n < 1) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(zero_sync_kernel, dim3(1), dim3(256), 0, st, sync, n);
+  return hipGetLastError();
+}
+
 hipError_t launch_plan(const PlanArgs& a, hipStream_t st) {
   if (a.num_seqs < 1 || a.num_seqs > kMaxPlanSeqs || !a.plan || !a.sync) return hipErrorInvalidValue;
   hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(1024), 0, st, a);
@@ -1320,11 +1328,6 @@ hipError_t launch_chunk(const ScanArgs& a, const SeqOrder& order, const FusedCon
     return hipErrorInvalidValue;
   if (fc.plan && (fc.plan_seqs != a.num_seqs || !fc.sync || a.width < 1 || a.width > 4)) return hipErrorInvalidValue;
   const int rows = fc.plan ? a.num_seqs : order.n > 0 ? order.n : a.num_seqs;
-  if (fc.n > 0 && !fc.plan) {  // the task counters start at zero (a kernel, not a memset, so the call stays capturable)
-    hipLaunchKernelGGL(zero_sync_kernel, dim3(1), dim3(256), 0, st, fc.sync, 1 + fc.n);
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
   dim3 grid(rows * a.num_v_heads);
   if (fc.plan) hipLaunchKernelGGL(chunk_scan_kernel<true>, grid, dim3(NT), 0, st, a, order, fc);
   else hipLaunchKernelGGL(chunk_scan_kernel<false>, grid, dim3(NT), 0, st, a, order, fc);

@@ -191,6 +191,7 @@ struct PlanArgs {
   int32_t* sync;      // zeroed: 1 + num_seqs counters
 };
 hipError_t launch_plan(const PlanArgs& a, hipStream_t st);
+hipError_t launch_zero_sync(int32_t* sync, int n, hipStream_t st);  // n counters to zero
 
 hipError_t launch_chunk(const ScanArgs& a, const SeqOrder& order, const FusedConv& fc, int dk, int dv,
                         hipStream_t st);
