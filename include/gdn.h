@@ -131,10 +131,13 @@ int gdn_workspace_size(const gdn_layer_desc* desc, int32_t total_tokens,
  * all zero.  read_idx[i] == write_idx[i] is the ordinary in-place continue.
  * stream is a hipStream_t (NULL = the default stream).
  *
- * Launch plan: the conv of the chunked rows runs either in its own kernel or
- * inside the chunk kernel, chosen by a time model; the environment variable
- * GDN_CONV_IN_SCAN=always|never (read at every call) overrides the choice.
- * Every output and state is the same bit for bit either way.
+ * Launch plan: the conv of the chunked rows runs in its own kernel, inside the
+ * chunk kernel before the scans, or (host plan only, when the scans leave at
+ * least 32 CUs free) streamed by helper workgroups of a cooperative chunk
+ * kernel while the scans run; a time model chooses.  The environment variable
+ * GDN_CONV_IN_SCAN=never|always|stream (read at every call) overrides the
+ * choice ("stream" falls back to the others where it cannot run).  Every
+ * output and state is the same bit for bit in all three.
  */
 int gdn_varlen_forward(const gdn_layer_desc* desc, const void* x,
                        const void* conv_weight, const float* g, const float* beta,

@@ -84,7 +84,9 @@ WsLayout ws_layout(const gdn_layer_desc* d, int64_t total_tokens, int64_t num_se
   WsLayout l{0, 0, 0};
   if (total_tokens <= 0) return l;
   l.sync = round_up((size_t)total_tokens * (size_t)channels(d) * (size_t)act_size(d), 256);
-  const size_t sync_bytes = std::max(gdn::kFusedSyncBytes, 4 * (size_t)(1 + std::max<int64_t>(num_seqs, 0)));
+  // counters: phased conv 1 + N; streaming 1 + 2N + chunks (at most T/64 + N)
+  const size_t ns = (size_t)std::max<int64_t>(num_seqs, 0);
+  const size_t sync_bytes = std::max(gdn::kFusedSyncBytes, 4 * (2 + 3 * ns + (size_t)total_tokens / 64));
   l.plan = l.sync + round_up(sync_bytes, 256);
   l.total = l.plan + round_up(4 * gdn::plan_ints((int)std::min<int64_t>(std::max<int64_t>(num_seqs, 0), INT_MAX / 4)), 256);
   return l;
@@ -105,14 +107,16 @@ double task_us(int C, const gdn_layer_desc* d) {
   return 2.0 * gdn::kConvTaskRows * std::min(C, gdn::kConvTaskChannels) * act_size(d) / kTaskBytesPerUs;
 }
 
-// GDN_CONV_IN_SCAN: "always" runs the conv inside the chunk kernel whenever
-// its workgroups all fit on the device, "never" always runs the conv kernel,
-// anything else (or unset) lets the time model choose.  The result is the same
+// GDN_CONV_IN_SCAN: "always" runs the conv inside the chunk kernel (phased)
+// whenever its workgroups all fit on the device, "stream" streams it from
+// helper workgroups whenever at least 32 CUs are left for them, "never" always
+// runs the conv kernel, anything else (or unset) lets the time model choose.  The result is the same
 // bit for bit either way; the override exists for tests and tuning.
 int conv_in_scan_mode() {
   const char* v = getenv("GDN_CONV_IN_SCAN");
   if (!v) return 0;
-  if (!strcmp(v, "always")) return 1;
+  if (!strcmp(v, "always")) return 1;   // the phased conv inside the chunk kernel
+  if (!strcmp(v, "stream")) return 2;   // streaming, when there are spare CUs for helpers
   if (!strcmp(v, "never")) return -1;
   return 0;
 }
@@ -429,9 +433,12 @@ extern "C" int gdn_varlen_forward(const gdn_layer_desc* desc, const void* x, con
     fc.n = 0;
     fc.plan = nullptr;
     fc.plan_seqs = 0;
+    fc.stream = 0;
+    fc.helpers = 0;
     const int mode = conv_in_scan_mode();
+    const int cus = device_cus(st);
     if (mode >= 0 && order.n > 0 && order.n <= gdn::kMaxFusedRanks && aligned(conv_weight, 16) &&
-        (int64_t)order.n * desc->num_v_heads <= device_cus(st)) {
+        (int64_t)order.n * desc->num_v_heads <= cus) {
       fc.slices = (C + gdn::kConvTaskChannels - 1) / gdn::kConvTaskChannels;
       fc.first[0] = 0;
       const double scan0 = kScan0Us, scan1 = kScan1Us;
@@ -448,7 +455,16 @@ extern "C" int gdn_varlen_forward(const gdn_layer_desc* desc, const void* x, con
       const double fused = std::max((fc.first[order.n] * task_us + desc->num_v_heads * scans) /
                                     ((double)order.n * desc->num_v_heads), longest + 2.0 * task_us);
       const double apart = 2.0 * (double)total_tokens * C * act_size(desc) / kConvBytesPerUs + longest + 3.0;
-      if (mode > 0 || 1.05 * fused < apart) {
+      // streaming: spare CUs run helper workgroups that convert rows just
+      // ahead of the scans, which all start at once; it ends when both the
+      // longest scan and the helpers' share of the conv are done
+      const int helpers = cus - order.n * desc->num_v_heads;
+      const bool stream_ok = helpers >= 32 && mode != 1;
+      const double streamed = std::max(1.05 * longest, fc.first[order.n] * task_us / std::max(helpers, 1)) +
+                              2.0 * task_us;
+      const bool use_stream = stream_ok && (mode == 2 || (mode == 0 && streamed < std::min(1.05 * fused, apart)));
+      const bool use_phased = !use_stream && (mode == 1 || (mode == 0 && 1.05 * fused < apart));
+      if (use_stream || use_phased) {
         fc.n = order.n;
         fc.sync = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(workspace) + wl.sync);
         fc.target = (int32_t)(fused * kTargetMargin * 100.0);  // 100 ticks per microsecond
@@ -456,15 +472,35 @@ extern "C" int gdn_varlen_forward(const gdn_layer_desc* desc, const void* x, con
         fc.scan0 = (int32_t)(scan0 * 100.0);
         fc.scan1 = (int32_t)(scan1 * 100.0);
       }
+      if (use_stream) {  // first[r]: the first chunk counter of rank r
+        fc.stream = 1;
+        fc.helpers = helpers;
+        fc.first[0] = 0;
+        for (int r = 0; r < order.n; ++r) {
+          const int L = cu_seqlens_host[order.seq[r] + 1] - cu_seqlens_host[order.seq[r]];
+          fc.first[r + 1] = fc.first[r] + (L + 63) / 64;
+        }
+      }
     }
     if (fc.n == 0) {
       e = timed(K_CONV, st, [&] { return gdn::launch_conv(ca, W, bf16, true, st); });
       if (e != hipSuccess) return fail(GDN_EHIP, "conv launch: %s", hipGetErrorString(e));
     } else {
-      e = timed(K_ZERO, st, [&] { return gdn::launch_zero_sync(fc.sync, 1 + fc.n, st); });
+      const int counters = fc.stream ? 1 + 2 * fc.n + fc.first[fc.n] : 1 + fc.n;
+      e = timed(K_ZERO, st, [&] { return gdn::launch_zero_sync(fc.sync, counters, st); });
       if (e != hipSuccess) return fail(GDN_EHIP, "counter reset launch: %s", hipGetErrorString(e));
     }
     e = timed(K_CHUNK, st, [&] { return gdn::launch_chunk(sa, order, fc, desc->head_k_dim, desc->head_v_dim, st); });
+    if (e != hipSuccess && fc.stream) {
+      // the cooperative launch was refused (not every workgroup could be
+      // resident): the conv kernel first, then the plain scan
+      (void)hipGetLastError();
+      fc.n = 0;
+      fc.stream = 0;
+      e = timed(K_CONV, st, [&] { return gdn::launch_conv(ca, W, bf16, true, st); });
+      if (e != hipSuccess) return fail(GDN_EHIP, "conv launch: %s", hipGetErrorString(e));
+      e = timed(K_CHUNK, st, [&] { return gdn::launch_chunk(sa, order, fc, desc->head_k_dim, desc->head_v_dim, st); });
+    }
     if (e != hipSuccess) return fail(GDN_EHIP, "chunk scan launch: %s", hipGetErrorString(e));
     tails_done = fc.n > 0;
   }

@@ -103,7 +103,7 @@ struct alignas(16) Smem {
   float gw[BT];               // gamma, gram wave
   int dflag;                  // chunks whose Q / K / V rows are in LDS
   int aflag;                  // chunks whose diagonal blocks of A are in `at`
-  int task;                   // conv task claimed by thread 0, for the workgroup
+  int task, task2, task3, task4;  // conv tasks claimed for the workgroup
 };
 static_assert(sizeof(Smem) <= 160 * 1024, "LDS");
 static_assert(offsetof(Smem, task) >= 16 * 8 * 1024, "the conv row staging (16 rows x 8 KiB) stays clear of the task slot");
@@ -689,10 +689,31 @@ __device__ __forceinline__ void state_role(Smem& sm, float* sst, const ScanArgs&
 }
 
 // ---- wave 4: A for chunk i + 2, its diagonal blocks published first
-__device__ __forceinline__ void gram_role(Smem& sm, const ScanArgs& a, const Seq& q, int lane, const Lane& ln) {
+// Streaming: waits until every conv task of chunk c of `rank` is counted
+// (bounded: the tasks are run by helper workgroups that never wait, all
+// resident under the cooperative launch).  Chunk c's rows were never read
+// before in this kernel (scans read a chunk only after this wait, helpers never
+// read y), so no cache can hold a stale copy of them: no invalidation needed.
+// `publish`: this workgroup tells the helpers which chunk its rank needs.
+__device__ __forceinline__ void stream_wait(const FusedConv& fc, int rank, int n, int L, int c, bool publish) {
+  int32_t* need = fc.sync + 1 + n;
+  const int32_t* ready = fc.sync + 1 + 2 * n + fc.first[rank];
+  if (publish) __hip_atomic_store(&need[rank], c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const int want = min(BT / kConvTaskRows, (L - BT * c + kConvTaskRows - 1) / kConvTaskRows) * fc.slices;
+  for (int it = 0; it < (1 << 24); ++it) {
+    if (__hip_atomic_load(&ready[c], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= want) break;
+    __builtin_amdgcn_s_sleep(1);
+  }
+  asm volatile("" ::: "memory");
+}
+
+template <bool STREAM>
+__device__ __forceinline__ void gram_role(Smem& sm, const ScanArgs& a, const Seq& q, int lane, const Lane& ln,
+                                          const FusedConv& fc, int rank, int n, bool publish) {
   Blk gk[4];
   float g4, b4;
   auto load = [&](int c) {
+    if constexpr (STREAM) stream_wait(fc, rank, n, q.L, c, publish);
     const __amdgpu_buffer_rsrc_t ry = chunk_rows(a, q, c);
 #pragma unroll
     for (int b = 0; b < 4; ++b) gk[b] = ld_blk_g(ry, a.channels, q.koff, b, ln);
@@ -1206,19 +1227,177 @@ __global__ __launch_bounds__(1024) void plan_kernel(PlanArgs a) {
   }
 }
 
+// New conv state of sequence s (the last W-1 rows of [old state; x]) once no
+// conv task reads the old one any more; each thread reads its rows before it
+// writes them, so the in-place case is safe.
+__device__ void write_tail(const ScanArgs& a, int s) {
+  const int W = a.width;
+  if (W < 2 || !seq_active(a.read_idx, a.write_idx, s, a.num_blocks)) return;
+  const int r0 = a.cu[s], L = a.cu[s + 1] - r0, C = a.channels;
+  const gptr<const u32x4> x = as_global(reinterpret_cast<const u32x4*>(a.x));
+  const gptr<const u32x4> src = as_global(reinterpret_cast<const u32x4*>(a.conv_pool + (int64_t)a.read_idx[s] * a.conv_stride));
+  const gptr<u32x4> dst = as_global(reinterpret_cast<u32x4*>(const_cast<char*>(a.conv_pool) + (int64_t)a.write_idx[s] * a.conv_stride));
+  for (int cq = threadIdx.x; cq < C / 8; cq += NT) {
+    u32x4 v[3];
+#pragma unroll
+    for (int j = 0; j < 3; ++j) {
+      const int i = L + j;  // row of [old state; x]
+      if (j < W - 1) v[j] = i < W - 1 ? src[(int64_t)i * (C / 8) + cq] : x[(int64_t)(r0 + i - (W - 1)) * (C / 8) + cq];
+    }
+#pragma unroll
+    for (int j = 0; j < 3; ++j)
+      if (j < W - 1) dst[(int64_t)j * (C / 8) + cq] = v[j];
+  }
+}
+
+// Streaming helper workgroup: converts the rows the scans need next.  Thread
+// 0 picks the rank whose claimed rows lead the chunk its scan needs by the
+// least and claims that rank's next task (16 rows x 4096 channels, in row
+// order); the workgroup converts it and counts it in its chunk's counter.  As
+// in conv_phase, the next task is claimed one task ahead and its rows load
+// into LDS while the current one is computed.  Ends when every task is
+// claimed; never waits for anything.
+// Wave 0 picks and claims a streaming task: lane r reads rank r's claim count
+// and needed chunk (one round trip for all ranks), the wave takes the rank of
+// least lead, and lane 0 claims its next task.  Returns (rank, task) or (-1, 0)
+// once every task is claimed.  Called when no other vector memory operation of
+// the wave is outstanding, so its waits cover only its own loads.
+__device__ __forceinline__ int2 stream_claim(const ScanArgs& a, const SeqOrder& ord, const FusedConv& fc, int lane) {
+  const int n = fc.n;
+  int32_t* claims = fc.sync + 1;
+  const int32_t* need = fc.sync + 1 + n;
+  for (int tries = 0; tries < 4 * n + 4; ++tries) {
+    int best_key = INT_MAX;  // (lead << 8) | rank: the least lead, then the lower rank
+    for (int r0 = 0; r0 < n; r0 += 64) {
+      const int r = r0 + lane;
+      int key = INT_MAX;
+      if (r < n) {
+        const int s = ord.seq[r];
+        const int tasks = (a.cu[s + 1] - a.cu[s] + kConvTaskRows - 1) / kConvTaskRows * fc.slices;
+        const int cl = __hip_atomic_load(&claims[r], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const int nd = __hip_atomic_load(&need[r], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (cl < tasks) {
+          const int lead = min(max(cl / fc.slices / (BT / kConvTaskRows) - nd, -(1 << 20)), 1 << 20);
+          key = ((lead + (1 << 20)) << 8) | (r & 255);
+        }
+      }
+      for (int off = 32; off >= 1; off >>= 1) key = min(key, __shfl_xor(key, off));
+      best_key = min(best_key, key);
+    }
+    if (best_key == INT_MAX) return int2{-1, 0};  // every task is claimed
+    const int best = best_key & 255;
+    int t = 0;
+    if (lane == 0) t = __hip_atomic_fetch_add(&claims[best], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    t = __builtin_amdgcn_readfirstlane(t);
+    const int s = ord.seq[best];
+    if (t < (a.cu[s + 1] - a.cu[s] + kConvTaskRows - 1) / kConvTaskRows * fc.slices) return int2{best, t};
+  }
+  return int2{-1, 0};
+}
+
+__device__ __forceinline__ ConvTask stream_task(const ScanArgs& a, const SeqOrder& ord, const FusedConv& fc, int r, int t) {
+  ConvTask k;
+  k.rank = r;
+  k.s = ord.seq[r];
+  k.seq0 = a.cu[k.s];
+  k.r0 = k.seq0 + (t / fc.slices) * kConvTaskRows;
+  k.n = min(kConvTaskRows, a.cu[k.s + 1] - k.r0);
+  k.c0 = (t % fc.slices) * kConvTaskChannels + (int)threadIdx.x * 8;
+  k.on = k.c0 < a.channels;
+  return k;
+}
+
+template <int W>
+__device__ void stream_helper(Smem& sm, const ScanArgs& a, const SeqOrder& ord, const FusedConv& fc) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  int32_t* ready = fc.sync + 1 + 2 * fc.n;
+  const u32x4* st = conv_stage(sm);
+  // the first two tasks
+  if (wv == 0) {
+    const int2 c0 = stream_claim(a, ord, fc, lane);
+    const int2 c1 = c0.x >= 0 ? stream_claim(a, ord, fc, lane) : int2{-1, 0};
+    if (lane == 0) {
+      sm.task = c0.x;
+      sm.task2 = c0.y;
+      sm.task3 = c1.x;
+      sm.task4 = c1.y;
+    }
+  }
+  lds_barrier();
+  int r = sm.task, t = sm.task2, ur = sm.task3, ut = sm.task4;
+  lds_barrier();  // read before wave 0 writes them again
+  ConvTask k{};
+  ConvSide<W> cur, nxt;
+  if (r >= 0) {
+    k = stream_task(a, ord, fc, r, t);
+    conv_prefetch<W>(sm, a, k, nxt);
+  }
+  u32x4 rx[kConvTaskRows];
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  while (r >= 0) {
+    // wave 0 claims the task after the next one, with nothing else in flight
+    int2 v{-1, 0};
+    if (wv == 0 && ur >= 0) v = stream_claim(a, ord, fc, lane);
+    cur = nxt;
+    if (k.on) {
+#pragma unroll
+      for (int i = 0; i < kConvTaskRows; ++i) rx[i] = st[(i * kConvWaves + wv) * 64 + lane];
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // read before the next rows overwrite them
+    ConvTask kn{};
+    if (ur >= 0) {
+      kn = stream_task(a, ord, fc, ur, ut);
+      conv_prefetch<W>(sm, a, kn, nxt);
+    }
+    conv_compute<W>(a, k, cur, rx);
+    if (tid == 0) {
+      sm.task = v.x;
+      sm.task2 = v.y;
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this task's stores, the next task's rows
+    lds_barrier();
+    if (tid == 0)
+      __hip_atomic_fetch_add(&ready[fc.first[k.rank] + (t / fc.slices) / (BT / kConvTaskRows)], 1,
+                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    k = kn;
+    r = ur;
+    t = ut;
+    ur = sm.task;
+    ut = sm.task2;
+    lds_barrier();  // read before wave 0 writes them again
+  }
+}
+
+__device__ __forceinline__ void stream_helper_w(Smem& sm, const ScanArgs& a, const SeqOrder& ord, const FusedConv& fc) {
+  switch (a.width) {
+    case 1: stream_helper<1>(sm, a, ord, fc); break;
+    case 2: stream_helper<2>(sm, a, ord, fc); break;
+    case 3: stream_helper<3>(sm, a, ord, fc); break;
+    default: stream_helper<4>(sm, a, ord, fc); break;
+  }
+}
+
 __global__ void zero_sync_kernel(int32_t* p, int n) {
   for (int i = threadIdx.x; i < n; i += blockDim.x) p[i] = 0;
 }
 
-template <bool DP>
+template <bool DP, bool STREAM>
 __global__ __launch_bounds__(NT) void chunk_scan_kernel(ScanArgs a, SeqOrder ord, FusedConv fc) {
   __shared__ Smem sm;
   const int Hv = a.num_v_heads;
   const int rank = blockIdx.x / Hv;
+  if constexpr (STREAM) {
+    if (rank >= fc.n) {  // a helper
+      stream_helper_w(sm, a, ord, fc);
+      return;
+    }
+  }
   Seq q;
   q.m = blockIdx.x % Hv;
   const int n_ord = plan_n<DP>(ord, fc);
-  const int fused_n = plan_fused_n<DP>(fc);  // 0, or every rank of the launch order
+  const int fused_n = STREAM ? 0 : plan_fused_n<DP>(fc);  // 0, or every rank of the launch order (phased conv)
+  const bool lead_wg = (int)(blockIdx.x % Hv) == 0;
   if (DP && rank >= n_ord) return;  // device plan: the grid covers every sequence
   q.s = n_ord > 0 ? (rank < n_ord ? plan_seq<DP>(ord, fc, rank) : a.num_seqs) : rank;
   if (fused_n > 0) {
@@ -1227,6 +1406,8 @@ __global__ __launch_bounds__(NT) void chunk_scan_kernel(ScanArgs a, SeqOrder ord
     // others, write the new conv states: workgroup j those of ranks j, j + H_v, ...
     if (rank == fused_n - 1)
       for (int r = q.m; r < fused_n; r += Hv) commit_tail<DP>(sm, a, ord, fc, r);
+  }
+  if (fused_n > 0 || STREAM) {
     // value heads of one key head on one XCD (workgroups go round-robin over
     // the 8 XCDs), so the second reader of the shared Q and K rows can hit L2
     const int g = Hv / a.num_k_heads, per = Hv / 8;
@@ -1285,7 +1466,7 @@ __global__ __launch_bounds__(NT) void chunk_scan_kernel(ScanArgs a, SeqOrder ord
       sm.aflag = 0;
     }
     lds_barrier();
-    if (wv == NS) gram_role(sm, a, q, lane, ln);
+    if (wv == NS) gram_role<STREAM>(sm, a, q, lane, ln, fc, rank, n_ord, lead_wg);
     else if (wv == NS + 1) blocks_role(sm, q, ln);
     else if (wv == NS + 2) load_role(sm, a, q, lane);
     else p_role(sm, q, ln);
@@ -1300,6 +1481,11 @@ __global__ __launch_bounds__(NT) void chunk_scan_kernel(ScanArgs a, SeqOrder ord
       const int f = tid + NT * it, row = f >> 5, c4 = f & 31;
       __builtin_amdgcn_raw_buffer_store_b128(*reinterpret_cast<const u32x4*>(&sst[row * PS + 4 * c4]), rs, 16 * f, 0, 0);
     }
+  }
+  // streaming: this scan consumed every chunk, so every conv task of the
+  // sequence (the readers of its old conv state) is done
+  if constexpr (STREAM) {
+    if (lead_wg) write_tail(a, q.s);
   }
 }
 
@@ -1328,9 +1514,20 @@ hipError_t launch_chunk(const ScanArgs& a, const SeqOrder& order, const FusedCon
     return hipErrorInvalidValue;
   if (fc.plan && (fc.plan_seqs != a.num_seqs || !fc.sync || a.width < 1 || a.width > 4)) return hipErrorInvalidValue;
   const int rows = fc.plan ? a.num_seqs : order.n > 0 ? order.n : a.num_seqs;
+  if (fc.stream) {
+    // every workgroup must be resident at once: scans wait for helpers
+    if (fc.plan || fc.n != order.n || fc.n < 1 || fc.helpers < 1 || !fc.sync) return hipErrorInvalidValue;
+    const int blocks = fc.n * a.num_v_heads + fc.helpers;
+    ScanArgs aa = a;
+    SeqOrder oo = order;
+    FusedConv ff = fc;
+    void* args[] = {&aa, &oo, &ff};
+    return hipLaunchCooperativeKernel(reinterpret_cast<const void*>(chunk_scan_kernel<false, true>), dim3(blocks),
+                                      dim3(NT), args, 0, st);
+  }
   dim3 grid(rows * a.num_v_heads);
-  if (fc.plan) hipLaunchKernelGGL(chunk_scan_kernel<true>, grid, dim3(NT), 0, st, a, order, fc);
-  else hipLaunchKernelGGL(chunk_scan_kernel<false>, grid, dim3(NT), 0, st, a, order, fc);
+  if (fc.plan) hipLaunchKernelGGL((chunk_scan_kernel<true, false>), grid, dim3(NT), 0, st, a, order, fc);
+  else hipLaunchKernelGGL((chunk_scan_kernel<false, false>), grid, dim3(NT), 0, st, a, order, fc);
   return hipGetLastError();
 }
 

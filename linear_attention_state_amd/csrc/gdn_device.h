@@ -171,6 +171,14 @@ struct FusedConv {
   // from this array instead, laid out as below, for up to plan_seqs sequences.
   const int32_t* plan;
   int32_t plan_seqs;
+  // Streaming (host plan only): the n * H_v scan workgroups start at once and
+  // wait chunk by chunk, while `helpers` more workgroups convert rows just
+  // ahead of them.  first[r] is then the first chunk of rank r in the ready
+  // counters (first[n] = all chunks), and sync holds [0] unused, [1, 1 + n)
+  // tasks claimed per rank, [1 + n, 1 + 2n) the chunk each rank's scan needs
+  // next, [1 + 2n, 1 + 2n + first[n]) tasks finished per chunk.
+  int32_t stream;
+  int32_t helpers;
 };
 constexpr size_t kFusedSyncBytes = 4096;  // room for sync[0 .. kMaxFusedRanks]
 

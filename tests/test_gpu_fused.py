@@ -95,3 +95,42 @@ def test_narrow_layer_partial_channel_slice():
     layer = workloads.Layer(2, 4, 128, 128, 4, "bf16")
     b = workloads.random_batch(layer, [77, 3, 140], seed=49)
     _both_ways(b, "narrow")
+
+
+def _stream_vs_separate(batch, name):
+    print("case stream-%s: lengths %s" % (name, batch.lengths), flush=True)
+    (out_f, cp_f, sp_f), k_f = _run(batch, "stream")
+    (out_s, cp_s, sp_s), k_s = _run(batch, "never")
+    assert "conv_silu_norm" not in k_f and "chunk_scan" in k_f, k_f
+    assert "conv_silu_norm" in k_s, k_s
+    assert torch.equal(_bits(out_f), _bits(out_s))
+    assert torch.equal(_bits(cp_f), _bits(cp_s))
+    assert torch.equal(sp_f, sp_s)
+    errs = compare(batch, (out_f, cp_f, sp_f), run_oracle(batch))
+    print("stream-%s: out %.3e state %.3e" % (name, errs["out_rel_l2"], errs["state_rel_l2"]), flush=True)
+
+
+STREAM_CASES = {
+    "ragged": (workloads.BIG, [2, 3, 17, 63, 65, 130, 200], None),
+    "fresh": (workloads.BIG, [700, 5, 300], [1, 0, 1]),
+    "mixed": (workloads.BIG, [1, 300, 1, 70, 1], None),
+    "single": (workloads.BIG, [1000], None),
+    "W2": (workloads.Layer(16, 32, 128, 128, 2, "bf16"), [2, 31, 500], None),
+    "W3": (workloads.Layer(16, 32, 128, 128, 3, "bf16"), [150, 31, 2], None),
+    "narrow": (workloads.Layer(2, 4, 128, 128, 4, "bf16"), [77, 3, 640], None),
+}
+
+
+@pytest.mark.parametrize("name", sorted(STREAM_CASES))
+def test_streamed_conv_equals_separate(name):
+    """Streaming (helper workgroups convert rows while the scans wait chunk by
+    chunk) against the conv kernel: bitwise, and within the oracle bar."""
+    layer, lengths, fresh = STREAM_CASES[name]
+    b = workloads.random_batch(layer, lengths, seed=51 + len(name), fresh=fresh)
+    _stream_vs_separate(b, name)
+
+
+def test_streamed_padding_sequence():
+    b = workloads.random_batch(workloads.BIG, [64, 270, 9], seed=58)
+    b.write_idx[1] = -2
+    _stream_vs_separate(b, "padding")
