@@ -84,7 +84,7 @@ WsLayout ws_layout(const gdn_layer_desc* d, int64_t total_tokens, int64_t num_se
   WsLayout l{0, 0, 0};
   if (total_tokens <= 0) return l;
   l.sync = round_up((size_t)total_tokens * (size_t)channels(d) * (size_t)act_size(d), 256);
-  // counters: phased conv 1 + N; streaming 1 + 2N + chunks (at most T/64 + N)
+  // counters: phased conv 1 + N; streaming 1 + chunks (at most T/64 + N)
   const size_t ns = (size_t)std::max<int64_t>(num_seqs, 0);
   const size_t sync_bytes = std::max(gdn::kFusedSyncBytes, 4 * (2 + 3 * ns + (size_t)total_tokens / 64));
   l.plan = l.sync + round_up(sync_bytes, 256);
@@ -486,7 +486,7 @@ extern "C" int gdn_varlen_forward(const gdn_layer_desc* desc, const void* x, con
       e = timed(K_CONV, st, [&] { return gdn::launch_conv(ca, W, bf16, true, st); });
       if (e != hipSuccess) return fail(GDN_EHIP, "conv launch: %s", hipGetErrorString(e));
     } else {
-      const int counters = fc.stream ? 1 + 2 * fc.n + fc.first[fc.n] : 1 + fc.n;
+      const int counters = fc.stream ? 1 + fc.first[fc.n] : 1 + fc.n;
       e = timed(K_ZERO, st, [&] { return gdn::launch_zero_sync(fc.sync, counters, st); });
       if (e != hipSuccess) return fail(GDN_EHIP, "counter reset launch: %s", hipGetErrorString(e));
     }

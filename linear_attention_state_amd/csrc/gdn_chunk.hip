@@ -694,26 +694,35 @@ __device__ __forceinline__ void state_role(Smem& sm, float* sst, const ScanArgs&
 // resident under the cooperative launch).  Chunk c's rows were never read
 // before in this kernel (scans read a chunk only after this wait, helpers never
 // read y), so no cache can hold a stale copy of them: no invalidation needed.
-// `publish`: this workgroup tells the helpers which chunk its rank needs.
-__device__ __forceinline__ void stream_wait(const FusedConv& fc, int rank, int n, int L, int c, bool publish) {
-  int32_t* need = fc.sync + 1 + n;
-  const int32_t* ready = fc.sync + 1 + 2 * n + fc.first[rank];
-  if (publish) __hip_atomic_store(&need[rank], c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  const int want = min(BT / kConvTaskRows, (L - BT * c + kConvTaskRows - 1) / kConvTaskRows) * fc.slices;
+// Returns the first chunk from c on that is not known to be converted.
+__device__ __forceinline__ int stream_wait(const FusedConv& fc, int rank, int L, int c, int upto, int lane) {
+  const int32_t* ready = fc.sync + 1 + fc.first[rank];
+  if (c < upto) return upto;
+  // lane l looks at chunk c + l: one round trip finds how many chunks from c on
+  // are complete, and the scan polls again only after it has used them up
+  const int cc = c + lane;
+  const int want = min(BT / kConvTaskRows, (L - BT * cc + kConvTaskRows - 1) / kConvTaskRows) * fc.slices;
+  const bool mine = cc * BT < L;
   for (int it = 0; it < (1 << 24); ++it) {
-    if (__hip_atomic_load(&ready[c], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= want) break;
+    const bool ok = !mine || __hip_atomic_load(&ready[cc], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= want;
+    const uint64_t late = __ballot(!ok);
+    if (!(late & 1)) {
+      asm volatile("" ::: "memory");
+      return c + (late ? __builtin_ctzll(late) : 64);
+    }
     __builtin_amdgcn_s_sleep(1);
   }
-  asm volatile("" ::: "memory");
+  return c + 1;
 }
 
 template <bool STREAM>
 __device__ __forceinline__ void gram_role(Smem& sm, const ScanArgs& a, const Seq& q, int lane, const Lane& ln,
-                                          const FusedConv& fc, int rank, int n, bool publish) {
+                                          const FusedConv& fc, int rank) {
   Blk gk[4];
   float g4, b4;
+  int upto = 0;  // streaming: chunks below this one are known to be converted
   auto load = [&](int c) {
-    if constexpr (STREAM) stream_wait(fc, rank, n, q.L, c, publish);
+    if constexpr (STREAM) upto = stream_wait(fc, rank, q.L, c, upto, lane);
     const __amdgpu_buffer_rsrc_t ry = chunk_rows(a, q, c);
 #pragma unroll
     for (int b = 0; b < 4; ++b) gk[b] = ld_blk_g(ry, a.channels, q.koff, b, ln);
@@ -1250,49 +1259,43 @@ __device__ void write_tail(const ScanArgs& a, int s) {
   }
 }
 
-// Streaming helper workgroup: converts the rows the scans need next.  Thread
-// 0 picks the rank whose claimed rows lead the chunk its scan needs by the
-// least and claims that rank's next task (16 rows x 4096 channels, in row
-// order); the workgroup converts it and counts it in its chunk's counter.  As
-// in conv_phase, the next task is claimed one task ahead and its rows load
-// into LDS while the current one is computed.  Ends when every task is
-// claimed; never waits for anything.
-// Wave 0 picks and claims a streaming task: lane r reads rank r's claim count
-// and needed chunk (one round trip for all ranks), the wave takes the rank of
-// least lead, and lane 0 claims its next task.  Returns (rank, task) or (-1, 0)
-// once every task is claimed.  Called when no other vector memory operation of
-// the wave is outstanding, so its waits cover only its own loads.
+// Streaming helper workgroup: converts the rows the scans need next, in
+// chunk-major order (the tasks of every rank's chunk 0, then of every rank's
+// chunk 1, ...), the order in which the scans, which start together and step
+// at the same pace, consume them.  Each task (16 rows x 4096 channels) is
+// counted in its chunk's counter.  As in conv_phase, the next task is claimed
+// one task ahead and its rows load into LDS while the current one is
+// computed.  Ends when every task is claimed; never waits for anything.
+//
+// Claims the next task: one atomic on the global counter, decoded over the
+// ranks' chunk counts (ranks run longest first, so the ranks that still have
+// a chunk c are a prefix of the order).  Returns (rank, task within the rank)
+// or (-1, 0) once every task is claimed.  Tasks past a sequence's end in its
+// last chunk are skipped; each pass takes a larger index, so the loop ends.
+// Called by one wave with no other vector memory operation outstanding.
 __device__ __forceinline__ int2 stream_claim(const ScanArgs& a, const SeqOrder& ord, const FusedConv& fc, int lane) {
-  const int n = fc.n;
-  int32_t* claims = fc.sync + 1;
-  const int32_t* need = fc.sync + 1 + n;
-  for (int tries = 0; tries < 4 * n + 4; ++tries) {
-    int best_key = INT_MAX;  // (lead << 8) | rank: the least lead, then the lower rank
-    for (int r0 = 0; r0 < n; r0 += 64) {
-      const int r = r0 + lane;
-      int key = INT_MAX;
-      if (r < n) {
-        const int s = ord.seq[r];
-        const int tasks = (a.cu[s + 1] - a.cu[s] + kConvTaskRows - 1) / kConvTaskRows * fc.slices;
-        const int cl = __hip_atomic_load(&claims[r], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        const int nd = __hip_atomic_load(&need[r], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (cl < tasks) {
-          const int lead = min(max(cl / fc.slices / (BT / kConvTaskRows) - nd, -(1 << 20)), 1 << 20);
-          key = ((lead + (1 << 20)) << 8) | (r & 255);
-        }
+  const int U = BT / kConvTaskRows * fc.slices;  // tasks per chunk of one rank
+  for (;;) {
+    int g = 0;
+    if (lane == 0) g = __hip_atomic_fetch_add(fc.sync, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    g = __builtin_amdgcn_readfirstlane(g);
+    int c0 = 0, r = -1, t = 0;
+    for (int act = fc.n; act >= 1; --act) {  // chunks [c0, c1) are held by ranks 0 .. act-1
+      const int c1 = fc.first[act] - fc.first[act - 1];
+      const int span = (c1 - c0) * act * U;
+      if (g < span) {
+        const int c = c0 + g / (act * U), j = g % (act * U);
+        r = j / U;
+        t = c * U + j % U;
+        break;
       }
-      for (int off = 32; off >= 1; off >>= 1) key = min(key, __shfl_xor(key, off));
-      best_key = min(best_key, key);
+      g -= span;
+      c0 = c1;
     }
-    if (best_key == INT_MAX) return int2{-1, 0};  // every task is claimed
-    const int best = best_key & 255;
-    int t = 0;
-    if (lane == 0) t = __hip_atomic_fetch_add(&claims[best], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    t = __builtin_amdgcn_readfirstlane(t);
-    const int s = ord.seq[best];
-    if (t < (a.cu[s + 1] - a.cu[s] + kConvTaskRows - 1) / kConvTaskRows * fc.slices) return int2{best, t};
+    if (r < 0) return int2{-1, 0};  // every task is claimed
+    const int s = ord.seq[r];
+    if ((t / fc.slices) * kConvTaskRows < a.cu[s + 1] - a.cu[s]) return int2{r, t};
   }
-  return int2{-1, 0};
 }
 
 __device__ __forceinline__ ConvTask stream_task(const ScanArgs& a, const SeqOrder& ord, const FusedConv& fc, int r, int t) {
@@ -1311,7 +1314,7 @@ template <int W>
 __device__ void stream_helper(Smem& sm, const ScanArgs& a, const SeqOrder& ord, const FusedConv& fc) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-  int32_t* ready = fc.sync + 1 + 2 * fc.n;
+  int32_t* ready = fc.sync + 1;
   const u32x4* st = conv_stage(sm);
   // the first two tasks
   if (wv == 0) {
@@ -1466,7 +1469,7 @@ __global__ __launch_bounds__(NT) void chunk_scan_kernel(ScanArgs a, SeqOrder ord
       sm.aflag = 0;
     }
     lds_barrier();
-    if (wv == NS) gram_role<STREAM>(sm, a, q, lane, ln, fc, rank, n_ord, lead_wg);
+    if (wv == NS) gram_role<STREAM>(sm, a, q, lane, ln, fc, rank);
     else if (wv == NS + 1) blocks_role(sm, q, ln);
     else if (wv == NS + 2) load_role(sm, a, q, lane);
     else p_role(sm, q, ln);

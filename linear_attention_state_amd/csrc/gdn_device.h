@@ -174,9 +174,9 @@ struct FusedConv {
   // Streaming (host plan only): the n * H_v scan workgroups start at once and
   // wait chunk by chunk, while `helpers` more workgroups convert rows just
   // ahead of them.  first[r] is then the first chunk of rank r in the ready
-  // counters (first[n] = all chunks), and sync holds [0] unused, [1, 1 + n)
-  // tasks claimed per rank, [1 + n, 1 + 2n) the chunk each rank's scan needs
-  // next, [1 + 2n, 1 + 2n + first[n]) tasks finished per chunk.
+  // counters (first[n] = all chunks), and sync holds [0] the next task to
+  // claim (in chunk-major order over the ranks), [1, 1 + first[n]) tasks
+  // finished per chunk.
   int32_t stream;
   int32_t helpers;
 };
