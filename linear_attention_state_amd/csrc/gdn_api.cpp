@@ -103,6 +103,23 @@ size_t workspace_bytes_for(const gdn_layer_desc* d, int64_t total_tokens, int64_
 constexpr double kScan0Us = 11.0, kScan1Us = 2.8, kTaskBytesPerUs = 17e3, kConvBytesPerUs = 4.2e6;
 constexpr double kTargetMargin = 1.03;
 
+// Choice of the conv placement, fitted to a sweep over 1-8 equal sequences of
+// 1024-32768 tokens, one long sequence beside short ones, and the prefill mix:
+// - conv kernel first: a scan then takes kScanPlainUs per chunk while at most
+//   half the CUs scan, rising by up to kScanCrowdUs with every CU scanning;
+// - phased: the estimate above runs about 5% high on long sequences
+//   (kPhasedScale);
+// - streamed: kStreamStartUs of start-up and kStreamScanScale on the longest
+//   scan (it runs beside the helpers' traffic), unless the helpers are the
+//   bound: each converts a task's rows at about kHelperBytesPerUs.
+constexpr double kScanPlainUs = 2.55, kScanCrowdUs = 0.65, kPhasedScale = 0.95;
+constexpr double kStreamStartUs = 40.0, kStreamScanScale = 1.06, kHelperBytesPerUs = 18.7e3;
+
+double plain_scan1(int64_t wgs, int cus) {
+  const double half = std::max(cus, 2) / 2.0;
+  return kScanPlainUs + kScanCrowdUs * std::min(1.0, std::max(0.0, (wgs - half) / half));
+}
+
 double task_us(int C, const gdn_layer_desc* d) {
   return 2.0 * gdn::kConvTaskRows * std::min(C, gdn::kConvTaskChannels) * act_size(d) / kTaskBytesPerUs;
 }
@@ -365,6 +382,8 @@ extern "C" int gdn_varlen_forward(const gdn_layer_desc* desc, const void* x, con
       pa.conv_us_per_token = 2.0 * C * act_size(desc) / kConvBytesPerUs;
       pa.task_us = task_us(C, desc);
       pa.scan0_us = kScan0Us; pa.scan1_us = kScan1Us; pa.margin = kTargetMargin * 100.0;
+      pa.cus = device_cus(st); pa.plain_scan1_us = kScanPlainUs; pa.crowd_scan1_us = kScanCrowdUs;
+      pa.phased_scale = kPhasedScale;
       pa.plan = plan; pa.sync = sync;
       e = timed(K_PLAN, st, [&] { return gdn::launch_plan(pa, st); });
       if (e != hipSuccess) return fail(GDN_EHIP, "plan launch: %s", hipGetErrorString(e));
@@ -450,20 +469,25 @@ extern "C" int gdn_varlen_forward(const gdn_layer_desc* desc, const void* x, con
         scans += scan0 + scan1 * ((L + 63) / 64);
       }
       const int L0 = cu_seqlens_host[order.seq[0] + 1] - cu_seqlens_host[order.seq[0]];
-      const double longest = scan0 + scan1 * ((L0 + 63) / 64);
+      const int chunks0 = (L0 + 63) / 64;
+      const double longest = scan0 + scan1 * chunks0;
       // work spread evenly over the workgroups, but no earlier than the longest scan allows
       const double fused = std::max((fc.first[order.n] * task_us + desc->num_v_heads * scans) /
                                     ((double)order.n * desc->num_v_heads), longest + 2.0 * task_us);
-      const double apart = 2.0 * (double)total_tokens * C * act_size(desc) / kConvBytesPerUs + longest + 3.0;
+      const int64_t wgs = (int64_t)order.n * desc->num_v_heads;
+      const double apart = 2.0 * (double)total_tokens * C * act_size(desc) / kConvBytesPerUs + scan0 +
+                           plain_scan1(wgs, cus) * chunks0 + 3.0;
       // streaming: spare CUs run helper workgroups that convert rows just
       // ahead of the scans, which all start at once; it ends when both the
       // longest scan and the helpers' share of the conv are done
-      const int helpers = cus - order.n * desc->num_v_heads;
+      const int helpers = cus - (int)wgs;
       const bool stream_ok = helpers >= 32 && mode != 1;
-      const double streamed = std::max(1.05 * longest, fc.first[order.n] * task_us / std::max(helpers, 1)) +
-                              2.0 * task_us;
-      const bool use_stream = stream_ok && (mode == 2 || (mode == 0 && streamed < std::min(1.05 * fused, apart)));
-      const bool use_phased = !use_stream && (mode == 1 || (mode == 0 && 1.05 * fused < apart));
+      const double helper_task_us = task_us * kTaskBytesPerUs / kHelperBytesPerUs;
+      const double streamed = std::max(kStreamScanScale * (scan0 + kScanPlainUs * chunks0) + kStreamStartUs,
+                                       fc.first[order.n] * helper_task_us / std::max(helpers, 1) + 25.0);
+      const double phased = kPhasedScale * fused;
+      const bool use_stream = stream_ok && (mode == 2 || (mode == 0 && streamed < std::min(phased, apart)));
+      const bool use_phased = !use_stream && (mode == 1 || (mode == 0 && phased < apart));
       if (use_stream || use_phased) {
         fc.n = order.n;
         fc.sync = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(workspace) + wl.sync);

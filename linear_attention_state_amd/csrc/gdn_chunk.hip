@@ -1227,8 +1227,11 @@ __global__ __launch_bounds__(1024) void plan_kernel(PlanArgs a) {
     const double lng = a.scan0_us + a.scan1_us * ((longest + BT - 1) / BT);
     double fused = n > 0 ? (total * a.task_us + a.num_v_heads * scans) / ((double)n * a.num_v_heads) : 0.0;
     fused = fmax(fused, lng + 2.0 * a.task_us);
-    const double apart = a.conv_us_per_token * T + lng + 3.0;
-    const int use = a.fused_allowed && n > 0 && (a.fused_forced || 1.05 * fused < apart);
+    const double half = (a.cus > 2 ? a.cus : 2) / 2.0;
+    const double crowd = fmin(1.0, fmax(0.0, ((double)n * a.num_v_heads - half) / half));
+    const double apart = a.conv_us_per_token * T + a.scan0_us +
+                         (a.plain_scan1_us + a.crowd_scan1_us * crowd) * ((longest + BT - 1) / BT) + 3.0;
+    const int use = a.fused_allowed && n > 0 && (a.fused_forced || a.phased_scale * fused < apart);
     a.plan[kPlanN] = n;
     a.plan[kPlanFused] = use;
     a.plan[kPlanTarget] = (int32_t)(fused * a.margin);

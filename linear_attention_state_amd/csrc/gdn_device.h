@@ -195,6 +195,8 @@ struct PlanArgs {
   int fused_allowed;  // every scan workgroup fits at once, the weights are aligned, no override against
   int fused_forced;   // the override asks for it whenever allowed
   double conv_us_per_token, task_us, scan0_us, scan1_us, margin;
+  int cus;  // compute units: the per-chunk scan time after the conv kernel
+  double plain_scan1_us, crowd_scan1_us, phased_scale;  // grows with the share of them scanning
   int32_t* plan;
   int32_t* sync;      // zeroed: 1 + num_seqs counters
 };
