@@ -73,9 +73,9 @@ def token_path_bytes(layer, n_tokens: int) -> float:
     return n_tokens * per_tok + C * layer.conv_width * s
 
 
-def load_traffic(kernel: str):
+def load_traffic(kernel: str, workload: str):
     """HBM bytes per launch measured with rocprofv3 counters, if a summary for
-    this kernel's current source is committed under profiles/."""
+    this kernel's current source on this workload is committed under profiles/."""
     import hashlib
 
     path = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
@@ -90,12 +90,13 @@ def load_traffic(kernel: str):
     with open(path) as f:
         for line in f:
             parts = line.split()
-            if len(parts) >= 4 and not line.startswith("#") and parts[0] == kernel and parts[1] == sha:
+            if (len(parts) >= 5 and not line.startswith("#") and parts[0] == kernel and parts[1] == sha
+                    and parts[4] == workload):
                 return float(parts[2]) + float(parts[3])
     return None
 
 
-def run(cfg_id: int, steps: int, warmup: int):
+def run(cfg_id: int, steps: int, warmup: int, placements=()):
     import torch
 
     import linear_attention_state_amd as gdn
@@ -157,13 +158,29 @@ def run(cfg_id: int, steps: int, warmup: int):
     roof["step_frac"] = roof["achieved"] * dom_s / (ms * 1e-3) / roof["peak"]
     if dom == "chunk_scan" and "conv_silu_norm" not in kernels:
         roof["note"] = "chunk_scan also ran the conv of the rows (no separate conv kernel)"
-    traffic = load_traffic(dom)
+    traffic = load_traffic(dom, {1: "prefill", 2: "decode", 4: "long"}.get(cfg_id, ""))
     roof["traffic"] = traffic
     roof["kernel"] = dom
-    return {
+    res = {
         "batch": b, "ms_per_step": ms, "ms_per_step_with_kernel_events": ms_events, "wall_s": wall, "tokens": T,
         "value": T * steps / (ms * steps * 1e-3), "kernels": kernels, "roofline": roof,
     }
+    # the same steps with the conv placement forced (GDN_CONV_IN_SCAN), for comparison
+    if placements:
+        old = os.environ.get("GDN_CONV_IN_SCAN")
+        res["ms_per_step_forced"] = {}
+        try:
+            for mode in placements:
+                os.environ["GDN_CONV_IN_SCAN"] = mode
+                for _ in range(3):
+                    step()
+                res["ms_per_step_forced"][mode] = timed_steps()[0]
+        finally:
+            if old is None:
+                os.environ.pop("GDN_CONV_IN_SCAN", None)
+            else:
+                os.environ["GDN_CONV_IN_SCAN"] = old
+    return res
 
 
 def run_graph(steps: int, warmup: int):
@@ -256,7 +273,7 @@ def run_conv(steps: int, warmup: int):
     roof = {"bound": "hbm", "achieved": work / (conv_ms * 1e-3) / 1e9, "peak": PEAK_HBM / 1e9, "unit": "GB/s",
             "kernel": "conv_silu_norm"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = load_traffic("conv_silu_norm")
+    roof["traffic"] = load_traffic("conv_silu_norm", "conv")
     return {"workload": "standalone varlen conv + SiLU: the prefill rows (T=%d, C=%d, W=%d, bf16), "
                         "%d sequences from the trash block" % (T, C, W, n),
             "value": T / (ms * 1e-3), "unit": "tokens/s", "ms_per_step": ms, "roofline": roof,
@@ -337,7 +354,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-conv", action="store_true", help="skip the standalone conv layer and fork copy entries")
-    ap.add_argument("--only", choices=["prefill", "decode", "conv", "copy", "graph"], default=None,
+    ap.add_argument("--no-long", action="store_true", help="skip the long-prefill entry (4 x 32768 tokens)")
+    ap.add_argument("--only", choices=["prefill", "decode", "conv", "copy", "graph", "long"], default=None,
                     help="run one workload alone and print its numbers (profiling runs)")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="run only a device-to-device copy of this many bytes (calibrates HBM byte counters)")
@@ -366,7 +384,7 @@ def main():
         print(json.dumps(run_graph(args.steps, args.warmup)), flush=True)
         return
     if args.only:
-        r = run(1 if args.only == "prefill" else 2, args.steps, args.warmup)
+        r = run({"prefill": 1, "decode": 2, "long": 4}[args.only], args.steps, args.warmup)
         print(json.dumps({"workload": args.only, "value": r["value"], "ms_per_step": r["ms_per_step"],
                           "roofline": r["roofline"], "kernels": r["kernels"]}), flush=True)
         return
@@ -388,6 +406,17 @@ def main():
                           "value": dec["value"], "unit": "tokens/s", "ms_per_step": dec["ms_per_step"],
                           "roofline": dec["roofline"], "kernels": dec["kernels"]}
         del dec
+    if not args.no_long:
+        lp = run(4, args.steps, args.warmup, placements=("never", "always"))
+        lp_note = ("conv streamed by helper workgroups inside chunk_scan"
+                   if "conv_silu_norm" not in lp["kernels"] else "separate conv kernel")
+        line["long_prefill"] = {
+            "workload": "long prefill: 4 sequences of 32768 tokens, all continuing from their blocks; same layer",
+            "value": lp["value"], "unit": "tokens/s", "ms_per_step": lp["ms_per_step"], "placement": lp_note,
+            "ms_per_step_conv_kernel_first": lp["ms_per_step_forced"]["never"],
+            "ms_per_step_phased": lp["ms_per_step_forced"]["always"],
+            "roofline": lp["roofline"], "kernels": lp["kernels"]}
+        del lp
     if not args.no_conv:
         line["prefill_graph"] = run_graph(args.steps, args.warmup)
         line["conv"] = run_conv(args.steps, args.warmup)
