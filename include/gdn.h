@@ -188,12 +188,57 @@ int gdn_state_copy(const gdn_layer_desc* desc, void* conv_pool, int64_t conv_blo
                    float* ssm_pool, int64_t ssm_block_stride, int32_t num_blocks,
                    const int32_t* src, const int32_t* dst, int32_t n, void* stream);
 
+/* ---- Mamba2 scan with per-sequence states.
+ * The model-support tracker page (continuous batching for the remaining
+ * linear-attention and state-space hybrids) names a varlen scan with
+ * per-sequence states for the Mamba2 mixers as groundwork, beside the varlen
+ * conv (gdn_varlen_conv runs that conv: SiLU, no normalisation).  The pages
+ * give no formula; the recurrence is Mamba2's selective state space model with
+ * a scalar decay per head (Dao and Gu, "Transformers are SSMs", ICML 2024):
+ *   d_t = softplus(dt_t + dt_bias_m) (or dt_t + dt_bias_m), a_t = exp(d_t A_m),
+ *   h_t = a_t h_{t-1} + d_t x_t B_t^T (h [P][N] fp32), y_t = h_t C_t + D_m x_t.
+ * Sequence i starts from ssm_pool block read_idx[i] (block 0 is the all-zero
+ * trash block) and its final h overwrites block write_idx[i]; write_idx[i] < 0
+ * marks a padding sequence (nothing read or written); a sequence of length 0
+ * copies its state.  The same paging rules as gdn_varlen_forward apply. */
+typedef struct {
+  int32_t num_heads;    /* H */
+  int32_t head_dim;     /* P: this build runs 64 */
+  int32_t num_groups;   /* G, divides H; head m reads the B and C of group m / (H / G) */
+  int32_t state_dim;    /* N: this build runs 128 */
+  int32_t dt_softplus;  /* nonzero: d = softplus(dt + dt_bias) */
+} ssd_layer_desc;
+
+/*   x          bf16, row t of head m at x + t*x_row_stride + m*P (elements)
+ *   B, C       bf16, row t of group g at B + t*bc_row_stride + g*N (same for C);
+ *              x, B and C may be views into one conv output row [x | B | C]
+ *   x_row_stride, bc_row_stride  in elements, multiples of 8, at most 2^23
+ *   dt         [T][H] fp32; dt_bias [H] fp32 or NULL (0); A [H] fp32 (negative
+ *              for a decay); D [H] fp32 or NULL (no skip term)
+ *   cu_seqlens [num_seqs+1] int32, device; cu_seqlens_host: the same on the
+ *              host, or NULL (then not checked: non-decreasing from 0 to
+ *              total_tokens; sequences whose offsets leave [0, total_tokens]
+ *              are skipped)
+ *   read_idx, write_idx [num_seqs] int32, device
+ *   ssm_pool   num_blocks blocks of [H][P][N] fp32 at ssm_pool + i*ssm_block_stride
+ *              bytes (a multiple of 16, >= H*P*N*4)
+ *   y          [T][H][P] bf16 (rows of padding sequences are left as they are)
+ * All device pointers 16-byte aligned.  Returns GDN_EUNSUPPORTED for other
+ * head or state sizes.  One kernel, enqueued on `stream`; no allocation, no
+ * host sync.  Precision: bf16 operands into fp32 products, fp32 state. */
+int ssd_varlen_scan(const ssd_layer_desc* desc, const void* x, int64_t x_row_stride, const void* B,
+                    const void* C, int64_t bc_row_stride, const float* dt, const float* dt_bias,
+                    const float* A, const float* D, const int32_t* cu_seqlens,
+                    const int32_t* cu_seqlens_host, int32_t num_seqs, int32_t total_tokens,
+                    const int32_t* read_idx, const int32_t* write_idx, float* ssm_pool,
+                    int64_t ssm_block_stride, int32_t num_blocks, void* y, void* stream);
+
 /* Message of the last non-OK status returned on this thread ("" if none). */
 const char* gdn_last_error(void);
 
 /* Measurement support (not needed to run the layer).
- * gdn_kernel_timing(1) makes every later gdn_varlen_forward, gdn_varlen_conv
- * and gdn_state_copy in this process record a HIP event pair on the call's
+ * gdn_kernel_timing(1) makes every later gdn_varlen_forward, gdn_varlen_conv,
+ * gdn_state_copy and ssd_varlen_scan in this process record a HIP event pair on the call's
  * stream around each kernel it launches,
  * and clears the totals; gdn_kernel_timing(0) stops recording.
  * gdn_kernel_times() waits for the recorded events (a host sync), adds their
@@ -202,7 +247,7 @@ const char* gdn_last_error(void);
  * The library creates the events it records and keeps them for reuse. */
 typedef struct {
   char name[32];      /* kernel: "conv_silu_norm", "chunk_scan", "token_recurrent", "conv_state_commit",
-                         "state_copy", "task_counter_reset", "device_plan" */
+                         "state_copy", "task_counter_reset", "device_plan", "ssd_scan" */
   double total_ms;    /* summed event-to-event time of its timed launches */
   int64_t launches;
 } gdn_kernel_time;

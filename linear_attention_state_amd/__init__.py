@@ -17,7 +17,7 @@ LIB_PATH = os.path.join(HERE, "_lib", "libgdn.so")
 GDN_OK, GDN_EINVAL, GDN_EUNSUPPORTED, GDN_EWORKSPACE, GDN_EHIP = 0, -1, -2, -3, -4
 GDN_F32, GDN_BF16 = 0, 1
 EXPORTS = ("gdn_state_spec", "gdn_workspace_size", "gdn_varlen_forward", "gdn_varlen_conv", "gdn_state_copy",
-           "gdn_last_error",
+           "ssd_varlen_scan", "gdn_last_error",
            "gdn_kernel_timing", "gdn_kernel_times")
 
 _lib = None
@@ -54,6 +54,16 @@ class gdn_state_decl(ctypes.Structure):
     ]
 
 
+class ssd_layer_desc(ctypes.Structure):
+    _fields_ = [
+        ("num_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("num_groups", ctypes.c_int32),
+        ("state_dim", ctypes.c_int32),
+        ("dt_softplus", ctypes.c_int32),
+    ]
+
+
 class gdn_kernel_time(ctypes.Structure):
     _fields_ = [("name", ctypes.c_char * 32), ("total_ms", ctypes.c_double), ("launches", ctypes.c_int64)]
 
@@ -86,6 +96,10 @@ def load_library():
         lib.gdn_state_copy.restype = ctypes.c_int
         lib.gdn_state_copy.argtypes = [ctypes.POINTER(gdn_layer_desc), P, ctypes.c_int64, P, ctypes.c_int64,
                                        ctypes.c_int32, P, P, ctypes.c_int32, P]
+        lib.ssd_varlen_scan.restype = ctypes.c_int
+        lib.ssd_varlen_scan.argtypes = [
+            ctypes.POINTER(ssd_layer_desc), P, ctypes.c_int64, P, P, ctypes.c_int64, P, P, P, P, P, P,
+            ctypes.c_int32, ctypes.c_int32, P, P, P, ctypes.c_int64, ctypes.c_int32, P, P]
         lib.gdn_kernel_timing.restype = ctypes.c_int
         lib.gdn_kernel_timing.argtypes = [ctypes.c_int]
         lib.gdn_kernel_times.restype = ctypes.c_int
@@ -133,6 +147,13 @@ def _dev_ptr(t, name):
         raise ValueError("%s must be a device tensor" % name)
     if not t.is_contiguous():
         raise ValueError("%s must be contiguous" % name)
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _view_ptr(t, name):
+    """Device pointer of a strided view (rows at the tensor's own stride)."""
+    if not t.is_cuda:
+        raise ValueError("%s must be a device tensor" % name)
     return ctypes.c_void_p(t.data_ptr())
 
 
@@ -236,6 +257,45 @@ def gdn_state_copy(layer, conv_pool, ssm_pool, src, dst, stream=None):
         _dev_ptr(src, "src"), _dev_ptr(dst, "dst"), int(src.numel()), ctypes.c_void_p(stream)))
 
 
+def ssd_varlen_scan(layer, x, B, C, dt, A, cu_seqlens, cu_seqlens_host, read_idx, write_idx, ssm_pool, y,
+                    dt_bias=None, D=None, stream=None):
+    """Enqueues the Mamba2 scan of a packed batch (``layer``: num_heads,
+    head_dim, num_groups, state_dim, dt_softplus).  x: [T][>= H*P] bf16 rows
+    (a 2-D view, row stride x.stride(0)); B and C: [T][>= G*N] bf16 views with
+    one row stride; dt [T][H] fp32; A, D, dt_bias [H] fp32; ssm_pool
+    [P_blocks][H][head_dim][state_dim] fp32 (updated in place); y
+    [T][H][head_dim] bf16.  cu_seqlens_host may be None."""
+    import torch
+
+    for name, t in (("x", x), ("B", B), ("C", C)):
+        if t.dtype != torch.bfloat16 or t.dim() != 2 or t.stride(1) != 1:
+            raise ValueError("%s must be a 2-D bf16 view with unit column stride" % name)
+    if B.stride(0) != C.stride(0):
+        raise ValueError("B and C must share one row stride")
+    for name, t in (("dt", dt), ("A", A), ("ssm_pool", ssm_pool)) + tuple(
+            (n, t) for n, t in (("dt_bias", dt_bias), ("D", D)) if t is not None):
+        if t.dtype != torch.float32 or not t.is_contiguous():
+            raise ValueError("%s must be a contiguous float32 tensor" % name)
+    if y.dtype != torch.bfloat16 or not y.is_contiguous():
+        raise ValueError("y must be a contiguous bf16 tensor")
+    if stream is None:
+        stream = torch.cuda.current_stream(y.device).cuda_stream
+    T, n = int(dt.shape[0]), int(read_idx.numel())
+    host = None
+    if cu_seqlens_host is not None:
+        h = cu_seqlens_host.to(torch.int32).contiguous()
+        host = ctypes.cast(h.data_ptr(), ctypes.c_void_p)
+    desc = ssd_layer_desc(int(layer.num_heads), int(layer.head_dim), int(layer.num_groups), int(layer.state_dim),
+                          1 if layer.dt_softplus else 0)
+    opt = lambda t, nm: _dev_ptr(t, nm) if t is not None else None
+    _check(load_library().ssd_varlen_scan(
+        ctypes.byref(desc), _view_ptr(x, "x"), int(x.stride(0)), _view_ptr(B, "B"), _view_ptr(C, "C"), int(B.stride(0)),
+        _dev_ptr(dt, "dt"), opt(dt_bias, "dt_bias"), _dev_ptr(A, "A"), opt(D, "D"), _dev_ptr(cu_seqlens, "cu_seqlens"),
+        host, n, T, _dev_ptr(read_idx, "read_idx"), _dev_ptr(write_idx, "write_idx"), _dev_ptr(ssm_pool, "ssm_pool"),
+        ssm_pool.stride(0) * ssm_pool.element_size(), int(ssm_pool.shape[0]), _dev_ptr(y, "y"),
+        ctypes.c_void_p(stream)))
+
+
 def gdn_kernel_timing(enable: bool) -> None:
     """Turns per-kernel HIP event timing of later forward calls on or off."""
     _check(load_library().gdn_kernel_timing(1 if enable else 0))
@@ -243,7 +303,7 @@ def gdn_kernel_timing(enable: bool) -> None:
 
 def gdn_kernel_times() -> dict:
     """{kernel: (total_ms, launches)} of the timed launches so far (waits for them)."""
-    arr = (gdn_kernel_time * 8)()
+    arr = (gdn_kernel_time * 16)()
     n = ctypes.c_int32(0)
-    _check(load_library().gdn_kernel_times(arr, 8, ctypes.byref(n)))
-    return {arr[i].name.decode(): (arr[i].total_ms, arr[i].launches) for i in range(min(n.value, 8))}
+    _check(load_library().gdn_kernel_times(arr, 16, ctypes.byref(n)))
+    return {arr[i].name.decode(): (arr[i].total_ms, arr[i].launches) for i in range(min(n.value, 16))}

@@ -156,9 +156,9 @@ int device_cus(hipStream_t st) {
 bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
 
 // ---- optional per-kernel event timing (measurement only)
-enum { K_CONV = 0, K_CHUNK, K_TOKEN, K_TAIL, K_COPY, K_ZERO, K_PLAN, K_COUNT };
+enum { K_CONV = 0, K_CHUNK, K_TOKEN, K_TAIL, K_COPY, K_ZERO, K_PLAN, K_SSD, K_COUNT };
 const char* const kKernelNames[K_COUNT] = {"conv_silu_norm", "chunk_scan", "token_recurrent", "conv_state_commit",
-                                           "state_copy", "task_counter_reset", "device_plan"};
+                                           "state_copy", "task_counter_reset", "device_plan", "ssd_scan"};
 
 struct Timing {
   std::mutex mu;
@@ -637,5 +637,68 @@ extern "C" int gdn_state_copy(const gdn_layer_desc* desc, void* conv_pool, int64
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   const hipError_t e = timed(K_COPY, st, [&] { return gdn::launch_state_copy(ca, n, st); });
   if (e != hipSuccess) return fail(GDN_EHIP, "state copy launch: %s", hipGetErrorString(e));
+  return GDN_OK;
+}
+
+extern "C" int ssd_varlen_scan(const ssd_layer_desc* desc, const void* x, int64_t x_row_stride, const void* B,
+                               const void* C, int64_t bc_row_stride, const float* dt, const float* dt_bias,
+                               const float* A, const float* D, const int32_t* cu_seqlens,
+                               const int32_t* cu_seqlens_host, int32_t num_seqs, int32_t total_tokens,
+                               const int32_t* read_idx, const int32_t* write_idx, float* ssm_pool,
+                               int64_t ssm_block_stride, int32_t num_blocks, void* y, void* stream) {
+  if (!desc) return fail(GDN_EINVAL, "layer descriptor is NULL");
+  const int H = desc->num_heads, P = desc->head_dim, G = desc->num_groups, N = desc->state_dim;
+  if (H < 1 || G < 1 || P < 1 || N < 1) return fail(GDN_EINVAL, "H=%d, P=%d, G=%d, N=%d must be >= 1", H, P, G, N);
+  if (H % G) return fail(GDN_EINVAL, "H=%d is not a multiple of G=%d", H, G);
+  if (!gdn::ssd_supported(P, N))
+    return fail(GDN_EUNSUPPORTED, "head_dim=%d, state_dim=%d: this build runs head_dim 64 with state_dim 128", P, N);
+  if (num_seqs < 0 || total_tokens < 0) return fail(GDN_EINVAL, "num_seqs=%d, total_tokens=%d", num_seqs, total_tokens);
+  if (num_seqs == 0) return GDN_OK;
+  if (!cu_seqlens || !read_idx || !write_idx || !A || !ssm_pool) return fail(GDN_EINVAL, "a required pointer is NULL");
+  if (total_tokens > 0 && (!x || !B || !C || !dt || !y)) return fail(GDN_EINVAL, "x, B, C, dt or y is NULL");
+  if (num_blocks < 1) return fail(GDN_EINVAL, "num_blocks=%d", num_blocks);
+  const int64_t state_bytes = (int64_t)H * P * N * 4;
+  if (ssm_block_stride < state_bytes || ssm_block_stride % 16)
+    return fail(GDN_EINVAL, "ssm_block_stride=%lld must be a multiple of 16 and >= %lld", (long long)ssm_block_stride,
+                (long long)state_bytes);
+  if (x_row_stride < (int64_t)H * P || x_row_stride % 8 || bc_row_stride < (int64_t)G * N || bc_row_stride % 8)
+    return fail(GDN_EINVAL, "row strides (x %lld, B/C %lld) must be multiples of 8 and cover a row",
+                (long long)x_row_stride, (long long)bc_row_stride);
+  // the kernel's buffer offsets are 32-bit: 64 rows of either stride must fit
+  if (x_row_stride > (1LL << 23) || bc_row_stride > (1LL << 23))
+    return fail(GDN_EUNSUPPORTED, "row strides above 2^23 elements");
+  if (!aligned(x, 16) || !aligned(B, 16) || !aligned(C, 16) || !aligned(y, 16) || !aligned(ssm_pool, 16))
+    return fail(GDN_EINVAL, "x, B, C, y and ssm_pool must be 16-byte aligned");
+  if (cu_seqlens_host) {
+    if (cu_seqlens_host[0] != 0 || cu_seqlens_host[num_seqs] != total_tokens)
+      return fail(GDN_EINVAL, "cu_seqlens must run from 0 to total_tokens=%d", total_tokens);
+    for (int i = 0; i < num_seqs; ++i)
+      if (cu_seqlens_host[i + 1] < cu_seqlens_host[i]) return fail(GDN_EINVAL, "cu_seqlens decreases at %d", i);
+  }
+  gdn::SsdArgs a{};
+  a.x = reinterpret_cast<const uint16_t*>(x);
+  a.b = reinterpret_cast<const uint16_t*>(B);
+  a.c = reinterpret_cast<const uint16_t*>(C);
+  a.x_stride = x_row_stride;
+  a.bc_stride = bc_row_stride;
+  a.dt = dt;
+  a.dt_bias = dt_bias;
+  a.A = A;
+  a.D = D;
+  a.cu = cu_seqlens;
+  a.read_idx = read_idx;
+  a.write_idx = write_idx;
+  a.pool = ssm_pool;
+  a.pool_stride = ssm_block_stride / 4;
+  a.num_blocks = num_blocks;
+  a.num_seqs = num_seqs;
+  a.num_heads = H;
+  a.num_groups = G;
+  a.softplus = desc->dt_softplus != 0;
+  a.total_tokens = total_tokens;
+  a.y = reinterpret_cast<uint16_t*>(y);
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const hipError_t e = timed(K_SSD, st, [&] { return gdn::launch_ssd(a, st); });
+  if (e != hipSuccess) return fail(GDN_EHIP, "ssd scan launch: %s", hipGetErrorString(e));
   return GDN_OK;
 }

@@ -145,6 +145,31 @@ struct StateCopyArgs {
   int num_blocks;
 };
 hipError_t launch_state_copy(const StateCopyArgs& a, int n, hipStream_t st);
+
+// Mamba2 scan (ssd_scan.hip): x, B, C bf16 rows at the given strides (in
+// elements, multiples of 8, 16-byte aligned bases), dt [T][H] fp32, y
+// [T][H][P] bf16, states [H][P][N] fp32 per block.  One workgroup per
+// (sequence, head); P = 64 and N = 128 only (ssd_supported).
+struct SsdArgs {
+  const uint16_t* x;
+  const uint16_t* b;
+  const uint16_t* c;
+  int64_t x_stride, bc_stride;
+  const float* dt;
+  const float* dt_bias;  // may be null
+  const float* A;
+  const float* D;        // may be null
+  const int32_t* cu;
+  const int32_t* read_idx;
+  const int32_t* write_idx;
+  float* pool;
+  int64_t pool_stride;   // floats between blocks
+  int num_blocks, num_seqs, num_heads, num_groups, softplus;
+  int total_tokens;      // sequences whose offsets leave [0, total_tokens] are skipped
+  uint16_t* y;
+};
+bool ssd_supported(int head_dim, int state_dim);
+hipError_t launch_ssd(const SsdArgs& a, hipStream_t st);
 hipError_t launch_recurrent(const ScanArgs& a, int dk, int dv, bool bf16, hipStream_t st);
 // The conv of the chunked sequences run by the chunk-scan workgroups
 // themselves, as tasks they claim before their scans.  Task t belongs to

@@ -1,0 +1,261 @@
+// ssd_scan.hip -- packed-batch Mamba2 scan with per-sequence paged states, gfx950.
+//
+// The recurrence (Mamba2's selective SSM with A a scalar per head: Dao and
+// Gu, "Transformers are SSMs", ICML 2024), per sequence and head m:
+//   d_t = softplus(dt_t + dt_bias_m),  a_t = exp(d_t A_m)
+//   h_t = a_t h_{t-1} + d_t x_t B_t^T          h: [P][N] fp32
+//   y_t = h_t C_t + D_m x_t
+// run chunk by chunk in its dual (quadratic) form.  With gamma_t the running
+// sum of d A inside a chunk of 64 rows and Gamma = e^gamma:
+//   Y = diag(Gamma) C S + (L o C B^T) X + D X,  L_tj = e^{gamma_t - gamma_j} d_j (j <= t)
+//   S <- Gamma_last S + B^T diag(e^{gamma_last - gamma} d) X
+// where S = h^T ([N][P]) enters the chunk and X, B, C are its rows.  Unlike
+// the delta rule, nothing inside a chunk depends on S except the C S term.
+//
+// One 256-thread workgroup per (sequence, head), P = 64, N = 128.  Wave w owns
+// state columns [16w, 16w + 16) (8 accumulator tiles over N, fp32) and output
+// columns [16w, 16w + 16); rows 16w..16w+15 of the masked C B^T.  The chunk's
+// C, B and X rows are staged in LDS in their natural row-major order; the
+// transposed operands (B^T and X as the k side) are read with
+// ds_read_b64_tr_b16.  All products are v_mfma_f32_16x16x32_bf16.
+#include "gdn_device.h"
+
+namespace gdn {
+namespace {
+
+constexpr int SBT = 64;   // chunk rows
+constexpr int SN = 128;   // state size
+constexpr int SP = 64;    // head size
+constexpr int SNT = 256;  // threads
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+struct SsdSmem {
+  uint16_t c[SBT * SN];    // C rows [t][n]; 16-byte chunks XOR-swizzled by row
+  uint16_t b[SBT * SN];    // B rows [t][n]
+  uint16_t x[SBT * SP];    // X rows [t][p]
+  uint16_t p[SBT * SBT];   // L o C B^T [t][j], bf16
+  uint16_t y[SBT * SP];    // output rows [t][p], bf16
+  float gam[SBT];          // running sum of d A within the chunk
+  float dd[SBT];           // d_t (0 past the sequence end)
+  float wv[SBT];           // e^{gamma_last - gamma_j} d_j
+};
+static_assert(sizeof(SsdSmem) <= 80 * 1024, "two workgroups per CU");
+
+// Element offsets in the swizzled tiles: 256-byte rows (16 chunks) and 128-byte rows (8 chunks).
+__device__ __forceinline__ int sw256(int row, int col) { return row * 128 + ((((col >> 3) ^ (row & 15)) << 3) | (col & 7)); }
+__device__ __forceinline__ int sw128(int row, int col) { return row * 64 + ((((col >> 3) ^ (row & 7)) << 3) | (col & 7)); }
+
+__device__ __forceinline__ f32x4 mma(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ bf16x8 ld8(const uint16_t* p) { return *reinterpret_cast<const bf16x8*>(p); }
+__device__ __forceinline__ bf16x4 ld4(const uint16_t* p) { return *reinterpret_cast<const bf16x4*>(p); }
+__device__ __forceinline__ bf16x8 join(bf16x4 lo, bf16x4 hi) { return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7); }
+// ds_read_b64_tr_b16: within each 16-lane group, lane 16g + a + 4i reads 4
+// consecutive bf16 of row (base + i) at columns c0 + 4a..c0 + 4a + 3, and lane
+// 16g + n receives column c0 + n of rows base..base + 3.  Never under a partial exec mask.
+__device__ __forceinline__ bf16x4 ldtr(const uint16_t* p) {
+  return __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(const_cast<uint16_t*>(p))));
+}
+
+// k order of an operand: "natural" puts k = 8g + e at element e of lane group
+// g; "pair" puts k = 4g + e (e < 4) and 16 + 4g + e - 4 (e >= 4), the order in
+// which two accumulator tiles (rows 4g..4g+3 each) form one operand.  Both
+// operands of a product use the same order.
+
+__device__ __forceinline__ float softplus_f(float v) { return v > 20.f ? v : log1pf(__expf(v)); }
+
+__global__ __launch_bounds__(SNT, 2) void ssd_chunk_kernel(SsdArgs a) {
+  __shared__ SsdSmem sm;
+  const int H = a.num_heads;
+  const int s = blockIdx.x / H;
+  int m = blockIdx.x % H;
+  if (H % 8 == 0) m = (m % 8) * (H / 8) + m / 8;  // heads of a group on one XCD (workgroups go round-robin over 8)
+  if (s >= a.num_seqs || !seq_active(a.read_idx, a.write_idx, s, a.num_blocks)) return;
+  const int grp = m / (H / a.num_groups);
+  const int r0 = a.cu[s], L = a.cu[s + 1] - r0;
+  if (r0 < 0 || L < 0 || r0 + L > a.total_tokens) return;  // offsets outside the packed rows
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, i16 = lane & 15;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const float Am = a.A[m], Dm = a.D ? a.D[m] : 0.f, bias = a.dt_bias ? a.dt_bias[m] : 0.f;
+
+  // state: accumulator tile nb holds S[16nb + 4g + r][16w + i16] = h[p][n]
+  f32x4 S[8];
+  {
+    const gptr<const f32x4> src = as_global(reinterpret_cast<const f32x4*>(
+        a.pool + (int64_t)a.read_idx[s] * a.pool_stride + (int64_t)m * SP * SN + (16 * w + i16) * SN));
+#pragma unroll
+    for (int nb = 0; nb < 8; ++nb) S[nb] = src[4 * nb + g];
+  }
+  gptr<f32x4> dst = as_global(reinterpret_cast<f32x4*>(
+      a.pool + (int64_t)a.write_idx[s] * a.pool_stride + (int64_t)m * SP * SN + (16 * w + i16) * SN));
+
+  const int nch = (L + SBT - 1) / SBT;
+  // chunk loads: C and B tiles 4 x 16 bytes per thread (16 threads per row),
+  // X 2 x 16 bytes (8 threads per row), d A of row `lane` in wave 0
+  u32x4 rc[4], rb[4], rx[2];
+  float rdt = 0.f;
+  auto load = [&](int c) {
+    const int row0 = r0 + c * SBT, nv = min(SBT, L - c * SBT);
+    const __amdgpu_buffer_rsrc_t cs = make_rsrc(a.c + (int64_t)row0 * a.bc_stride + grp * SN,
+                                                (uint32_t)(((int64_t)(nv - 1) * a.bc_stride + SN) * 2));
+    const __amdgpu_buffer_rsrc_t bs = make_rsrc(a.b + (int64_t)row0 * a.bc_stride + grp * SN,
+                                                (uint32_t)(((int64_t)(nv - 1) * a.bc_stride + SN) * 2));
+    const __amdgpu_buffer_rsrc_t xs = make_rsrc(a.x + (int64_t)row0 * a.x_stride + m * SP,
+                                                (uint32_t)(((int64_t)(nv - 1) * a.x_stride + SP) * 2));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int q = tid + SNT * i, t = q >> 4, cc = q & 15;
+      const int off = t < nv ? (int)((t * a.bc_stride + 8 * cc) * 2) : -1;  // rows past the end read 0
+      rc[i] = __builtin_amdgcn_raw_buffer_load_b128(cs, (uint32_t)off, 0, 0);
+      rb[i] = __builtin_amdgcn_raw_buffer_load_b128(bs, (uint32_t)off, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int q = tid + SNT * i, t = q >> 3, cc = q & 7;
+      const int off = t < nv ? (int)((t * a.x_stride + 8 * cc) * 2) : -1;
+      rx[i] = __builtin_amdgcn_raw_buffer_load_b128(xs, (uint32_t)off, 0, 0);
+    }
+    if (w == 0) rdt = lane < nv ? a.dt[(int64_t)(row0 + lane) * H + m] : 0.f;
+  };
+  if (nch > 0) load(0);
+  for (int c = 0; c < nch; ++c) {
+    const int nv = min(SBT, L - c * SBT);
+    lds_barrier();  // the previous chunk's LDS reads are done
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int q = tid + SNT * i, t = q >> 4, cc = q & 15;
+      *reinterpret_cast<u32x4*>(&sm.c[sw256(t, 8 * cc)]) = rc[i];
+      *reinterpret_cast<u32x4*>(&sm.b[sw256(t, 8 * cc)]) = rb[i];
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int q = tid + SNT * i, t = q >> 3, cc = q & 7;
+      *reinterpret_cast<u32x4*>(&sm.x[sw128(t, 8 * cc)]) = rx[i];
+    }
+    if (w == 0) {
+      float d = 0.f;
+      if (lane < nv) d = a.softplus ? softplus_f(rdt + bias) : rdt + bias;
+      float v = d * Am;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const float u = __shfl_up(v, off);
+        if (lane >= off) v += u;
+      }
+      const float last = __shfl(v, 63);
+      sm.gam[lane] = v;
+      sm.dd[lane] = d;
+      sm.wv[lane] = __expf(last - v) * d;
+    }
+    if (c + 1 < nch) load(c + 1);  // the next chunk's rows stay in flight through this one
+    lds_barrier();
+
+    // rows 16w..16w+15 of L o C B^T (blocks right of the diagonal are zero)
+    {
+      const float gt[4] = {sm.gam[16 * w + 4 * g], sm.gam[16 * w + 4 * g + 1], sm.gam[16 * w + 4 * g + 2],
+                           sm.gam[16 * w + 4 * g + 3]};
+      for (int jb = 0; jb < 4; ++jb) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        if (jb <= w) {
+#pragma unroll
+          for (int kk = 0; kk < 4; ++kk)
+            acc = mma(ld8(&sm.c[sw256(16 * w + i16, 32 * kk + 8 * g)]), ld8(&sm.b[sw256(16 * jb + i16, 32 * kk + 8 * g)]), acc);
+        }
+        const int j = 16 * jb + i16;
+        const float gj = sm.gam[j], dj = sm.dd[j];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int t = 16 * w + 4 * g + r;
+          const float v = j <= t ? acc[r] * __expf(gt[r] - gj) * dj : 0.f;
+          sm.p[sw128(t, j)] = f32_to_bf16_bits(v);
+        }
+      }
+    }
+    // S as the k side of C S, pair order: tiles 2kk and 2kk + 1
+    bf16x8 sop[4];
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        sop[kk][e] = (__bf16)S[2 * kk][e];
+        sop[kk][4 + e] = (__bf16)S[2 * kk + 1][e];
+      }
+    // X as the k side (rows j, column 16w + i16), pair order
+    bf16x8 xop[2];
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      const int a4 = lane & 3, i4 = (lane >> 2) & 3;
+      xop[kk] = join(ldtr(&sm.x[sw128(32 * kk + 4 * g + i4, 16 * w + 4 * a4)]),
+                     ldtr(&sm.x[sw128(32 * kk + 16 + 4 * g + i4, 16 * w + 4 * a4)]));
+    }
+    lds_barrier();  // every row of L o C B^T is written
+
+    // Y[:, 16w..16w+15] = Gamma (C S) + (L o C B^T) X + D X
+    for (int tb = 0; tb < 4; ++tb) {
+      f32x4 ys = {0.f, 0.f, 0.f, 0.f}, yp = {0.f, 0.f, 0.f, 0.f};
+      const int tr = 16 * tb + i16;
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk)
+        ys = mma(join(ld4(&sm.c[sw256(tr, 32 * kk + 4 * g)]), ld4(&sm.c[sw256(tr, 32 * kk + 16 + 4 * g)])), sop[kk], ys);
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk)
+        if (kk <= tb / 2)
+          yp = mma(join(ld4(&sm.p[sw128(tr, 32 * kk + 4 * g)]), ld4(&sm.p[sw128(tr, 32 * kk + 16 + 4 * g)])), xop[kk], yp);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int t = 16 * tb + 4 * g + r, p = 16 * w + i16;
+        const float xv = bf16_bits_to_f32(sm.x[sw128(t, p)]);
+        sm.y[sw128(t, p)] = f32_to_bf16_bits(__expf(sm.gam[t]) * ys[r] + yp[r] + Dm * xv);
+      }
+    }
+    // S <- Gamma_last S + B^T diag(w) X
+    {
+      const float glast = __expf(sm.gam[SBT - 1]);
+      bf16x8 xw[2];
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int j = 32 * kk + (e < 4 ? 4 * g + e : 16 + 4 * g + e - 4);
+          xw[kk][e] = (__bf16)((float)xop[kk][e] * sm.wv[j]);
+        }
+      const int a4 = lane & 3, i4 = (lane >> 2) & 3;
+#pragma unroll
+      for (int nb = 0; nb < 8; ++nb) {
+        f32x4 acc = S[nb] * glast;
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+          acc = mma(join(ldtr(&sm.b[sw256(32 * kk + 4 * g + i4, 16 * nb + 4 * a4)]),
+                         ldtr(&sm.b[sw256(32 * kk + 16 + 4 * g + i4, 16 * nb + 4 * a4)])),
+                    xw[kk], acc);
+        S[nb] = acc;
+      }
+    }
+    lds_barrier();  // every output row is staged
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int q = tid + SNT * i, t = q >> 3, cc = q & 7;
+      if (t < nv)
+        *reinterpret_cast<gptr<u32x4>>(as_global(a.y + ((int64_t)(r0 + c * SBT + t) * H + m) * SP + 8 * cc)) =
+            *reinterpret_cast<const u32x4*>(&sm.y[sw128(t, 8 * cc)]);
+    }
+  }
+#pragma unroll
+  for (int nb = 0; nb < 8; ++nb) dst[4 * nb + g] = S[nb];
+}
+
+}  // namespace
+
+bool ssd_supported(int head_dim, int state_dim) { return head_dim == SP && state_dim == SN; }
+
+hipError_t launch_ssd(const SsdArgs& a, hipStream_t st) {
+  if (a.num_seqs <= 0 || a.num_heads <= 0) return hipSuccess;
+  const int64_t blocks = (int64_t)a.num_seqs * a.num_heads;
+  if (blocks > INT32_MAX) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(ssd_chunk_kernel, dim3((unsigned)blocks), dim3(SNT), 0, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace gdn

@@ -16,7 +16,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 def _declared():
     with open(os.path.join(ROOT, "include", "gdn.h")) as f:
         text = f.read()
-    return sorted(set(re.findall(r"\b(gdn_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b((?:gdn|ssd)_[a-z_]+)\s*\(", text)))
 
 
 def test_library_exports_every_declared_function():
@@ -166,4 +166,46 @@ def test_state_copy_rejects_bad_arguments(over, status, needle):
 
 def test_state_copy_of_nothing_is_ok():
     rc, _ = _copy_call(n=0, src=None, dst=None)
+    assert rc == gdn.GDN_OK
+
+
+def _ssd_call(cu_host, T, H=128, P=64, G=8, N=128, **over):
+    """ssd_varlen_scan with fake (never dereferenced) device pointers."""
+    lib = gdn.load_library()
+    fake = ctypes.c_void_p(1 << 20)
+    cu = (ctypes.c_int32 * len(cu_host))(*cu_host)
+    args = dict(x=fake, xs=H * P + 2 * G * N, b=fake, c=fake, bcs=H * P + 2 * G * N, dt=fake, bias=None, A=fake,
+                D=None, cu=fake, cuh=cu, n=len(cu_host) - 1, T=T, ri=fake, wi=fake, ssm=fake,
+                sstride=H * P * N * 4, nb=8, y=fake)
+    args.update(over)
+    desc = gdn.ssd_layer_desc(H, P, G, N, 1)
+    rc = lib.ssd_varlen_scan(ctypes.byref(desc), args["x"], args["xs"], args["b"], args["c"], args["bcs"], args["dt"],
+                             args["bias"], args["A"], args["D"], args["cu"], args["cuh"], args["n"], args["T"],
+                             args["ri"], args["wi"], args["ssm"], args["sstride"], args["nb"], args["y"], None)
+    return rc, gdn.gdn_last_error()
+
+
+@pytest.mark.parametrize("cu,T,kw,status,needle", [
+    ([0, 4], 4, {"H": 12, "G": 8}, gdn.GDN_EINVAL, "multiple of G"),
+    ([0, 4], 4, {"P": 128}, gdn.GDN_EUNSUPPORTED, "head_dim"),
+    ([0, 4], 4, {"N": 64}, gdn.GDN_EUNSUPPORTED, "state_dim"),
+    ([0, 5, 3], 3, {}, gdn.GDN_EINVAL, "decreases"),
+    ([0, 5, 9], 8, {}, gdn.GDN_EINVAL, "total_tokens"),
+    ([0, 4], 4, {"A": None}, gdn.GDN_EINVAL, "NULL"),
+    ([0, 4], 4, {"y": None}, gdn.GDN_EINVAL, "NULL"),
+    ([0, 4], 4, {"nb": 0}, gdn.GDN_EINVAL, "num_blocks"),
+    ([0, 4], 4, {"sstride": 128 * 64 * 128 * 4 - 16}, gdn.GDN_EINVAL, "ssm_block_stride"),
+    ([0, 4], 4, {"xs": 10244}, gdn.GDN_EINVAL, "row strides"),
+    ([0, 4], 4, {"bcs": 1016}, gdn.GDN_EINVAL, "row strides"),
+    ([0, 4], 4, {"xs": 1 << 24}, gdn.GDN_EUNSUPPORTED, "2^23"),
+    ([0, 4], 4, {"b": ctypes.c_void_p((1 << 20) + 8)}, gdn.GDN_EINVAL, "aligned"),
+])
+def test_ssd_scan_rejects_bad_arguments(cu, T, kw, status, needle):
+    shape = {k: kw.pop(k) for k in ("H", "P", "G", "N") if k in kw}
+    rc, msg = _ssd_call(cu, T, **shape, **kw)
+    assert rc == status and needle in msg, (rc, msg)
+
+
+def test_ssd_scan_of_no_sequences_is_ok():
+    rc, _ = _ssd_call([0], 0, cuh=None, cu=None, n=0)
     assert rc == gdn.GDN_OK

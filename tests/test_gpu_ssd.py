@@ -1,0 +1,158 @@
+"""GPU parity of the Mamba2 scan (ssd_varlen_scan) against the fp64 oracle
+(oracle/ssd_oracle.py), through the C ABI.
+
+Bar: y per sequence and head within relative L2 error 1e-2 (bf16 output of
+bf16-operand products with fp32 accumulation), final states within 1e-2;
+rows of padding sequences and blocks no sequence writes untouched (bitwise).
+At the full layer size the oracle runs on sampled heads, each given its
+group's B and C.  x, B and C are read as strided views of one conv-output row.
+"""
+import numpy as np
+import pytest
+import torch
+
+import linear_attention_state_amd as gdn
+import workloads
+from oracle import ssd_oracle
+
+pytestmark = pytest.mark.gpu
+
+TOL = 1e-2
+
+
+def _run_gpu(b, dt_bias=True, D=True, fill=7.0):
+    L = b.layer
+    dev = lambda t: t.cuda().contiguous()
+    xbc = dev(b.xbc)
+    x, B, C = b.views(xbc)
+    pool = dev(b.ssm_pool)
+    y = torch.full((b.total_tokens, L.num_heads, L.head_dim), fill, dtype=torch.bfloat16, device="cuda")
+    gdn.ssd_varlen_scan(L, x, B, C, dev(b.dt), dev(b.A), dev(b.cu_seqlens), b.cu_seqlens, dev(b.read_idx),
+                        dev(b.write_idx), pool, y, dt_bias=dev(b.dt_bias) if dt_bias else None,
+                        D=dev(b.D) if D else None)
+    torch.cuda.synchronize()
+    return y.cpu(), pool.cpu()
+
+
+def _oracle(b, heads, dt_bias=True, D=True):
+    """The oracle on the given heads only (each its own group of B and C)."""
+    L = b.layer
+    x, B, C = b.views(b.xbc)
+    T = b.total_tokens
+    x = x.double().numpy().reshape(T, L.num_heads, L.head_dim)[:, heads]
+    per = L.num_heads // L.num_groups
+    grp = [m // per for m in heads]
+    Bn = B.double().numpy().reshape(T, L.num_groups, L.state_dim)[:, grp]
+    Cn = C.double().numpy().reshape(T, L.num_groups, L.state_dim)[:, grp]
+    pool = b.ssm_pool.numpy()[:, heads]
+    return ssd_oracle.varlen_scan(
+        x, b.dt.numpy()[:, heads], b.A.numpy()[heads], Bn, Cn, b.D.numpy()[heads] if D else None,
+        b.dt_bias.numpy()[heads] if dt_bias else None, b.cu_seqlens.numpy(), b.read_idx.numpy(),
+        b.write_idx.numpy(), pool, dt_softplus=L.dt_softplus)
+
+
+def _rel(a, r):
+    return float(np.linalg.norm(a - r)) / max(float(np.linalg.norm(r)), 1e-30)
+
+
+def _check(name, b, heads=None, dt_bias=True, D=True):
+    L = b.layer
+    heads = list(range(L.num_heads)) if heads is None else heads
+    print("case %s: H=%d G=%d lengths %s, heads %s" % (name, L.num_heads, L.num_groups, b.lengths[:12], heads[:8]),
+          flush=True)
+    y, pool = _run_gpu(b, dt_bias, D)
+    ry, rpool = _oracle(b, heads, dt_bias, D)
+    worst_y = worst_s = 0.0
+    written = set()
+    for s in range(len(b.lengths)):
+        rows = slice(int(b.cu_seqlens[s]), int(b.cu_seqlens[s + 1]))
+        wb = int(b.write_idx[s])
+        if wb < 0:
+            assert bool((y[rows].float() == 7.0).all()), "padding rows written"
+            continue
+        written.add(wb)
+        for i, m in enumerate(heads):
+            if rows.stop > rows.start:
+                worst_y = max(worst_y, _rel(y[rows, m].double().numpy(), ry[rows, i]))
+            worst_s = max(worst_s, _rel(pool[wb, m].double().numpy(), rpool[wb, i]))
+    for blk in range(b.ssm_pool.shape[0]):
+        if blk not in written:
+            assert torch.equal(pool[blk], b.ssm_pool[blk]), "block %d written" % blk
+    print("%s: y %.3e state %.3e" % (name, worst_y, worst_s), flush=True)
+    assert worst_y <= TOL and worst_s <= TOL, (worst_y, worst_s)
+
+
+def test_ragged_lengths_around_chunk_edges():
+    b = workloads.ssd_batch(workloads.MAMBA2_SMALL, [1, 2, 63, 64, 65, 130, 200, 17], seed=11,
+                            fresh=[0, 1, 0, 1, 0, 0, 1, 0])
+    _check("ragged", b)
+
+
+def test_decode_tokens_beside_chunks():
+    b = workloads.ssd_batch(workloads.MAMBA2_SMALL, [1, 300, 1, 1, 64, 1], seed=12)
+    _check("mixed", b)
+
+
+def test_empty_and_padding_sequences():
+    b = workloads.ssd_batch(workloads.MAMBA2_SMALL, [40, 0, 9, 70], seed=13, num_blocks=8)
+    b.write_idx[2] = -1
+    b.read_idx[1] = 6  # the empty sequence carries block 6 over to its own write block
+    _check("empty+padding", b)
+
+
+def test_without_bias_skip_or_softplus():
+    import dataclasses
+    layer = dataclasses.replace(workloads.MAMBA2_SMALL, dt_softplus=False)
+    b = workloads.ssd_batch(layer, [33, 100, 1], seed=14)
+    b.dt = b.dt.abs() * 0.05  # dt used as is: keep it a small positive step
+    _check("no-softplus-bias-D", b, dt_bias=False, D=False)
+
+
+def test_one_group_for_all_heads():
+    layer = workloads.SsdLayer(8, 64, 1, 128, 4)
+    b = workloads.ssd_batch(layer, [90, 7, 129], seed=15)
+    _check("G1", b)
+
+
+def test_heads_not_a_multiple_of_eight():
+    layer = workloads.SsdLayer(6, 64, 3, 128, 4)
+    b = workloads.ssd_batch(layer, [66, 5], seed=16)
+    _check("H6", b)
+
+
+def test_prefill_workload_sampled_heads():
+    """8 sequences of 256-4096 tokens on the 128-head layer, oracle on 6 heads of 3 groups."""
+    b = workloads.ssd_config(0)
+    _check("prefill", b, heads=[0, 5, 17, 64, 100, 127])
+
+
+def test_decode_workload_sampled_heads():
+    b = workloads.ssd_config(1)
+    _check("decode", b, heads=[0, 1, 63, 64, 126, 127])
+
+
+def test_repeated_calls_continue_in_place():
+    """Two calls over halves of every sequence, the second reading the blocks
+    the first wrote, equal one call over the whole sequences (same kernel, so
+    only the chunk boundaries differ: within the bar, not bitwise)."""
+    b = workloads.ssd_batch(workloads.MAMBA2_SMALL, [100, 37, 64], seed=17)
+    full_y, full_pool = _run_gpu(b)
+    halves = [[l // 2 for l in b.lengths], [l - l // 2 for l in b.lengths]]
+    pool = b.ssm_pool.clone()
+    ys = []
+    for part, lens in enumerate(halves):
+        starts = b.cu_seqlens[:-1] + (0 if part == 0 else torch.tensor(halves[0], dtype=torch.int32))
+        rows = torch.cat([torch.arange(int(s), int(s) + l) for s, l in zip(starts, lens)])
+        sub = workloads.SsdBatch(layer=b.layer, lengths=lens, xbc=b.xbc[rows], dt=b.dt[rows], dt_bias=b.dt_bias,
+                                 A=b.A, D=b.D, cu_seqlens=torch.tensor(np.concatenate([[0], np.cumsum(lens)]),
+                                                                      dtype=torch.int32),
+                                 read_idx=b.read_idx if part == 0 else b.write_idx, write_idx=b.write_idx,
+                                 ssm_pool=pool)
+        y, pool = _run_gpu(sub)
+        ys.append((rows, y))
+    y2 = torch.zeros_like(full_y)
+    for rows, y in ys:
+        y2[rows] = y
+    assert _rel(y2.double().numpy(), full_y.double().numpy()) <= TOL
+    for wb in b.write_idx.tolist():
+        assert _rel(pool[wb].double().numpy(), full_pool[wb].double().numpy()) <= TOL

@@ -34,3 +34,21 @@ def test_chunk_kernel_has_no_scratch(tmp_path):
             seen[kernel] = int(m.group(1))
     assert len(seen) == 3, seen  # host-planned, device-planned and streaming instantiations
     assert all(v == 0 for v in seen.values()), seen
+
+
+@pytest.mark.skipif(not os.path.exists(build.HIPCC), reason="hipcc not installed")
+def test_mamba2_scan_kernel_fits_two_waves_per_simd(tmp_path):
+    """The Mamba2 scan kernel holds its state in registers: no scratch, and at
+    most 256 VGPRs so that two workgroups share a CU."""
+    src = os.path.join(ROOT, "linear_attention_state_amd", "csrc", "ssd_scan.hip")
+    flags = [f for f in build.FLAGS if f not in ("-shared", "-fPIC")]
+    cmd = [build.HIPCC, *flags, "--offload-device-only", "-c", "-I", os.path.join(ROOT, "include"), src,
+           "-o", str(tmp_path / "ssd.o"), "-Rpass-analysis=kernel-resource-usage"]
+    res = subprocess.run(cmd, capture_output=True, text=True, timeout=600)
+    assert res.returncode == 0, res.stderr[-2000:]
+    text = res.stderr
+    assert "ssd_chunk_kernel" in text
+    scratch = [int(v) for v in re.findall(r"ScratchSize \[bytes/lane\]: (\d+)", text)]
+    occ = [int(v) for v in re.findall(r"Occupancy \[waves/SIMD\]: (\d+)", text)]
+    assert scratch and all(v == 0 for v in scratch), scratch
+    assert occ and min(occ) >= 2, occ

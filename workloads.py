@@ -189,3 +189,106 @@ def random_batch(layer: Layer, lengths, seed: int, num_blocks: int | None = None
     reads = [0 if f else b for f, b in zip(fresh, blocks)]
     priors = [b for f, b in zip(fresh, blocks) if not f]
     return make_batch(layer, lengths, reads, blocks, P, priors, rng, "random")
+
+
+# ---------------------------------------------------------------- Mamba2 scan
+#
+# Inputs of the Mamba2 scan (ssd_varlen_scan) in the same packed-batch,
+# paged-state setting.  The pages give no Mamba2 shapes or distributions; the
+# layer below has the mixer shape of an 8B-class Mamba2 hybrid (128 heads of
+# 64, 8 groups of B and C, state 128, conv width 4), and the draws follow the
+# Mamba2 initialisation: dt_bias = softplus^-1(d0) with d0 log-uniform in
+# [0.001, 0.1], A = -U[1, 16], D = 1 + N(0, 0.1^2).  The conv output rows
+# x | B | C ~ N(0, 1) in bf16 (one row of conv_channels, so the scan reads
+# x, B and C as strided views), dt ~ N(0, 0.5^2), prior states ~ N(0, 0.5^2),
+# filler blocks N(0, 1), block 0 zero.
+# Draw order: lengths / blocks (by the caller), xbc, dt, dt_bias, A, D, prior
+# states, filler.
+
+@dataclasses.dataclass(frozen=True)
+class SsdLayer:
+    num_heads: int
+    head_dim: int
+    num_groups: int
+    state_dim: int
+    conv_width: int = 4
+    dt_softplus: bool = True
+
+    @property
+    def conv_channels(self) -> int:
+        return self.num_heads * self.head_dim + 2 * self.num_groups * self.state_dim
+
+
+MAMBA2 = SsdLayer(128, 64, 8, 128, 4)
+MAMBA2_SMALL = SsdLayer(8, 64, 2, 128, 4)
+
+
+@dataclasses.dataclass
+class SsdBatch:
+    layer: SsdLayer
+    lengths: list
+    xbc: torch.Tensor        # [T][conv_channels] bf16: x | B | C
+    dt: torch.Tensor         # [T][H] fp32
+    dt_bias: torch.Tensor    # [H] fp32
+    A: torch.Tensor          # [H] fp32
+    D: torch.Tensor          # [H] fp32
+    cu_seqlens: torch.Tensor
+    read_idx: torch.Tensor
+    write_idx: torch.Tensor
+    ssm_pool: torch.Tensor   # [P][H][head_dim][state_dim] fp32
+
+    @property
+    def total_tokens(self) -> int:
+        return int(self.cu_seqlens[-1])
+
+    def views(self, xbc):
+        """x [T][H*P], B [T][G*N], C [T][G*N]: column slices of the xbc rows."""
+        L = self.layer
+        hp, gn = L.num_heads * L.head_dim, L.num_groups * L.state_dim
+        return xbc[:, :hp], xbc[:, hp:hp + gn], xbc[:, hp + gn:hp + 2 * gn]
+
+
+def ssd_batch(layer: SsdLayer, lengths, seed: int, fresh=None, num_blocks: int | None = None) -> SsdBatch:
+    """A batch of the given lengths; sequence i continues from its own block
+    unless ``fresh[i]``, in which case it reads the trash block."""
+    rng = np.random.default_rng(seed)
+    n = len(lengths)
+    P = num_blocks if num_blocks is not None else n + 2
+    blocks = rng.choice(np.arange(1, P), size=n, replace=False).tolist()
+    fresh = fresh if fresh is not None else [False] * n
+    reads = [0 if f else b for f, b in zip(fresh, blocks)]
+    lengths = [int(v) for v in lengths]
+    T = sum(lengths)
+    H, Pd, N = layer.num_heads, layer.head_dim, layer.state_dim
+    xbc = torch.from_numpy(_normal(rng, (T, layer.conv_channels))).to(torch.bfloat16)
+    dt = _normal(rng, (T, H), std=0.5)
+    d0 = np.exp(rng.uniform(math.log(1e-3), math.log(1e-1), size=H))
+    dt_bias = d0 + np.log(-np.expm1(-d0))  # softplus^-1(d0)
+    A = -rng.uniform(1.0, 16.0, size=H)
+    D = 1.0 + _normal(rng, (H,), std=0.1)
+    pool = np.zeros((P, H, Pd, N), dtype=np.float32)
+    priors = [b for f, b in zip(fresh, blocks) if not f]
+    for b in priors:
+        pool[b] = _normal(rng, (H, Pd, N), std=0.5)
+    for b in range(1, P):
+        if b not in set(priors):
+            pool[b] = _normal(rng, (H, Pd, N))
+    cu = np.zeros(n + 1, dtype=np.int32)
+    cu[1:] = np.cumsum(lengths)
+    f32 = lambda a: torch.from_numpy(np.asarray(a, dtype=np.float32))
+    return SsdBatch(layer=layer, lengths=lengths, xbc=xbc, dt=f32(dt), dt_bias=f32(dt_bias), A=f32(A), D=f32(D),
+                    cu_seqlens=torch.from_numpy(cu), read_idx=torch.tensor(reads, dtype=torch.int32),
+                    write_idx=torch.tensor(blocks, dtype=torch.int32), ssm_pool=torch.from_numpy(pool))
+
+
+def ssd_config(i: int, seed: int | None = None) -> SsdBatch:
+    """Mamba2 workloads on MAMBA2: 0 prefill, 8 sequences of lengths uniform
+    in [256, 4096], all from the trash block; 1 decode, 256 one-token
+    sequences continuing from 256 of 512 blocks."""
+    rng = np.random.default_rng(2000 + i if seed is None else seed)
+    if i == 0:
+        lengths = rng.integers(256, 4096, size=8, endpoint=True).tolist()
+        return ssd_batch(MAMBA2, lengths, int(rng.integers(1 << 30)), fresh=[True] * 8, num_blocks=16)
+    if i == 1:
+        return ssd_batch(MAMBA2, [1] * 256, int(rng.integers(1 << 30)), num_blocks=512)
+    raise ValueError("no Mamba2 workload %d" % i)
