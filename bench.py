@@ -82,7 +82,7 @@ def load_traffic(kernel: str, workload: str):
     if not os.path.exists(path):
         return None
     src = {"chunk_scan": "gdn_chunk.hip", "token_recurrent": "gdn_recurrent.hip",
-           "conv_silu_norm": "gdn_conv.hip"}.get(kernel)
+           "conv_silu_norm": "gdn_conv.hip", "ssd_scan": "ssd_scan.hip"}.get(kernel)
     if src is None:
         return None
     with open(os.path.join(ROOT, "linear_attention_state_amd", "csrc", src), "rb") as f:
@@ -280,6 +280,82 @@ def run_conv(steps: int, warmup: int):
             "kernels": {k: {"avg_ms": v[0] / max(v[1], 1), "launches": v[1]} for k, v in kt.items()}}
 
 
+def ssd_bytes(layer, lengths) -> float:
+    """Algorithmic HBM bytes of one Mamba2 scan launch: per token the head
+    inputs x (H*P bf16), B and C (2*G*N bf16), dt (H fp32) and the output y
+    (H*P bf16); per sequence its state (H*P*N fp32) read and written."""
+    H, P, G, N = layer.num_heads, layer.head_dim, layer.num_groups, layer.state_dim
+    T = sum(lengths)
+    return T * (H * P * 2 + 2 * G * N * 2 + H * 4 + H * P * 2) + len(lengths) * H * P * N * 4 * 2
+
+
+def ssd_flops(layer, lengths, chunk: int = 64) -> float:
+    """Flops of the dense products the chunked dual form defines: per chunk of
+    c rows and head, C B^T on and below the diagonal (c(c+1)N), its product
+    with X (c(c+1)P), C S and B^T X (2cNP each)."""
+    H, P, N = layer.num_heads, layer.head_dim, layer.state_dim
+    total = 0.0
+    for L in lengths:
+        for c0 in range(0, L, chunk):
+            cc = min(chunk, L - c0)
+            total += H * (cc * (cc + 1) * (N + P) + 4 * cc * N * P)
+    return total
+
+
+def run_ssd(cfg: int, steps: int, warmup: int):
+    """The Mamba2 scan (ssd_varlen_scan) on a Mamba2 workload: 0 prefill, 1 decode."""
+    import torch
+
+    import linear_attention_state_amd as gdn
+    import workloads
+
+    b = workloads.ssd_config(cfg)
+    L = b.layer
+    dev = torch.device("cuda", 0)
+    xbc = b.xbc.to(dev).contiguous()
+    x, B, C = b.views(xbc)
+    t = {k: getattr(b, k).to(dev).contiguous() for k in ("dt", "A", "D", "dt_bias", "cu_seqlens", "read_idx",
+                                                          "write_idx", "ssm_pool")}
+    y = torch.empty(b.total_tokens, L.num_heads, L.head_dim, dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    cu_host = b.cu_seqlens.clone()
+
+    def step():
+        gdn.ssd_varlen_scan(L, x, B, C, t["dt"], t["A"], t["cu_seqlens"], cu_host, t["read_idx"], t["write_idx"],
+                            t["ssm_pool"], y, dt_bias=t["dt_bias"], D=t["D"], stream=stream.cuda_stream)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for _ in range(steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / steps
+    gdn.gdn_kernel_timing(True)
+    for _ in range(steps):
+        step()
+    kt = gdn.gdn_kernel_times()
+    gdn.gdn_kernel_timing(False)
+    k_ms = kt["ssd_scan"][0] / kt["ssd_scan"][1]
+    byt, fl = ssd_bytes(L, b.lengths), ssd_flops(L, b.lengths)
+    # arithmetic intensity below the machine balance (2.5e15 / 8e12 = 312 flop/B): priced against HBM
+    roof = {"bound": "hbm", "achieved": byt / (k_ms * 1e-3) / 1e9, "peak": PEAK_HBM / 1e9, "unit": "GB/s",
+            "kernel": "ssd_scan", "mfma_tflops": fl / (k_ms * 1e-3) / 1e12,
+            "flop_per_byte": fl / byt}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = load_traffic("ssd_scan", "mamba2_prefill" if cfg == 0 else "mamba2_decode")
+    n = len(b.lengths)
+    what = ("prefill: %d sequences, lengths %s, T=%d, from the trash block" % (n, b.lengths, b.total_tokens)
+            if cfg == 0 else "decode: %d sequences of 1 token, %d-block pool" % (n, b.ssm_pool.shape[0]))
+    return {"workload": "Mamba2 scan, H=%d heads of %d, G=%d, N=%d; %s" % (L.num_heads, L.head_dim, L.num_groups,
+                                                                           L.state_dim, what),
+            "value": b.total_tokens / (ms * 1e-3), "unit": "tokens/s", "ms_per_step": ms, "roofline": roof,
+            "kernels": {k: {"avg_ms": v[0] / max(v[1], 1), "launches": v[1]} for k, v in kt.items()}}
+
+
 def run_state_copy(steps: int, warmup: int):
     """The fork copy (gdn_state_copy) of 256 blocks of the decode workload's
     1024-block pool into 256 other blocks."""
@@ -355,7 +431,9 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-conv", action="store_true", help="skip the standalone conv layer and fork copy entries")
     ap.add_argument("--no-long", action="store_true", help="skip the long-prefill entry (4 x 32768 tokens)")
-    ap.add_argument("--only", choices=["prefill", "decode", "conv", "copy", "graph", "long"], default=None,
+    ap.add_argument("--no-mamba2", action="store_true", help="skip the Mamba2 scan entries")
+    ap.add_argument("--only", choices=["prefill", "decode", "conv", "copy", "graph", "long", "mamba2_prefill",
+                                       "mamba2_decode"], default=None,
                     help="run one workload alone and print its numbers (profiling runs)")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="run only a device-to-device copy of this many bytes (calibrates HBM byte counters)")
@@ -379,6 +457,9 @@ def main():
         return
     if args.only == "copy":
         print(json.dumps(run_state_copy(args.steps, args.warmup)), flush=True)
+        return
+    if args.only in ("mamba2_prefill", "mamba2_decode"):
+        print(json.dumps(run_ssd(0 if args.only == "mamba2_prefill" else 1, args.steps, args.warmup)), flush=True)
         return
     if args.only == "graph":
         print(json.dumps(run_graph(args.steps, args.warmup)), flush=True)
@@ -421,6 +502,9 @@ def main():
         line["prefill_graph"] = run_graph(args.steps, args.warmup)
         line["conv"] = run_conv(args.steps, args.warmup)
         line["state_copy"] = run_state_copy(args.steps, args.warmup)
+    if not args.no_mamba2:
+        line["mamba2_prefill"] = run_ssd(0, args.steps, args.warmup)
+        line["mamba2_decode"] = run_ssd(1, args.steps, args.warmup)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(b)
     print(json.dumps(line), flush=True)
