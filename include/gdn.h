@@ -224,8 +224,11 @@ typedef struct {
  *              bytes (a multiple of 16, >= H*P*N*4)
  *   y          [T][H][P] bf16 (rows of padding sequences are left as they are)
  * All device pointers 16-byte aligned.  Returns GDN_EUNSUPPORTED for other
- * head or state sizes.  One kernel, enqueued on `stream`; no allocation, no
- * host sync.  Precision: bf16 operands into fp32 products, fp32 state. */
+ * head or state sizes.  Enqueued on `stream` (a chunked kernel for sequences
+ * of length >= 2, a token kernel for lengths 0 and 1; with cu_seqlens_host
+ * only the kernels some sequence needs); no allocation, no host sync.
+ * Precision: chunks take bf16 operands into fp32 products; the token step is
+ * fp32; the state is fp32. */
 int ssd_varlen_scan(const ssd_layer_desc* desc, const void* x, int64_t x_row_stride, const void* B,
                     const void* C, int64_t bc_row_stride, const float* dt, const float* dt_bias,
                     const float* A, const float* D, const int32_t* cu_seqlens,
@@ -247,7 +250,7 @@ const char* gdn_last_error(void);
  * The library creates the events it records and keeps them for reuse. */
 typedef struct {
   char name[32];      /* kernel: "conv_silu_norm", "chunk_scan", "token_recurrent", "conv_state_commit",
-                         "state_copy", "task_counter_reset", "device_plan", "ssd_scan" */
+                         "state_copy", "task_counter_reset", "device_plan", "ssd_scan", "ssd_token" */
   double total_ms;    /* summed event-to-event time of its timed launches */
   int64_t launches;
 } gdn_kernel_time;

@@ -156,9 +156,10 @@ int device_cus(hipStream_t st) {
 bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
 
 // ---- optional per-kernel event timing (measurement only)
-enum { K_CONV = 0, K_CHUNK, K_TOKEN, K_TAIL, K_COPY, K_ZERO, K_PLAN, K_SSD, K_COUNT };
+enum { K_CONV = 0, K_CHUNK, K_TOKEN, K_TAIL, K_COPY, K_ZERO, K_PLAN, K_SSD, K_SSD_TOKEN, K_COUNT };
 const char* const kKernelNames[K_COUNT] = {"conv_silu_norm", "chunk_scan", "token_recurrent", "conv_state_commit",
-                                           "state_copy", "task_counter_reset", "device_plan", "ssd_scan"};
+                                           "state_copy", "task_counter_reset", "device_plan", "ssd_scan",
+                                           "ssd_token"};
 
 struct Timing {
   std::mutex mu;
@@ -669,11 +670,17 @@ extern "C" int ssd_varlen_scan(const ssd_layer_desc* desc, const void* x, int64_
     return fail(GDN_EUNSUPPORTED, "row strides above 2^23 elements");
   if (!aligned(x, 16) || !aligned(B, 16) || !aligned(C, 16) || !aligned(y, 16) || !aligned(ssm_pool, 16))
     return fail(GDN_EINVAL, "x, B, C, y and ssm_pool must be 16-byte aligned");
+  // with the host offsets, a kernel with no sequence of its kind is not launched
+  bool any_long = true, any_short = true;
   if (cu_seqlens_host) {
     if (cu_seqlens_host[0] != 0 || cu_seqlens_host[num_seqs] != total_tokens)
       return fail(GDN_EINVAL, "cu_seqlens must run from 0 to total_tokens=%d", total_tokens);
-    for (int i = 0; i < num_seqs; ++i)
-      if (cu_seqlens_host[i + 1] < cu_seqlens_host[i]) return fail(GDN_EINVAL, "cu_seqlens decreases at %d", i);
+    any_long = any_short = false;
+    for (int i = 0; i < num_seqs; ++i) {
+      const int L = cu_seqlens_host[i + 1] - cu_seqlens_host[i];
+      if (L < 0) return fail(GDN_EINVAL, "cu_seqlens decreases at %d", i);
+      if (L >= 2) any_long = true; else any_short = true;
+    }
   }
   gdn::SsdArgs a{};
   a.x = reinterpret_cast<const uint16_t*>(x);
@@ -698,7 +705,15 @@ extern "C" int ssd_varlen_scan(const ssd_layer_desc* desc, const void* x, int64_
   a.total_tokens = total_tokens;
   a.y = reinterpret_cast<uint16_t*>(y);
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  const hipError_t e = timed(K_SSD, st, [&] { return gdn::launch_ssd(a, st); });
-  if (e != hipSuccess) return fail(GDN_EHIP, "ssd scan launch: %s", hipGetErrorString(e));
+  // sequences of length >= 2 in chunks, those of length 0 and 1 in the token
+  // kernel; they touch disjoint blocks, so the two launches need no order
+  if (any_long) {
+    const hipError_t e = timed(K_SSD, st, [&] { return gdn::launch_ssd(a, st); });
+    if (e != hipSuccess) return fail(GDN_EHIP, "ssd scan launch: %s", hipGetErrorString(e));
+  }
+  if (any_short) {
+    const hipError_t e = timed(K_SSD_TOKEN, st, [&] { return gdn::launch_ssd_token(a, st); });
+    if (e != hipSuccess) return fail(GDN_EHIP, "ssd token launch: %s", hipGetErrorString(e));
+  }
   return GDN_OK;
 }

@@ -169,7 +169,8 @@ struct SsdArgs {
   uint16_t* y;
 };
 bool ssd_supported(int head_dim, int state_dim);
-hipError_t launch_ssd(const SsdArgs& a, hipStream_t st);
+hipError_t launch_ssd(const SsdArgs& a, hipStream_t st);        // sequences of length >= 2
+hipError_t launch_ssd_token(const SsdArgs& a, hipStream_t st);  // sequences of length 0 and 1
 hipError_t launch_recurrent(const ScanArgs& a, int dk, int dv, bool bf16, hipStream_t st);
 // The conv of the chunked sequences run by the chunk-scan workgroups
 // themselves, as tasks they claim before their scans.  Task t belongs to

@@ -29,6 +29,7 @@ constexpr int SP = 64;    // head size
 constexpr int SNT = 256;  // threads
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 struct SsdSmem {
@@ -76,7 +77,7 @@ __global__ __launch_bounds__(SNT, 2) void ssd_chunk_kernel(SsdArgs a) {
   if (s >= a.num_seqs || !seq_active(a.read_idx, a.write_idx, s, a.num_blocks)) return;
   const int grp = m / (H / a.num_groups);
   const int r0 = a.cu[s], L = a.cu[s + 1] - r0;
-  if (r0 < 0 || L < 0 || r0 + L > a.total_tokens) return;  // offsets outside the packed rows
+  if (r0 < 0 || L < 2 || r0 + L > a.total_tokens) return;  // token kernel: L <= 1; offsets outside the rows
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, i16 = lane & 15;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const float Am = a.A[m], Dm = a.D ? a.D[m] : 0.f, bias = a.dt_bias ? a.dt_bias[m] : 0.f;
@@ -246,9 +247,75 @@ __global__ __launch_bounds__(SNT, 2) void ssd_chunk_kernel(SsdArgs a) {
   for (int nb = 0; nb < 8; ++nb) dst[4 * nb + g] = S[nb];
 }
 
+// One token (or none) per sequence: the recurrence step itself, in fp32, as a
+// streaming read-modify-write of the head's state.  256 threads per (sequence,
+// head); pass i moves 4 KiB of h: thread t holds h[p][n..n+3] with
+// p = 8i + t / 32 and n = 4 (t % 32), so every load and store of a wave covers
+// 1 KiB contiguously.  y_p sums over the 32 lanes that hold row p.  A sequence
+// of length 0 copies its state.
+__global__ __launch_bounds__(SNT) void ssd_token_kernel(SsdArgs a) {
+  const int H = a.num_heads;
+  const int s = blockIdx.x / H;
+  int m = blockIdx.x % H;
+  if (H % 8 == 0) m = (m % 8) * (H / 8) + m / 8;
+  if (s >= a.num_seqs || !seq_active(a.read_idx, a.write_idx, s, a.num_blocks)) return;
+  const int r0 = a.cu[s], L = a.cu[s + 1] - r0;
+  if (r0 < 0 || L < 0 || L > 1 || r0 + L > a.total_tokens) return;
+  const int tid = threadIdx.x, lane = tid & 63, n0 = 4 * (tid & 31), prow = tid >> 5;
+  const int64_t head = (int64_t)m * SP * SN;
+  const f32x4* src = reinterpret_cast<const f32x4*>(a.pool + (int64_t)a.read_idx[s] * a.pool_stride + head) + tid;
+  f32x4* dst = reinterpret_cast<f32x4*>(a.pool + (int64_t)a.write_idx[s] * a.pool_stride + head) + tid;
+  f32x4 h[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) h[i] = __builtin_nontemporal_load(src + SNT * i);
+  if (L == 1) {
+    const int grp = m / (H / a.num_groups);
+    const float bias = a.dt_bias ? a.dt_bias[m] : 0.f;
+    float d = a.dt[(int64_t)r0 * H + m] + bias;
+    if (a.softplus) d = softplus_f(d);
+    const float decay = __expf(d * a.A[m]);
+    const float Dm = a.D ? a.D[m] : 0.f;
+    const uint16_t* xr = a.x + (int64_t)r0 * a.x_stride + m * SP;
+    const u32x2 bw = *reinterpret_cast<const u32x2*>(a.b + (int64_t)r0 * a.bc_stride + grp * SN + n0);
+    const u32x2 cw = *reinterpret_cast<const u32x2*>(a.c + (int64_t)r0 * a.bc_stride + grp * SN + n0);
+    float bn[4], cn[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t bb = bw[e / 2], cc = cw[e / 2];
+      bn[e] = __uint_as_float((e & 1) ? (bb & 0xffff0000u) : (bb << 16));
+      cn[e] = __uint_as_float((e & 1) ? (cc & 0xffff0000u) : (cc << 16));
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int p = 8 * i + prow;
+      const float xp = bf16_bits_to_f32(xr[p]);
+      const float dx = d * xp;
+      float acc = 0.f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        h[i][e] = decay * h[i][e] + dx * bn[e];
+        acc += h[i][e] * cn[e];
+      }
+#pragma unroll
+      for (int off = 16; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
+      if ((lane & 31) == 0) a.y[((int64_t)r0 * H + m) * SP + p] = f32_to_bf16_bits(acc + Dm * xp);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) __builtin_nontemporal_store(h[i], dst + SNT * i);
+}
+
 }  // namespace
 
 bool ssd_supported(int head_dim, int state_dim) { return head_dim == SP && state_dim == SN; }
+
+hipError_t launch_ssd_token(const SsdArgs& a, hipStream_t st) {
+  if (a.num_seqs <= 0 || a.num_heads <= 0) return hipSuccess;
+  const int64_t blocks = (int64_t)a.num_seqs * a.num_heads;
+  if (blocks > INT32_MAX) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(ssd_token_kernel, dim3((unsigned)blocks), dim3(SNT), 0, st, a);
+  return hipGetLastError();
+}
 
 hipError_t launch_ssd(const SsdArgs& a, hipStream_t st) {
   if (a.num_seqs <= 0 || a.num_heads <= 0) return hipSuccess;
