@@ -308,7 +308,8 @@ namespace {
 
 // Copies block src[i] of both pools to block dst[i].  Block x = pair i, block y
 // = 64 KiB piece of the concatenation [recurrent state; conv state]; 256
-// threads move 16 bytes per load, 16 loads in flight each.
+// threads move 16 bytes per load, 16 loads in flight each, non-temporal (the
+// blocks are touched once; 4% faster than cached accesses).
 __global__ __launch_bounds__(256) void state_copy_kernel(StateCopyArgs a) {
   const int i = blockIdx.x;
   const int sb = a.src[i], db = a.dst[i];
@@ -324,7 +325,7 @@ __global__ __launch_bounds__(256) void state_copy_kernel(StateCopyArgs a) {
     if (o < total) {
       const char* src = o < ssm_bytes ? a.ssm_pool + (int64_t)sb * a.ssm_stride + o
                                       : a.conv_pool + (int64_t)sb * a.conv_stride + (o - ssm_bytes);
-      v[k] = *as_global(reinterpret_cast<const u32x4*>(src));
+      v[k] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src));
     }
   }
 #pragma unroll
@@ -333,7 +334,7 @@ __global__ __launch_bounds__(256) void state_copy_kernel(StateCopyArgs a) {
     if (o < total) {
       char* dst = o < ssm_bytes ? a.ssm_pool + (int64_t)db * a.ssm_stride + o
                                 : a.conv_pool + (int64_t)db * a.conv_stride + (o - ssm_bytes);
-      *as_global(reinterpret_cast<u32x4*>(dst)) = v[k];
+      __builtin_nontemporal_store(v[k], reinterpret_cast<u32x4*>(dst));
     }
   }
 }
