@@ -156,3 +156,51 @@ def test_repeated_calls_continue_in_place():
     assert _rel(y2.double().numpy(), full_y.double().numpy()) <= TOL
     for wb in b.write_idx.tolist():
         assert _rel(pool[wb].double().numpy(), full_pool[wb].double().numpy()) <= TOL
+
+
+def test_graph_replays_for_other_batches():
+    """Without host offsets every launch depends only on the counts, so a HIP
+    graph captured with one batch replays for others of the same sequence and
+    token counts (other lengths, blocks and data); each replay against an eager
+    run (bitwise) and the oracle, with eager work between replays."""
+    layer = workloads.MAMBA2_SMALL
+    shapes = [[60, 1, 100, 0], [1, 1, 150, 9], [80, 40, 20, 21], [161, 0, 0, 0]]
+    batches = [workloads.ssd_batch(layer, l, seed=70 + i, num_blocks=9) for i, l in enumerate(shapes)]
+    a = batches[0]
+    dev = lambda t: t.cuda().contiguous()
+    d = {k: dev(getattr(a, k)) for k in ("xbc", "dt", "A", "D", "dt_bias", "cu_seqlens", "read_idx", "write_idx",
+                                          "ssm_pool")}
+    y = torch.zeros(a.total_tokens, layer.num_heads, layer.head_dim, dtype=torch.bfloat16, device="cuda")
+
+    def fwd():
+        x, B, C = a.views(d["xbc"])
+        gdn.ssd_varlen_scan(layer, x, B, C, d["dt"], d["A"], d["cu_seqlens"], None, d["read_idx"], d["write_idx"],
+                            d["ssm_pool"], y, dt_bias=d["dt_bias"], D=d["D"])
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fwd()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        fwd()
+    torch.cuda.synchronize()
+    for rep, b in enumerate(batches[1:] + batches[:1]):
+        for k in d:
+            d[k].copy_(dev(getattr(b, k)))
+        y.fill_(7.0)
+        junk = torch.randn(1 << 20, device="cuda").sum()  # eager work between replays
+        graph.replay()
+        torch.cuda.synchronize()
+        got_y, got_pool = y.cpu(), d["ssm_pool"].cpu()
+        ref_y, ref_pool = _run_gpu(b)
+        assert torch.equal(got_y.view(torch.int16), ref_y.view(torch.int16))
+        assert torch.equal(got_pool, ref_pool)
+        ry, rpool = _oracle(b, list(range(layer.num_heads)))
+        worst = max(_rel(got_y[int(b.cu_seqlens[s]):int(b.cu_seqlens[s + 1])].double().numpy(),
+                         ry[int(b.cu_seqlens[s]):int(b.cu_seqlens[s + 1])])
+                    for s in range(len(b.lengths)) if b.lengths[s] > 0)
+        print("replay %d lengths %s: y %.3e (%.1f)" % (rep, b.lengths, worst, float(junk)), flush=True)
+        assert worst <= TOL
