@@ -29,7 +29,6 @@ constexpr int SP = 64;    // head size
 constexpr int SNT = 256;  // threads
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 struct SsdSmem {
@@ -45,8 +44,18 @@ struct SsdSmem {
 static_assert(sizeof(SsdSmem) <= 80 * 1024, "two workgroups per CU");
 
 // Element offsets in the swizzled tiles: 256-byte rows (16 chunks) and 128-byte rows (8 chunks).
-__device__ __forceinline__ int sw256(int row, int col) { return row * 128 + ((((col >> 3) ^ (row & 15)) << 3) | (col & 7)); }
-__device__ __forceinline__ int sw128(int row, int col) { return row * 64 + ((((col >> 3) ^ (row & 7)) << 3) | (col & 7)); }
+__device__ __forceinline__ int sw256(int row, int col) {
+  const int f = ((row & 7) << 1) | ((row >> 3) & 1);
+  return row * 128 + ((((col >> 3) ^ f) << 3) | (col & 7));
+}
+__device__ __forceinline__ int sw128(int row, int col) {
+  const int f = (((row >> 1) & 3) << 1) | ((row >> 3) & 1);
+  return row * 64 + ((((col >> 3) ^ f) << 3) | (col & 7));
+}
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ u32x2 pack4(float a, float b, float c, float d) {
+  return u32x2{pack_bf16x2(a, b), pack_bf16x2(c, d)};
+}
 
 __device__ __forceinline__ f32x4 mma(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -155,23 +164,24 @@ __global__ __launch_bounds__(SNT, 2) void ssd_chunk_kernel(SsdArgs a) {
 
     // rows 16w..16w+15 of L o C B^T (blocks right of the diagonal are zero)
     {
-      const float gt[4] = {sm.gam[16 * w + 4 * g], sm.gam[16 * w + 4 * g + 1], sm.gam[16 * w + 4 * g + 2],
-                           sm.gam[16 * w + 4 * g + 3]};
+      // computed transposed (B C^T): a lane holds 4 consecutive j of row t
+      const int t = 16 * w + i16;
+      const float gt = sm.gam[t];
+#pragma unroll
       for (int jb = 0; jb < 4; ++jb) {
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
         if (jb <= w) {
 #pragma unroll
           for (int kk = 0; kk < 4; ++kk)
-            acc = mma(ld8(&sm.c[sw256(16 * w + i16, 32 * kk + 8 * g)]), ld8(&sm.b[sw256(16 * jb + i16, 32 * kk + 8 * g)]), acc);
+            acc = mma(ld8(&sm.b[sw256(16 * jb + i16, 32 * kk + 8 * g)]), ld8(&sm.c[sw256(t, 32 * kk + 8 * g)]), acc);
         }
-        const int j = 16 * jb + i16;
-        const float gj = sm.gam[j], dj = sm.dd[j];
+        const int j0 = 16 * jb + 4 * g;
+        const f32x4 gj = *reinterpret_cast<const f32x4*>(&sm.gam[j0]);
+        const f32x4 dj = *reinterpret_cast<const f32x4*>(&sm.dd[j0]);
+        float v[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int t = 16 * w + 4 * g + r;
-          const float v = j <= t ? acc[r] * __expf(gt[r] - gj) * dj : 0.f;
-          sm.p[sw128(t, j)] = f32_to_bf16_bits(v);
-        }
+        for (int r = 0; r < 4; ++r) v[r] = j0 + r <= t ? acc[r] * __expf(gt - gj[r]) * dj[r] : 0.f;
+        *reinterpret_cast<u32x2*>(&sm.p[sw128(t, j0)]) = pack4(v[0], v[1], v[2], v[3]);
       }
     }
     // S as the k side of C S, pair order: tiles 2kk and 2kk + 1
@@ -199,17 +209,22 @@ __global__ __launch_bounds__(SNT, 2) void ssd_chunk_kernel(SsdArgs a) {
       const int tr = 16 * tb + i16;
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk)
-        ys = mma(join(ld4(&sm.c[sw256(tr, 32 * kk + 4 * g)]), ld4(&sm.c[sw256(tr, 32 * kk + 16 + 4 * g)])), sop[kk], ys);
+        ys = mma(sop[kk], join(ld4(&sm.c[sw256(tr, 32 * kk + 4 * g)]), ld4(&sm.c[sw256(tr, 32 * kk + 16 + 4 * g)])), ys);
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk)
         if (kk <= tb / 2)
-          yp = mma(join(ld4(&sm.p[sw128(tr, 32 * kk + 4 * g)]), ld4(&sm.p[sw128(tr, 32 * kk + 16 + 4 * g)])), xop[kk], yp);
+          yp = mma(xop[kk], join(ld4(&sm.p[sw128(tr, 32 * kk + 4 * g)]), ld4(&sm.p[sw128(tr, 32 * kk + 16 + 4 * g)])), yp);
+      // transposed: lane holds y[tr][16w + 4g .. + 3]
+      const u32x2 xr = *reinterpret_cast<const u32x2*>(&sm.x[sw128(tr, 16 * w + 4 * g)]);
+      const float egt = __expf(sm.gam[tr]);
+      float yv[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int t = 16 * tb + 4 * g + r, p = 16 * w + i16;
-        const float xv = bf16_bits_to_f32(sm.x[sw128(t, p)]);
-        sm.y[sw128(t, p)] = f32_to_bf16_bits(__expf(sm.gam[t]) * ys[r] + yp[r] + Dm * xv);
+        const uint32_t xw2 = xr[r / 2];
+        const float xv = __uint_as_float((r & 1) ? (xw2 & 0xffff0000u) : (xw2 << 16));
+        yv[r] = egt * ys[r] + yp[r] + Dm * xv;
       }
+      *reinterpret_cast<u32x2*>(&sm.y[sw128(tr, 16 * w + 4 * g)]) = pack4(yv[0], yv[1], yv[2], yv[3]);
     }
     // S <- Gamma_last S + B^T diag(w) X
     {
