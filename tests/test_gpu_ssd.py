@@ -204,3 +204,47 @@ def test_graph_replays_for_other_batches():
                     for s in range(len(b.lengths)) if b.lengths[s] > 0)
         print("replay %d lengths %s: y %.3e (%.1f)" % (rep, b.lengths, worst, float(junk)), flush=True)
         assert worst <= TOL
+
+
+def test_conv_then_scan_as_a_mamba2_mixer_core():
+    """The varlen conv layer (gdn_varlen_conv, SiLU) over raw x | B | C rows,
+    then the scan reading its output as strided views: against the conv oracle
+    followed by the scan oracle run on the oracle's own (bf16-rounded) conv
+    output, so that both sides scan the same inputs."""
+    import math
+
+    import oracle
+
+    layer = workloads.MAMBA2_SMALL
+    b = workloads.ssd_batch(layer, [70, 1, 129, 3], seed=80, fresh=[1, 0, 0, 1])
+    rng = np.random.default_rng(81)
+    C, W = layer.conv_channels, layer.conv_width
+    w = torch.tensor(rng.standard_normal((C, W)) / math.sqrt(W), dtype=torch.float32).to(torch.bfloat16)
+    cpool = torch.tensor(rng.standard_normal((b.ssm_pool.shape[0], W - 1, C)), dtype=torch.float32).to(torch.bfloat16)
+    cpool[0] = 0
+    raw = b.xbc  # used as the conv input here
+    dev = lambda t: t.cuda().contiguous()
+    xbc = torch.empty_like(dev(raw))
+    cpool_d = dev(cpool)
+    gdn.gdn_varlen_conv(dev(raw), dev(w), dev(b.cu_seqlens), b.cu_seqlens, dev(b.read_idx), dev(b.write_idx),
+                        cpool_d, xbc, silu=True)
+    x, B, C_ = b.views(xbc)
+    pool = dev(b.ssm_pool)
+    y = torch.zeros(b.total_tokens, layer.num_heads, layer.head_dim, dtype=torch.bfloat16, device="cuda")
+    gdn.ssd_varlen_scan(layer, x, B, C_, dev(b.dt), dev(b.A), dev(b.cu_seqlens), b.cu_seqlens, dev(b.read_idx),
+                        dev(b.write_idx), pool, y, dt_bias=dev(b.dt_bias), D=dev(b.D))
+    torch.cuda.synchronize()
+    ref_conv, ref_cpool = oracle.varlen_conv(raw, w, b.cu_seqlens, b.read_idx, b.write_idx, cpool, silu=True)
+    assert torch.equal(cpool_d.cpu().view(torch.int16), ref_cpool.view(torch.int16))
+    b2 = workloads.SsdBatch(layer=layer, lengths=b.lengths, xbc=torch.from_numpy(ref_conv).to(torch.bfloat16),
+                            dt=b.dt, dt_bias=b.dt_bias, A=b.A, D=b.D, cu_seqlens=b.cu_seqlens,
+                            read_idx=b.read_idx, write_idx=b.write_idx, ssm_pool=b.ssm_pool)
+    ry, rpool = _oracle(b2, list(range(layer.num_heads)))
+    yc, pc = y.cpu(), pool.cpu()
+    worst = 0.0
+    for s in range(len(b.lengths)):
+        rows = slice(int(b.cu_seqlens[s]), int(b.cu_seqlens[s + 1]))
+        worst = max(worst, _rel(yc[rows].double().numpy(), ry[rows]),
+                    _rel(pc[int(b.write_idx[s])].double().numpy(), rpool[int(b.write_idx[s])]))
+    print("conv+scan: worst %.3e" % worst, flush=True)
+    assert worst <= 2 * TOL
