@@ -357,6 +357,58 @@ def run_ssd(cfg: int, steps: int, warmup: int):
             "kernels": {k: {"avg_ms": v[0] / max(v[1], 1), "launches": v[1]} for k, v in kt.items()}}
 
 
+def run_kda_decode(steps: int, warmup: int):
+    """The KDA layer (kda_varlen_forward) on the decode workload: 256 one-token
+    sequences of the gated-delta-net layer's shape, with a decay per key channel."""
+    import numpy as np
+    import torch
+
+    import linear_attention_state_amd as gdn
+    import workloads
+
+    b = workloads.config(2)
+    L = b.layer
+    dev = torch.device("cuda", 0)
+    d = {k: getattr(b, k).to(dev).contiguous() for k in
+         ("x", "conv_weight", "beta", "cu_seqlens", "read_idx", "write_idx", "conv_pool", "ssm_pool")}
+    rng = np.random.default_rng(7)
+    g = torch.tensor(-np.logaddexp(0.0, rng.standard_normal((b.total_tokens, L.num_v_heads, L.head_k_dim))),
+                     dtype=torch.float32, device=dev)
+    out = torch.empty(b.total_tokens, L.num_v_heads, L.head_v_dim, dtype=L.torch_act, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    cu_host = b.cu_seqlens.clone()
+
+    def step():
+        gdn.kda_varlen_forward(L, d["x"], d["conv_weight"], g, d["beta"], d["cu_seqlens"], cu_host, d["read_idx"],
+                               d["write_idx"], d["conv_pool"], d["ssm_pool"], out, stream=stream.cuda_stream)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for _ in range(steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / steps
+    gdn.gdn_kernel_timing(True)
+    for _ in range(steps):
+        step()
+    kt = gdn.gdn_kernel_times()
+    gdn.gdn_kernel_timing(False)
+    k_ms = kt["token_recurrent"][0] / kt["token_recurrent"][1]
+    # the gated-delta-net decode bytes, with g per key channel instead of per head
+    work = token_path_bytes(L, b.total_tokens) + b.total_tokens * L.num_v_heads * (L.head_k_dim - 1) * 4
+    roof = {"bound": "hbm", "achieved": work / (k_ms * 1e-3) / 1e9, "peak": PEAK_HBM / 1e9, "unit": "GB/s",
+            "kernel": "token_recurrent", "traffic": None}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    return {"workload": "KDA decode: 256 sequences of 1 token, H_k=16, H_v=32, d=128, W=4, bf16, "
+                        "g per key channel, 1024-block pool",
+            "value": b.total_tokens / (ms * 1e-3), "unit": "tokens/s", "ms_per_step": ms, "roofline": roof,
+            "kernels": {k: {"avg_ms": v[0] / max(v[1], 1), "launches": v[1]} for k, v in kt.items()}}
+
+
 def run_state_copy(steps: int, warmup: int):
     """The fork copy (gdn_state_copy) of 256 blocks of the decode workload's
     1024-block pool into 256 other blocks."""
@@ -434,7 +486,7 @@ def main():
     ap.add_argument("--no-long", action="store_true", help="skip the long-prefill entry (4 x 32768 tokens)")
     ap.add_argument("--no-mamba2", action="store_true", help="skip the Mamba2 scan entries")
     ap.add_argument("--only", choices=["prefill", "decode", "conv", "copy", "graph", "long", "mamba2_prefill",
-                                       "mamba2_decode"], default=None,
+                                       "mamba2_decode", "kda_decode"], default=None,
                     help="run one workload alone and print its numbers (profiling runs)")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="run only a device-to-device copy of this many bytes (calibrates HBM byte counters)")
@@ -458,6 +510,9 @@ def main():
         return
     if args.only == "copy":
         print(json.dumps(run_state_copy(args.steps, args.warmup)), flush=True)
+        return
+    if args.only == "kda_decode":
+        print(json.dumps(run_kda_decode(args.steps, args.warmup)), flush=True)
         return
     if args.only in ("mamba2_prefill", "mamba2_decode"):
         print(json.dumps(run_ssd(0 if args.only == "mamba2_prefill" else 1, args.steps, args.warmup)), flush=True)
@@ -504,6 +559,7 @@ def main():
         line["conv"] = run_conv(args.steps, args.warmup)
         line["state_copy"] = run_state_copy(args.steps, args.warmup)
     if not args.no_mamba2:
+        line["kda_decode"] = run_kda_decode(args.steps, args.warmup)
         line["mamba2_prefill"] = run_ssd(0, args.steps, args.warmup)
         line["mamba2_decode"] = run_ssd(1, args.steps, args.warmup)
     if not args.no_cpu_baseline:

@@ -188,6 +188,28 @@ int gdn_state_copy(const gdn_layer_desc* desc, void* conv_pool, int64_t conv_blo
                    float* ssm_pool, int64_t ssm_block_stride, int32_t num_blocks,
                    const int32_t* src, const int32_t* dst, int32_t n, void* stream);
 
+/* ---- Kimi delta attention (KDA) layer with per-sequence states.
+ * The pages list KDA (Kimi Linear, GLM5-next) among the layers whose states
+ * the cache holds, without a formula.  The recurrence is the published one
+ * (Kimi Linear technical report, 2025): the gated delta rule with a decay per
+ * key channel, S_t = (I - b_t k_t k_t^T) diag(a_t) S_{t-1} + b_t k_t v_t^T,
+ * o_t = S_t^T q_t, a_t = exp(g_t) with g_t in R^{d_k} per value head.  The
+ * rest of the layer (conv + SiLU from the conv state, q/k L2 norm, q scale,
+ * GQA head map, paged states, padding and empty sequences) is that of
+ * gdn_varlen_forward.
+ *   g  [T][H_v][d_k] fp32 (log decay per key channel; <= 0 for a decay)
+ *   every other argument as for gdn_varlen_forward; cu_seqlens_host is required
+ * This build runs every sequence token by token (one workgroup per sequence
+ * and value head, the conv, norms and recurrence in one pass), then the
+ * conv-state commit: exact for any length, tuned for decode, not for long
+ * prefill.  No workspace, no allocation, no host sync. */
+int kda_varlen_forward(const gdn_layer_desc* desc, const void* x, const void* conv_weight,
+                       const float* g, const float* beta, const int32_t* cu_seqlens,
+                       const int32_t* cu_seqlens_host, int32_t num_seqs, int32_t total_tokens,
+                       const int32_t* read_idx, const int32_t* write_idx, void* conv_pool,
+                       int64_t conv_block_stride, float* ssm_pool, int64_t ssm_block_stride,
+                       int32_t num_blocks, void* out, void* stream);
+
 /* ---- Mamba2 scan with per-sequence states.
  * The model-support tracker page (continuous batching for the remaining
  * linear-attention and state-space hybrids) names a varlen scan with
@@ -241,7 +263,7 @@ const char* gdn_last_error(void);
 
 /* Measurement support (not needed to run the layer).
  * gdn_kernel_timing(1) makes every later gdn_varlen_forward, gdn_varlen_conv,
- * gdn_state_copy and ssd_varlen_scan in this process record a HIP event pair on the call's
+ * gdn_state_copy, kda_varlen_forward and ssd_varlen_scan in this process record a HIP event pair on the call's
  * stream around each kernel it launches,
  * and clears the totals; gdn_kernel_timing(0) stops recording.
  * gdn_kernel_times() waits for the recorded events (a host sync), adds their

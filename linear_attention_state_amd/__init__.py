@@ -17,7 +17,7 @@ LIB_PATH = os.path.join(HERE, "_lib", "libgdn.so")
 GDN_OK, GDN_EINVAL, GDN_EUNSUPPORTED, GDN_EWORKSPACE, GDN_EHIP = 0, -1, -2, -3, -4
 GDN_F32, GDN_BF16 = 0, 1
 EXPORTS = ("gdn_state_spec", "gdn_workspace_size", "gdn_varlen_forward", "gdn_varlen_conv", "gdn_state_copy",
-           "ssd_varlen_scan", "gdn_last_error",
+           "ssd_varlen_scan", "kda_varlen_forward", "gdn_last_error",
            "gdn_kernel_timing", "gdn_kernel_times")
 
 _lib = None
@@ -96,6 +96,10 @@ def load_library():
         lib.gdn_state_copy.restype = ctypes.c_int
         lib.gdn_state_copy.argtypes = [ctypes.POINTER(gdn_layer_desc), P, ctypes.c_int64, P, ctypes.c_int64,
                                        ctypes.c_int32, P, P, ctypes.c_int32, P]
+        lib.kda_varlen_forward.restype = ctypes.c_int
+        lib.kda_varlen_forward.argtypes = [
+            ctypes.POINTER(gdn_layer_desc), P, P, P, P, P, P, ctypes.c_int32, ctypes.c_int32, P, P, P,
+            ctypes.c_int64, P, ctypes.c_int64, ctypes.c_int32, P, P]
         lib.ssd_varlen_scan.restype = ctypes.c_int
         lib.ssd_varlen_scan.argtypes = [
             ctypes.POINTER(ssd_layer_desc), P, ctypes.c_int64, P, P, ctypes.c_int64, P, P, P, P, P, P,
@@ -255,6 +259,29 @@ def gdn_state_copy(layer, conv_pool, ssm_pool, src, dst, stream=None):
         ctypes.byref(make_desc(layer)), _dev_ptr(conv_pool, "conv_pool") if has_conv else None, conv_stride,
         _dev_ptr(ssm_pool, "ssm_pool"), ssm_pool.stride(0) * ssm_pool.element_size(), int(ssm_pool.shape[0]),
         _dev_ptr(src, "src"), _dev_ptr(dst, "dst"), int(src.numel()), ctypes.c_void_p(stream)))
+
+
+def kda_varlen_forward(layer, x, conv_weight, g, beta, cu_seqlens, cu_seqlens_host, read_idx, write_idx,
+                       conv_pool, ssm_pool, out, stream=None):
+    """Enqueues the KDA layer forward: as gdn_varlen_forward, with g [T][H_v][d_k]
+    float32 (a log decay per key channel); cu_seqlens_host is required."""
+    import torch
+
+    if g.dtype != torch.float32 or g.dim() != 3 or g.shape[2] != layer.head_k_dim:
+        raise ValueError("g must be float32 [T][H_v][d_k]")
+    if stream is None:
+        stream = torch.cuda.current_stream(x.device).cuda_stream
+    host = cu_seqlens_host.to(torch.int32).contiguous()
+    W = int(layer.conv_width)
+    has_conv = conv_pool is not None and conv_pool.numel() > 0
+    conv_stride = conv_pool.stride(0) * conv_pool.element_size() if has_conv else 0
+    _check(load_library().kda_varlen_forward(
+        ctypes.byref(make_desc(layer)), _dev_ptr(x, "x"), _dev_ptr(conv_weight, "conv_weight"), _dev_ptr(g, "g"),
+        _dev_ptr(beta, "beta"), _dev_ptr(cu_seqlens, "cu_seqlens"), ctypes.cast(host.data_ptr(), ctypes.c_void_p),
+        int(read_idx.numel()), int(x.shape[0]), _dev_ptr(read_idx, "read_idx"), _dev_ptr(write_idx, "write_idx"),
+        _dev_ptr(conv_pool, "conv_pool") if (has_conv and W > 1) else None, conv_stride,
+        _dev_ptr(ssm_pool, "ssm_pool"), ssm_pool.stride(0) * ssm_pool.element_size(), int(ssm_pool.shape[0]),
+        _dev_ptr(out, "out"), ctypes.c_void_p(stream)))
 
 
 def ssd_varlen_scan(layer, x, B, C, dt, A, cu_seqlens, cu_seqlens_host, read_idx, write_idx, ssm_pool, y,

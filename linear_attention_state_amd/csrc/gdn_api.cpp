@@ -717,3 +717,66 @@ extern "C" int ssd_varlen_scan(const ssd_layer_desc* desc, const void* x, int64_
   }
   return GDN_OK;
 }
+
+extern "C" int kda_varlen_forward(const gdn_layer_desc* desc, const void* x, const void* conv_weight,
+                                  const float* g, const float* beta, const int32_t* cu_seqlens,
+                                  const int32_t* cu_seqlens_host, int32_t num_seqs, int32_t total_tokens,
+                                  const int32_t* read_idx, const int32_t* write_idx, void* conv_pool,
+                                  int64_t conv_block_stride, float* ssm_pool, int64_t ssm_block_stride,
+                                  int32_t num_blocks, void* out, void* stream) {
+  int rc = check_desc(desc);
+  if (rc) return rc;
+  const int W = desc->conv_width;
+  const bool bf16 = desc->act_dtype == GDN_BF16;
+  if (num_seqs < 1) return fail(GDN_EINVAL, "no sequences in batch (num_seqs=%d)", num_seqs);
+  if (total_tokens < 0) return fail(GDN_EINVAL, "total_tokens=%d is negative", total_tokens);
+  if (!cu_seqlens_host) return fail(GDN_EINVAL, "cu_seqlens_host is NULL");
+  if (cu_seqlens_host[0] != 0) return fail(GDN_EINVAL, "cu_seqlens[0]=%d, expected 0", cu_seqlens_host[0]);
+  for (int i = 0; i < num_seqs; ++i)
+    if (cu_seqlens_host[i + 1] < cu_seqlens_host[i])
+      return fail(GDN_EINVAL, "cu_seqlens decreases at %d (%d -> %d)", i, cu_seqlens_host[i], cu_seqlens_host[i + 1]);
+  if (cu_seqlens_host[num_seqs] != total_tokens)
+    return fail(GDN_EINVAL, "cu_seqlens[%d]=%d differs from total_tokens=%d", num_seqs, cu_seqlens_host[num_seqs],
+                total_tokens);
+  if (!cu_seqlens || !read_idx || !write_idx) return fail(GDN_EINVAL, "device cu_seqlens/read_idx/write_idx is NULL");
+  if (!ssm_pool) return fail(GDN_EINVAL, "ssm_pool is NULL");
+  if (W > 1 && !conv_pool) return fail(GDN_EINVAL, "conv_pool is NULL but conv_width=%d > 1", W);
+  if (total_tokens > 0 && (!x || !g || !beta || !out || !conv_weight))
+    return fail(GDN_EINVAL, "x, conv_weight, g, beta and out must be non-NULL when total_tokens > 0");
+  if (num_blocks < 2) return fail(GDN_EINVAL, "num_blocks=%d; the pool needs the trash block and one more", num_blocks);
+  if (ssm_block_stride < ssm_state_bytes(desc) || ssm_block_stride % 16)
+    return fail(GDN_EINVAL, "ssm_block_stride=%lld must be a multiple of 16 and >= %lld", (long long)ssm_block_stride,
+                (long long)ssm_state_bytes(desc));
+  if (W > 1 && (conv_block_stride < conv_state_bytes(desc) || conv_block_stride % 16))
+    return fail(GDN_EINVAL, "conv_block_stride=%lld must be a multiple of 16 and >= %lld",
+                (long long)conv_block_stride, (long long)conv_state_bytes(desc));
+  if (!aligned(x, 16) || !aligned(out, 16) || !aligned(ssm_pool, 16) || !aligned(conv_pool, 16) ||
+      !aligned(g, 4) || !aligned(beta, 4))
+    return fail(GDN_EINVAL, "x, out and the pools must be 16-byte aligned");
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const int C = (int)channels(desc);
+  gdn::ScanArgs sa{};
+  sa.x = x; sa.w = conv_weight;
+  sa.conv_pool = W > 1 ? reinterpret_cast<const char*>(conv_pool) : nullptr;
+  sa.conv_stride = conv_block_stride; sa.width = W; sa.eps = desc->l2norm_eps;
+  sa.q_scale = desc->q_scale > 0.f ? desc->q_scale : 1.0f / sqrtf((float)desc->head_k_dim);
+  sa.g = g; sa.beta = beta; sa.cu = cu_seqlens; sa.read_idx = read_idx;
+  sa.write_idx = write_idx; sa.ssm_pool = ssm_pool; sa.ssm_stride = ssm_block_stride; sa.out = out;
+  sa.num_seqs = num_seqs; sa.num_blocks = num_blocks; sa.num_k_heads = desc->num_k_heads;
+  sa.num_v_heads = desc->num_v_heads; sa.channels = C;
+  sa.min_len = 0; sa.max_len = INT_MAX; sa.kda = 1;
+  // every sequence token by token (conv, norms and the recurrence in one pass),
+  // then the new conv states once every reader of the old ones is enqueued
+  hipError_t e = timed(K_TOKEN, st, [&] { return gdn::launch_recurrent(sa, desc->head_k_dim, desc->head_v_dim, bf16, st); });
+  if (e != hipSuccess) return fail(GDN_EHIP, "token path launch: %s", hipGetErrorString(e));
+  if (W > 1) {
+    gdn::TailArgs ta{};
+    ta.x = x; ta.cu = cu_seqlens; ta.read_idx = read_idx; ta.write_idx = write_idx;
+    ta.conv_pool = reinterpret_cast<char*>(conv_pool); ta.conv_stride = conv_block_stride;
+    ta.num_seqs = num_seqs; ta.num_blocks = num_blocks; ta.channels = C;
+    ta.max_len = INT_MAX;
+    e = timed(K_TAIL, st, [&] { return gdn::launch_tail_commit(ta, W, bf16, st); });
+    if (e != hipSuccess) return fail(GDN_EHIP, "conv state commit launch: %s", hipGetErrorString(e));
+  }
+  return GDN_OK;
+}

@@ -120,6 +120,7 @@ struct ScanArgs {
   void* out;
   int num_seqs, num_blocks, num_k_heads, num_v_heads, channels;
   int min_len, max_len;  // only sequences with min_len <= L <= max_len
+  int kda;               // token path: g is [T][H_v][d_k], a decay per key channel (Kimi delta attention)
 };
 
 // Sequences of the chunked launch, longest first (one workgroup row per entry).

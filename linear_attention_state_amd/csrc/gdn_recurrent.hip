@@ -5,6 +5,10 @@
 // head stored [d_k][d_v] with d_v fastest, carried per request in its block
 // (page "Continuous batching for linear attention layers", PR description):
 //     S_t = a_t (I - b_t k_t k_t^T) S_{t-1} + b_t k_t v_t^T,   o_t = S_t^T q_t.
+// Kimi delta attention (KDA; Kimi Linear technical report, 2025) replaces the
+// scalar a_t by a decay per key channel: S_t = (I - b_t k_t k_t^T) diag(a_t) S_{t-1}
+// + b_t k_t v_t^T; the same pass runs it with each state row's decay folded into
+// k and q (template flag KDA, g then [T][H_v][d_k]).
 // Evaluated in delta form: kS = S^T k, u = b (v - a kS), S <- a S + k u^T, and
 // o = a S_{t-1}^T q + (k.q) u, so one reduction pass over d_k serves both kS and
 // the output.  The kernel also runs the token's causal conv + SiLU for the
@@ -68,7 +72,7 @@ __device__ __forceinline__ float4 f4_fma(float a, float4 x, float4 y) {
   return make_float4(fmaf(a, x.x, y.x), fmaf(a, x.y, y.y), fmaf(a, x.z, y.z), fmaf(a, x.w, y.w));
 }
 
-template <bool BF16, int DK, int DV, int DVS>
+template <bool BF16, int DK, int DV, int DVS, bool KDA>
 __global__ __launch_bounds__(256) void recurrent_kernel(ScanArgs a) {
   constexpr int NT = 256;
   constexpr int C4 = DVS / 4;         // threads across the workgroup's part of a state row
@@ -148,7 +152,15 @@ __global__ __launch_bounds__(256) void recurrent_kernel(ScanArgs a) {
       }
       sy[tid + NT * e] = silu(acc);
     }
-    const float gv = a.g[r * a.num_v_heads + m];
+    // decay: one per value head (gated delta rule), or one per key channel (KDA),
+    // the latter for this thread's state rows
+    const float gv = KDA ? 0.f : a.g[r * a.num_v_heads + m];
+    float ar[RPT];
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+      const int row = rg + RG * i;
+      ar[i] = KDA && row < DK ? __expf(a.g[(r * a.num_v_heads + m) * DK + row]) : 1.f;
+    }
     const float bv = a.beta[r * a.num_v_heads + m];
     __syncthreads();
 
@@ -160,8 +172,9 @@ __global__ __launch_bounds__(256) void recurrent_kernel(ScanArgs a) {
       const int row = rg + RG * i;
       if (row < DK) {
         const float kr = sy[DK + row], qr = sy[row];
-        kS = f4_fma(kr, S[i], kS);
-        Sq = f4_fma(qr, S[i], Sq);
+        // KDA reads the decayed state diag(a) S: the row's decay folded into k and q
+        kS = f4_fma(KDA ? kr * ar[i] : kr, S[i], kS);
+        Sq = f4_fma(KDA ? qr * ar[i] : qr, S[i], Sq);
         kq = fmaf(kr, qr, kq);
         kk = fmaf(kr, kr, kk);
         qq = fmaf(qr, qr, qq);
@@ -203,7 +216,7 @@ __global__ __launch_bounds__(256) void recurrent_kernel(ScanArgs a) {
     // normalisation folded in: k_hat = k / sqrt(|k|^2 + eps), q_hat = q_scale q / sqrt(|q|^2 + eps)
     const float ik = rsqrt_fast(kk + a.eps);
     const float iq = a.q_scale * rsqrt_fast(qq + a.eps);
-    const float av = __expf(gv);
+    const float av = KDA ? 1.f : __expf(gv);  // KDA: already in kS and Sq
     const float4 v = *reinterpret_cast<const float4*>(&sy[2 * DK + c4 * 4]);
     float4 u;
     u.x = bv * (v.x - av * kS.x * ik); u.y = bv * (v.y - av * kS.y * ik);
@@ -213,8 +226,9 @@ __global__ __launch_bounds__(256) void recurrent_kernel(ScanArgs a) {
       const int row = rg + RG * i;
       if (row < DK) {
         const float kr = sy[DK + row] * ik;
-        S[i].x = fmaf(av, S[i].x, kr * u.x); S[i].y = fmaf(av, S[i].y, kr * u.y);
-        S[i].z = fmaf(av, S[i].z, kr * u.z); S[i].w = fmaf(av, S[i].w, kr * u.w);
+        const float dec = KDA ? ar[i] : av;
+        S[i].x = fmaf(dec, S[i].x, kr * u.x); S[i].y = fmaf(dec, S[i].y, kr * u.y);
+        S[i].z = fmaf(dec, S[i].z, kr * u.z); S[i].w = fmaf(dec, S[i].w, kr * u.w);
       }
     }
     if (rg == 0) {
@@ -241,7 +255,10 @@ template <bool BF16, int DK, int DV>
 hipError_t rec_dispatch(const ScanArgs& a, hipStream_t st) {
   constexpr int DVS = DV;
   dim3 grid(a.num_seqs, a.num_v_heads, DV / DVS);
-  hipLaunchKernelGGL((recurrent_kernel<BF16, DK, DV, DVS>), grid, dim3(256), 0, st, a);
+  if (a.kda)
+    hipLaunchKernelGGL((recurrent_kernel<BF16, DK, DV, DVS, true>), grid, dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL((recurrent_kernel<BF16, DK, DV, DVS, false>), grid, dim3(256), 0, st, a);
   return hipGetLastError();
 }
 

@@ -16,7 +16,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 def _declared():
     with open(os.path.join(ROOT, "include", "gdn.h")) as f:
         text = f.read()
-    return sorted(set(re.findall(r"\b((?:gdn|ssd)_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b((?:gdn|ssd|kda)_[a-z_]+)\s*\(", text)))
 
 
 def test_library_exports_every_declared_function():

@@ -1,0 +1,105 @@
+"""GPU parity of the KDA layer (kda_varlen_forward: the gated delta rule with a
+decay per key channel) against the fp64 KDA oracle (oracle/kda_oracle.py),
+through the C ABI.
+
+Bar as for the gated-delta-net layer: outputs and final states per (sequence,
+value head) within relative L2 error 1e-2 in bf16 and 1e-4 in fp32; conv
+states bit-exact; blocks no sequence writes and the trash block untouched.  At
+the decode workload's size the oracle runs on sampled value heads.
+"""
+import numpy as np
+import pytest
+import torch
+
+import linear_attention_state_amd as gdn
+import workloads
+from gpu_util import TOL, rel_l2, to_device
+from oracle import kda_oracle
+
+pytestmark = pytest.mark.gpu
+
+
+def _g(batch, seed):
+    rng = np.random.default_rng(seed)
+    L = batch.layer
+    raw = rng.standard_normal((batch.total_tokens, L.num_v_heads, L.head_k_dim))
+    return torch.tensor(-np.logaddexp(0.0, raw), dtype=torch.float32)
+
+
+def _run(batch, g):
+    d = to_device(batch)
+    L = batch.layer
+    out = torch.full((batch.total_tokens, L.num_v_heads, L.head_v_dim), 7.0, dtype=L.torch_act, device="cuda")
+    gdn.kda_varlen_forward(L, d["x"], d["conv_weight"], g.cuda().contiguous(), d["beta"], d["cu_seqlens"],
+                           batch.cu_seqlens, d["read_idx"], d["write_idx"], d["conv_pool"], d["ssm_pool"], out)
+    torch.cuda.synchronize()
+    return out.cpu(), d["conv_pool"].cpu(), d["ssm_pool"].cpu()
+
+
+def _check(name, batch, g, heads=None):
+    L = batch.layer
+    print("case %s: lengths %s" % (name, batch.lengths[:12]), flush=True)
+    out, cp, sp = _run(batch, g)
+    ro, rcp, rsp = kda_oracle.forward(L, batch.x, batch.conv_weight, g, batch.beta, batch.cu_seqlens,
+                                      batch.read_idx, batch.write_idx, batch.conv_pool, batch.ssm_pool, heads=heads)
+    heads = range(L.num_v_heads) if heads is None else heads
+    cu = batch.cu_seqlens.tolist()
+    worst_o = worst_s = 0.0
+    written = set()
+    for s in range(len(cu) - 1):
+        wb = int(batch.write_idx[s])
+        if wb < 0:
+            assert bool((out[cu[s]:cu[s + 1]].float() == 7.0).all()), "padding rows written"
+            continue
+        written.add(wb)
+        for m in heads:
+            if cu[s + 1] > cu[s]:
+                worst_o = max(worst_o, rel_l2(out[cu[s]:cu[s + 1], m].double().numpy(), ro[cu[s]:cu[s + 1], m]))
+            worst_s = max(worst_s, rel_l2(sp[wb, m].double().numpy(), rsp[wb, m]))
+    assert torch.equal(cp.view(torch.uint8), rcp.view(torch.uint8)), "conv pool differs"
+    for blk in range(batch.ssm_pool.shape[0]):
+        if blk not in written:
+            assert torch.equal(sp[blk], batch.ssm_pool[blk]), "block %d written" % blk
+    tol = TOL[L.act_dtype]
+    print("%s: out %.3e state %.3e" % (name, worst_o, worst_s), flush=True)
+    assert worst_o <= tol and worst_s <= tol, (worst_o, worst_s)
+
+
+def test_bf16_ragged_with_decode_tokens():
+    b = workloads.random_batch(workloads.BIG, [1, 40, 1, 3, 130, 1], seed=61, fresh=[0, 1, 0, 0, 0, 1])
+    _check("bf16-ragged", b, _g(b, 62), heads=[0, 1, 13, 30, 31])
+
+
+def test_fp32_small_layer_all_heads():
+    layer = workloads.Layer(2, 4, 64, 32, 4, "f32")
+    b = workloads.random_batch(layer, [17, 1, 0, 66], seed=63)
+    _check("fp32", b, _g(b, 64))
+
+
+def test_padding_sequence_and_width_two():
+    layer = workloads.Layer(4, 8, 128, 128, 2, "bf16")
+    b = workloads.random_batch(layer, [9, 20, 1], seed=65)
+    b.write_idx[1] = -1
+    _check("padding-W2", b, _g(b, 66))
+
+
+def test_uniform_decay_matches_the_gated_delta_rule_kernels():
+    """A decay equal on every channel gives the gated-delta-net layer: against
+    gdn_varlen_forward (its token path for the decode tokens, the chunk kernel
+    for the rest) within the bar."""
+    from gpu_util import run_gpu
+
+    b = workloads.random_batch(workloads.BIG, [1, 1, 70, 1], seed=67)
+    out, cp, sp = _run(b, kda_oracle.with_scalar_decay(b.g, b.layer.head_k_dim))
+    go, gcp, gsp = run_gpu(b)
+    for s in range(4):
+        rows = slice(int(b.cu_seqlens[s]), int(b.cu_seqlens[s + 1]))
+        assert rel_l2(out[rows].double().numpy(), go[rows].double().numpy()) <= 1e-2
+        wb = int(b.write_idx[s])
+        assert rel_l2(sp[wb].double().numpy(), gsp[wb].double().numpy()) <= 1e-2
+    assert torch.equal(cp.view(torch.uint8), gcp.view(torch.uint8))
+
+
+def test_decode_workload_sampled_heads():
+    b = workloads.config(2)
+    _check("decode", b, _g(b, 68), heads=[0, 17, 31])
