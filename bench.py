@@ -401,7 +401,7 @@ def run_kda_decode(steps: int, warmup: int):
     # the gated-delta-net decode bytes, with g per key channel instead of per head
     work = token_path_bytes(L, b.total_tokens) + b.total_tokens * L.num_v_heads * (L.head_k_dim - 1) * 4
     roof = {"bound": "hbm", "achieved": work / (k_ms * 1e-3) / 1e9, "peak": PEAK_HBM / 1e9, "unit": "GB/s",
-            "kernel": "token_recurrent", "traffic": None}
+            "kernel": "token_recurrent", "traffic": load_traffic("token_recurrent", "kda_decode")}
     roof["frac"] = roof["achieved"] / roof["peak"]
     return {"workload": "KDA decode: 256 sequences of 1 token, H_k=16, H_v=32, d=128, W=4, bf16, "
                         "g per key channel, 1024-block pool",
