@@ -73,7 +73,7 @@ __device__ __forceinline__ float4 f4_fma(float a, float4 x, float4 y) {
 }
 
 template <bool BF16, int DK, int DV, int DVS, bool KDA>
-__global__ __launch_bounds__(256) void recurrent_kernel(ScanArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KDA ? 3 : 1))) void recurrent_kernel(ScanArgs a) {
   constexpr int NT = 256;
   constexpr int C4 = DVS / 4;         // threads across the workgroup's part of a state row
   constexpr int RG = NT / C4;         // row groups
@@ -132,6 +132,7 @@ __global__ __launch_bounds__(256) void recurrent_kernel(ScanArgs a) {
   }
 
   __shared__ __align__(16) float sy[NCH];
+  __shared__ float sdec[KDA ? DK : 1];  // KDA: exp(g) of the token, per key channel
   __shared__ __align__(16) float red[NW][2 * DVS + 4];
 
   for (int t = 0; t < L; ++t) {
@@ -152,15 +153,10 @@ __global__ __launch_bounds__(256) void recurrent_kernel(ScanArgs a) {
       }
       sy[tid + NT * e] = silu(acc);
     }
-    // decay: one per value head (gated delta rule), or one per key channel (KDA),
-    // the latter for this thread's state rows
+    // decay: one per value head (gated delta rule), or one per key channel
+    // (KDA: read once per row into LDS, beside the conv outputs)
     const float gv = KDA ? 0.f : a.g[r * a.num_v_heads + m];
-    float ar[RPT];
-#pragma unroll
-    for (int i = 0; i < RPT; ++i) {
-      const int row = rg + RG * i;
-      ar[i] = KDA && row < DK ? __expf(a.g[(r * a.num_v_heads + m) * DK + row]) : 1.f;
-    }
+    if (KDA && tid < DK) sdec[tid] = __expf(a.g[(r * a.num_v_heads + m) * DK + tid]);
     const float bv = a.beta[r * a.num_v_heads + m];
     __syncthreads();
 
@@ -173,8 +169,9 @@ __global__ __launch_bounds__(256) void recurrent_kernel(ScanArgs a) {
       if (row < DK) {
         const float kr = sy[DK + row], qr = sy[row];
         // KDA reads the decayed state diag(a) S: the row's decay folded into k and q
-        kS = f4_fma(KDA ? kr * ar[i] : kr, S[i], kS);
-        Sq = f4_fma(KDA ? qr * ar[i] : qr, S[i], Sq);
+        const float dr = KDA ? sdec[row] : 1.f;  // read at each use: no registers held for it
+        kS = f4_fma(KDA ? kr * dr : kr, S[i], kS);
+        Sq = f4_fma(KDA ? qr * dr : qr, S[i], Sq);
         kq = fmaf(kr, qr, kq);
         kk = fmaf(kr, kr, kk);
         qq = fmaf(qr, qr, qq);
@@ -226,7 +223,7 @@ __global__ __launch_bounds__(256) void recurrent_kernel(ScanArgs a) {
       const int row = rg + RG * i;
       if (row < DK) {
         const float kr = sy[DK + row] * ik;
-        const float dec = KDA ? ar[i] : av;
+        const float dec = KDA ? sdec[row] : av;
         S[i].x = fmaf(dec, S[i].x, kr * u.x); S[i].y = fmaf(dec, S[i].y, kr * u.y);
         S[i].z = fmaf(dec, S[i].z, kr * u.z); S[i].w = fmaf(dec, S[i].w, kr * u.w);
       }
