@@ -209,3 +209,33 @@ def test_ssd_scan_rejects_bad_arguments(cu, T, kw, status, needle):
 def test_ssd_scan_of_no_sequences_is_ok():
     rc, _ = _ssd_call([0], 0, cuh=None, cu=None, n=0)
     assert rc == gdn.GDN_OK
+
+
+def _kda_call(cu_host, T, **over):
+    """kda_varlen_forward with fake (never dereferenced) device pointers."""
+    lib = gdn.load_library()
+    fake = ctypes.c_void_p(1 << 20)
+    cu = (ctypes.c_int32 * len(cu_host))(*cu_host) if cu_host is not None else None
+    args = dict(x=fake, w=fake, g=fake, b=fake, cu=fake, cuh=cu, n=(len(cu_host) - 1) if cu_host else 1, T=T,
+                ri=fake, wi=fake, conv=fake, cstride=3 * 8192 * 2, ssm=fake, sstride=2 << 20, P=8, out=fake)
+    args.update(over)
+    rc = lib.kda_varlen_forward(ctypes.byref(gdn.make_desc(workloads.BIG)), args["x"], args["w"], args["g"], args["b"],
+                                args["cu"], args["cuh"], args["n"], args["T"], args["ri"], args["wi"], args["conv"],
+                                args["cstride"], args["ssm"], args["sstride"], args["P"], args["out"], None)
+    return rc, gdn.gdn_last_error()
+
+
+@pytest.mark.parametrize("cu,T,over,status,needle", [
+    ([0], 0, {}, gdn.GDN_EINVAL, "no sequences"),
+    (None, 4, {}, gdn.GDN_EINVAL, "cu_seqlens_host"),
+    ([0, 5, 3], 3, {}, gdn.GDN_EINVAL, "decreases"),
+    ([0, 5, 9], 8, {}, gdn.GDN_EINVAL, "total_tokens"),
+    ([0, 4], 4, {"g": None}, gdn.GDN_EINVAL, "non-NULL"),
+    ([0, 4], 4, {"ssm": None}, gdn.GDN_EINVAL, "ssm_pool"),
+    ([0, 4], 4, {"P": 1}, gdn.GDN_EINVAL, "num_blocks"),
+    ([0, 4], 4, {"sstride": (2 << 20) - 16}, gdn.GDN_EINVAL, "ssm_block_stride"),
+    ([0, 4], 4, {"out": ctypes.c_void_p((1 << 20) + 8)}, gdn.GDN_EINVAL, "aligned"),
+])
+def test_kda_forward_rejects_bad_arguments(cu, T, over, status, needle):
+    rc, msg = _kda_call(cu, T, **over)
+    assert rc == status and needle in msg, (rc, msg)
