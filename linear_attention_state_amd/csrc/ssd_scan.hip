@@ -31,17 +31,21 @@ constexpr int SNT = 256;  // threads
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
+// HP heads of one group per workgroup: C and B rows (and C B^T) are shared,
+// the rest is per head.
+template <int HP>
 struct SsdSmem {
-  uint16_t c[SBT * SN];    // C rows [t][n]; 16-byte chunks XOR-swizzled by row
-  uint16_t b[SBT * SN];    // B rows [t][n]
-  uint16_t x[SBT * SP];    // X rows [t][p]
-  uint16_t p[SBT * SBT];   // L o C B^T [t][j], bf16
-  uint16_t y[SBT * SP];    // output rows [t][p], bf16
-  float gam[SBT];          // running sum of d A within the chunk
-  float dd[SBT];           // d_t (0 past the sequence end)
-  float wv[SBT];           // e^{gamma_last - gamma_j} d_j
+  uint16_t c[SBT * SN];        // C rows [t][n]; 16-byte chunks XOR-swizzled by row
+  uint16_t b[SBT * SN];        // B rows [t][n]
+  uint16_t x[HP][SBT * SP];    // X rows [t][p]
+  uint16_t p[HP][SBT * SBT];   // L o C B^T [t][j], bf16
+  uint16_t y[HP][SBT * SP];    // output rows [t][p], bf16
+  float gam[HP][SBT];          // running sum of d A within the chunk
+  float dd[HP][SBT];           // d_t (0 past the sequence end)
+  float wv[HP][SBT];           // e^{gamma_last - gamma_j} d_j
 };
-static_assert(sizeof(SsdSmem) <= 80 * 1024, "two workgroups per CU");
+static_assert(sizeof(SsdSmem<1>) <= 80 * 1024, "two workgroups per CU");
+static_assert(sizeof(SsdSmem<2>) <= 160 * 1024, "LDS");
 
 // Element offsets in the swizzled tiles: 256-byte rows (16 chunks) and 128-byte rows (8 chunks).
 __device__ __forceinline__ int sw256(int row, int col) {
@@ -77,35 +81,45 @@ __device__ __forceinline__ bf16x4 ldtr(const uint16_t* p) {
 
 __device__ __forceinline__ float softplus_f(float v) { return v > 20.f ? v : log1pf(__expf(v)); }
 
-__global__ __launch_bounds__(SNT, 2) void ssd_chunk_kernel(SsdArgs a) {
-  __shared__ SsdSmem sm;
-  const int H = a.num_heads;
-  const int s = blockIdx.x / H;
-  int m = blockIdx.x % H;
-  if (H % 8 == 0) m = (m % 8) * (H / 8) + m / 8;  // heads of a group on one XCD (workgroups go round-robin over 8)
+// HP = 1: 256 threads per (sequence, head), two workgroups per CU.  HP = 2:
+// 512 threads per (sequence, pair of heads of one group): waves 4h..4h+3 own
+// head h; the C and B rows are staged once and each C B^T tile is formed once
+// and masked for both heads.
+template <int HP>
+__global__ __launch_bounds__(SNT * HP, 2 / HP) void ssd_chunk_kernel(SsdArgs a) {
+  constexpr int NTH = SNT * HP;
+  __shared__ SsdSmem<HP> sm;
+  const int H = a.num_heads, HB = H / HP;  // workgroups per sequence
+  const int s = blockIdx.x / HB;
+  int k = blockIdx.x % HB;
+  if (HB % 8 == 0) k = (k % 8) * (HB / 8) + k / 8;  // heads of a group on one XCD (workgroups go round-robin over 8)
   if (s >= a.num_seqs || !seq_active(a.read_idx, a.write_idx, s, a.num_blocks)) return;
-  const int grp = m / (H / a.num_groups);
   const int r0 = a.cu[s], L = a.cu[s + 1] - r0;
   if (r0 < 0 || L < 2 || r0 + L > a.total_tokens) return;  // token kernel: L <= 1; offsets outside the rows
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, i16 = lane & 15;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hh = w >> 2, wl = w & 3, lt = tid & (SNT - 1);  // this wave's head, its wave and thread within the head
+  const int m = HP * k + hh;
+  const int grp = (HP * k) / (H / a.num_groups);
   const float Am = a.A[m], Dm = a.D ? a.D[m] : 0.f, bias = a.dt_bias ? a.dt_bias[m] : 0.f;
 
-  // state: accumulator tile nb holds S[16nb + 4g + r][16w + i16] = h[p][n]
+  // state: accumulator tile nb holds S[16nb + 4g + r][16wl + i16] = h[p][n]
   f32x4 S[8];
   {
     const gptr<const f32x4> src = as_global(reinterpret_cast<const f32x4*>(
-        a.pool + (int64_t)a.read_idx[s] * a.pool_stride + (int64_t)m * SP * SN + (16 * w + i16) * SN));
+        a.pool + (int64_t)a.read_idx[s] * a.pool_stride + (int64_t)m * SP * SN + (16 * wl + i16) * SN));
 #pragma unroll
     for (int nb = 0; nb < 8; ++nb) S[nb] = src[4 * nb + g];
   }
   gptr<f32x4> dst = as_global(reinterpret_cast<f32x4*>(
-      a.pool + (int64_t)a.write_idx[s] * a.pool_stride + (int64_t)m * SP * SN + (16 * w + i16) * SN));
+      a.pool + (int64_t)a.write_idx[s] * a.pool_stride + (int64_t)m * SP * SN + (16 * wl + i16) * SN));
 
   const int nch = (L + SBT - 1) / SBT;
-  // chunk loads: C and B tiles 4 x 16 bytes per thread (16 threads per row),
-  // X 2 x 16 bytes (8 threads per row), d A of row `lane` in wave 0
-  u32x4 rc[4], rb[4], rx[2];
+  // chunk loads: C and B tiles 4/HP x 16 bytes per thread (16 threads per
+  // row), each head's X 2 x 16 bytes (8 threads per row), d A of row `lane`
+  // of each head in its first wave
+  constexpr int NCB = 4 / HP;
+  u32x4 rc[NCB], rb[NCB], rx[2];
   float rdt = 0.f;
   auto load = [&](int c) {
     const int row0 = r0 + c * SBT, nv = min(SBT, L - c * SBT);
@@ -116,36 +130,36 @@ __global__ __launch_bounds__(SNT, 2) void ssd_chunk_kernel(SsdArgs a) {
     const __amdgpu_buffer_rsrc_t xs = make_rsrc(a.x + (int64_t)row0 * a.x_stride + m * SP,
                                                 (uint32_t)(((int64_t)(nv - 1) * a.x_stride + SP) * 2));
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int q = tid + SNT * i, t = q >> 4, cc = q & 15;
+    for (int i = 0; i < NCB; ++i) {
+      const int q = tid + NTH * i, t = q >> 4, cc = q & 15;
       const int off = t < nv ? (int)((t * a.bc_stride + 8 * cc) * 2) : -1;  // rows past the end read 0
       rc[i] = __builtin_amdgcn_raw_buffer_load_b128(cs, (uint32_t)off, 0, 0);
       rb[i] = __builtin_amdgcn_raw_buffer_load_b128(bs, (uint32_t)off, 0, 0);
     }
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      const int q = tid + SNT * i, t = q >> 3, cc = q & 7;
+      const int q = lt + SNT * i, t = q >> 3, cc = q & 7;
       const int off = t < nv ? (int)((t * a.x_stride + 8 * cc) * 2) : -1;
       rx[i] = __builtin_amdgcn_raw_buffer_load_b128(xs, (uint32_t)off, 0, 0);
     }
-    if (w == 0) rdt = lane < nv ? a.dt[(int64_t)(row0 + lane) * H + m] : 0.f;
+    if (wl == 0) rdt = lane < nv ? a.dt[(int64_t)(row0 + lane) * H + m] : 0.f;
   };
   if (nch > 0) load(0);
   for (int c = 0; c < nch; ++c) {
     const int nv = min(SBT, L - c * SBT);
     lds_barrier();  // the previous chunk's LDS reads are done
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int q = tid + SNT * i, t = q >> 4, cc = q & 15;
+    for (int i = 0; i < NCB; ++i) {
+      const int q = tid + NTH * i, t = q >> 4, cc = q & 15;
       *reinterpret_cast<u32x4*>(&sm.c[sw256(t, 8 * cc)]) = rc[i];
       *reinterpret_cast<u32x4*>(&sm.b[sw256(t, 8 * cc)]) = rb[i];
     }
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      const int q = tid + SNT * i, t = q >> 3, cc = q & 7;
-      *reinterpret_cast<u32x4*>(&sm.x[sw128(t, 8 * cc)]) = rx[i];
+      const int q = lt + SNT * i, t = q >> 3, cc = q & 7;
+      *reinterpret_cast<u32x4*>(&sm.x[hh][sw128(t, 8 * cc)]) = rx[i];
     }
-    if (w == 0) {
+    if (wl == 0) {
       float d = 0.f;
       if (lane < nv) d = a.softplus ? softplus_f(rdt + bias) : rdt + bias;
       float v = d * Am;
@@ -155,33 +169,39 @@ __global__ __launch_bounds__(SNT, 2) void ssd_chunk_kernel(SsdArgs a) {
         if (lane >= off) v += u;
       }
       const float last = __shfl(v, 63);
-      sm.gam[lane] = v;
-      sm.dd[lane] = d;
-      sm.wv[lane] = __expf(last - v) * d;
+      sm.gam[hh][lane] = v;
+      sm.dd[hh][lane] = d;
+      sm.wv[hh][lane] = __expf(last - v) * d;
     }
     if (c + 1 < nch) load(c + 1);  // the next chunk's rows stay in flight through this one
     lds_barrier();
 
-    // rows 16w..16w+15 of L o C B^T (blocks right of the diagonal are zero)
+    // rows 16wl..16wl+15 of L o C B^T (blocks right of the diagonal are
+    // zero), computed transposed (B C^T): a lane holds 4 consecutive j of row
+    // t.  With two heads, the waves of head h form the j blocks of parity h
+    // and mask each tile for both heads.
     {
-      // computed transposed (B C^T): a lane holds 4 consecutive j of row t
-      const int t = 16 * w + i16;
-      const float gt = sm.gam[t];
+      const int t = 16 * wl + i16;
 #pragma unroll
-      for (int jb = 0; jb < 4; ++jb) {
+      for (int jj = 0; jj < 4 / HP; ++jj) {
+        const int jb = HP == 1 ? jj : 2 * jj + hh;
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        if (jb <= w) {
+        if (jb <= wl) {
 #pragma unroll
           for (int kk = 0; kk < 4; ++kk)
             acc = mma(ld8(&sm.b[sw256(16 * jb + i16, 32 * kk + 8 * g)]), ld8(&sm.c[sw256(t, 32 * kk + 8 * g)]), acc);
         }
         const int j0 = 16 * jb + 4 * g;
-        const f32x4 gj = *reinterpret_cast<const f32x4*>(&sm.gam[j0]);
-        const f32x4 dj = *reinterpret_cast<const f32x4*>(&sm.dd[j0]);
-        float v[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) v[r] = j0 + r <= t ? acc[r] * __expf(gt - gj[r]) * dj[r] : 0.f;
-        *reinterpret_cast<u32x2*>(&sm.p[sw128(t, j0)]) = pack4(v[0], v[1], v[2], v[3]);
+        for (int e = 0; e < HP; ++e) {
+          const float gt = sm.gam[e][t];
+          const f32x4 gj = *reinterpret_cast<const f32x4*>(&sm.gam[e][j0]);
+          const f32x4 dj = *reinterpret_cast<const f32x4*>(&sm.dd[e][j0]);
+          float v[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) v[r] = j0 + r <= t ? acc[r] * __expf(gt - gj[r]) * dj[r] : 0.f;
+          *reinterpret_cast<u32x2*>(&sm.p[e][sw128(t, j0)]) = pack4(v[0], v[1], v[2], v[3]);
+        }
       }
     }
     // S as the k side of C S, pair order: tiles 2kk and 2kk + 1
@@ -193,17 +213,23 @@ __global__ __launch_bounds__(SNT, 2) void ssd_chunk_kernel(SsdArgs a) {
         sop[kk][e] = (__bf16)S[2 * kk][e];
         sop[kk][4 + e] = (__bf16)S[2 * kk + 1][e];
       }
-    // X as the k side (rows j, column 16w + i16), pair order
+    // X as the k side (rows j, column 16wl + i16), pair order
+    const uint16_t* X = sm.x[hh];
     bf16x8 xop[2];
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
       const int a4 = lane & 3, i4 = (lane >> 2) & 3;
-      xop[kk] = join(ldtr(&sm.x[sw128(32 * kk + 4 * g + i4, 16 * w + 4 * a4)]),
-                     ldtr(&sm.x[sw128(32 * kk + 16 + 4 * g + i4, 16 * w + 4 * a4)]));
+      xop[kk] = join(ldtr(&X[sw128(32 * kk + 4 * g + i4, 16 * wl + 4 * a4)]),
+                     ldtr(&X[sw128(32 * kk + 16 + 4 * g + i4, 16 * wl + 4 * a4)]));
     }
     lds_barrier();  // every row of L o C B^T is written
 
-    // Y[:, 16w..16w+15] = Gamma (C S) + (L o C B^T) X + D X
+    // Y[:, 16wl..16wl+15] = Gamma (C S) + (L o C B^T) X + D X, computed
+    // transposed (S^T C^T + X^T P^T): a lane holds 4 consecutive p of one row t
+    const uint16_t* P = sm.p[hh];
+    uint16_t* Y = sm.y[hh];
+    const float* gam = sm.gam[hh];
+#pragma unroll
     for (int tb = 0; tb < 4; ++tb) {
       f32x4 ys = {0.f, 0.f, 0.f, 0.f}, yp = {0.f, 0.f, 0.f, 0.f};
       const int tr = 16 * tb + i16;
@@ -213,10 +239,9 @@ __global__ __launch_bounds__(SNT, 2) void ssd_chunk_kernel(SsdArgs a) {
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk)
         if (kk <= tb / 2)
-          yp = mma(xop[kk], join(ld4(&sm.p[sw128(tr, 32 * kk + 4 * g)]), ld4(&sm.p[sw128(tr, 32 * kk + 16 + 4 * g)])), yp);
-      // transposed: lane holds y[tr][16w + 4g .. + 3]
-      const u32x2 xr = *reinterpret_cast<const u32x2*>(&sm.x[sw128(tr, 16 * w + 4 * g)]);
-      const float egt = __expf(sm.gam[tr]);
+          yp = mma(xop[kk], join(ld4(&P[sw128(tr, 32 * kk + 4 * g)]), ld4(&P[sw128(tr, 32 * kk + 16 + 4 * g)])), yp);
+      const u32x2 xr = *reinterpret_cast<const u32x2*>(&X[sw128(tr, 16 * wl + 4 * g)]);
+      const float egt = __expf(gam[tr]);
       float yv[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
@@ -224,18 +249,18 @@ __global__ __launch_bounds__(SNT, 2) void ssd_chunk_kernel(SsdArgs a) {
         const float xv = __uint_as_float((r & 1) ? (xw2 & 0xffff0000u) : (xw2 << 16));
         yv[r] = egt * ys[r] + yp[r] + Dm * xv;
       }
-      *reinterpret_cast<u32x2*>(&sm.y[sw128(tr, 16 * w + 4 * g)]) = pack4(yv[0], yv[1], yv[2], yv[3]);
+      *reinterpret_cast<u32x2*>(&Y[sw128(tr, 16 * wl + 4 * g)]) = pack4(yv[0], yv[1], yv[2], yv[3]);
     }
     // S <- Gamma_last S + B^T diag(w) X
     {
-      const float glast = __expf(sm.gam[SBT - 1]);
+      const float glast = __expf(gam[SBT - 1]);
       bf16x8 xw[2];
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const int j = 32 * kk + (e < 4 ? 4 * g + e : 16 + 4 * g + e - 4);
-          xw[kk][e] = (__bf16)((float)xop[kk][e] * sm.wv[j]);
+          xw[kk][e] = (__bf16)((float)xop[kk][e] * sm.wv[hh][j]);
         }
       const int a4 = lane & 3, i4 = (lane >> 2) & 3;
 #pragma unroll
@@ -252,10 +277,10 @@ __global__ __launch_bounds__(SNT, 2) void ssd_chunk_kernel(SsdArgs a) {
     lds_barrier();  // every output row is staged
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      const int q = tid + SNT * i, t = q >> 3, cc = q & 7;
+      const int q = lt + SNT * i, t = q >> 3, cc = q & 7;
       if (t < nv)
         *reinterpret_cast<gptr<u32x4>>(as_global(a.y + ((int64_t)(r0 + c * SBT + t) * H + m) * SP + 8 * cc)) =
-            *reinterpret_cast<const u32x4*>(&sm.y[sw128(t, 8 * cc)]);
+            *reinterpret_cast<const u32x4*>(&Y[sw128(t, 8 * cc)]);
     }
   }
 #pragma unroll
@@ -336,7 +361,10 @@ hipError_t launch_ssd(const SsdArgs& a, hipStream_t st) {
   if (a.num_seqs <= 0 || a.num_heads <= 0) return hipSuccess;
   const int64_t blocks = (int64_t)a.num_seqs * a.num_heads;
   if (blocks > INT32_MAX) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(ssd_chunk_kernel, dim3((unsigned)blocks), dim3(SNT), 0, st, a);
+  if ((a.num_heads / a.num_groups) % 2 == 0)  // pairs of heads of one group share B, C and C B^T
+    hipLaunchKernelGGL(ssd_chunk_kernel<2>, dim3((unsigned)(blocks / 2)), dim3(2 * SNT), 0, st, a);
+  else
+    hipLaunchKernelGGL(ssd_chunk_kernel<1>, dim3((unsigned)blocks), dim3(SNT), 0, st, a);
   return hipGetLastError();
 }
 

@@ -120,6 +120,14 @@ def test_heads_not_a_multiple_of_eight():
     _check("H6", b)
 
 
+def test_odd_heads_per_group():
+    """Three heads per group: the kernel then runs one head per workgroup
+    (pairs of heads share a workgroup only within a group)."""
+    layer = workloads.SsdLayer(6, 64, 2, 128, 4)
+    b = workloads.ssd_batch(layer, [66, 1, 130], seed=18)
+    _check("H6-G2", b)
+
+
 def test_prefill_workload_sampled_heads():
     """8 sequences of 256-4096 tokens on the 128-head layer, oracle on 6 heads of 3 groups."""
     b = workloads.ssd_config(0)
