@@ -18,10 +18,13 @@ that oracle), q and k L2-normalised per head with q scaled, key head
 m // (H_v / H_k), the paged states (block 0 the zero trash block, write blocks
 overwritten in place, write_idx < 0 a padding sequence).
 
-Parity pins (tests/test_oracle_kda_pins.py): a decay equal across the channels
-reduces to the gated-delta-rule oracle; without the delta term (b = 0) the state
-decays row by row in closed form; one token from the trash block; a sequence
-split over two calls.
+Parity pins (tests/test_oracle_kda_pins.py): a hand-worked 2 x 2 example with
+two different channel decays per token (tests/golden/kda_hand.txt), whose first
+key does not commute with the decay, so the order of decay and projection is
+fixed; brute force with the explicit d_k x d_k transition (I - b k k^T)
+diag(exp(g)); a decay equal across the channels reduces to the gated-delta-rule
+oracle; without the delta term (b = 0) the state decays row by row in closed
+form; one token from the trash block; a sequence split over two calls.
 """
 from __future__ import annotations
 

@@ -1,16 +1,23 @@
 """Pins of the KDA oracle (oracle/kda_oracle.py) to facts that do not come from
-it: a decay equal on every channel is the gated delta rule (its own oracle,
-pinned in tests/test_oracle_pins.py); without the delta term the state decays
-row by row in closed form; one token from the trash block has a closed form; a
-sequence split over two calls equals one call.  The recurrence is the published
-KDA one (Kimi Linear technical report, 2025).
+it: a hand-worked 2 x 2 example with two different channel decays per token
+(tests/golden/kda_hand.txt); brute force with the explicit d_k x d_k transition
+matrix (I - b k k^T) diag(exp(g)) for d_k != d_v and decays that differ across
+the channels; a decay equal on every channel is the gated delta rule (its own
+oracle, pinned in tests/test_oracle_pins.py); without the delta term the state
+decays row by row in closed form; one token from the trash block has a closed
+form; a sequence split over two calls equals one call.  The recurrence is the
+published KDA one (Kimi Linear technical report, 2025).
 
-A decay applied to columns instead of rows, applied after the delta term, or
-read one token off, fails one of them.
+A decay applied to columns instead of rows fails the decay-only pin and the
+golden; the decay applied after the projection, diag(a) (I - b k k^T) S, fails
+the golden (token 1) and the brute force, whose keys do not commute with the
+decays; reading o from S_{t-1} fails the golden.
 """
 import math
+import os
 
 import numpy as np
+import pytest
 import torch
 
 import oracle
@@ -18,6 +25,48 @@ import workloads
 from oracle import kda_oracle
 
 LAYER = workloads.Layer(2, 4, 16, 8, 4, "f32")
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _golden(name):
+    rec = {}
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            if line.strip() and not line.startswith("#"):
+                parts = line.split()
+                rec[parts[0]] = np.array([float(v) for v in parts[1:]])
+    return rec
+
+
+def test_hand_worked_example_with_channel_decays():
+    """tests/golden/kda_hand.txt: three tokens, d_k = d_v = 2, worked by hand."""
+    r = _golden("kda_hand.txt")
+    k, v, q = r["k"].reshape(3, 2), r["v"].reshape(3, 2), r["q"].reshape(3, 2)
+    g = np.log(r["a"].reshape(3, 2))
+    o, S = kda_oracle.recurrence(q, k, v, g, r["b"], r["S0"].reshape(2, 2))
+    np.testing.assert_allclose(o, r["o"].reshape(3, 2), rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(S, r["S3"].reshape(2, 2), rtol=1e-12, atol=1e-14)
+
+
+@pytest.mark.parametrize("dk,dv", [(5, 3), (3, 4)])
+def test_brute_force_transition_matrix(dk, dv):
+    """Brute force on tiny inputs: the d_k x d_k transition (I - b k k^T) diag(exp(g_t))
+    built explicitly and multiplied, with decays spread across the channels and
+    keys that are neither unit nor axis-aligned."""
+    rng = np.random.default_rng(40 + dk)
+    L = 8
+    q, k = rng.standard_normal((L, dk)), rng.standard_normal((L, dk))
+    v = rng.standard_normal((L, dv))
+    g = -3.0 * rng.random((L, dk))           # channel decays from 1 down to e^-3
+    b = rng.random(L)
+    S0 = rng.standard_normal((dk, dv))
+    o, S = kda_oracle.recurrence(q, k, v, g, b, S0)
+    Sref = S0.copy()
+    for t in range(L):
+        M = (np.eye(dk) - b[t] * np.outer(k[t], k[t])) @ np.diag(np.exp(g[t]))
+        Sref = M @ Sref + b[t] * np.outer(k[t], v[t])
+        np.testing.assert_allclose(o[t], Sref.T @ q[t], rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(S, Sref, rtol=1e-12, atol=1e-13)
 
 
 def _g_channels(b, seed, spread=1.0):
