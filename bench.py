@@ -7,21 +7,27 @@ state pools) are generated once, copied to HBM before timing, and stay there.
 
 Primary line: the prefill workload (8 sequences, lengths uniform in [256, 4096],
 H_k=16, H_v=32, d_k=d_v=128, W=4, bf16 activations, fp32 state), tokens/s.
-The same JSON line carries the decode workload (256 sequences of one token,
-1024-block pool), the prefill step planned on the device and replayed from a
-HIP graph, the standalone varlen conv layer (gdn_varlen_conv on the prefill
-rows) and the fork copy (gdn_state_copy of 256 blocks) as nested objects, each with the roofline of its dominant
-kernel and the per-kernel event timings, and the fp64 CPU oracle timed on the
-host cores beside them.
+The same JSON line carries, as nested objects, the decode workload (256
+sequences of one token, 1024-block pool), the mixed continuous-batching step
+(64 decode tokens beside 4 prefill chunks of 512 tokens), the long prefill (4
+sequences of 32768 tokens), the prefill step planned on the device and
+replayed from a HIP graph, the standalone varlen conv layer (gdn_varlen_conv on
+the prefill rows), the fork copy (gdn_state_copy of 256 blocks), the KDA decode
+and the Mamba2 scan, each with the roofline of its dominant kernel and the
+per-kernel event timings.  Every gated-delta-net entry also carries the fp64
+CPU oracle timed on the host cores on the same workload (`cpu_baseline`), and
+the parity of its first call (from fresh pools) against that oracle run: max
+relative L2 error over (sequence, value head) slabs and the bit-exact verdicts.
 
     python bench.py [--gpus 1] [--steps 50] [--warmup 50] [--no-cpu-baseline]
 
-The default warm-up is long enough (about 20 ms of GPU work) for the clocks to
-settle: the first few dozen steps after the inputs are uploaded run up to 10%
-slower, and the line reports the steady rate.  The K timed steps run twice:
-once end to end for `value` and `ms_per_step`, once more with the library's
-event pair around every kernel for `kernels` and `roofline` (those events
-add a few percent to a step, so they stay out of the first pass).
+Warm-up runs at least `--warmup` steps and at least 60 ms of back-to-back GPU
+work, so the clocks have settled (the first few dozen steps after the inputs
+are uploaded run up to 10% slower) whatever count is asked for; the line
+reports the count run.  The K timed steps run twice: once end to end for
+`value` and `ms_per_step`, once more with the library's event pair around every
+kernel for `kernels` and `roofline` (those events add a few percent to a step,
+so they stay out of the first pass).
 
 On the prefill workload the chunk kernel also runs the conv of the rows (its
 workgroups convert rows before their scans), so its duration covers both; the
@@ -96,6 +102,31 @@ def load_traffic(kernel: str, workload: str):
     return None
 
 
+def step_bytes(layer, lengths) -> float:
+    """Algorithmic HBM bytes of one whole step of the layer: per token the x row
+    read, the output row written, g and beta read; per sequence its recurrent
+    state and conv state read and written; the conv taps once."""
+    C = layer.conv_channels
+    s = 2 if layer.act_dtype == "bf16" else 4
+    per_tok = C * s + layer.num_v_heads * layer.head_v_dim * s + 2 * layer.num_v_heads * 4
+    per_seq = 2 * (layer.num_v_heads * layer.head_k_dim * layer.head_v_dim * 4 + (layer.conv_width - 1) * C * s)
+    return sum(lengths) * per_tok + len(lengths) * per_seq + C * layer.conv_width * s
+
+
+def warm(step, sync, min_steps: int, min_ms: float = 60.0) -> int:
+    """Runs `step` at least min_steps times and until min_ms of wall time (the
+    GPU busy all along) has passed, so the clocks have settled whatever warm-up
+    count was asked for.  Returns the number of steps run."""
+    n = 0
+    t0 = time.perf_counter()
+    while n < min_steps or (time.perf_counter() - t0) * 1e3 < min_ms:
+        for _ in range(5):
+            step()
+        n += 5
+        sync()
+    return n
+
+
 def run(cfg_id: int, steps: int, warmup: int, placements=()):
     import torch
 
@@ -118,9 +149,13 @@ def run(cfg_id: int, steps: int, warmup: int, placements=()):
                                d["read_idx"], d["write_idx"], d["conv_pool"], d["ssm_pool"], out,
                                workspace=ws, stream=stream.cuda_stream)
 
-    for _ in range(warmup):
-        step()
-    torch.cuda.synchronize()
+    # the first call, from the fresh pools: its results are what the oracle leg
+    # checks (later steps run on the pools this one wrote)
+    gdn.gdn_device_status(clear=True)
+    step()
+    first = (out.cpu(), d["conv_pool"].cpu(), d["ssm_pool"].cpu())
+    status = gdn.gdn_device_status(clear=True)
+    warm_steps = warm(step, torch.cuda.synchronize, warmup)
 
     def timed_steps():
         ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -142,11 +177,13 @@ def run(cfg_id: int, steps: int, warmup: int, placements=()):
     ms_events, _ = timed_steps()
     kt = gdn.gdn_kernel_times()
     gdn.gdn_kernel_timing(False)
+    status |= gdn.gdn_device_status(clear=True)
     kernels = {k: {"avg_ms": v[0] / max(v[1], 1), "launches": v[1]} for k, v in kt.items()}
     dom = max(kernels, key=lambda k: kernels[k]["avg_ms"] * kernels[k]["launches"])
     dom_s = kernels[dom]["avg_ms"] * 1e-3
+    flops = chunk_flops(L, b.lengths)
     if dom == "chunk_scan":
-        work = chunk_flops(L, b.lengths)
+        work = flops
         roof = {"bound": "mfma", "achieved": work / dom_s / 1e12, "peak": PEAK_BF16_MFMA / 1e12,
                 "unit": "TFLOP/s"}
     else:
@@ -158,12 +195,16 @@ def run(cfg_id: int, steps: int, warmup: int, placements=()):
     roof["step_frac"] = roof["achieved"] * dom_s / (ms * 1e-3) / roof["peak"]
     if dom == "chunk_scan" and "conv_silu_norm" not in kernels:
         roof["note"] = "chunk_scan also ran the conv of the rows (no separate conv kernel)"
-    traffic = load_traffic(dom, {1: "prefill", 2: "decode", 4: "long"}.get(cfg_id, ""))
+    traffic = load_traffic(dom, {1: "prefill", 2: "decode", 3: "mixed", 4: "long"}.get(cfg_id, ""))
     roof["traffic"] = traffic
     roof["kernel"] = dom
     res = {
         "batch": b, "ms_per_step": ms, "ms_per_step_with_kernel_events": ms_events, "wall_s": wall, "tokens": T,
-        "value": T * steps / (ms * steps * 1e-3), "kernels": kernels, "roofline": roof,
+        "value": T * steps / (ms * steps * 1e-3), "kernels": kernels, "roofline": roof, "first": first,
+        "warmup_steps_run": warm_steps, "device_status": status,
+        # the whole step against both roofs: every algorithmic byte and chunk flop over the step time
+        "step_hbm_frac": step_bytes(L, b.lengths) / (ms * 1e-3) / PEAK_HBM,
+        "step_mfma_frac": flops / (ms * 1e-3) / PEAK_BF16_MFMA,
     }
     # the same steps with the conv placement forced (GDN_CONV_IN_SCAN), for comparison
     if placements:
@@ -457,9 +498,45 @@ def run_state_copy(steps: int, warmup: int):
             "kernels": {k: {"avg_ms": v[0] / max(v[1], 1), "launches": v[1]} for k, v in kt.items()}}
 
 
-def cpu_baseline(batch):
-    """The fp64 oracle on the host cores, on the same workload (all of it when
-    it takes under half a minute), tokens/s."""
+def first_call_parity(batch, first, ref) -> dict:
+    """The first call's results (from fresh pools) against the oracle's: max
+    relative L2 error over (sequence, value head) slabs of outputs and final
+    states, and the bit-exact verdicts (conv pool, blocks no sequence writes,
+    the trash block)."""
+    import numpy as np
+    import torch
+
+    out_g, cp_g, sp_g = first
+    out_r, fin_r, cp_r, _ = ref
+    cu = batch.cu_seqlens.tolist()
+    worst_o = worst_s = 0.0
+    for s in range(len(cu) - 1):
+        wb = int(batch.write_idx[s])
+        if wb < 0:
+            continue
+        og = out_g[cu[s]:cu[s + 1]].double().numpy()
+        for m in range(batch.layer.num_v_heads):
+            if cu[s + 1] > cu[s]:
+                r = out_r[cu[s]:cu[s + 1], m]
+                worst_o = max(worst_o, float(np.linalg.norm(og[:, m] - r) / max(np.linalg.norm(r), 1e-300)))
+            r = fin_r[s, m]
+            e = sp_g[wb, m].double().numpy() - r
+            worst_s = max(worst_s, float(np.linalg.norm(e) / max(np.linalg.norm(r), 1e-300)))
+    written = set(int(v) for v in batch.write_idx.tolist() if v >= 0)
+    idx = torch.tensor([b for b in range(batch.ssm_pool.shape[0]) if b not in written], dtype=torch.long)
+    conv_exact = bool(torch.equal(cp_g.view(torch.uint8) if cp_g.numel() else cp_g,
+                                  cp_r.view(torch.uint8) if cp_r.numel() else cp_r))
+    return {"out_max_rel_l2": worst_o, "state_max_rel_l2": worst_s,
+            "tolerance": 1e-2 if batch.layer.act_dtype == "bf16" else 1e-4,
+            "conv_pool_bit_exact": conv_exact,
+            "unwritten_blocks_bit_exact": bool(torch.equal(sp_g[idx], batch.ssm_pool[idx])),
+            "trash_block_zero": not bool(sp_g[0].any())}
+
+
+def cpu_baseline(batch, first=None):
+    """The fp64 oracle on the host cores, on the same workload (all of it: it
+    takes from under a second to about 15 s), tokens/s.  With the first GPU
+    call's results, the same oracle run also gives that call's parity."""
     import oracle
 
     threads = len(os.sched_getaffinity(0))
@@ -467,12 +544,15 @@ def cpu_baseline(batch):
     if omp and omp.isdigit():
         threads = min(threads, int(omp))
     t0 = time.perf_counter()
-    oracle.forward(batch.layer, batch.x, batch.conv_weight, batch.g, batch.beta, batch.cu_seqlens,
-                   batch.read_idx, batch.write_idx, batch.conv_pool, batch.ssm_pool, threads=threads)
+    ref = oracle.forward(batch.layer, batch.x, batch.conv_weight, batch.g, batch.beta, batch.cu_seqlens,
+                         batch.read_idx, batch.write_idx, batch.conv_pool, batch.ssm_pool, threads=threads)
     dt = time.perf_counter() - t0
-    return {"value": batch.total_tokens / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": "the whole workload (%d tokens, %d sequences), %.1f s" % (batch.total_tokens,
-                                                                              len(batch.lengths), dt)}
+    res = {"value": batch.total_tokens / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+           "sample": "the whole workload (%d tokens, %d sequences), %.1f s" % (batch.total_tokens,
+                                                                             len(batch.lengths), dt)}
+    if first is not None:
+        res["first_call_parity"] = first_call_parity(batch, first, ref)
+    return res
 
 
 def main():
@@ -485,7 +565,7 @@ def main():
     ap.add_argument("--no-conv", action="store_true", help="skip the standalone conv layer and fork copy entries")
     ap.add_argument("--no-long", action="store_true", help="skip the long-prefill entry (4 x 32768 tokens)")
     ap.add_argument("--no-mamba2", action="store_true", help="skip the Mamba2 scan entries")
-    ap.add_argument("--only", choices=["prefill", "decode", "conv", "copy", "graph", "long", "mamba2_prefill",
+    ap.add_argument("--only", choices=["prefill", "decode", "mixed", "conv", "copy", "graph", "long", "mamba2_prefill",
                                        "mamba2_decode", "kda_decode"], default=None,
                     help="run one workload alone and print its numbers (profiling runs)")
     ap.add_argument("--copy-bytes", type=int, default=0,
@@ -520,11 +600,22 @@ def main():
     if args.only == "graph":
         print(json.dumps(run_graph(args.steps, args.warmup)), flush=True)
         return
-    if args.only:
-        r = run({"prefill": 1, "decode": 2, "long": 4}[args.only], args.steps, args.warmup)
+    if args.only in ("prefill", "decode", "mixed", "long"):
+        r = run({"prefill": 1, "decode": 2, "mixed": 3, "long": 4}[args.only], args.steps, args.warmup)
         print(json.dumps({"workload": args.only, "value": r["value"], "ms_per_step": r["ms_per_step"],
                           "roofline": r["roofline"], "kernels": r["kernels"]}), flush=True)
         return
+
+    def entry(r, what, cpu=True):
+        """A nested entry of the line for one GDN workload run by `run`."""
+        e = {"workload": what, "value": r["value"], "unit": "tokens/s", "ms_per_step": r["ms_per_step"],
+             "roofline": r["roofline"], "step_hbm_frac": r["step_hbm_frac"], "step_mfma_frac": r["step_mfma_frac"],
+             "kernels": r["kernels"], "warmup_steps_run": r["warmup_steps_run"],
+             "device_status": r["device_status"]}
+        if cpu and not args.no_cpu_baseline:
+            e["cpu_baseline"] = cpu_baseline(r["batch"], r["first"])
+        return e
+
     pre = run(1, args.steps, args.warmup)
     b = pre["batch"]
     line = {
@@ -535,24 +626,27 @@ def main():
                                "C=8192; bf16 activations, fp32 state; all from the trash block"
                                % (len(b.lengths), b.lengths, b.total_tokens),
                    "global_batch": len(b.lengths), "seq_len": max(b.lengths), "tokens": b.total_tokens},
-        "roofline": pre["roofline"], "kernels": pre["kernels"],
+        "roofline": pre["roofline"], "kernels": pre["kernels"], "warmup_steps_run": pre["warmup_steps_run"],
+        "step_hbm_frac": pre["step_hbm_frac"], "device_status": pre["device_status"],
     }
     if not args.no_decode:
         dec = run(2, args.steps, args.warmup)
-        line["decode"] = {"workload": "decode: 256 sequences of 1 token, 1024-block pool of 2 MiB fp32 states",
-                          "value": dec["value"], "unit": "tokens/s", "ms_per_step": dec["ms_per_step"],
-                          "roofline": dec["roofline"], "kernels": dec["kernels"]}
+        line["decode"] = entry(dec, "decode: 256 sequences of 1 token, 1024-block pool of 2 MiB fp32 states")
         del dec
+        mix = run(3, args.steps, args.warmup)
+        line["mixed"] = entry(mix, "mixed continuous-batching step: 64 decode tokens and 4 prefill chunks of 512 "
+                                   "tokens (2 continuing, 2 from the trash block) in seeded order, T=2112, "
+                                   "512-block pool; same layer")
+        del mix
     if not args.no_long:
         lp = run(4, args.steps, args.warmup, placements=("never", "always"))
         lp_note = ("conv streamed by helper workgroups inside chunk_scan"
                    if "conv_silu_norm" not in lp["kernels"] else "separate conv kernel")
-        line["long_prefill"] = {
-            "workload": "long prefill: 4 sequences of 32768 tokens, all continuing from their blocks; same layer",
-            "value": lp["value"], "unit": "tokens/s", "ms_per_step": lp["ms_per_step"], "placement": lp_note,
-            "ms_per_step_conv_kernel_first": lp["ms_per_step_forced"]["never"],
-            "ms_per_step_phased": lp["ms_per_step_forced"]["always"],
-            "roofline": lp["roofline"], "kernels": lp["kernels"]}
+        line["long_prefill"] = entry(
+            lp, "long prefill: 4 sequences of 32768 tokens, all continuing from their blocks; same layer")
+        line["long_prefill"]["placement"] = lp_note
+        line["long_prefill"]["ms_per_step_conv_kernel_first"] = lp["ms_per_step_forced"]["never"]
+        line["long_prefill"]["ms_per_step_phased"] = lp["ms_per_step_forced"]["always"]
         del lp
     if not args.no_conv:
         line["prefill_graph"] = run_graph(args.steps, args.warmup)
@@ -563,7 +657,7 @@ def main():
         line["mamba2_prefill"] = run_ssd(0, args.steps, args.warmup)
         line["mamba2_decode"] = run_ssd(1, args.steps, args.warmup)
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(b)
+        line["cpu_baseline"] = cpu_baseline(b, pre["first"])
     print(json.dumps(line), flush=True)
 
 

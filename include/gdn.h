@@ -48,7 +48,8 @@ typedef enum {
   GDN_EINVAL = -1,        /* an argument is invalid (null, inconsistent, out of range) */
   GDN_EUNSUPPORTED = -2,  /* valid, but a shape or dtype this build does not run */
   GDN_EWORKSPACE = -3,    /* workspace missing or smaller than gdn_workspace_size() */
-  GDN_EHIP = -4           /* the HIP runtime reported an error (message has its text) */
+  GDN_EHIP = -4,          /* the HIP runtime reported an error (message has its text) */
+  GDN_EDEVICE = -5        /* gdn_device_status only: a kernel raised a device-side status bit */
 } gdn_status;
 
 typedef enum { GDN_F32 = 0, GDN_BF16 = 1 } gdn_dtype;
@@ -126,15 +127,17 @@ int gdn_workspace_size(const gdn_layer_desc* desc, int32_t total_tokens,
  *                the host plan.
  * Preconditions the library cannot check without a sync (violations give
  * undefined results, never out-of-bounds accesses for indices outside [0, P),
- * which are skipped): device cu_seqlens equals cu_seqlens_host; write blocks are
+ * which are skipped and raise GDN_DEV_BAD_INDEX, see gdn_device_status): device
+ * cu_seqlens equals cu_seqlens_host; write blocks are
  * distinct, never block 0 and never another sequence's read block; block 0 is
  * all zero.  read_idx[i] == write_idx[i] is the ordinary in-place continue.
  * stream is a hipStream_t (NULL = the default stream).
  *
  * Launch plan: the conv of the chunked rows runs in its own kernel, inside the
  * chunk kernel before the scans, or (host plan only, when the scans leave at
- * least 32 CUs free) streamed by helper workgroups of a cooperative chunk
- * kernel while the scans run; a time model chooses.  The environment variable
+ * least 32 CUs free) streamed by helper workgroups of the chunk kernel while
+ * the scans run (the first workgroups to start become the helpers, so no scan
+ * waits for a workgroup that has not started); a time model chooses.  The environment variable
  * GDN_CONV_IN_SCAN=never|always|stream (read at every call) overrides the
  * choice ("stream" falls back to the others where it cannot run).  Every
  * output and state is the same bit for bit in all three.
@@ -260,6 +263,25 @@ int ssd_varlen_scan(const ssd_layer_desc* desc, const void* x, int64_t x_row_str
 
 /* Message of the last non-OK status returned on this thread ("" if none). */
 const char* gdn_last_error(void);
+
+/* Device-side status of the current device.  Some failures happen where no
+ * return value can carry them, so the kernels of every entry point raise
+ * sticky bits instead:
+ *   GDN_DEV_WAIT_EXPIRED  a bounded wait between the waves or workgroups of a
+ *       kernel gave up (no kernel can hang, but the outputs and states of that
+ *       call are then not valid);
+ *   GDN_DEV_BAD_INDEX  a device-resident read or write block outside [0, P)
+ *       was skipped (a negative write block marks padding and raises nothing);
+ *       the page's allocator commit likewise refuses bad states with a readable
+ *       error rather than running on them.
+ * The call waits for `stream` (a host sync: a check for tests and debugging,
+ * not for the step itself), then reads the bits raised since the last clear
+ * into *bits (may be NULL); clear != 0 resets them.  Returns GDN_OK when no bit
+ * is set, GDN_EDEVICE with a message naming them otherwise, GDN_EHIP when the
+ * device could not be read. */
+#define GDN_DEV_WAIT_EXPIRED 1u
+#define GDN_DEV_BAD_INDEX 2u
+int gdn_device_status(int clear, uint32_t* bits, void* stream);
 
 /* Measurement support (not needed to run the layer).
  * gdn_kernel_timing(1) makes every later gdn_varlen_forward, gdn_varlen_conv,

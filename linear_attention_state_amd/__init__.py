@@ -14,10 +14,11 @@ import os
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "_lib", "libgdn.so")
 
-GDN_OK, GDN_EINVAL, GDN_EUNSUPPORTED, GDN_EWORKSPACE, GDN_EHIP = 0, -1, -2, -3, -4
+GDN_OK, GDN_EINVAL, GDN_EUNSUPPORTED, GDN_EWORKSPACE, GDN_EHIP, GDN_EDEVICE = 0, -1, -2, -3, -4, -5
 GDN_F32, GDN_BF16 = 0, 1
+GDN_DEV_WAIT_EXPIRED, GDN_DEV_BAD_INDEX = 1, 2
 EXPORTS = ("gdn_state_spec", "gdn_workspace_size", "gdn_varlen_forward", "gdn_varlen_conv", "gdn_state_copy",
-           "ssd_varlen_scan", "kda_varlen_forward", "gdn_last_error",
+           "ssd_varlen_scan", "kda_varlen_forward", "gdn_last_error", "gdn_device_status",
            "gdn_kernel_timing", "gdn_kernel_times")
 
 _lib = None
@@ -104,6 +105,8 @@ def load_library():
         lib.ssd_varlen_scan.argtypes = [
             ctypes.POINTER(ssd_layer_desc), P, ctypes.c_int64, P, P, ctypes.c_int64, P, P, P, P, P, P,
             ctypes.c_int32, ctypes.c_int32, P, P, P, ctypes.c_int64, ctypes.c_int32, P, P]
+        lib.gdn_device_status.restype = ctypes.c_int
+        lib.gdn_device_status.argtypes = [ctypes.c_int, ctypes.POINTER(ctypes.c_uint32), P]
         lib.gdn_kernel_timing.restype = ctypes.c_int
         lib.gdn_kernel_timing.argtypes = [ctypes.c_int]
         lib.gdn_kernel_times.restype = ctypes.c_int
@@ -321,6 +324,22 @@ def ssd_varlen_scan(layer, x, B, C, dt, A, cu_seqlens, cu_seqlens_host, read_idx
         host, n, T, _dev_ptr(read_idx, "read_idx"), _dev_ptr(write_idx, "write_idx"), _dev_ptr(ssm_pool, "ssm_pool"),
         ssm_pool.stride(0) * ssm_pool.element_size(), int(ssm_pool.shape[0]), _dev_ptr(y, "y"),
         ctypes.c_void_p(stream)))
+
+
+def gdn_device_status(clear: bool = True, stream=None) -> int:
+    """The device-side status bits raised since the last clear (0 when none;
+    GDN_DEV_WAIT_EXPIRED, GDN_DEV_BAD_INDEX).  Waits for ``stream`` (default:
+    torch's current stream) first.  Does not raise for set bits: the caller
+    decides what they mean for its test."""
+    import torch
+
+    if stream is None:
+        stream = torch.cuda.current_stream().cuda_stream
+    bits = ctypes.c_uint32(0)
+    rc = load_library().gdn_device_status(int(bool(clear)), ctypes.byref(bits), ctypes.c_void_p(stream))
+    if rc not in (GDN_OK, GDN_EDEVICE):
+        _check(rc)
+    return int(bits.value)
 
 
 def gdn_kernel_timing(enable: bool) -> None:

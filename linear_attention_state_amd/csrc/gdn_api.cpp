@@ -279,6 +279,21 @@ extern "C" int gdn_workspace_size(const gdn_layer_desc* desc, int32_t total_toke
 
 extern "C" const char* gdn_last_error(void) { return g_last_error.c_str(); }
 
+extern "C" int gdn_device_status(int clear, uint32_t* bits, void* stream) {
+  hipError_t e = hipStreamSynchronize(reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(GDN_EHIP, "device status: %s", hipGetErrorString(e));
+  uint32_t v = 0;
+  for (auto fn : {gdn::status_chunk, gdn::status_conv, gdn::status_recurrent, gdn::status_ssd}) {
+    e = fn(&v, clear);
+    if (e != hipSuccess) return fail(GDN_EHIP, "device status: %s", hipGetErrorString(e));
+  }
+  if (bits) *bits = v;
+  if (!v) return GDN_OK;
+  return fail(GDN_EDEVICE, "device status 0x%x:%s%s", v,
+              (v & GDN_DEV_WAIT_EXPIRED) ? " a bounded wait gave up (that call's results are not valid);" : "",
+              (v & GDN_DEV_BAD_INDEX) ? " a state block index outside the pool was skipped;" : "");
+}
+
 extern "C" int gdn_varlen_forward(const gdn_layer_desc* desc, const void* x, const void* conv_weight,
                                   const float* g, const float* beta, const int32_t* cu_seqlens,
                                   const int32_t* cu_seqlens_host, int32_t num_seqs, int32_t total_tokens,
@@ -481,7 +496,7 @@ extern "C" int gdn_varlen_forward(const gdn_layer_desc* desc, const void* x, con
       // streaming: spare CUs run helper workgroups that convert rows just
       // ahead of the scans, which all start at once; it ends when both the
       // longest scan and the helpers' share of the conv are done
-      const int helpers = cus - (int)wgs;
+      const int helpers = (cus - (int)wgs) / 8 * 8;  // a multiple of the 8 XCDs
       const bool stream_ok = helpers >= 32 && mode != 1;
       const double helper_task_us = task_us * kTaskBytesPerUs / kHelperBytesPerUs;
       const double streamed = std::max(kStreamScanScale * (scan0 + kScanPlainUs * chunks0) + kStreamStartUs,
@@ -511,21 +526,11 @@ extern "C" int gdn_varlen_forward(const gdn_layer_desc* desc, const void* x, con
       e = timed(K_CONV, st, [&] { return gdn::launch_conv(ca, W, bf16, true, st); });
       if (e != hipSuccess) return fail(GDN_EHIP, "conv launch: %s", hipGetErrorString(e));
     } else {
-      const int counters = fc.stream ? 1 + fc.first[fc.n] : 1 + fc.n;
+      const int counters = fc.stream ? 2 + fc.first[fc.n] : 1 + fc.n;  // streaming: + the role ticket
       e = timed(K_ZERO, st, [&] { return gdn::launch_zero_sync(fc.sync, counters, st); });
       if (e != hipSuccess) return fail(GDN_EHIP, "counter reset launch: %s", hipGetErrorString(e));
     }
     e = timed(K_CHUNK, st, [&] { return gdn::launch_chunk(sa, order, fc, desc->head_k_dim, desc->head_v_dim, st); });
-    if (e != hipSuccess && fc.stream) {
-      // the cooperative launch was refused (not every workgroup could be
-      // resident): the conv kernel first, then the plain scan
-      (void)hipGetLastError();
-      fc.n = 0;
-      fc.stream = 0;
-      e = timed(K_CONV, st, [&] { return gdn::launch_conv(ca, W, bf16, true, st); });
-      if (e != hipSuccess) return fail(GDN_EHIP, "conv launch: %s", hipGetErrorString(e));
-      e = timed(K_CHUNK, st, [&] { return gdn::launch_chunk(sa, order, fc, desc->head_k_dim, desc->head_v_dim, st); });
-    }
     if (e != hipSuccess) return fail(GDN_EHIP, "chunk scan launch: %s", hipGetErrorString(e));
     tails_done = fc.n > 0;
   }

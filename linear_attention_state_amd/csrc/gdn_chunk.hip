@@ -382,13 +382,16 @@ __device__ __forceinline__ void set_flag(int* flag, int v) {
   *(volatile lds_int*)(flag) = v;
 }
 // Waits until the flag reaches `target`.  The wait is bounded (about 2^20
-// polls), so a kernel can never hang on it.
+// polls), so a kernel can never hang on it; a wait that gives up raises
+// kStatusWaitExpired (the call's results are then not valid).
 __device__ __forceinline__ void wait_flag(const int* flag, int target) {
-  for (int n = 0; n < (1 << 20); ++n) {
+  bool done = false;
+  for (int n = 0; n < (1 << 20) && !done; ++n) {
     const int v = __builtin_amdgcn_readfirstlane(*(const volatile lds_int*)(flag));
-    if (v >= target) break;
-    __builtin_amdgcn_s_sleep(1);
+    done = v >= target;
+    if (!done) __builtin_amdgcn_s_sleep(1);
   }
+  if (!done && (threadIdx.x & 63) == 0) raise_status(kStatusWaitExpired);
   asm volatile("" ::: "memory");
 }
 
@@ -690,11 +693,13 @@ __device__ __forceinline__ void state_role(Smem& sm, float* sst, const ScanArgs&
 
 // ---- wave 4: A for chunk i + 2, its diagonal blocks published first
 // Streaming: waits until every conv task of chunk c of `rank` is counted
-// (bounded: the tasks are run by helper workgroups that never wait, all
-// resident under the cooperative launch).  Chunk c's rows were never read
-// before in this kernel (scans read a chunk only after this wait, helpers never
-// read y), so no cache can hold a stale copy of them: no invalidation needed.
-// Returns the first chunk from c on that is not known to be converted.
+// (bounded: the tasks are run by helper workgroups that never wait, and every
+// helper has started before any scan, see chunk_scan_kernel).  After a
+// successful poll an agent-scope acquire fence drops any stale copy of the
+// rows from this CU's caches (a workspace reused from an earlier call may
+// still be cached from that call).  A wait that gives up raises
+// kStatusWaitExpired.  Returns the first chunk from c on that is not known to
+// be converted.
 __device__ __forceinline__ int stream_wait(const FusedConv& fc, int rank, int L, int c, int upto, int lane) {
   const int32_t* ready = fc.sync + 1 + fc.first[rank];
   if (c < upto) return upto;
@@ -707,11 +712,12 @@ __device__ __forceinline__ int stream_wait(const FusedConv& fc, int rank, int L,
     const bool ok = !mine || __hip_atomic_load(&ready[cc], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= want;
     const uint64_t late = __ballot(!ok);
     if (!(late & 1)) {
-      asm volatile("" ::: "memory");
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
       return c + (late ? __builtin_ctzll(late) : 64);
     }
     __builtin_amdgcn_s_sleep(1);
   }
+  if (lane == 0) raise_status(kStatusWaitExpired);
   return c + 1;
 }
 
@@ -1128,10 +1134,12 @@ template <bool DP>
 __device__ __forceinline__ void conv_wait(const FusedConv& fc, int rank) {
   if (threadIdx.x == 0) {
     const int need = plan_first<DP>(fc, rank + 1) - plan_first<DP>(fc, rank);
-    for (int it = 0; it < (1 << 24); ++it) {
-      if (__hip_atomic_load(&fc.sync[1 + rank], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= need) break;
-      __builtin_amdgcn_s_sleep(2);
+    bool done = false;
+    for (int it = 0; it < (1 << 24) && !done; ++it) {
+      done = __hip_atomic_load(&fc.sync[1 + rank], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= need;
+      if (!done) __builtin_amdgcn_s_sleep(2);
     }
+    if (!done) raise_status(kStatusWaitExpired);
   }
   __syncthreads();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
@@ -1392,18 +1400,29 @@ template <bool DP, bool STREAM>
 __global__ __launch_bounds__(NT) void chunk_scan_kernel(ScanArgs a, SeqOrder ord, FusedConv fc) {
   __shared__ Smem sm;
   const int Hv = a.num_v_heads;
-  const int rank = blockIdx.x / Hv;
+  int bid = blockIdx.x;
   if constexpr (STREAM) {
-    if (rank >= fc.n) {  // a helper
+    // Roles by arrival: the first fc.helpers workgroups to start take a ticket
+    // below fc.helpers and convert rows; the later ones scan.  So every helper
+    // has started before any scan waits for converted rows, and the waits end
+    // without any assumption about which workgroups are resident together.
+    if (threadIdx.x == 0)
+      sm.task = __hip_atomic_fetch_add(fc.sync + 1 + fc.first[fc.n], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    bid = sm.task;
+    __syncthreads();  // read before a helper overwrites it
+    if (bid < fc.helpers) {
       stream_helper_w(sm, a, ord, fc);
       return;
     }
+    bid -= fc.helpers;
   }
+  const int rank = bid / Hv;
   Seq q;
-  q.m = blockIdx.x % Hv;
+  q.m = bid % Hv;
   const int n_ord = plan_n<DP>(ord, fc);
   const int fused_n = STREAM ? 0 : plan_fused_n<DP>(fc);  // 0, or every rank of the launch order (phased conv)
-  const bool lead_wg = (int)(blockIdx.x % Hv) == 0;
+  const bool lead_wg = q.m == 0;
   if (DP && rank >= n_ord) return;  // device plan: the grid covers every sequence
   q.s = n_ord > 0 ? (rank < n_ord ? plan_seq<DP>(ord, fc, rank) : a.num_seqs) : rank;
   if (fused_n > 0) {
@@ -1521,20 +1540,19 @@ hipError_t launch_chunk(const ScanArgs& a, const SeqOrder& order, const FusedCon
   if (fc.plan && (fc.plan_seqs != a.num_seqs || !fc.sync || a.width < 1 || a.width > 4)) return hipErrorInvalidValue;
   const int rows = fc.plan ? a.num_seqs : order.n > 0 ? order.n : a.num_seqs;
   if (fc.stream) {
-    // every workgroup must be resident at once: scans wait for helpers
+    // scans wait for helpers; roles go by arrival order (a ticket), so a plain
+    // launch is enough: no workgroup waits for one that has not started
     if (fc.plan || fc.n != order.n || fc.n < 1 || fc.helpers < 1 || !fc.sync) return hipErrorInvalidValue;
     const int blocks = fc.n * a.num_v_heads + fc.helpers;
-    ScanArgs aa = a;
-    SeqOrder oo = order;
-    FusedConv ff = fc;
-    void* args[] = {&aa, &oo, &ff};
-    return hipLaunchCooperativeKernel(reinterpret_cast<const void*>(chunk_scan_kernel<false, true>), dim3(blocks),
-                                      dim3(NT), args, 0, st);
+    hipLaunchKernelGGL((chunk_scan_kernel<false, true>), dim3(blocks), dim3(NT), 0, st, a, order, fc);
+    return hipGetLastError();
   }
   dim3 grid(rows * a.num_v_heads);
   if (fc.plan) hipLaunchKernelGGL((chunk_scan_kernel<true, false>), grid, dim3(NT), 0, st, a, order, fc);
   else hipLaunchKernelGGL((chunk_scan_kernel<false, false>), grid, dim3(NT), 0, st, a, order, fc);
   return hipGetLastError();
 }
+
+GDN_STATUS_ACCESSOR(status_chunk)
 
 }  // namespace gdn

@@ -350,4 +350,6 @@ hipError_t launch_state_copy(const StateCopyArgs& a, int n, hipStream_t st) {
   return hipGetLastError();
 }
 
+GDN_STATUS_ACCESSOR(status_conv)
+
 }  // namespace gdn

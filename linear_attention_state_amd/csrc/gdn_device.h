@@ -58,12 +58,41 @@ __device__ __forceinline__ float silu(float v) { return v * __builtin_amdgcn_rcp
 // 1 / sqrt(x) with the hardware reciprocal square root (about 1 ulp), x > 0.
 __device__ __forceinline__ float rsqrt_fast(float x) { return __builtin_amdgcn_rsqf(x); }
 
+// Sticky status bits raised by the kernels (read and cleared by
+// gdn_device_status through the accessor each HIP source defines with
+// GDN_STATUS_ACCESSOR; every source has its own word, the query ORs them).
+constexpr uint32_t kStatusWaitExpired = 1u;  // a bounded wait between waves or workgroups gave up
+constexpr uint32_t kStatusBadIndex = 2u;     // a read or write block outside the pool was skipped
+static __device__ uint32_t g_status;
+__device__ __forceinline__ void raise_status(uint32_t bit) {
+  __hip_atomic_fetch_or(&g_status, bit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+#define GDN_STATUS_ACCESSOR(fn)                                                                      \
+  hipError_t fn(uint32_t* bits, int clear) {                                                         \
+    uint32_t v = 0;                                                                                  \
+    hipError_t e = hipMemcpyFromSymbol(&v, HIP_SYMBOL(g_status), sizeof(v), 0, hipMemcpyDeviceToHost); \
+    if (e == hipSuccess && clear && v) {                                                             \
+      const uint32_t z = 0;                                                                          \
+      e = hipMemcpyToSymbol(HIP_SYMBOL(g_status), &z, sizeof(z), 0, hipMemcpyHostToDevice);          \
+    }                                                                                                \
+    *bits |= v;                                                                                      \
+    return e;                                                                                        \
+  }
+hipError_t status_chunk(uint32_t* bits, int clear);
+hipError_t status_conv(uint32_t* bits, int clear);
+hipError_t status_recurrent(uint32_t* bits, int clear);
+hipError_t status_ssd(uint32_t* bits, int clear);
+
 // A sequence takes part in a call when it has a write block inside the pool and
-// a read block inside the pool; anything else is skipped without memory access.
+// a read block inside the pool; anything else is skipped without memory access
+// (a negative write block is a padding sequence; any other index outside the
+// pool raises kStatusBadIndex).
 __device__ __forceinline__ bool seq_active(const int32_t* read_idx, const int32_t* write_idx,
                                            int s, int num_blocks) {
   int rb = read_idx[s], wb = write_idx[s];
-  return wb >= 0 && wb < num_blocks && rb >= 0 && rb < num_blocks;
+  const bool ok = wb >= 0 && wb < num_blocks && rb >= 0 && rb < num_blocks;
+  if (!ok && wb >= 0) raise_status(kStatusBadIndex);
+  return ok;
 }
 
 // Index s with cu[s] <= row < cu[s+1] (the last such s when empty sequences repeat offsets).

@@ -288,4 +288,6 @@ hipError_t launch_recurrent(const ScanArgs& a, int dk, int dv, bool bf16, hipStr
   return bf16 ? rec_dk<true>(a, dk, dv, st) : rec_dk<false>(a, dk, dv, st);
 }
 
+GDN_STATUS_ACCESSOR(status_recurrent)
+
 }  // namespace gdn

@@ -368,4 +368,6 @@ hipError_t launch_ssd(const SsdArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
+GDN_STATUS_ACCESSOR(status_ssd)
+
 }  // namespace gdn

@@ -4,7 +4,6 @@ Bar: conv states (and every block no sequence writes) bit-exact; outputs and
 final recurrent states within max relative L2 error 1e-2 per (sequence, value
 head) slab with bf16 activations and fp32 state, 1e-4 with all-fp32.
 """
-import numpy as np
 import pytest
 import torch
 
@@ -46,14 +45,13 @@ def test_config3_mixed():
     _report("cfg3", compare(b, run_gpu(b), run_oracle(b)))
 
 
-def test_config4_long_prefill_sampled_heads():
-    """Full 4 x 32768 run on the GPU; the oracle recomputes two value heads
-    (one of each key-head parity) of every sequence token by token."""
+def test_config4_long_prefill():
+    """Full 4 x 32768 run on the GPU against the oracle on every (sequence,
+    value head) slab of outputs and final states (the oracle runs the 128
+    chains token by token, about 10 s on 16 host cores)."""
     b = workloads.config(4)
-    mask = np.zeros(32, dtype=np.uint8)
-    mask[[0, 31]] = 1
     gpu = run_gpu(b)
-    _report("cfg4", compare(b, gpu, run_oracle(b, head_mask=mask), head_mask=mask))
+    _report("cfg4", compare(b, gpu, run_oracle(b)))
 
 
 EDGE = [0, 1, 2, 3, 63, 64, 65, 127, 128, 129, 200]
@@ -171,3 +169,27 @@ def test_stream_contract_host_and_device_inputs_reusable():
     torch.cuda.synchronize()
     assert torch.equal(out.cpu().view(torch.int16), ref_out.view(torch.int16))
     assert torch.equal(d["ssm_pool"].cpu(), ref_sp)
+
+
+def test_out_of_pool_index_is_skipped_and_reported():
+    """A read block outside the pool is skipped (nothing read or written for
+    that sequence, its out rows untouched) and raises GDN_DEV_BAD_INDEX; the
+    other sequences are unaffected."""
+    import linear_attention_state_amd as gdn
+
+    b = workloads.random_batch(workloads.BIG, [70, 1, 5], seed=36)
+    P = b.ssm_pool.shape[0]
+    bad = b.read_idx.clone()
+    bad[0] = P + 5
+    b_bad = workloads.Batch("bad", b.layer, b.x, b.conv_weight, b.g, b.beta, b.cu_seqlens, bad,
+                            b.write_idx.clone(), b.conv_pool, b.ssm_pool)
+    out, cp, sp = run_gpu(b_bad, out_fill=7.0)
+    bits = gdn.gdn_device_status(clear=True)
+    assert bits == gdn.GDN_DEV_BAD_INDEX, bits
+    assert (out[:70].float() == 7.0).all()
+    # the same batch with sequence 0 as padding is what the oracle runs
+    pad = b.write_idx.clone()
+    pad[0] = -1
+    b_pad = workloads.Batch("pad", b.layer, b.x, b.conv_weight, b.g, b.beta, b.cu_seqlens, b.read_idx.clone(),
+                            pad, b.conv_pool, b.ssm_pool)
+    compare(b_pad, (out, cp, sp), run_oracle(b_pad))
