@@ -151,6 +151,31 @@ int gdn_varlen_forward(const gdn_layer_desc* desc, const void* x,
                        int64_t ssm_block_stride, int32_t num_blocks, void* out,
                        void* workspace, size_t workspace_bytes, void* stream);
 
+/* gdn_varlen_forward for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  The same arguments without the workspace; the scratch the call
+ * needs (gdn_workspace_size for the batch) lives in a static device buffer of
+ * GDN_STATIC_SCRATCH_BYTES that the library holds on every device it runs on
+ * until the process ends.  No allocation of any kind, no host sync.
+ *   A batch that needs more scratch than that is rejected with
+ *   GDN_EWORKSPACE before any device work (64 MiB holds the scratch of a
+ *   batch of up to about 4000 tokens of an 8192-channel bf16 layer).
+ *   Every call on one device shares that device's buffer, and a call leaves
+ *   its contents behind: calls that overlap in time on one device (on
+ *   different streams, or from different threads) race and give undefined
+ *   results.  Calls in stream order on one stream are always safe: each call
+ *   resets what it needs at zero itself.
+ * Results are bitwise those of gdn_varlen_forward. */
+#define GDN_STATIC_SCRATCH_BYTES ((size_t)64 << 20)
+int gdn_varlen_forward_noalloc(const gdn_layer_desc* desc, const void* x,
+                               const void* conv_weight, const float* g, const float* beta,
+                               const int32_t* cu_seqlens, const int32_t* cu_seqlens_host,
+                               int32_t num_seqs, int32_t total_tokens,
+                               const int32_t* read_idx, const int32_t* write_idx,
+                               void* conv_pool, int64_t conv_block_stride, float* ssm_pool,
+                               int64_t ssm_block_stride, int32_t num_blocks, void* out,
+                               void* stream);
+
 /* A standalone varlen conv layer (the tracker page lists models with conv-only
  * layers): step 1 above, with or without the SiLU, and the conv-state part of
  * step 4, without the split, normalisation and recurrence.  For every sequence

@@ -17,7 +17,8 @@ LIB_PATH = os.path.join(HERE, "_lib", "libgdn.so")
 GDN_OK, GDN_EINVAL, GDN_EUNSUPPORTED, GDN_EWORKSPACE, GDN_EHIP, GDN_EDEVICE = 0, -1, -2, -3, -4, -5
 GDN_F32, GDN_BF16 = 0, 1
 GDN_DEV_WAIT_EXPIRED, GDN_DEV_BAD_INDEX = 1, 2
-EXPORTS = ("gdn_state_spec", "gdn_workspace_size", "gdn_varlen_forward", "gdn_varlen_conv", "gdn_state_copy",
+EXPORTS = ("gdn_state_spec", "gdn_workspace_size", "gdn_varlen_forward", "gdn_varlen_forward_noalloc",
+           "gdn_varlen_conv", "gdn_state_copy",
            "ssd_varlen_scan", "kda_varlen_forward", "gdn_last_error", "gdn_device_status",
            "gdn_kernel_timing", "gdn_kernel_times")
 
@@ -90,6 +91,10 @@ def load_library():
         lib.gdn_varlen_forward.argtypes = [
             ctypes.POINTER(gdn_layer_desc), P, P, P, P, P, P, ctypes.c_int32, ctypes.c_int32, P, P,
             P, ctypes.c_int64, P, ctypes.c_int64, ctypes.c_int32, P, P, ctypes.c_size_t, P]
+        lib.gdn_varlen_forward_noalloc.restype = ctypes.c_int
+        lib.gdn_varlen_forward_noalloc.argtypes = [
+            ctypes.POINTER(gdn_layer_desc), P, P, P, P, P, P, ctypes.c_int32, ctypes.c_int32, P, P,
+            P, ctypes.c_int64, P, ctypes.c_int64, ctypes.c_int32, P, P]
         lib.gdn_varlen_conv.restype = ctypes.c_int
         lib.gdn_varlen_conv.argtypes = [
             ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, P, P, P, P, ctypes.c_int32,
@@ -207,6 +212,45 @@ def gdn_varlen_forward(layer, x, conv_weight, g, beta, cu_seqlens, cu_seqlens_ho
         conv_stride, _dev_ptr(ssm_pool, "ssm_pool"), ssm_stride, int(ssm_pool.shape[0]),
         _dev_ptr(out, "out"), _dev_ptr(workspace, "workspace"), workspace.numel(),
         ctypes.c_void_p(stream))
+    _check(rc)
+    return out
+
+
+def gdn_varlen_forward_noalloc(layer, x, conv_weight, g, beta, cu_seqlens, cu_seqlens_host, read_idx, write_idx,
+                               conv_pool, ssm_pool, out, stream=None):
+    """gdn_varlen_forward without a workspace: the library's static scratch
+    buffer serves instead (at most GDN_STATIC_SCRATCH_BYTES; calls that overlap
+    in time on one device race).  Arguments as for gdn_varlen_forward."""
+    import torch
+
+    lib = load_library()
+    if cu_seqlens_host is None:
+        cu_h = None
+        num_seqs = cu_seqlens.numel() - 1
+    else:
+        if not isinstance(cu_seqlens_host, torch.Tensor):
+            cu_seqlens_host = torch.tensor(list(cu_seqlens_host), dtype=torch.int32)
+        cu_h = cu_seqlens_host.to(torch.int32).contiguous()
+        if cu_h.is_cuda:
+            raise ValueError("cu_seqlens_host must be host memory")
+        num_seqs = cu_h.numel() - 1
+    for name, t, dt in (("cu_seqlens", cu_seqlens, torch.int32), ("read_idx", read_idx, torch.int32),
+                        ("write_idx", write_idx, torch.int32), ("g", g, torch.float32),
+                        ("beta", beta, torch.float32), ("ssm_pool", ssm_pool, torch.float32)):
+        if t.dtype != dt:
+            raise ValueError("%s must be %s" % (name, dt))
+    if stream is None:
+        stream = torch.cuda.current_stream(x.device).cuda_stream
+    conv_stride = conv_pool.stride(0) * conv_pool.element_size() if conv_pool is not None and conv_pool.dim() else 0
+    ssm_stride = ssm_pool.stride(0) * ssm_pool.element_size()
+    rc = lib.gdn_varlen_forward_noalloc(
+        ctypes.byref(make_desc(layer)), _dev_ptr(x, "x"), _dev_ptr(conv_weight, "conv_weight"),
+        _dev_ptr(g, "g"), _dev_ptr(beta, "beta"), _dev_ptr(cu_seqlens, "cu_seqlens"),
+        ctypes.c_void_p(cu_h.data_ptr()) if cu_h is not None else None, num_seqs, int(x.shape[0]),
+        _dev_ptr(read_idx, "read_idx"), _dev_ptr(write_idx, "write_idx"),
+        _dev_ptr(conv_pool, "conv_pool") if conv_pool is not None and conv_pool.numel() else None,
+        conv_stride, _dev_ptr(ssm_pool, "ssm_pool"), ssm_stride, int(ssm_pool.shape[0]),
+        _dev_ptr(out, "out"), ctypes.c_void_p(stream))
     _check(rc)
     return out
 

@@ -294,6 +294,17 @@ extern "C" int gdn_device_status(int clear, uint32_t* bits, void* stream) {
               (v & GDN_DEV_BAD_INDEX) ? " a state block index outside the pool was skipped;" : "");
 }
 
+namespace {
+// The whole forward with the scratch it needs at `workspace`; `noalloc` says
+// the scratch is the library's static buffer (looked up only once every host
+// check has passed, so a rejected call touches no device).
+int forward_impl(const gdn_layer_desc* desc, const void* x, const void* conv_weight, const float* g,
+                 const float* beta, const int32_t* cu_seqlens, const int32_t* cu_seqlens_host, int32_t num_seqs,
+                 int32_t total_tokens, const int32_t* read_idx, const int32_t* write_idx, void* conv_pool,
+                 int64_t conv_block_stride, float* ssm_pool, int64_t ssm_block_stride, int32_t num_blocks,
+                 void* out, void* workspace, size_t workspace_bytes, void* stream, bool noalloc);
+}  // namespace
+
 extern "C" int gdn_varlen_forward(const gdn_layer_desc* desc, const void* x, const void* conv_weight,
                                   const float* g, const float* beta, const int32_t* cu_seqlens,
                                   const int32_t* cu_seqlens_host, int32_t num_seqs, int32_t total_tokens,
@@ -301,6 +312,66 @@ extern "C" int gdn_varlen_forward(const gdn_layer_desc* desc, const void* x, con
                                   int64_t conv_block_stride, float* ssm_pool, int64_t ssm_block_stride,
                                   int32_t num_blocks, void* out, void* workspace, size_t workspace_bytes,
                                   void* stream) {
+  return forward_impl(desc, x, conv_weight, g, beta, cu_seqlens, cu_seqlens_host, num_seqs, total_tokens, read_idx,
+                      write_idx, conv_pool, conv_block_stride, ssm_pool, ssm_block_stride, num_blocks, out,
+                      workspace, workspace_bytes, stream, false);
+}
+
+namespace {
+
+// Scratch of the allocation-free entry point: one static device buffer, which
+// every device the library runs on holds (at its own address) until the
+// process ends.  In host code `scratch` only names the symbol; its device
+// address on each device comes from hipGetSymbolAddress, looked up once per
+// device with that device current, and only that address is ever passed on.
+static __device__ __align__(256) unsigned char scratch[GDN_STATIC_SCRATCH_BYTES];
+
+hipError_t scratch_address(hipStream_t st, void** ptr) {
+  static std::mutex mu;
+  static std::vector<void*> addr;
+  int dev = 0;
+  hipError_t e = hipStreamGetDevice(st, &dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lock(mu);
+  if ((int)addr.size() <= dev) addr.resize(dev + 1, nullptr);
+  if (!addr[dev]) {
+    int cur = 0;
+    e = hipGetDevice(&cur);
+    if (e != hipSuccess) return e;
+    if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return e;
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (cur != dev) {
+      const hipError_t e2 = hipSetDevice(cur);
+      if (e == hipSuccess) e = e2;
+    }
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
+}
+
+}  // namespace
+
+extern "C" int gdn_varlen_forward_noalloc(const gdn_layer_desc* desc, const void* x, const void* conv_weight,
+                                          const float* g, const float* beta, const int32_t* cu_seqlens,
+                                          const int32_t* cu_seqlens_host, int32_t num_seqs, int32_t total_tokens,
+                                          const int32_t* read_idx, const int32_t* write_idx, void* conv_pool,
+                                          int64_t conv_block_stride, float* ssm_pool, int64_t ssm_block_stride,
+                                          int32_t num_blocks, void* out, void* stream) {
+  return forward_impl(desc, x, conv_weight, g, beta, cu_seqlens, cu_seqlens_host, num_seqs, total_tokens, read_idx,
+                      write_idx, conv_pool, conv_block_stride, ssm_pool, ssm_block_stride, num_blocks, out, nullptr,
+                      GDN_STATIC_SCRATCH_BYTES, stream, true);
+}
+
+namespace {
+int forward_impl(const gdn_layer_desc* desc, const void* x, const void* conv_weight, const float* g,
+                 const float* beta, const int32_t* cu_seqlens, const int32_t* cu_seqlens_host, int32_t num_seqs,
+                 int32_t total_tokens, const int32_t* read_idx, const int32_t* write_idx, void* conv_pool,
+                 int64_t conv_block_stride, float* ssm_pool, int64_t ssm_block_stride, int32_t num_blocks,
+                 void* out, void* workspace, size_t workspace_bytes, void* stream, bool noalloc) {
   int rc = check_desc(desc);
   if (rc) return rc;
   const int W = desc->conv_width;
@@ -342,11 +413,20 @@ extern "C" int gdn_varlen_forward(const gdn_layer_desc* desc, const void* x, con
     return fail(GDN_EINVAL, "x, out and the pools must be 16-byte aligned");
   const WsLayout wl = ws_layout(desc, total_tokens, num_seqs);
   const size_t need = wl.total;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  if (noalloc) {
+    if (need > workspace_bytes)
+      return fail(GDN_EWORKSPACE,
+                  "the batch needs %zu bytes of scratch, more than the %zu of the static buffer "
+                  "(gdn_varlen_forward_noalloc); call gdn_varlen_forward with a workspace instead",
+                  need, workspace_bytes);
+    const hipError_t e = scratch_address(st, &workspace);
+    if (e != hipSuccess) return fail(GDN_EHIP, "static scratch buffer: %s", hipGetErrorString(e));
+  }
   if (need > 0 && (!workspace || workspace_bytes < need))
     return fail(GDN_EWORKSPACE, "workspace of %zu bytes is smaller than the %zu needed", workspace_bytes, need);
   if (workspace && !aligned(workspace, 256)) return fail(GDN_EINVAL, "workspace must be 256-byte aligned");
 
-  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   const int C = (int)channels(desc);
   hipError_t e = hipSuccess;
 
@@ -546,6 +626,7 @@ extern "C" int gdn_varlen_forward(const gdn_layer_desc* desc, const void* x, con
   }
   return GDN_OK;
 }
+}  // namespace
 
 extern "C" int gdn_varlen_conv(int32_t channels, int32_t conv_width, int32_t act_dtype, int32_t silu,
                                const void* x, const void* conv_weight, const int32_t* cu_seqlens,
