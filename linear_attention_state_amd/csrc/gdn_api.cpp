@@ -295,6 +295,65 @@ extern "C" int gdn_device_status(int clear, uint32_t* bits, void* stream) {
 }
 
 namespace {
+
+// A mixed step (decode tokens beside chunked sequences) runs the token path on
+// a side stream beside the conv and chunk kernels: they touch disjoint
+// sequences and blocks, and the token kernel is HBM-bound while the chunk
+// kernel is latency-bound, so the two overlap.  One side stream and one pair of
+// events per device, created on first use (default priority, non-blocking);
+// fork and join are event records and waits, so the call stays asynchronous
+// and capturable.  Each record and its wait are made under one lock, so calls
+// from several threads never wait on each other's records.
+struct Side {
+  std::mutex mu;
+  std::vector<hipStream_t> stream;
+  std::vector<hipEvent_t> fork_ev, join_ev;
+};
+Side g_side;
+
+hipError_t fork_side(hipStream_t st, hipStream_t* side) {
+  int dev = 0;
+  hipError_t e = hipStreamGetDevice(st, &dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lock(g_side.mu);
+  if ((int)g_side.stream.size() <= dev) {
+    g_side.stream.resize(dev + 1, nullptr);
+    g_side.fork_ev.resize(dev + 1, nullptr);
+    g_side.join_ev.resize(dev + 1, nullptr);
+  }
+  if (!g_side.stream[dev]) {
+    int cur = 0;
+    if ((e = hipGetDevice(&cur)) != hipSuccess) return e;
+    if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return e;
+    hipStream_t s = nullptr;
+    hipEvent_t a = nullptr, b = nullptr;
+    const unsigned fl = hipEventDisableTiming | hipEventDisableSystemFence;
+    e = hipStreamCreateWithFlags(&s, hipStreamNonBlocking);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&a, fl);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&b, fl);
+    if (cur != dev) hipSetDevice(cur);
+    if (e != hipSuccess) return e;
+    g_side.stream[dev] = s;
+    g_side.fork_ev[dev] = a;
+    g_side.join_ev[dev] = b;
+  }
+  *side = g_side.stream[dev];
+  if ((e = hipEventRecord(g_side.fork_ev[dev], st)) != hipSuccess) return e;
+  return hipStreamWaitEvent(*side, g_side.fork_ev[dev], 0);
+}
+
+hipError_t join_side(hipStream_t st, hipStream_t side) {
+  int dev = 0;
+  hipError_t e = hipStreamGetDevice(side, &dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lock(g_side.mu);
+  if ((e = hipEventRecord(g_side.join_ev[dev], side)) != hipSuccess) return e;
+  return hipStreamWaitEvent(st, g_side.join_ev[dev], 0);
+}
+
+}  // namespace
+
+namespace {
 // The whole forward with the scratch it needs at `workspace`; `noalloc` says
 // the scratch is the library's static buffer (looked up only once every host
 // check has passed, so a rejected call touches no device).
@@ -465,6 +524,18 @@ int forward_impl(const gdn_layer_desc* desc, const void* x, const void* conv_wei
   // ---- plan on the device: every launch size depends on num_seqs and
   // total_tokens only, so a captured graph replays for any offsets and indices
   if (dev_plan) {
+    // the token path (which skips the chunked sequences itself) on the side
+    // stream beside the chunked path; captured graphs keep the fork
+    const bool fork = !noalloc && chunked && total_tokens > 0;
+    hipStream_t side = nullptr;
+    if (fork) {
+      e = fork_side(st, &side);
+      if (e != hipSuccess) return fail(GDN_EHIP, "side stream: %s", hipGetErrorString(e));
+      gdn::ScanArgs ts = sa;
+      ts.min_len = 0; ts.max_len = 1;
+      e = timed(K_TOKEN, side, [&] { return gdn::launch_recurrent(ts, desc->head_k_dim, desc->head_v_dim, bf16, side); });
+      if (e != hipSuccess) return fail(GDN_EHIP, "token path launch: %s", hipGetErrorString(e));
+    }
     if (chunked && total_tokens > 0) {
       int32_t* plan = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(workspace) + wl.plan);
       int32_t* sync = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(workspace) + wl.sync);
@@ -498,9 +569,14 @@ int forward_impl(const gdn_layer_desc* desc, const void* x, const void* conv_wei
       if (e != hipSuccess) return fail(GDN_EHIP, "chunk scan launch: %s", hipGetErrorString(e));
       ta.fused = plan + gdn::kPlanFused;
     }
-    sa.min_len = 0; sa.max_len = chunked ? 1 : INT_MAX;
-    e = timed(K_TOKEN, st, [&] { return gdn::launch_recurrent(sa, desc->head_k_dim, desc->head_v_dim, bf16, st); });
-    if (e != hipSuccess) return fail(GDN_EHIP, "token path launch: %s", hipGetErrorString(e));
+    if (fork) {
+      e = join_side(st, side);
+      if (e != hipSuccess) return fail(GDN_EHIP, "side stream: %s", hipGetErrorString(e));
+    } else {
+      sa.min_len = 0; sa.max_len = chunked ? 1 : INT_MAX;
+      e = timed(K_TOKEN, st, [&] { return gdn::launch_recurrent(sa, desc->head_k_dim, desc->head_v_dim, bf16, st); });
+      if (e != hipSuccess) return fail(GDN_EHIP, "token path launch: %s", hipGetErrorString(e));
+    }
     if (W > 1) {
       e = timed(K_TAIL, st, [&] { return gdn::launch_tail_commit(ta, W, bf16, st); });
       if (e != hipSuccess) return fail(GDN_EHIP, "conv state commit launch: %s", hipGetErrorString(e));
@@ -523,6 +599,18 @@ int forward_impl(const gdn_layer_desc* desc, const void* x, const void* conv_wei
   // old conv states has been enqueued (when the chunk kernel ran the conv, it
   // also wrote the chunked sequences' states, and this covers the rest).
   bool tails_done = false;  // the chunk kernel has written the chunked sequences' conv states
+  // a mixed batch: the token path on the side stream, beside the chunked path
+  // (not for the allocation-free entry point, which creates nothing)
+  const bool fork = !noalloc && chunked && n_long > 0 && n_short > 0;
+  hipStream_t side = nullptr;
+  if (fork) {
+    e = fork_side(st, &side);
+    if (e != hipSuccess) return fail(GDN_EHIP, "side stream: %s", hipGetErrorString(e));
+    gdn::ScanArgs ts = sa;
+    ts.min_len = 0; ts.max_len = 1;
+    e = timed(K_TOKEN, side, [&] { return gdn::launch_recurrent(ts, desc->head_k_dim, desc->head_v_dim, bf16, side); });
+    if (e != hipSuccess) return fail(GDN_EHIP, "token path launch: %s", hipGetErrorString(e));
+  }
   if (chunked && n_long > 0) {
     sa.min_len = 2; sa.max_len = INT_MAX;
     // longest sequences first, so the longest chains start before the short ones
@@ -614,7 +702,10 @@ int forward_impl(const gdn_layer_desc* desc, const void* x, const void* conv_wei
     if (e != hipSuccess) return fail(GDN_EHIP, "chunk scan launch: %s", hipGetErrorString(e));
     tails_done = fc.n > 0;
   }
-  if (!chunked || n_short > 0) {
+  if (fork) {
+    e = join_side(st, side);
+    if (e != hipSuccess) return fail(GDN_EHIP, "side stream: %s", hipGetErrorString(e));
+  } else if (!chunked || n_short > 0) {
     sa.min_len = 0; sa.max_len = chunked ? 1 : INT_MAX;
     e = timed(K_TOKEN, st, [&] { return gdn::launch_recurrent(sa, desc->head_k_dim, desc->head_v_dim, bf16, st); });
     if (e != hipSuccess) return fail(GDN_EHIP, "token path launch: %s", hipGetErrorString(e));

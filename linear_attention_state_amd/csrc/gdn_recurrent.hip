@@ -35,6 +35,18 @@ __device__ __forceinline__ float ld1(const void* base, int64_t i) {
   else return reinterpret_cast<const float*>(base)[i];
 }
 
+// element i as raw bits (bf16 in the low half), and those bits as fp32
+template <bool BF16>
+__device__ __forceinline__ uint32_t ldraw(const void* base, int64_t i) {
+  if constexpr (BF16) return reinterpret_cast<const uint16_t*>(base)[i];
+  else return reinterpret_cast<const uint32_t*>(base)[i];
+}
+template <bool BF16>
+__device__ __forceinline__ float rawf(uint32_t b) {
+  if constexpr (BF16) return __uint_as_float(b << 16);
+  else return __uint_as_float(b);
+}
+
 template <bool BF16>
 __device__ __forceinline__ float4 ld4(const void* base, int64_t i) {
   if constexpr (BF16) {
@@ -59,14 +71,17 @@ __device__ __forceinline__ void st4(void* base, int64_t i, float4 v) {
 }
 
 // The state is read once and written once per call: non-temporal accesses
-// keep it from displacing cached data.
-__device__ __forceinline__ float4 ld_stream(const float* p) {
-  const f32x4 v = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
-  return make_float4(v[0], v[1], v[2], v[3]);
+// (cache policy NT) keep it from displacing cached data.  Offsets: a per-lane
+// byte offset plus a constant one (folded into the instruction's immediate or
+// its scalar offset).
+constexpr int kNonTemporal = 2;
+__device__ __forceinline__ float4 ld_state(__amdgpu_buffer_rsrc_t rs, int voff, int coff) {
+  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rs, voff + coff, 0, kNonTemporal);
+  return make_float4(__uint_as_float(v[0]), __uint_as_float(v[1]), __uint_as_float(v[2]), __uint_as_float(v[3]));
 }
-__device__ __forceinline__ void st_stream(float* p, float4 v) {
-  const f32x4 w = {v.x, v.y, v.z, v.w};
-  __builtin_nontemporal_store(w, reinterpret_cast<f32x4*>(p));
+__device__ __forceinline__ void st_state(__amdgpu_buffer_rsrc_t rs, int voff, int coff, float4 v) {
+  const u32x4 w = {__float_as_uint(v.x), __float_as_uint(v.y), __float_as_uint(v.z), __float_as_uint(v.w)};
+  __builtin_amdgcn_raw_buffer_store_b128(w, rs, voff + coff, 0, kNonTemporal);
 }
 
 __device__ __forceinline__ float4 f4_fma(float a, float4 x, float4 y) {
@@ -94,6 +109,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KDA ? 3 : 1
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int c4 = tid % C4, rg = tid / C4;
+  // whether state row `row` of this thread exists (always, when the row groups
+  // tile d_k exactly: a compile-time fact the loads below must not branch on)
+  auto row_ok = [](int row) { return RG * RPT == DK || row < DK; };
   const int h = m / (a.num_v_heads / a.num_k_heads);
   const int64_t head_off = (int64_t)m * DK * DV + n0;
   const float* S0 = reinterpret_cast<const float*>(
@@ -101,35 +119,68 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KDA ? 3 : 1
   float* S1 = reinterpret_cast<float*>(
       reinterpret_cast<char*>(a.ssm_pool) + (int64_t)a.write_idx[s] * a.ssm_stride) + head_off;
 
-  float4 S[RPT];
-#pragma unroll
-  for (int i = 0; i < RPT; ++i) {
-    const int row = rg * RPT + i;
-    S[i] = row < DK ? ld_stream(S0 + row * DV + c4 * 4) : make_float4(0.f, 0.f, 0.f, 0.f);
-  }
-
   // conv channels owned by this thread (index i into [q | k | v] of this head)
   const int64_t C = a.channels;
   const int W = a.width;
   int64_t gch[2];
   bool has[2];
   float wt[2][4], win[2][3], wlast[2];
-  const char* tail = a.conv_pool ? a.conv_pool + (int64_t)a.read_idx[s] * a.conv_stride : nullptr;
+  const char* tail = a.conv_pool && W > 1 ? a.conv_pool + (int64_t)a.read_idx[s] * a.conv_stride : nullptr;
+  // The conv inputs of the first token (taps, the W-1 previous inputs, x) are
+  // loaded first, all at once, as raw bits: every load is unconditional at a
+  // clamped index (a thread past the channel count reads channel 0), and no
+  // value is used before the state loads below have been issued, so neither
+  // group waits for the other.  Where a source does not exist (an empty
+  // sequence, whose x and taps may be NULL; no conv state) the load reads
+  // element 0 of the state pool instead, and the value is masked.
+  uint32_t wraw[2][4], traw[2][3], xraw[2];
+  const bool have_in = L > 0;
+  const void* wsrc = have_in ? a.w : (const void*)a.ssm_pool;
+  const void* xsrc = have_in ? a.x : (const void*)a.ssm_pool;
+  const void* tsrc = have_in && tail ? (const void*)tail : (const void*)a.ssm_pool;
 #pragma unroll
   for (int e = 0; e < 2; ++e) {
     const int i = tid + NT * e;
-    has[e] = i < NCH && L > 0;  // an empty sequence reads no input at all
-    gch[e] = i < DK ? (int64_t)h * DK + i
-           : i < 2 * DK ? (int64_t)a.num_k_heads * DK + h * DK + (i - DK)
-                        : 2 * (int64_t)a.num_k_heads * DK + (int64_t)m * DV + n0 + (i - 2 * DK);
+    has[e] = i < NCH && have_in;
+    const int ic = i < NCH ? i : 0;
+    gch[e] = ic < DK ? (int64_t)h * DK + ic
+           : ic < 2 * DK ? (int64_t)a.num_k_heads * DK + h * DK + (ic - DK)
+                         : 2 * (int64_t)a.num_k_heads * DK + (int64_t)m * DV + n0 + (ic - 2 * DK);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) wt[e][j] = (has[e] && j < W) ? ld1<BF16>(a.w, gch[e] * W + j) : 0.f;
+    for (int j = 0; j < 4; ++j) wraw[e][j] = ldraw<BF16>(wsrc, have_in ? gch[e] * W + (j < W ? j : 0) : 0);
 #pragma unroll
-    for (int j = 0; j < 3; ++j) win[e][j] = (has[e] && j < W - 1) ? ld1<BF16>(tail, (int64_t)j * C + gch[e]) : 0.f;
+    for (int j = 0; j < 3; ++j)
+      traw[e][j] = ldraw<BF16>(tsrc, have_in && tail ? (int64_t)(j < W - 1 ? j : 0) * C + gch[e] : 0);
+    xraw[e] = ldraw<BF16>(xsrc, have_in ? (int64_t)r0 * C + gch[e] : 0);
+  }
+  // scheduling barriers: the state loads issue right after the conv-input
+  // loads, before anything waits for those
+  __builtin_amdgcn_sched_barrier(0);
+  // the thread's rows through one buffer resource per head (scalar base): one
+  // offset register for all RPT loads, each at a fixed offset from it
+  const __amdgpu_buffer_rsrc_t rs0 = make_rsrc(S0, (uint32_t)(DK * DV * 4));
+  const int soff = (rg * RPT * DV + c4 * 4) * 4;
+  float4 S[RPT];
+#pragma unroll
+  for (int i = 0; i < RPT; ++i) {
+    const int row = rg * RPT + i;
+    S[i] = row_ok(row) ? ld_state(rs0, soff, i * DV * 4) : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  // the taps, window and first input, converted and masked only now (taps
+  // past W, window rows past W-1, threads past the channel count, no inputs)
+  float xin0[2];
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
     wlast[e] = 0.f;
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < 4; ++j) {
+      wt[e][j] = has[e] && j < W ? rawf<BF16>(wraw[e][j]) : 0.f;
       if (j == W - 1) wlast[e] = wt[e][j];
+    }
+#pragma unroll
+    for (int j = 0; j < 3; ++j) win[e][j] = has[e] && tail && j < W - 1 ? rawf<BF16>(traw[e][j]) : 0.f;
+    xin0[e] = has[e] ? rawf<BF16>(xraw[e]) : 0.f;
   }
 
   __shared__ __align__(16) float sy[NCH];
@@ -138,11 +189,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KDA ? 3 : 1
 
   for (int t = 0; t < L; ++t) {
     const int64_t r = r0 + t;
-    // ---- causal conv + SiLU of this token for the head's channels
+    // ---- causal conv + SiLU of this token for the head's channels (the first
+    // token's x was loaded with the taps; later ones at a clamped index)
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
+      const float xin = t == 0 ? xin0[e] : ld1<BF16>(a.x, r * C + gch[e]);
       if (!has[e]) continue;
-      const float xin = ld1<BF16>(a.x, r * C + gch[e]);
       float acc = wlast[e] * xin;
 #pragma unroll
       for (int j = 0; j < 3; ++j)
@@ -167,7 +219,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KDA ? 3 : 1
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
       const int row = rg * RPT + i;
-      if (row < DK) {
+      if (row_ok(row)) {
         const float kr = sy[DK + row], qr = sy[row];
         // KDA reads the decayed state diag(a) S: the row's decay folded into k and q
         const float dr = KDA ? sdec[row] : 1.f;  // read at each use: no registers held for it
@@ -222,7 +274,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KDA ? 3 : 1
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
       const int row = rg * RPT + i;
-      if (row < DK) {
+      if (row_ok(row)) {
         const float kr = sy[DK + row] * ik;
         const float dec = KDA ? sdec[row] : av;
         S[i].x = fmaf(dec, S[i].x, kr * u.x); S[i].y = fmaf(dec, S[i].y, kr * u.y);
@@ -239,10 +291,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KDA ? 3 : 1
     __syncthreads();
   }
 
+  const __amdgpu_buffer_rsrc_t rs1 = make_rsrc(S1, (uint32_t)(DK * DV * 4));
 #pragma unroll
   for (int i = 0; i < RPT; ++i) {
     const int row = rg * RPT + i;
-    if (row < DK) st_stream(S1 + row * DV + c4 * 4, S[i]);
+    if (row_ok(row)) st_state(rs1, soff, i * DV * 4, S[i]);
   }
 }
 
