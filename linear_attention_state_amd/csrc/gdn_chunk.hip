@@ -1239,7 +1239,8 @@ __global__ __launch_bounds__(1024) void plan_kernel(PlanArgs a) {
     const double crowd = fmin(1.0, fmax(0.0, ((double)n * a.num_v_heads - half) / half));
     const double apart = a.conv_us_per_token * T + a.scan0_us +
                          (a.plain_scan1_us + a.crowd_scan1_us * crowd) * ((longest + BT - 1) / BT) + 3.0;
-    const int use = a.fused_allowed && n > 0 && (a.fused_forced || a.phased_scale * fused < apart);
+    const int use = a.fused_allowed && n > 0 &&
+                    (a.fused_forced || a.phased_scale * fused < apart || (a.beside_tokens && n < N));
     a.plan[kPlanN] = n;
     a.plan[kPlanFused] = use;
     a.plan[kPlanTarget] = (int32_t)(fused * a.margin);

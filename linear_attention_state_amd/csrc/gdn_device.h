@@ -253,6 +253,7 @@ struct PlanArgs {
   double conv_us_per_token, task_us, scan0_us, scan1_us, margin;
   int cus;  // compute units: the per-chunk scan time after the conv kernel
   double plain_scan1_us, crowd_scan1_us, phased_scale;  // grows with the share of them scanning
+  int beside_tokens;  // the token kernel runs beside on a side stream: with one-token sequences, conv inside
   int32_t* plan;
   int32_t* sync;      // zeroed: 1 + num_seqs counters
 };
