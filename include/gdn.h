@@ -226,17 +226,26 @@ int gdn_state_copy(const gdn_layer_desc* desc, void* conv_pool, int64_t conv_blo
  * GQA head map, paged states, padding and empty sequences) is that of
  * gdn_varlen_forward.
  *   g  [T][H_v][d_k] fp32 (log decay per key channel; <= 0 for a decay)
+ *   workspace  device scratch of at least gdn_workspace_size() bytes, 256-byte
+ *              aligned, or NULL (then every sequence runs token by token)
  *   every other argument as for gdn_varlen_forward; cu_seqlens_host is required
- * This build runs every sequence token by token (one workgroup per sequence
- * and value head, the conv, norms and recurrence in one pass), then the
- * conv-state commit: exact for any length, tuned for decode, not for long
- * prefill.  No workspace, no allocation, no host sync. */
+ * Sequences of two or more tokens run in chunks of 64 rows (bf16 with
+ * d_k = d_v = 128 and a workspace): the conv kernel writes the normalised rows
+ * into the workspace, then a chunk kernel evaluates the WY / UT form with the
+ * decay inside the channel sums of its block products (every exponentiated
+ * decay difference <= 1, except on a diagonal 16-row block, bounded there by
+ * that block's own decay; a block whose decay passes e^80 on some channel is
+ * computed in fp32 without that factor).  Sequences of length 0 and 1, and
+ * every sequence in other shapes or in fp32, run token by token (one workgroup
+ * per sequence and value head, the conv, norms and recurrence in one pass).
+ * Then the conv-state commit.  No allocation, no host sync. */
 int kda_varlen_forward(const gdn_layer_desc* desc, const void* x, const void* conv_weight,
                        const float* g, const float* beta, const int32_t* cu_seqlens,
                        const int32_t* cu_seqlens_host, int32_t num_seqs, int32_t total_tokens,
                        const int32_t* read_idx, const int32_t* write_idx, void* conv_pool,
                        int64_t conv_block_stride, float* ssm_pool, int64_t ssm_block_stride,
-                       int32_t num_blocks, void* out, void* stream);
+                       int32_t num_blocks, void* out, void* workspace, size_t workspace_bytes,
+                       void* stream);
 
 /* ---- Mamba2 scan with per-sequence states.
  * The model-support tracker page (continuous batching for the remaining
@@ -319,7 +328,8 @@ int gdn_device_status(int clear, uint32_t* bits, void* stream);
  * The library creates the events it records and keeps them for reuse. */
 typedef struct {
   char name[32];      /* kernel: "conv_silu_norm", "chunk_scan", "token_recurrent", "conv_state_commit",
-                         "state_copy", "task_counter_reset", "device_plan", "ssd_scan", "ssd_token" */
+                         "state_copy", "task_counter_reset", "device_plan", "ssd_scan", "ssd_token",
+                         "kda_chunk" */
   double total_ms;    /* summed event-to-event time of its timed launches */
   int64_t launches;
 } gdn_kernel_time;

@@ -105,7 +105,7 @@ def load_library():
         lib.kda_varlen_forward.restype = ctypes.c_int
         lib.kda_varlen_forward.argtypes = [
             ctypes.POINTER(gdn_layer_desc), P, P, P, P, P, P, ctypes.c_int32, ctypes.c_int32, P, P, P,
-            ctypes.c_int64, P, ctypes.c_int64, ctypes.c_int32, P, P]
+            ctypes.c_int64, P, ctypes.c_int64, ctypes.c_int32, P, P, ctypes.c_size_t, P]
         lib.ssd_varlen_scan.restype = ctypes.c_int
         lib.ssd_varlen_scan.argtypes = [
             ctypes.POINTER(ssd_layer_desc), P, ctypes.c_int64, P, P, ctypes.c_int64, P, P, P, P, P, P,
@@ -309,9 +309,11 @@ def gdn_state_copy(layer, conv_pool, ssm_pool, src, dst, stream=None):
 
 
 def kda_varlen_forward(layer, x, conv_weight, g, beta, cu_seqlens, cu_seqlens_host, read_idx, write_idx,
-                       conv_pool, ssm_pool, out, stream=None):
+                       conv_pool, ssm_pool, out, workspace=None, stream=None):
     """Enqueues the KDA layer forward: as gdn_varlen_forward, with g [T][H_v][d_k]
-    float32 (a log decay per key channel); cu_seqlens_host is required."""
+    float32 (a log decay per key channel); cu_seqlens_host is required.
+    ``workspace``: a uint8 device tensor of at least gdn_workspace_size bytes
+    (allocated here when None); ``False`` runs every sequence token by token."""
     import torch
 
     if g.dtype != torch.float32 or g.dim() != 3 or g.shape[2] != layer.head_k_dim:
@@ -319,6 +321,11 @@ def kda_varlen_forward(layer, x, conv_weight, g, beta, cu_seqlens, cu_seqlens_ho
     if stream is None:
         stream = torch.cuda.current_stream(x.device).cuda_stream
     host = cu_seqlens_host.to(torch.int32).contiguous()
+    if workspace is None:
+        nbytes = gdn_workspace_size(layer, int(x.shape[0]), int(read_idx.numel()))
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=x.device)
+    ws_ptr = None if workspace is False else _dev_ptr(workspace, "workspace")
+    ws_bytes = 0 if workspace is False else workspace.numel()
     W = int(layer.conv_width)
     has_conv = conv_pool is not None and conv_pool.numel() > 0
     conv_stride = conv_pool.stride(0) * conv_pool.element_size() if has_conv else 0
@@ -328,7 +335,7 @@ def kda_varlen_forward(layer, x, conv_weight, g, beta, cu_seqlens, cu_seqlens_ho
         int(read_idx.numel()), int(x.shape[0]), _dev_ptr(read_idx, "read_idx"), _dev_ptr(write_idx, "write_idx"),
         _dev_ptr(conv_pool, "conv_pool") if (has_conv and W > 1) else None, conv_stride,
         _dev_ptr(ssm_pool, "ssm_pool"), ssm_pool.stride(0) * ssm_pool.element_size(), int(ssm_pool.shape[0]),
-        _dev_ptr(out, "out"), ctypes.c_void_p(stream)))
+        _dev_ptr(out, "out"), ws_ptr, ws_bytes, ctypes.c_void_p(stream)))
 
 
 def ssd_varlen_scan(layer, x, B, C, dt, A, cu_seqlens, cu_seqlens_host, read_idx, write_idx, ssm_pool, y,

@@ -156,10 +156,10 @@ int device_cus(hipStream_t st) {
 bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
 
 // ---- optional per-kernel event timing (measurement only)
-enum { K_CONV = 0, K_CHUNK, K_TOKEN, K_TAIL, K_COPY, K_ZERO, K_PLAN, K_SSD, K_SSD_TOKEN, K_COUNT };
+enum { K_CONV = 0, K_CHUNK, K_TOKEN, K_TAIL, K_COPY, K_ZERO, K_PLAN, K_SSD, K_SSD_TOKEN, K_KDA_CHUNK, K_COUNT };
 const char* const kKernelNames[K_COUNT] = {"conv_silu_norm", "chunk_scan", "token_recurrent", "conv_state_commit",
                                            "state_copy", "task_counter_reset", "device_plan", "ssd_scan",
-                                           "ssd_token"};
+                                           "ssd_token", "kda_chunk"};
 
 struct Timing {
   std::mutex mu;
@@ -283,7 +283,7 @@ extern "C" int gdn_device_status(int clear, uint32_t* bits, void* stream) {
   hipError_t e = hipStreamSynchronize(reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(GDN_EHIP, "device status: %s", hipGetErrorString(e));
   uint32_t v = 0;
-  for (auto fn : {gdn::status_chunk, gdn::status_conv, gdn::status_recurrent, gdn::status_ssd}) {
+  for (auto fn : {gdn::status_chunk, gdn::status_conv, gdn::status_recurrent, gdn::status_ssd, gdn::status_kda}) {
     e = fn(&v, clear);
     if (e != hipSuccess) return fail(GDN_EHIP, "device status: %s", hipGetErrorString(e));
   }
@@ -907,7 +907,8 @@ extern "C" int kda_varlen_forward(const gdn_layer_desc* desc, const void* x, con
                                   const int32_t* cu_seqlens_host, int32_t num_seqs, int32_t total_tokens,
                                   const int32_t* read_idx, const int32_t* write_idx, void* conv_pool,
                                   int64_t conv_block_stride, float* ssm_pool, int64_t ssm_block_stride,
-                                  int32_t num_blocks, void* out, void* stream) {
+                                  int32_t num_blocks, void* out, void* workspace, size_t workspace_bytes,
+                                  void* stream) {
   int rc = check_desc(desc);
   if (rc) return rc;
   const int W = desc->conv_width;
@@ -948,11 +949,59 @@ extern "C" int kda_varlen_forward(const gdn_layer_desc* desc, const void* x, con
   sa.write_idx = write_idx; sa.ssm_pool = ssm_pool; sa.ssm_stride = ssm_block_stride; sa.out = out;
   sa.num_seqs = num_seqs; sa.num_blocks = num_blocks; sa.num_k_heads = desc->num_k_heads;
   sa.num_v_heads = desc->num_v_heads; sa.channels = C;
-  sa.min_len = 0; sa.max_len = INT_MAX; sa.kda = 1;
-  // every sequence token by token (conv, norms and the recurrence in one pass),
-  // then the new conv states once every reader of the old ones is enqueued
-  hipError_t e = timed(K_TOKEN, st, [&] { return gdn::launch_recurrent(sa, desc->head_k_dim, desc->head_v_dim, bf16, st); });
-  if (e != hipSuccess) return fail(GDN_EHIP, "token path launch: %s", hipGetErrorString(e));
+  sa.kda = 1;
+  // Sequences of two or more tokens run chunked (bf16, d_k = d_v = 128, with a
+  // workspace for the conv output): the conv kernel writes the normalised q, k
+  // and v rows, then the KDA chunk kernel walks each sequence 64 rows at a time,
+  // longest first.  The others (and everything without a workspace or in
+  // another shape) run token by token.  The new conv states come last, once
+  // every reader of the old ones is enqueued.
+  int n_long = 0;
+  for (int i = 0; i < num_seqs; ++i) n_long += cu_seqlens_host[i + 1] - cu_seqlens_host[i] >= 2;
+  const size_t y_bytes = (size_t)total_tokens * C * act_size(desc);
+  const bool chunked = bf16 && n_long > 0 && workspace && gdn::kda_chunk_supported(desc->head_k_dim, desc->head_v_dim);
+  if (chunked && workspace_bytes < y_bytes)
+    return fail(GDN_EWORKSPACE, "workspace of %zu bytes is smaller than the %zu needed", workspace_bytes, y_bytes);
+  if (workspace && !aligned(workspace, 256)) return fail(GDN_EINVAL, "workspace must be 256-byte aligned");
+  hipError_t e = hipSuccess;
+  if (chunked) {
+    gdn::ConvArgs ca{};
+    ca.x = x; ca.w = conv_weight; ca.cu = cu_seqlens; ca.read_idx = read_idx; ca.write_idx = write_idx;
+    ca.conv_pool = reinterpret_cast<const char*>(conv_pool); ca.conv_stride = conv_block_stride;
+    ca.y = workspace;
+    ca.num_seqs = num_seqs; ca.total_tokens = total_tokens; ca.num_blocks = num_blocks; ca.channels = C;
+    ca.qk_channels = desc->num_k_heads * desc->head_k_dim; ca.head_k_dim = desc->head_k_dim;
+    const int groups = (C + 511) / 512;
+    const int slices = std::max(1, 4096 / groups);
+    const int rows = (total_tokens + slices - 1) / slices;
+    ca.rows_per_block = std::min(256, std::max(4, (rows + 3) / 4 * 4));
+    ca.eps = sa.eps;
+    ca.q_scale = sa.q_scale;
+    e = timed(K_CONV, st, [&] { return gdn::launch_conv(ca, W, bf16, true, st); });
+    if (e != hipSuccess) return fail(GDN_EHIP, "conv launch: %s", hipGetErrorString(e));
+    static thread_local gdn::SeqOrder order;
+    order.n = 0;
+    if (n_long <= gdn::kMaxOrder && num_seqs <= 65535) {
+      std::vector<std::pair<int, int>> lens;
+      for (int i = 0; i < num_seqs; ++i) {
+        const int L = cu_seqlens_host[i + 1] - cu_seqlens_host[i];
+        if (L >= 2) lens.push_back({-L, i});
+      }
+      std::stable_sort(lens.begin(), lens.end());
+      for (size_t i = 0; i < lens.size(); ++i) order.seq[i] = (uint16_t)lens[i].second;
+      order.n = (int32_t)lens.size();
+    }
+    gdn::ScanArgs ka = sa;
+    ka.y = workspace;
+    ka.min_len = 2; ka.max_len = INT_MAX;
+    e = timed(K_KDA_CHUNK, st, [&] { return gdn::launch_kda_chunk(ka, order, st); });
+    if (e != hipSuccess) return fail(GDN_EHIP, "KDA chunk launch: %s", hipGetErrorString(e));
+  }
+  if (!chunked || n_long < num_seqs) {
+    sa.min_len = 0; sa.max_len = chunked ? 1 : INT_MAX;
+    e = timed(K_TOKEN, st, [&] { return gdn::launch_recurrent(sa, desc->head_k_dim, desc->head_v_dim, bf16, st); });
+    if (e != hipSuccess) return fail(GDN_EHIP, "token path launch: %s", hipGetErrorString(e));
+  }
   if (W > 1) {
     gdn::TailArgs ta{};
     ta.x = x; ta.cu = cu_seqlens; ta.read_idx = read_idx; ta.write_idx = write_idx;

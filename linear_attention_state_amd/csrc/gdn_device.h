@@ -82,6 +82,7 @@ hipError_t status_chunk(uint32_t* bits, int clear);
 hipError_t status_conv(uint32_t* bits, int clear);
 hipError_t status_recurrent(uint32_t* bits, int clear);
 hipError_t status_ssd(uint32_t* bits, int clear);
+hipError_t status_kda(uint32_t* bits, int clear);
 
 // A sequence takes part in a call when it has a write block inside the pool and
 // a read block inside the pool; anything else is skipped without memory access
@@ -263,5 +264,11 @@ hipError_t launch_zero_sync(int32_t* sync, int n, hipStream_t st);  // n counter
 hipError_t launch_chunk(const ScanArgs& a, const SeqOrder& order, const FusedConv& fc, int dk, int dv,
                         hipStream_t st);
 bool chunk_supported(int dk, int dv);
+
+// Kimi delta attention, chunked (kda_chunk.hip): sequences with min_len <= L <= max_len,
+// launch order as for launch_chunk, reading the conv output y (bf16, normalised)
+// and g [T][H_v][d_k]; d_k = d_v = 128 only (kda_chunk_supported).
+hipError_t launch_kda_chunk(const ScanArgs& a, const SeqOrder& order, hipStream_t st);
+bool kda_chunk_supported(int dk, int dv);
 
 }  // namespace gdn

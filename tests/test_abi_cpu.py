@@ -217,11 +217,13 @@ def _kda_call(cu_host, T, **over):
     fake = ctypes.c_void_p(1 << 20)
     cu = (ctypes.c_int32 * len(cu_host))(*cu_host) if cu_host is not None else None
     args = dict(x=fake, w=fake, g=fake, b=fake, cu=fake, cuh=cu, n=(len(cu_host) - 1) if cu_host else 1, T=T,
-                ri=fake, wi=fake, conv=fake, cstride=3 * 8192 * 2, ssm=fake, sstride=2 << 20, P=8, out=fake)
+                ri=fake, wi=fake, conv=fake, cstride=3 * 8192 * 2, ssm=fake, sstride=2 << 20, P=8, out=fake,
+                ws=None, wsb=0)
     args.update(over)
     rc = lib.kda_varlen_forward(ctypes.byref(gdn.make_desc(workloads.BIG)), args["x"], args["w"], args["g"], args["b"],
                                 args["cu"], args["cuh"], args["n"], args["T"], args["ri"], args["wi"], args["conv"],
-                                args["cstride"], args["ssm"], args["sstride"], args["P"], args["out"], None)
+                                args["cstride"], args["ssm"], args["sstride"], args["P"], args["out"], args["ws"],
+                                args["wsb"], None)
     return rc, gdn.gdn_last_error()
 
 
@@ -235,6 +237,8 @@ def _kda_call(cu_host, T, **over):
     ([0, 4], 4, {"P": 1}, gdn.GDN_EINVAL, "num_blocks"),
     ([0, 4], 4, {"sstride": (2 << 20) - 16}, gdn.GDN_EINVAL, "ssm_block_stride"),
     ([0, 4], 4, {"out": ctypes.c_void_p((1 << 20) + 8)}, gdn.GDN_EINVAL, "aligned"),
+    ([0, 4], 4, {"ws": ctypes.c_void_p(1 << 20), "wsb": 1000}, gdn.GDN_EWORKSPACE, "workspace"),
+    ([0, 4], 4, {"ws": ctypes.c_void_p((1 << 20) + 64), "wsb": 1 << 30}, gdn.GDN_EINVAL, "256-byte"),
 ])
 def test_kda_forward_rejects_bad_arguments(cu, T, over, status, needle):
     rc, msg = _kda_call(cu, T, **over)

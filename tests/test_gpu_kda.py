@@ -103,3 +103,57 @@ def test_uniform_decay_matches_the_gated_delta_rule_kernels():
 def test_decode_workload_sampled_heads():
     b = workloads.config(2)
     _check("decode", b, _g(b, 68), heads=[0, 17, 31])
+
+
+# ---- the chunked path (sequences of two or more tokens, bf16, d = 128)
+
+def test_chunked_edge_lengths_around_64():
+    """Lengths around the chunk size (2, 3, 63, 64, 65, 127-129, 200) beside
+    decode tokens and an empty sequence, half of them from the trash block."""
+    lengths = [2, 3, 63, 64, 65, 1, 127, 128, 0, 129, 200]
+    b = workloads.random_batch(workloads.BIG, lengths, seed=71, fresh=[i % 2 for i in range(len(lengths))])
+    _check("chunk-edges", b, _g(b, 72), heads=[0, 1, 16, 31])
+
+
+def test_chunked_prefill_workload_sampled_heads():
+    """The gated-delta-net prefill workload (8 sequences of 256-4096 tokens,
+    about 20k tokens) with a decay per key channel; the oracle runs two value
+    heads of every sequence token by token."""
+    b = workloads.config(1)
+    _check("kda-prefill", b, _g(b, 73), heads=[0, 31])
+
+
+def test_strong_decay_blocks_take_the_exact_path():
+    """A decay of -8 per row on some channels over whole 16-row blocks (their
+    own decay e^-128 would overflow the fp32 factor of the block products):
+    those diagonal blocks are computed from the channel sums in fp32."""
+    layer = workloads.Layer(2, 4, 128, 128, 4, "bf16")
+    b = workloads.random_batch(layer, [100, 70, 1], seed=74, fresh=[1, 0, 0])
+    g = _g(b, 75)
+    g[10:40, :, :32] = -8.0    # rows 10-39 of the first sequence, channels 0-31
+    g[120:150, 1, 64:] = -8.0  # rows 20-49 of the second sequence, head 1, channels 64-127
+    _check("strong-decay", b, g)
+
+
+def test_chunked_split_over_two_calls():
+    """A sequence split at rows 70 and 130 over three calls, each continuing
+    from the block the previous one wrote, equals one call (and the oracle)."""
+    layer = workloads.Layer(2, 4, 128, 128, 4, "bf16")
+    b = workloads.random_batch(layer, [200], seed=76)
+    g = _g(b, 77)
+    one, cp1, sp1 = _run(b, g)
+    cut = [0, 70, 130, 200]
+    outs = []
+    cp, sp = b.conv_pool, b.ssm_pool
+    for i in range(3):
+        r0, r1 = cut[i], cut[i + 1]
+        part = workloads.Batch("part", layer, b.x[r0:r1].contiguous(), b.conv_weight, b.g[r0:r1].contiguous(),
+                               b.beta[r0:r1].contiguous(), torch.tensor([0, r1 - r0], dtype=torch.int32),
+                               (b.read_idx if i == 0 else b.write_idx).clone(), b.write_idx.clone(), cp, sp)
+        o, cp, sp = _run(part, g[r0:r1].contiguous())
+        outs.append(o)
+    wb = int(b.write_idx[0])
+    assert torch.equal(cp.view(torch.uint8), cp1.view(torch.uint8)), "conv states differ"
+    assert rel_l2(torch.cat(outs).double().numpy(), one.double().numpy()) <= 1e-2
+    assert rel_l2(sp[wb].double().numpy(), sp1[wb].double().numpy()) <= 1e-2
+    _check("kda-one-pass", b, g)
