@@ -12,8 +12,9 @@ sequences of one token, 1024-block pool), the mixed continuous-batching step
 (64 decode tokens beside 4 prefill chunks of 512 tokens), the long prefill (4
 sequences of 32768 tokens), the prefill step planned on the device and
 replayed from a HIP graph, the standalone varlen conv layer (gdn_varlen_conv on
-the prefill rows), the fork copy (gdn_state_copy of 256 blocks), the KDA decode
-and the Mamba2 scan, each with the roofline of its dominant kernel and the
+the prefill rows), the fork copy (gdn_state_copy of 256 blocks), the KDA layer
+(a decay per key channel) on the prefill and decode workloads, and the Mamba2
+scan, each with the roofline of its dominant kernel and the
 per-kernel event timings.  Every gated-delta-net entry also carries the fp64
 CPU oracle timed on the host cores on the same workload (`cpu_baseline`), and
 the parity of its first call (from fresh pools) against that oracle run: max
@@ -87,7 +88,7 @@ def load_traffic(kernel: str, workload: str):
     path = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
     if not os.path.exists(path):
         return None
-    src = {"chunk_scan": "gdn_chunk.hip", "token_recurrent": "gdn_recurrent.hip",
+    src = {"chunk_scan": "gdn_chunk.hip", "token_recurrent": "gdn_recurrent.hip", "kda_chunk": "kda_chunk.hip",
            "conv_silu_norm": "gdn_conv.hip", "ssd_scan": "ssd_scan.hip", "ssd_token": "ssd_scan.hip"}.get(kernel)
     if src is None:
         return None
@@ -400,16 +401,34 @@ def run_ssd(cfg: int, steps: int, warmup: int):
             "kernels": {k: {"avg_ms": v[0] / max(v[1], 1), "launches": v[1]} for k, v in kt.items()}}
 
 
-def run_kda_decode(steps: int, warmup: int):
-    """The KDA layer (kda_varlen_forward) on the decode workload: 256 one-token
-    sequences of the gated-delta-net layer's shape, with a decay per key channel."""
+def kda_flops(layer, lengths, c: int = 64) -> float:
+    """Algorithmic flops of the chunked KDA form: the decay differs per value
+    head and key channel, so every value head has its own decayed Gram pair
+    (4 c^2 d_k) beside the same dense products as the gated delta rule
+    (2 c^2 (d_k + d_v) + 2 c^2 d_v + 6 c d_k d_v + 2/3 c^3)."""
+    Hv, dk, dv = layer.num_v_heads, layer.head_k_dim, layer.head_v_dim
+    total = 0.0
+    for L in lengths:
+        if L < 2:
+            continue
+        full, rem = divmod(L, c)
+        for cc in [c] * full + ([rem] if rem else []):
+            total += Hv * (4 * cc * cc * dk + 2 * cc * cc * (dk + dv) + 2 * cc * cc * dv + 6 * cc * dk * dv
+                           + (2.0 / 3.0) * cc ** 3)
+    return total
+
+
+def run_kda(cfg_id: int, steps: int, warmup: int):
+    """The KDA layer (kda_varlen_forward: the gated delta rule with a decay per
+    key channel) on the gated-delta-net prefill (cfg_id 1: chunk kernel on
+    MFMA) or decode (cfg_id 2: token kernel, HBM bound) workload."""
     import numpy as np
     import torch
 
     import linear_attention_state_amd as gdn
     import workloads
 
-    b = workloads.config(2)
+    b = workloads.config(cfg_id)
     L = b.layer
     dev = torch.device("cuda", 0)
     d = {k: getattr(b, k).to(dev).contiguous() for k in
@@ -420,14 +439,15 @@ def run_kda_decode(steps: int, warmup: int):
     out = torch.empty(b.total_tokens, L.num_v_heads, L.head_v_dim, dtype=L.torch_act, device=dev)
     stream = torch.cuda.current_stream(dev)
     cu_host = b.cu_seqlens.clone()
+    ws = torch.empty(max(gdn.gdn_workspace_size(L, b.total_tokens, len(b.lengths)), 1), dtype=torch.uint8,
+                     device=dev)
 
     def step():
         gdn.kda_varlen_forward(L, d["x"], d["conv_weight"], g, d["beta"], d["cu_seqlens"], cu_host, d["read_idx"],
-                               d["write_idx"], d["conv_pool"], d["ssm_pool"], out, stream=stream.cuda_stream)
+                               d["write_idx"], d["conv_pool"], d["ssm_pool"], out, stream=stream.cuda_stream,
+                               workspace=ws)
 
-    for _ in range(warmup):
-        step()
-    torch.cuda.synchronize()
+    warmed = warm(step, torch.cuda.synchronize, warmup)
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     ev0.record(stream)
     for _ in range(steps):
@@ -440,15 +460,25 @@ def run_kda_decode(steps: int, warmup: int):
         step()
     kt = gdn.gdn_kernel_times()
     gdn.gdn_kernel_timing(False)
-    k_ms = kt["token_recurrent"][0] / kt["token_recurrent"][1]
-    # the gated-delta-net decode bytes, with g per key channel instead of per head
-    work = token_path_bytes(L, b.total_tokens) + b.total_tokens * L.num_v_heads * (L.head_k_dim - 1) * 4
-    roof = {"bound": "hbm", "achieved": work / (k_ms * 1e-3) / 1e9, "peak": PEAK_HBM / 1e9, "unit": "GB/s",
-            "kernel": "token_recurrent", "traffic": load_traffic("token_recurrent", "kda_decode")}
+    status = gdn.gdn_device_status(clear=True)
+    if cfg_id == 2:
+        k_ms = kt["token_recurrent"][0] / kt["token_recurrent"][1]
+        # the gated-delta-net decode bytes, with g per key channel instead of per head
+        work = token_path_bytes(L, b.total_tokens) + b.total_tokens * L.num_v_heads * (L.head_k_dim - 1) * 4
+        roof = {"bound": "hbm", "achieved": work / (k_ms * 1e-3) / 1e9, "peak": PEAK_HBM / 1e9, "unit": "GB/s",
+                "kernel": "token_recurrent", "traffic": load_traffic("token_recurrent", "kda_decode")}
+        what = "KDA decode: 256 sequences of 1 token"
+    else:
+        k_ms = kt["kda_chunk"][0] / kt["kda_chunk"][1]
+        roof = {"bound": "mfma", "achieved": kda_flops(L, b.lengths) / (k_ms * 1e-3) / 1e12,
+                "peak": PEAK_BF16_MFMA / 1e12, "unit": "TFLOP/s", "kernel": "kda_chunk",
+                "traffic": load_traffic("kda_chunk", "kda_prefill")}
+        what = "KDA prefill: %d sequences, lengths %s, T=%d" % (len(b.lengths), b.lengths, b.total_tokens)
     roof["frac"] = roof["achieved"] / roof["peak"]
-    return {"workload": "KDA decode: 256 sequences of 1 token, H_k=16, H_v=32, d=128, W=4, bf16, "
-                        "g per key channel, 1024-block pool",
+    return {"workload": what + "; H_k=16, H_v=32, d=128, W=4, bf16, g per key channel, %d-block pool"
+                        % b.ssm_pool.shape[0],
             "value": b.total_tokens / (ms * 1e-3), "unit": "tokens/s", "ms_per_step": ms, "roofline": roof,
+            "warmup_steps_run": warmed, "device_status": status,
             "kernels": {k: {"avg_ms": v[0] / max(v[1], 1), "launches": v[1]} for k, v in kt.items()}}
 
 
@@ -568,7 +598,7 @@ def main():
     ap.add_argument("--no-long", action="store_true", help="skip the long-prefill entry (4 x 32768 tokens)")
     ap.add_argument("--no-mamba2", action="store_true", help="skip the Mamba2 scan entries")
     ap.add_argument("--only", choices=["prefill", "decode", "mixed", "conv", "copy", "graph", "long", "mamba2_prefill",
-                                       "mamba2_decode", "kda_decode"], default=None,
+                                       "mamba2_decode", "kda_prefill", "kda_decode"], default=None,
                     help="run one workload alone and print its numbers (profiling runs)")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="run only a device-to-device copy of this many bytes (calibrates HBM byte counters)")
@@ -593,8 +623,8 @@ def main():
     if args.only == "copy":
         print(json.dumps(run_state_copy(args.steps, args.warmup)), flush=True)
         return
-    if args.only == "kda_decode":
-        print(json.dumps(run_kda_decode(args.steps, args.warmup)), flush=True)
+    if args.only in ("kda_prefill", "kda_decode"):
+        print(json.dumps(run_kda(1 if args.only == "kda_prefill" else 2, args.steps, args.warmup)), flush=True)
         return
     if args.only in ("mamba2_prefill", "mamba2_decode"):
         print(json.dumps(run_ssd(0 if args.only == "mamba2_prefill" else 1, args.steps, args.warmup)), flush=True)
@@ -655,7 +685,8 @@ def main():
         line["conv"] = run_conv(args.steps, args.warmup)
         line["state_copy"] = run_state_copy(args.steps, args.warmup)
     if not args.no_mamba2:
-        line["kda_decode"] = run_kda_decode(args.steps, args.warmup)
+        line["kda_prefill"] = run_kda(1, args.steps, args.warmup)
+        line["kda_decode"] = run_kda(2, args.steps, args.warmup)
         line["mamba2_prefill"] = run_ssd(0, args.steps, args.warmup)
         line["mamba2_decode"] = run_ssd(1, args.steps, args.warmup)
     if not args.no_cpu_baseline:

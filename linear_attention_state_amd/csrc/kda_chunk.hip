@@ -23,22 +23,33 @@
 // block bj of Kr = e^{gamma_e - gamma_j} o k (B side), times a channel factor for
 // pairs two or more blocks apart.  On a diagonal block the B side is Kr times
 // e^{gamma_{16b-1} - gamma_{16b+15}} >= 1, the block's own decay: bounded by the
-// decay over 16 rows, and computed exactly in fp32 instead (exact_diag) for a
+// decay over 16 rows, and computed exactly in fp32 instead (kda_exact) for a
 // block where that factor would leave the range of fp32.  Only differences of
-// running sums are exponentiated.
+// running sums are exponentiated; the tiles of the state pass take their
+// factors as products of two factors <= 1 (e^{gamma_t} = e^{gamma_{16b-1}}
+// e^{gamma_t - gamma_{16b-1}}, and likewise for Kh).
 //
 // Work split: one 512-thread workgroup (8 waves) per (sequence, value head),
-// chunk by chunk in three phases separated by workgroup barriers:
-//   1. all waves: thread (block b, channel c) loads its 16 rows of q, k, v (the
-//      conv output, normalised) and g, forms gamma within the block and across
-//      the blocks, and writes the decay-scaled tiles Kb, Qb, Kr, Kt, Qt, Kh and V;
-//   2. all waves: the ten A blocks and ten P blocks (MFMA), then T = (I + A)^-1
-//      (diagonal blocks by fp32 forward substitution, the others by block
-//      products) written as T2^T = (T diag(b))^T;
-//   3. waves 0-3: wave w owns d_v columns [32w, 32w+32) of the fp32 state in
-//      registers and computes Kt S, U = T2 (V - Kt S), (Qt S)^T, O^T and the
-//      state update (each state row scaled by its channel's e^{gamma_last}).
-// All products are v_mfma_f32_16x16x32_bf16 (bf16 operands, fp32 accumulate).
+// walking the chunks as a two-stage pipeline with one workgroup barrier per
+// step.  In step i:
+//   waves 0-3 (state)     chunk i: wave w owns d_v columns [32w, 32w+32) of the
+//                         fp32 state in registers and computes Kt S, U =
+//                         T2 (V - Kt S), (Qt S)^T, O^T and the state update;
+//   waves 4-7 (producers) chunk i+1: wave 4+b owns the 16 rows of block b, in
+//                         MFMA operand layout (lane (r, g): row 16b + r,
+//                         channels 32kk + 8g .. +7), loaded from global memory
+//                         one step ahead with 16-byte buffer loads; it forms the
+//                         running sums within the block across the lanes of a
+//                         DPP row, keeps Kb and Qb in registers as the A
+//                         operands of its row of A and P blocks, writes Kr,
+//                         Kt, Qt, Kh and V; wave 4 then solves T.
+// The producers wait among themselves on LDS flags.  Kt, V and Qt of chunk i+1
+// go into single buffers once the state waves have flagged that they have read
+// chunk i's (Kt and V early in the state pass, Qt in its middle); Kh, P, T2 and
+// e^{gamma_last} are double-buffered.  The barriers wait for LDS traffic only,
+// so the loads of the next chunk and the output stores stay in flight across
+// them.  All products are v_mfma_f32_16x16x32_bf16 (bf16 operands, fp32
+// accumulate).
 #include "gdn_device.h"
 #include "gdn_mfma.h"
 
@@ -55,27 +66,30 @@ constexpr float kMaxGrowth = 80.f;
 
 // LDS.  The [64][128] bf16 tiles use the swizzled row-major layout of swz_off.
 struct alignas(16) KSmem {
-  uint16_t kb[BT * D];   // e^{gamma_t - gamma_{16b-1}} o k_t: A side of the A blocks (t in block b)
-  uint16_t qb[BT * D];   // e^{gamma_t - gamma_{16b-1}} o q_t: A side of the P blocks
-  uint16_t kr[BT * D];   // e^{gamma_{16b+15} - gamma_t} o k_t: B side of the A and P blocks
-  uint16_t kt[BT * D];   // e^{gamma_t} o k_t: K S
-  uint16_t qt[BT * D];   // e^{gamma_t} o q_t: Q S
-  uint16_t kh[BT * D];   // e^{gamma_last - gamma_t} o k_t: the state update
+  uint16_t kr[BT * D];         // e^{gamma_{16b+15} - gamma_t} o k_t: B side of the A and P blocks
+  uint16_t kt[BT * D];         // e^{gamma_t} o k_t: K S
+  uint16_t qt[BT * D];         // e^{gamma_t} o q_t: Q S
   uint16_t v[BT * D];
-  uint16_t p[BT * PP];         // P [t][j in pair order]; blocks above the diagonal stay zero
-  uint16_t t2[11][16 * PB];    // (T diag(b))^T as 16 x 16 blocks, and the zero block (slot 10)
+  uint16_t kh[2][BT * D];      // e^{gamma_last - gamma_t} o k_t: the state update, chunk parity
+  uint16_t p[2][BT * PP];      // P [t][j in pair order]; blocks above the diagonal stay zero
+  uint16_t t2[2][11][16 * PB]; // (T diag(b))^T as 16 x 16 blocks, and the zero block (slot 10)
   uint16_t ab[6][16 * PB];     // A^T blocks below the diagonal
   uint16_t tb[5][16 * PB];     // T^T blocks 00, 11, 22, 33 and 32
   float at[4 * 16 * PA];       // diagonal blocks of A, fp32, [block][j][t]
   float beta[BT];
   float btot[4][D];            // per block and channel: the sum of g over its rows (<= 0)
+  float eoff[4][D];            // e^{gamma_{16b-1}}: Kt and Qt from the A-side factor
+  float etail[4][D];           // e^{gamma_last - gamma_{16b+15}}: Kh from the B-side factor
   float fac[7][D];             // B-side channel factors: pairs (2,0), (3,1), (3,0); diagonal blocks 0..3
-  float glast[D];              // e^{gamma_last} per channel
-  float gex[16 * D];           // exact_diag: gamma within the block, per row and channel
-  int diag_exact;              // bit b: diagonal block b computed in fp32
+  float glast[2][D];           // e^{gamma_last} per channel, chunk parity
+  int c1[KNS];                 // state wave w has read Kt and V of chunks < c1[w]
+  int c2[KNS];                 // ... and Qt
+  int pf[4];                   // producer sync counters
+  int dex[4];                  // block b's diagonal is computed in fp32
 };
 static_assert(sizeof(KSmem) <= 160 * 1024, "LDS");
-static_assert(D * KPS * 4 <= 5 * BT * D * 2, "state staging fits the first five tiles");
+static_assert(D * KPS * 4 <= 6 * BT * D * 2, "state staging fits the first six tiles");
+static_assert(16 * D * 4 <= BT * D * 2, "exact-path running sums fit the Kr tile");
 
 struct KSeq {
   int s, r0, L, N, m, h;
@@ -101,101 +115,78 @@ __device__ __forceinline__ bf16x8 scaled8(bf16x8 x, const float* f) {
   return r;
 }
 
-// ---- phase 1: the decay-scaled tiles of chunk c, by the 256 producer threads:
-// thread (bp, c) owns channel c of the 32 rows of blocks 2bp and 2bp+1; rows past
-// the sequence's end are zero with g = 0 and b = 0, so they change nothing.
-// Pass 1 (before the barrier the caller places): each block's total decay.
-__device__ __forceinline__ void kda_totals(KSmem& sm, const ScanArgs& a, const KSeq& q, int chunk, int tp) {
-  const int bp = tp >> 7, ch = tp & 127, Hv = a.num_v_heads;
-#pragma unroll 1
-  for (int hb = 0; hb < 2; ++hb) {
-    const int b = 2 * bp + hb;
-    const int64_t rb = (int64_t)q.r0 + chunk * BT + 16 * b;
-    const int nv = max(0, min(16, q.L - chunk * BT - 16 * b));
-    const float* gp = a.g + ((rb * Hv + q.m) * D + ch);
-    float acc = 0.f;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) acc += i < nv ? gp[i * (int64_t)Hv * D] : 0.f;
-    sm.btot[b][ch] = acc;
-    if (-acc > kMaxGrowth) atomicOr(&sm.diag_exact, 1 << b);
-  }
-  if (tp < BT) {
-    const int t = tp, in = chunk * BT + t < q.L;
-    sm.beta[t] = in ? a.beta[((int64_t)q.r0 + chunk * BT + t) * Hv + q.m] : 0.f;
-  }
+// Inclusive prefix sum over the 16 lanes of each DPP row (the 16 rows of a block).
+__device__ __forceinline__ float row_scan16(float v) {
+  v += dpp_move<0x111, 0xf>(v);  // row_shr:1
+  v += dpp_move<0x112, 0xf>(v);  // row_shr:2
+  v += dpp_move<0x114, 0xf>(v);  // row_shr:4
+  v += dpp_move<0x118, 0xf>(v);  // row_shr:8
+  return v;
 }
 
-// Pass 2 (after it): the tiles, four rows at a time (g read again, now from the caches).
-__device__ __forceinline__ void kda_tiles(KSmem& sm, const ScanArgs& a, const KSeq& q, int chunk, int tp) {
-  const int bp = tp >> 7, ch = tp & 127;
+// Compiler-only ordering point: a wave's own LDS writes reach its later reads in
+// program order, so cross-lane exchanges within one wave need no hardware wait.
+__device__ __forceinline__ void lds_order() { asm volatile("" ::: "memory"); }
+
+// The four producer waves meet: every LDS write made before it by any of them
+// is visible after it.
+__device__ __forceinline__ void psync(KSmem& sm, int pw, int& seq) {
+  ++seq;
+  set_flag(&sm.pf[pw], seq);
+#pragma unroll
+  for (int w = 0; w < 4; ++w)
+    if (w != pw) wait_flag(&sm.pf[w], seq);
+}
+
+// ---- producers: the raw rows of one 16-row block of chunk c, held in registers
+// from one step to the next.  Lane (r, g): row 16 pw + r, channels 32kk + 8g .. +7
+// of q, k and v (bf16) and g (fp32), and b of the row.  Rows past the sequence's
+// end read as zero (g = 0, b = 0), so they change nothing.
+struct KRaw {
+  bf16x8 k[4], q[4], v[4];
+  f32x4 g[8];  // g[2kk + h]: channels 32kk + 8g + 4h .. +3
+  float beta;
+};
+
+// part: 1 = g and b, 2 = q, k and v, 3 = both
+__device__ __forceinline__ void kda_load(KRaw& x, const ScanArgs& a, const KSeq& q, int c, int pw, const Lane& ln,
+                                         int part) {
   const int Hv = a.num_v_heads, C = a.channels, Hk = a.num_k_heads;
-  const uint16_t* y = reinterpret_cast<const uint16_t*>(a.y);
-  float tot[4], glast = 0.f;
+  const int row0 = BT * c + 16 * pw;
+  const int nv = max(0, min(16, q.L - row0));
+  const int64_t grow = (int64_t)q.r0 + row0;
+  const __amdgpu_buffer_rsrc_t ry =
+      make_rsrc(reinterpret_cast<const uint16_t*>(a.y) + grow * C, (uint32_t)(nv * C * 2));
+  const __amdgpu_buffer_rsrc_t rg = make_rsrc(a.g + grow * Hv * D, (uint32_t)(nv * Hv * D * 4));
+  const __amdgpu_buffer_rsrc_t rb = make_rsrc(a.beta + grow * Hv, (uint32_t)(nv * Hv * 4));
+  const int yo = ln.r * C + 8 * ln.g;
+  const int go = (ln.r * Hv + q.m) * D + 8 * ln.g;
+  if (part & 1) {
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    tot[j] = sm.btot[j][ch];
-    glast += tot[j];
-  }
-  // rows are walked with rolled loops: unrolled, their addresses (hoisted out of
-  // the chunk loop) would not fit the registers
-#pragma unroll 1
-  for (int hb = 0; hb < 2; ++hb) {
-    const int b = 2 * bp + hb;
-    const int64_t rb = (int64_t)q.r0 + chunk * BT + 16 * b;
-    const int nv = max(0, min(16, q.L - chunk * BT - 16 * b));
-    const float acc = tot[b];
-    const float off = b == 0 ? 0.f : b == 1 ? tot[0] : b == 2 ? tot[0] + tot[1] : tot[0] + tot[1] + tot[2];
-    const float* gp = a.g + ((rb * Hv + q.m) * D + ch);
-    const uint16_t* kp = y + rb * C + (int64_t)Hk * D + q.h * D + ch;
-    const uint16_t* qp = y + rb * C + (int64_t)q.h * D + ch;
-    const uint16_t* vp = y + rb * C + 2 * (int64_t)Hk * D + (int64_t)q.m * D + ch;
-    float gl = 0.f;
-#pragma unroll 1
-    for (int i0 = 0; i0 < 16; i0 += 4) {
-      float g[4], k[4], qq[4], v[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int i = i0 + e;
-        const bool in = i < nv;
-        const int64_t ro = in ? i : 0;  // a clamped row for the loads past the end
-        g[e] = gp[ro * (int64_t)Hv * D];
-        k[e] = bf16_bits_to_f32(kp[ro * C]);
-        qq[e] = bf16_bits_to_f32(qp[ro * C]);
-        v[e] = bf16_bits_to_f32(vp[ro * C]);
-        if (!in) g[e] = k[e] = qq[e] = v[e] = 0.f;
-      }
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        gl += g[e];
-        const int o = swz_off(16 * b + i0 + e, ch);
-        const float e1 = __expf(gl);                 // e^{gamma_t - gamma_{16b-1}}
-        const float e2 = __expf(acc - gl);           // e^{gamma_{16b+15} - gamma_t}
-        const float e3 = __expf(off + gl);           // e^{gamma_t}
-        const float e4 = __expf(glast - off - gl);   // e^{gamma_last - gamma_t}
-        sm.kb[o] = f32_to_bf16_bits(k[e] * e1);
-        sm.qb[o] = f32_to_bf16_bits(qq[e] * e1);
-        sm.kr[o] = f32_to_bf16_bits(k[e] * e2);
-        sm.kt[o] = f32_to_bf16_bits(k[e] * e3);
-        sm.qt[o] = f32_to_bf16_bits(qq[e] * e3);
-        sm.kh[o] = f32_to_bf16_bits(k[e] * e4);
-        sm.v[o] = f32_to_bf16_bits(v[e]);
-      }
+    for (int kk = 0; kk < 4; ++kk) {
+      x.g[2 * kk] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rg, 4 * (go + 32 * kk), 0, 0));
+      x.g[2 * kk + 1] =
+          __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rg, 4 * (go + 32 * kk + 4), 0, 0));
     }
-    // diagonal block b: e^{-(sum of g over the block)} >= 1, kept finite (a block
-    // past the bound is computed exactly instead)
-    sm.fac[3 + b][ch] = __expf(fminf(-acc, kMaxGrowth));
+    x.beta = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rb, 4 * (ln.r * Hv + q.m), 0, 0));
   }
-  if (bp == 0) {
-    sm.fac[0][ch] = __expf(tot[1]);           // pair (2,0): e^{gamma_31 - gamma_15}
-    sm.fac[1][ch] = __expf(tot[2]);           // pair (3,1): e^{gamma_47 - gamma_31}
-    sm.fac[2][ch] = __expf(tot[1] + tot[2]);  // pair (3,0): e^{gamma_47 - gamma_15}
-    sm.glast[ch] = __expf(glast);
+  if (part & 2) {
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      x.q[kk] =
+          __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(ry, 2 * (yo + q.h * D + 32 * kk), 0, 0));
+      x.k[kk] = __builtin_bit_cast(
+          bf16x8, __builtin_amdgcn_raw_buffer_load_b128(ry, 2 * (yo + (Hk + q.h) * D + 32 * kk), 0, 0));
+      x.v[kk] = __builtin_bit_cast(
+          bf16x8, __builtin_amdgcn_raw_buffer_load_b128(ry, 2 * (yo + 2 * Hk * D + q.m * D + 32 * kk), 0, 0));
+    }
   }
 }
 
-// ---- phase 2a: A and P blocks.  Producer wave w (0..3): row block bi = w of A
-// and of P; both share the B-side operands of the blocks bj <= bi.
-__device__ __forceinline__ void kda_blocks(KSmem& sm, int bi, const Lane& ln) {
+// ---- producers: row block bi of A and of P.  Kb and Qb of block bi come from
+// registers; the B side (Kr of the blocks bj <= bi) from LDS.
+__device__ __forceinline__ void kda_pairs(KSmem& sm, int bi, const Lane& ln, const bf16x8 (&kb)[4],
+                                          const bf16x8 (&qb)[4], uint16_t* pbuf) {
   int roff[4];
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk) roff[kk] = swz_off(ln.r, 32 * kk + 8 * ln.g);
@@ -206,11 +197,9 @@ __device__ __forceinline__ void kda_blocks(KSmem& sm, int bi, const Lane& ln) {
     for (int kk = 0; kk < 4; ++kk) {
       bf16x8 yr = lds8(sm.kr + roff[kk] + 16 * bj * D);
       if (fs >= 0) yr = scaled8(yr, &sm.fac[fs][32 * kk + 8 * ln.g]);
-      const bf16x8 ka = lds8(sm.kb + roff[kk] + 16 * bi * D);
-      const bf16x8 qa = lds8(sm.qb + roff[kk] + 16 * bi * D);
       // A: lane holds A[16bi + 4g + i][16bj + r]; P transposed: P[16bi + r][16bj + 4g + i]
-      acc = mfma(ka, yr, acc);
-      pacc = mfma(yr, qa, pacc);
+      acc = mfma(kb[kk], yr, acc);
+      pacc = mfma(yr, qb[kk], pacc);
     }
     {
       const int j = 16 * bj + ln.r;
@@ -229,30 +218,33 @@ __device__ __forceinline__ void kda_blocks(KSmem& sm, int bi, const Lane& ln) {
       float v[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) v[i] = (16 * bj + 4 * ln.g + i <= t) ? pacc[i] : 0.f;
-      st4bf(&sm.p[t * PP + perm(16 * bj + 4 * ln.g)], v[0], v[1], v[2], v[3]);
+      st4bf(&pbuf[t * PP + perm(16 * bj + 4 * ln.g)], v[0], v[1], v[2], v[3]);
     }
   }
 }
 
-// ---- phase 2b (only for a diagonal block whose own decay leaves the fp32 range):
-// its A and P entries from the channel sums themselves, with every
-// e^{gamma_t - gamma_j} formed from the difference of running sums (<= 0).  All
-// threads; block b's gamma (relative to the row before it) is first put in gex.
-__device__ void exact_diag(KSmem& sm, const ScanArgs& a, const KSeq& q, int chunk, int b, int tid) {
+// ---- producers (only for a diagonal block whose own decay leaves the fp32
+// range): its A and P entries from the channel sums themselves, with every
+// e^{gamma_t - gamma_j} formed from the difference of running sums (<= 0).
+// Block b's running sums (relative to the row before it) are first put over the
+// Kr tile, which the A and P blocks no longer read.  tp: producer thread 0..255.
+__device__ void kda_exact(KSmem& sm, const ScanArgs& a, const KSeq& q, int chunk, int b, int tp, int pw,
+                          uint16_t* pbuf, int& seq) {
   const int Hv = a.num_v_heads, C = a.channels, Hk = a.num_k_heads;
   const int64_t rb = (int64_t)q.r0 + chunk * BT + 16 * b;
   const int nv = max(0, min(16, q.L - chunk * BT - 16 * b));
   const uint16_t* y = reinterpret_cast<const uint16_t*>(a.y);
-  if (tid < D) {
+  float* gex = reinterpret_cast<float*>(sm.kr);
+  if (tp < D) {
     float acc = 0.f;
     for (int i = 0; i < 16; ++i) {
-      if (i < nv) acc += a.g[((rb + i) * Hv + q.m) * D + tid];
-      sm.gex[i * D + tid] = acc;
+      if (i < nv) acc += a.g[((rb + i) * Hv + q.m) * D + tp];
+      gex[i * D + tp] = acc;
     }
   }
-  __syncthreads();  // (every wave of the workgroup meets it: see the main loop)
+  psync(sm, pw, seq);
   // 136 pairs (j <= t) x 4 channel quarters; the quarters of a pair are adjacent lanes
-  for (int w = tid; w < 136 * 4; w += KNT / 2) {
+  for (int w = tp; w < 136 * 4; w += 256) {
     const int pr = w >> 2, qd = w & 3;
     int t = 0, rem = pr;  // pair index -> (t, j), j <= t
     while (rem > t) { rem -= t + 1; ++t; }
@@ -263,7 +255,7 @@ __device__ void exact_diag(KSmem& sm, const ScanArgs& a, const KSeq& q, int chun
         const float kt = bf16_bits_to_f32(y[(rb + t) * C + (int64_t)Hk * D + q.h * D + c]);
         const float kj = bf16_bits_to_f32(y[(rb + j) * C + (int64_t)Hk * D + q.h * D + c]);
         const float qt = bf16_bits_to_f32(y[(rb + t) * C + (int64_t)q.h * D + c]);
-        const float e = __expf(sm.gex[t * D + c] - sm.gex[j * D + c]);
+        const float e = __expf(gex[t * D + c] - gex[j * D + c]);
         sa = fmaf(kt * kj, e, sa);
         sp = fmaf(qt * kj, e, sp);
       }
@@ -275,20 +267,139 @@ __device__ void exact_diag(KSmem& sm, const ScanArgs& a, const KSeq& q, int chun
     if (qd == 0) {
       const int tt = 16 * b + t, jj = 16 * b + j;
       if (j < t) sm.at[(16 * b + j) * PA + t] = sm.beta[tt] * sa;
-      sm.p[tt * PP + perm(jj)] = f32_to_bf16_bits(sp);
+      pbuf[tt * PP + perm(jj)] = f32_to_bf16_bits(sp);
     }
+  }
+  psync(sm, pw, seq);  // gex is free again; the exact entries are written
+}
+
+// ---- producers: everything the state pass of chunk c reads.  pw: producer wave
+// 0..3 (its block); x: the raw rows of chunk c, replaced by those of chunk c + 1.
+__device__ __forceinline__ void kda_produce(KSmem& sm, const ScanArgs& a, const KSeq& q, int c, int pw,
+                                            const Lane& ln, KRaw& x, int& seq) {
+  const int lane = 16 * ln.g + ln.r, par = c & 1;
+  // running sums of g within the block (in place), block totals, b
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) x.g[j][e] = row_scan16(x.g[j][e]);
+  bool big = false;
+  if (ln.r == 15) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      *reinterpret_cast<f32x4*>(&sm.btot[pw][32 * (j >> 1) + 8 * ln.g + 4 * (j & 1)]) = x.g[j];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) big = big || (-x.g[j][e] > kMaxGrowth);
+    }
+  }
+  if (ln.g == 0) sm.beta[16 * pw + ln.r] = x.beta;
+  const bool dex_own = __builtin_amdgcn_ballot_w64(big) != 0;
+  if (lane == 0) sm.dex[pw] = dex_own ? 1 : 0;
+  psync(sm, pw, seq);  // every block's totals
+  // per-channel factors of this block, two channels per lane
+  {
+    const int ch = 2 * lane;
+    float2 t[4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) t[b] = *reinterpret_cast<const float2*>(&sm.btot[b][ch]);
+    float off0 = 0.f, off1 = 0.f, gl0 = 0.f, gl1 = 0.f;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      if (b < pw) {
+        off0 += t[b].x;
+        off1 += t[b].y;
+      }
+      gl0 += t[b].x;
+      gl1 += t[b].y;
+    }
+    const float2 own = *reinterpret_cast<const float2*>(&sm.btot[pw][ch]);
+    *reinterpret_cast<float2*>(&sm.eoff[pw][ch]) = make_float2(__expf(off0), __expf(off1));
+    *reinterpret_cast<float2*>(&sm.etail[pw][ch]) =
+        make_float2(__expf(gl0 - off0 - own.x), __expf(gl1 - off1 - own.y));
+    *reinterpret_cast<float2*>(&sm.fac[3 + pw][ch]) =
+        make_float2(__expf(fminf(-own.x, kMaxGrowth)), __expf(fminf(-own.y, kMaxGrowth)));
+    if (pw == 0) *reinterpret_cast<float2*>(&sm.glast[par][ch]) = make_float2(__expf(gl0), __expf(gl1));
+    if (pw == 2) *reinterpret_cast<float2*>(&sm.fac[0][ch]) = make_float2(__expf(t[1].x), __expf(t[1].y));
+    if (pw == 3) {
+      *reinterpret_cast<float2*>(&sm.fac[1][ch]) = make_float2(__expf(t[2].x), __expf(t[2].y));
+      *reinterpret_cast<float2*>(&sm.fac[2][ch]) = make_float2(__expf(t[1].x + t[2].x), __expf(t[1].y + t[2].y));
+    }
+  }
+  lds_order();
+  // the tiles of the block's rows (Kt and V once every state wave has read
+  // chunk c - 1's)
+#pragma unroll
+  for (int w = 0; w < KNS; ++w) wait_flag(&sm.c1[w], c);
+  bf16x8 kb[4], qb[4], qt[4];
+  const int row = 16 * pw + ln.r;
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) {
+    const int cb = 32 * kk + 8 * ln.g;
+    const f32x4 tot[2] = {*reinterpret_cast<const f32x4*>(&sm.btot[pw][cb]),
+                          *reinterpret_cast<const f32x4*>(&sm.btot[pw][cb + 4])};
+    const f32x4 eo[2] = {*reinterpret_cast<const f32x4*>(&sm.eoff[pw][cb]),
+                         *reinterpret_cast<const f32x4*>(&sm.eoff[pw][cb + 4])};
+    const f32x4 et[2] = {*reinterpret_cast<const f32x4*>(&sm.etail[pw][cb]),
+                         *reinterpret_cast<const f32x4*>(&sm.etail[pw][cb + 4])};
+    bf16x8 kr, kh, kt;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float gm = x.g[2 * kk + (e >> 2)][e & 3];
+      const float e1 = __expf(gm);                        // e^{gamma_t - gamma_{16b-1}}
+      const float e2 = __expf(tot[e >> 2][e & 3] - gm);   // e^{gamma_{16b+15} - gamma_t}
+      const float e3 = e1 * eo[e >> 2][e & 3];            // e^{gamma_t}
+      const float e4 = e2 * et[e >> 2][e & 3];            // e^{gamma_last - gamma_t}
+      const float kv = (float)x.k[kk][e], qv = (float)x.q[kk][e];
+      kb[kk][e] = (__bf16)(kv * e1);
+      qb[kk][e] = (__bf16)(qv * e1);
+      kr[e] = (__bf16)(kv * e2);
+      kt[e] = (__bf16)(kv * e3);
+      qt[kk][e] = (__bf16)(qv * e3);
+      kh[e] = (__bf16)(kv * e4);
+    }
+    const int o = swz_off(row, cb);
+    *reinterpret_cast<bf16x8*>(&sm.kr[o]) = kr;
+    *reinterpret_cast<bf16x8*>(&sm.kh[par][o]) = kh;
+    *reinterpret_cast<bf16x8*>(&sm.kt[o]) = kt;
+    *reinterpret_cast<bf16x8*>(&sm.v[o]) = x.v[kk];
+  }
+  // the next chunk's rows load while this one's products and solve run (not
+  // before this point: the compiler would hold both chunks' rows at once); the
+  // solving wave loads its q, k and v after the solve
+  lds_order();
+  if (c + 1 < q.N) kda_load(x, a, q, c + 1, pw, ln, pw == 0 ? 1 : 3);
+  psync(sm, pw, seq);  // Kr of every block
+  kda_pairs(sm, pw, ln, kb, qb, sm.p[par]);
+  const int ex = sm.dex[0] | (sm.dex[1] << 1) | (sm.dex[2] << 2) | (sm.dex[3] << 3);  // uniform
+  if (ex) {
+    psync(sm, pw, seq);  // the A and P blocks no longer read Kr
+    for (int b = 0; b < 4; ++b)
+      if (ex & (1 << b)) kda_exact(sm, a, q, c, b, 64 * pw + lane, pw, sm.p[par], seq);
+  }
+  psync(sm, pw, seq);  // every A block
+  // Qt once every state wave has read chunk c - 1's
+#pragma unroll
+  for (int w = 0; w < KNS; ++w) wait_flag(&sm.c2[w], c);
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk)
+    *reinterpret_cast<bf16x8*>(&sm.qt[swz_off(row, 32 * kk + 8 * ln.g)]) = qt[kk];
+  if (pw == 0) {
+    solve_diag(sm.at, sm.tb, &sm.t2[par][0][0], sm.beta, lane);
+    solve_blocks(sm.ab, sm.tb, &sm.t2[par][0][0], sm.beta, ln);
+    lds_order();
+    if (c + 1 < q.N) kda_load(x, a, q, c + 1, pw, ln, 2);
   }
 }
 
-// ---- phase 3: the state pass of one chunk for d_v columns [32 wv, 32 wv + 32)
+// ---- the state pass of one chunk for d_v columns [32 wv, 32 wv + 32)
 // (the arithmetic of the gated-delta-rule state pass with the decays in the tiles).
 struct StateLanes {
   int roff[4], toff[4][2], voffs[KNB], col[KNB], t2off, poff, olane;
 };
 
 __device__ __forceinline__ void kda_state_step(KSmem& sm, f32x4 (&sacc)[8][KNB], const StateLanes& sl,
-                                               const ScanArgs& a, const KSeq& q, int chunk, const Lane& ln) {
-  const int lg = ln.g;
+                                               const ScanArgs& a, const KSeq& q, int chunk, const Lane& ln, int wv) {
+  const int lg = ln.g, par = chunk & 1;
   // ---- Kt S (rows t, columns n)
   f32x4 ks[4][KNB];
 #pragma unroll
@@ -327,6 +438,8 @@ __device__ __forceinline__ void kda_state_step(KSmem& sm, f32x4 (&sacc)[8][KNB],
 #pragma unroll
       for (int i = 0; i < 4; ++i) ks[tb][nb][i] = (float)vv[i] - ks[tb][nb][i];
     }
+  set_flag(&sm.c1[wv], chunk + 1);  // Kt and V of this chunk are read
+  const uint16_t* t2 = &sm.t2[par][0][0];
   f32x4 u[4][KNB];
 #pragma unroll
   for (int tb = 0; tb < 4; ++tb)
@@ -339,8 +452,8 @@ __device__ __forceinline__ void kda_state_step(KSmem& sm, f32x4 (&sacc)[8][KNB],
     for (int nb = 0; nb < KNB; ++nb) xb[nb] = pair_operand(ks[2 * kk][nb], ks[2 * kk + 1][nb]);
 #pragma unroll
     for (int tb = 2 * kk; tb < 4; ++tb) {
-      const bf16x8 a2 = cat(ldtr(&sm.t2[t2_slot(tb, 2 * kk)][0] + sl.t2off),
-                            ldtr(&sm.t2[t2_slot(tb, 2 * kk + 1)][0] + sl.t2off));
+      const bf16x8 a2 = cat(ldtr(t2 + t2_slot(tb, 2 * kk) * 16 * PB + sl.t2off),
+                            ldtr(t2 + t2_slot(tb, 2 * kk + 1) * 16 * PB + sl.t2off));
 #pragma unroll
       for (int nb = 0; nb < KNB; ++nb) u[tb][nb] = mfma(a2, xb[nb], u[tb][nb]);
     }
@@ -372,6 +485,8 @@ __device__ __forceinline__ void kda_state_step(KSmem& sm, f32x4 (&sacc)[8][KNB],
       for (int nb = 0; nb < KNB; ++nb) ot[nb][tb] = mfma(sb[nb], qa[cur][tb], ot[nb][tb]);
   }
   fence();
+  set_flag(&sm.c2[wv], chunk + 1);  // Qt of this chunk is read
+  const uint16_t* pb = sm.p[par];
   bf16x8 ub[2][KNB];
 #pragma unroll
   for (int k2 = 0; k2 < 2; ++k2)
@@ -381,24 +496,25 @@ __device__ __forceinline__ void kda_state_step(KSmem& sm, f32x4 (&sacc)[8][KNB],
   for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
     for (int tb = 2 * kk; tb < 4; ++tb) {
-      const bf16x8 pa = lds8(sm.p + sl.poff + 16 * tb * PP + 32 * kk);
+      const bf16x8 pa = lds8(pb + sl.poff + 16 * tb * PP + 32 * kk);
 #pragma unroll
       for (int nb = 0; nb < KNB; ++nb) ot[nb][tb] = mfma(ub[kk][nb], pa, ot[nb][tb]);
     }
   // ---- S <- diag(e^{gamma_last}) S + Kh^T U (register row d holds state row sigma(d))
 #pragma unroll
   for (int db = 0; db < 8; ++db) {
-    const f32x4 f = *reinterpret_cast<const f32x4*>(&sm.glast[sigma(16 * db + 4 * lg)]);
+    const f32x4 f = *reinterpret_cast<const f32x4*>(&sm.glast[par][sigma(16 * db + 4 * lg)]);
 #pragma unroll
     for (int nb = 0; nb < KNB; ++nb) sacc[db][nb] *= f;
   }
+  const uint16_t* kh = sm.kh[par];
 #pragma unroll
   for (int half = 0; half < 2; ++half) {
     fence();
     bf16x8 kt[8];
 #pragma unroll
     for (int db = 0; db < 8; ++db) {
-      const uint16_t* src = sm.kh + sl.toff[db >> 1][db & 1] + 32 * half * D;
+      const uint16_t* src = kh + sl.toff[db >> 1][db & 1] + 32 * half * D;
       kt[db] = cat(ldtr(src), ldtr(src + 16 * D));
     }
     fence();
@@ -441,7 +557,7 @@ __global__ __launch_bounds__(KNT) void kda_chunk_kernel(ScanArgs a, SeqOrder ord
   const Lane ln{lane & 15, lane >> 4, lane & 3, (lane >> 2) & 3};
 
   // the state [d][n] staged through the first tiles (free before the first chunk)
-  float* sst = reinterpret_cast<float*>(&sm.kb[0]);
+  float* sst = reinterpret_cast<float*>(&sm.kr[0]);
   const int64_t head_off = (int64_t)q.m * D * D;
   {
     const __amdgpu_buffer_rsrc_t rs = make_rsrc(
@@ -453,18 +569,22 @@ __global__ __launch_bounds__(KNT) void kda_chunk_kernel(ScanArgs a, SeqOrder ord
       *reinterpret_cast<u32x4*>(&sst[row * KPS + 4 * c4]) = __builtin_amdgcn_raw_buffer_load_b128(rs, 16 * f, 0, 0);
     }
   }
-  // the zero block of T2 and the P blocks above the diagonal are read by the
-  // full-width products and never written (p lies outside the staging area)
+  // the zero blocks of T2 and the P blocks above the diagonal are read by the
+  // full-width products and never written (they lie outside the staging area)
   {
     const u32x4 zero = {0u, 0u, 0u, 0u};
-    for (int i = tid; i < BT * PP / 8; i += KNT) reinterpret_cast<u32x4*>(&sm.p[0])[i] = zero;
-    for (int i = tid; i < 16 * PB / 8; i += KNT) reinterpret_cast<u32x4*>(&sm.t2[10][0])[i] = zero;
+    for (int i = tid; i < 2 * BT * PP / 8; i += KNT) reinterpret_cast<u32x4*>(&sm.p[0][0])[i] = zero;
+    for (int i = tid; i < 2 * 16 * PB / 8; i += KNT)
+      reinterpret_cast<u32x4*>(&sm.t2[i / (16 * PB / 8)][10][0])[i % (16 * PB / 8)] = zero;
+    if (tid < KNS) {
+      sm.c1[tid] = 0;
+      sm.c2[tid] = 0;
+      sm.pf[tid] = 0;
+    }
   }
   __syncthreads();
-  // Two roles with the same sequence of workgroup barriers per chunk:
-  //   [1] diag_exact cleared  [2] block totals  [3] tiles  [4] A and P blocks
-  //   (2 per diagonal block computed exactly)  [5] diagonal solve  [6] block solve
-  //   [7] state pass done, the tiles are free again.
+  // Per step, one workgroup barrier: the state waves run chunk i while the
+  // producers prepare chunk i + 1 (step -1: chunk 0 alone).
   if (wv < KNS) {
     // ---- state waves: the fp32 state of their columns in registers
     StateLanes sl;
@@ -489,22 +609,11 @@ __global__ __launch_bounds__(KNT) void kda_chunk_kernel(ScanArgs a, SeqOrder ord
     sl.t2off = (4 * lg + ln.i) * PB + 4 * ln.a;
     sl.poff = li * PP + 8 * lg;
     sl.olane = 2 * (li * Hv * D + 8 * lg + q.m * D + n0);
-    __syncthreads();  // the staged state has been read
+    lds_barrier();  // the staged state has been read
+    lds_barrier();  // step -1
     for (int c = 0; c < q.N; ++c) {
-      __syncthreads();  // [1]
-      __syncthreads();  // [2]
-      __syncthreads();  // [3]
-      __syncthreads();  // [4]
-      const int ex = sm.diag_exact;  // uniform
-      for (int b = 0; b < 4; ++b)
-        if (ex & (1 << b)) {
-          __syncthreads();
-          __syncthreads();
-        }
-      __syncthreads();  // [5]
-      __syncthreads();  // [6]
-      kda_state_step(sm, sacc, sl, a, q, c, ln);
-      __syncthreads();  // [7]
+      kda_state_step(sm, sacc, sl, a, q, c, ln, wv);
+      lds_barrier();  // step c
     }
 #pragma unroll
     for (int db = 0; db < 8; ++db)
@@ -513,30 +622,21 @@ __global__ __launch_bounds__(KNT) void kda_chunk_kernel(ScanArgs a, SeqOrder ord
 #pragma unroll
         for (int i = 0; i < 4; ++i) sst[sigma(16 * db + 4 * lg + i) * KPS + sl.col[nb]] = sacc[db][nb][i];
   } else {
-    // ---- producer waves: tiles, A and P blocks, T
-    const int tp = tid - 64 * KNS;
-    __syncthreads();  // the state waves have read the staged state
+    // ---- producer waves
+    const int pw = wv - KNS;
+    KRaw x;
+    kda_load(x, a, q, 0, pw, ln, 3);
+    int seq = 0;
+    lds_barrier();  // the state waves have read the staged state
     for (int c = 0; c < q.N; ++c) {
-      if (tp == 0) sm.diag_exact = 0;
-      __syncthreads();  // [1]
-      kda_totals(sm, a, q, c, tp);
-      __syncthreads();  // [2]
-      kda_tiles(sm, a, q, c, tp);
-      __syncthreads();  // [3]
-      kda_blocks(sm, wv - KNS, ln);
-      __syncthreads();  // [4]
-      const int ex = sm.diag_exact;  // uniform
-      for (int b = 0; b < 4; ++b)
-        if (ex & (1 << b)) {
-          exact_diag(sm, a, q, c, b, tp);  // one barrier inside
-          __syncthreads();
-        }
-      if (wv == KNS) solve_diag(sm.at, sm.tb, &sm.t2[0][0], sm.beta, lane);
-      __syncthreads();  // [5]
-      if (wv == KNS) solve_blocks(sm.ab, sm.tb, &sm.t2[0][0], sm.beta, ln);
-      __syncthreads();  // [6]
-      __syncthreads();  // [7]
+      // the lane's addresses are recomputed every step: hoisted out of the
+      // loop, they would not fit the registers beside the rows and operands
+      int l = lane, w = pw;
+      asm volatile("" : "+v"(l), "+s"(w));
+      kda_produce(sm, a, q, c, w, Lane{l & 15, l >> 4, l & 3, (l >> 2) & 3}, x, seq);
+      lds_barrier();  // step c - 1
     }
+    lds_barrier();  // step N - 1
   }
   __syncthreads();
   {
