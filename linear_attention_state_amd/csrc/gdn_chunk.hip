@@ -754,8 +754,11 @@ __device__ __forceinline__ void conv_compute(const ScanArgs& a, const ConvTask& 
       xw[(4 - j) & 3][2 * i] = __uint_as_float(sd.hx[j - 1][i] << 16);
       xw[(4 - j) & 3][2 * i + 1] = __uint_as_float(sd.hx[j - 1][i] & 0xffff0000u);
     }
+  // the task is the same for the whole workgroup: its rows in scalar registers
+  // keep the descriptor scalar
+  const int r0 = __builtin_amdgcn_readfirstlane(k.r0), n = __builtin_amdgcn_readfirstlane(k.n);
   const __amdgpu_buffer_rsrc_t ys =
-      make_rsrc(reinterpret_cast<const uint16_t*>(a.y) + (int64_t)k.r0 * C, (uint32_t)(k.n * C * 2));
+      make_rsrc(reinterpret_cast<const uint16_t*>(a.y) + (int64_t)r0 * C, (uint32_t)(n * C * 2));
 #pragma unroll
   for (int r = 0; r < kConvTaskRows; ++r) {
 #pragma unroll
@@ -782,7 +785,7 @@ __device__ __forceinline__ void conv_compute(const ScanArgs& a, const ConvTask& 
     u32x4 o;
 #pragma unroll
     for (int i = 0; i < 4; ++i) o[i] = pack_bf16x2(yv[2 * i], yv[2 * i + 1]);
-    if (r < k.n) __builtin_amdgcn_raw_buffer_store_b128(o, ys, (r * C + k.c0) * 2, 0, kStoreDeviceScope);
+    if (r < n) __builtin_amdgcn_raw_buffer_store_b128(o, ys, (r * C + k.c0) * 2, 0, kStoreDeviceScope);
   }
 }
 
@@ -814,7 +817,7 @@ __device__ void conv_phase(Smem& sm, const ScanArgs& a, const SeqOrder& ord, con
   const uint64_t t_begin = __builtin_amdgcn_s_memrealtime();
   if (tid == 0) sm.task = __hip_atomic_fetch_add(fc.sync, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   lds_barrier();
-  int t = sm.task;
+  int t = __builtin_amdgcn_readfirstlane(sm.task);
   lds_barrier();  // every thread has read sm.task before thread 0 writes it again
   ConvTask k{};
   ConvSide<W> cur, nxt;
@@ -824,7 +827,7 @@ __device__ void conv_phase(Smem& sm, const ScanArgs& a, const SeqOrder& ord, con
   }
   if (tid == 0) sm.task = claim_after(fc, t, total, last, latest, t_begin);
   lds_barrier();
-  int u = sm.task;
+  int u = __builtin_amdgcn_readfirstlane(sm.task);
   u32x4 rx[kConvTaskRows];
   const u32x4* st = conv_stage(sm);
   while (t < total) {
@@ -852,7 +855,7 @@ __device__ void conv_phase(Smem& sm, const ScanArgs& a, const SeqOrder& ord, con
     if (tid == 0) __hip_atomic_fetch_add(&fc.sync[1 + k.rank], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     k = kn;
     t = u;
-    u = sm.task;
+    u = __builtin_amdgcn_readfirstlane(sm.task);
   }
 }
 
@@ -1107,8 +1110,8 @@ __device__ void stream_helper(Smem& sm, const ScanArgs& a, const SeqOrder& ord, 
     k = kn;
     r = ur;
     t = ut;
-    ur = sm.task;
-    ut = sm.task2;
+    ur = __builtin_amdgcn_readfirstlane(sm.task);
+    ut = __builtin_amdgcn_readfirstlane(sm.task2);
     lds_barrier();  // read before wave 0 writes them again
   }
 }
@@ -1139,7 +1142,7 @@ __global__ __launch_bounds__(NT) void chunk_scan_kernel(ScanArgs a, SeqOrder ord
     if (threadIdx.x == 0)
       sm.task = __hip_atomic_fetch_add(fc.sync + 1 + fc.first[fc.n], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __syncthreads();
-    bid = sm.task;
+    bid = __builtin_amdgcn_readfirstlane(sm.task);
     __syncthreads();  // read before a helper overwrites it
     if (bid < fc.helpers) {
       stream_helper_w(sm, a, ord, fc);
@@ -1193,7 +1196,8 @@ __global__ __launch_bounds__(NT) void chunk_scan_kernel(ScanArgs a, SeqOrder ord
   {
     const __amdgpu_buffer_rsrc_t rs = make_rsrc(
         reinterpret_cast<const float*>(reinterpret_cast<const char*>(a.ssm_pool) +
-                                       (int64_t)a.read_idx[q.s] * a.ssm_stride) + head_off, D * D * 4);
+                                       (int64_t)__builtin_amdgcn_readfirstlane(a.read_idx[q.s]) * a.ssm_stride) +
+            head_off, D * D * 4);
 #pragma unroll
     for (int it = 0; it < D * D / 4 / NT; ++it) {
       const int f = tid + NT * it, row = f >> 5, c4 = f & 31;
@@ -1229,7 +1233,8 @@ __global__ __launch_bounds__(NT) void chunk_scan_kernel(ScanArgs a, SeqOrder ord
   lds_barrier();
   {
     const __amdgpu_buffer_rsrc_t rs = make_rsrc(
-        reinterpret_cast<float*>(reinterpret_cast<char*>(a.ssm_pool) + (int64_t)a.write_idx[q.s] * a.ssm_stride) +
+        reinterpret_cast<float*>(reinterpret_cast<char*>(a.ssm_pool) +
+                                 (int64_t)__builtin_amdgcn_readfirstlane(a.write_idx[q.s]) * a.ssm_stride) +
             head_off, D * D * 4);
 #pragma unroll
     for (int it = 0; it < D * D / 4 / NT; ++it) {

@@ -153,7 +153,8 @@ __device__ __forceinline__ void kda_load(KRaw& x, const ScanArgs& a, const KSeq&
                                          int part) {
   const int Hv = a.num_v_heads, C = a.channels, Hk = a.num_k_heads;
   const int row0 = BT * c + 16 * pw;
-  const int nv = max(0, min(16, q.L - row0));
+  // uniform by construction; in scalar registers, so the buffer descriptors are too
+  const int nv = __builtin_amdgcn_readfirstlane(max(0, min(16, q.L - row0)));
   const int64_t grow = (int64_t)q.r0 + row0;
   const __amdgpu_buffer_rsrc_t ry =
       make_rsrc(reinterpret_cast<const uint16_t*>(a.y) + grow * C, (uint32_t)(nv * C * 2));
@@ -562,7 +563,8 @@ __global__ __launch_bounds__(KNT) void kda_chunk_kernel(ScanArgs a, SeqOrder ord
   {
     const __amdgpu_buffer_rsrc_t rs = make_rsrc(
         reinterpret_cast<const float*>(reinterpret_cast<const char*>(a.ssm_pool) +
-                                       (int64_t)a.read_idx[q.s] * a.ssm_stride) + head_off, D * D * 4);
+                                       (int64_t)__builtin_amdgcn_readfirstlane(a.read_idx[q.s]) * a.ssm_stride) +
+            head_off, D * D * 4);
 #pragma unroll
     for (int it = 0; it < D * D / 4 / KNT; ++it) {
       const int f = tid + KNT * it, row = f >> 5, c4 = f & 31;
@@ -641,7 +643,8 @@ __global__ __launch_bounds__(KNT) void kda_chunk_kernel(ScanArgs a, SeqOrder ord
   __syncthreads();
   {
     const __amdgpu_buffer_rsrc_t rs = make_rsrc(
-        reinterpret_cast<float*>(reinterpret_cast<char*>(a.ssm_pool) + (int64_t)a.write_idx[q.s] * a.ssm_stride) +
+        reinterpret_cast<float*>(reinterpret_cast<char*>(a.ssm_pool) +
+                                 (int64_t)__builtin_amdgcn_readfirstlane(a.write_idx[q.s]) * a.ssm_stride) +
             head_off, D * D * 4);
 #pragma unroll
     for (int it = 0; it < D * D / 4 / KNT; ++it) {
