@@ -418,6 +418,18 @@ def kda_flops(layer, lengths, c: int = 64) -> float:
     return total
 
 
+def kda_chunk_bytes(layer, lengths) -> float:
+    """Algorithmic HBM bytes of the KDA chunk kernel: per row of a chunked
+    sequence its conv output row (q, k, v), its decays g (fp32, one per value
+    head and key channel), b and its output row; per sequence the fp32 state
+    read and written."""
+    s = 2 if layer.act_dtype == "bf16" else 4
+    Hv, dk, dv = layer.num_v_heads, layer.head_k_dim, layer.head_v_dim
+    rows = sum(L for L in lengths if L >= 2)
+    seqs = sum(1 for L in lengths if L >= 2)
+    return rows * (layer.conv_channels * s + Hv * dk * 4 + Hv * 4 + Hv * dv * s) + seqs * 2 * Hv * dk * dv * 4
+
+
 def run_kda(cfg_id: int, steps: int, warmup: int):
     """The KDA layer (kda_varlen_forward: the gated delta rule with a decay per
     key channel) on the gated-delta-net prefill (cfg_id 1: chunk kernel on
@@ -473,6 +485,10 @@ def run_kda(cfg_id: int, steps: int, warmup: int):
         roof = {"bound": "mfma", "achieved": kda_flops(L, b.lengths) / (k_ms * 1e-3) / 1e12,
                 "peak": PEAK_BF16_MFMA / 1e12, "unit": "TFLOP/s", "kernel": "kda_chunk",
                 "traffic": load_traffic("kda_chunk", "kda_prefill")}
+        # about 117 flop per algorithmic byte, below the chip's 312: the bytes bound it first
+        kb = kda_chunk_bytes(L, b.lengths)
+        roof["hbm_bytes"] = kb
+        roof["hbm_frac"] = kb / (k_ms * 1e-3) / PEAK_HBM
         what = "KDA prefill: %d sequences, lengths %s, T=%d" % (len(b.lengths), b.lengths, b.total_tokens)
     roof["frac"] = roof["achieved"] / roof["peak"]
     return {"workload": what + "; H_k=16, H_v=32, d=128, W=4, bf16, g per key channel, %d-block pool"

@@ -327,11 +327,13 @@ __device__ __forceinline__ void kda_produce(KSmem& sm, const ScanArgs& a, const 
     }
   }
   lds_order();
-  // the tiles of the block's rows (Kt and V once every state wave has read
-  // chunk c - 1's)
+  // the tiles of the block's rows (Kt, V and Qt once every state wave has read
+  // chunk c - 1's: in the state pass both flags come well before this point)
 #pragma unroll
   for (int w = 0; w < KNS; ++w) wait_flag(&sm.c1[w], c);
-  bf16x8 kb[4], qb[4], qt[4];
+#pragma unroll
+  for (int w = 0; w < KNS; ++w) wait_flag(&sm.c2[w], c);
+  bf16x8 kb[4], qb[4];
   const int row = 16 * pw + ln.r;
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk) {
@@ -342,7 +344,7 @@ __device__ __forceinline__ void kda_produce(KSmem& sm, const ScanArgs& a, const 
                          *reinterpret_cast<const f32x4*>(&sm.eoff[pw][cb + 4])};
     const f32x4 et[2] = {*reinterpret_cast<const f32x4*>(&sm.etail[pw][cb]),
                          *reinterpret_cast<const f32x4*>(&sm.etail[pw][cb + 4])};
-    bf16x8 kr, kh, kt;
+    bf16x8 kr, kh, kt, qt;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const float gm = x.g[2 * kk + (e >> 2)][e & 3];
@@ -355,7 +357,7 @@ __device__ __forceinline__ void kda_produce(KSmem& sm, const ScanArgs& a, const 
       qb[kk][e] = (__bf16)(qv * e1);
       kr[e] = (__bf16)(kv * e2);
       kt[e] = (__bf16)(kv * e3);
-      qt[kk][e] = (__bf16)(qv * e3);
+      qt[e] = (__bf16)(qv * e3);
       kh[e] = (__bf16)(kv * e4);
     }
     const int o = swz_off(row, cb);
@@ -363,12 +365,15 @@ __device__ __forceinline__ void kda_produce(KSmem& sm, const ScanArgs& a, const 
     *reinterpret_cast<bf16x8*>(&sm.kh[par][o]) = kh;
     *reinterpret_cast<bf16x8*>(&sm.kt[o]) = kt;
     *reinterpret_cast<bf16x8*>(&sm.v[o]) = x.v[kk];
+    *reinterpret_cast<bf16x8*>(&sm.qt[o]) = qt;
   }
-  // the next chunk's rows load while this one's products and solve run (not
-  // before this point: the compiler would hold both chunks' rows at once); the
-  // solving wave loads its q, k and v after the solve
+  // the solving wave loads the next chunk's g and b now (not before this point:
+  // the compiler would hold both chunks' rows at once), its q, k and v after
+  // the solve; the other producers load all of it at the end of the step.  A
+  // wave stalls while it issues these loads (each touches 16 rows), so they
+  // stay off the path to the A blocks.
   lds_order();
-  if (c + 1 < q.N) kda_load(x, a, q, c + 1, pw, ln, pw == 0 ? 1 : 3);
+  if (c + 1 < q.N && pw == 0) kda_load(x, a, q, c + 1, pw, ln, 1);
   psync(sm, pw, seq);  // Kr of every block
   kda_pairs(sm, pw, ln, kb, qb, sm.p[par]);
   const int ex = sm.dex[0] | (sm.dex[1] << 1) | (sm.dex[2] << 2) | (sm.dex[3] << 3);  // uniform
@@ -378,18 +383,12 @@ __device__ __forceinline__ void kda_produce(KSmem& sm, const ScanArgs& a, const 
       if (ex & (1 << b)) kda_exact(sm, a, q, c, b, 64 * pw + lane, pw, sm.p[par], seq);
   }
   psync(sm, pw, seq);  // every A block
-  // Qt once every state wave has read chunk c - 1's
-#pragma unroll
-  for (int w = 0; w < KNS; ++w) wait_flag(&sm.c2[w], c);
-#pragma unroll
-  for (int kk = 0; kk < 4; ++kk)
-    *reinterpret_cast<bf16x8*>(&sm.qt[swz_off(row, 32 * kk + 8 * ln.g)]) = qt[kk];
   if (pw == 0) {
     solve_diag(sm.at, sm.tb, &sm.t2[par][0][0], sm.beta, lane);
     solve_blocks(sm.ab, sm.tb, &sm.t2[par][0][0], sm.beta, ln);
-    lds_order();
-    if (c + 1 < q.N) kda_load(x, a, q, c + 1, pw, ln, 2);
   }
+  lds_order();
+  if (c + 1 < q.N) kda_load(x, a, q, c + 1, pw, ln, pw == 0 ? 2 : 3);
 }
 
 // ---- the state pass of one chunk for d_v columns [32 wv, 32 wv + 32)
