@@ -156,10 +156,11 @@ int device_cus(hipStream_t st) {
 bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
 
 // ---- optional per-kernel event timing (measurement only)
-enum { K_CONV = 0, K_CHUNK, K_TOKEN, K_TAIL, K_COPY, K_ZERO, K_PLAN, K_SSD, K_SSD_TOKEN, K_KDA_CHUNK, K_COUNT };
+enum { K_CONV = 0, K_CHUNK, K_TOKEN, K_TAIL, K_COPY, K_ZERO, K_PLAN, K_SSD, K_SSD_TOKEN, K_KDA_CHUNK, K_CHUNK_GEN,
+       K_COUNT };
 const char* const kKernelNames[K_COUNT] = {"conv_silu_norm", "chunk_scan", "token_recurrent", "conv_state_commit",
                                            "state_copy", "task_counter_reset", "device_plan", "ssd_scan",
-                                           "ssd_token", "kda_chunk"};
+                                           "ssd_token", "kda_chunk", "chunk_generic"};
 
 struct Timing {
   std::mutex mu;
@@ -499,6 +500,8 @@ int forward_impl(const gdn_layer_desc* desc, const void* x, const void* conv_wei
   sa.num_seqs = num_seqs; sa.num_blocks = num_blocks; sa.num_k_heads = desc->num_k_heads;
   sa.num_v_heads = desc->num_v_heads; sa.channels = C;
   const bool chunked = bf16 && gdn::chunk_supported(desc->head_k_dim, desc->head_v_dim);
+  // every other head size, and the fp32 layer: the fp32 chunk kernel
+  const bool generic = !chunked && gdn::chunk_generic_supported(desc->head_k_dim, desc->head_v_dim);
 
   gdn::TailArgs ta{};
   ta.x = x; ta.cu = cu_seqlens; ta.read_idx = read_idx; ta.write_idx = write_idx;
@@ -569,12 +572,22 @@ int forward_impl(const gdn_layer_desc* desc, const void* x, const void* conv_wei
       e = timed(K_CHUNK, st, [&] { return gdn::launch_chunk(sa, none, fc, desc->head_k_dim, desc->head_v_dim, st); });
       if (e != hipSuccess) return fail(GDN_EHIP, "chunk scan launch: %s", hipGetErrorString(e));
       ta.fused = plan + gdn::kPlanFused;
+    } else if (generic && total_tokens > 0) {
+      e = timed(K_CONV, st, [&] { return gdn::launch_conv(ca, W, bf16, true, st); });
+      if (e != hipSuccess) return fail(GDN_EHIP, "conv launch: %s", hipGetErrorString(e));
+      static thread_local gdn::SeqOrder none_g;
+      none_g.n = 0;
+      sa.min_len = 2; sa.max_len = INT_MAX;
+      e = timed(K_CHUNK_GEN, st, [&] {
+        return gdn::launch_chunk_generic(sa, none_g, desc->head_k_dim, desc->head_v_dim, bf16, st);
+      });
+      if (e != hipSuccess) return fail(GDN_EHIP, "chunk scan launch: %s", hipGetErrorString(e));
     }
     if (fork) {
       e = join_side(st, side);
       if (e != hipSuccess) return fail(GDN_EHIP, "side stream: %s", hipGetErrorString(e));
     } else {
-      sa.min_len = 0; sa.max_len = chunked ? 1 : INT_MAX;
+      sa.min_len = 0; sa.max_len = (chunked || generic) ? 1 : INT_MAX;
       e = timed(K_TOKEN, st, [&] { return gdn::launch_recurrent(sa, desc->head_k_dim, desc->head_v_dim, bf16, st); });
       if (e != hipSuccess) return fail(GDN_EHIP, "token path launch: %s", hipGetErrorString(e));
     }
@@ -709,11 +722,35 @@ int forward_impl(const gdn_layer_desc* desc, const void* x, const void* conv_wei
     if (e != hipSuccess) return fail(GDN_EHIP, "chunk scan launch: %s", hipGetErrorString(e));
     tails_done = fc.n > 0;
   }
+  if (generic && n_long > 0) {
+    // conv kernel first (the fp32 kernel reads y), longest sequences first
+    e = timed(K_CONV, st, [&] { return gdn::launch_conv(ca, W, bf16, true, st); });
+    if (e != hipSuccess) return fail(GDN_EHIP, "conv launch: %s", hipGetErrorString(e));
+    static thread_local gdn::SeqOrder order_g;
+    order_g.n = 0;
+    if (n_long <= gdn::kMaxOrder && num_seqs <= 65535) {
+      std::vector<std::pair<int, int>> lens;
+      lens.reserve(n_long);
+      for (int i = 0; i < num_seqs; ++i) {
+        const int L = cu_seqlens_host[i + 1] - cu_seqlens_host[i];
+        if (L >= 2) lens.push_back({-L, i});
+      }
+      std::stable_sort(lens.begin(), lens.end());
+      for (size_t i = 0; i < lens.size(); ++i) order_g.seq[i] = (uint16_t)lens[i].second;
+      order_g.n = (int32_t)lens.size();
+    }
+    sa.min_len = 2; sa.max_len = INT_MAX;
+    e = timed(K_CHUNK_GEN, st, [&] {
+      return gdn::launch_chunk_generic(sa, order_g, desc->head_k_dim, desc->head_v_dim, bf16, st);
+    });
+    if (e != hipSuccess) return fail(GDN_EHIP, "chunk scan launch: %s", hipGetErrorString(e));
+  }
+  const bool any_chunk = (chunked || generic) && n_long > 0;
   if (fork) {
     e = join_side(st, side);
     if (e != hipSuccess) return fail(GDN_EHIP, "side stream: %s", hipGetErrorString(e));
-  } else if (!chunked || n_short > 0) {
-    sa.min_len = 0; sa.max_len = chunked ? 1 : INT_MAX;
+  } else if (!any_chunk || n_short > 0) {
+    sa.min_len = 0; sa.max_len = any_chunk ? 1 : INT_MAX;
     e = timed(K_TOKEN, st, [&] { return gdn::launch_recurrent(sa, desc->head_k_dim, desc->head_v_dim, bf16, st); });
     if (e != hipSuccess) return fail(GDN_EHIP, "token path launch: %s", hipGetErrorString(e));
   }

@@ -265,6 +265,14 @@ hipError_t launch_chunk(const ScanArgs& a, const SeqOrder& order, const FusedCon
                         hipStream_t st);
 bool chunk_supported(int dk, int dv);
 
+// Chunked prefill for every other head size and the fp32 layer
+// (gdn_chunk_generic.hip): sequences with min_len <= L <= max_len, launch order
+// as for launch_chunk, reading the conv output y (act dtype, normalised); fp32
+// arithmetic; d_k, d_v in {16, 32, 64, 128} (chunk_generic_supported).
+hipError_t launch_chunk_generic(const ScanArgs& a, const SeqOrder& order, int dk, int dv, bool bf16,
+                                hipStream_t st);
+bool chunk_generic_supported(int dk, int dv);
+
 // Kimi delta attention, chunked (kda_chunk.hip): sequences with min_len <= L <= max_len,
 // launch order as for launch_chunk, reading the conv output y (bf16, normalised)
 // and g [T][H_v][d_k]; d_k = d_v = 128 only (kda_chunk_supported).
