@@ -12,9 +12,10 @@ sequences of one token, 1024-block pool), the mixed continuous-batching step
 (64 decode tokens beside 4 prefill chunks of 512 tokens), the long prefill (4
 sequences of 32768 tokens), the prefill step planned on the device and
 replayed from a HIP graph, the standalone varlen conv layer (gdn_varlen_conv on
-the prefill rows), the fork copy (gdn_state_copy of 256 blocks), the KDA layer
-(a decay per key channel) on the prefill and decode workloads, and the Mamba2
-scan, each with the roofline of its dominant kernel and the
+the prefill rows), the fork copy (gdn_state_copy of 256 blocks), the fp32
+chunk kernel on the prefill lengths for the all-fp32 layer and for a bf16 layer
+with 64-wide heads, the KDA layer (a decay per key channel) on the prefill and
+decode workloads, and the Mamba2 scan, each with the roofline of its dominant kernel and the
 per-kernel event timings.  Every gated-delta-net entry also carries the fp64
 CPU oracle timed on the host cores on the same workload (`cpu_baseline`), and
 the parity of its first call (from fresh pools) against that oracle run: max
@@ -498,6 +499,62 @@ def run_kda(cfg_id: int, steps: int, warmup: int):
             "kernels": {k: {"avg_ms": v[0] / max(v[1], 1), "launches": v[1]} for k, v in kt.items()}}
 
 
+PEAK_F32_MFMA = 157.3e12  # dense fp32 MFMA, MI355X
+
+
+def run_generic(act: str, d: int, steps: int, warmup: int):
+    """The chunk kernel for other head sizes and the all-fp32 layer
+    (chunk_generic, fp32 MFMA) on the prefill lengths: H_k=16, H_v=32, head
+    size d, activations in `act`, all sequences from the trash block."""
+    import numpy as np
+    import torch
+
+    import linear_attention_state_amd as gdn
+    import workloads
+
+    b1 = workloads.config(1)
+    L = workloads.Layer(16, 32, d, d, 4, act)
+    b = workloads.make_batch(L, b1.lengths, [0] * len(b1.lengths), b1.write_idx.tolist(), 16, [],
+                             np.random.default_rng(1101), "prefill-%s-d%d" % (act, d))
+    dev = torch.device("cuda", 0)
+    dd = {k: getattr(b, k).to(dev).contiguous() for k in
+          ("x", "conv_weight", "g", "beta", "cu_seqlens", "read_idx", "write_idx", "conv_pool", "ssm_pool")}
+    out = torch.empty(b.total_tokens, L.num_v_heads, L.head_v_dim, dtype=L.torch_act, device=dev)
+    ws = torch.empty(max(gdn.gdn_workspace_size(L, b.total_tokens, len(b.lengths)), 1), dtype=torch.uint8,
+                     device=dev)
+    stream = torch.cuda.current_stream(dev)
+    cu_host = b.cu_seqlens.clone()
+
+    def step():
+        gdn.gdn_varlen_forward(L, dd["x"], dd["conv_weight"], dd["g"], dd["beta"], dd["cu_seqlens"], cu_host,
+                               dd["read_idx"], dd["write_idx"], dd["conv_pool"], dd["ssm_pool"], out,
+                               workspace=ws, stream=stream.cuda_stream)
+
+    warmed = warm(step, torch.cuda.synchronize, warmup)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for _ in range(steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / steps
+    gdn.gdn_kernel_timing(True)
+    for _ in range(steps):
+        step()
+    kt = gdn.gdn_kernel_times()
+    gdn.gdn_kernel_timing(False)
+    k_ms = kt["chunk_generic"][0] / kt["chunk_generic"][1]
+    # the operands are fp32 whatever the activations: priced against the fp32 MFMA peak
+    roof = {"bound": "mfma", "achieved": chunk_flops(L, b.lengths) / (k_ms * 1e-3) / 1e12,
+            "peak": PEAK_F32_MFMA / 1e12, "unit": "TFLOP/s", "kernel": "chunk_generic", "traffic": None}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    return {"workload": "prefill lengths %s, T=%d; H_k=16, H_v=32, d_k=d_v=%d, W=4, %s activations, fp32 "
+                        "arithmetic" % (b.lengths, b.total_tokens, d, act),
+            "value": b.total_tokens / (ms * 1e-3), "unit": "tokens/s", "ms_per_step": ms, "roofline": roof,
+            "warmup_steps_run": warmed, "device_status": gdn.gdn_device_status(clear=True),
+            "kernels": {k: {"avg_ms": v[0] / max(v[1], 1), "launches": v[1]} for k, v in kt.items()}}
+
+
 def run_state_copy(steps: int, warmup: int):
     """The fork copy (gdn_state_copy) of 256 blocks of the decode workload's
     1024-block pool into 256 other blocks."""
@@ -614,7 +671,8 @@ def main():
     ap.add_argument("--no-long", action="store_true", help="skip the long-prefill entry (4 x 32768 tokens)")
     ap.add_argument("--no-mamba2", action="store_true", help="skip the Mamba2 scan entries")
     ap.add_argument("--only", choices=["prefill", "decode", "mixed", "conv", "copy", "graph", "long", "mamba2_prefill",
-                                       "mamba2_decode", "kda_prefill", "kda_decode"], default=None,
+                                       "mamba2_decode", "kda_prefill", "kda_decode", "prefill_fp32", "prefill_d64"],
+                    default=None,
                     help="run one workload alone and print its numbers (profiling runs)")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="run only a device-to-device copy of this many bytes (calibrates HBM byte counters)")
@@ -638,6 +696,11 @@ def main():
         return
     if args.only == "copy":
         print(json.dumps(run_state_copy(args.steps, args.warmup)), flush=True)
+        return
+    if args.only in ("prefill_fp32", "prefill_d64"):
+        r = run_generic("f32", 128, args.steps, args.warmup) if args.only == "prefill_fp32" else \
+            run_generic("bf16", 64, args.steps, args.warmup)
+        print(json.dumps(r), flush=True)
         return
     if args.only in ("kda_prefill", "kda_decode"):
         print(json.dumps(run_kda(1 if args.only == "kda_prefill" else 2, args.steps, args.warmup)), flush=True)
@@ -701,6 +764,8 @@ def main():
         line["conv"] = run_conv(args.steps, args.warmup)
         line["state_copy"] = run_state_copy(args.steps, args.warmup)
     if not args.no_mamba2:
+        line["prefill_fp32"] = run_generic("f32", 128, args.steps, args.warmup)
+        line["prefill_d64"] = run_generic("bf16", 64, args.steps, args.warmup)
         line["kda_prefill"] = run_kda(1, args.steps, args.warmup)
         line["kda_decode"] = run_kda(2, args.steps, args.warmup)
         line["mamba2_prefill"] = run_ssd(0, args.steps, args.warmup)
