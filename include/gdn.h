@@ -133,8 +133,15 @@ int gdn_workspace_size(const gdn_layer_desc* desc, int32_t total_tokens,
  * all zero.  read_idx[i] == write_idx[i] is the ordinary in-place continue.
  * stream is a hipStream_t (NULL = the default stream).
  *
- * Launch plan: the conv of the chunked rows runs in its own kernel, inside the
- * chunk kernel before the scans, or (host plan only, when the scans leave at
+ * Paths: sequences of two or more tokens run in chunks of 64 rows in the WY / UT
+ * form, sequences of length 0 and 1 run token by token beside them.  The bf16
+ * layer with d_k = d_v = 128 takes the bf16-operand MFMA chunk kernel
+ * ("chunk_scan"); every other head size, and the all-fp32 layer, take a chunk
+ * kernel that computes in fp32 on the fp32 MFMA ("chunk_generic"), after the
+ * conv kernel has written the normalised rows into the workspace.
+ *
+ * Launch plan (bf16, 128 x 128 heads): the conv of the chunked rows runs in its
+ * own kernel, inside the chunk kernel before the scans, or (host plan only, when the scans leave at
  * least 32 CUs free) streamed by helper workgroups of the chunk kernel while
  * the scans run (the first workgroups to start become the helpers, so no scan
  * waits for a workgroup that has not started); a time model chooses.  The environment variable
@@ -329,7 +336,7 @@ int gdn_device_status(int clear, uint32_t* bits, void* stream);
 typedef struct {
   char name[32];      /* kernel: "conv_silu_norm", "chunk_scan", "token_recurrent", "conv_state_commit",
                          "state_copy", "task_counter_reset", "device_plan", "ssd_scan", "ssd_token",
-                         "kda_chunk" */
+                         "kda_chunk", "chunk_generic" */
   double total_ms;    /* summed event-to-event time of its timed launches */
   int64_t launches;
 } gdn_kernel_time;
