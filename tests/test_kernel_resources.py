@@ -52,3 +52,40 @@ def test_mamba2_scan_kernel_fits_two_waves_per_simd(tmp_path):
     occ = [int(v) for v in re.findall(r"Occupancy \[waves/SIMD\]: (\d+)", text)]
     assert scratch and all(v == 0 for v in scratch), scratch
     assert occ and min(occ) >= 2, occ
+
+
+def _resources(src_name, tmp_path):
+    src = os.path.join(ROOT, "linear_attention_state_amd", "csrc", src_name)
+    flags = [f for f in build.FLAGS if f not in ("-shared", "-fPIC")]
+    cmd = [build.HIPCC, *flags, "--offload-device-only", "-c", "-I", os.path.join(ROOT, "include"), src,
+           "-o", str(tmp_path / "k.o"), "-Rpass-analysis=kernel-resource-usage"]
+    res = subprocess.run(cmd, capture_output=True, text=True, timeout=900)
+    assert res.returncode == 0, res.stderr[-2000:]
+    kernel, seen = None, {}
+    for line in res.stderr.splitlines():
+        m = re.search(r"Function Name: (\S+)", line)
+        if m:
+            kernel = m.group(1)
+        m = re.search(r"ScratchSize \[bytes/lane\]: (\d+)", line)
+        if m and kernel:
+            seen[kernel] = int(m.group(1))
+    return seen
+
+
+@pytest.mark.skipif(not os.path.exists(build.HIPCC), reason="hipcc not installed")
+def test_fp32_chunk_kernel_has_no_scratch(tmp_path):
+    """Every instantiation (d_k, d_v in 16..128, bf16 and fp32 activations) keeps
+    its state tiles in registers without scratch."""
+    seen = {k: v for k, v in _resources("gdn_chunk_generic.hip", tmp_path).items() if "chunk_generic_kernel" in k}
+    assert len(seen) == 32, seen
+    assert all(v == 0 for v in seen.values()), seen
+
+
+@pytest.mark.skipif(not os.path.exists(build.HIPCC), reason="hipcc not installed")
+def test_kda_chunk_kernel_spills_only_outside_its_loops(tmp_path):
+    """The KDA chunk kernel spills a few values that live across the whole
+    sequence loop (stored before it, reloaded after it: at most 64 bytes per
+    lane); a larger scratch size means a spill inside a step."""
+    seen = {k: v for k, v in _resources("kda_chunk.hip", tmp_path).items() if "kda_chunk_kernel" in k}
+    assert len(seen) == 1, seen
+    assert all(v <= 64 for v in seen.values()), seen
