@@ -90,6 +90,7 @@ def load_traffic(kernel: str, workload: str):
     if not os.path.exists(path):
         return None
     src = {"chunk_scan": "gdn_chunk.hip", "token_recurrent": "gdn_recurrent.hip", "kda_chunk": "kda_chunk.hip",
+           "chunk_generic": "gdn_chunk_generic.hip",
            "conv_silu_norm": "gdn_conv.hip", "ssd_scan": "ssd_scan.hip", "ssd_token": "ssd_scan.hip"}.get(kernel)
     if src is None:
         return None
@@ -546,7 +547,8 @@ def run_generic(act: str, d: int, steps: int, warmup: int):
     k_ms = kt["chunk_generic"][0] / kt["chunk_generic"][1]
     # the operands are fp32 whatever the activations: priced against the fp32 MFMA peak
     roof = {"bound": "mfma", "achieved": chunk_flops(L, b.lengths) / (k_ms * 1e-3) / 1e12,
-            "peak": PEAK_F32_MFMA / 1e12, "unit": "TFLOP/s", "kernel": "chunk_generic", "traffic": None}
+            "peak": PEAK_F32_MFMA / 1e12, "unit": "TFLOP/s", "kernel": "chunk_generic",
+            "traffic": load_traffic("chunk_generic", "prefill_fp32" if act == "f32" else "prefill_d64")}
     roof["frac"] = roof["achieved"] / roof["peak"]
     return {"workload": "prefill lengths %s, T=%d; H_k=16, H_v=32, d_k=d_v=%d, W=4, %s activations, fp32 "
                         "arithmetic" % (b.lengths, b.total_tokens, d, act),
