@@ -41,8 +41,11 @@
 //                         one step ahead with 16-byte buffer loads; it forms the
 //                         running sums within the block across the lanes of a
 //                         DPP row, keeps Kb and Qb in registers as the A
-//                         operands of its row of A and P blocks, writes Kr,
-//                         Kt, Qt, Kh and V; wave 4 then solves T.
+//                         operands of its row of A and P blocks (its diagonal
+//                         block first), writes Kr, Kt, Qt, Kh and V;
+//   state wave 0          once its pass is done, T of chunk i+1: the diagonal
+//                         blocks as soon as the producers have flagged theirs,
+//                         the others once every block of A is in.
 // The producers wait among themselves on LDS flags.  Kt, V and Qt of chunk i+1
 // go into single buffers once the state waves have flagged that they have read
 // chunk i's (Kt and V early in the state pass, Qt in its middle); Kh, P, T2 and
@@ -86,6 +89,8 @@ struct alignas(16) KSmem {
   int c2[KNS];                 // ... and Qt
   int pf[4];                   // producer sync counters
   int dex[4];                  // block b's diagonal is computed in fp32
+  int dflag[4];                // producer wave b: its diagonal block of A is final for chunks < dflag[b]
+  int aflag[4];                // ... and all its blocks of A
 };
 static_assert(sizeof(KSmem) <= 160 * 1024, "LDS");
 static_assert(D * KPS * 4 <= 6 * BT * D * 2, "state staging fits the first six tiles");
@@ -186,12 +191,15 @@ __device__ __forceinline__ void kda_load(KRaw& x, const ScanArgs& a, const KSeq&
 
 // ---- producers: row block bi of A and of P.  Kb and Qb of block bi come from
 // registers; the B side (Kr of the blocks bj <= bi) from LDS.
+// The diagonal block comes first and is flagged (when no block of the chunk takes
+// the exact path), so the solver can start on it while the others are formed.
 __device__ __forceinline__ void kda_pairs(KSmem& sm, int bi, const Lane& ln, const bf16x8 (&kb)[4],
-                                          const bf16x8 (&qb)[4], uint16_t* pbuf) {
+                                          const bf16x8 (&qb)[4], uint16_t* pbuf, int flag_val) {
   int roff[4];
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk) roff[kk] = swz_off(ln.r, 32 * kk + 8 * ln.g);
-  for (int bj = 0; bj <= bi; ++bj) {
+  for (int jj = 0; jj <= bi; ++jj) {
+    const int bj = jj == 0 ? bi : jj - 1;
     const int fs = fac_slot(bi, bj);
     f32x4 acc = {0.f, 0.f, 0.f, 0.f}, pacc = acc;
 #pragma unroll
@@ -221,6 +229,7 @@ __device__ __forceinline__ void kda_pairs(KSmem& sm, int bi, const Lane& ln, con
       for (int i = 0; i < 4; ++i) v[i] = (16 * bj + 4 * ln.g + i <= t) ? pacc[i] : 0.f;
       st4bf(&pbuf[t * PP + perm(16 * bj + 4 * ln.g)], v[0], v[1], v[2], v[3]);
     }
+    if (jj == 0 && flag_val > 0) set_flag(&sm.dflag[bi], flag_val);
   }
 }
 
@@ -367,28 +376,35 @@ __device__ __forceinline__ void kda_produce(KSmem& sm, const ScanArgs& a, const 
     *reinterpret_cast<bf16x8*>(&sm.v[o]) = x.v[kk];
     *reinterpret_cast<bf16x8*>(&sm.qt[o]) = qt;
   }
-  // the solving wave loads the next chunk's g and b now (not before this point:
-  // the compiler would hold both chunks' rows at once), its q, k and v after
-  // the solve; the other producers load all of it at the end of the step.  A
-  // wave stalls while it issues these loads (each touches 16 rows), so they
-  // stay off the path to the A blocks.
-  lds_order();
-  if (c + 1 < q.N && pw == 0) kda_load(x, a, q, c + 1, pw, ln, 1);
   psync(sm, pw, seq);  // Kr of every block
-  kda_pairs(sm, pw, ln, kb, qb, sm.p[par]);
   const int ex = sm.dex[0] | (sm.dex[1] << 1) | (sm.dex[2] << 2) | (sm.dex[3] << 3);  // uniform
+  kda_pairs(sm, pw, ln, kb, qb, sm.p[par], ex ? 0 : c + 1);
   if (ex) {
     psync(sm, pw, seq);  // the A and P blocks no longer read Kr
     for (int b = 0; b < 4; ++b)
       if (ex & (1 << b)) kda_exact(sm, a, q, c, b, 64 * pw + lane, pw, sm.p[par], seq);
+    set_flag(&sm.dflag[pw], c + 1);
   }
-  psync(sm, pw, seq);  // every A block
-  if (pw == 0) {
-    solve_diag(sm.at, sm.tb, &sm.t2[par][0][0], sm.beta, lane);
-    solve_blocks(sm.ab, sm.tb, &sm.t2[par][0][0], sm.beta, ln);
-  }
+  set_flag(&sm.aflag[pw], c + 1);  // the solver (state wave 0) takes it from here
+  // the next chunk's rows, at the end of the step (not before this point: the
+  // compiler would hold both chunks' rows at once); a wave stalls while it
+  // issues these loads (each touches 16 rows), so they stay off the path to
+  // the A blocks
   lds_order();
-  if (c + 1 < q.N) kda_load(x, a, q, c + 1, pw, ln, pw == 0 ? 2 : 3);
+  if (c + 1 < q.N) kda_load(x, a, q, c + 1, pw, ln, 3);
+}
+
+// ---- T = (I + A)^-1 of chunk c by state wave 0, once its state pass is done:
+// the diagonal blocks as soon as every producer has flagged its own, the blocks
+// below them once every block of A is in (written as T2 = (T diag(b))^T).
+__device__ __forceinline__ void kda_solve(KSmem& sm, int c, int lane, const Lane& ln) {
+#pragma unroll
+  for (int w = 0; w < 4; ++w) wait_flag(&sm.dflag[w], c + 1);
+  uint16_t* t2 = &sm.t2[c & 1][0][0];
+  solve_diag(sm.at, sm.tb, t2, sm.beta, lane);
+#pragma unroll
+  for (int w = 0; w < 4; ++w) wait_flag(&sm.aflag[w], c + 1);
+  solve_blocks(sm.ab, sm.tb, t2, sm.beta, ln);
 }
 
 // ---- the state pass of one chunk for d_v columns [32 wv, 32 wv + 32)
@@ -581,6 +597,8 @@ __global__ __launch_bounds__(KNT) void kda_chunk_kernel(ScanArgs a, SeqOrder ord
       sm.c1[tid] = 0;
       sm.c2[tid] = 0;
       sm.pf[tid] = 0;
+      sm.dflag[tid] = 0;
+      sm.aflag[tid] = 0;
     }
   }
   __syncthreads();
@@ -611,9 +629,17 @@ __global__ __launch_bounds__(KNT) void kda_chunk_kernel(ScanArgs a, SeqOrder ord
     sl.poff = li * PP + 8 * lg;
     sl.olane = 2 * (li * Hv * D + 8 * lg + q.m * D + n0);
     lds_barrier();  // the staged state has been read
+    if (wv == 0) kda_solve(sm, 0, lane, ln);
     lds_barrier();  // step -1
     for (int c = 0; c < q.N; ++c) {
       kda_state_step(sm, sacc, sl, a, q, c, ln, wv);
+      if (wv == 0 && c + 1 < q.N) {
+        // the solve's lane addresses are formed here each step (hoisted out of
+        // the loop they would push the state wave's registers into scratch)
+        int l = lane;
+        asm volatile("" : "+v"(l));
+        kda_solve(sm, c + 1, l, Lane{l & 15, l >> 4, l & 3, (l >> 2) & 3});
+      }
       lds_barrier();  // step c
     }
 #pragma unroll
