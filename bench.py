@@ -23,6 +23,11 @@ relative L2 error over (sequence, value head) slabs and the bit-exact verdicts.
 
     python bench.py [--gpus 1] [--steps 50] [--warmup 50] [--no-cpu-baseline]
 
+The line also carries `measured_peaks` (the MFMA rate of back-to-back
+products from gdn_mfma_peak_probe, bf16 and fp32, and the HBM rate of the
+library's 1 GiB streaming copy, gdn_hbm_copy_probe, with torch's copy beside it)
+and every roofline its `frac_of_measured` beside `frac`.
+
 Warm-up runs at least `--warmup` steps and at least 60 ms of back-to-back GPU
 work, so the clocks have settled (the first few dozen steps after the inputs
 are uploaded run up to 10% slower) whatever count is asked for; the line
@@ -49,6 +54,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_MFMA = 2.5e15  # dense bf16 MFMA, MI355X
 PEAK_HBM = 8.0e12        # HBM3E, MI355X
+PEAK_F32_MFMA = 157.3e12  # dense fp32 MFMA, MI355X
 METRIC = "GDN layer tokens/s (prefill, decode) at 1 GPU; % MFMA / HBM peak"
 
 
@@ -500,9 +506,6 @@ def run_kda(cfg_id: int, steps: int, warmup: int):
             "kernels": {k: {"avg_ms": v[0] / max(v[1], 1), "launches": v[1]} for k, v in kt.items()}}
 
 
-PEAK_F32_MFMA = 157.3e12  # dense fp32 MFMA, MI355X
-
-
 def run_generic(act: str, d: int, steps: int, warmup: int):
     """The chunk kernel for other head sizes and the all-fp32 layer
     (chunk_generic, fp32 MFMA) on the prefill lengths: H_k=16, H_v=32, head
@@ -662,6 +665,53 @@ def cpu_baseline(batch, first=None):
     return res
 
 
+def measured_peaks() -> dict:
+    """What this device reaches on plain work, to quote kernel rates against:
+    dense MFMA on back-to-back independent products (gdn_mfma_peak_probe, bf16
+    and fp32) and HBM on a 1 GiB streaming copy (gdn_hbm_copy_probe: bytes read
+    plus bytes written), with torch's own device copy of the same buffer beside
+    it."""
+    import torch
+
+    import linear_attention_state_amd as gdn
+
+    bf = gdn.gdn_mfma_peak_probe("bf16", 4096)
+    f32 = gdn.gdn_mfma_peak_probe("f32", 4096)
+    n = 1 << 28
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    copy = gdn.gdn_hbm_copy_probe(src, dst, reps=10)
+    for _ in range(3):
+        dst.copy_(src)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for _ in range(10):
+        dst.copy_(src)
+    ev1.record()
+    torch.cuda.synchronize()
+    torch_gbs = 2.0 * 4 * n * 10 / (ev0.elapsed_time(ev1) * 1e-3) / 1e9
+    del src, dst
+    torch.cuda.empty_cache()
+    return {"mfma_bf16_tflops": bf, "mfma_f32_tflops": f32, "hbm_copy_gbs": copy, "torch_copy_gbs": torch_gbs}
+
+
+def annotate(obj, peaks: dict) -> None:
+    """Adds to every roofline in the line its fraction of the measured peak of
+    the same resource (`frac_of_measured`)."""
+    if isinstance(obj, dict):
+        roof = obj.get("roofline")
+        if isinstance(roof, dict) and "achieved" in roof:
+            if roof["bound"] == "hbm":
+                ref = peaks["hbm_copy_gbs"]
+            elif roof["peak"] == PEAK_F32_MFMA / 1e12:
+                ref = peaks["mfma_f32_tflops"]
+            else:
+                ref = peaks["mfma_bf16_tflops"]
+            roof["frac_of_measured"] = roof["achieved"] / ref
+        for v in obj.values():
+            annotate(v, peaks)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -673,7 +723,7 @@ def main():
     ap.add_argument("--no-long", action="store_true", help="skip the long-prefill entry (4 x 32768 tokens)")
     ap.add_argument("--no-mamba2", action="store_true", help="skip the Mamba2 scan entries")
     ap.add_argument("--only", choices=["prefill", "decode", "mixed", "conv", "copy", "graph", "long", "mamba2_prefill",
-                                       "mamba2_decode", "kda_prefill", "kda_decode", "prefill_fp32", "prefill_d64"],
+                                       "mamba2_decode", "kda_prefill", "kda_decode", "prefill_fp32", "prefill_d64", "peaks"],
                     default=None,
                     help="run one workload alone and print its numbers (profiling runs)")
     ap.add_argument("--copy-bytes", type=int, default=0,
@@ -712,6 +762,9 @@ def main():
         return
     if args.only == "graph":
         print(json.dumps(run_graph(args.steps, args.warmup)), flush=True)
+        return
+    if args.only == "peaks":
+        print(json.dumps(measured_peaks()), flush=True)
         return
     if args.only in ("prefill", "decode", "mixed", "long"):
         r = run({"prefill": 1, "decode": 2, "mixed": 3, "long": 4}[args.only], args.steps, args.warmup)
@@ -774,6 +827,8 @@ def main():
         line["mamba2_decode"] = run_ssd(1, args.steps, args.warmup)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(b, pre["first"])
+    line["measured_peaks"] = measured_peaks()
+    annotate(line, line["measured_peaks"])
     print(json.dumps(line), flush=True)
 
 

@@ -344,6 +344,26 @@ typedef struct {
 int gdn_kernel_timing(int enable);
 int gdn_kernel_times(gdn_kernel_time* out, int32_t max, int32_t* count);
 
+/* Measurement support: the dense MFMA rate the device reaches on back-to-back
+ * independent products (v_mfma_f32_16x16x32_bf16 for dtype GDN_BF16,
+ * v_mfma_f32_16x16x4_f32 for GDN_F32; four waves per SIMD, eight accumulator
+ * chains per wave, `iters` rounds in [1, 2^20]), in TFLOP/s, so kernel rates can
+ * be quoted against a measured peak beside the published one.  Runs a warm-up
+ * launch and a timed one on `stream` and waits for them (a host sync);
+ * allocates nothing but two events, destroyed before it returns. */
+int gdn_mfma_peak_probe(int32_t dtype, int32_t iters, double* tflops, void* stream);
+
+/* Measurement support: the HBM rate of a plain streaming copy of `bytes` bytes
+ * (a positive multiple of 16, at most 2^36) from device buffer `src` to device
+ * buffer `dst` (both 16-byte aligned, not overlapping, each at least `bytes`
+ * long; the caller owns them), in GB/s counting bytes read plus bytes written.
+ * 16-byte non-temporal loads and stores, four in flight per thread, one
+ * 256-thread block per 32 KiB span.  Runs a
+ * warm-up copy and `reps` timed ones (in [1, 1000]) on `stream` and waits for
+ * them (a host sync); allocates nothing but two events, destroyed before it
+ * returns.  dst ends up equal to src. */
+int gdn_hbm_copy_probe(const void* src, void* dst, int64_t bytes, int32_t reps, double* gbs, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

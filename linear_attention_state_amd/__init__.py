@@ -20,7 +20,8 @@ GDN_DEV_WAIT_EXPIRED, GDN_DEV_BAD_INDEX = 1, 2
 EXPORTS = ("gdn_state_spec", "gdn_workspace_size", "gdn_varlen_forward", "gdn_varlen_forward_noalloc",
            "gdn_varlen_conv", "gdn_state_copy",
            "ssd_varlen_scan", "kda_varlen_forward", "gdn_last_error", "gdn_device_status",
-           "gdn_kernel_timing", "gdn_kernel_times")
+           "gdn_kernel_timing", "gdn_kernel_times", "gdn_mfma_peak_probe",
+           "gdn_hbm_copy_probe")
 
 _lib = None
 
@@ -117,6 +118,10 @@ def load_library():
         lib.gdn_kernel_times.restype = ctypes.c_int
         lib.gdn_kernel_times.argtypes = [ctypes.POINTER(gdn_kernel_time), ctypes.c_int32,
                                          ctypes.POINTER(ctypes.c_int32)]
+        lib.gdn_mfma_peak_probe.restype = ctypes.c_int
+        lib.gdn_mfma_peak_probe.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.POINTER(ctypes.c_double), P]
+        lib.gdn_hbm_copy_probe.restype = ctypes.c_int
+        lib.gdn_hbm_copy_probe.argtypes = [P, P, ctypes.c_int64, ctypes.c_int32, ctypes.POINTER(ctypes.c_double), P]
         _lib = lib
     return _lib
 
@@ -391,6 +396,39 @@ def gdn_device_status(clear: bool = True, stream=None) -> int:
     if rc not in (GDN_OK, GDN_EDEVICE):
         _check(rc)
     return int(bits.value)
+
+
+def gdn_mfma_peak_probe(dtype: str = "bf16", iters: int = 4096, stream=None) -> float:
+    """The dense MFMA rate the device reaches on back-to-back products, TFLOP/s
+    (dtype "bf16" or "f32"); waits for the probe."""
+    import torch
+
+    if stream is None:
+        stream = torch.cuda.current_stream().cuda_stream
+    lib = load_library()
+    out = ctypes.c_double(0.0)
+    _check(lib.gdn_mfma_peak_probe(GDN_BF16 if dtype == "bf16" else GDN_F32, int(iters), ctypes.byref(out),
+                                   ctypes.c_void_p(stream)))
+    return out.value
+
+
+def gdn_hbm_copy_probe(src, dst, reps: int = 10, stream=None) -> float:
+    """The HBM rate of the library's streaming copy from the device tensor
+    ``src`` into ``dst`` (contiguous, same number of bytes), GB/s of bytes read
+    plus bytes written; waits for the copies."""
+    import torch
+
+    if not (src.is_cuda and dst.is_cuda and src.is_contiguous() and dst.is_contiguous()):
+        raise ValueError("src and dst must be contiguous device tensors")
+    nbytes = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() != nbytes:
+        raise ValueError("src and dst differ in size")
+    if stream is None:
+        stream = torch.cuda.current_stream().cuda_stream
+    out = ctypes.c_double(0.0)
+    _check(load_library().gdn_hbm_copy_probe(ctypes.c_void_p(src.data_ptr()), ctypes.c_void_p(dst.data_ptr()),
+                                             nbytes, int(reps), ctypes.byref(out), ctypes.c_void_p(stream)))
+    return out.value
 
 
 def gdn_kernel_timing(enable: bool) -> None:

@@ -217,6 +217,62 @@ extern "C" int gdn_kernel_timing(int enable) {
   return GDN_OK;
 }
 
+extern "C" int gdn_mfma_peak_probe(int32_t dtype, int32_t iters, double* tflops, void* stream) {
+  if (!tflops) return fail(GDN_EINVAL, "tflops is NULL");
+  if (dtype != GDN_BF16 && dtype != GDN_F32) return fail(GDN_EINVAL, "dtype %d is neither GDN_BF16 nor GDN_F32", dtype);
+  if (iters < 1 || iters > (1 << 20)) return fail(GDN_EINVAL, "iters=%d outside [1, 2^20]", iters);
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const int cus = device_cus(st);
+  if (cus <= 0) return fail(GDN_EHIP, "could not read the device's compute unit count");
+  const int blocks = 4 * cus;  // 16 waves per CU, four per SIMD
+  const bool bf16 = dtype == GDN_BF16;
+  hipEvent_t ev[2] = {nullptr, nullptr};
+  hipError_t e = hipEventCreate(&ev[0]);
+  if (e == hipSuccess) e = hipEventCreate(&ev[1]);
+  if (e == hipSuccess) e = gdn::launch_mfma_probe(bf16, blocks, iters, st);  // warm-up
+  if (e == hipSuccess) e = hipEventRecord(ev[0], st);
+  if (e == hipSuccess) e = gdn::launch_mfma_probe(bf16, blocks, iters, st);
+  if (e == hipSuccess) e = hipEventRecord(ev[1], st);
+  if (e == hipSuccess) e = hipEventSynchronize(ev[1]);
+  float ms = 0.f;
+  if (e == hipSuccess) e = hipEventElapsedTime(&ms, ev[0], ev[1]);
+  for (hipEvent_t v : ev)
+    if (v) hipEventDestroy(v);
+  if (e != hipSuccess) return fail(GDN_EHIP, "MFMA probe: %s", hipGetErrorString(e));
+  const double flop_per = bf16 ? 16.0 * 16 * 32 * 2 : 16.0 * 16 * 4 * 2;
+  *tflops = (double)blocks * 4 * iters * 8 * flop_per / (ms * 1e-3) / 1e12;
+  return GDN_OK;
+}
+
+extern "C" int gdn_hbm_copy_probe(const void* src, void* dst, int64_t bytes, int32_t reps, double* gbs,
+                                  void* stream) {
+  if (!gbs) return fail(GDN_EINVAL, "gbs is NULL");
+  if (!src || !dst) return fail(GDN_EINVAL, "src or dst is NULL");
+  if (bytes <= 0 || bytes % 16 != 0 || bytes > ((int64_t)1 << 36))
+    return fail(GDN_EINVAL, "bytes=%lld is not a positive multiple of 16 up to 2^36", (long long)bytes);
+  if (((uintptr_t)src | (uintptr_t)dst) % 16 != 0) return fail(GDN_EINVAL, "src or dst is not 16-byte aligned");
+  const uintptr_t s0 = (uintptr_t)src, d0 = (uintptr_t)dst;
+  if (s0 < d0 + (uintptr_t)bytes && d0 < s0 + (uintptr_t)bytes) return fail(GDN_EINVAL, "src and dst overlap");
+  if (reps < 1 || reps > 1000) return fail(GDN_EINVAL, "reps=%d outside [1, 1000]", reps);
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const int64_t n16 = bytes / 16;
+  hipEvent_t ev[2] = {nullptr, nullptr};
+  hipError_t e = hipEventCreate(&ev[0]);
+  if (e == hipSuccess) e = hipEventCreate(&ev[1]);
+  if (e == hipSuccess) e = gdn::launch_copy_probe(src, dst, n16, st);  // warm-up
+  if (e == hipSuccess) e = hipEventRecord(ev[0], st);
+  for (int r = 0; r < reps && e == hipSuccess; ++r) e = gdn::launch_copy_probe(src, dst, n16, st);
+  if (e == hipSuccess) e = hipEventRecord(ev[1], st);
+  if (e == hipSuccess) e = hipEventSynchronize(ev[1]);
+  float ms = 0.f;
+  if (e == hipSuccess) e = hipEventElapsedTime(&ms, ev[0], ev[1]);
+  for (hipEvent_t v : ev)
+    if (v) hipEventDestroy(v);
+  if (e != hipSuccess) return fail(GDN_EHIP, "copy probe: %s", hipGetErrorString(e));
+  *gbs = 2.0 * (double)bytes * reps / (ms * 1e-3) / 1e9;
+  return GDN_OK;
+}
+
 extern "C" int gdn_kernel_times(gdn_kernel_time* out, int32_t max, int32_t* count) {
   std::lock_guard<std::mutex> lock(g_timing.mu);
   for (auto& r : g_timing.pending) {

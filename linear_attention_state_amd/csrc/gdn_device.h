@@ -273,6 +273,12 @@ hipError_t launch_chunk_generic(const ScanArgs& a, const SeqOrder& order, int dk
                                 hipStream_t st);
 bool chunk_generic_supported(int dk, int dv);
 
+// Measurement support (gdn_probe.hip): blocks x 256 threads issuing `iters`
+// rounds of 8 independent MFMAs per wave (bf16 16x16x32 or fp32 16x16x4); a
+// streaming copy of n16 16-byte elements, one 256-thread block per 32 KiB.
+hipError_t launch_mfma_probe(bool bf16, int blocks, int iters, hipStream_t st);
+hipError_t launch_copy_probe(const void* src, void* dst, int64_t n16, hipStream_t st);
+
 // Kimi delta attention, chunked (kda_chunk.hip): sequences with min_len <= L <= max_len,
 // launch order as for launch_chunk, reading the conv output y (bf16, normalised)
 // and g [T][H_v][d_k]; d_k = d_v = 128 only (kda_chunk_supported).

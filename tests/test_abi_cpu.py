@@ -243,3 +243,37 @@ def _kda_call(cu_host, T, **over):
 def test_kda_forward_rejects_bad_arguments(cu, T, over, status, needle):
     rc, msg = _kda_call(cu, T, **over)
     assert rc == status and needle in msg, (rc, msg)
+
+
+def test_mfma_probe_rejects_bad_arguments_before_any_launch():
+    lib = gdn.load_library()
+    out = ctypes.c_double(0.0)
+    assert lib.gdn_mfma_peak_probe(gdn.GDN_BF16, 16, None, None) == gdn.GDN_EINVAL
+    assert b"tflops" in lib.gdn_last_error()
+    assert lib.gdn_mfma_peak_probe(7, 16, ctypes.byref(out), None) == gdn.GDN_EINVAL
+    assert b"dtype" in lib.gdn_last_error()
+    assert lib.gdn_mfma_peak_probe(gdn.GDN_F32, 0, ctypes.byref(out), None) == gdn.GDN_EINVAL
+    assert lib.gdn_mfma_peak_probe(gdn.GDN_F32, (1 << 20) + 1, ctypes.byref(out), None) == gdn.GDN_EINVAL
+    assert b"iters" in lib.gdn_last_error()
+
+
+def test_copy_probe_rejects_bad_arguments_before_any_launch():
+    """Every check runs on the host before the device is touched (the pointers
+    below are never dereferenced)."""
+    lib = gdn.load_library()
+    out = ctypes.c_double(0.0)
+    a, b = ctypes.c_void_p(1 << 20), ctypes.c_void_p(1 << 30)
+    assert lib.gdn_hbm_copy_probe(a, b, 1024, 1, None, None) == gdn.GDN_EINVAL
+    assert b"gbs" in lib.gdn_last_error()
+    assert lib.gdn_hbm_copy_probe(None, b, 1024, 1, ctypes.byref(out), None) == gdn.GDN_EINVAL
+    assert b"NULL" in lib.gdn_last_error()
+    for n in (0, -16, 1000, (1 << 36) + 16):
+        assert lib.gdn_hbm_copy_probe(a, b, n, 1, ctypes.byref(out), None) == gdn.GDN_EINVAL
+        assert b"multiple of 16" in lib.gdn_last_error()
+    assert lib.gdn_hbm_copy_probe(ctypes.c_void_p((1 << 20) + 8), b, 1024, 1, ctypes.byref(out), None) == gdn.GDN_EINVAL
+    assert b"aligned" in lib.gdn_last_error()
+    assert lib.gdn_hbm_copy_probe(a, ctypes.c_void_p((1 << 20) + 512), 1024, 1, ctypes.byref(out), None) == gdn.GDN_EINVAL
+    assert b"overlap" in lib.gdn_last_error()
+    for r in (0, 1001):
+        assert lib.gdn_hbm_copy_probe(a, b, 1024, r, ctypes.byref(out), None) == gdn.GDN_EINVAL
+        assert b"reps" in lib.gdn_last_error()
