@@ -594,8 +594,9 @@ __device__ __forceinline__ void p_role(Smem& sm, const Seq& q, const Lane& ln) {
 
 // ---- the conv of the chunked rows, run by the scan workgroups as claimed tasks
 //
-// Every workgroup first claims conv tasks (16 rows x 4096 channels of one
-// sequence; the tasks of the longest sequence come first) from a counter in
+// Every workgroup first claims conv tasks (kConvTaskRows rows x
+// kConvTaskChannels channels of one sequence, each wave converting 16 rows of
+// 512 channels; the tasks of the longest sequence come first) from a counter in
 // global memory: at least until every task of its own sequence has been
 // claimed, and beyond that while its scan, priced by the host's time model,
 // can still end by the host's estimate of the balanced finish.  It then waits
@@ -644,12 +645,26 @@ __device__ __forceinline__ int32_t plan_target(const FusedConv& fc) {
   else return fc.target;
 }
 
-// One task: rows [r0, r0 + n) of sequence s (rows from seq0) at channels
-// c0..c0+7 of each thread; `on` is false for the threads past the channel count.
+// One task as one wave sees it: the wave's rows [r0, r0 + n) of sequence s
+// (rows from seq0; n <= 0 past the sequence's end) at channels c0..c0+7 of
+// each thread; `on` is false for the threads past the channel count or the
+// sequence's end.  `row` is the task's first row group (in kConvTaskRows).
 struct ConvTask {
-  int rank, s, seq0, r0, n, c0;
+  int rank, s, seq0, r0, n, c0, row;
   bool on;
 };
+
+// Wave wv's part of the task at row group b and channel slice c of sequence s:
+// 16 rows of 512 channels.  Every value but c0 is uniform over the wave.
+__device__ __forceinline__ void conv_part(const ScanArgs& a, ConvTask& k, int b, int c) {
+  constexpr int kSegWaves = kConvTaskChannels / 512;  // waves across the task's channels
+  const int wv = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+  k.row = b;
+  k.r0 = k.seq0 + b * kConvTaskRows + (wv / kSegWaves) * kConvWaveRows;
+  k.n = min(kConvWaveRows, a.cu[k.s + 1] - k.r0);
+  k.c0 = c * kConvTaskChannels + (wv % kSegWaves) * 512 + ((int)threadIdx.x & 63) * 8;
+  k.on = k.c0 < a.channels && k.n > 0;
+}
 
 template <bool DP>
 __device__ __forceinline__ ConvTask conv_decode(const ScanArgs& a, const SeqOrder& ord, const FusedConv& fc, int t) {
@@ -663,10 +678,7 @@ __device__ __forceinline__ ConvTask conv_decode(const ScanArgs& a, const SeqOrde
   k.rank = lo;
   k.s = plan_seq<DP>(ord, fc, lo);
   k.seq0 = a.cu[k.s];
-  k.r0 = k.seq0 + (loc / fc.slices) * kConvTaskRows;
-  k.n = min(kConvTaskRows, a.cu[k.s + 1] - k.r0);
-  k.c0 = (loc % fc.slices) * kConvTaskChannels + (int)threadIdx.x * 8;
-  k.on = k.c0 < a.channels;
+  conv_part(a, k, loc / fc.slices, loc % fc.slices);
   return k;
 }
 
@@ -711,13 +723,14 @@ __device__ __forceinline__ void conv_prefetch(Smem& sm, const ScanArgs& a, const
 #pragma unroll
   for (int i = 0; i < W; ++i) sd.wr[i] = wp[i];
   const int wv = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+  const int r0 = __builtin_amdgcn_readfirstlane(k.r0), n = __builtin_amdgcn_readfirstlane(k.n);
   const __amdgpu_buffer_rsrc_t xs =
-      make_rsrc(reinterpret_cast<const uint16_t*>(a.x) + (int64_t)k.r0 * C, (uint32_t)(k.n * C * 2));
+      make_rsrc(reinterpret_cast<const uint16_t*>(a.x) + (int64_t)r0 * C, (uint32_t)(n * C * 2));
   u32x4* st = conv_stage(sm);
 #pragma unroll
-  for (int r = 0; r < kConvTaskRows; ++r)  // rows past the task's end load its last row again
+  for (int r = 0; r < kConvWaveRows; ++r)  // rows past the wave's end load its last row again
     __builtin_amdgcn_raw_ptr_buffer_load_lds(xs, (__attribute__((address_space(3))) void*)(st + (r * kConvWaves + wv) * 64),
-                                             16, (min(r, k.n - 1) * C + k.c0) * 2, 0, 0, 0);
+                                             16, (min(r, n - 1) * C + k.c0) * 2, 0, 0, 0);
 }
 
 // Sum over the 16 lanes of a key head (a DPP row): the same pairings as a
@@ -735,7 +748,7 @@ __device__ __forceinline__ float head_sum(float v) {
 // Computes and stores task k from its rows (registers) and its halo and taps.
 template <int W>
 __device__ __forceinline__ void conv_compute(const ScanArgs& a, const ConvTask& k, const ConvSide<W>& sd,
-                                             const u32x4 (&rx)[kConvTaskRows]) {
+                                             const u32x4 (&rx)[kConvWaveRows]) {
   if (!k.on) return;  // whole 16-lane head groups (the channel count is a multiple of 128)
   const int C = a.channels;
   float wt[8][W];
@@ -760,7 +773,7 @@ __device__ __forceinline__ void conv_compute(const ScanArgs& a, const ConvTask& 
   const __amdgpu_buffer_rsrc_t ys =
       make_rsrc(reinterpret_cast<const uint16_t*>(a.y) + (int64_t)r0 * C, (uint32_t)(n * C * 2));
 #pragma unroll
-  for (int r = 0; r < kConvTaskRows; ++r) {
+  for (int r = 0; r < kConvWaveRows; ++r) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       xw[r & 3][2 * i] = __uint_as_float(rx[r][i] << 16);
@@ -828,7 +841,7 @@ __device__ void conv_phase(Smem& sm, const ScanArgs& a, const SeqOrder& ord, con
   if (tid == 0) sm.task = claim_after(fc, t, total, last, latest, t_begin);
   lds_barrier();
   int u = __builtin_amdgcn_readfirstlane(sm.task);
-  u32x4 rx[kConvTaskRows];
+  u32x4 rx[kConvWaveRows];
   const u32x4* st = conv_stage(sm);
   while (t < total) {
     // this task's rows and halo have arrived; read the rows back from LDS
@@ -836,7 +849,7 @@ __device__ void conv_phase(Smem& sm, const ScanArgs& a, const SeqOrder& ord, con
     cur = nxt;
     if (k.on) {
 #pragma unroll
-      for (int r = 0; r < kConvTaskRows; ++r) rx[r] = st[(r * kConvWaves + wv) * 64 + lane];
+      for (int r = 0; r < kConvWaveRows; ++r) rx[r] = st[(r * kConvWaves + wv) * 64 + lane];
     }
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // read before the next rows overwrite them
     lds_barrier();  // every thread has read sm.task (u)
@@ -1006,8 +1019,8 @@ __device__ void write_tail(const ScanArgs& a, int s) {
 // Streaming helper workgroup: converts the rows the scans need next, in
 // chunk-major order (the tasks of every rank's chunk 0, then of every rank's
 // chunk 1, ...), the order in which the scans, which start together and step
-// at the same pace, consume them.  Each task (16 rows x 4096 channels) is
-// counted in its chunk's counter.  As in conv_phase, the next task is claimed
+// at the same pace, consume them.  Each task (kConvTaskRows rows x
+// kConvTaskChannels channels) is counted in its chunk's counter.  As in conv_phase, the next task is claimed
 // one task ahead and its rows load into LDS while the current one is
 // computed.  Ends when every task is claimed; never waits for anything.
 //
@@ -1047,10 +1060,7 @@ __device__ __forceinline__ ConvTask stream_task(const ScanArgs& a, const SeqOrde
   k.rank = r;
   k.s = ord.seq[r];
   k.seq0 = a.cu[k.s];
-  k.r0 = k.seq0 + (t / fc.slices) * kConvTaskRows;
-  k.n = min(kConvTaskRows, a.cu[k.s + 1] - k.r0);
-  k.c0 = (t % fc.slices) * kConvTaskChannels + (int)threadIdx.x * 8;
-  k.on = k.c0 < a.channels;
+  conv_part(a, k, t / fc.slices, t % fc.slices);
   return k;
 }
 
@@ -1080,7 +1090,7 @@ __device__ void stream_helper(Smem& sm, const ScanArgs& a, const SeqOrder& ord, 
     k = stream_task(a, ord, fc, r, t);
     conv_prefetch<W>(sm, a, k, nxt);
   }
-  u32x4 rx[kConvTaskRows];
+  u32x4 rx[kConvWaveRows];
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   while (r >= 0) {
     // wave 0 claims the task after the next one, with nothing else in flight
@@ -1089,7 +1099,7 @@ __device__ void stream_helper(Smem& sm, const ScanArgs& a, const SeqOrder& ord, 
     cur = nxt;
     if (k.on) {
 #pragma unroll
-      for (int i = 0; i < kConvTaskRows; ++i) rx[i] = st[(i * kConvWaves + wv) * 64 + lane];
+      for (int i = 0; i < kConvWaveRows; ++i) rx[i] = st[(i * kConvWaves + wv) * 64 + lane];
     }
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // read before the next rows overwrite them
     ConvTask kn{};
@@ -1105,7 +1115,7 @@ __device__ void stream_helper(Smem& sm, const ScanArgs& a, const SeqOrder& ord, 
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this task's stores, the next task's rows
     lds_barrier();
     if (tid == 0)
-      __hip_atomic_fetch_add(&ready[fc.first[k.rank] + (t / fc.slices) / (BT / kConvTaskRows)], 1,
+      __hip_atomic_fetch_add(&ready[fc.first[k.rank] + k.row / (BT / kConvTaskRows)], 1,
                              __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     k = kn;
     r = ur;

@@ -209,8 +209,17 @@ hipError_t launch_recurrent(const ScanArgs& a, int dk, int dv, bool bf16, hipStr
 // [cu[s] + b * kConvTaskRows, ...) of sequence s = order.seq[r] and channels
 // [c * kConvTaskChannels, ...), with b = (t - first[r]) / slices and
 // c = (t - first[r]) % slices.  n == 0: y was written by the conv kernel.
-constexpr int kConvTaskRows = 16;
-constexpr int kConvTaskChannels = 4096;
+// Each of the workgroup's 8 waves converts kConvWaveRows rows of 512 channels
+// of the task; the task is kConvTaskChannels / 512 such segments wide and as
+// many 16-row parts deep as the waves fill.
+#ifndef GDN_CONV_TASK_CHANNELS
+#define GDN_CONV_TASK_CHANNELS 1024
+#endif
+constexpr int kConvTaskChannels = GDN_CONV_TASK_CHANNELS;
+constexpr int kConvWaveRows = 16;
+constexpr int kConvTaskRows = kConvWaveRows * 8 * 512 / kConvTaskChannels;
+static_assert(kConvTaskChannels % 512 == 0 && 8 * 512 % kConvTaskChannels == 0, "whole wave segments");
+static_assert(64 % kConvTaskRows == 0, "a task lies in one 64-row chunk");
 constexpr int kMaxFusedRanks = 256;
 // Times are in ticks of the 100 MHz real-time counter, counted from the start
 // of a workgroup's conv phase.  A workgroup of a sequence with N chunks keeps
