@@ -770,7 +770,9 @@ int forward_impl(const gdn_layer_desc* desc, const void* x, const void* conv_wei
       e = timed(K_CONV, st, [&] { return gdn::launch_conv(ca, W, bf16, true, st); });
       if (e != hipSuccess) return fail(GDN_EHIP, "conv launch: %s", hipGetErrorString(e));
     } else {
-      const int counters = fc.stream ? 2 + fc.first[fc.n] : 1 + fc.n;  // streaming: + the role ticket
+      // streaming: the task counter, the chunk counters and the role ticket;
+      // phased: the task counter, one per rank and one per chunk of each rank
+      const int counters = fc.stream ? 2 + fc.first[fc.n] : 1 + fc.n + fc.first[fc.n] / fc.slices;
       e = timed(K_ZERO, st, [&] { return gdn::launch_zero_sync(fc.sync, counters, st); });
       if (e != hipSuccess) return fail(GDN_EHIP, "counter reset launch: %s", hipGetErrorString(e));
     }

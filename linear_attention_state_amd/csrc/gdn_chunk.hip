@@ -421,21 +421,22 @@ __device__ __forceinline__ void state_role(Smem& sm, float* sst, const ScanArgs&
 }
 
 // ---- wave 4: A for chunk i + 2, its diagonal blocks published first
-// Streaming: waits until every conv task of chunk c of `rank` is counted
-// (bounded: the tasks are run by helper workgroups that never wait, and every
-// helper has started before any scan, see chunk_scan_kernel).  After a
-// successful poll an agent-scope acquire fence drops any stale copy of the
-// rows from this CU's caches (a workspace reused from an earlier call may
-// still be cached from that call).  A wait that gives up raises
-// kStatusWaitExpired.  Returns the first chunk from c on that is not known to
-// be converted.
-__device__ __forceinline__ int stream_wait(const FusedConv& fc, int rank, int L, int c, int upto, int lane) {
-  const int32_t* ready = fc.sync + 1 + fc.first[rank];
+// With the conv inside the kernel: waits until every conv task of chunk c of
+// the sequence is counted in ready[c].  Bounded: streaming, the tasks are run
+// by helper workgroups that never wait, and every helper has started before
+// any scan (see chunk_scan_kernel); phased, every task of the sequence was
+// claimed before its workgroups left their conv phase, and a claimed task
+// never waits.  After a successful poll an agent-scope acquire fence drops any
+// stale copy of the rows from this CU's caches (a workspace reused from an
+// earlier call may still be cached from that call).  A wait that gives up
+// raises kStatusWaitExpired.  Returns the first chunk from c on that is not
+// known to be converted.
+__device__ __forceinline__ int chunk_wait(const int32_t* ready, int slices, int L, int c, int upto, int lane) {
   if (c < upto) return upto;
   // lane l looks at chunk c + l: one round trip finds how many chunks from c on
   // are complete, and the scan polls again only after it has used them up
   const int cc = c + lane;
-  const int want = min(BT / kConvTaskRows, (L - BT * cc + kConvTaskRows - 1) / kConvTaskRows) * fc.slices;
+  const int want = slices;  // tasks are one chunk deep
   const bool mine = cc * BT < L;
   for (int it = 0; it < (1 << 24); ++it) {
     const bool ok = !mine || __hip_atomic_load(&ready[cc], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= want;
@@ -450,14 +451,15 @@ __device__ __forceinline__ int stream_wait(const FusedConv& fc, int rank, int L,
   return c + 1;
 }
 
-template <bool STREAM>
+// ready: the chunk counters of the sequence when the conv runs inside the
+// kernel, else NULL (the conv kernel ran before it)
 __device__ __forceinline__ void gram_role(Smem& sm, const ScanArgs& a, const Seq& q, int lane, const Lane& ln,
-                                          const FusedConv& fc, int rank) {
+                                          const int32_t* ready, int slices) {
   Blk gk[4];
   float g4, b4;
-  int upto = 0;  // streaming: chunks below this one are known to be converted
+  int upto = 0;  // chunks below this one are known to be converted
   auto load = [&](int c) {
-    if constexpr (STREAM) upto = stream_wait(fc, rank, q.L, c, upto, lane);
+    if (ready) upto = chunk_wait(ready, slices, q.L, c, upto, lane);
     const __amdgpu_buffer_rsrc_t ry = chunk_rows(a, q, c);
 #pragma unroll
     for (int b = 0; b < 4; ++b) gk[b] = ld_blk_g(ry, a.channels, q.koff, b, ln);
@@ -599,20 +601,22 @@ __device__ __forceinline__ void p_role(Smem& sm, const Seq& q, const Lane& ln) {
 // 512 channels; the tasks of the longest sequence come first) from a counter in
 // global memory: at least until every task of its own sequence has been
 // claimed, and beyond that while its scan, priced by the host's time model,
-// can still end by the host's estimate of the balanced finish.  It then waits
-// until its own sequence's tasks are finished and starts its scan.  A
-// workgroup only ever waits for tasks that are already claimed, and a claimed
-// task never waits for anything, so the wait ends whatever the number of
-// resident workgroups.  The rows are computed exactly as by the conv kernel
+// can still end by the host's estimate of the balanced finish.  It then starts
+// its scan, which waits for each chunk's rows when it first needs them (each
+// task is counted for its sequence and for its chunk), so later chunks may
+// still be converting by other workgroups while it scans.  A workgroup only
+// ever waits for tasks that are already claimed, and a claimed task never
+// waits for anything, so every wait ends whatever the number of resident
+// workgroups.  The rows are computed exactly as by the conv kernel
 // (same tap order, SiLU, and head reduction across the 16 lanes of a key
 // head), so y is bitwise the same either way.
 //
 // Visibility across XCDs without writing back whole L2 caches: the rows are
 // stored with device-scope coherence (the SC1 bit, as the compiler emits for an
 // agent-scope atomic store), every wave waits for its stores to complete, the
-// workgroup meets at a barrier, and only then is the task counted.  A
-// workgroup that has seen its count reach the total invalidates its caches (an
-// agent-scope acquire fence) before the scan reads the rows.
+// workgroup meets at a barrier, and only then is the task counted.  A scan
+// that has seen a chunk's count complete invalidates its caches (an
+// agent-scope acquire fence) before it reads the chunk's rows.
 constexpr int kStoreDeviceScope = 16 | 2;  // buffer store cache policy: SC1 (device scope) | NT (streaming)
 
 // The launch order and the conv task plan: from the kernel arguments (planned
@@ -813,7 +817,7 @@ __device__ __forceinline__ int claim_after(const FusedConv& fc, int newest, int 
 }
 
 // Claims and runs conv tasks, at least until every task of `rank` is claimed
-// (conv_wait then waits for those to finish).  All threads of the workgroup
+// (the scan then waits for them chunk by chunk).  All threads of the workgroup
 // call it.  While a task is computed from registers, the rows of the next
 // claimed task are loading into LDS, and a third task is being claimed.  On
 // return no LDS access or load of the phase is outstanding.
@@ -821,7 +825,8 @@ template <bool DP, int W>
 __device__ void conv_phase(Smem& sm, const ScanArgs& a, const SeqOrder& ord, const FusedConv& fc, int rank) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int total = plan_first<DP>(fc, plan_fused_n<DP>(fc));
+  const int n_ranks = plan_fused_n<DP>(fc);
+  const int total = plan_first<DP>(fc, n_ranks);
   const int last = plan_first<DP>(fc, rank + 1);  // my rank's tasks end here
   // latest claim of a task that two more precede before my scan
   const int my_s = plan_seq<DP>(ord, fc, rank);
@@ -862,10 +867,15 @@ __device__ void conv_phase(Smem& sm, const ScanArgs& a, const SeqOrder& ord, con
     if (tid == 0) v = claim_after(fc, u, total, last, latest, t_begin);
     conv_compute<W>(a, k, cur, rx);
     if (tid == 0) sm.task = v;
-    // this task's device-scope stores complete (and the next task's loads), then one count
+    // this task's device-scope stores complete (and the next task's loads),
+    // then the counts: its rank's, and its chunk's (the scans wait on these)
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     lds_barrier();
-    if (tid == 0) __hip_atomic_fetch_add(&fc.sync[1 + k.rank], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (tid == 0) {
+      __hip_atomic_fetch_add(&fc.sync[1 + k.rank], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_fetch_add(&fc.sync[1 + n_ranks + plan_first<DP>(fc, k.rank) / fc.slices + k.row], 1,
+                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
     k = kn;
     t = u;
     u = __builtin_amdgcn_readfirstlane(sm.task);
@@ -941,7 +951,6 @@ __global__ __launch_bounds__(1024) void plan_kernel(PlanArgs a) {
   __shared__ int tasks[kMaxPlanSeqs];
   __shared__ int n_long, longest, chunks_sum;
   const int tid = threadIdx.x, N = a.num_seqs;
-  for (int i = tid; i < 1 + N; i += blockDim.x) a.sync[i] = 0;
   if (tid == 0) {
     n_long = 0;
     longest = 0;
@@ -961,6 +970,8 @@ __global__ __launch_bounds__(1024) void plan_kernel(PlanArgs a) {
   }
   __syncthreads();
   const int n = n_long;
+  // the task counters: [0], one per rank, one per chunk of each rank
+  for (int i = tid; i < 1 + n + chunks_sum; i += blockDim.x) a.sync[i] = 0;
   if (rank >= 0) tasks[rank] = (len[tid] + a.conv_rows - 1) / a.conv_rows * a.slices;
   __syncthreads();
   // inclusive scan of tasks[0 .. n) (Hillis-Steele; one entry per thread)
@@ -1115,7 +1126,7 @@ __device__ void stream_helper(Smem& sm, const ScanArgs& a, const SeqOrder& ord, 
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this task's stores, the next task's rows
     lds_barrier();
     if (tid == 0)
-      __hip_atomic_fetch_add(&ready[fc.first[k.rank] + k.row / (BT / kConvTaskRows)], 1,
+      __hip_atomic_fetch_add(&ready[fc.first[k.rank] + k.row], 1,
                              __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     k = kn;
     r = ur;
@@ -1214,9 +1225,11 @@ __global__ __launch_bounds__(NT) void chunk_scan_kernel(ScanArgs a, SeqOrder ord
       *reinterpret_cast<u32x4*>(&sst[row * PS + 4 * c4]) = __builtin_amdgcn_raw_buffer_load_b128(rs, 16 * f, 0, 0);
     }
   }
-  // the state does not depend on the conv: it was staged while the sequence's
-  // last rows may still have been converting; now wait for those rows
-  if (fused_n > 0) conv_wait<DP>(fc, rank);
+  // the scan waits for the converted rows chunk by chunk (the gram wave, the
+  // first reader of each chunk's rows)
+  const int32_t* ready = nullptr;
+  if constexpr (STREAM) ready = fc.sync + 1 + fc.first[rank];
+  else if (fused_n > 0) ready = fc.sync + 1 + fused_n + plan_first<DP>(fc, rank) / fc.slices;
   lds_barrier();
   if (wv < NS) {
     state_role(sm, sst, a, q, wv, ln);
@@ -1235,7 +1248,7 @@ __global__ __launch_bounds__(NT) void chunk_scan_kernel(ScanArgs a, SeqOrder ord
       sm.aflag = 0;
     }
     lds_barrier();
-    if (wv == NS) gram_role<STREAM>(sm, a, q, lane, ln, fc, rank);
+    if (wv == NS) gram_role(sm, a, q, lane, ln, ready, fc.slices);
     else if (wv == NS + 1) blocks_role(sm, q, ln);
     else if (wv == NS + 2) load_role(sm, a, q, lane);
     else p_role(sm, q, ln);

@@ -211,15 +211,13 @@ hipError_t launch_recurrent(const ScanArgs& a, int dk, int dv, bool bf16, hipStr
 // c = (t - first[r]) % slices.  n == 0: y was written by the conv kernel.
 // Each of the workgroup's 8 waves converts kConvWaveRows rows of 512 channels
 // of the task; the task is kConvTaskChannels / 512 such segments wide and as
-// many 16-row parts deep as the waves fill.
-#ifndef GDN_CONV_TASK_CHANNELS
-#define GDN_CONV_TASK_CHANNELS 1024
-#endif
-constexpr int kConvTaskChannels = GDN_CONV_TASK_CHANNELS;
+// many 16-row parts deep as the waves fill: one 64-row chunk, so a chunk's
+// rows are converted by exactly `slices` tasks.
+constexpr int kConvTaskChannels = 1024;
 constexpr int kConvWaveRows = 16;
 constexpr int kConvTaskRows = kConvWaveRows * 8 * 512 / kConvTaskChannels;
 static_assert(kConvTaskChannels % 512 == 0 && 8 * 512 % kConvTaskChannels == 0, "whole wave segments");
-static_assert(64 % kConvTaskRows == 0, "a task lies in one 64-row chunk");
+static_assert(kConvTaskRows == 64, "a task is one 64-row chunk deep");
 constexpr int kMaxFusedRanks = 256;
 // Times are in ticks of the 100 MHz real-time counter, counted from the start
 // of a workgroup's conv phase.  A workgroup of a sequence with N chunks keeps
@@ -229,7 +227,8 @@ constexpr int kMaxFusedRanks = 256;
 struct FusedConv {
   int32_t n;         // ranks (entries of the launch order), 0 = no fused conv
   int32_t slices;    // channel slices per row block
-  int32_t* sync;     // [0] next task to claim, [1 + r] tasks of rank r finished; zero before the launch
+  int32_t* sync;     // [0] next task to claim, [1 + r] tasks of rank r finished, [1 + n + first[r] / slices + c]
+                     // tasks of chunk c of rank r finished; zero before the launch
   int32_t target, task, scan0, scan1;
   int32_t first[kMaxFusedRanks + 1];
   // Device plan (launches planned on the device from cu_seqlens, see
@@ -265,7 +264,7 @@ struct PlanArgs {
   double plain_scan1_us, crowd_scan1_us, phased_scale;  // grows with the share of them scanning
   int beside_tokens;  // the token kernel runs beside on a side stream: with one-token sequences, conv inside
   int32_t* plan;
-  int32_t* sync;      // zeroed: 1 + num_seqs counters
+  int32_t* sync;      // zeroed: 1 + n + (chunks of the n chunked sequences) counters
 };
 hipError_t launch_plan(const PlanArgs& a, hipStream_t st);
 hipError_t launch_zero_sync(int32_t* sync, int n, hipStream_t st);  // n counters to zero
