@@ -114,6 +114,9 @@ constexpr double kTargetMargin = 1.03;
 //   bound: each converts a task's rows at about kHelperBytesPerUs.
 constexpr double kScanPlainUs = 2.55, kScanCrowdUs = 0.65, kPhasedScale = 0.95;
 constexpr double kStreamStartUs = 40.0, kStreamScanScale = 1.06, kHelperBytesPerUs = 18.7e3;
+// The KDA chunk kernel's scan: kKdaScan0Us + kKdaScan1Us per chunk (measured on
+// MI355X, 128 x 128 head); the conv inside it is placed by the phased rule.
+constexpr double kKdaScan0Us = 10.0, kKdaScan1Us = 8.3;
 
 double plain_scan1(int64_t wgs, int cus) {
   const double half = std::max(cus, 2) / 2.0;
@@ -1046,10 +1049,11 @@ extern "C" int kda_varlen_forward(const gdn_layer_desc* desc, const void* x, con
   sa.num_v_heads = desc->num_v_heads; sa.channels = C;
   sa.kda = 1;
   // Sequences of two or more tokens run chunked (bf16, d_k = d_v = 128, with a
-  // workspace for the conv output): the conv kernel writes the normalised q, k
-  // and v rows, then the KDA chunk kernel walks each sequence 64 rows at a time,
-  // longest first.  The others (and everything without a workspace or in
-  // another shape) run token by token.  The new conv states come last, once
+  // workspace for the conv output): the normalised q, k and v rows are written
+  // into the workspace, by the chunk kernel's own workgroups or by the conv
+  // kernel before it, and the KDA chunk kernel walks each sequence 64 rows at
+  // a time, longest first.  The others (and everything without a workspace or
+  // in another shape) run token by token.  The new conv states come last, once
   // every reader of the old ones is enqueued.
   int n_long = 0;
   for (int i = 0; i < num_seqs; ++i) n_long += cu_seqlens_host[i + 1] - cu_seqlens_host[i] >= 2;
@@ -1060,20 +1064,6 @@ extern "C" int kda_varlen_forward(const gdn_layer_desc* desc, const void* x, con
   if (workspace && !aligned(workspace, 256)) return fail(GDN_EINVAL, "workspace must be 256-byte aligned");
   hipError_t e = hipSuccess;
   if (chunked) {
-    gdn::ConvArgs ca{};
-    ca.x = x; ca.w = conv_weight; ca.cu = cu_seqlens; ca.read_idx = read_idx; ca.write_idx = write_idx;
-    ca.conv_pool = reinterpret_cast<const char*>(conv_pool); ca.conv_stride = conv_block_stride;
-    ca.y = workspace;
-    ca.num_seqs = num_seqs; ca.total_tokens = total_tokens; ca.num_blocks = num_blocks; ca.channels = C;
-    ca.qk_channels = desc->num_k_heads * desc->head_k_dim; ca.head_k_dim = desc->head_k_dim;
-    const int groups = (C + 511) / 512;
-    const int slices = std::max(1, 4096 / groups);
-    const int rows = (total_tokens + slices - 1) / slices;
-    ca.rows_per_block = std::min(256, std::max(4, (rows + 3) / 4 * 4));
-    ca.eps = sa.eps;
-    ca.q_scale = sa.q_scale;
-    e = timed(K_CONV, st, [&] { return gdn::launch_conv(ca, W, bf16, true, st); });
-    if (e != hipSuccess) return fail(GDN_EHIP, "conv launch: %s", hipGetErrorString(e));
     static thread_local gdn::SeqOrder order;
     order.n = 0;
     if (n_long <= gdn::kMaxOrder && num_seqs <= 65535) {
@@ -1086,10 +1076,68 @@ extern "C" int kda_varlen_forward(const gdn_layer_desc* desc, const void* x, con
       for (size_t i = 0; i < lens.size(); ++i) order.seq[i] = (uint16_t)lens[i].second;
       order.n = (int32_t)lens.size();
     }
+    // The conv of the chunked rows runs inside the KDA chunk kernel (phased, as
+    // for the gated delta rule) when every workgroup of the kernel is resident
+    // at once and the workspace holds the task counters; the workgroups of the
+    // short sequences, whose scans end long before the longest one's, then
+    // convert most of the rows.  Otherwise the conv kernel runs first.
+    static thread_local gdn::FusedConv fc;
+    fc.n = 0;
+    fc.plan = nullptr;
+    fc.plan_seqs = 0;
+    fc.stream = 0;
+    fc.helpers = 0;
+    const WsLayout wl = ws_layout(desc, total_tokens, num_seqs);
+    const int mode = conv_in_scan_mode();
+    if (mode >= 0 && order.n > 0 && order.n <= gdn::kMaxFusedRanks && aligned(conv_weight, 16) &&
+        workspace_bytes >= wl.plan && (int64_t)order.n * desc->num_v_heads <= device_cus(st)) {
+      fc.slices = (C + gdn::kConvTaskChannels - 1) / gdn::kConvTaskChannels;
+      fc.first[0] = 0;
+      const double tus = ::task_us(C, desc);
+      double scans = 0.0;
+      for (int r = 0; r < order.n; ++r) {
+        const int L = cu_seqlens_host[order.seq[r] + 1] - cu_seqlens_host[order.seq[r]];
+        fc.first[r + 1] = fc.first[r] + (L + gdn::kConvTaskRows - 1) / gdn::kConvTaskRows * fc.slices;
+        scans += kKdaScan0Us + kKdaScan1Us * ((L + 63) / 64);
+      }
+      const int L0 = cu_seqlens_host[order.seq[0] + 1] - cu_seqlens_host[order.seq[0]];
+      const double longest = kKdaScan0Us + kKdaScan1Us * ((L0 + 63) / 64);
+      const double fused = std::max((fc.first[order.n] * tus + desc->num_v_heads * scans) /
+                                    ((double)order.n * desc->num_v_heads), longest + 2.0 * tus);
+      const double apart = 2.0 * (double)total_tokens * C * act_size(desc) / kConvBytesPerUs + longest + 3.0;
+      if (mode == 1 || mode == 2 || kPhasedScale * fused < apart) {
+        fc.n = order.n;
+        fc.sync = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(workspace) + wl.sync);
+        fc.target = (int32_t)(fused * kTargetMargin * 100.0);  // 100 ticks per microsecond
+        fc.task = (int32_t)(tus * 100.0);
+        fc.scan0 = (int32_t)(kKdaScan0Us * 100.0);
+        fc.scan1 = (int32_t)(kKdaScan1Us * 100.0);
+      }
+    }
+    if (fc.n > 0) {
+      // the task counter, one per rank and one per chunk of each rank
+      e = timed(K_ZERO, st, [&] { return gdn::launch_zero_sync(fc.sync, 1 + fc.n + fc.first[fc.n] / fc.slices, st); });
+      if (e != hipSuccess) return fail(GDN_EHIP, "counter reset launch: %s", hipGetErrorString(e));
+    } else {
+      gdn::ConvArgs ca{};
+      ca.x = x; ca.w = conv_weight; ca.cu = cu_seqlens; ca.read_idx = read_idx; ca.write_idx = write_idx;
+      ca.conv_pool = reinterpret_cast<const char*>(conv_pool); ca.conv_stride = conv_block_stride;
+      ca.y = workspace;
+      ca.num_seqs = num_seqs; ca.total_tokens = total_tokens; ca.num_blocks = num_blocks; ca.channels = C;
+      ca.qk_channels = desc->num_k_heads * desc->head_k_dim; ca.head_k_dim = desc->head_k_dim;
+      const int groups = (C + 511) / 512;
+      const int slices = std::max(1, 4096 / groups);
+      const int rows = (total_tokens + slices - 1) / slices;
+      ca.rows_per_block = std::min(256, std::max(4, (rows + 3) / 4 * 4));
+      ca.eps = sa.eps;
+      ca.q_scale = sa.q_scale;
+      e = timed(K_CONV, st, [&] { return gdn::launch_conv(ca, W, bf16, true, st); });
+      if (e != hipSuccess) return fail(GDN_EHIP, "conv launch: %s", hipGetErrorString(e));
+    }
     gdn::ScanArgs ka = sa;
     ka.y = workspace;
     ka.min_len = 2; ka.max_len = INT_MAX;
-    e = timed(K_KDA_CHUNK, st, [&] { return gdn::launch_kda_chunk(ka, order, st); });
+    e = timed(K_KDA_CHUNK, st, [&] { return gdn::launch_kda_chunk(ka, order, fc, st); });
     if (e != hipSuccess) return fail(GDN_EHIP, "KDA chunk launch: %s", hipGetErrorString(e));
   }
   if (!chunked || n_long < num_seqs) {

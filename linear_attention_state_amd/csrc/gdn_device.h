@@ -289,8 +289,10 @@ hipError_t launch_copy_probe(const void* src, void* dst, int64_t n16, hipStream_
 
 // Kimi delta attention, chunked (kda_chunk.hip): sequences with min_len <= L <= max_len,
 // launch order as for launch_chunk, reading the conv output y (bf16, normalised)
-// and g [T][H_v][d_k]; d_k = d_v = 128 only (kda_chunk_supported).
-hipError_t launch_kda_chunk(const ScanArgs& a, const SeqOrder& order, hipStream_t st);
+// and g [T][H_v][d_k]; d_k = d_v = 128 only (kda_chunk_supported).  fc.n > 0:
+// the kernel's workgroups write y themselves first (phased, host plan only;
+// fc.sync zeroed: 1 + n + the ranks' chunks counters).
+hipError_t launch_kda_chunk(const ScanArgs& a, const SeqOrder& order, const FusedConv& fc, hipStream_t st);
 bool kda_chunk_supported(int dk, int dv);
 
 }  // namespace gdn

@@ -55,6 +55,7 @@
 // accumulate).
 #include "gdn_device.h"
 #include "gdn_mfma.h"
+#include "gdn_convtask.h"
 
 namespace gdn {
 namespace {
@@ -91,8 +92,11 @@ struct alignas(16) KSmem {
   int dex[4];                  // block b's diagonal is computed in fp32
   int dflag[4];                // producer wave b: its diagonal block of A is final for chunks < dflag[b]
   int aflag[4];                // ... and all its blocks of A
+  int task;                    // conv tasks run by the workgroup (the conv of the rows inside this kernel)
 };
 static_assert(sizeof(KSmem) <= 160 * 1024, "LDS");
+static_assert(offsetof(KSmem, task) >= 16 * 8 * 1024, "the conv row staging (16 rows x 8 KiB) stays clear of the task slot");
+static_assert(KNT == kConvThreads, "the conv tasks assume 8 waves");
 static_assert(D * KPS * 4 <= 6 * BT * D * 2, "state staging fits the first six tiles");
 static_assert(16 * D * 4 <= BT * D * 2, "exact-path running sums fit the Kr tile");
 
@@ -553,12 +557,27 @@ __device__ __forceinline__ void kda_state_step(KSmem& sm, f32x4 (&sacc)[8][KNB],
   }
 }
 
-__global__ __launch_bounds__(KNT) void kda_chunk_kernel(ScanArgs a, SeqOrder ord) {
+// fc.n > 0: the conv of the rows runs inside the kernel, as tasks every
+// workgroup claims before its scan (gdn_convtask.h); the producers then wait
+// for each chunk's rows before they load them.
+__global__ __launch_bounds__(KNT) void kda_chunk_kernel(ScanArgs a, SeqOrder ord, FusedConv fc) {
   __shared__ KSmem sm;
   const int Hv = a.num_v_heads;
   const int rank = blockIdx.x / Hv;
   KSeq q;
   q.m = blockIdx.x % Hv;
+  const int32_t* ready = nullptr;  // the chunk counters of the sequence, with the conv inside
+  if (fc.n > 0) {
+    conv_phase_w<false>(sm, a, ord, fc, rank);
+    ready = fc.sync + 1 + fc.n + fc.first[rank] / fc.slices;
+    // value heads of one key head on one XCD (workgroups go round-robin over
+    // the 8 XCDs), so the second reader of the shared q and k rows can hit L2
+    const int g = Hv / a.num_k_heads, per = Hv / 8;
+    if (Hv % 8 == 0 && per % g == 0) {
+      const int x = q.m % 8, sl = q.m / 8;
+      q.m = g * (x * (per / g) + sl / g) + sl % g;
+    }
+  }
   q.s = ord.n > 0 ? (rank < ord.n ? (int)ord.seq[rank] : a.num_seqs) : rank;
   if (q.s >= a.num_seqs) return;
   q.r0 = a.cu[q.s];
@@ -652,10 +671,14 @@ __global__ __launch_bounds__(KNT) void kda_chunk_kernel(ScanArgs a, SeqOrder ord
     // ---- producer waves
     const int pw = wv - KNS;
     KRaw x;
+    int upto = 0;  // chunks below this one are known to be converted
+    if (ready) upto = chunk_wait(ready, fc.slices, q.L, 0, upto, lane);
     kda_load(x, a, q, 0, pw, ln, 3);
     int seq = 0;
     lds_barrier();  // the state waves have read the staged state
     for (int c = 0; c < q.N; ++c) {
+      // the rows of chunk c + 1, loaded at the end of this step
+      if (ready && c + 1 < q.N) upto = chunk_wait(ready, fc.slices, q.L, c + 1, upto, lane);
       // the lane's addresses are recomputed every step: hoisted out of the
       // loop, they would not fit the registers beside the rows and operands
       int l = lane, w = pw;
@@ -683,10 +706,13 @@ __global__ __launch_bounds__(KNT) void kda_chunk_kernel(ScanArgs a, SeqOrder ord
 
 bool kda_chunk_supported(int dk, int dv) { return dk == D && dv == D; }
 
-hipError_t launch_kda_chunk(const ScanArgs& a, const SeqOrder& order, hipStream_t st) {
+hipError_t launch_kda_chunk(const ScanArgs& a, const SeqOrder& order, const FusedConv& fc, hipStream_t st) {
   if (!kda_chunk_supported(D, D) || !a.y) return hipErrorInvalidValue;
+  if (fc.n > 0 && (fc.n != order.n || fc.n > kMaxFusedRanks || !fc.sync || fc.plan || fc.stream || a.width < 1 ||
+                   a.width > 4 || fc.slices < 1))
+    return hipErrorInvalidValue;
   const int rows = order.n > 0 ? order.n : a.num_seqs;
-  hipLaunchKernelGGL(kda_chunk_kernel, dim3(rows * a.num_v_heads), dim3(KNT), 0, st, a, order);
+  hipLaunchKernelGGL(kda_chunk_kernel, dim3(rows * a.num_v_heads), dim3(KNT), 0, st, a, order, fc);
   return hipGetLastError();
 }
 

@@ -7,6 +7,8 @@ value head) within relative L2 error 1e-2 in bf16 and 1e-4 in fp32; conv
 states bit-exact; blocks no sequence writes and the trash block untouched.  At
 the decode workload's size the oracle runs on sampled value heads.
 """
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -157,3 +159,42 @@ def test_chunked_split_over_two_calls():
     assert rel_l2(torch.cat(outs).double().numpy(), one.double().numpy()) <= 1e-2
     assert rel_l2(sp[wb].double().numpy(), sp1[wb].double().numpy()) <= 1e-2
     _check("kda-one-pass", b, g)
+
+
+def _run_placed(batch, g, mode):
+    """_run with the conv placement forced (GDN_CONV_IN_SCAN) and the kernels
+    that ran recorded."""
+    old = os.environ.get("GDN_CONV_IN_SCAN")
+    os.environ["GDN_CONV_IN_SCAN"] = mode
+    try:
+        gdn.gdn_kernel_timing(True)
+        res = _run(batch, g)
+        kernels = gdn.gdn_kernel_times()
+    finally:
+        gdn.gdn_kernel_timing(False)
+        if old is None:
+            del os.environ["GDN_CONV_IN_SCAN"]
+        else:
+            os.environ["GDN_CONV_IN_SCAN"] = old
+    return res, kernels
+
+
+def test_conv_inside_the_chunk_kernel_matches_the_conv_kernel_bitwise():
+    """The conv of the chunked rows run by the KDA chunk kernel's own
+    workgroups (its scans waiting chunk by chunk) against the conv kernel
+    before it: outputs, conv states and recurrent states bit for bit the same,
+    on lengths around the chunk size beside a decode token and an empty
+    sequence (7 chunked sequences: every workgroup resident), and the oracle
+    bar met."""
+    lengths = [2, 65, 1, 129, 0, 200, 63, 3, 64]
+    b = workloads.random_batch(workloads.BIG, lengths, seed=78, fresh=[i % 2 for i in range(len(lengths))])
+    g = _g(b, 79)
+    print("case kda-fused: lengths %s" % lengths, flush=True)
+    (out_f, cp_f, sp_f), k_f = _run_placed(b, g, "always")
+    (out_s, cp_s, sp_s), k_s = _run_placed(b, g, "never")
+    assert "conv_silu_norm" not in k_f and "kda_chunk" in k_f, k_f
+    assert "conv_silu_norm" in k_s and "kda_chunk" in k_s, k_s
+    assert torch.equal(out_f.view(torch.int16), out_s.view(torch.int16))
+    assert torch.equal(cp_f.view(torch.int16), cp_s.view(torch.int16))
+    assert torch.equal(sp_f, sp_s)
+    _check("kda-fused", b, g, heads=[0, 1, 16, 31])
