@@ -87,21 +87,37 @@ def token_path_bytes(layer, n_tokens: int) -> float:
     return n_tokens * per_tok + C * layer.conv_width * s
 
 
+# The source files of each profiled kernel: its own file, and for the two chunk
+# kernels the header holding the conv tasks they run.
+KERNEL_SOURCES = {"chunk_scan": ("gdn_chunk.hip", "gdn_convtask.h"), "token_recurrent": ("gdn_recurrent.hip",),
+                  "kda_chunk": ("kda_chunk.hip", "gdn_convtask.h"), "chunk_generic": ("gdn_chunk_generic.hip",),
+                  "conv_silu_norm": ("gdn_conv.hip",), "ssd_scan": ("ssd_scan.hip",), "ssd_token": ("ssd_scan.hip",)}
+
+
+def kernel_source_sha(kernel: str):
+    """sha256[:16] of the kernel's source files, concatenated in order (the key
+    of its lines in profiles/hbm_traffic.txt), or None for an unknown kernel."""
+    import hashlib
+
+    files = KERNEL_SOURCES.get(kernel)
+    if files is None:
+        return None
+    h = hashlib.sha256()
+    for name in files:
+        with open(os.path.join(ROOT, "linear_attention_state_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
 def load_traffic(kernel: str, workload: str):
     """HBM bytes per launch measured with rocprofv3 counters, if a summary for
     this kernel's current source on this workload is committed under profiles/."""
-    import hashlib
-
     path = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
     if not os.path.exists(path):
         return None
-    src = {"chunk_scan": "gdn_chunk.hip", "token_recurrent": "gdn_recurrent.hip", "kda_chunk": "kda_chunk.hip",
-           "chunk_generic": "gdn_chunk_generic.hip",
-           "conv_silu_norm": "gdn_conv.hip", "ssd_scan": "ssd_scan.hip", "ssd_token": "ssd_scan.hip"}.get(kernel)
-    if src is None:
+    sha = kernel_source_sha(kernel)
+    if sha is None:
         return None
-    with open(os.path.join(ROOT, "linear_attention_state_amd", "csrc", src), "rb") as f:
-        sha = hashlib.sha256(f.read()).hexdigest()[:16]
     with open(path) as f:
         for line in f:
             parts = line.split()
