@@ -134,3 +134,52 @@ def test_streamed_padding_sequence():
     b = workloads.random_batch(workloads.BIG, [64, 270, 9], seed=58)
     b.write_idx[1] = -2
     _stream_vs_separate(b, "padding")
+
+
+def _call(batch, ws, mode):
+    """One gdn_varlen_forward of a fresh device copy of `batch` on the given
+    workspace, with the conv placement forced; no synchronisation."""
+    from gpu_util import to_device
+    d = to_device(batch)
+    L = batch.layer
+    out = torch.empty(batch.total_tokens, L.num_v_heads, L.head_v_dim, dtype=L.torch_act, device="cuda")
+    old = os.environ.get("GDN_CONV_IN_SCAN")
+    os.environ["GDN_CONV_IN_SCAN"] = mode
+    try:
+        gdn.gdn_varlen_forward(L, d["x"], d["conv_weight"], d["g"], d["beta"], d["cu_seqlens"], batch.cu_seqlens,
+                               d["read_idx"], d["write_idx"], d["conv_pool"], d["ssm_pool"], out, workspace=ws)
+    finally:
+        if old is None:
+            del os.environ["GDN_CONV_IN_SCAN"]
+        else:
+            os.environ["GDN_CONV_IN_SCAN"] = old
+    return out, d["conv_pool"], d["ssm_pool"]
+
+
+@pytest.mark.parametrize("mode", ["always", "stream"])
+def test_reused_workspace_reads_no_stale_rows(mode):
+    """Two batches of the same lengths and different inputs run back to back on
+    one workspace: the second call's scans must read the rows its own conv
+    tasks wrote, never the first call's rows at the same addresses (the waits
+    end with an acquire fence), so it equals the same call on a fresh
+    workspace bit for bit."""
+    lengths = [300, 70, 129, 64]
+    first = workloads.random_batch(workloads.BIG, lengths, seed=60)
+    second = workloads.random_batch(workloads.BIG, lengths, seed=61)
+    print("case reuse-%s: lengths %s" % (mode, lengths), flush=True)
+    nbytes = gdn.gdn_workspace_size(workloads.BIG, second.total_tokens, len(lengths))
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    fresh = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    gdn.gdn_kernel_timing(True)
+    try:
+        _call(first, ws, mode)
+        reused = _call(second, ws, mode)
+        torch.cuda.synchronize()
+        kernels = gdn.gdn_kernel_times()
+    finally:
+        gdn.gdn_kernel_timing(False)
+    assert "conv_silu_norm" not in kernels and kernels["chunk_scan"][1] == 2, kernels
+    ref = _call(second, fresh, mode)
+    torch.cuda.synchronize()
+    for a, b in zip(reused, ref):
+        assert torch.equal(_bits(a), _bits(b))

@@ -198,3 +198,48 @@ def test_conv_inside_the_chunk_kernel_matches_the_conv_kernel_bitwise():
     assert torch.equal(cp_f.view(torch.int16), cp_s.view(torch.int16))
     assert torch.equal(sp_f, sp_s)
     _check("kda-fused", b, g, heads=[0, 1, 16, 31])
+
+
+def test_reused_workspace_reads_no_stale_rows():
+    """Two KDA batches of the same lengths and different inputs back to back on
+    one workspace, the conv inside the chunk kernel: the second call equals the
+    same call on a fresh workspace bit for bit (no scan reads the first call's
+    rows)."""
+    lengths = [300, 70, 129, 64]
+    first = workloads.random_batch(workloads.BIG, lengths, seed=80)
+    second = workloads.random_batch(workloads.BIG, lengths, seed=81)
+    g1, g2 = _g(first, 82), _g(second, 83)
+    print("case kda-reuse: lengths %s" % lengths, flush=True)
+    L = workloads.BIG
+    nbytes = gdn.gdn_workspace_size(L, second.total_tokens, len(lengths))
+
+    def call(batch, g, ws):
+        d = to_device(batch)
+        out = torch.empty(batch.total_tokens, L.num_v_heads, L.head_v_dim, dtype=L.torch_act, device="cuda")
+        gdn.kda_varlen_forward(L, d["x"], d["conv_weight"], g.cuda().contiguous(), d["beta"], d["cu_seqlens"],
+                               batch.cu_seqlens, d["read_idx"], d["write_idx"], d["conv_pool"], d["ssm_pool"], out,
+                               workspace=ws)
+        return out, d["conv_pool"], d["ssm_pool"]
+
+    old = os.environ.get("GDN_CONV_IN_SCAN")
+    os.environ["GDN_CONV_IN_SCAN"] = "always"
+    try:
+        ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+        gdn.gdn_kernel_timing(True)
+        try:
+            call(first, g1, ws)
+            reused = call(second, g2, ws)
+            torch.cuda.synchronize()
+            kernels = gdn.gdn_kernel_times()
+        finally:
+            gdn.gdn_kernel_timing(False)
+        ref = call(second, g2, torch.empty(nbytes, dtype=torch.uint8, device="cuda"))
+        torch.cuda.synchronize()
+    finally:
+        if old is None:
+            del os.environ["GDN_CONV_IN_SCAN"]
+        else:
+            os.environ["GDN_CONV_IN_SCAN"] = old
+    assert "conv_silu_norm" not in kernels and kernels["kda_chunk"][1] == 2, kernels
+    for a, b in zip(reused, ref):
+        assert torch.equal(a.view(torch.uint8), b.view(torch.uint8))
