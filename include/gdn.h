@@ -237,8 +237,10 @@ int gdn_state_copy(const gdn_layer_desc* desc, void* conv_pool, int64_t conv_blo
  *              aligned, or NULL (then every sequence runs token by token)
  *   every other argument as for gdn_varlen_forward; cu_seqlens_host is required
  * Sequences of two or more tokens run in chunks of 64 rows (bf16 with
- * d_k = d_v = 128 and a workspace): the conv kernel writes the normalised rows
- * into the workspace, then a chunk kernel evaluates the WY / UT form with the
+ * d_k = d_v = 128 and a workspace): the normalised rows are written into the
+ * workspace (by the chunk kernel's own workgroups before their scans when all
+ * of them fit on the device at once and the workspace is gdn_workspace_size()
+ * bytes, else by the conv kernel first), and a chunk kernel evaluates the WY / UT form with the
  * decay inside the channel sums of its block products (every exponentiated
  * decay difference <= 1, except on a diagonal 16-row block, bounded there by
  * that block's own decay; a block whose decay passes e^80 on some channel is
