@@ -183,3 +183,11 @@ def test_reused_workspace_reads_no_stale_rows(mode):
     torch.cuda.synchronize()
     for a, b in zip(reused, ref):
         assert torch.equal(_bits(a), _bits(b))
+
+
+def test_single_sequence_converts_all_its_own_rows():
+    """One chunked sequence beside a decode token: its workgroups are the only
+    claimers (the first rank is also the last), convert every task, and their
+    scans then wait chunk by chunk."""
+    b = workloads.random_batch(workloads.BIG, [700, 1], seed=62)
+    _both_ways(b, "single")

@@ -243,3 +243,19 @@ def test_reused_workspace_reads_no_stale_rows():
     assert "conv_silu_norm" not in kernels and kernels["kda_chunk"][1] == 2, kernels
     for a, b in zip(reused, ref):
         assert torch.equal(a.view(torch.uint8), b.view(torch.uint8))
+
+
+def test_conv_inside_for_a_single_sequence():
+    """One chunked KDA sequence (its workgroups convert every row themselves)
+    beside a decode token: bitwise equal to the conv kernel placement."""
+    lengths = [700, 1]
+    b = workloads.random_batch(workloads.BIG, lengths, seed=84)
+    g = _g(b, 85)
+    print("case kda-fused-single: lengths %s" % lengths, flush=True)
+    (out_f, cp_f, sp_f), k_f = _run_placed(b, g, "always")
+    (out_s, cp_s, sp_s), k_s = _run_placed(b, g, "never")
+    assert "conv_silu_norm" not in k_f and "kda_chunk" in k_f, k_f
+    assert "conv_silu_norm" in k_s, k_s
+    assert torch.equal(out_f.view(torch.int16), out_s.view(torch.int16))
+    assert torch.equal(cp_f.view(torch.int16), cp_s.view(torch.int16))
+    assert torch.equal(sp_f, sp_s)
