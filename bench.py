@@ -26,7 +26,10 @@ relative L2 error over (sequence, value head) slabs and the bit-exact verdicts.
 The line also carries `measured_peaks` (the MFMA rate of back-to-back
 products from gdn_mfma_peak_probe, bf16 and fp32, and the HBM rate of the
 library's 1 GiB streaming copy, gdn_hbm_copy_probe, with torch's copy beside it)
-and every roofline its `frac_of_measured` beside `frac`.
+and every roofline its `frac_of_measured` beside `frac`; a roofline whose
+kernel has a measured traffic line in profiles/hbm_traffic.txt also carries
+`traffic_gbs` (those bytes over the kernel's duration) and its fraction of the
+measured copy rate.
 
 Warm-up runs at least `--warmup` steps and at least 60 ms of back-to-back GPU
 work, so the clocks have settled (the first few dozen steps after the inputs
@@ -127,6 +130,16 @@ def load_traffic(kernel: str, workload: str):
     return None
 
 
+def add_traffic(roof: dict, kernel: str, workload: str, kernel_ms: float) -> None:
+    """Records in a roofline the kernel's average duration, its measured HBM
+    bytes per launch (profiles/hbm_traffic.txt, null when no line matches the
+    current source), and the rate those bytes make over the duration."""
+    roof["kernel_ms"] = kernel_ms
+    roof["traffic"] = load_traffic(kernel, workload)
+    if roof["traffic"] is not None:
+        roof["traffic_gbs"] = roof["traffic"] / (kernel_ms * 1e-3) / 1e9
+
+
 def step_bytes(layer, lengths) -> float:
     """Algorithmic HBM bytes of one whole step of the layer: per token the x row
     read, the output row written, g and beta read; per sequence its recurrent
@@ -222,8 +235,7 @@ def run(cfg_id: int, steps: int, warmup: int, placements=()):
     roof["step_frac"] = roof["achieved"] * dom_s / (ms * 1e-3) / roof["peak"]
     if dom == "chunk_scan" and "conv_silu_norm" not in kernels:
         roof["note"] = "chunk_scan also ran the conv of the rows (no separate conv kernel)"
-    traffic = load_traffic(dom, {1: "prefill", 2: "decode", 3: "mixed", 4: "long"}.get(cfg_id, ""))
-    roof["traffic"] = traffic
+    add_traffic(roof, dom, {1: "prefill", 2: "decode", 3: "mixed", 4: "long"}.get(cfg_id, ""), dom_s * 1e3)
     roof["kernel"] = dom
     res = {
         "batch": b, "ms_per_step": ms, "ms_per_step_with_kernel_events": ms_events, "wall_s": wall, "tokens": T,
@@ -341,7 +353,7 @@ def run_conv(steps: int, warmup: int):
     roof = {"bound": "hbm", "achieved": work / (conv_ms * 1e-3) / 1e9, "peak": PEAK_HBM / 1e9, "unit": "GB/s",
             "kernel": "conv_silu_norm"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = load_traffic("conv_silu_norm", "conv")
+    add_traffic(roof, "conv_silu_norm", "conv", conv_ms)
     return {"workload": "standalone varlen conv + SiLU: the prefill rows (T=%d, C=%d, W=%d, bf16), "
                         "%d sequences from the trash block" % (T, C, W, n),
             "value": T / (ms * 1e-3), "unit": "tokens/s", "ms_per_step": ms, "roofline": roof,
@@ -415,7 +427,7 @@ def run_ssd(cfg: int, steps: int, warmup: int):
             "kernel": dom, "mfma_tflops": fl / (k_ms * 1e-3) / 1e12,
             "flop_per_byte": fl / byt}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = load_traffic(dom, "mamba2_prefill" if cfg == 0 else "mamba2_decode")
+    add_traffic(roof, dom, "mamba2_prefill" if cfg == 0 else "mamba2_decode", k_ms)
     n = len(b.lengths)
     what = ("prefill: %d sequences, lengths %s, T=%d, from the trash block" % (n, b.lengths, b.total_tokens)
             if cfg == 0 else "decode: %d sequences of 1 token, %d-block pool" % (n, b.ssm_pool.shape[0]))
@@ -502,13 +514,14 @@ def run_kda(cfg_id: int, steps: int, warmup: int):
         # the gated-delta-net decode bytes, with g per key channel instead of per head
         work = token_path_bytes(L, b.total_tokens) + b.total_tokens * L.num_v_heads * (L.head_k_dim - 1) * 4
         roof = {"bound": "hbm", "achieved": work / (k_ms * 1e-3) / 1e9, "peak": PEAK_HBM / 1e9, "unit": "GB/s",
-                "kernel": "token_recurrent", "traffic": load_traffic("token_recurrent", "kda_decode")}
+                "kernel": "token_recurrent"}
+        add_traffic(roof, "token_recurrent", "kda_decode", k_ms)
         what = "KDA decode: 256 sequences of 1 token"
     else:
         k_ms = kt["kda_chunk"][0] / kt["kda_chunk"][1]
         roof = {"bound": "mfma", "achieved": kda_flops(L, b.lengths) / (k_ms * 1e-3) / 1e12,
-                "peak": PEAK_BF16_MFMA / 1e12, "unit": "TFLOP/s", "kernel": "kda_chunk",
-                "traffic": load_traffic("kda_chunk", "kda_prefill")}
+                "peak": PEAK_BF16_MFMA / 1e12, "unit": "TFLOP/s", "kernel": "kda_chunk"}
+        add_traffic(roof, "kda_chunk", "kda_prefill", k_ms)
         # about 117 flop per algorithmic byte, below the chip's 312: the bytes bound it first
         kb = kda_chunk_bytes(L, b.lengths)
         roof["hbm_bytes"] = kb
@@ -566,8 +579,8 @@ def run_generic(act: str, d: int, steps: int, warmup: int):
     k_ms = kt["chunk_generic"][0] / kt["chunk_generic"][1]
     # the operands are fp32 whatever the activations: priced against the fp32 MFMA peak
     roof = {"bound": "mfma", "achieved": chunk_flops(L, b.lengths) / (k_ms * 1e-3) / 1e12,
-            "peak": PEAK_F32_MFMA / 1e12, "unit": "TFLOP/s", "kernel": "chunk_generic",
-            "traffic": load_traffic("chunk_generic", "prefill_fp32" if act == "f32" else "prefill_d64")}
+            "peak": PEAK_F32_MFMA / 1e12, "unit": "TFLOP/s", "kernel": "chunk_generic"}
+    add_traffic(roof, "chunk_generic", "prefill_fp32" if act == "f32" else "prefill_d64", k_ms)
     roof["frac"] = roof["achieved"] / roof["peak"]
     return {"workload": "prefill lengths %s, T=%d; H_k=16, H_v=32, d_k=d_v=%d, W=4, %s activations, fp32 "
                         "arithmetic" % (b.lengths, b.total_tokens, d, act),
@@ -713,7 +726,9 @@ def measured_peaks() -> dict:
 
 def annotate(obj, peaks: dict) -> None:
     """Adds to every roofline in the line its fraction of the measured peak of
-    the same resource (`frac_of_measured`)."""
+    the same resource (`frac_of_measured`), and where its measured HBM traffic
+    is known, that traffic's rate over the measured streaming-copy rate
+    (`traffic_frac_of_measured_copy`)."""
     if isinstance(obj, dict):
         roof = obj.get("roofline")
         if isinstance(roof, dict) and "achieved" in roof:
@@ -724,6 +739,8 @@ def annotate(obj, peaks: dict) -> None:
             else:
                 ref = peaks["mfma_bf16_tflops"]
             roof["frac_of_measured"] = roof["achieved"] / ref
+            if roof.get("traffic_gbs") is not None:
+                roof["traffic_frac_of_measured_copy"] = roof["traffic_gbs"] / peaks["hbm_copy_gbs"]
         for v in obj.values():
             annotate(v, peaks)
 
