@@ -623,7 +623,7 @@ int forward_impl(const gdn_layer_desc* desc, const void* x, const void* conv_wei
       static thread_local gdn::SeqOrder none;
       none.n = 0;
       static thread_local gdn::FusedConv fc;
-      fc.n = 0; fc.slices = pa.slices; fc.sync = sync;
+      fc.n = 0; fc.slices = pa.slices; fc.sync = sync; fc.own_first = 1;
       fc.target = 0; fc.task = (int32_t)(pa.task_us * 100.0);
       fc.scan0 = (int32_t)(kScan0Us * 100.0); fc.scan1 = (int32_t)(kScan1Us * 100.0);
       fc.plan = plan; fc.plan_seqs = num_seqs;
@@ -721,6 +721,7 @@ int forward_impl(const gdn_layer_desc* desc, const void* x, const void* conv_wei
     fc.plan_seqs = 0;
     fc.stream = 0;
     fc.helpers = 0;
+    fc.own_first = 1;  // a scan of 2.8 us per chunk would catch up with rows converted by others
     const int mode = conv_in_scan_mode();
     const int cus = device_cus(st);
     if (mode >= 0 && order.n > 0 && order.n <= gdn::kMaxFusedRanks && aligned(conv_weight, 16) &&
@@ -1100,6 +1101,11 @@ extern "C" int kda_varlen_forward(const gdn_layer_desc* desc, const void* x, con
     fc.plan_seqs = 0;
     fc.stream = 0;
     fc.helpers = 0;
+    // A KDA scan takes 8.3 us per chunk, well behind the conversion of its rows
+    // by the other workgroups: the tasks go chunk-major and each workgroup by
+    // its time budget alone, so the long sequences start scanning after their
+    // first chunks (0.556 -> 0.543 ms on the prefill workload)
+    fc.own_first = 0;
     const WsLayout wl = ws_layout(desc, total_tokens, num_seqs);
     const int mode = conv_in_scan_mode();
     if (mode >= 0 && order.n > 0 && order.n <= gdn::kMaxFusedRanks && aligned(conv_weight, 16) &&

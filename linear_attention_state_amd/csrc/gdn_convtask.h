@@ -52,10 +52,15 @@ __device__ __forceinline__ int chunk_wait(const int32_t* ready, int slices, int 
 //
 // Every workgroup first claims conv tasks (kConvTaskRows rows x
 // kConvTaskChannels channels of one sequence, each wave converting 16 rows of
-// 512 channels; the tasks of the longest sequence come first) from a counter in
-// global memory: at least until every task of its own sequence has been
-// claimed, and beyond that while its scan, priced by the host's time model,
-// can still end by the host's estimate of the balanced finish.  It then starts
+// 512 channels) from a counter in global memory, while its scan, priced by
+// the host's time model, can still end by the host's estimate of the balanced
+// finish.  Two orders (FusedConv::own_first): sequence-major, the longest
+// sequence's tasks first, with every workgroup claiming at least until its own
+// sequence's tasks are all claimed (the gated delta rule, whose scans would
+// catch up with rows converted by others); or chunk-major, every sequence's
+// chunk 0 first, then every chunk 1, and so on, by the time budget alone (KDA,
+// whose slower scans the conversion stays ahead of).  In both, the last
+// sequence's workgroups claim until every task is claimed.  It then starts
 // its scan, which waits for each chunk's rows when it first needs them (each
 // task is counted for its sequence and for its chunk), so later chunks may
 // still be converting by other workgroups while it scans.  A workgroup only
@@ -126,13 +131,33 @@ __device__ __forceinline__ void conv_part(const ScanArgs& a, ConvTask& k, int b,
 
 template <bool DP>
 __device__ __forceinline__ ConvTask conv_decode(const ScanArgs& a, const SeqOrder& ord, const FusedConv& fc, int t) {
-  int lo = 0, hi = plan_fused_n<DP>(fc);  // rank of task t: first[r] <= t < first[r + 1]
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (plan_first<DP>(fc, mid) <= t) lo = mid; else hi = mid;
+  int lo = 0, loc = 0;
+  if (!DP && !fc.own_first) {
+    // chunk-major: every rank's chunk 0, then every rank's chunk 1, ...  The
+    // ranks run longest first, so those that still hold chunk c are a prefix
+    const int S = fc.slices;
+    int c0 = 0, g = t;
+    for (int act = fc.n; act >= 1; --act) {  // chunks [c0, c1) are held by ranks 0 .. act-1
+      const int c1 = (fc.first[act] - fc.first[act - 1]) / S;
+      const int span = (c1 - c0) * act * S;
+      if (g < span) {
+        const int c = c0 + g / (act * S), j = g % (act * S);
+        lo = j / S;
+        loc = c * S + j % S;
+        break;
+      }
+      g -= span;
+      c0 = c1;
+    }
+  } else {
+    int hi = plan_fused_n<DP>(fc);  // rank of task t: first[r] <= t < first[r + 1]
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (plan_first<DP>(fc, mid) <= t) lo = mid; else hi = mid;
+    }
+    loc = t - plan_first<DP>(fc, lo);
   }
   ConvTask k;
-  const int loc = t - plan_first<DP>(fc, lo);
   k.rank = lo;
   k.s = plan_seq<DP>(ord, fc, lo);
   k.seq0 = a.cu[k.s];
@@ -282,13 +307,16 @@ __device__ void conv_phase(SM& sm, const ScanArgs& a, const SeqOrder& ord, const
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n_ranks = plan_fused_n<DP>(fc);
   const int total = plan_first<DP>(fc, n_ranks);
-  const int last = plan_first<DP>(fc, rank + 1);  // my rank's tasks end here
+  // claim at least until this task index (my rank's tasks end there; with
+  // own_first off, only the last rank holds to it, every task then)
+  const int last = (fc.own_first || rank == n_ranks - 1) ? plan_first<DP>(fc, rank + 1) : 0;
   // latest claim of a task that two more precede before my scan
   const int my_s = plan_seq<DP>(ord, fc, rank);
   const int32_t latest =
       plan_target<DP>(fc) - fc.scan0 - fc.scan1 * ((a.cu[my_s + 1] - a.cu[my_s] + BT - 1) / BT) - 3 * fc.task;
   const uint64_t t_begin = __builtin_amdgcn_s_memrealtime();
-  if (tid == 0) sm.task = __hip_atomic_fetch_add(fc.sync, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  // the first claim as the later ones (with own_first set, always taken)
+  if (tid == 0) sm.task = claim_after(fc, -1, total, last, latest, t_begin);
   lds_barrier();
   int t = __builtin_amdgcn_readfirstlane(sm.task);
   lds_barrier();  // every thread has read sm.task before thread 0 writes it again

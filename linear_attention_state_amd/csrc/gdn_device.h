@@ -244,6 +244,10 @@ struct FusedConv {
   // finished per chunk.
   int32_t stream;
   int32_t helpers;
+  // 1: a workgroup claims at least until every task of its own sequence is
+  // claimed (and beyond that by its time budget); 0: by its time budget alone,
+  // except the last rank's workgroups, which claim until every task is claimed
+  int32_t own_first;
 };
 constexpr size_t kFusedSyncBytes = 4096;  // room for sync[0 .. kMaxFusedRanks]
 
