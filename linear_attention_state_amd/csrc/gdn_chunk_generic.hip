@@ -29,6 +29,8 @@
 // X, U) serves directly as the B operand of a later product when that product's
 // k steps run in the order k = 4 kq + s (step s takes element s of the tile),
 // with the A operand read from LDS in the same order.
+#include <type_traits>
+
 #include "gdn_device.h"
 #include "gdn_mfma.h"
 
@@ -49,7 +51,7 @@ struct GSmem {
   float q[GC][DK + 4];
   float v[GC][DV + 4];
   float a[GC][GPA];  // A (blocks above the diagonal stay zero)
-  float t[GC][GPA];  // T, then T diag(b)
+  float t[GC][GPA];  // T (b enters through the rows of X)
   float p[GC][GPA];  // P = M o Q K^T
   float gam[GC], eg[GC], ed[GC], bet[GC];
 };
@@ -64,6 +66,24 @@ __device__ __forceinline__ float4 load4(const void* y, int64_t idx) {
   } else {
     return *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(y) + idx);
   }
+}
+
+// 4 consecutive activations as raw bits (8 bytes in bf16, 16 in fp32), and as fp32
+template <bool BF16>
+struct Raw4 {
+  typedef typename std::conditional<BF16, uint2, float4>::type type;
+};
+template <bool BF16>
+__device__ __forceinline__ typename Raw4<BF16>::type load_raw4(const void* y, int64_t idx) {
+  if constexpr (BF16) return *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(y) + idx);
+  else return *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(y) + idx);
+}
+template <bool BF16>
+__device__ __forceinline__ float4 raw4_f32(typename Raw4<BF16>::type w) {
+  if constexpr (BF16)
+    return make_float4(__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xffff0000u), __uint_as_float(w.y << 16),
+                       __uint_as_float(w.y & 0xffff0000u));
+  else return w;
 }
 
 // pair index 0..9 -> block (R, C), C <= R, in the order (0,0) (1,0) (1,1) (2,0) ...
@@ -111,33 +131,78 @@ __global__ __launch_bounds__(GT) void chunk_generic_kernel(ScanArgs a, SeqOrder 
         S[j][dt][i] = nt < NVT ? s_in[(16 * dt + 4 * lq + i) * DV + 16 * nt + lr] : 0.f;
   }
 
+  // The chunk's q, k, v rows: groups of 4 activations, group i = tid + GT j of
+  // the [GC][2 DK + DV] rows (a thread's NL groups).  Where their raw bits fit
+  // the registers beside the state pass (PF), chunk c + 1's rows load while
+  // chunk c is computed; else each chunk loads its own at the start.
+  constexpr int W4 = (2 * DK + DV) / 4;
+  constexpr int NL = GC * W4 / GT;
+  static_assert(GC * W4 % GT == 0, "whole groups per thread");
+  constexpr bool PF = NL * (BF16 ? 2 : 4) <= 48 && DK * DV < D * D;  // the 128 x 128 state leaves no room
+  typename Raw4<BF16>::type raw[PF ? NL : 1];
+  float gpre = 0.f, bpre = 0.f;
+  auto group = [&](int i, int& t, int& gcol, float*& dst) {
+    t = i / W4;
+    const int col = 4 * (i % W4);
+    if (col < DK) {
+      gcol = h * DK + col;
+      dst = &sm.q[t][col];
+    } else if (col < 2 * DK) {
+      gcol = (Hk + h) * DK + col - DK;
+      dst = &sm.k[t][col - DK];
+    } else {
+      gcol = 2 * Hk * DK + m * DV + col - 2 * DK;
+      dst = &sm.v[t][col - 2 * DK];
+    }
+  };
+  // rows past the end of the sequence load as zero
+  auto prefetch = [&](int c) {
+    const int nv = min(GC, L - c * GC);
+    const int64_t row0 = (int64_t)r0 + c * GC;
+#pragma unroll
+    for (int j = 0; j < NL; ++j) {
+      int t, gcol;
+      float* dst;
+      group(tid + GT * j, t, gcol, dst);
+      raw[PF ? j : 0] = t < nv ? load_raw4<BF16>(a.y, (row0 + t) * C + gcol) : typename Raw4<BF16>::type{};
+    }
+    if (wv == 0) {
+      gpre = lane < nv ? a.g[(row0 + lane) * Hv + m] : 0.f;
+      bpre = lane < nv ? a.beta[(row0 + lane) * Hv + m] : 0.f;
+    }
+  };
+  if constexpr (PF) prefetch(0);
+
   for (int c = 0; c < N; ++c) {
     const int nv = min(GC, L - c * GC);
     const int64_t row0 = (int64_t)r0 + c * GC;
     __syncthreads();  // the previous chunk's tiles are read
     // ---- q, k, v rows (zero past the end), g and b
-    constexpr int W4 = (2 * DK + DV) / 4;
-    for (int i = tid; i < GC * W4; i += GT) {
-      const int t = i / W4, col = 4 * (i % W4);
-      int gcol;
-      float* dst;
-      if (col < DK) {
-        gcol = h * DK + col;
-        dst = &sm.q[t][col];
-      } else if (col < 2 * DK) {
-        gcol = (Hk + h) * DK + col - DK;
-        dst = &sm.k[t][col - DK];
-      } else {
-        gcol = 2 * Hk * DK + m * DV + col - 2 * DK;
-        dst = &sm.v[t][col - 2 * DK];
+    if constexpr (PF) {
+#pragma unroll
+      for (int j = 0; j < NL; ++j) {
+        int t, gcol;
+        float* dst;
+        group(tid + GT * j, t, gcol, dst);
+        *reinterpret_cast<float4*>(dst) = raw4_f32<BF16>(raw[j]);
       }
-      const float4 val = t < nv ? load4<BF16>(a.y, (row0 + t) * C + gcol) : make_float4(0.f, 0.f, 0.f, 0.f);
-      *reinterpret_cast<float4*>(dst) = val;
+    } else {
+      for (int i = tid; i < GC * W4; i += GT) {
+        int t, gcol;
+        float* dst;
+        group(i, t, gcol, dst);
+        const float4 val = t < nv ? load4<BF16>(a.y, (row0 + t) * C + gcol) : make_float4(0.f, 0.f, 0.f, 0.f);
+        *reinterpret_cast<float4*>(dst) = val;
+      }
+      if (wv == 0) {
+        gpre = lane < nv ? a.g[(row0 + lane) * Hv + m] : 0.f;
+        bpre = lane < nv ? a.beta[(row0 + lane) * Hv + m] : 0.f;
+      }
     }
     if (wv == 0) {
       const int t = lane;
-      const float g = t < nv ? a.g[(row0 + t) * Hv + m] : 0.f;
-      const float b = t < nv ? a.beta[(row0 + t) * Hv + m] : 0.f;
+      const float g = gpre;
+      const float b = bpre;
       const float gm = wave_prefix_sum(g);  // rows past the end add nothing
       const float glast = __shfl(gm, GC - 1);
       sm.gam[t] = gm;
@@ -146,6 +211,9 @@ __global__ __launch_bounds__(GT) void chunk_generic_kernel(ScanArgs a, SeqOrder 
       sm.bet[t] = b;
     }
     __syncthreads();
+    if constexpr (PF) {
+      if (c + 1 < N) prefetch(c + 1);  // in flight through this chunk's products
+    }
     // ---- blocks of A (even w) and P (odd w): lane holds D[t = 16R + 4 lq + i][j = 16Cb + lr]
     for (int w = wv; w < 20; w += 4) {
       int R, Cb;
@@ -205,8 +273,6 @@ __global__ __launch_bounds__(GT) void chunk_generic_kernel(ScanArgs a, SeqOrder 
         }
     }
     __syncthreads();
-    for (int i = tid; i < GC * GC; i += GT) sm.t[i / GC][i % GC] *= sm.bet[i % GC];
-    __syncthreads();
     // ---- state pass over the wave's column tiles
     const float glast = sm.eg[GC - 1];
 #pragma unroll
@@ -228,14 +294,14 @@ __global__ __launch_bounds__(GT) void chunk_generic_kernel(ScanArgs a, SeqOrder 
             qs[tb] = mfma4(sm.q[16 * tb + lr][16 * dt + 4 * lq + st], sb, qs[tb]);
           }
         }
-      // X = V - e^gamma K S (in place of K S), then U = T2 X
+      // diag(b) X with X = V - e^gamma K S (in place of K S), then U = T diag(b) X
       f32x4 u[4];
 #pragma unroll
       for (int tb = 0; tb < 4; ++tb)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int t = 16 * tb + 4 * lq + i;
-          ks[tb][i] = sm.v[t][col] - sm.eg[t] * ks[tb][i];
+          ks[tb][i] = sm.bet[t] * (sm.v[t][col] - sm.eg[t] * ks[tb][i]);
         }
 #pragma unroll
       for (int tb = 0; tb < 4; ++tb) {
