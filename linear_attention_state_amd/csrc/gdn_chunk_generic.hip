@@ -171,7 +171,31 @@ __global__ __launch_bounds__(GT) void chunk_generic_kernel(ScanArgs a, SeqOrder 
       bpre = lane < nv ? a.beta[(row0 + lane) * Hv + m] : 0.f;
     }
   };
+  // Split prefetch (SP, fp32 where PF does not fit): chunk c + 1's q and k rows
+  // into registers while chunk c is computed, and chunk c's v rows issued at
+  // its start, in flight through the A and P products (v is first read by the
+  // state pass).
+  constexpr bool SP = !PF && !BF16;
+  constexpr int WQK = DK / 2, WV = DV / 4;  // groups per row of q and k, of v
+  constexpr int NQK = GC * WQK / GT, NV = GC * WV / GT;
+  static_assert(GC * WQK % GT == 0 && GC * WV % GT == 0, "whole groups per thread");
+  float4 qkraw[SP ? NQK : 1], vraw[SP ? NV : 1];
+  auto prefetch_qk = [&](int c) {
+    const int nv = min(GC, L - c * GC);
+    const int64_t row0 = (int64_t)r0 + c * GC;
+#pragma unroll
+    for (int j = 0; j < NQK; ++j) {
+      const int i = tid + GT * j, t = i / WQK, col = 4 * (i % WQK);
+      const int gcol = col < DK ? h * DK + col : (Hk + h) * DK + col - DK;
+      qkraw[SP ? j : 0] = t < nv ? load4<false>(a.y, (row0 + t) * C + gcol) : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    if (wv == 0) {
+      gpre = lane < nv ? a.g[(row0 + lane) * Hv + m] : 0.f;
+      bpre = lane < nv ? a.beta[(row0 + lane) * Hv + m] : 0.f;
+    }
+  };
   if constexpr (PF) prefetch(0);
+  if constexpr (SP) prefetch_qk(0);
 
   for (int c = 0; c < N; ++c) {
     const int nv = min(GC, L - c * GC);
@@ -185,6 +209,18 @@ __global__ __launch_bounds__(GT) void chunk_generic_kernel(ScanArgs a, SeqOrder 
         float* dst;
         group(tid + GT * j, t, gcol, dst);
         *reinterpret_cast<float4*>(dst) = raw4_f32<BF16>(raw[j]);
+      }
+    } else if constexpr (SP) {
+#pragma unroll
+      for (int j = 0; j < NV; ++j) {
+        const int i = tid + GT * j, t = i / WV, col = 4 * (i % WV);
+        vraw[j] = t < nv ? load4<false>(a.y, (row0 + t) * C + 2 * Hk * DK + m * DV + col) : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+#pragma unroll
+      for (int j = 0; j < NQK; ++j) {
+        const int i = tid + GT * j, t = i / WQK, col = 4 * (i % WQK);
+        float* dst = col < DK ? &sm.q[t][col] : &sm.k[t][col - DK];
+        *reinterpret_cast<float4*>(dst) = qkraw[j];
       }
     } else {
       for (int i = tid; i < GC * W4; i += GT) {
@@ -214,6 +250,9 @@ __global__ __launch_bounds__(GT) void chunk_generic_kernel(ScanArgs a, SeqOrder 
     if constexpr (PF) {
       if (c + 1 < N) prefetch(c + 1);  // in flight through this chunk's products
     }
+    if constexpr (SP) {
+      if (c + 1 < N) prefetch_qk(c + 1);
+    }
     // ---- blocks of A (even w) and P (odd w): lane holds D[t = 16R + 4 lq + i][j = 16Cb + lr]
     for (int w = wv; w < 20; w += 4) {
       int R, Cb;
@@ -235,6 +274,13 @@ __global__ __launch_bounds__(GT) void chunk_generic_kernel(ScanArgs a, SeqOrder 
           sm.p[t][j] = j <= t ? e * acc[i] : 0.f;
         else
           sm.a[t][j] = j < t ? sm.bet[t] * e * acc[i] : 0.f;
+      }
+    }
+    if constexpr (SP) {
+#pragma unroll
+      for (int j = 0; j < NV; ++j) {
+        const int i = tid + GT * j, t = i / WV, col = 4 * (i % WV);
+        *reinterpret_cast<float4*>(&sm.v[t][col]) = vraw[j];
       }
     }
     __syncthreads();
