@@ -307,34 +307,41 @@ namespace gdn {
 namespace {
 
 // Copies block src[i] of both pools to block dst[i].  Block x = pair i, block y
-// = 64 KiB piece of the concatenation [recurrent state; conv state]; 256
-// threads move 16 bytes per load, 16 loads in flight each, non-temporal (the
-// blocks are touched once; 4% faster than cached accesses).
+// = 32 KiB piece of the concatenation [recurrent state; conv state]; 256
+// threads move 16 bytes per access, in two rounds of four loads followed by
+// their four stores, non-temporal (the blocks are touched once; 4% faster than
+// cached accesses).  Measured on 256 pairs of 2 MiB + 48 KiB: 0.207 ms, against
+// 0.214 ms for 64 KiB pieces with all sixteen loads issued before any store;
+// eight loads before the first store ran at 0.475 ms.
+constexpr int kCopyPiece = 32768;
 __global__ __launch_bounds__(256) void state_copy_kernel(StateCopyArgs a) {
   const int i = blockIdx.x;
   const int sb = a.src[i], db = a.dst[i];
   if (sb < 0 || sb >= a.num_blocks || db < 0 || db >= a.num_blocks || sb == db) return;
-  const int64_t piece = (int64_t)blockIdx.y * 65536;
+  const int64_t piece = (int64_t)blockIdx.y * kCopyPiece;
   const int64_t ssm_bytes = a.ssm_bytes, total = a.ssm_bytes + a.conv_bytes;
   if (piece >= total) return;
-  constexpr int K = 16;
-  u32x4 v[K];
+  constexpr int K = kCopyPiece / (256 * 16), G = 4;
 #pragma unroll
-  for (int k = 0; k < K; ++k) {
-    const int64_t o = piece + ((int64_t)k * 256 + threadIdx.x) * 16;
-    if (o < total) {
-      const char* src = o < ssm_bytes ? a.ssm_pool + (int64_t)sb * a.ssm_stride + o
-                                      : a.conv_pool + (int64_t)sb * a.conv_stride + (o - ssm_bytes);
-      v[k] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src));
+  for (int g0 = 0; g0 < K; g0 += G) {
+    u32x4 v[G];
+#pragma unroll
+    for (int k = 0; k < G; ++k) {
+      const int64_t o = piece + ((int64_t)(g0 + k) * 256 + threadIdx.x) * 16;
+      if (o < total) {
+        const char* src = o < ssm_bytes ? a.ssm_pool + (int64_t)sb * a.ssm_stride + o
+                                        : a.conv_pool + (int64_t)sb * a.conv_stride + (o - ssm_bytes);
+        v[k] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src));
+      }
     }
-  }
 #pragma unroll
-  for (int k = 0; k < K; ++k) {
-    const int64_t o = piece + ((int64_t)k * 256 + threadIdx.x) * 16;
-    if (o < total) {
-      char* dst = o < ssm_bytes ? a.ssm_pool + (int64_t)db * a.ssm_stride + o
-                                : a.conv_pool + (int64_t)db * a.conv_stride + (o - ssm_bytes);
-      __builtin_nontemporal_store(v[k], reinterpret_cast<u32x4*>(dst));
+    for (int k = 0; k < G; ++k) {
+      const int64_t o = piece + ((int64_t)(g0 + k) * 256 + threadIdx.x) * 16;
+      if (o < total) {
+        char* dst = o < ssm_bytes ? a.ssm_pool + (int64_t)db * a.ssm_stride + o
+                                  : a.conv_pool + (int64_t)db * a.conv_stride + (o - ssm_bytes);
+        __builtin_nontemporal_store(v[k], reinterpret_cast<u32x4*>(dst));
+      }
     }
   }
 }
@@ -343,7 +350,7 @@ __global__ __launch_bounds__(256) void state_copy_kernel(StateCopyArgs a) {
 
 hipError_t launch_state_copy(const StateCopyArgs& a, int n, hipStream_t st) {
   const int64_t total = a.ssm_bytes + a.conv_bytes;
-  const int64_t pieces = (total + 65535) / 65536;
+  const int64_t pieces = (total + kCopyPiece - 1) / kCopyPiece;
   if (n <= 0 || pieces <= 0) return hipSuccess;
   if (pieces > 65535 || n > 2147483647) return hipErrorInvalidValue;
   hipLaunchKernelGGL(state_copy_kernel, dim3(n, (unsigned)pieces), dim3(256), 0, st, a);
