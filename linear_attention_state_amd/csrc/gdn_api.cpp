@@ -1004,7 +1004,22 @@ extern "C" int ssd_varlen_scan(const ssd_layer_desc* desc, const void* x, int64_
   // sequences of length >= 2 in chunks, those of length 0 and 1 in the token
   // kernel; they touch disjoint blocks, so the two launches need no order
   if (any_long) {
-    const hipError_t e = timed(K_SSD, st, [&] { return gdn::launch_ssd(a, st); });
+    // with the host offsets: the sequences of length >= 2 only, longest first
+    // (a pair of heads fills a CU, so the grid runs in rounds; on 8 sequences
+    // of 256-4096 tokens the longest chains otherwise started in the second)
+    static thread_local gdn::SeqOrder order;
+    order.n = 0;
+    if (cu_seqlens_host && num_seqs <= gdn::kMaxOrder) {
+      std::vector<std::pair<int, int>> lens;
+      for (int i = 0; i < num_seqs; ++i) {
+        const int L = cu_seqlens_host[i + 1] - cu_seqlens_host[i];
+        if (L >= 2) lens.push_back({-L, i});
+      }
+      std::stable_sort(lens.begin(), lens.end());
+      for (size_t i = 0; i < lens.size(); ++i) order.seq[i] = (uint16_t)lens[i].second;
+      order.n = (int32_t)lens.size();
+    }
+    const hipError_t e = timed(K_SSD, st, [&] { return gdn::launch_ssd(a, order, st); });
     if (e != hipSuccess) return fail(GDN_EHIP, "ssd scan launch: %s", hipGetErrorString(e));
   }
   if (any_short) {

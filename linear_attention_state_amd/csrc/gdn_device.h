@@ -200,7 +200,9 @@ struct SsdArgs {
   uint16_t* y;
 };
 bool ssd_supported(int head_dim, int state_dim);
-hipError_t launch_ssd(const SsdArgs& a, hipStream_t st);        // sequences of length >= 2
+// sequences of length >= 2; ord (n > 0): only the sequences it lists, one rank
+// of workgroups each, in its order (ord.seq[r] < num_seqs)
+hipError_t launch_ssd(const SsdArgs& a, const SeqOrder& ord, hipStream_t st);
 hipError_t launch_ssd_token(const SsdArgs& a, hipStream_t st);  // sequences of length 0 and 1
 hipError_t launch_recurrent(const ScanArgs& a, int dk, int dv, bool bf16, hipStream_t st);
 // The conv of the chunked sequences run by the chunk-scan workgroups

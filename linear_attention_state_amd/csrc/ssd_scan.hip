@@ -85,12 +85,16 @@ __device__ __forceinline__ float softplus_f(float v) { return v > 20.f ? v : log
 // 512 threads per (sequence, pair of heads of one group): waves 4h..4h+3 own
 // head h; the C and B rows are staged once and each C B^T tile is formed once
 // and masked for both heads.
+// Workgroups go by rank in `ord` (longest sequence first) when it is given:
+// a pair's workgroup fills a CU, so the grid runs in rounds, and the longest
+// chains must start in the first.
 template <int HP>
-__global__ __launch_bounds__(SNT * HP, 2 / HP) void ssd_chunk_kernel(SsdArgs a) {
+__global__ __launch_bounds__(SNT * HP, 2 / HP) void ssd_chunk_kernel(SsdArgs a, SeqOrder ord) {
   constexpr int NTH = SNT * HP;
   __shared__ SsdSmem<HP> sm;
   const int H = a.num_heads, HB = H / HP;  // workgroups per sequence
-  const int s = blockIdx.x / HB;
+  const int rank = blockIdx.x / HB;
+  const int s = ord.n > 0 ? (rank < ord.n ? (int)ord.seq[rank] : a.num_seqs) : rank;
   int k = blockIdx.x % HB;
   if (HB % 8 == 0) k = (k % 8) * (HB / 8) + k / 8;  // heads of a group on one XCD (workgroups go round-robin over 8)
   if (s >= a.num_seqs || !seq_active(a.read_idx, a.write_idx, s, a.num_blocks)) return;
@@ -357,14 +361,15 @@ hipError_t launch_ssd_token(const SsdArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
-hipError_t launch_ssd(const SsdArgs& a, hipStream_t st) {
+hipError_t launch_ssd(const SsdArgs& a, const SeqOrder& ord, hipStream_t st) {
   if (a.num_seqs <= 0 || a.num_heads <= 0) return hipSuccess;
-  const int64_t blocks = (int64_t)a.num_seqs * a.num_heads;
+  if (ord.n < 0 || ord.n > kMaxOrder || ord.n > a.num_seqs) return hipErrorInvalidValue;
+  const int64_t blocks = (int64_t)(ord.n > 0 ? ord.n : a.num_seqs) * a.num_heads;
   if (blocks > INT32_MAX) return hipErrorInvalidValue;
   if ((a.num_heads / a.num_groups) % 2 == 0)  // pairs of heads of one group share B, C and C B^T
-    hipLaunchKernelGGL(ssd_chunk_kernel<2>, dim3((unsigned)(blocks / 2)), dim3(2 * SNT), 0, st, a);
+    hipLaunchKernelGGL(ssd_chunk_kernel<2>, dim3((unsigned)(blocks / 2)), dim3(2 * SNT), 0, st, a, ord);
   else
-    hipLaunchKernelGGL(ssd_chunk_kernel<1>, dim3((unsigned)blocks), dim3(SNT), 0, st, a);
+    hipLaunchKernelGGL(ssd_chunk_kernel<1>, dim3((unsigned)blocks), dim3(SNT), 0, st, a, ord);
   return hipGetLastError();
 }
 
