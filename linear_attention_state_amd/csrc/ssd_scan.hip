@@ -133,6 +133,12 @@ __global__ __launch_bounds__(SNT * HP, 2 / HP) void ssd_chunk_kernel(SsdArgs a, 
                                                 (uint32_t)(((int64_t)(nv - 1) * a.bc_stride + SN) * 2));
     const __amdgpu_buffer_rsrc_t xs = make_rsrc(a.x + (int64_t)row0 * a.x_stride + m * SP,
                                                 (uint32_t)(((int64_t)(nv - 1) * a.x_stride + SP) * 2));
+    // d A first, by every wave (wave 0 of each head uses it), rows past the end
+    // reading 0: no memory access of the step sits under a branch and the rows
+    // follow this load, so the waits for them and for it never cover the
+    // previous chunk's y stores
+    const __amdgpu_buffer_rsrc_t ds = make_rsrc(a.dt + (int64_t)row0 * H + m, (uint32_t)(((nv - 1) * H + 1) * 4));
+    rdt = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(ds, lane < nv ? lane * H * 4 : -1, 0, 0));
 #pragma unroll
     for (int i = 0; i < NCB; ++i) {
       const int q = tid + NTH * i, t = q >> 4, cc = q & 15;
@@ -146,11 +152,19 @@ __global__ __launch_bounds__(SNT * HP, 2 / HP) void ssd_chunk_kernel(SsdArgs a, 
       const int off = t < nv ? (int)((t * a.x_stride + 8 * cc) * 2) : -1;
       rx[i] = __builtin_amdgcn_raw_buffer_load_b128(xs, (uint32_t)off, 0, 0);
     }
-    if (wl == 0) rdt = lane < nv ? a.dt[(int64_t)(row0 + lane) * H + m] : 0.f;
   };
   if (nch > 0) load(0);
+  // a chunk's output rows go out at the start of the next step, before the
+  // waits for that step's rows, so that on every path into the loop the same
+  // accesses follow those loads and the waits never cover the stores (the
+  // first step's stores have no rows: the range check drops them)
+  u32x4 yst[2] = {};
+  int yoff[2] = {-1, -1};
+  __amdgpu_buffer_rsrc_t ysr = make_rsrc(a.y, 0u);
   for (int c = 0; c < nch; ++c) {
     const int nv = min(SBT, L - c * SBT);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) __builtin_amdgcn_raw_buffer_store_b128(yst[i], ysr, yoff[i], 0, 0);
     lds_barrier();  // the previous chunk's LDS reads are done
 #pragma unroll
     for (int i = 0; i < NCB; ++i) {
@@ -279,14 +293,18 @@ __global__ __launch_bounds__(SNT * HP, 2 / HP) void ssd_chunk_kernel(SsdArgs a, 
       }
     }
     lds_barrier();  // every output row is staged
+    // this chunk's output rows, stored at the start of the next step (rows
+    // past the end are dropped by the buffer's range check)
+    ysr = make_rsrc(a.y + ((int64_t)(r0 + c * SBT) * H + m) * SP, (uint32_t)(((nv - 1) * H + 1) * SP * 2));
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int q = lt + SNT * i, t = q >> 3, cc = q & 7;
-      if (t < nv)
-        *reinterpret_cast<gptr<u32x4>>(as_global(a.y + ((int64_t)(r0 + c * SBT + t) * H + m) * SP + 8 * cc)) =
-            *reinterpret_cast<const u32x4*>(&Y[sw128(t, 8 * cc)]);
+      yst[i] = *reinterpret_cast<const u32x4*>(&Y[sw128(t, 8 * cc)]);
+      yoff[i] = t < nv ? (t * H * SP + 8 * cc) * 2 : -1;
     }
   }
+#pragma unroll
+  for (int i = 0; i < 2; ++i) __builtin_amdgcn_raw_buffer_store_b128(yst[i], ysr, yoff[i], 0, 0);
 #pragma unroll
   for (int nb = 0; nb < 8; ++nb) dst[4 * nb + g] = S[nb];
 }
