@@ -146,8 +146,13 @@ int gdn_workspace_size(const gdn_layer_desc* desc, int32_t total_tokens,
  * the scans run (the first workgroups to start become the helpers, so no scan
  * waits for a workgroup that has not started); a time model chooses.  The environment variable
  * GDN_CONV_IN_SCAN=never|always|stream (read at every call) overrides the
- * choice ("stream" falls back to the others where it cannot run).  Every
- * output and state is the same bit for bit in all three.
+ * choice ("stream" falls back to the others where it cannot run).  Inside the
+ * chunk kernel (host plan), the workgroups claim the conv tasks either longest
+ * sequence first, each until its own sequence's tasks are claimed, or chunk by
+ * chunk across the sequences by a time budget alone (for batches whose lengths
+ * are far apart); the host's estimates choose, and GDN_CONV_CLAIM=own|budget
+ * overrides them.  Every output and state is the same bit for bit in all of
+ * these.
  */
 int gdn_varlen_forward(const gdn_layer_desc* desc, const void* x,
                        const void* conv_weight, const float* g, const float* beta,

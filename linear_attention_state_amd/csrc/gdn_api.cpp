@@ -114,6 +114,21 @@ constexpr double kTargetMargin = 1.03;
 //   bound: each converts a task's rows at about kHelperBytesPerUs.
 constexpr double kScanPlainUs = 2.55, kScanCrowdUs = 0.65, kPhasedScale = 0.95;
 constexpr double kStreamStartUs = 40.0, kStreamScanScale = 1.06, kHelperBytesPerUs = 18.7e3;
+// The claim rule of the phased conv, chosen per batch.  Sequence-major with
+// every workgroup claiming until its own sequence's tasks are claimed (the
+// constants above) suits batches of similar lengths; chunk-major by time budget
+// alone (FusedConv::own_first = 0) lets the long sequences start their scans
+// at once while the short ones convert, which suits skewed batches.  The
+// budgets of the latter take the per-workgroup timeline's constants: a scan
+// of kCalScan0Us + kCalScan1Us per chunk, a task of kCalTaskUs, and a target
+// kBudgetSlackTasks tasks past the larger of the even spread and the longest
+// scan (a multiple of the even spread fails small batches, whose target sits
+// at that bound: every budget would go negative).  Measured (ms, own tasks ->
+// budget): 4 x 4096 beside 4 x 128 0.312 -> 0.250; 4096, 4096, 2048, 2048,
+// 1024, 1024, 512, 256: 0.261 -> 0.246; 4 x 2048 beside 4 x 64 0.170 -> 0.152;
+// but the prefill mix 0.281 -> 0.283, eight of 2500 0.280 -> 0.281 and the
+// mixed step 0.093 -> 0.096, which the estimates below keep on their own tasks.
+constexpr double kCalScan0Us = 4.5, kCalScan1Us = 2.95, kCalTaskUs = 12.5, kBudgetSlackTasks = 2.0;
 // The KDA chunk kernel's scan: kKdaScan0Us + kKdaScan1Us per chunk (measured on
 // MI355X, 128 x 128 head); the conv inside it is placed by the phased rule.
 constexpr double kKdaScan0Us = 10.0, kKdaScan1Us = 8.3;
@@ -138,6 +153,17 @@ int conv_in_scan_mode() {
   if (!strcmp(v, "always")) return 1;   // the phased conv inside the chunk kernel
   if (!strcmp(v, "stream")) return 2;   // streaming, when there are spare CUs for helpers
   if (!strcmp(v, "never")) return -1;
+  return 0;
+}
+
+// GDN_CONV_CLAIM: "own" keeps the phased conv's workgroups claiming until
+// their own sequence's tasks are claimed, "budget" makes them claim by time
+// budget alone; unset (or anything else), the host's estimates choose.
+int conv_claim_mode() {
+  const char* v = getenv("GDN_CONV_CLAIM");
+  if (!v) return 0;
+  if (!strcmp(v, "own")) return 1;
+  if (!strcmp(v, "budget")) return 2;
   return 0;
 }
 
@@ -769,6 +795,31 @@ int forward_impl(const gdn_layer_desc* desc, const void* x, const void* conv_wei
         fc.task = (int32_t)(task_us * 100.0);
         fc.scan0 = (int32_t)(scan0 * 100.0);
         fc.scan1 = (int32_t)(scan1 * 100.0);
+      }
+      if (use_phased && fc.n > 0) {
+        // own tasks: sequence r scans once the tasks up to its own are claimed,
+        // at the rate of every workgroup converting; by budget: the target
+        // below.  A task of a narrower layer is priced in proportion.
+        const double task_cal =
+            kCalTaskUs * task_us / (2.0 * gdn::kConvTaskRows * gdn::kConvTaskChannels * 2.0 / kTaskBytesPerUs);
+        const double rate = (double)wgs / task_cal;
+        double own_end = 0.0, scans_cal = 0.0;
+        for (int r = 0; r < order.n; ++r) {
+          const int n_r = (fc.first[r + 1] - fc.first[r]) / fc.slices;
+          own_end = std::max(own_end, fc.first[r + 1] / rate + kCalScan0Us + kCalScan1Us * n_r);
+          scans_cal += kCalScan0Us + kCalScan1Us * n_r;
+        }
+        const double even = (fc.first[order.n] * task_cal + desc->num_v_heads * scans_cal) / (double)wgs;
+        const double budget_end = std::max(even, kCalScan0Us + kCalScan1Us * chunks0 + 2.0 * task_cal) +
+                                  kBudgetSlackTasks * task_cal;
+        const int claim = conv_claim_mode();
+        if (claim == 2 || (claim == 0 && own_end >= budget_end)) {
+          fc.own_first = 0;
+          fc.target = (int32_t)(budget_end * 100.0);
+          fc.task = (int32_t)(task_cal * 100.0);
+          fc.scan0 = (int32_t)(kCalScan0Us * 100.0);
+          fc.scan1 = (int32_t)(kCalScan1Us * 100.0);
+        }
       }
       if (use_stream) {  // first[r]: the first chunk counter of rank r
         fc.stream = 1;

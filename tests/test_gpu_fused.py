@@ -191,3 +191,52 @@ def test_single_sequence_converts_all_its_own_rows():
     scans then wait chunk by chunk."""
     b = workloads.random_batch(workloads.BIG, [700, 1], seed=62)
     _both_ways(b, "single")
+
+
+def _run_claim(batch, rule):
+    """The phased conv with its claim rule forced ("own", "budget") or chosen
+    by the host (None)."""
+    old = {k: os.environ.get(k) for k in ("GDN_CONV_IN_SCAN", "GDN_CONV_CLAIM")}
+    os.environ["GDN_CONV_IN_SCAN"] = "always"
+    if rule is None:
+        os.environ.pop("GDN_CONV_CLAIM", None)
+    else:
+        os.environ["GDN_CONV_CLAIM"] = rule
+    try:
+        gdn.gdn_kernel_timing(True)
+        res = run_gpu(batch)
+        kernels = gdn.gdn_kernel_times()
+    finally:
+        gdn.gdn_kernel_timing(False)
+        for k, v in old.items():
+            if v is None:
+                os.environ.pop(k, None)
+            else:
+                os.environ[k] = v
+    assert "conv_silu_norm" not in kernels and "chunk_scan" in kernels, kernels
+    return res
+
+
+@pytest.mark.parametrize("name,lengths,fresh", [
+    ("skewed", [2048, 64, 2048, 64, 2048, 64, 2048, 64], None),
+    # (the two-token sequence continues from its block: started fresh, its
+    # first output row is b (q.k) v, whose slab norm can nearly vanish, so a
+    # relative error over that slab says nothing about the arithmetic)
+    ("spread", [900, 700, 300, 130, 65, 3, 2], [1, 0, 0, 1, 0, 0, 0]),
+    ("decode-beside", [1, 640, 1, 70, 1, 2], None),
+])
+def test_claim_rules_give_the_same_bits(name, lengths, fresh):
+    """Chunk-major claiming by time budget alone (the shortest sequence's
+    workgroups claim whatever is left) and sequence-major claiming of one's
+    own tasks first convert the same rows with the same arithmetic: outputs
+    and both states equal bit for bit, whichever rule the host picks, and
+    within the oracle bar."""
+    b = workloads.random_batch(workloads.BIG, lengths, seed=63, fresh=fresh)
+    print("case claim-%s: lengths %s" % (name, lengths), flush=True)
+    own = _run_claim(b, "own")
+    for rule in ("budget", None):
+        res = _run_claim(b, rule)
+        for a, c in zip(res, own):
+            assert torch.equal(_bits(a), _bits(c)), rule
+    errs = compare(b, own, run_oracle(b))
+    print("claim-%s: out %.3e state %.3e" % (name, errs["out_rel_l2"], errs["state_rel_l2"]), flush=True)
