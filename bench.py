@@ -94,7 +94,8 @@ def token_path_bytes(layer, n_tokens: int) -> float:
 # kernels the header holding the conv tasks they run.
 KERNEL_SOURCES = {"chunk_scan": ("gdn_chunk.hip", "gdn_convtask.h"), "token_recurrent": ("gdn_recurrent.hip",),
                   "kda_chunk": ("kda_chunk.hip", "gdn_convtask.h"), "chunk_generic": ("gdn_chunk_generic.hip",),
-                  "conv_silu_norm": ("gdn_conv.hip",), "ssd_scan": ("ssd_scan.hip",), "ssd_token": ("ssd_scan.hip",)}
+                  "conv_silu_norm": ("gdn_conv.hip",), "ssd_scan": ("ssd_scan.hip",), "ssd_token": ("ssd_scan.hip",),
+                  "state_copy": ("gdn_conv.hip",)}
 
 
 def kernel_source_sha(kernel: str):
@@ -631,7 +632,7 @@ def run_state_copy(steps: int, warmup: int):
     roof = {"bound": "hbm", "achieved": work / (k_ms * 1e-3) / 1e9, "peak": PEAK_HBM / 1e9, "unit": "GB/s",
             "kernel": "state_copy"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = None
+    add_traffic(roof, "state_copy", "copy", k_ms)
     return {"workload": "fork copy of 256 blocks (2 MiB recurrent + 48 KiB conv state each) within a 1024-block pool",
             "value": 256 / (ms * 1e-3), "unit": "blocks/s", "ms_per_step": ms, "roofline": roof,
             "kernels": {k: {"avg_ms": v[0] / max(v[1], 1), "launches": v[1]} for k, v in kt.items()}}
