@@ -29,6 +29,26 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
 
+// DPP lane move within each row of 16 lanes (or across rows for the row
+// broadcasts); lanes without a source lane get zero.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_move(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, ROW_MASK, 0xf, false));
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave: shifts by 1, 2, 4, 8 inside
+// each row of 16 lanes, then lane 15 of row 0 and lane 31 carried into the
+// later rows.
+__device__ __forceinline__ float wave_prefix_sum(float v) {
+  v += dpp_move<0x111, 0xf>(v);  // row_shr:1
+  v += dpp_move<0x112, 0xf>(v);  // row_shr:2
+  v += dpp_move<0x114, 0xf>(v);  // row_shr:4
+  v += dpp_move<0x118, 0xf>(v);  // row_shr:8
+  v += dpp_move<0x142, 0xa>(v);  // row_bcast:15 into rows 1 and 3
+  v += dpp_move<0x143, 0xc>(v);  // row_bcast:31 into rows 2 and 3
+  return v;
+}
+
 __device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {
   return __uint_as_float((uint32_t)b << 16);
 }

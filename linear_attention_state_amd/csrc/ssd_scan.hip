@@ -180,13 +180,11 @@ __global__ __launch_bounds__(SNT * HP, 2 / HP) void ssd_chunk_kernel(SsdArgs a, 
     if (wl == 0) {
       float d = 0.f;
       if (lane < nv) d = a.softplus ? softplus_f(rdt + bias) : rdt + bias;
-      float v = d * Am;
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const float u = __shfl_up(v, off);
-        if (lane >= off) v += u;
-      }
-      const float last = __shfl(v, 63);
+      // running sum of d A over the chunk's rows (lanes): in lane registers
+      // (row shifts and broadcasts), not through LDS permutes, since every
+      // other wave waits for it at the next barrier
+      const float v = wave_prefix_sum(d * Am);
+      const float last = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
       sm.gam[hh][lane] = v;
       sm.dd[hh][lane] = d;
       sm.wv[hh][lane] = __expf(last - v) * d;
