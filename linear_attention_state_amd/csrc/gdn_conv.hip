@@ -197,7 +197,7 @@ __global__ __launch_bounds__(256) void conv_silu_norm_kernel(ConvArgs a) {
         yv[e] = SILU ? silu(acc) : acc;
         ss += yv[e] * yv[e];
       }
-      for (int off = 1; off < group; off <<= 1) ss += __shfl_xor(ss, off);
+      ss = group_sum(ss, group);
       if (do_norm) {
         const float inv = scale * rsqrt_fast(ss + a.eps);
 #pragma unroll

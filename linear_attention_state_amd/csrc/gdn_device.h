@@ -36,6 +36,19 @@ __device__ __forceinline__ float dpp_move(float v) {
   return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, ROW_MASK, 0xf, false));
 }
 
+// Sum over the `group` lanes of a head (2, 4, 8 or 16, aligned within a row
+// of 16, the same for the whole wave), in lane registers: the pairings of a
+// butterfly over lane xor 1, 2, 4 and 8.  After each step both lanes of a pair
+// hold the same bits, so pairing by mirror (lane 7 - i within 8, 15 - i within
+// 16) adds the same two partial sums as xor 4 and xor 8 would.
+__device__ __forceinline__ float group_sum(float v, int group) {
+  if (group >= 2) v += dpp_move<0xB1, 0xf>(v);   // quad_perm [1,0,3,2]: lane ^ 1
+  if (group >= 4) v += dpp_move<0x4E, 0xf>(v);   // quad_perm [2,3,0,1]: lane ^ 2
+  if (group >= 8) v += dpp_move<0x141, 0xf>(v);  // row_half_mirror
+  if (group >= 16) v += dpp_move<0x140, 0xf>(v); // row_mirror
+  return v;
+}
+
 // Inclusive prefix sum over the 64 lanes of a wave: shifts by 1, 2, 4, 8 inside
 // each row of 16 lanes, then lane 15 of row 0 and lane 31 carried into the
 // later rows.
