@@ -165,7 +165,9 @@ __global__ __launch_bounds__(SNT * HP, 2 / HP) void ssd_chunk_kernel(SsdArgs a, 
     const int nv = min(SBT, L - c * SBT);
 #pragma unroll
     for (int i = 0; i < 2; ++i) __builtin_amdgcn_raw_buffer_store_b128(yst[i], ysr, yoff[i], 0, 0);
-    lds_barrier();  // the previous chunk's LDS reads are done
+    // no barrier before the staging: every read of C, B, X and the gamma rows
+    // of the previous chunk came before its last barrier, and the only reads
+    // since (its output rows) touch none of what is staged here
 #pragma unroll
     for (int i = 0; i < NCB; ++i) {
       const int q = tid + NTH * i, t = q >> 4, cc = q & 15;
