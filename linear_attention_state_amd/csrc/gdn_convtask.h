@@ -218,9 +218,10 @@ __device__ __forceinline__ void conv_prefetch(SM& sm, const ScanArgs& a, const C
 }
 
 // Sum over the 16 lanes of a key head (a DPP row): the same pairings as a
-// butterfly over lane xor 1, 2, 4, 8, so every lane ends with the same bits as
-// the conv kernel's shuffle reduction (each step adds two equal partial sums
-// of the two halves, and the order of the two does not change a float sum).
+// butterfly over lane xor 1, 2, 4, 8, and the same steps as the conv kernel's
+// group_sum, so every lane ends with the bits the conv kernel computes (each
+// step adds two equal partial sums of the two halves, and the order of the
+// two does not change a float sum).
 __device__ __forceinline__ float head_sum(float v) {
   v += dpp_move<0xB1, 0xf>(v);   // quad_perm [1,0,3,2]: lane ^ 1
   v += dpp_move<0x4E, 0xf>(v);   // quad_perm [2,3,0,1]: lane ^ 2
