@@ -193,3 +193,15 @@ def test_out_of_pool_index_is_skipped_and_reported():
     b_pad = workloads.Batch("pad", b.layer, b.x, b.conv_weight, b.g, b.beta, b.cu_seqlens, b.read_idx.clone(),
                             pad, b.conv_pool, b.ssm_pool)
     compare(b_pad, (out, cp, sp), run_oracle(b_pad))
+
+
+def test_more_sequences_than_the_launch_order_holds():
+    """1,030 chunked sequences of 2-66 tokens beside one-token and empty ones,
+    more than the 1,024 the longest-first launch order holds: the conv kernel
+    then runs first and the chunk kernel covers every sequence in index order."""
+    layer = workloads.Layer(2, 4, 128, 128, 4, "bf16")
+    lengths = ([2, 3, 66, 5, 2, 9, 4, 2, 7, 3] * 103)[:1030] + [1, 0, 1, 1]
+    b = workloads.random_batch(layer, lengths, seed=17)
+    print("case many: %d sequences, T=%d" % (len(lengths), b.total_tokens), flush=True)
+    errs = compare(b, run_gpu(b), run_oracle(b))
+    print("many: out %.3e state %.3e" % (errs["out_rel_l2"], errs["state_rel_l2"]), flush=True)

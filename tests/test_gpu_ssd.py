@@ -256,3 +256,12 @@ def test_conv_then_scan_as_a_mamba2_mixer_core():
                     _rel(pc[int(b.write_idx[s])].double().numpy(), rpool[int(b.write_idx[s])]))
     print("conv+scan: worst %.3e" % worst, flush=True)
     assert worst <= 2 * TOL
+
+
+def test_more_sequences_than_the_launch_order_holds():
+    """1,030 sequences of 0-66 tokens, more than the 1,024 the longest-first
+    launch order holds: the chunk kernel then covers every sequence in index
+    order."""
+    lengths = ([2, 3, 1, 0, 2, 66, 5, 1, 2, 9] * 103)[:1030]
+    b = workloads.ssd_batch(workloads.MAMBA2_SMALL, lengths, seed=16)
+    _check("many", b)
