@@ -69,3 +69,16 @@ def test_tiny_fp32_workload_takes_the_chunk_kernel():
     gpu, kt = _run_timed(b)
     assert kt.get("chunk_generic", (0.0, 0))[1] == 1, kt
     compare(b, gpu, run_oracle(b))
+
+
+def test_more_sequences_than_the_launch_order_holds():
+    """1,030 chunked sequences beside short ones, more than the 1,024 the
+    longest-first launch order holds: the fp32 chunk kernel then covers every
+    sequence in index order."""
+    layer = workloads.Layer(2, 4, 32, 64, 3, "f32")
+    lengths = ([2, 3, 66, 5, 2, 9, 4, 2, 7, 3] * 103)[:1030] + [1, 0, 1, 1]
+    b = workloads.random_batch(layer, lengths, seed=301)
+    print("case many: %d sequences, T=%d" % (len(lengths), b.total_tokens), flush=True)
+    gpu, kt = _run_timed(b)
+    assert kt.get("chunk_generic", (0.0, 0))[1] == 1, kt
+    compare(b, gpu, run_oracle(b))

@@ -259,3 +259,13 @@ def test_conv_inside_for_a_single_sequence():
     assert torch.equal(out_f.view(torch.int16), out_s.view(torch.int16))
     assert torch.equal(cp_f.view(torch.int16), cp_s.view(torch.int16))
     assert torch.equal(sp_f, sp_s)
+
+
+def test_more_sequences_than_the_launch_order_holds():
+    """1,030 chunked sequences beside short ones, more than the 1,024 the
+    longest-first launch order holds: the conv kernel then runs first and the
+    KDA chunk kernel covers every sequence in index order."""
+    layer = workloads.Layer(2, 4, 128, 128, 4, "bf16")
+    lengths = ([2, 3, 66, 5, 2, 9, 4, 2, 7, 3] * 103)[:1030] + [1, 0, 1, 1]
+    b = workloads.random_batch(layer, lengths, seed=18)
+    _check("many", b, _g(b, 19))
