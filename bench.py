@@ -92,10 +92,13 @@ def token_path_bytes(layer, n_tokens: int) -> float:
 
 # The source files of each profiled kernel: its own file, and for the two chunk
 # kernels the header holding the conv tasks they run.
-KERNEL_SOURCES = {"chunk_scan": ("gdn_chunk.hip", "gdn_convtask.h"), "token_recurrent": ("gdn_recurrent.hip",),
-                  "kda_chunk": ("kda_chunk.hip", "gdn_convtask.h"), "chunk_generic": ("gdn_chunk_generic.hip",),
-                  "conv_silu_norm": ("gdn_conv.hip",), "ssd_scan": ("ssd_scan.hip",), "ssd_token": ("ssd_scan.hip",),
-                  "state_copy": ("gdn_conv.hip",)}
+# each kernel's .hip followed by every local header it includes, directly or not
+KERNEL_SOURCES = {"chunk_scan": ("gdn_chunk.hip", "gdn_device.h", "gdn_mfma.h", "gdn_convtask.h"),
+                  "token_recurrent": ("gdn_recurrent.hip", "gdn_device.h"),
+                  "kda_chunk": ("kda_chunk.hip", "gdn_device.h", "gdn_mfma.h", "gdn_convtask.h"),
+                  "chunk_generic": ("gdn_chunk_generic.hip", "gdn_device.h", "gdn_mfma.h"),
+                  "conv_silu_norm": ("gdn_conv.hip", "gdn_device.h"), "ssd_scan": ("ssd_scan.hip", "gdn_device.h"),
+                  "ssd_token": ("ssd_scan.hip", "gdn_device.h"), "state_copy": ("gdn_conv.hip", "gdn_device.h")}
 
 
 def kernel_source_sha(kernel: str):

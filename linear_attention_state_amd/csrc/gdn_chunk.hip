@@ -78,9 +78,8 @@ constexpr int NB = D / 16 / NS;   // 16-column state tiles per state wave
 constexpr int PS = D + 4;         // fp32 pitch of the state staged in LDS (start and end)
 
 // LDS.  The [64][128] bf16 tiles keep natural row-major order with the 16-byte
-// chunk c of row t stored at chunk c ^ f(t), f(t) = 2 (t & 7) + ((t >> 3) & 1):
-// the 16 rows of a row-operand read, and the 16 rows of a transposed read, then
-// fall on distinct banks.
+// chunk c of row t stored at chunk c ^ f(t) (swz_f): every pass of a row-operand
+// read then falls on distinct banks, and a transposed read on each bank twice.
 struct ChunkBuf {
   uint16_t q[BT * D];
   uint16_t k[BT * D];
