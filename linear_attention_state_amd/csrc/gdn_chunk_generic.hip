@@ -46,7 +46,7 @@ __device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
 }
 
 template <int DK, int DV>
-struct GSmem {
+struct alignas(16) GSmem {
   float k[GC][DK + 4];
   float q[GC][DK + 4];
   float v[GC][DV + 4];

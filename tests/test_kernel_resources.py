@@ -75,18 +75,13 @@ def _resources(src_name, tmp_path):
 @pytest.mark.skipif(not os.path.exists(build.HIPCC), reason="hipcc not installed")
 def test_fp32_chunk_kernel_has_no_scratch(tmp_path):
     """Every instantiation (d_k, d_v in 16..128, bf16 and fp32 activations) keeps
-    its state tiles in registers without scratch, except the fp32-activation
-    128 x 128 one: its next chunk's q/k rows held in registers over the chunk
-    push out a few loop-invariant values (addresses, bounds), stored before the
-    chunk loop and reloaded once per chunk outside the unrolled products; at
-    most 160 bytes per lane.  That variant is still faster than the one that
-    keeps no rows in flight, which needs no scratch."""
+    its state tiles in registers without scratch, the fp32-activation 128 x 128
+    one included, although it holds the next chunk's q/k rows in registers over
+    the chunk: its operand reads are 16-byte LDS loads (the LDS struct is
+    16-byte aligned), which leaves room for them."""
     seen = {k: v for k, v in _resources("gdn_chunk_generic.hip", tmp_path).items() if "chunk_generic_kernel" in k}
     assert len(seen) == 32, seen
-    fp32_128 = next((k for k in seen if "chunk_generic_kernelILi128ELi128ELb0E" in k), None)
-    assert fp32_128 is not None, sorted(seen)
-    assert seen[fp32_128] <= 160, seen
-    assert all(v == 0 for k, v in seen.items() if k != fp32_128), seen
+    assert all(v == 0 for v in seen.values()), seen
 
 
 @pytest.mark.skipif(not os.path.exists(build.HIPCC), reason="hipcc not installed")
