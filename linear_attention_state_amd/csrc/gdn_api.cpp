@@ -221,10 +221,22 @@ hipError_t timed(int k, hipStream_t st, F launch) {
   if (!g_timing.on) return launch();
   std::lock_guard<std::mutex> lock(g_timing.mu);
   hipEvent_t a = take_event(), b = take_event();
-  if (!a || !b) return launch();
-  hipEventRecord(a, st);
-  hipError_t e = launch();
-  hipEventRecord(b, st);
+  if (!a || !b) {
+    if (a) g_timing.spare.push_back(a);
+    if (b) g_timing.spare.push_back(b);
+    return launch();
+  }
+  if (hipEventRecord(a, st) != hipSuccess) {  // this launch goes untimed
+    g_timing.spare.push_back(a);
+    g_timing.spare.push_back(b);
+    return launch();
+  }
+  const hipError_t e = launch();
+  if (hipEventRecord(b, st) != hipSuccess) {
+    g_timing.spare.push_back(a);
+    g_timing.spare.push_back(b);
+    return e;
+  }
   g_timing.pending.push_back({k, a, b});
   return e;
 }
@@ -235,9 +247,13 @@ extern "C" int gdn_kernel_timing(int enable) {
   std::lock_guard<std::mutex> lock(g_timing.mu);
   if (enable) {
     for (auto& r : g_timing.pending) {
-      hipEventSynchronize(r.b);
-      g_timing.spare.push_back(r.a);
-      g_timing.spare.push_back(r.b);
+      if (hipEventSynchronize(r.b) == hipSuccess) {
+        g_timing.spare.push_back(r.a);
+        g_timing.spare.push_back(r.b);
+      } else {  // not reused: an event in an error state would spoil later timings
+        (void)hipEventDestroy(r.a);
+        (void)hipEventDestroy(r.b);
+      }
     }
     g_timing.pending.clear();
     for (int k = 0; k < K_COUNT; ++k) { g_timing.total_ms[k] = 0; g_timing.launches[k] = 0; }
@@ -266,7 +282,7 @@ extern "C" int gdn_mfma_peak_probe(int32_t dtype, int32_t iters, double* tflops,
   float ms = 0.f;
   if (e == hipSuccess) e = hipEventElapsedTime(&ms, ev[0], ev[1]);
   for (hipEvent_t v : ev)
-    if (v) hipEventDestroy(v);
+    if (v) (void)hipEventDestroy(v);  // clean-up: the probe's own status is e
   if (e != hipSuccess) return fail(GDN_EHIP, "MFMA probe: %s", hipGetErrorString(e));
   const double flop_per = bf16 ? 16.0 * 16 * 32 * 2 : 16.0 * 16 * 4 * 2;
   *tflops = (double)blocks * 4 * iters * 8 * flop_per / (ms * 1e-3) / 1e12;
@@ -296,7 +312,7 @@ extern "C" int gdn_hbm_copy_probe(const void* src, void* dst, int64_t bytes, int
   float ms = 0.f;
   if (e == hipSuccess) e = hipEventElapsedTime(&ms, ev[0], ev[1]);
   for (hipEvent_t v : ev)
-    if (v) hipEventDestroy(v);
+    if (v) (void)hipEventDestroy(v);  // clean-up: the probe's own status is e
   if (e != hipSuccess) return fail(GDN_EHIP, "copy probe: %s", hipGetErrorString(e));
   *gbs = 2.0 * (double)bytes * reps / (ms * 1e-3) / 1e9;
   return GDN_OK;
@@ -417,11 +433,17 @@ hipError_t fork_side(hipStream_t st, hipStream_t* side) {
     e = hipStreamCreateWithFlags(&s, hipStreamNonBlocking);
     if (e == hipSuccess) e = hipEventCreateWithFlags(&a, fl);
     if (e == hipSuccess) e = hipEventCreateWithFlags(&b, fl);
-    if (cur != dev) hipSetDevice(cur);
-    if (e != hipSuccess) return e;
+    const hipError_t back = cur != dev ? hipSetDevice(cur) : hipSuccess;
+    if (e != hipSuccess) {  // nothing half-made is kept
+      if (b) (void)hipEventDestroy(b);
+      if (a) (void)hipEventDestroy(a);
+      if (s) (void)hipStreamDestroy(s);
+      return e;
+    }
     g_side.stream[dev] = s;
     g_side.fork_ev[dev] = a;
     g_side.join_ev[dev] = b;
+    if (back != hipSuccess) return back;  // the caller's device could not be restored
   }
   *side = g_side.stream[dev];
   if ((e = hipEventRecord(g_side.fork_ev[dev], st)) != hipSuccess) return e;
