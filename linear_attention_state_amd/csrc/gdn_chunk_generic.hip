@@ -253,16 +253,20 @@ __global__ __launch_bounds__(GT) void chunk_generic_kernel(ScanArgs a, SeqOrder 
     if constexpr (SP) {
       if (c + 1 < N) prefetch_qk(c + 1);
     }
-    // ---- blocks of A (even w) and P (odd w): lane holds D[t = 16R + 4 lq + i][j = 16Cb + lr]
+    // ---- blocks of A (even w) and P (odd w): lane holds D[t = 16R + 4 lq + i][j = 16Cb + lr].
+    // The channel sum runs in the order 16 g + 4 lq + s, so that a lane's four
+    // channels of group g are one 16-byte read of each operand row.
     for (int w = wv; w < 20; w += 4) {
       int R, Cb;
       pair_rc(w >> 1, R, Cb);
       const bool isp = w & 1;
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int st = 0; st < DK / 4; ++st) {
-        const float x = isp ? sm.q[16 * R + lr][4 * st + lq] : sm.k[16 * R + lr][4 * st + lq];
-        acc = mfma4(x, sm.k[16 * Cb + lr][4 * st + lq], acc);
+      for (int g = 0; g < DK / 16; ++g) {
+        const f32x4 xv = *reinterpret_cast<const f32x4*>(isp ? &sm.q[16 * R + lr][16 * g + 4 * lq] : &sm.k[16 * R + lr][16 * g + 4 * lq]);
+        const f32x4 yv = *reinterpret_cast<const f32x4*>(&sm.k[16 * Cb + lr][16 * g + 4 * lq]);
+#pragma unroll
+        for (int s = 0; s < 4; ++s) acc = mfma4(xv[s], yv[s], acc);
       }
       const int j = 16 * Cb + lr;
       const float gj = sm.gam[j];
